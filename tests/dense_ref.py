@@ -1,0 +1,111 @@
+"""Brute-force dense evaluation of a decode MoE layer in NumPy fp64.
+
+A second, independent evaluation used only to pin the oracle on tiny inputs:
+it decodes stored codes with lookup tables (the oracle uses bit formulas),
+routes with a stable argsort (the oracle scans), and evaluates EVERY expert on
+every row, weighting by a mask that is zero for the experts a row did not
+select (the oracle evaluates only the selected ones, slot by slot).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# OCP Microscaling Formats v1.0, FP4 E2M1 element values by code 0..15.
+E2M1_TABLE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                       -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def act_to_f64(a: np.ndarray, fmt: str) -> np.ndarray:
+    return np.asarray(a, np.float32).astype(np.float64) if fmt == "f32" else bf16_to_f64(a)
+
+
+def _unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    n, kh = packed.shape
+    out = np.empty((n, 2 * kh), np.uint8)
+    out[:, 0::2] = packed & 15
+    out[:, 1::2] = packed >> 4
+    return out
+
+
+def dense_weight(proj, e: int) -> np.ndarray:
+    """Expert e of a synth.Projection as a dense float64 [N, K] matrix."""
+    if proj.fmt == "f32":
+        return proj.data[e].astype(np.float64)
+    if proj.fmt == "bf16":
+        return bf16_to_f64(proj.data[e])
+    q = _unpack_nibbles(proj.data[e])
+    if proj.fmt == "aff4":
+        s = np.repeat(bf16_to_f64(proj.scale[e]), 64, axis=1)
+        b = np.repeat(bf16_to_f64(proj.bias[e]), 64, axis=1)
+        return s * q.astype(np.float64) + b
+    if proj.fmt == "mxfp4":
+        sc = np.repeat(np.ldexp(1.0, proj.scale[e].astype(np.int64) - 127), 32, axis=1)
+        return E2M1_TABLE[q] * sc
+    raise ValueError(proj.fmt)
+
+
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def _sigmoid(v):
+    return 1.0 / (1.0 + np.exp(-v))
+
+
+def dense_forward(layer, x: np.ndarray):
+    """Returns (out [m,H], mask-weight matrix [m,E], selected index lists)."""
+    spec = layer.spec
+    E, k = spec.num_experts, spec.top_k
+    X = act_to_f64(x, spec.act_fmt)                      # [m, H]
+    Wr = act_to_f64(layer.router, spec.act_fmt)          # [E, H]
+    L = X @ Wr.T                                         # [m, E]
+    if spec.routing == "sigmoid_bias":
+        key = _sigmoid(L) + layer.expert_bias.astype(np.float64)[None, :]
+    else:
+        key = L
+    m = X.shape[0]
+    weights = np.zeros((m, E))
+    selected = []
+    for r in range(m):
+        order = np.argsort(-key[r], kind="stable")[:k]   # ties: lower index first
+        selected.append(order)
+        if spec.routing == "softmax":
+            p = np.exp(L[r] - L[r].max())
+            p = p / p.sum()
+            wsel = p[order]
+        else:
+            wsel = _sigmoid(L[r][order])
+        if spec.norm_topk:
+            wsel = wsel / wsel.sum()
+        wsel = wsel * spec.routed_scaling_factor
+        weights[r, order] = wsel
+    mask = np.zeros((m, E), bool)
+    for r, order in enumerate(selected):
+        mask[r, order] = True
+    out = np.zeros_like(X)
+    for e in range(E):
+        Wg = dense_weight(layer.gate, e)
+        Wu = dense_weight(layer.up, e)
+        Wd = dense_weight(layer.down, e)
+        if spec.weight_before_ffn:
+            U = X * weights[:, e:e + 1]
+            c = mask[:, e].astype(np.float64)
+        else:
+            U = X
+            c = weights[:, e]
+        Y = (_silu(U @ Wg.T) * (U @ Wu.T)) @ Wd.T
+        out += c[:, None] * Y
+    if spec.shared:
+        Sg = act_to_f64(layer.sh_gate, spec.act_fmt)
+        Su = act_to_f64(layer.sh_up, spec.act_fmt)
+        Sd = act_to_f64(layer.sh_down, spec.act_fmt)
+        ys = (_silu(X @ Sg.T) * (X @ Su.T)) @ Sd.T
+        if spec.shared_gated:
+            g = _sigmoid(X @ act_to_f64(layer.sh_gate_vec, spec.act_fmt))
+            ys = ys * g[:, None]
+        out += ys
+    return out, weights, selected

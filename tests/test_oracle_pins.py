@@ -1,0 +1,398 @@
+"""Pins of the oracle against things other than itself (CPU only).
+
+Each test ties the oracle to a value the pages print, a standard's table, a
+closed form, a special case, or the independent NumPy brute-force dense
+evaluation in ``dense_ref.py``.  Chosen so that a dropped term, a wrong sign
+or index, or a transposed operand in the oracle fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from mixture_experts_decode_amd import synth
+from tests import dense_ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny(**kw):
+    base = dict(name="tiny", hidden=64, num_experts=8, top_k=2, inter=64, shared_inter=32,
+                act_fmt="f32", expert_fmt="f32", routing="softmax", norm_topk=True,
+                w_std=0.1, rows=(4,))
+    base.update(kw)
+    return synth.LayerSpec(**base)
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+# ------------------------------------------------------------------ P-1 formats
+
+def test_e2m1_all_codes_match_ocp_table():
+    table = json.load(open(os.path.join(GOLDEN, "e2m1_ocp.json")))["code_to_value"]
+    codes = np.arange(32, dtype=np.uint8) % 16
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)[None, :]
+    scale = np.array([[127]], np.uint8)                       # 2^0
+    got = oracle.decode_row("mxfp4", packed, scale, None, 32, 0)
+    want = np.array([table[c] for c in codes])
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_e8m0_all_finite_codes():
+    e = np.arange(255, dtype=np.uint8)
+    codes = np.full(32, 2, np.uint8)                          # E2M1 1.0
+    packed = np.tile((codes[0::2] | (codes[1::2] << 4)).astype(np.uint8), (255, 1))
+    for n in range(255):
+        got = oracle.decode_row("mxfp4", packed, e[:, None], None, 32, n)
+        assert np.all(got == math.ldexp(1.0, n - 127)), n
+
+
+def test_aff4_all_codes_random_scale_bias():
+    rng = np.random.default_rng(1)
+    for trial in range(20):
+        s_bits = synth.f32_to_bf16_bits(rng.standard_normal(2).astype(np.float32) * 0.01)
+        b_bits = synth.f32_to_bf16_bits(rng.standard_normal(2).astype(np.float32) * 0.05)
+        q = np.concatenate([np.arange(16), rng.integers(0, 16, 112)]).astype(np.uint8)
+        packed = (q[0::2] | (q[1::2] << 4)).astype(np.uint8)[None, :]
+        got = oracle.decode_row("aff4", packed, s_bits[None, :], b_bits[None, :], 128, 0)
+        s = dense_ref.bf16_to_f64(s_bits)
+        b = dense_ref.bf16_to_f64(b_bits)
+        want = np.array([s[i // 64] * float(q[i]) + b[i // 64] for i in range(128)])
+        assert np.array_equal(got, want)
+
+
+def test_packed_nibble_order_low_first():
+    # Byte 0x21: element 0 is code 1 (0.5), element 1 is code 2 (1.0).
+    packed = np.zeros((1, 16), np.uint8)
+    packed[0, 0] = 0x21
+    got = oracle.decode_row("mxfp4", packed, np.array([[127]], np.uint8), None, 32, 0)
+    assert got[0] == 0.5 and got[1] == 1.0 and np.all(got[2:] == 0)
+
+
+def test_bf16_and_f32_decode():
+    rng = np.random.default_rng(2)
+    bits = rng.integers(0, 1 << 16, 4096).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]                   # finite only
+    got = oracle.decode_act("bf16", bits)
+    want = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(got, want)
+    f = rng.standard_normal(64).astype(np.float32)
+    assert np.array_equal(oracle.decode_act("f32", f), f.astype(np.float64))
+
+
+# ------------------------------------------------------ P-3 page's worked example
+
+def test_routed_slot_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "routed_slot.json")))
+    for case in g["cases"]:
+        xo, wo = oracle.routed_slot(g["x"], g["w"], case["before_ffn"])
+        assert list(xo) == case["x_out"] and wo == case["w_out"]
+
+
+# ------------------------------------------------ P-4 closed forms at x = 0
+
+@pytest.mark.parametrize("routing", ["softmax", "sigmoid_logit"])
+def test_zero_input_selects_first_k_uniform(routing):
+    spec = tiny(top_k=4, routing=routing, norm_topk=True)
+    layer = synth.make_layer(spec, seed=3)
+    x = np.zeros((2, spec.hidden), np.float32)
+    r = oracle.forward(layer, x)
+    assert np.array_equal(r.idx, np.tile(np.arange(4, dtype=np.int32), (2, 1)))
+    assert np.all(r.w == 0.25)
+    assert np.all(r.out == 0.0)
+
+
+def test_zero_input_sigmoid_bias_selects_top_bias():
+    spec = tiny(top_k=3, routing="sigmoid_bias", norm_topk=True)
+    layer = synth.make_layer(spec, seed=4)
+    layer.expert_bias[:] = np.array([0.1, 0.5, 0.5, -0.2, 0.7, 0.0, 0.5, 0.3], np.float32)
+    x = np.zeros((1, spec.hidden), np.float32)
+    r = oracle.forward(layer, x)
+    assert list(r.idx[0]) == [4, 1, 2]          # 0.7, then the tie 0.5 by lower index
+    assert np.all(r.w == 1.0 / 3.0)
+
+
+def test_zero_input_raw_logit_top1_weight_half():
+    spec = tiny(top_k=1, routing="sigmoid_logit", norm_topk=False, weight_before_ffn=True)
+    layer = synth.make_layer(spec, seed=5)
+    r = oracle.forward(layer, np.zeros((1, spec.hidden), np.float32))
+    assert r.idx[0, 0] == 0 and r.w[0, 0] == 0.5
+
+
+# ---------------------------------------------------- P-5 tie-break by index
+
+def test_duplicate_router_rows_lower_index_first():
+    spec = tiny(top_k=2)
+    layer = synth.make_layer(spec, seed=6)
+    x = synth.make_x(spec, 6, rows=4)
+    r0 = oracle.forward(layer, x)
+    # Copy the winning expert's router row onto a lower-numbered expert.
+    for row in range(4):
+        lay = synth.make_layer(spec, seed=6)
+        win = int(r0.idx[row, 0])
+        other = 0 if win != 0 else None
+        if other is None:
+            continue
+        lay.router[other] = lay.router[win]
+        r = oracle.forward(lay, x[row:row + 1])
+        assert list(r.idx[0]) == [other, win]
+        assert r.w[0, 0] == r.w[0, 1]
+
+
+# ------------------------------------------------------- P-6 / P-8 weights
+
+def test_softmax_norm_equals_softmax_over_selected():
+    spec = tiny(top_k=3, routed_scaling_factor=2.5)
+    layer = synth.make_layer(spec, seed=7)
+    x = synth.make_x(spec, 7, rows=4)
+    r = oracle.forward(layer, x)
+    for row in range(4):
+        sel = r.logits[row, r.idx[row]]
+        e = [math.exp(v - max(sel)) for v in sel]
+        want = [2.5 * v / math.fsum(e) for v in e]
+        assert np.allclose(r.w[row], want, rtol=4e-16, atol=0)
+        assert abs(math.fsum(r.w[row]) - 2.5) < 1e-14
+
+
+def test_softmax_without_norm_is_full_softmax():
+    # k = E without norm: the weights are the whole softmax, summing to rsf.
+    spec = tiny(top_k=8, num_experts=8, norm_topk=False, routed_scaling_factor=1.0)
+    layer = synth.make_layer(spec, seed=19)
+    r = oracle.forward(layer, synth.make_x(spec, 19, rows=4))
+    assert np.allclose(r.w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    # k < E: each weight is exp(l - max) over the sum across ALL experts.
+    spec2 = tiny(top_k=2, num_experts=8, norm_topk=False)
+    layer2 = synth.make_layer(spec2, seed=19)
+    r2 = oracle.forward(layer2, synth.make_x(spec2, 19, rows=4))
+    for row in range(4):
+        l = r2.logits[row]
+        den = math.fsum(math.exp(v - l.max()) for v in l)
+        want = [math.exp(l[e] - l.max()) / den for e in r2.idx[row]]
+        assert np.allclose(r2.w[row], want, rtol=1e-15, atol=0)
+        assert r2.w[row].sum() < 1.0
+
+
+def test_top1_norm_weight_is_exactly_one():
+    for routing in ("softmax", "sigmoid_bias", "sigmoid_logit"):
+        spec = tiny(top_k=1, routing=routing, norm_topk=True)
+        layer = synth.make_layer(spec, seed=8)
+        r = oracle.forward(layer, synth.make_x(spec, 8, rows=4))
+        assert np.all(r.w == 1.0)
+
+
+def test_sigmoid_bias_weights_are_unbiased():
+    spec = tiny(top_k=3, routing="sigmoid_bias", norm_topk=False)
+    layer = synth.make_layer(spec, seed=9)
+    r = oracle.forward(layer, synth.make_x(spec, 9, rows=4))
+    for row in range(4):
+        want = [1.0 / (1.0 + math.exp(-v)) for v in r.logits[row, r.idx[row]]]
+        assert np.allclose(r.w[row], want, rtol=1e-15, atol=0)
+        keys = [1.0 / (1.0 + math.exp(-r.logits[row, e])) + float(layer.expert_bias[e])
+                for e in range(spec.num_experts)]
+        assert sorted(r.idx[row]) == sorted(np.argsort(-np.array(keys), kind="stable")[:3])
+
+
+# ------------------------------------------------- P-7 dense limit (k = E)
+
+def test_k_equals_E_is_dense_softmax_mixture():
+    spec = tiny(top_k=8, num_experts=8)
+    layer = synth.make_layer(spec, seed=10)
+    x = synth.make_x(spec, 10, rows=3)
+    r = oracle.forward(layer, x)
+    X = x.astype(np.float64)
+    L = X @ layer.router.astype(np.float64).T
+    P = np.exp(L - L.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    want = np.zeros_like(X)
+    for e in range(8):
+        Wg, Wu, Wd = (layer.gate.data[e].astype(np.float64), layer.up.data[e].astype(np.float64),
+                      layer.down.data[e].astype(np.float64))
+        g = X @ Wg.T
+        want += P[:, e:e + 1] * (((g / (1 + np.exp(-g))) * (X @ Wu.T)) @ Wd.T)
+    assert np.max(np.abs(r.out - want)) <= 1e-13 * rms(want)
+
+
+# ---------------------------------------------- P-9 SwiGLU wiring, identity
+
+@pytest.mark.parametrize("before", [False, True])
+def test_identity_experts_give_silu_times_x(before):
+    spec = tiny(hidden=64, inter=64, top_k=1, routing="sigmoid_logit", norm_topk=False,
+                weight_before_ffn=before)
+    layer = synth.make_layer(spec, seed=11)
+    eye = np.eye(64, dtype=np.float32)
+    for p in (layer.gate, layer.up, layer.down):
+        p.data[:] = eye
+    x = synth.make_x(spec, 11, rows=3)
+    r = oracle.forward(layer, x)
+    for row in range(3):
+        w = r.w[row, 0]
+        xs = x[row].astype(np.float64)
+        if before:
+            u = w * xs
+            want = u / (1 + np.exp(-u)) * u
+        else:
+            want = w * (xs / (1 + np.exp(-xs)) * xs)
+        assert np.allclose(r.out[row], want, rtol=1e-15, atol=1e-300)
+
+
+# ------------------------------------------ P-10 brute force, all variants
+
+VARIANTS = list(itertools.product(
+    ["f32", "bf16"], ["f32", "bf16", "aff4", "mxfp4"],
+    ["softmax", "sigmoid_bias", "sigmoid_logit"], [False, True], [False, True],
+    ["none", "plain", "gated"]))
+
+
+@pytest.mark.parametrize("act,fmt,routing,norm,before,shared", VARIANTS)
+def test_oracle_matches_dense_brute_force(act, fmt, routing, norm, before, shared):
+    spec = tiny(act_fmt=act, expert_fmt=fmt, routing=routing, weight_before_ffn=before,
+                top_k=3, norm_topk=norm, routed_scaling_factor=1.5,
+                shared=shared != "none", shared_gated=shared == "gated", shared_inter=32,
+                w_std=0.1)
+    seed = VARIANTS.index((act, fmt, routing, norm, before, shared))
+    layer = synth.make_layer(spec, seed=seed, threads=1)
+    x = synth.make_x(spec, seed, rows=4)
+    r = oracle.forward(layer, x)
+    want, weights, selected = dense_ref.dense_forward(layer, x)
+    for row in range(4):
+        assert list(r.idx[row]) == list(selected[row])
+        assert np.allclose(r.w[row], weights[row, selected[row]], rtol=1e-14, atol=0)
+    assert np.max(np.abs(r.out - want)) <= 1e-12 * rms(want)
+
+
+# --------------------------------------------------------------- P-11 sort
+
+@pytest.mark.parametrize("m,k,E", [(1, 1, 1), (1, 8, 128), (8, 8, 128), (32, 1, 16),
+                                   (16, 8, 256), (5, 3, 4)])
+def test_sort_is_stable_argsort_with_invariants(m, k, E):
+    rng = np.random.default_rng(m * 1000 + k * 10 + E)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(m)]).astype(np.int32)
+    s = oracle.sort_pairs(idx, E)
+    flat = idx.reshape(-1)
+    assert np.array_equal(s["sorted_pair"], np.argsort(flat, kind="stable"))
+    counts = np.bincount(flat, minlength=E)
+    assert np.array_equal(s["expert_offsets"], np.concatenate([[0], np.cumsum(counts)]))
+    assert s["expert_offsets"][-1] == m * k
+    assert np.array_equal(s["sorted_pair"][s["pair_to_perm"]], np.arange(m * k))
+    assert np.array_equal(s["active_experts"], np.nonzero(counts)[0])
+    assert s["active_count"] == np.count_nonzero(counts)
+    assert s["active_count"] <= min(m * k, E)
+
+
+# ------------------------------------------------------ P-12 m-invariance
+
+def test_row_result_does_not_depend_on_m():
+    spec = tiny(act_fmt="bf16", expert_fmt="aff4", routing="sigmoid_bias", top_k=3,
+                shared=True, shared_gated=True)
+    layer = synth.make_layer(spec, seed=12)
+    x = synth.make_x(spec, 12, rows=4)
+    full = oracle.forward(layer, x)
+    for row in range(4):
+        one = oracle.forward(layer, x[row:row + 1])
+        assert np.array_equal(one.out[0], full.out[row])
+        assert np.array_equal(one.idx[0], full.idx[row])
+
+
+# ---------------------------------- P-13 raw-logit vs sigmoid-value selection
+
+def test_raw_logit_selects_same_as_sigmoid_values():
+    spec = tiny(top_k=2, routing="sigmoid_logit", norm_topk=False, num_experts=16)
+    layer = synth.make_layer(spec, seed=13)
+    x = np.random.default_rng(13).standard_normal((64, 64)).astype(np.float32)
+    r = oracle.forward(layer, x)
+    for row in range(64):
+        sig = 1.0 / (1.0 + np.exp(-r.logits[row]))
+        if len(np.unique(sig)) < len(sig):
+            continue
+        assert sorted(r.idx[row]) == sorted(np.argsort(-sig, kind="stable")[:2])
+
+
+def test_raw_logit_differs_from_sigmoid_only_under_saturation():
+    spec = tiny(top_k=1, routing="sigmoid_logit", norm_topk=False, num_experts=4)
+    layer = synth.make_layer(spec, seed=14)
+    layer.router[:] = 0
+    layer.router[0, 0] = 40.0
+    layer.router[1, 0] = 45.0
+    x = np.zeros((1, 64), np.float32)
+    x[0, 0] = 1.0
+    r = oracle.forward(layer, x)
+    # Both sigmoid values round to 1.0 in double (a value tie that would go to
+    # expert 0); the raw logits do not tie and pick expert 1.
+    assert 1.0 / (1.0 + math.exp(-40.0)) == 1.0 / (1.0 + math.exp(-45.0)) == 1.0
+    assert r.idx[0, 0] == 1
+
+
+# --------------------------------------- P-14 weight before vs after the FFN
+
+def test_weight_placement_differs_and_each_matches_its_definition():
+    base = dict(top_k=2, routing="sigmoid_logit", norm_topk=False, w_std=0.3)
+    after = synth.make_layer(tiny(weight_before_ffn=False, **base), seed=15)
+    before = synth.make_layer(tiny(weight_before_ffn=True, **base), seed=15)
+    x = synth.make_x(after.spec, 15, rows=4)
+    ra, rb = oracle.forward(after, x), oracle.forward(before, x)
+    assert np.array_equal(ra.idx, rb.idx)
+    assert np.all(ra.w != 1.0)
+    # SwiGLU is not homogeneous: the placements differ by far more than any
+    # tolerance used for parity.
+    assert np.max(np.abs(ra.out - rb.out)) > 0.1 * rms(ra.out)
+    for lay, r in ((after, ra), (before, rb)):
+        want, _, _ = dense_ref.dense_forward(lay, x)
+        assert np.max(np.abs(r.out - want)) <= 1e-12 * rms(want)
+
+
+def test_weight_placement_equal_when_weight_is_one():
+    base = dict(top_k=1, routing="softmax", norm_topk=True)
+    after = synth.make_layer(tiny(weight_before_ffn=False, **base), seed=16)
+    before = synth.make_layer(tiny(weight_before_ffn=True, **base), seed=16)
+    x = synth.make_x(after.spec, 16, rows=4)
+    assert np.array_equal(oracle.forward(after, x).out, oracle.forward(before, x).out)
+
+
+def test_input_weight_commutes_with_projection():
+    # Wg (w x) == w (Wg x) up to rounding: a kernel may scale the projection
+    # instead of the input.
+    spec = tiny(top_k=2, routing="sigmoid_logit", norm_topk=False, weight_before_ffn=True)
+    layer = synth.make_layer(spec, seed=17)
+    x = synth.make_x(spec, 17, rows=4)
+    r = oracle.forward(layer, x)
+    X = x.astype(np.float64)
+    out = np.zeros_like(X)
+    for row in range(4):
+        for j in range(2):
+            e, w = r.idx[row, j], r.w[row, j]
+            g = w * (layer.gate.data[e].astype(np.float64) @ X[row])
+            v = w * (layer.up.data[e].astype(np.float64) @ X[row])
+            out[row] += layer.down.data[e].astype(np.float64) @ (g / (1 + np.exp(-g)) * v)
+    assert np.max(np.abs(out - r.out)) <= 1e-13 * rms(r.out)
+
+
+# ------------------------------------------- P-15 quantized decode is exact
+
+@pytest.mark.parametrize("fmt", ["aff4", "mxfp4"])
+def test_quantized_layer_equals_f32_layer_of_decoded_values(fmt):
+    spec = tiny(act_fmt="bf16", expert_fmt=fmt, top_k=3, w_std=0.02)
+    layer = synth.make_layer(spec, seed=18)
+    x = synth.make_x(spec, 18, rows=4)
+    dense = synth.make_layer(spec.replace(expert_fmt="f32"), seed=18)
+    for name in ("gate", "up", "down"):
+        q, d = getattr(layer, name), getattr(dense, name)
+        for e in range(spec.num_experts):
+            v = dense_ref.dense_weight(q, e)
+            assert np.array_equal(v.astype(np.float32).astype(np.float64), v)  # exact in f32
+            d.data[e] = v.astype(np.float32)
+    rq, rd = oracle.forward(layer, x), oracle.forward(dense, x)
+    assert np.array_equal(rq.idx, rd.idx)
+    assert np.array_equal(rq.out, rd.out)
+
+
+def test_invalid_description_rejected():
+    spec = tiny(expert_fmt="aff4", inter=32)      # aff4 needs I % 64 == 0
+    with pytest.raises(ValueError):
+        synth.check_spec(spec)
