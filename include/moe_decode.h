@@ -1,0 +1,203 @@
+/*
+ * moe_decode.h -- C ABI of libmoe_decode.so: the fused small-batch decode
+ * Mixture-of-Experts layer on one AMD Instinct MI355X (gfx950).
+ *
+ * One call of moe_decode_forward evaluates, for m = 1..max_rows token rows,
+ * the whole decode MoE layer that the metrale page
+ * "forward_bf16_grouped_decode.rs" (fn forward_bf16_grouped_decode) lays out
+ * as five steps -- the per-row router, the sort of (row, slot) pairs by
+ * expert, expert gate+up with SiLU, expert down, and the grouped blend with a
+ * gated shared expert -- on the caller's HIP stream, without host
+ * synchronisation:
+ *
+ *   logits[r,e] = sum_h x[r,h] * Wr[e,h]
+ *   selection   softmax:        top-k of the logits, weight softmax(l)
+ *               sigmoid+bias:   top-k of sigmoid(l)+bias, weight sigmoid(l)
+ *                               (mlxcel page "perf(moe): wire lfm2 to the
+ *                               fused decode-MoE kernel", Summary; iron page
+ *                               "refactor(gemm): split the gemv_q8 grab-bag
+ *                               by family", commit message: select by the
+ *                               biased score, weight by the unbiased one)
+ *               raw-logit:      top-k of the logits, weight sigmoid(l)
+ *                               (frink page "routed_weight_site.rs", module doc)
+ *               ties go to the lower expert index; slots are ordered by key
+ *               descending.  Optional norm_topk_prob (divide by the sum of the
+ *               selected weights), then times routed_scaling_factor.
+ *   expert      y = Wd * (silu(Wg u) * (Wu u)), u = x (weight on the output)
+ *               or u = w x (weight on the input, frink "routed_weight_site.rs",
+ *               fn routed_slot)
+ *   out[r]      = sum_j c_rj y_rj + gamma_r * shared(x_r), c = w or 1,
+ *               gamma = sigmoid(x . w_g) (gated) or 1.
+ *
+ * Ownership: the caller owns every device buffer (weights, pointer tables,
+ * x, out, idx/w outputs, workspace).  A plan owns host memory only; it is
+ * immutable after moe_decode_plan and may be shared by threads and streams,
+ * with one workspace per concurrently running call.  moe_decode_forward
+ * allocates nothing, never synchronises, never reads device memory on the
+ * host, and launches only kernels (no memset/memcpy nodes), so it can be
+ * captured into a HIP graph.
+ *
+ * Errors: every entry point returns a moe_status.  On any status other than
+ * MOE_OK nothing has been launched (except MOE_EHIP from a launch itself);
+ * moe_decode_last_error() then returns a thread-local message.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* bad argument: null pointer, m out of range, ... */
+  MOE_EUNSUPPORTED = 2,  /* a shape or format combination the kernels do not serve */
+  MOE_EWORKSPACE = 3,    /* workspace missing, too small or misaligned */
+  MOE_EHIP = 4           /* a HIP call failed; the message holds its error string */
+} moe_status;
+
+/* Storage formats.  All arrays are row-major [N, K] with K the reduction
+ * dimension (gate/up: N = inter, K = hidden; down: N = hidden, K = inter),
+ * as in the metrale page "helpers_a.rs" (packed [N, K/2] weights and
+ * [N, K/group] scales; scale block 32 for E8M0).
+ *   MOE_F32        float32
+ *   MOE_BF16       bfloat16 bit patterns (uint16)
+ *   MOE_AFF4_G64   4-bit unsigned codes q, packed [N, K/2] with element 2t in
+ *                  the low nibble of byte t; value = scale*q + bias with one
+ *                  bf16 scale and one bf16 bias per 64 elements along K
+ *                  ([N, K/64] each)
+ *   MOE_MXFP4_B32  OCP MX FP4 E2M1 codes, packed like aff4; value =
+ *                  E2M1(code) * 2^(e-127) with one E8M0 byte e per 32
+ *                  elements along K ([N, K/32]); e = 255 (NaN) is not valid. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_AFF4_G64 = 2, MOE_MXFP4_B32 = 3 } moe_format;
+
+typedef enum {
+  MOE_ROUTE_SOFTMAX = 0,        /* select by logit, weight softmax(l) over all E */
+  MOE_ROUTE_SIGMOID_BIAS = 1,   /* select by sigmoid(l)+bias, weight sigmoid(l) */
+  MOE_ROUTE_SIGMOID_LOGIT = 2   /* select by logit, weight sigmoid(l) */
+} moe_routing;
+
+enum {
+  MOE_NORM_TOPK = 1,          /* divide the selected weights by their sum */
+  MOE_WEIGHT_BEFORE_FFN = 2,  /* the routing weight scales the expert input; output weight 1 */
+  MOE_SHARED = 4,             /* add a shared SwiGLU expert on every row (unscaled input) */
+  MOE_SHARED_GATED = 8,       /* ... times sigmoid(x . w_g) (requires MOE_SHARED) */
+  MOE_OUT_F32 = 16            /* write out as float32 instead of act_fmt */
+};
+
+typedef struct {
+  int32_t hidden;        /* H: multiple of 8 (f32/bf16), 64 (aff4), 32 (mxfp4) */
+  int32_t num_experts;   /* E: 1..256 */
+  int32_t top_k;         /* k: 1..min(E, 16) */
+  int32_t inter;         /* I: routed expert intermediate size, same multiples as H */
+  int32_t shared_inter;  /* Is: shared expert intermediate (multiple of 8), 0 without MOE_SHARED */
+  int32_t max_rows;      /* largest m a forward will be given: 1..32 */
+  int32_t act_fmt;       /* moe_format of x, out, router, shared expert, w_g: MOE_F32 or MOE_BF16 */
+  int32_t expert_fmt;    /* moe_format of the routed experts: any */
+  int32_t routing;       /* moe_routing */
+  uint32_t flags;        /* MOE_NORM_TOPK | MOE_WEIGHT_BEFORE_FFN | MOE_SHARED | ... */
+  float routed_scaling_factor;
+} moe_decode_desc;
+
+/* Device pointers.  The per-expert tables are DEVICE arrays of E uint64
+ * device addresses (one per routed expert); each entry must be non-null and
+ * 16-byte aligned, which the library documents but does not check. */
+typedef struct {
+  const void *router_w;        /* [E, H] act_fmt */
+  const float *expert_bias;    /* [E] float32; MOE_ROUTE_SIGMOID_BIAS only, else NULL */
+  const uint64_t *gate_w;      /* table: [I, H] (packed [I, H/2] for 4-bit) */
+  const uint64_t *up_w;        /* table: [I, H] */
+  const uint64_t *down_w;      /* table: [H, I] (packed [H, I/2]) */
+  const uint64_t *gate_s;      /* table of scales: aff4 bf16 [I, H/64], mxfp4 u8 [I, H/32]; else NULL */
+  const uint64_t *up_s;
+  const uint64_t *down_s;      /* aff4 bf16 [H, I/64], mxfp4 u8 [H, I/32] */
+  const uint64_t *gate_b;      /* table of aff4 biases, bf16 like the scales; else NULL */
+  const uint64_t *up_b;
+  const uint64_t *down_b;
+  const void *sh_gate_w;       /* [Is, H] act_fmt (MOE_SHARED) */
+  const void *sh_up_w;         /* [Is, H] act_fmt */
+  const void *sh_down_w;       /* [H, Is] act_fmt */
+  const void *sh_gate_vec;     /* [H] act_fmt (MOE_SHARED_GATED) */
+} moe_decode_weights;
+
+typedef struct moe_decode_plan moe_decode_plan_t;
+
+/* Byte offsets (from the workspace base) of the arrays a forward leaves in
+ * the workspace, for inspection.  Sizes are for max_rows rows;
+ * te = max_rows * top_k, cap = min(te, E). */
+typedef struct {
+  size_t logits;          /* double [max_rows, E+1]: router logits; column E = x . w_g */
+  size_t topk_idx;        /* int32 [te]: selected experts, row-major [m, k] */
+  size_t topk_w;          /* float [te]: routing weights (before placement) */
+  size_t row_gate;        /* float [max_rows]: shared-expert gate gamma_r */
+  size_t sorted_pair;     /* int32 [te]: pair ids p = r*k + j sorted by expert, stable */
+  size_t expert_offsets;  /* int32 [E+1]: start of each expert's run in sorted_pair */
+  size_t pair_to_perm;    /* int32 [te]: position of pair p in sorted_pair */
+  size_t active_experts;  /* int32 [cap]: experts with at least one pair, ascending */
+  size_t active_count;    /* int32 [1] */
+  size_t act;             /* float [te, I]: routed SwiGLU activations, sorted order */
+  size_t shared_act;      /* float [max_rows, Is] */
+  size_t sync;            /* uint32 [16]: completion counters, zero between calls */
+  size_t total;           /* bytes a workspace must have */
+} moe_decode_ws_layout;
+
+/* Validate a layer description and build a plan.  MOE_EUNSUPPORTED for shapes
+ * or format combinations the kernels do not serve; *workspace_bytes receives
+ * the workspace size (alignment 256 bytes). */
+moe_status moe_decode_plan(const moe_decode_desc *desc, moe_decode_plan_t **plan,
+                           size_t *workspace_bytes);
+
+void moe_decode_plan_destroy(moe_decode_plan_t *plan);
+
+/* Fill *layout for this plan (host only). */
+moe_status moe_decode_workspace_layout(const moe_decode_plan_t *plan,
+                                       moe_decode_ws_layout *layout);
+
+/* Prepare a freshly allocated workspace (zeroes its completion counters with
+ * a kernel on `stream`).  Required once before the first forward on a
+ * workspace; every forward leaves the counters zero again. */
+moe_status moe_decode_workspace_init(const moe_decode_plan_t *plan, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/* The layer on m rows.
+ *   x          device [m, H] act_fmt
+ *   out        device [m, H] act_fmt (float32 with MOE_OUT_F32)
+ *   idx_out    device int32 [m, k] selected experts, or NULL
+ *   w_out      device float [m, k] routing weights, or NULL
+ *   workspace  device, >= the plan's size, 256-byte aligned, initialised once
+ *   stream     hipStream_t (NULL = the null stream)
+ * MOE_EINVAL for m outside 1..max_rows or a missing pointer the flags need,
+ * MOE_EWORKSPACE for a missing/small/misaligned workspace; nothing launches
+ * on error.  Calls that share a workspace must not overlap. */
+moe_status moe_decode_forward(const moe_decode_plan_t *plan, const moe_decode_weights *w,
+                              const void *x, int32_t m, void *out, int32_t *idx_out,
+                              float *w_out, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Number of kernel launches (stages) one forward makes, and the name of
+ * stage i ("route", "gate_up", "down_blend", ...). */
+int32_t moe_decode_num_stages(const moe_decode_plan_t *plan);
+const char *moe_decode_stage_name(const moe_decode_plan_t *plan, int32_t i);
+
+/* As moe_decode_forward, and records events[i] (hipEvent_t) on `stream`
+ * right before stage i is launched and events[num_stages] after the last:
+ * the per-stage timing hook used by the bench.  n_events must equal
+ * moe_decode_num_stages(plan) + 1. */
+moe_status moe_decode_forward_timed(const moe_decode_plan_t *plan, const moe_decode_weights *w,
+                                    const void *x, int32_t m, void *out, int32_t *idx_out,
+                                    float *w_out, void *workspace, size_t workspace_bytes,
+                                    void *stream, void *const *events, int32_t n_events);
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char *moe_decode_last_error(void);
+
+/* Library version string. */
+const char *moe_decode_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_DECODE_H */

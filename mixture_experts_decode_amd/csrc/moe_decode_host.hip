@@ -1,0 +1,363 @@
+// moe_decode_host.hip -- host side of libmoe_decode.so: plan validation,
+// workspace layout, kernel-variant choice and the launch sequence behind the
+// C ABI of include/moe_decode.h.
+//
+// The forward follows the predicate-gated shape of the metrale page
+// "forward_bf16_grouped_decode.rs" (fn forward_bf16_grouped_decode and
+// bf16_grouped_decode_arena_ok): everything the kernels need is checked on
+// the host first and an unsupported call returns an error having launched
+// nothing; grids are sized for the worst case (cap = min(m*k, E) active
+// experts) and the device-side active count trims the work, so the host never
+// waits on the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "moe_decode.h"
+#include "moe_kernels.hpp"
+#include "moe_launch.hpp"
+
+struct moe_decode_plan {
+  moe_decode_desc d;
+  moe_decode_ws_layout L;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool log_enabled() {
+  const char *v = getenv("MOE_DECODE_LOG");
+  return v && v[0] == '1';
+}
+
+int next_pow2(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+const char *const kStageNames[] = {"route", "gate_up", "down_blend"};
+constexpr int kNumStages = 3;
+
+// Input vectors handled per pass over a weight tile: routed rows (pairs of
+// one expert) and shared rows (all m rows).  Restricted to the pairs listed
+// in MOE_PASS_VARIANTS.
+void pass_variant(const moe_decode_desc &d, int m, int *cr, int *cs) {
+  if (m == 1) { *cr = 1; *cs = 1; return; }
+  if (m == 2) { *cr = 2; *cs = 2; return; }
+  if (m <= 4) { *cr = 2; *cs = 4; return; }
+  // Mean pairs per active expert (rounded up) plus one of headroom.
+  const int need = (m * d.top_k + d.num_experts - 1) / d.num_experts + 1;
+  *cs = 8;
+  *cr = need <= 2 ? 2 : need <= 4 ? 4 : 8;
+}
+
+// Lanes per down row: the smallest of 16/32/64 that covers the row's chunks
+// without leaving most lanes idle.
+int down_lanes(int chunks) {
+  if (chunks <= 16) return 16;
+  if (chunks <= 32) return 32;
+  if (chunks < 128 && chunks % 64 != 0 && chunks % 32 == 0) return 32;
+  return 64;
+}
+
+int elems_per_chunk(int fmt) { return fmt == MOE_F32 ? 4 : fmt == MOE_BF16 ? 8 : 32; }
+
+typedef hipError_t (*gate_up_fn)(int, int, const moe::Args &, int, hipStream_t);
+typedef hipError_t (*down_fn)(int, int, int, const moe::Args &, int, hipStream_t);
+
+gate_up_fn gate_up_for(int act, int ef) {
+  static const gate_up_fn t[2][4] = {
+      {moe::launch_gate_up_f32_f32, moe::launch_gate_up_f32_bf16, moe::launch_gate_up_f32_aff4,
+       moe::launch_gate_up_f32_mxfp4},
+      {moe::launch_gate_up_bf16_f32, moe::launch_gate_up_bf16_bf16,
+       moe::launch_gate_up_bf16_aff4, moe::launch_gate_up_bf16_mxfp4}};
+  return t[act][ef];
+}
+
+down_fn down_for(int act, int ef) {
+  static const down_fn t[2][4] = {
+      {moe::launch_down_blend_f32_f32, moe::launch_down_blend_f32_bf16,
+       moe::launch_down_blend_f32_aff4, moe::launch_down_blend_f32_mxfp4},
+      {moe::launch_down_blend_bf16_f32, moe::launch_down_blend_bf16_bf16,
+       moe::launch_down_blend_bf16_aff4, moe::launch_down_blend_bf16_mxfp4}};
+  return t[act][ef];
+}
+
+moe_status check_desc(const moe_decode_desc &d) {
+  if (d.hidden <= 0 || d.num_experts <= 0 || d.top_k <= 0 || d.inter <= 0 || d.max_rows <= 0)
+    return fail(MOE_EINVAL, "hidden, num_experts, top_k, inter and max_rows must be positive");
+  if (d.act_fmt != MOE_F32 && d.act_fmt != MOE_BF16)
+    return fail(MOE_EINVAL, "act_fmt must be MOE_F32 or MOE_BF16 (got %d)", d.act_fmt);
+  if (d.expert_fmt < MOE_F32 || d.expert_fmt > MOE_MXFP4_B32)
+    return fail(MOE_EINVAL, "unknown expert_fmt %d", d.expert_fmt);
+  if (d.routing < MOE_ROUTE_SOFTMAX || d.routing > MOE_ROUTE_SIGMOID_LOGIT)
+    return fail(MOE_EINVAL, "unknown routing %d", d.routing);
+  const uint32_t known = MOE_NORM_TOPK | MOE_WEIGHT_BEFORE_FFN | MOE_SHARED | MOE_SHARED_GATED | MOE_OUT_F32;
+  if (d.flags & ~known) return fail(MOE_EINVAL, "unknown flag bits 0x%x", d.flags & ~known);
+  if ((d.flags & MOE_SHARED_GATED) && !(d.flags & MOE_SHARED))
+    return fail(MOE_EINVAL, "MOE_SHARED_GATED requires MOE_SHARED");
+  if (!std::isfinite(d.routed_scaling_factor))
+    return fail(MOE_EINVAL, "routed_scaling_factor must be finite");
+  if (d.num_experts > moe::MAX_EXPERTS)
+    return fail(MOE_EUNSUPPORTED, "num_experts %d > %d", d.num_experts, moe::MAX_EXPERTS);
+  if (d.top_k > d.num_experts || d.top_k > moe::MAX_TOPK)
+    return fail(MOE_EUNSUPPORTED, "top_k %d must be <= min(num_experts, %d)", d.top_k, moe::MAX_TOPK);
+  if (d.max_rows > moe::MAX_ROWS)
+    return fail(MOE_EUNSUPPORTED, "max_rows %d > %d", d.max_rows, moe::MAX_ROWS);
+  if (d.hidden % 8 || d.inter % 8)
+    return fail(MOE_EUNSUPPORTED, "hidden and inter must be multiples of 8");
+  if (d.expert_fmt == MOE_AFF4_G64 && (d.hidden % 64 || d.inter % 64))
+    return fail(MOE_EUNSUPPORTED, "aff4-g64 experts need hidden and inter multiples of 64");
+  if (d.expert_fmt == MOE_MXFP4_B32 && (d.hidden % 32 || d.inter % 32))
+    return fail(MOE_EUNSUPPORTED, "mxfp4 experts need hidden and inter multiples of 32");
+  if (d.flags & MOE_SHARED) {
+    if (d.shared_inter <= 0 || d.shared_inter % 8)
+      return fail(MOE_EUNSUPPORTED, "shared_inter must be a positive multiple of 8");
+  }
+  return MOE_OK;
+}
+
+void layout_for(const moe_decode_desc &d, moe_decode_ws_layout *L) {
+  const size_t A = 256;
+  const size_t R = (size_t)d.max_rows, E = (size_t)d.num_experts;
+  const size_t te = R * (size_t)d.top_k;
+  const size_t cap = te < E ? te : E;
+  const size_t Is = (d.flags & MOE_SHARED) ? (size_t)d.shared_inter : 0;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + (bytes ? bytes : 4), A);
+    return at;
+  };
+  L->sync = take(16 * sizeof(uint32_t));
+  L->logits = take(R * (E + 1) * sizeof(double));
+  L->topk_idx = take(te * 4);
+  L->topk_w = take(te * 4);
+  L->row_gate = take(R * 4);
+  L->sorted_pair = take(te * 4);
+  L->expert_offsets = take((E + 1) * 4);
+  L->pair_to_perm = take(te * 4);
+  L->active_experts = take(cap * 4);
+  L->active_count = take(4);
+  L->act = take(te * (size_t)d.inter * 4);
+  L->shared_act = take(R * Is * 4);
+  L->total = o;
+}
+
+moe_status check_weights(const moe_decode_desc &d, const moe_decode_weights *w) {
+  if (!w) return fail(MOE_EINVAL, "weights is NULL");
+  if (!w->router_w || !aligned(w->router_w, 16))
+    return fail(MOE_EINVAL, "router_w must be a non-null 16-byte aligned device pointer");
+  if (!w->gate_w || !w->up_w || !w->down_w)
+    return fail(MOE_EINVAL, "gate_w, up_w and down_w tables are required");
+  if (d.expert_fmt == MOE_AFF4_G64 || d.expert_fmt == MOE_MXFP4_B32) {
+    if (!w->gate_s || !w->up_s || !w->down_s)
+      return fail(MOE_EINVAL, "4-bit experts need gate_s, up_s and down_s tables");
+  }
+  if (d.expert_fmt == MOE_AFF4_G64 && (!w->gate_b || !w->up_b || !w->down_b))
+    return fail(MOE_EINVAL, "aff4 experts need gate_b, up_b and down_b tables");
+  if (d.routing == MOE_ROUTE_SIGMOID_BIAS && !w->expert_bias)
+    return fail(MOE_EINVAL, "sigmoid+bias routing needs expert_bias");
+  if (d.flags & MOE_SHARED) {
+    if (!w->sh_gate_w || !w->sh_up_w || !w->sh_down_w || !aligned(w->sh_gate_w, 16) ||
+        !aligned(w->sh_up_w, 16) || !aligned(w->sh_down_w, 16))
+      return fail(MOE_EINVAL, "MOE_SHARED needs 16-byte aligned sh_gate_w, sh_up_w, sh_down_w");
+  }
+  if ((d.flags & MOE_SHARED_GATED) && (!w->sh_gate_vec || !aligned(w->sh_gate_vec, 16)))
+    return fail(MOE_EINVAL, "MOE_SHARED_GATED needs a 16-byte aligned sh_gate_vec");
+  return MOE_OK;
+}
+
+moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights *w, const void *x,
+                        int32_t m, void *out, int32_t *idx_out, float *w_out, void *workspace,
+                        size_t workspace_bytes, void *stream, void *const *events, int32_t n_events) {
+  if (!plan) return fail(MOE_EINVAL, "plan is NULL");
+  const moe_decode_desc &d = plan->d;
+  const moe_decode_ws_layout &L = plan->L;
+  if (m < 1 || m > d.max_rows) return fail(MOE_EINVAL, "m = %d outside 1..max_rows (%d)", m, d.max_rows);
+  if (!x || !aligned(x, 16)) return fail(MOE_EINVAL, "x must be a non-null 16-byte aligned device pointer");
+  if (!out || !aligned(out, 16)) return fail(MOE_EINVAL, "out must be a non-null 16-byte aligned device pointer");
+  if (!workspace) return fail(MOE_EWORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(MOE_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(MOE_EWORKSPACE, "workspace has %zu bytes, the plan needs %zu", workspace_bytes, L.total);
+  if (events && n_events != kNumStages + 1)
+    return fail(MOE_EINVAL, "n_events must be %d", kNumStages + 1);
+  moe_status st = check_weights(d, w);
+  if (st != MOE_OK) return st;
+
+  char *ws = static_cast<char *>(workspace);
+  moe::Args a;
+  memset(&a, 0, sizeof a);
+  a.H = d.hidden;
+  a.E = d.num_experts;
+  a.K = d.top_k;
+  a.I = d.inter;
+  a.Is = (d.flags & MOE_SHARED) ? d.shared_inter : 0;
+  a.m = m;
+  a.te = m * d.top_k;
+  a.cap = a.te < d.num_experts ? a.te : d.num_experts;
+  a.act_fmt = d.act_fmt;
+  a.expert_fmt = d.expert_fmt;
+  a.routing = d.routing;
+  a.flags = d.flags;
+  a.rsf = d.routed_scaling_factor;
+  a.x = x;
+  a.out = out;
+  a.idx_out = idx_out;
+  a.w_out = w_out;
+  a.router = w->router_w;
+  a.ebias = w->expert_bias;
+  a.gw = w->gate_w; a.uw = w->up_w; a.dw = w->down_w;
+  a.gs = w->gate_s; a.us = w->up_s; a.ds = w->down_s;
+  a.gb = w->gate_b; a.ub = w->up_b; a.db = w->down_b;
+  a.sgw = w->sh_gate_w; a.suw = w->sh_up_w; a.sdw = w->sh_down_w; a.sgv = w->sh_gate_vec;
+  a.logits = reinterpret_cast<double *>(ws + L.logits);
+  a.topk_idx = reinterpret_cast<int32_t *>(ws + L.topk_idx);
+  a.topk_w = reinterpret_cast<float *>(ws + L.topk_w);
+  a.row_gate = reinterpret_cast<float *>(ws + L.row_gate);
+  a.sorted_pair = reinterpret_cast<int32_t *>(ws + L.sorted_pair);
+  a.offsets = reinterpret_cast<int32_t *>(ws + L.expert_offsets);
+  a.pair_to_perm = reinterpret_cast<int32_t *>(ws + L.pair_to_perm);
+  a.active = reinterpret_cast<int32_t *>(ws + L.active_experts);
+  a.active_count = reinterpret_cast<int32_t *>(ws + L.active_count);
+  a.act = reinterpret_cast<float *>(ws + L.act);
+  a.sact = reinterpret_cast<float *>(ws + L.shared_act);
+  a.sync = reinterpret_cast<unsigned *>(ws + L.sync);
+
+  int cr, cs;
+  pass_variant(d, m, &cr, &cs);
+  const int lpr = down_lanes(d.inter / elems_per_chunk(d.expert_fmt));
+  const int route_rows = d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0);
+  const int route_blocks = (route_rows + moe::ROUTE_THREADS / moe::WAVE - 1) / (moe::ROUTE_THREADS / moe::WAVE);
+  const int ni = moe::GATE_UP_ROWS / 2;
+  const long gu_waves = (long)a.cap * ((d.inter + ni - 1) / ni) + ((d.flags & MOE_SHARED) ? (a.Is + ni - 1) / ni : 0);
+  const int wpb = moe::GEMV_THREADS / moe::WAVE;
+  const int gu_blocks = (int)((gu_waves + wpb - 1) / wpb);
+  const int db_blocks = (d.hidden + moe::DOWN_TILE - 1) / moe::DOWN_TILE;
+
+  static thread_local bool logged = false;
+  if (!logged && log_enabled()) {
+    logged = true;
+    fprintf(stderr,
+            "[moe_decode] first forward: m=%d H=%d E=%d k=%d I=%d Is=%d act=%d expert=%d routing=%d "
+            "flags=0x%x | route %d blocks, gate_up %d blocks (CR=%d CS=%d), down_blend %d blocks "
+            "(LPR=%d)\n",
+            m, d.hidden, d.num_experts, d.top_k, d.inter, a.Is, d.act_fmt, d.expert_fmt, d.routing,
+            d.flags, route_blocks, gu_blocks, cr, cs, db_blocks, lpr);
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto rec = [&](int i) -> hipError_t {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
+  };
+  hipError_t e;
+  if ((e = rec(0)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
+  if ((e = moe::launch_route(d.act_fmt, a, route_blocks, s)) != hipSuccess)
+    return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
+  if ((e = rec(1)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
+  if ((e = gate_up_for(d.act_fmt, d.expert_fmt)(cr, cs, a, gu_blocks, s)) != hipSuccess)
+    return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
+  if ((e = rec(2)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
+  if ((e = down_for(d.act_fmt, d.expert_fmt)(cr, cs, lpr, a, db_blocks, s)) != hipSuccess)
+    return fail(MOE_EHIP, "down_blend launch: %s", hipGetErrorString(e));
+  if ((e = rec(3)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_decode_plan(const moe_decode_desc *desc, moe_decode_plan_t **plan,
+                           size_t *workspace_bytes) {
+  if (!desc || !plan || !workspace_bytes) return fail(MOE_EINVAL, "desc, plan and workspace_bytes are required");
+  *plan = nullptr;
+  moe_status st = check_desc(*desc);
+  if (st != MOE_OK) return st;
+  moe_decode_plan_t *p = new (std::nothrow) moe_decode_plan_t;
+  if (!p) return fail(MOE_EINVAL, "out of host memory");
+  p->d = *desc;
+  if (!(p->d.flags & MOE_SHARED)) p->d.shared_inter = 0;
+  layout_for(p->d, &p->L);
+  *plan = p;
+  *workspace_bytes = p->L.total;
+  return ok();
+}
+
+void moe_decode_plan_destroy(moe_decode_plan_t *plan) { delete plan; }
+
+moe_status moe_decode_workspace_layout(const moe_decode_plan_t *plan, moe_decode_ws_layout *layout) {
+  if (!plan || !layout) return fail(MOE_EINVAL, "plan and layout are required");
+  *layout = plan->L;
+  return ok();
+}
+
+moe_status moe_decode_workspace_init(const moe_decode_plan_t *plan, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  if (!plan) return fail(MOE_EINVAL, "plan is NULL");
+  if (!workspace || !aligned(workspace, 256)) return fail(MOE_EWORKSPACE, "workspace must be non-null and 256-byte aligned");
+  if (workspace_bytes < plan->L.total)
+    return fail(MOE_EWORKSPACE, "workspace has %zu bytes, the plan needs %zu", workspace_bytes, plan->L.total);
+  hipError_t e = moe::launch_clear_sync(reinterpret_cast<unsigned *>(static_cast<char *>(workspace) + plan->L.sync), 16,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_EHIP, "workspace init launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+moe_status moe_decode_forward(const moe_decode_plan_t *plan, const moe_decode_weights *w, const void *x,
+                              int32_t m, void *out, int32_t *idx_out, float *w_out, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  return forward_impl(plan, w, x, m, out, idx_out, w_out, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+moe_status moe_decode_forward_timed(const moe_decode_plan_t *plan, const moe_decode_weights *w,
+                                    const void *x, int32_t m, void *out, int32_t *idx_out, float *w_out,
+                                    void *workspace, size_t workspace_bytes, void *stream,
+                                    void *const *events, int32_t n_events) {
+  if (!events) return fail(MOE_EINVAL, "events is NULL");
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return fail(MOE_EINVAL, "events[%d] is NULL", i);
+  return forward_impl(plan, w, x, m, out, idx_out, w_out, workspace, workspace_bytes, stream, events,
+                      n_events);
+}
+
+int32_t moe_decode_num_stages(const moe_decode_plan_t *plan) { return plan ? kNumStages : 0; }
+
+const char *moe_decode_stage_name(const moe_decode_plan_t *plan, int32_t i) {
+  if (!plan || i < 0 || i >= kNumStages) return "";
+  return kStageNames[i];
+}
+
+const char *moe_decode_last_error(void) { return g_err.c_str(); }
+
+const char *moe_decode_version(void) { return "moe_decode 0.1 (gfx950)"; }
+
+}  // extern "C"

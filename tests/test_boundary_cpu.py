@@ -1,0 +1,162 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+entry point the header declares, validates descriptions, lays out the
+workspace, and rejects bad forward calls before anything is launched."""
+import ctypes as C
+import subprocess
+
+import pytest
+
+from mixture_experts_decode_amd import moe_decode as md
+from mixture_experts_decode_amd import synth
+from mixture_experts_decode_amd.device import desc_of
+
+
+def test_library_exports_every_declared_entry_point():
+    names = md.header_entry_points()
+    assert len(names) >= 10
+    lib = md.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    syms = subprocess.run(["nm", "-D", "--defined-only", md.LIB_PATH], capture_output=True,
+                          text=True, check=True).stdout
+    exported = {line.split()[-1] for line in syms.splitlines() if " T " in line}
+    assert set(names) <= exported
+    assert "gfx950" in md.moe_decode_version()
+
+
+def _desc(**kw):
+    spec = synth.WORKLOADS["qwen3_30b_a3b_bf16"]
+    d = desc_of(spec)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("hidden", 0, md.MOE_EINVAL),
+    ("hidden", 2044, md.MOE_EUNSUPPORTED),
+    ("num_experts", 257, md.MOE_EUNSUPPORTED),
+    ("top_k", 17, md.MOE_EUNSUPPORTED),
+    ("top_k", 0, md.MOE_EINVAL),
+    ("max_rows", 33, md.MOE_EUNSUPPORTED),
+    ("max_rows", 0, md.MOE_EINVAL),
+    ("act_fmt", md.MOE_AFF4_G64, md.MOE_EINVAL),
+    ("expert_fmt", 7, md.MOE_EINVAL),
+    ("routing", 3, md.MOE_EINVAL),
+    ("flags", 1 << 10, md.MOE_EINVAL),
+    ("flags", md.MOE_SHARED_GATED, md.MOE_EINVAL),
+    ("inter", 100, md.MOE_EUNSUPPORTED),
+])
+def test_plan_rejects(field, value, status):
+    with pytest.raises(md.MoeDecodeError) as ei:
+        md.moe_decode_plan(_desc(**{field: value}))
+    assert ei.value.status == status
+    assert md.moe_decode_last_error()
+
+
+def test_plan_rejects_4bit_shapes():
+    with pytest.raises(md.MoeDecodeError) as ei:
+        md.moe_decode_plan(_desc(expert_fmt=md.MOE_AFF4_G64, inter=96))
+    assert ei.value.status == md.MOE_EUNSUPPORTED
+    with pytest.raises(md.MoeDecodeError) as ei:
+        md.moe_decode_plan(_desc(expert_fmt=md.MOE_MXFP4_B32, hidden=2048 + 16))
+    assert ei.value.status == md.MOE_EUNSUPPORTED
+    with pytest.raises(md.MoeDecodeError) as ei:
+        md.moe_decode_plan(_desc(flags=md.MOE_SHARED, shared_inter=0))
+    assert ei.value.status == md.MOE_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_plan_and_layout_for_every_workload(name):
+    spec = synth.WORKLOADS[name]
+    plan, ws = md.moe_decode_plan(desc_of(spec))
+    try:
+        L = md.moe_decode_workspace_layout(plan)
+        assert L.total == ws
+        te = spec.max_rows * spec.top_k
+        fields = [(L.sync, 64), (L.logits, spec.max_rows * (spec.num_experts + 1) * 8),
+                  (L.topk_idx, te * 4), (L.topk_w, te * 4), (L.row_gate, spec.max_rows * 4),
+                  (L.sorted_pair, te * 4), (L.expert_offsets, (spec.num_experts + 1) * 4),
+                  (L.pair_to_perm, te * 4), (L.active_experts, min(te, spec.num_experts) * 4),
+                  (L.active_count, 4), (L.act, te * spec.inter * 4),
+                  (L.shared_act, spec.max_rows * (spec.shared_inter if spec.shared else 0) * 4)]
+        spans = sorted((o, o + max(n, 1)) for o, n in fields)
+        for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+            assert a1 <= b0, "workspace arrays overlap"
+        assert all(o % 256 == 0 for o, _ in fields)
+        assert spans[-1][1] <= ws
+        assert md.moe_decode_num_stages(plan) == 3
+        assert [md.moe_decode_stage_name(plan, i) for i in range(3)] == \
+            ["route", "gate_up", "down_blend"]
+        assert md.moe_decode_stage_name(plan, 3) == ""
+    finally:
+        md.moe_decode_plan_destroy(plan)
+
+
+def _weights_stub():
+    # Host addresses only: the calls below must fail validation before any
+    # use of them.
+    w = md.moe_decode_weights()
+    for f, _ in md.moe_decode_weights._fields_:
+        setattr(w, f, 4096)
+    return w
+
+
+@pytest.mark.parametrize("m", [0, -1, 9])
+def test_forward_rejects_m_out_of_range(m):
+    plan, ws = md.moe_decode_plan(desc_of(synth.WORKLOADS["qwen3_30b_a3b_bf16"]))
+    try:
+        with pytest.raises(md.MoeDecodeError) as ei:
+            md.moe_decode_forward(plan, _weights_stub(), 4096, m, 4096, None, None, 4096 * 256,
+                                  ws, 0)
+        assert ei.value.status == md.MOE_EINVAL
+    finally:
+        md.moe_decode_plan_destroy(plan)
+
+
+def test_forward_rejects_bad_pointers_and_workspace():
+    plan, ws = md.moe_decode_plan(desc_of(synth.WORKLOADS["qwen35_35b_a3b_mxfp4"]))
+    try:
+        def call(**kw):
+            a = dict(w=_weights_stub(), x=4096, m=1, out=4096, ws=4096 * 256, ws_bytes=ws)
+            a.update(kw)
+            with pytest.raises(md.MoeDecodeError) as ei:
+                md.moe_decode_forward(plan, a["w"], a["x"], a["m"], a["out"], None, None, a["ws"],
+                                      a["ws_bytes"], 0)
+            return ei.value.status
+        assert call(x=None) == md.MOE_EINVAL
+        assert call(x=4097) == md.MOE_EINVAL          # misaligned
+        assert call(out=None) == md.MOE_EINVAL
+        assert call(ws=None) == md.MOE_EWORKSPACE
+        assert call(ws=4096 * 256 + 16) == md.MOE_EWORKSPACE
+        assert call(ws_bytes=ws - 1) == md.MOE_EWORKSPACE
+        for field in ("router_w", "gate_w", "down_s", "sh_up_w", "sh_gate_vec"):
+            w = _weights_stub()
+            setattr(w, field, None)
+            assert call(w=w) == md.MOE_EINVAL, field
+        lib = md.lib()
+        assert lib.moe_decode_forward(plan, None, 4096, 1, 4096, None, None, 4096 * 256, ws,
+                                      None) == md.MOE_EINVAL
+        assert lib.moe_decode_forward(None, C.byref(_weights_stub()), 4096, 1, 4096, None, None,
+                                      4096 * 256, ws, None) == md.MOE_EINVAL
+        ev = (C.c_void_p * 2)(4096, 4096)
+        assert lib.moe_decode_forward_timed(plan, C.byref(_weights_stub()), 4096, 1, 4096, None,
+                                            None, 4096 * 256, ws, None, ev, 2) == md.MOE_EINVAL
+    finally:
+        md.moe_decode_plan_destroy(plan)
+
+
+def test_sigmoid_bias_needs_expert_bias():
+    plan, ws = md.moe_decode_plan(desc_of(synth.WORKLOADS["lfm2_8b_a1b_aff4"]))
+    try:
+        w = _weights_stub()
+        w.expert_bias = None
+        with pytest.raises(md.MoeDecodeError) as ei:
+            md.moe_decode_forward(plan, w, 4096, 1, 4096, None, None, 4096 * 256, ws, 0)
+        assert ei.value.status == md.MOE_EINVAL
+        w = _weights_stub()
+        w.up_b = None
+        with pytest.raises(md.MoeDecodeError):
+            md.moe_decode_forward(plan, w, 4096, 1, 4096, None, None, 4096 * 256, ws, 0)
+    finally:
+        md.moe_decode_plan_destroy(plan)

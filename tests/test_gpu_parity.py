@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Expert indices must equal the oracle's bit for bit (slot order included),
+routing weights agree to 1e-6 relative, and outputs satisfy
+max|gpu - oracle| <= tol * rms(oracle) with tol = 2e-2 for bf16 activations
+and 1e-5 for the fp32 path.  Sizes: every workload at every row count it
+lists, plus small ragged layers over every format / routing / placement /
+shared-expert variant and every kernel variant the host can pick.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_decode_amd import moe_decode as md
+from mixture_experts_decode_amd import synth
+from mixture_experts_decode_amd.device import DeviceLayer, out_to_numpy, to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+# With MOE_OUT_F32 the bf16-activation path is only limited by fp32
+# accumulation (inputs and dequantised weights are exact): a tighter bound.
+TOL_OUT_F32 = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+def run(dl: DeviceLayer, x_np: np.ndarray, m: int):
+    spec = dl.spec
+    x = to_device(np.ascontiguousarray(x_np[:m]), "cuda")
+    out = dl.new_out(m)
+    idx = torch.full((m, spec.top_k), -1, dtype=torch.int32, device="cuda")
+    w = torch.full((m, spec.top_k), float("nan"), dtype=torch.float32, device="cuda")
+    dl.forward(x, m, out, idx, w)
+    torch.cuda.synchronize()
+    return out_to_numpy(spec, out), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def check(spec, got, idx, w, ref, m, tol, what=""):
+    assert np.array_equal(idx, ref.idx[:m]), f"{what}: expert indices differ\n{idx}\n{ref.idx[:m]}"
+    werr = np.abs(w.astype(np.float64) - ref.w[:m])
+    assert np.all(werr <= 1e-6 * np.abs(ref.w[:m]) + 1e-12), f"{what}: weights {werr.max()}"
+    r = ref.out[:m]
+    err = float(np.max(np.abs(got - r)))
+    bound = tol * rms(r)
+    assert err <= bound, f"{what}: max|diff| {err:.3e} > {bound:.3e} (rms {rms(r):.3e})"
+    return err / max(rms(r), 1e-300)
+
+
+def check_sort(dl, m, idx):
+    spec = dl.spec
+    te = m * spec.top_k
+    want = oracle.sort_pairs(idx, spec.num_experts)
+    sp = dl.ws_view("sorted_pair", torch.int32, te).cpu().numpy()
+    off = dl.ws_view("expert_offsets", torch.int32, spec.num_experts + 1).cpu().numpy()
+    p2p = dl.ws_view("pair_to_perm", torch.int32, te).cpu().numpy()
+    cnt = int(dl.ws_view("active_count", torch.int32, 1).cpu().numpy()[0])
+    act = dl.ws_view("active_experts", torch.int32, max(cnt, 1)).cpu().numpy()[:cnt]
+    assert np.array_equal(sp, want["sorted_pair"])
+    assert np.array_equal(off, want["expert_offsets"])
+    assert np.array_equal(p2p, want["pair_to_perm"])
+    assert cnt == want["active_count"] and np.array_equal(act, want["active_experts"])
+
+
+# --------------------------------------------------------------- workloads
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_parity_all_rows(name):
+    spec = synth.WORKLOADS[name]
+    say(f"[gpu] workload {name}: generating")
+    layer = synth.make_layer(spec, seed=0)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)       # rows are independent: one call serves every m
+    say(f"[gpu] workload {name}: oracle done, min margin {ref.margin.min():.3e}")
+    dl = DeviceLayer(layer)
+    outs = {}
+    for m in spec.rows:
+        say(f"[gpu] workload {name} m={m}: forward")
+        got, idx, w = run(dl, x, m)
+        rel = check(spec, got, idx, w, ref, m, TOL[spec.act_fmt], f"{name} m={m}")
+        check_sort(dl, m, idx)
+        outs[m] = got
+        say(f"[gpu] workload {name} m={m}: ok, max|diff|/rms = {rel:.2e}")
+    # A row's result does not depend on m (bitwise, same kernels).
+    mmax = max(spec.rows)
+    for m in spec.rows:
+        assert np.array_equal(outs[m], outs[mmax][:m]), f"{name}: rows differ between m={m} and m={mmax}"
+    # Deterministic across calls.
+    again, _, _ = run(dl, x, mmax)
+    assert np.array_equal(again, outs[mmax])
+    del dl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b_bf16", "qwen35_35b_a3b_mxfp4", "lfm2_8b_a1b_aff4",
+                                  "llama4_wbf_bf16"])
+def test_workload_fp32_output_tight(name):
+    spec = synth.WORKLOADS[name]
+    layer = synth.make_layer(spec, seed=1)
+    x = layer.x(3)
+    m = min(8, spec.max_rows)
+    ref = oracle.forward(layer, x[:m])
+    say(f"[gpu] workload {name} (f32 out) m={m}: forward")
+    dl = DeviceLayer(layer, out_f32=True)
+    got, idx, w = run(dl, x, m)
+    rel = check(spec, got, idx, w, ref, m, TOL_OUT_F32, f"{name} f32-out")
+    say(f"[gpu] workload {name} f32-out: max|diff|/rms = {rel:.2e}")
+    del dl
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------ small ragged layers
+
+def small(**kw):
+    base = dict(name="small", hidden=320, num_experts=12, top_k=3, inter=192, shared_inter=136,
+                act_fmt="bf16", expert_fmt="bf16", routing="softmax", norm_topk=True,
+                w_std=0.05, rows=(8,))
+    base.update(kw)
+    return synth.LayerSpec(**base)
+
+
+# Every (activation, expert format, routing, placement) combination once; the
+# shared-expert variant (none / ungated / gated) rotates through them.
+_BASE = [(act, fmt, routing, before)
+         for act in ("f32", "bf16") for fmt in ("f32", "bf16", "aff4", "mxfp4")
+         for routing in ("softmax", "sigmoid_bias", "sigmoid_logit") for before in (False, True)]
+VARIANTS = [b + (("none", "plain", "gated")[i % 3],) for i, b in enumerate(_BASE)]
+
+
+@pytest.mark.parametrize("act,fmt,routing,before,shared", VARIANTS)
+def test_small_variant(act, fmt, routing, before, shared):
+    spec = small(act_fmt=act, expert_fmt=fmt, routing=routing, weight_before_ffn=before,
+                 norm_topk=routing != "sigmoid_logit", routed_scaling_factor=1.25,
+                 shared=shared != "none", shared_gated=shared == "gated")
+    seed = VARIANTS.index((act, fmt, routing, before, shared)) + 100
+    layer = synth.make_layer(spec, seed=seed, threads=4)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    what = f"{act}/{fmt}/{routing}/before={before}/shared={shared}"
+    say(f"[gpu] small {what}")
+    for out_f32 in (False, True):
+        dl = DeviceLayer(layer, out_f32=out_f32)
+        for m in (1, 5, 8):
+            got, idx, w = run(dl, x, m)
+            tol = TOL[act] if not out_f32 else (TOL_OUT_F32 if act == "bf16" else TOL["f32"])
+            check(spec, got, idx, w, ref, m, tol, f"{what} m={m} f32out={out_f32}")
+            check_sort(dl, m, idx)
+
+
+def test_every_row_count_and_pass_variant():
+    spec = small(hidden=256, num_experts=16, top_k=4, inter=128, shared=True, shared_gated=True,
+                 shared_inter=96, rows=(32,))
+    layer = synth.make_layer(spec, seed=7)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    dl = DeviceLayer(layer)
+    full = None
+    for m in range(32, 0, -1):
+        say(f"[gpu] m sweep m={m}")
+        got, idx, w = run(dl, x, m)
+        check(spec, got, idx, w, ref, m, TOL["bf16"], f"m={m}")
+        check_sort(dl, m, idx)
+        if full is None:
+            full = got
+        assert np.array_equal(got, full[:m])
+
+
+@pytest.mark.parametrize("fmt,inter", [("bf16", 64), ("bf16", 256), ("bf16", 768), ("bf16", 1024),
+                                       ("mxfp4", 512), ("mxfp4", 1024), ("aff4", 1792),
+                                       ("aff4", 128), ("f32", 32)])
+def test_down_lane_grouping(fmt, inter):
+    spec = small(expert_fmt=fmt, inter=inter, hidden=512, num_experts=8, top_k=2,
+                 act_fmt="f32" if fmt == "f32" else "bf16")
+    layer = synth.make_layer(spec, seed=inter)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    dl = DeviceLayer(layer)
+    for m in (1, 8):
+        say(f"[gpu] lanes {fmt} I={inter} m={m}")
+        got, idx, w = run(dl, x, m)
+        check(spec, got, idx, w, ref, m, TOL[spec.act_fmt], f"{fmt} I={inter} m={m}")
+
+
+def test_largest_pair_count_and_dense_limit():
+    # E = 256, k = 16, m = 32: te = 512 pairs, the most the sort handles.
+    spec = small(hidden=128, num_experts=256, top_k=16, inter=64, rows=(32,), w_std=0.1)
+    layer = synth.make_layer(spec, seed=11)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    dl = DeviceLayer(layer)
+    got, idx, w = run(dl, x, 32)
+    check(spec, got, idx, w, ref, 32, TOL["bf16"], "te=512")
+    check_sort(dl, 32, idx)
+    # k = E: every expert active, weights are the full softmax.
+    spec2 = small(hidden=128, num_experts=8, top_k=8, inter=64, rows=(4,))
+    layer2 = synth.make_layer(spec2, seed=12)
+    x2 = layer2.x(0)
+    ref2 = oracle.forward(layer2, x2)
+    dl2 = DeviceLayer(layer2)
+    got, idx, w = run(dl2, x2, 4)
+    check(spec2, got, idx, w, ref2, 4, TOL["bf16"], "k=E")
+
+
+def test_zero_input_and_ties():
+    spec = small(num_experts=8, top_k=3, routing="softmax")
+    layer = synth.make_layer(spec, seed=13)
+    x = np.zeros((2, spec.hidden), np.uint16)
+    dl = DeviceLayer(layer)
+    got, idx, w = run(dl, x, 2)
+    assert np.array_equal(idx, np.tile(np.arange(3, dtype=np.int32), (2, 1)))
+    assert np.all(w == np.float32(1.0 / 3.0)) and np.all(got == 0.0)
+    # Duplicate router rows: the lower index ranks first.
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    win = int(ref.idx[0, 0])
+    if win != 0:
+        layer.router[0] = layer.router[win]
+        ref = oracle.forward(layer, x)
+        dl = DeviceLayer(layer)
+        got, idx, w = run(dl, x, 1)
+        assert list(idx[0][:2]) == [0, win]
+        check(spec, got, idx, w, ref, 1, TOL["bf16"], "tie")
+
+
+def test_errors_launch_nothing():
+    spec = small()
+    layer = synth.make_layer(spec, seed=14)
+    dl = DeviceLayer(layer)
+    x = to_device(layer.x(0), "cuda")
+    out = torch.full((8, spec.hidden), 12345, dtype=torch.int16, device="cuda")
+    before = out.clone()
+    for m in (0, 9):
+        with pytest.raises(md.MoeDecodeError) as ei:
+            dl.forward(x, m, out)
+        assert ei.value.status == md.MOE_EINVAL
+    with pytest.raises(md.MoeDecodeError) as ei:
+        md.moe_decode_forward(dl.plan, dl.weights, x.data_ptr(), 1, out.data_ptr(), None, None,
+                              dl.workspace.data_ptr(), dl.ws_bytes - 256, 0)
+    assert ei.value.status == md.MOE_EWORKSPACE
+    torch.cuda.synchronize()
+    assert torch.equal(out, before)
+
+
+def test_graph_replay_matches_eager():
+    spec = synth.WORKLOADS["qwen35_35b_a3b_mxfp4"]
+    layer = synth.make_layer(spec, seed=2)
+    dl = DeviceLayer(layer)
+    x = to_device(layer.x(0), "cuda")
+    m = 8
+    eager = dl.new_out(m)
+    dl.forward(x, m, eager)
+    torch.cuda.synchronize()
+    out = dl.new_out(m)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            dl.forward(x, m, out, stream=s.cuda_stream)
+    for i in range(4):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        dl.forward(x, m, dl.new_out(m))      # eager work between replays
+        torch.cuda.synchronize()
