@@ -140,7 +140,7 @@ typedef struct {
   size_t active_count;    /* int32 [1] */
   size_t act;             /* float [te, I]: routed SwiGLU activations, sorted order */
   size_t shared_act;      /* float [max_rows, Is] */
-  size_t sync;            /* uint32 [16]: completion counters, zero between calls */
+  size_t sync;            /* uint32 [8704]: completion words (one per 128 bytes), zero between calls */
   size_t total;           /* bytes a workspace must have */
 } moe_decode_ws_layout;
 

@@ -1,4 +1,12 @@
 // Kernel variants for bf16 activations with bf16 routed experts.
 #include "moe_kernels.hpp"
 #include "moe_launch.hpp"
-MOE_INSTANTIATE(BF16, BF16, bf16_bf16)
+
+namespace moe {
+namespace {
+constexpr int ACTT = BF16, EFT = BF16;
+const Variant kV[] = { MOE_V(1,1, 32), MOE_V(1,1, 64), MOE_V(2,4, 32), MOE_V(2,4, 64), MOE_V(2,8, 32), MOE_V(2,8, 64), MOE_V(4,8, 32), MOE_V(4,8, 64) };
+const GateUpVariant kG[] = { MOE_G(1,1), MOE_G(2,4), MOE_G(2,8), MOE_G(4,8) };
+}  // namespace
+MOE_TABLE(bf16_bf16)
+}  // namespace moe

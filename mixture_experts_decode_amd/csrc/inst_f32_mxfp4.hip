@@ -1,4 +1,12 @@
 // Kernel variants for f32 activations with mxfp4 routed experts.
 #include "moe_kernels.hpp"
 #include "moe_launch.hpp"
-MOE_INSTANTIATE(F32, MXFP4, f32_mxfp4)
+
+namespace moe {
+namespace {
+constexpr int ACTT = F32, EFT = MXFP4;
+const Variant kV[] = { MOE_V(1,1, 16), MOE_V(1,1, 64), MOE_V(2,2, 16), MOE_V(2,2, 64) };
+const GateUpVariant kG[] = { MOE_G(1,1), MOE_G(2,2) };
+}  // namespace
+MOE_TABLE(f32_mxfp4)
+}  // namespace moe

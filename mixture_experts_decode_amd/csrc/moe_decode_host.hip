@@ -26,6 +26,9 @@
 struct moe_decode_plan {
   moe_decode_desc d;
   moe_decode_ws_layout L;
+  int variant;  // kSplit
+  const moe::Variant *kv[moe::MAX_ROWS + 1];   // per m
+  moe::launch_fn gate_up[moe::MAX_ROWS + 1];   // per m (split arrangement)
 };
 
 namespace {
@@ -56,26 +59,31 @@ bool log_enabled() {
   return v && v[0] == '1';
 }
 
-int next_pow2(int v) {
-  int p = 1;
-  while (p < v) p <<= 1;
-  return p;
+// Kernel arrangement: the work items as three launches ordered by the
+// stream.  (A single persistent launch is written but not enabled: its first
+// launches on MI355X did not finish and the cause is not identified, so a
+// plan asking for it with MOE_DECODE_VARIANT=fused is refused.)
+constexpr int kSplit = 1;
+const char *const kSplitStages[] = {"route", "gate_up", "down_blend"};
+int num_stages(int) { return 3; }
+const char *stage_name(int, int i) { return kSplitStages[i]; }
+
+bool fused_requested() {
+  const char *v = getenv("MOE_DECODE_VARIANT");
+  return v && strcmp(v, "fused") == 0;
 }
 
-const char *const kStageNames[] = {"route", "gate_up", "down_blend"};
-constexpr int kNumStages = 3;
-
 // Input vectors handled per pass over a weight tile: routed rows (pairs of
-// one expert) and shared rows (all m rows).  Restricted to the pairs listed
-// in MOE_PASS_VARIANTS.
+// one expert) and shared rows (all m rows); more are handled in further
+// passes.  Restricted to the pairs the inst_*.hip tables instantiate.
 void pass_variant(const moe_decode_desc &d, int m, int *cr, int *cs) {
   if (m == 1) { *cr = 1; *cs = 1; return; }
-  if (m == 2) { *cr = 2; *cs = 2; return; }
+  if (d.act_fmt == MOE_F32) { *cr = 2; *cs = 2; return; }   // the fp32 path keeps two variants
   if (m <= 4) { *cr = 2; *cs = 4; return; }
   // Mean pairs per active expert (rounded up) plus one of headroom.
   const int need = (m * d.top_k + d.num_experts - 1) / d.num_experts + 1;
   *cs = 8;
-  *cr = need <= 2 ? 2 : need <= 4 ? 4 : 8;
+  *cr = need <= 2 ? 2 : 4;
 }
 
 // Lanes per down row: the smallest of 16/32/64 that covers the row's chunks
@@ -89,25 +97,33 @@ int down_lanes(int chunks) {
 
 int elems_per_chunk(int fmt) { return fmt == MOE_F32 ? 4 : fmt == MOE_BF16 ? 8 : 32; }
 
-typedef hipError_t (*gate_up_fn)(int, int, const moe::Args &, int, hipStream_t);
-typedef hipError_t (*down_fn)(int, int, int, const moe::Args &, int, hipStream_t);
-
-gate_up_fn gate_up_for(int act, int ef) {
-  static const gate_up_fn t[2][4] = {
-      {moe::launch_gate_up_f32_f32, moe::launch_gate_up_f32_bf16, moe::launch_gate_up_f32_aff4,
-       moe::launch_gate_up_f32_mxfp4},
-      {moe::launch_gate_up_bf16_f32, moe::launch_gate_up_bf16_bf16,
-       moe::launch_gate_up_bf16_aff4, moe::launch_gate_up_bf16_mxfp4}};
-  return t[act][ef];
+const moe::FormatKernels &kernels_for(int act, int ef) {
+  typedef const moe::FormatKernels &(*getter)();
+  static const getter t[2][4] = {
+      {moe::kernels_f32_f32, moe::kernels_f32_bf16, moe::kernels_f32_aff4, moe::kernels_f32_mxfp4},
+      {moe::kernels_bf16_f32, moe::kernels_bf16_bf16, moe::kernels_bf16_aff4, moe::kernels_bf16_mxfp4}};
+  return t[act][ef]();
 }
 
-down_fn down_for(int act, int ef) {
-  static const down_fn t[2][4] = {
-      {moe::launch_down_blend_f32_f32, moe::launch_down_blend_f32_bf16,
-       moe::launch_down_blend_f32_aff4, moe::launch_down_blend_f32_mxfp4},
-      {moe::launch_down_blend_bf16_f32, moe::launch_down_blend_bf16_bf16,
-       moe::launch_down_blend_bf16_aff4, moe::launch_down_blend_bf16_mxfp4}};
-  return t[act][ef];
+// The variant for m rows: the pass sizes pass_variant picks, with the lane
+// grouping down_lanes wants if instantiated, else the widest available.
+bool pick_variant(const moe_decode_desc &d, int m, const moe::Variant **v, moe::launch_fn *gate_up) {
+  int cr, cs;
+  pass_variant(d, m, &cr, &cs);
+  const int want = down_lanes(d.inter / elems_per_chunk(d.expert_fmt));
+  const moe::FormatKernels &k = kernels_for(d.act_fmt, d.expert_fmt);
+  const moe::Variant *best = nullptr;
+  for (int i = 0; i < k.nv; ++i) {
+    const moe::Variant &c = k.v[i];
+    if (c.cr != cr || c.cs != cs) continue;
+    if (c.lpr == want) { best = &c; break; }
+    if (!best || c.lpr > best->lpr) best = &c;
+  }
+  *gate_up = nullptr;
+  for (int i = 0; i < k.ng; ++i)
+    if (k.g[i].cr == cr && k.g[i].cs == cs) *gate_up = k.g[i].gate_up;
+  *v = best;
+  return best && *gate_up;
 }
 
 moe_status check_desc(const moe_decode_desc &d) {
@@ -156,7 +172,7 @@ void layout_for(const moe_decode_desc &d, moe_decode_ws_layout *L) {
     o = align_up(o + (bytes ? bytes : 4), A);
     return at;
   };
-  L->sync = take(16 * sizeof(uint32_t));
+  L->sync = take(moe::SYNC_WORDS * sizeof(uint32_t));
   L->logits = take(R * (E + 1) * sizeof(double));
   L->topk_idx = take(te * 4);
   L->topk_w = take(te * 4);
@@ -208,8 +224,8 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   if (!aligned(workspace, 256)) return fail(MOE_EWORKSPACE, "workspace must be 256-byte aligned");
   if (workspace_bytes < L.total)
     return fail(MOE_EWORKSPACE, "workspace has %zu bytes, the plan needs %zu", workspace_bytes, L.total);
-  if (events && n_events != kNumStages + 1)
-    return fail(MOE_EINVAL, "n_events must be %d", kNumStages + 1);
+  const int nst = num_stages(plan->variant);
+  if (events && n_events != nst + 1) return fail(MOE_EINVAL, "n_events must be %d", nst + 1);
   moe_status st = check_weights(d, w);
   if (st != MOE_OK) return st;
 
@@ -252,26 +268,31 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   a.sact = reinterpret_cast<float *>(ws + L.shared_act);
   a.sync = reinterpret_cast<unsigned *>(ws + L.sync);
 
-  int cr, cs;
-  pass_variant(d, m, &cr, &cs);
-  const int lpr = down_lanes(d.inter / elems_per_chunk(d.expert_fmt));
-  const int route_rows = d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0);
-  const int route_blocks = (route_rows + moe::ROUTE_THREADS / moe::WAVE - 1) / (moe::ROUTE_THREADS / moe::WAVE);
-  const int ni = moe::GATE_UP_ROWS / 2;
-  const long gu_waves = (long)a.cap * ((d.inter + ni - 1) / ni) + ((d.flags & MOE_SHARED) ? (a.Is + ni - 1) / ni : 0);
-  const int wpb = moe::GEMV_THREADS / moe::WAVE;
-  const int gu_blocks = (int)((gu_waves + wpb - 1) / wpb);
-  const int db_blocks = (d.hidden + moe::DOWN_TILE - 1) / moe::DOWN_TILE;
+  const moe::Variant &kv = *plan->kv[m];
+  const int cr = kv.cr, cs = kv.cs, lpr = kv.lpr;
+  const bool shared = (d.flags & MOE_SHARED) != 0;
+  // Work items (each one 256-thread workgroup): see moe_kernels.hpp.
+  const int wpb = moe::WPB;
+  const int ni_r = d.expert_fmt >= MOE_AFF4_G64 ? 4 : 2;   // gate_up_ni<EF>()
+  const int ni_s = 2;                                       // gate_up_ni<ACT>()
+  a.n_router = (d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0) + wpb - 1) / wpb;
+  a.n_shared_gu = shared ? ((a.Is + ni_s - 1) / ni_s + wpb - 1) / wpb : 0;
+  a.gu_items_per_slot = ((d.inter + ni_r - 1) / ni_r + wpb - 1) / wpb;
+  a.n_routed_gu = a.cap * a.gu_items_per_slot;
+  a.down_dq = (a.cap + (shared ? 1 : 0)) < wpb ? 2 : 1;
+  a.n_down = (d.hidden + moe::DOWN_RD * a.down_dq - 1) / (moe::DOWN_RD * a.down_dq);
+  a.n_items = a.n_router + a.n_shared_gu + a.n_routed_gu + a.n_down;
 
   static thread_local bool logged = false;
   if (!logged && log_enabled()) {
     logged = true;
     fprintf(stderr,
-            "[moe_decode] first forward: m=%d H=%d E=%d k=%d I=%d Is=%d act=%d expert=%d routing=%d "
-            "flags=0x%x | route %d blocks, gate_up %d blocks (CR=%d CS=%d), down_blend %d blocks "
-            "(LPR=%d)\n",
-            m, d.hidden, d.num_experts, d.top_k, d.inter, a.Is, d.act_fmt, d.expert_fmt, d.routing,
-            d.flags, route_blocks, gu_blocks, cr, cs, db_blocks, lpr);
+            "[moe_decode] first forward: %s, m=%d H=%d E=%d k=%d I=%d Is=%d act=%d expert=%d "
+            "routing=%d flags=0x%x | items: router %d, shared gate/up %d, routed gate/up %d "
+            "(%d per slot), down %d (dq %d) | CR=%d CS=%d LPR=%d\n",
+            "split", m, d.hidden, d.num_experts, d.top_k,
+            d.inter, a.Is, d.act_fmt, d.expert_fmt, d.routing, d.flags, a.n_router, a.n_shared_gu,
+            a.n_routed_gu, a.gu_items_per_slot, a.n_down, a.down_dq, cr, cs, lpr);
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -280,13 +301,13 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   };
   hipError_t e;
   if ((e = rec(0)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if ((e = moe::launch_route(d.act_fmt, a, route_blocks, s)) != hipSuccess)
+  if ((e = moe::launch_route(d.act_fmt, cs, a, a.n_router + a.n_shared_gu, s)) != hipSuccess)
     return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
   if ((e = rec(1)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if ((e = gate_up_for(d.act_fmt, d.expert_fmt)(cr, cs, a, gu_blocks, s)) != hipSuccess)
+  if ((e = plan->gate_up[m](a, a.n_routed_gu, s)) != hipSuccess)
     return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
   if ((e = rec(2)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if ((e = down_for(d.act_fmt, d.expert_fmt)(cr, cs, lpr, a, db_blocks, s)) != hipSuccess)
+  if ((e = kv.down_blend(a, a.n_down, s)) != hipSuccess)
     return fail(MOE_EHIP, "down_blend launch: %s", hipGetErrorString(e));
   if ((e = rec(3)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
   return ok();
@@ -306,6 +327,17 @@ moe_status moe_decode_plan(const moe_decode_desc *desc, moe_decode_plan_t **plan
   if (!p) return fail(MOE_EINVAL, "out of host memory");
   p->d = *desc;
   if (!(p->d.flags & MOE_SHARED)) p->d.shared_inter = 0;
+  if (fused_requested()) {
+    delete p;
+    return fail(MOE_EUNSUPPORTED, "the single-launch arrangement is disabled");
+  }
+  p->variant = kSplit;
+  for (int m = 1; m <= p->d.max_rows; ++m) {
+    if (!pick_variant(p->d, m, &p->kv[m], &p->gate_up[m])) {
+      delete p;
+      return fail(MOE_EUNSUPPORTED, "no kernel variant for m = %d", m);
+    }
+  }
   layout_for(p->d, &p->L);
   *plan = p;
   *workspace_bytes = p->L.total;
@@ -326,7 +358,7 @@ moe_status moe_decode_workspace_init(const moe_decode_plan_t *plan, void *worksp
   if (!workspace || !aligned(workspace, 256)) return fail(MOE_EWORKSPACE, "workspace must be non-null and 256-byte aligned");
   if (workspace_bytes < plan->L.total)
     return fail(MOE_EWORKSPACE, "workspace has %zu bytes, the plan needs %zu", workspace_bytes, plan->L.total);
-  hipError_t e = moe::launch_clear_sync(reinterpret_cast<unsigned *>(static_cast<char *>(workspace) + plan->L.sync), 16,
+  hipError_t e = moe::launch_clear_sync(reinterpret_cast<unsigned *>(static_cast<char *>(workspace) + plan->L.sync), moe::SYNC_WORDS,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MOE_EHIP, "workspace init launch: %s", hipGetErrorString(e));
   return ok();
@@ -349,11 +381,11 @@ moe_status moe_decode_forward_timed(const moe_decode_plan_t *plan, const moe_dec
                       n_events);
 }
 
-int32_t moe_decode_num_stages(const moe_decode_plan_t *plan) { return plan ? kNumStages : 0; }
+int32_t moe_decode_num_stages(const moe_decode_plan_t *plan) { return plan ? num_stages(plan->variant) : 0; }
 
 const char *moe_decode_stage_name(const moe_decode_plan_t *plan, int32_t i) {
-  if (!plan || i < 0 || i >= kNumStages) return "";
-  return kStageNames[i];
+  if (!plan || i < 0 || i >= num_stages(plan->variant)) return "";
+  return stage_name(plan->variant, i);
 }
 
 const char *moe_decode_last_error(void) { return g_err.c_str(); }

@@ -1,5 +1,8 @@
-// moe_launch.hpp -- launchers of the kernel variants (one translation unit
-// per activation/expert format pair instantiates its variants).
+// moe_launch.hpp -- per-format tables of the instantiated kernel variants.
+//
+// Each inst_<act>_<expert>.hip translation unit instantiates the variants
+// its format pair needs and exposes them through a FormatKernels table; the
+// host picks a (CR, CS, LPR) present in the table.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -7,67 +10,59 @@ namespace moe {
 
 struct Args;
 
-// (CR, CS): input vectors per pass for routed and shared rows.  Kept to the
-// pairs the host's variant choice can produce.
-#define MOE_PASS_VARIANTS(X) X(1, 1) X(2, 2) X(2, 4) X(2, 8) X(4, 8) X(8, 8)
+typedef hipError_t (*launch_fn)(const Args &a, int blocks, hipStream_t st);
 
-hipError_t launch_route(int act, const Args &a, int blocks, hipStream_t st);
+// (CR, CS): input vectors per pass for routed and shared rows; LPR: lanes
+// per down row.
+struct Variant {
+  int cr, cs, lpr;
+  launch_fn down_blend;   // third launch
+};
+struct GateUpVariant {
+  int cr, cs;
+  launch_fn gate_up;      // second launch
+};
+struct FormatKernels {
+  const Variant *v;
+  int nv;
+  const GateUpVariant *g;
+  int ng;
+};
+
+// First launch: router items plus the shared expert's gate/up items.
+hipError_t launch_route(int act, int cs, const Args &a, int blocks, hipStream_t st);
 hipError_t launch_clear_sync(unsigned *sync, int n, hipStream_t st);
 
-#define MOE_DECLARE_FMT(NAME)                                                              \
-  hipError_t launch_gate_up_##NAME(int cr, int cs, const Args &a, int blocks, hipStream_t st); \
-  hipError_t launch_down_blend_##NAME(int cr, int cs, int lpr, const Args &a, int blocks,     \
-                                      hipStream_t st);
-MOE_DECLARE_FMT(f32_f32)
-MOE_DECLARE_FMT(f32_bf16)
-MOE_DECLARE_FMT(f32_aff4)
-MOE_DECLARE_FMT(f32_mxfp4)
-MOE_DECLARE_FMT(bf16_f32)
-MOE_DECLARE_FMT(bf16_bf16)
-MOE_DECLARE_FMT(bf16_aff4)
-MOE_DECLARE_FMT(bf16_mxfp4)
-#undef MOE_DECLARE_FMT
+const FormatKernels &kernels_f32_f32();
+const FormatKernels &kernels_f32_bf16();
+const FormatKernels &kernels_f32_aff4();
+const FormatKernels &kernels_f32_mxfp4();
+const FormatKernels &kernels_bf16_f32();
+const FormatKernels &kernels_bf16_bf16();
+const FormatKernels &kernels_bf16_aff4();
+const FormatKernels &kernels_bf16_mxfp4();
+
+#ifdef MOE_KERNELS_HPP_INCLUDED
+template <int EF, int ACT, int CR, int CS, int LPR>
+hipError_t launch_down_blend_t(const Args &a, int blocks, hipStream_t st) {
+  hipLaunchKernelGGL((down_blend_kernel<EF, ACT, CR, CS, LPR>), dim3(blocks), dim3(THREADS), 0, st, a);
+  return hipGetLastError();
+}
+template <int EF, int ACT, int CR, int CS>
+hipError_t launch_gate_up_t(const Args &a, int blocks, hipStream_t st) {
+  hipLaunchKernelGGL((gate_up_kernel<EF, ACT, CR, CS>), dim3(blocks), dim3(THREADS), 0, st, a);
+  return hipGetLastError();
+}
+#endif
 
 }  // namespace moe
 
-// Body of one instantiation unit: ACT_ and EF_ are format enums of moe; the
-// case macros below see them as the constants ACTT and EFT.
-#define MOE_INSTANTIATE(ACT_, EF_, NAME)                                                     \
-  namespace moe {                                                                            \
-  hipError_t launch_gate_up_##NAME(int cr, int cs, const Args &a, int blocks, hipStream_t st) { \
-    constexpr int EFT = EF_, ACTT = ACT_;                                                    \
-    bool done = false;                                                                       \
-    MOE_PASS_VARIANTS(MOE_GU_CASE)                                                           \
-    if (!done) return hipErrorInvalidValue;                                                  \
-    return hipGetLastError();                                                                \
-  }                                                                                          \
-  hipError_t launch_down_blend_##NAME(int cr, int cs, int lpr, const Args &a, int blocks,       \
-                                      hipStream_t st) {                                      \
-    constexpr int EFT = EF_, ACTT = ACT_;                                                    \
-    bool done = false;                                                                       \
-    MOE_PASS_VARIANTS(MOE_DB_CASE)                                                           \
-    if (!done) return hipErrorInvalidValue;                                                  \
-    return hipGetLastError();                                                                \
-  }                                                                                          \
-  }
-
-#define MOE_GU_CASE(CR_, CS_)                                                                 \
-  if (!done && cr == CR_ && cs == CS_) {                                                     \
-    hipLaunchKernelGGL((gate_up_kernel<EFT, ACTT, CR_, CS_>), dim3(blocks), dim3(GEMV_THREADS), \
-                       0, st, a);                                                            \
-    done = true;                                                                             \
-  }
-
-#define MOE_DB_CASE(CR_, CS_)                                                                 \
-  if (!done && cr == CR_ && cs == CS_) {                                                     \
-    if (lpr == 16)                                                                           \
-      hipLaunchKernelGGL((down_blend_kernel<EFT, ACTT, CR_, CS_, 16>), dim3(blocks),         \
-                         dim3(GEMV_THREADS), 0, st, a);                                      \
-    else if (lpr == 32)                                                                      \
-      hipLaunchKernelGGL((down_blend_kernel<EFT, ACTT, CR_, CS_, 32>), dim3(blocks),         \
-                         dim3(GEMV_THREADS), 0, st, a);                                      \
-    else                                                                                     \
-      hipLaunchKernelGGL((down_blend_kernel<EFT, ACTT, CR_, CS_, 64>), dim3(blocks),         \
-                         dim3(GEMV_THREADS), 0, st, a);                                      \
-    done = true;                                                                             \
+// Inside an inst_*.hip unit, with constexpr int EFT and ACTT in scope.
+#define MOE_V(CR, CS, LPR) { CR, CS, LPR, &launch_down_blend_t<EFT, ACTT, CR, CS, LPR> }
+#define MOE_G(CR, CS) { CR, CS, &launch_gate_up_t<EFT, ACTT, CR, CS> }
+#define MOE_TABLE(NAME)                                                            \
+  const FormatKernels &kernels_##NAME() {                                          \
+    static const FormatKernels k{kV, (int)(sizeof kV / sizeof kV[0]), kG,         \
+                                 (int)(sizeof kG / sizeof kG[0])};                 \
+    return k;                                                                      \
   }

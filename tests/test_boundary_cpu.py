@@ -85,10 +85,10 @@ def test_plan_and_layout_for_every_workload(name):
             assert a1 <= b0, "workspace arrays overlap"
         assert all(o % 256 == 0 for o, _ in fields)
         assert spans[-1][1] <= ws
-        assert md.moe_decode_num_stages(plan) == 3
-        assert [md.moe_decode_stage_name(plan, i) for i in range(3)] == \
-            ["route", "gate_up", "down_blend"]
-        assert md.moe_decode_stage_name(plan, 3) == ""
+        want = ["route", "gate_up", "down_blend"]
+        n = md.moe_decode_num_stages(plan)
+        assert [md.moe_decode_stage_name(plan, i) for i in range(n)] == want
+        assert md.moe_decode_stage_name(plan, n) == ""
     finally:
         md.moe_decode_plan_destroy(plan)
 
@@ -139,9 +139,10 @@ def test_forward_rejects_bad_pointers_and_workspace():
                                       None) == md.MOE_EINVAL
         assert lib.moe_decode_forward(None, C.byref(_weights_stub()), 4096, 1, 4096, None, None,
                                       4096 * 256, ws, None) == md.MOE_EINVAL
-        ev = (C.c_void_p * 2)(4096, 4096)
+        # An event count no arrangement uses (1 or 3 stages -> 2 or 4 events).
+        ev = (C.c_void_p * 7)(*([4096] * 7))
         assert lib.moe_decode_forward_timed(plan, C.byref(_weights_stub()), 4096, 1, 4096, None,
-                                            None, 4096 * 256, ws, None, ev, 2) == md.MOE_EINVAL
+                                            None, 4096 * 256, ws, None, ev, 7) == md.MOE_EINVAL
     finally:
         md.moe_decode_plan_destroy(plan)
 
@@ -160,3 +161,12 @@ def test_sigmoid_bias_needs_expert_bias():
             md.moe_decode_forward(plan, w, 4096, 1, 4096, None, None, 4096 * 256, ws, 0)
     finally:
         md.moe_decode_plan_destroy(plan)
+
+
+def test_single_launch_arrangement_is_refused(monkeypatch):
+    # The persistent single-launch arrangement is switched off: asking for it
+    # fails at plan time instead of launching it.
+    monkeypatch.setenv("MOE_DECODE_VARIANT", "fused")
+    with pytest.raises(md.MoeDecodeError) as ei:
+        md.moe_decode_plan(desc_of(synth.WORKLOADS["qwen3_30b_a3b_bf16"]))
+    assert ei.value.status == md.MOE_EUNSUPPORTED

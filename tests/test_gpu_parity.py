@@ -44,6 +44,19 @@ def rms(a):
     return float(np.sqrt(np.mean(np.square(a))))
 
 
+SYNC_STRIDE = 32                 # one completion word per 128 bytes
+SYNC_WORDS = 272 * SYNC_STRIDE
+SYNC_ERR = 5 * SYNC_STRIDE       # the expired-wait flag
+
+
+def check_sync_words(dl):
+    """After a call every completion word is back to zero (and no bounded
+    wait expired)."""
+    words = dl.ws_view("sync", torch.int32, SYNC_WORDS).cpu().numpy()
+    assert words[SYNC_ERR] == 0, "a bounded wait expired inside the kernel"
+    assert not words.any(), f"completion words not reset: {np.nonzero(words)[0][:8]}"
+
+
 def run(dl: DeviceLayer, x_np: np.ndarray, m: int):
     spec = dl.spec
     x = to_device(np.ascontiguousarray(x_np[:m]), "cuda")
@@ -52,6 +65,7 @@ def run(dl: DeviceLayer, x_np: np.ndarray, m: int):
     w = torch.full((m, spec.top_k), float("nan"), dtype=torch.float32, device="cuda")
     dl.forward(x, m, out, idx, w)
     torch.cuda.synchronize()
+    check_sync_words(dl)
     return out_to_numpy(spec, out), idx.cpu().numpy(), w.cpu().numpy()
 
 
@@ -281,5 +295,6 @@ def test_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i}"
+        check_sync_words(dl)
         dl.forward(x, m, dl.new_out(m))      # eager work between replays
         torch.cuda.synchronize()
