@@ -140,7 +140,7 @@ typedef struct {
   size_t active_count;    /* int32 [1] */
   size_t act;             /* float [te, I]: routed SwiGLU activations, sorted order */
   size_t shared_act;      /* float [max_rows, Is] */
-  size_t sync;            /* uint32 [8704]: completion words (one per 128 bytes), zero between calls */
+  size_t sync;            /* uint32 [512]: reserved completion words, kept zero */
   size_t total;           /* bytes a workspace must have */
 } moe_decode_ws_layout;
 
@@ -156,9 +156,9 @@ void moe_decode_plan_destroy(moe_decode_plan_t *plan);
 moe_status moe_decode_workspace_layout(const moe_decode_plan_t *plan,
                                        moe_decode_ws_layout *layout);
 
-/* Prepare a freshly allocated workspace (zeroes its completion counters with
- * a kernel on `stream`).  Required once before the first forward on a
- * workspace; every forward leaves the counters zero again. */
+/* Prepare a freshly allocated workspace (zeroes its reserved completion words
+ * with a kernel on `stream`).  Call once before the first forward on a
+ * workspace; forwards leave them zero. */
 moe_status moe_decode_workspace_init(const moe_decode_plan_t *plan, void *workspace,
                                      size_t workspace_bytes, void *stream);
 

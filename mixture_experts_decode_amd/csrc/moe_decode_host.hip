@@ -68,6 +68,9 @@ const char *const kSplitStages[] = {"route", "gate_up", "down_blend"};
 int num_stages(int) { return 3; }
 const char *stage_name(int, int i) { return kSplitStages[i]; }
 
+// Workgroups of the gate/up launch: a few per CU; each loops over items.
+constexpr int kGateUpMaxBlocks = 1024;
+
 bool fused_requested() {
   const char *v = getenv("MOE_DECODE_VARIANT");
   return v && strcmp(v, "fused") == 0;
@@ -275,13 +278,13 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   const int wpb = moe::WPB;
   const int ni_r = d.expert_fmt >= MOE_AFF4_G64 ? 4 : 2;   // gate_up_ni<EF>()
   const int ni_s = 2;                                       // gate_up_ni<ACT>()
-  a.n_router = (d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0) + wpb - 1) / wpb;
+  const int nrb = (m + 7) / 8;                               // input-row blocks per router row
+  a.n_router = ((d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0)) * nrb + wpb - 1) / wpb;
   a.n_shared_gu = shared ? ((a.Is + ni_s - 1) / ni_s + wpb - 1) / wpb : 0;
   a.gu_items_per_slot = ((d.inter + ni_r - 1) / ni_r + wpb - 1) / wpb;
   a.n_routed_gu = a.cap * a.gu_items_per_slot;
   a.down_dq = (a.cap + (shared ? 1 : 0)) < wpb ? 2 : 1;
   a.n_down = (d.hidden + moe::DOWN_RD * a.down_dq - 1) / (moe::DOWN_RD * a.down_dq);
-  a.n_items = a.n_router + a.n_shared_gu + a.n_routed_gu + a.n_down;
 
   static thread_local bool logged = false;
   if (!logged && log_enabled()) {
@@ -304,7 +307,9 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   if ((e = moe::launch_route(d.act_fmt, cs, a, a.n_router + a.n_shared_gu, s)) != hipSuccess)
     return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
   if ((e = rec(1)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if ((e = plan->gate_up[m](a, a.n_routed_gu, s)) != hipSuccess)
+  // gate_up: a grid-stride launch; every workgroup pays one routing prologue.
+  const int gu_blocks = a.n_routed_gu < kGateUpMaxBlocks ? a.n_routed_gu : kGateUpMaxBlocks;
+  if ((e = plan->gate_up[m](a, gu_blocks, s)) != hipSuccess)
     return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
   if ((e = rec(2)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
   if ((e = kv.down_blend(a, a.n_down, s)) != hipSuccess)

@@ -1,23 +1,20 @@
 // moe_kernels.hpp -- gfx950 device code of the decode MoE layer.
 //
-// The layer is cut into work items, each run by one 256-thread workgroup:
-//   router items       4 router rows each (fp64 accumulation); the last one
-//                      to finish scores, selects top-k, computes the routing
-//                      weights and counting-sorts the (row, slot) pairs by
-//                      expert in LDS ("route tail").
-//   shared gate/up     the shared expert's gate/up rows (all m rows of x).
-//   routed gate/up     (active-expert slot, row block): streams the slot's
-//                      gate and up rows once for all of its pairs,
-//                      dequantised in registers, writes silu(g)*v per pair.
-//   down tiles         a tile of output columns: the down rows of every
-//                      active expert and of the shared expert for the tile,
-//                      y per pair in LDS, then the slot-order blend.
-// They run as three ordinary kernels on the caller's stream, the kernel
-// boundaries ordering them: route_kernel (router items, then the route tail
-// in the last one to finish, beside the shared expert's gate/up items),
-// gate_up_kernel (routed gate/up items) and down_blend_kernel (down tiles).
-// fused_kernel, which would run all items in one persistent launch with
-// bounded waits between them, is kept in source but not launched (see it).
+// The layer runs as three kernels on the caller's stream, each made of
+// 256-thread work items:
+//   route_kernel     router units (router row x block of 8 input rows, fp64
+//                    accumulation) writing the logits, and -- since it needs
+//                    no routing -- the shared expert's gate/up rows.
+//   gate_up_kernel   every workgroup rebuilds the routing from the logits in
+//                    LDS (top-k per row, weights, stable counting sort by
+//                    expert; block 0 publishes it), then streams the gate and
+//                    up rows of its (active-expert slot, row block) once for
+//                    all of the slot's pairs, dequantised in registers, and
+//                    writes silu(g)*v per pair.
+//   down_blend_kernel  a tile of output columns: the down rows of every
+//                    active expert and of the shared expert for the tile, y
+//                    per pair in LDS, then the slot-order blend.
+// No workgroup ever waits for another; the kernel boundaries order the steps.
 //
 // Pages: metrale "forward_bf16_grouped_decode.rs" (the five steps and their
 // buffers), mlxcel "perf(moe): wire lfm2 to the fused decode-MoE kernel"
@@ -47,20 +44,9 @@ constexpr int MAX_PAIRS = MAX_ROWS * MAX_TOPK;
 constexpr int DOWN_RD = 8;              // down rows per wave sub-unit
 constexpr int MAX_DOWN_TILE = 2 * DOWN_RD;
 
-// Completion words in the workspace (zero between calls).  Word i lives at
-// sync[i * SYNC_STRIDE]: one 128-byte line each, so pollers of one word do
-// not contend with the atomics on another.
-enum : int {
-  SYNC_NEXT = 0,      // next work item to claim (fused)
-  SYNC_ROUTER = 1,    // router items finished (ticket)
-  SYNC_READY = 2,     // routing published (fused)
-  SYNC_EXIT = 3,      // workgroups that left the item loop (fused)
-  SYNC_SHARED = 4,    // shared gate/up items finished (fused)
-  SYNC_ERR = 5,       // a bounded wait expired: stays set until re-initialised
-  SYNC_SLOT0 = 16,    // gate/up items finished, per active slot
-  SYNC_STRIDE = 32,
-  SYNC_WORDS = (SYNC_SLOT0 + 256) * SYNC_STRIDE
-};
+// Reserved completion words in the workspace (zeroed by
+// moe_decode_workspace_init; unused by the current kernels).
+constexpr int SYNC_WORDS = 512;
 
 // Rows of intermediate per gate/up wave: 2 for 16-byte-per-8-or-4 element
 // formats, 4 for the 4-bit ones (their rows are 4x shorter).
@@ -77,7 +63,7 @@ struct Args {
   unsigned flags;
   float rsf;
   // work items
-  int n_router, n_shared_gu, gu_items_per_slot, n_routed_gu, n_down, n_items, down_dq;
+  int n_router, n_shared_gu, gu_items_per_slot, n_routed_gu, n_down, down_dq;
   const void *x;
   void *out;
   int32_t *idx_out;
@@ -211,77 +197,6 @@ __device__ __forceinline__ double wave_max_f64(double v) {
               fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
 }
 
-// ------------------------------------------------ completion words
-//
-// A producer publishes with a release fence at agent scope (its stores are
-// written back past the XCD's L2) and then an atomic add; a consumer polls
-// with relaxed agent-scope atomic loads and then takes an acquire fence.
-// Every wait is bounded: on expiry it sets SYNC_ERR and reports failure, and
-// the caller then skips the work that depended on it, so a broken counter
-// can give a wrong answer (flagged) but never a hang or a wild access.
-
-// Longest a wait may last: 200 ms of the 100 MHz constant clock.  A whole
-// forward of the largest layer takes about a millisecond.
-constexpr uint64_t WAIT_TICKS = 20000000ull;
-
-__device__ __forceinline__ unsigned *word(unsigned *sync, int i) { return sync + i * SYNC_STRIDE; }
-
-__device__ __forceinline__ unsigned load_word(const unsigned *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-
-// One thread polls until word i >= target.  Every 16th poll is an atomic RMW
-// that leaves the value unchanged (it always reads the coherent value), and
-// the wait gives up after WAIT_TICKS of wall time or once another wait has
-// given up.
-__device__ __noinline__ bool poll_geq(unsigned *sync, int i, unsigned target) {
-  unsigned *p = word(sync, i);
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  for (unsigned it = 1;; ++it) {
-    const unsigned v = (it & 15u) ? load_word(p) : atomicOr(p, 0u);
-    if (v >= target) return true;
-    if ((it & 15u) == 0u) {
-      if (atomicOr(word(sync, SYNC_ERR), 0u) != 0u) return false;
-      if (__builtin_amdgcn_s_memrealtime() - t0 > WAIT_TICKS) {
-        atomicOr(word(sync, SYNC_ERR), 1u);
-        return false;
-      }
-    }
-    __builtin_amdgcn_s_sleep(8);
-  }
-}
-
-// Whole workgroup waits (thread 0 polls); acquire for every thread.
-__device__ __forceinline__ bool wg_wait(unsigned *sync, int i, unsigned target) {
-  __shared__ int s_ok;
-  if (threadIdx.x == 0) s_ok = poll_geq(sync, i, target) ? 1 : 0;
-  __syncthreads();
-  const bool ok = s_ok != 0;
-  acquire_agent();
-  __syncthreads();
-  return ok;
-}
-
-// One wave waits (its lane 0 polls); acquire for the wave.
-__device__ __forceinline__ bool wave_wait(unsigned *sync, int i, unsigned target) {
-  int ok = 0;
-  if ((threadIdx.x & 63) == 0) ok = poll_geq(sync, i, target) ? 1 : 0;
-  ok = __builtin_amdgcn_readfirstlane(ok);
-  acquire_agent();
-  return ok != 0;
-}
-
-// Every thread's stores are written back (its own release), the barrier
-// orders them before thread 0's increment, which is itself a release.
-__device__ __forceinline__ void wg_signal(unsigned *sync, int i) {
-  release_agent();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(word(sync, i), 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // --------------------------------------------------- per-format chunk math
 //
@@ -325,16 +240,19 @@ __device__ __forceinline__ WChunk<WF> load_wchunk(const Row<WF> &r, int ch) {
   return c;
 }
 
-// The x elements matching one weight chunk, in the form the dot needs.
+// The x elements matching one weight chunk: fetch() issues the loads, prep()
+// turns them into the form dot() needs (kept apart so that the loads of
+// several chunk steps can be in flight together).
 template <int WF, int XF> struct XChunk;
 
 // bf16 weights . bf16 x: raw bf16 pairs, v_dot2.
 template <> struct XChunk<BF16, BF16> {
   uint32_t d[4];
-  __device__ __forceinline__ void load(const char *xrow, int ch) {
+  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
     u32x4 v = ld16(xrow + (size_t)ch * 16);
     d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
   }
+  __device__ __forceinline__ void prep() {}
   __device__ __forceinline__ float dot(const WChunk<BF16> &w, float acc) const {
     acc = dot2(w.q.x, d[0], acc);
     acc = dot2(w.q.y, d[1], acc);
@@ -346,7 +264,8 @@ template <> struct XChunk<BF16, BF16> {
 // bf16 weights . f32 x.
 template <> struct XChunk<BF16, F32> {
   float f[8];
-  __device__ __forceinline__ void load(const char *xrow, int ch) {
+  __device__ __forceinline__ void prep() {}
+  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
     u32x4 a = ld16(xrow + (size_t)ch * 32), b = ld16(xrow + (size_t)ch * 32 + 16);
     f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y);
     f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
@@ -367,7 +286,8 @@ template <> struct XChunk<BF16, F32> {
 // f32 weights . f32 x.
 template <> struct XChunk<F32, F32> {
   float f[4];
-  __device__ __forceinline__ void load(const char *xrow, int ch) {
+  __device__ __forceinline__ void prep() {}
+  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
     u32x4 a = ld16(xrow + (size_t)ch * 16);
     f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y);
     f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
@@ -383,9 +303,10 @@ template <> struct XChunk<F32, F32> {
 // f32 weights . bf16 x.
 template <> struct XChunk<F32, BF16> {
   float f[4];
-  __device__ __forceinline__ void load(const char *xrow, int ch) {
-    u32x2 a = ld8(xrow + (size_t)ch * 8);
-    f[0] = bf_lo(a.x); f[1] = bf_hi(a.x); f[2] = bf_lo(a.y); f[3] = bf_hi(a.y);
+  u32x2 raw;
+  __device__ __forceinline__ void fetch(const char *xrow, int ch) { raw = ld8(xrow + (size_t)ch * 8); }
+  __device__ __forceinline__ void prep() {
+    f[0] = bf_lo(raw.x); f[1] = bf_hi(raw.x); f[2] = bf_lo(raw.y); f[3] = bf_hi(raw.y);
   }
   __device__ __forceinline__ float dot(const WChunk<F32> &w, float acc) const {
     acc = __builtin_fmaf(__uint_as_float(w.q.x), f[0], acc);
@@ -404,20 +325,27 @@ template <> struct XChunk<F32, BF16> {
 template <> struct XChunk<AFF4, BF16> {
   uint32_t d[16];
   float xs;
-  __device__ __forceinline__ void load(const char *xrow, int ch) {
+  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
     const char *p = xrow + (size_t)ch * 64;
-    float s = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x4 r = ld16(p + 16 * g);  // (x0,x1) (x2,x3) (x4,x5) (x6,x7)
-      d[4 * g + 0] = (r.x & 0xFFFFu) | (r.z << 16);
-      d[4 * g + 1] = (r.x >> 16) | (r.z & 0xFFFF0000u);
-      d[4 * g + 2] = (r.y & 0xFFFFu) | (r.w << 16);
-      d[4 * g + 3] = (r.y >> 16) | (r.w & 0xFFFF0000u);
-      s = dot2(r.x, 0x3F803F80u, s);
-      s = dot2(r.y, 0x3F803F80u, s);
-      s = dot2(r.z, 0x3F803F80u, s);
-      s = dot2(r.w, 0x3F803F80u, s);
+      d[4 * g + 0] = r.x; d[4 * g + 1] = r.y; d[4 * g + 2] = r.z; d[4 * g + 3] = r.w;
+    }
+  }
+  __device__ __forceinline__ void prep() {
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t rx = d[4 * g], ry = d[4 * g + 1], rz = d[4 * g + 2], rw = d[4 * g + 3];
+      d[4 * g + 0] = (rx & 0xFFFFu) | (rz << 16);
+      d[4 * g + 1] = (rx >> 16) | (rz & 0xFFFF0000u);
+      d[4 * g + 2] = (ry & 0xFFFFu) | (rw << 16);
+      d[4 * g + 3] = (ry >> 16) | (rw & 0xFFFF0000u);
+      s = dot2(rx, 0x3F803F80u, s);
+      s = dot2(ry, 0x3F803F80u, s);
+      s = dot2(rz, 0x3F803F80u, s);
+      s = dot2(rw, 0x3F803F80u, s);
     }
     xs = s;
   }
@@ -441,15 +369,17 @@ template <> struct XChunk<AFF4, BF16> {
 template <> struct XChunk<AFF4, F32> {
   float f[32];
   float xs;
-  __device__ __forceinline__ void load(const char *xrow, int ch) {
+  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
     const char *p = xrow + (size_t)ch * 128;
-    float s = 0.f;
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       u32x4 r = ld16(p + 16 * g);
       f[4 * g + 0] = __uint_as_float(r.x); f[4 * g + 1] = __uint_as_float(r.y);
       f[4 * g + 2] = __uint_as_float(r.z); f[4 * g + 3] = __uint_as_float(r.w);
     }
+  }
+  __device__ __forceinline__ void prep() {
+    float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) s += f[i];
     xs = s;
@@ -476,7 +406,8 @@ template <> struct XChunk<AFF4, F32> {
 // lines up with the raw x pair; the E8M0 scale multiplies the chunk sum.
 template <> struct XChunk<MXFP4, BF16> {
   uint32_t d[16];
-  __device__ __forceinline__ void load(const char *xrow, int ch) {
+  __device__ __forceinline__ void prep() {}
+  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
     const char *p = xrow + (size_t)ch * 64;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -501,7 +432,8 @@ template <> struct XChunk<MXFP4, BF16> {
 // mxfp4 weights . f32 x.
 template <> struct XChunk<MXFP4, F32> {
   float f[32];
-  __device__ __forceinline__ void load(const char *xrow, int ch) {
+  __device__ __forceinline__ void prep() {}
+  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
     const char *p = xrow + (size_t)ch * 128;
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
@@ -536,14 +468,17 @@ template <> struct XChunk<MXFP4, F32> {
 // RG weight rows per lane group (each K = nchunks chunks long) against C
 // vectors (xrow[c]).  The wave is split into 64/LPR lane groups; the caller
 // passes in `rows` the RG rows of the calling lane's group.  Lane li of a
-// group takes chunks li, li + LPR, ...; the loads of U chunk steps are issued
-// together before any of them is used.  On return acc[t][c] holds, in every
-// lane of the group, the full dot product of rows[t] with vector c.  The
-// per-(row, vector) arithmetic does not depend on C, U or the other rows, so
-// results are the same for every m.
+// group takes chunks li, li + LPR, ...; the weight loads of U chunk steps --
+// and, where registers allow, their x loads -- are issued together before any
+// of them is used.  On return acc[t][c] holds, in every lane of the group,
+// the full dot product of rows[t] with vector c.  The per-(row, vector)
+// arithmetic does not depend on C, U or the other rows, so results are the
+// same for every m.
 template <int WF, int XF, int RG, int C, int LPR, int U>
 __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const char *const (&xrow)[C],
                                               int nchunks, float (&acc)[RG][C]) {
+  constexpr bool XPF = U * C * (int)(sizeof(XChunk<WF, XF>) / 4) <= 64;  // prefetch x too
+  constexpr int XU = XPF ? U : 1;
   const int li = threadIdx.x % LPR;
 #pragma unroll
   for (int t = 0; t < RG; ++t)
@@ -551,12 +486,17 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
     for (int c = 0; c < C; ++c) acc[t][c] = 0.f;
   for (int base = 0; base < nchunks; base += LPR * U) {
     WChunk<WF> w[U][RG];
+    XChunk<WF, XF> xc[XU][C];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ch = base + li + u * LPR;
       if (ch < nchunks) {
 #pragma unroll
         for (int t = 0; t < RG; ++t) w[u][t] = load_wchunk<WF>(rows[t], ch);
+        if constexpr (XPF) {
+#pragma unroll
+          for (int c = 0; c < C; ++c) xc[u][c].fetch(xrow[c], ch);
+        }
       }
     }
 #pragma unroll
@@ -565,10 +505,11 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
       if (ch < nchunks) {
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-          XChunk<WF, XF> xc;
-          xc.load(xrow[c], ch);
+          XChunk<WF, XF> &x = xc[XPF ? u : 0][c];
+          if constexpr (!XPF) x.fetch(xrow[c], ch);
+          x.prep();
 #pragma unroll
-          for (int t = 0; t < RG; ++t) acc[t][c] = xc.dot(w[u][t], acc[t][c]);
+          for (int t = 0; t < RG; ++t) acc[t][c] = x.dot(w[u][t], acc[t][c]);
         }
       }
     }
@@ -609,260 +550,293 @@ __device__ __forceinline__ const void *tbl(const uint64_t *t, int e) {
   return t ? reinterpret_cast<const void *>(t[e]) : nullptr;
 }
 
-// Routing results read back from the workspace, clamped so that even a
-// corrupted workspace cannot send an access out of bounds.
-__device__ __forceinline__ int active_slots(const Args &a) {
-  const int n = a.active_count[0];
-  return n < 0 ? 0 : (n > a.cap ? a.cap : n);
-}
 __device__ __forceinline__ int clamp_i(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // ------------------------------------------------------------------ router
 //
-// Wave w of router item `item` computes router row e = 4*item + w (row E is
-// the shared expert's gate vector w_g): logits[r, e] = sum_h x[r,h] W[e,h],
-// every product and sum in double, for all m rows.
+// Router unit u = (router row e, block of up to 8 input rows): logits[r, e] =
+// sum_h x[r,h] W[e,h], every product and sum in double.  Row E is the shared
+// expert's gate vector w_g.  The loads of a chunk step (the router chunk and
+// the 8 rows' x chunks) are issued before any is used.
 template <int ACT>
-__device__ __forceinline__ void router_rows(const Args &a, int item) {
+__device__ __forceinline__ void router_unit(const Args &a, int unit) {
   constexpr int EPC = ACT == F32 ? 4 : 8;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = item * WPB + wave;
+  constexpr int RU = 4;                      // chunk steps whose loads are in flight together
+  const int lane = threadIdx.x & 63;
   const int nrows = a.E + ((a.flags & SHARED_GATED) ? 1 : 0);
-  if (e >= nrows) return;
+  const int e = unit % nrows, r0 = (unit / nrows) * 8;
+  if (r0 >= a.m) return;
+  const int nr = min(8, a.m - r0);           // input rows of this unit
   const int nchunks = a.H / EPC;
   const size_t xstride = (size_t)a.H * act_bytes(ACT);
   const char *wrow = e < a.E ? reinterpret_cast<const char *>(a.router) + (size_t)e * xstride
                              : reinterpret_cast<const char *>(a.sgv);
-  const char *x = reinterpret_cast<const char *>(a.x);
+  const char *x = reinterpret_cast<const char *>(a.x) + (size_t)r0 * xstride;
   const int LD = a.E + 1;
-  for (int r0 = 0; r0 < a.m; r0 += 8) {
-    double acc[8];
+  double acc[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc[r] = 0.0;
-    for (int ch = lane; ch < nchunks; ch += WAVE) {
-      float w[EPC];
-      const u32x4 q = ld16(wrow + (size_t)ch * 16);
-      if constexpr (ACT == F32) {
-        w[0] = __uint_as_float(q.x); w[1] = __uint_as_float(q.y);
-        w[2] = __uint_as_float(q.z); w[3] = __uint_as_float(q.w);
-      } else {
-        w[0] = bf_lo(q.x); w[1] = bf_hi(q.x); w[2] = bf_lo(q.y); w[3] = bf_hi(q.y);
-        w[4] = bf_lo(q.z); w[5] = bf_hi(q.z); w[6] = bf_lo(q.w); w[7] = bf_hi(q.w);
-      }
+  for (int r = 0; r < 8; ++r) acc[r] = 0.0;
+  for (int base = 0; base < nchunks; base += WAVE * RU) {
+    u32x4 q[RU];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        if (r0 + r < a.m) {
-          const u32x4 v = ld16(x + (size_t)(r0 + r) * xstride + (size_t)ch * 16);
-          float xv[EPC];
-          if constexpr (ACT == F32) {
-            xv[0] = __uint_as_float(v.x); xv[1] = __uint_as_float(v.y);
-            xv[2] = __uint_as_float(v.z); xv[3] = __uint_as_float(v.w);
-          } else {
-            xv[0] = bf_lo(v.x); xv[1] = bf_hi(v.x); xv[2] = bf_lo(v.y); xv[3] = bf_hi(v.y);
-            xv[4] = bf_lo(v.z); xv[5] = bf_hi(v.z); xv[6] = bf_lo(v.w); xv[7] = bf_hi(v.w);
-          }
-#pragma unroll
-          for (int i = 0; i < EPC; ++i) acc[r] = __builtin_fma((double)w[i], (double)xv[i], acc[r]);
-        }
-      }
+    for (int u = 0; u < RU; ++u) {
+      const int ch = base + lane + u * WAVE;
+      if (ch < nchunks) q[u] = ld16(wrow + (size_t)ch * 16);
     }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      if (r0 + r < a.m) {
-        const double t = wave_sum_f64(acc[r]);
-        if (lane == 0) a.logits[(size_t)(r0 + r) * LD + e] = t;
+      if (r < nr) {
+        u32x4 v[RU];
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+          const int ch = base + lane + u * WAVE;
+          if (ch < nchunks) v[u] = ld16(x + (size_t)r * xstride + (size_t)ch * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+          const int ch = base + lane + u * WAVE;
+          if (ch < nchunks) {
+            float w[EPC], xv[EPC];
+            if constexpr (ACT == F32) {
+              w[0] = __uint_as_float(q[u].x); w[1] = __uint_as_float(q[u].y);
+              w[2] = __uint_as_float(q[u].z); w[3] = __uint_as_float(q[u].w);
+              xv[0] = __uint_as_float(v[u].x); xv[1] = __uint_as_float(v[u].y);
+              xv[2] = __uint_as_float(v[u].z); xv[3] = __uint_as_float(v[u].w);
+            } else {
+              w[0] = bf_lo(q[u].x); w[1] = bf_hi(q[u].x); w[2] = bf_lo(q[u].y); w[3] = bf_hi(q[u].y);
+              w[4] = bf_lo(q[u].z); w[5] = bf_hi(q[u].z); w[6] = bf_lo(q[u].w); w[7] = bf_hi(q[u].w);
+              xv[0] = bf_lo(v[u].x); xv[1] = bf_hi(v[u].x); xv[2] = bf_lo(v[u].y); xv[3] = bf_hi(v[u].y);
+              xv[4] = bf_lo(v[u].z); xv[5] = bf_hi(v[u].z); xv[6] = bf_lo(v[u].w); xv[7] = bf_hi(v[u].w);
+            }
+#pragma unroll
+            for (int i = 0; i < EPC; ++i) acc[r] = __builtin_fma((double)w[i], (double)xv[i], acc[r]);
+          }
+        }
       }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    if (r < nr) {
+      const double t = wave_sum_f64(acc[r]);
+      if (lane == 0) a.logits[(size_t)(r0 + r) * LD + e] = t;
     }
   }
 }
 
-// Block-wide exclusive scan of one int per thread.
-__device__ __forceinline__ int block_excl_scan(int v, int *s_wave, int *total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    const int o = __shfl_up(incl, d, WAVE);
-    if (lane >= d) incl += o;
+// --------------------------------------------------------- top-k and sort
+//
+// Routing state of one forward, rebuilt in LDS by every gate/up workgroup
+// from the logits (each computes the same result; block 0 also publishes it
+// to the workspace for the down/blend launch and the caller).
+struct RouteLDS {
+  int idx[MAX_PAIRS];        // selected expert of pair p = r*k + j
+  float w[MAX_PAIRS];        // routing weight of pair p (times rsf)
+  unsigned mask[MAX_EXPERTS];  // bit r: row r chose expert e
+  int off[MAX_EXPERTS + 1];  // start of each expert's run in `sorted`
+  int sorted[MAX_PAIRS];     // pairs sorted by expert, stable
+  int active[MAX_EXPERTS];   // experts with a pair, ascending
+  int nact;
+};
+
+// Compare-exchange for (key descending, index ascending).
+__device__ __forceinline__ void cx(double &ka, int &ia, double &la, double &kb, int &ib, double &lb) {
+  const bool sw = kb > ka || (kb == ka && ib < ia);
+  if (sw) {
+    const double tk = ka, tl = la;
+    const int ti = ia;
+    ka = kb; la = lb; ia = ib;
+    kb = tk; lb = tl; ib = ti;
   }
-  if (lane == WAVE - 1) s_wave[wave] = incl;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < WPB; ++w) {
-    if (w < wave) base += s_wave[w];
-    tot += s_wave[w];
-  }
-  __syncthreads();
-  *total = tot;
-  return base + incl - v;
 }
 
-// The route tail, run by one whole workgroup once every logit is written:
-// per row (one wave per row) the top-k by key (ties to the lower index) and
-// the weights, then the stable counting sort of the m*k pairs by expert.
-__device__ __forceinline__ void route_tail(const Args &a) {
-  constexpr int T = MAX_EXPERTS / WAVE;
-  __shared__ int s_idx[MAX_PAIRS];
-  __shared__ unsigned s_mask[MAX_EXPERTS];
-  __shared__ int s_off[MAX_EXPERTS + 1];
-  __shared__ int s_wave[WPB];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int E = a.E, k = a.K, m = a.m, LD = E + 1;
-  const bool norm = (a.flags & NORM_TOPK) != 0;
-
-  for (int r = wave; r < m; r += WPB) {
-    const double *lr = a.logits + (size_t)r * LD;
-    double lg[T], key[T];
-    bool taken[T];
+// Top-k of row r by one wave.  Lane l holds experts 4l..4l+3 (E <= 256),
+// sorts them locally by (key desc, index asc), and each round the wave takes
+// the best head: its key by a DPP max, its lane by a ballot -- the lowest
+// lane holding the maximum also holds the lowest index, because lanes own
+// ascending index ranges.  Slot j's expert and weight end up in lane j.
+__device__ __forceinline__ void row_topk(const Args &a, int r, int &my_e, double &my_w) {
+  const int lane = threadIdx.x & 63, E = a.E, k = a.K;
+  const double *lr = a.logits + (size_t)r * (E + 1);
+  double key[4], lg[4];
+  int id[4];
+  bool ok[4];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int e = lane + WAVE * t;
-      taken[t] = e >= E;
-      lg[t] = e < E ? lr[e] : 0.0;
-      key[t] = lg[t];
-      if (a.routing == ROUTE_SIGMOID_BIAS && e < E) key[t] = sigmoid_d(lg[t]) + (double)a.ebias[e];
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    ok[i] = e < E;
+    id[i] = e;
+    lg[i] = ok[i] ? lr[e] : 0.0;
+    key[i] = lg[i];
+    if (ok[i] && a.routing == ROUTE_SIGMOID_BIAS) key[i] = sigmoid_d(lg[i]) + (double)a.ebias[e];
+    if (!ok[i]) key[i] = -__builtin_inf();
+  }
+  // Entries past E sort last: give them the largest indices.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (!ok[i]) id[i] = 0x7FFFFFFF - (3 - i);
+  cx(key[0], id[0], lg[0], key[1], id[1], lg[1]);
+  cx(key[2], id[2], lg[2], key[3], id[3], lg[3]);
+  cx(key[0], id[0], lg[0], key[2], id[2], lg[2]);
+  cx(key[1], id[1], lg[1], key[3], id[3], lg[3]);
+  cx(key[1], id[1], lg[1], key[2], id[2], lg[2]);
+  int left = 0;  // entries of this lane already taken
+  int nvalid = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) nvalid += (id[i] < E) ? 1 : 0;
+  double lmax = 0.0, my_l = 0.0;
+  my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    const bool have = left < nvalid;
+    const double head = have ? key[0] : -__builtin_inf();
+    const double mx = wave_max_f64(head);
+    unsigned long long b = __builtin_amdgcn_ballot_w64(have && head == mx);
+    if (b == 0) b = __builtin_amdgcn_ballot_w64(have);   // only NaN keys left
+    const int wl = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(b));
+    const int win = __builtin_amdgcn_readlane(id[0], wl);
+    const double lw = readlane_f64(lg[0], wl);
+    if (lane == wl) {  // pop the head
+      key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = -__builtin_inf();
+      lg[0] = lg[1]; lg[1] = lg[2]; lg[2] = lg[3];
+      id[0] = id[1]; id[1] = id[2]; id[2] = id[3];
+      ++left;
     }
-    // Slot j's expert and logit end up in lane j.
-    int my_e = 0;
-    double my_l = 0.0, lmax = 0.0;
-    for (int j = 0; j < k; ++j) {
-      double mk = -__builtin_inf();
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-        if (!taken[t]) mk = fmax(mk, key[t]);
-      mk = wave_max_f64(mk);
-      // Lowest index holding the maximum (ballots are wave-uniform).
-      int win = -1;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const unsigned long long b = __builtin_amdgcn_ballot_w64(!taken[t] && key[t] == mk);
-        if (win < 0 && b) win = t * WAVE + __builtin_ctzll(b);
-      }
-      if (win < 0) {  // only NaN keys left: lowest index not yet taken
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const unsigned long long b = __builtin_amdgcn_ballot_w64(!taken[t]);
-          if (win < 0 && b) win = t * WAVE + __builtin_ctzll(b);
-        }
-      }
-      win = __builtin_amdgcn_readfirstlane(win);
-      const int wt = win >> 6, wl = win & 63;
-      double lw = 0.0;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        if (t == wt) {
-          lw = lg[t];
-          if (lane == wl) taken[t] = true;
-        }
-      }
-      lw = readlane_f64(lw, wl);
-      if (j == 0) lmax = lw;
-      if (lane == j) {
-        my_e = win;
-        my_l = lw;
-      }
+    if (j == 0) lmax = lw;
+    if (lane == j) {
+      my_e = win;
+      my_l = lw;
     }
-    // Weights, slot j in lane j (double).
-    const bool mine = lane < k;
-    double w;
-    if (a.routing == ROUTE_SOFTMAX) {
-      // softmax over all experts; with norm_topk_prob the full denominator
-      // cancels and only the selected terms remain.
-      const double num = mine ? exp(my_l - lmax) : 0.0;
-      double den;
-      if (norm) {
-        den = wave_sum_f64(num);
-      } else {
-        double s = 0.0;
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-          if (lane + WAVE * t < E) s += exp(lg[t] - lmax);
-        den = wave_sum_f64(s);
-      }
-      w = num / den;
+  }
+  // Weights in double, slot j in lane j.
+  const bool mine = lane < k;
+  double w;
+  if (a.routing == ROUTE_SOFTMAX) {
+    // softmax over all experts; with norm_topk_prob the full denominator
+    // cancels and only the selected terms remain.
+    const double num = mine ? exp(my_l - lmax) : 0.0;
+    double den;
+    if (a.flags & NORM_TOPK) {
+      den = wave_sum_f64(num);
     } else {
-      w = mine ? sigmoid_d(my_l) : 0.0;   // unbiased: the bias only selects
-      if (norm) w = w / wave_sum_f64(w);
+      double s = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * lane + i < E) s += exp(lr[4 * lane + i] - lmax);
+      den = wave_sum_f64(s);
     }
-    if (mine) {
+    w = num / den;
+  } else {
+    w = mine ? sigmoid_d(my_l) : 0.0;   // unbiased: the bias only selects
+    if (a.flags & NORM_TOPK) w = w / wave_sum_f64(w);
+  }
+  my_w = w;
+}
+
+// Every thread of the workgroup: routing of all m rows into L.  publish:
+// also write the workspace arrays (and the caller's idx/w outputs).
+__device__ __forceinline__ void route_select(const Args &a, RouteLDS &L, bool publish) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
+  const int E = a.E, k = a.K, m = a.m, te = m * k;
+  for (int r = wave; r < m; r += WPB) {
+    int e;
+    double w;
+    row_topk(a, r, e, w);
+    if (lane < k) {
       const float wf = (float)(w * (double)a.rsf);
       const int p = r * k + lane;
-      s_idx[p] = my_e;
-      a.topk_idx[p] = my_e;
-      a.topk_w[p] = wf;
-      if (a.idx_out) a.idx_out[p] = my_e;
-      if (a.w_out) a.w_out[p] = wf;
+      L.idx[p] = e;
+      L.w[p] = wf;
+      if (publish) {
+        a.topk_idx[p] = e;
+        a.topk_w[p] = wf;
+        if (a.idx_out) a.idx_out[p] = e;
+        if (a.w_out) a.w_out[p] = wf;
+      }
     }
-    if (lane == 0 && (a.flags & SHARED_GATED)) a.row_gate[r] = (float)sigmoid_d(lr[E]);
+    if (publish && lane == 0 && (a.flags & SHARED_GATED))
+      a.row_gate[r] = (float)sigmoid_d(a.logits[(size_t)r * (E + 1) + E]);
   }
+  for (int e = tid; e < E; e += THREADS) L.mask[e] = 0u;
   __syncthreads();
-
-  // Counting sort of the te = m*k pairs by expert, stable in pair order.  A
-  // row selects an expert at most once, so bit r of s_mask[e] says whether row
-  // r chose e; a pair's rank inside its expert is the number of earlier rows
-  // that chose the same expert.
-  const int te = m * k, tid = threadIdx.x;
-  for (int e = tid; e < E; e += THREADS) s_mask[e] = 0u;
+  // Stable counting sort by expert.  A row selects an expert at most once, so
+  // bit r of mask[e] says whether row r chose e, and a pair's rank inside its
+  // expert is the number of earlier rows that chose the same expert.
+  for (int p = tid; p < te; p += THREADS) atomicOr(&L.mask[L.idx[p]], 1u << (p / k));
   __syncthreads();
-  for (int p = tid; p < te; p += THREADS) atomicOr(&s_mask[s_idx[p]], 1u << (p / k));
-  __syncthreads();
-  const int cnt = tid < E ? __popc(s_mask[tid]) : 0;
-  int total;
-  const int excl = block_excl_scan(cnt, s_wave, &total);
-  int nact;
-  const int aexcl = block_excl_scan(cnt > 0 ? 1 : 0, s_wave, &nact);
-  if (tid < E) {
-    s_off[tid] = excl;
-    a.offsets[tid] = excl;
-    if (cnt > 0) a.active[aexcl] = tid;
-  }
-  if (tid == 0) {
-    s_off[E] = total;
-    a.offsets[E] = total;
-    a.active_count[0] = nact;
+  if (wave == 0) {
+    // Lane l: experts 4l..4l+3; wave-wide exclusive scans of counts and of
+    // "active" flags.
+    int cnt[4], act[4], ct = 0, at = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      cnt[i] = e < E ? __popc(L.mask[e]) : 0;
+      act[i] = cnt[i] > 0 ? 1 : 0;
+      ct += cnt[i];
+      at += act[i];
+    }
+    int ci = ct, ai = at;
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) {
+      const int oc = __shfl_up(ci, d, WAVE), oa = __shfl_up(ai, d, WAVE);
+      if (lane >= d) {
+        ci += oc;
+        ai += oa;
+      }
+    }
+    int co = ci - ct, ao = ai - at;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < E) {
+        L.off[e] = co;
+        if (publish) a.offsets[e] = co;
+        if (act[i]) {
+          L.active[ao] = e;
+          if (publish) a.active[ao] = e;
+        }
+      }
+      co += cnt[i];
+      ao += act[i];
+    }
+    if (lane == WAVE - 1) {
+      L.off[E] = ci;
+      L.nact = ai;
+      if (publish) {
+        a.offsets[E] = ci;
+        a.active_count[0] = ai;
+      }
+    }
   }
   __syncthreads();
   for (int p = tid; p < te; p += THREADS) {
-    const int e = s_idx[p], r = p / k;
-    const int pos = s_off[e] + __popc(s_mask[e] & ((1u << r) - 1u));
-    a.sorted_pair[pos] = p;
-    a.pair_to_perm[p] = pos;
+    const int e = L.idx[p], r = p / k;
+    const int pos = L.off[e] + __popc(L.mask[e] & ((1u << r) - 1u));
+    L.sorted[pos] = p;
+    if (publish) {
+      a.sorted_pair[pos] = p;
+      a.pair_to_perm[p] = pos;
+    }
   }
-}
-
-// One router item; the workgroup that finishes last runs the route tail.
-// FUSED: the tail then publishes SYNC_READY.
-template <int ACT, bool FUSED>
-__device__ __forceinline__ void router_item(const Args &a, int item) {
-  __shared__ unsigned s_ticket;
-  router_rows<ACT>(a, item);
-  release_agent();
   __syncthreads();
-  if (threadIdx.x == 0)
-    s_ticket = __hip_atomic_fetch_add(word(a.sync, SYNC_ROUTER), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (s_ticket != (unsigned)(a.n_router - 1)) return;
-  acquire_agent();
-  route_tail(a);
-  if (threadIdx.x == 0) *word(a.sync, SYNC_ROUTER) = 0u;  // every ticket is taken
-  if constexpr (FUSED) wg_signal(a.sync, SYNC_READY);
 }
 
 // ---------------------------------------------------------------- gate/up
 //
 // One wave: intermediate rows [i0, i0 + NI) of one expert (gate and up), for
-// the pairs p = pair(0..np-1) in passes of C; writes silu(g) * v.
-
+// pairs pair[0..np-1] (routed: row = pair / k, routing weight w[pair]) or
+// input rows 0..np-1 (shared), in passes of C; writes silu(g) * v at
+// dst[(off + c) * ld + i].
 template <int EF, int ACT, int C, int NI>
 __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, const void *uw,
                                              const void *gs, const void *us, const void *gb,
                                              const void *ub, int N, int i0, int off, int np,
-                                             bool routed, float *dst, int ld) {
+                                             const int *pairs, const float *pw, float *dst, int ld) {
   constexpr int RG = 2 * NI;
   const int H = a.H, k = a.K;
   const size_t xstride = (size_t)H * act_bytes(ACT);
   const char *x = reinterpret_cast<const char *>(a.x);
+  const bool routed = pairs != nullptr;
   Row<EF> rows[RG];
 #pragma unroll
   for (int t = 0; t < NI; ++t) {
@@ -877,17 +851,17 @@ __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, cons
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int q = c0 + min(c, nc - 1);
-      pair[c] = routed ? clamp_i(a.sorted_pair[off + q], 0, a.te - 1) : q;
+      pair[c] = routed ? pairs[q] : q;
       xrow[c] = x + (size_t)(routed ? pair[c] / k : q) * xstride;
     }
     float acc[RG][C];
     wave_rows_dot<EF, ACT, RG, C, WAVE, unroll_for<RG>()>(rows, xrow, H / Fmt<EF>::EPC, acc);
     if ((threadIdx.x & 63) == 0) {
+      const bool scale = routed && (a.flags & WEIGHT_BEFORE);
 #pragma unroll
       for (int c = 0; c < C; ++c) {
         if (c < nc) {
-          const bool scale = routed && (a.flags & WEIGHT_BEFORE);
-          const float w = scale ? a.topk_w[pair[c]] : 1.0f;
+          const float w = scale ? pw[pair[c]] : 1.0f;
 #pragma unroll
           for (int t = 0; t < NI; ++t) {
             if (i0 + t < N) {
@@ -905,37 +879,6 @@ __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, cons
   }
 }
 
-// Routed gate/up item: slot s = it / items_per_slot, its waves take row
-// groups (it % items_per_slot) * 4 + wave.
-template <int EF, int ACT, int C, bool FUSED>
-__device__ __forceinline__ void routed_gu_item(const Args &a, int it) {
-  constexpr int NI = gate_up_ni<EF>();
-  const int s = it / a.gu_items_per_slot, b = it - s * a.gu_items_per_slot;
-  if constexpr (FUSED) {
-    if (!wg_wait(a.sync, SYNC_READY, 1u)) return;
-  }
-  if (s >= active_slots(a)) return;
-  const int e = clamp_i(a.active[s], 0, a.E - 1);
-  const int off = clamp_i(a.offsets[e], 0, a.te);
-  const int np = clamp_i(a.offsets[e + 1], off, a.te) - off;
-  const int i0 = (b * WPB + (threadIdx.x >> 6)) * NI;
-  if (i0 < a.I)
-    gate_up_rows<EF, ACT, C, NI>(a, tbl(a.gw, e), tbl(a.uw, e), tbl(a.gs, e), tbl(a.us, e),
-                                 tbl(a.gb, e), tbl(a.ub, e), a.I, i0, off, np, true, a.act, a.I);
-  if constexpr (FUSED) wg_signal(a.sync, SYNC_SLOT0 + s);
-}
-
-// Shared-expert gate/up item (act-format weights, unscaled rows of x).
-template <int ACT, int C, bool FUSED>
-__device__ __forceinline__ void shared_gu_item(const Args &a, int it) {
-  constexpr int NI = gate_up_ni<ACT>();
-  const int i0 = (it * WPB + (threadIdx.x >> 6)) * NI;
-  if (i0 < a.Is)
-    gate_up_rows<ACT, ACT, C, NI>(a, a.sgw, a.suw, nullptr, nullptr, nullptr, nullptr, a.Is, i0, 0,
-                                  a.m, false, a.sact, a.Is);
-  if constexpr (FUSED) wg_signal(a.sync, SYNC_SHARED);
-}
-
 // --------------------------------------------------------- down + blend
 //
 // Down tile `tile`: output columns [h0, h0 + HT), HT = DOWN_RD * down_dq.
@@ -943,23 +886,17 @@ __device__ __forceinline__ void shared_gu_item(const Args &a, int it) {
 // row block q; waves take sub-units round-robin, y per pair goes to LDS, then
 //   out[r, h] = sum_j c_rj y[perm(r, j), h] + gamma_r ys[r, h]
 // in slot order.
-template <int EF, int ACT, int CR, int CS, int LPR, bool FUSED>
+template <int EF, int ACT, int CR, int CS, int LPR>
 __device__ __forceinline__ void down_item(const Args &a, int tile) {
   constexpr int GR = WAVE / LPR;                 // routed rows in parallel per wave
   constexpr int RGR = DOWN_RD / GR;              // routed rows per lane group
   static_assert(DOWN_RD % GR == 0, "down rows must split over lane groups");
   __shared__ float y_lds[MAX_PAIRS * MAX_DOWN_TILE];
   __shared__ float ys_lds[MAX_ROWS * MAX_DOWN_TILE];
-  __shared__ int s_fail;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int H = a.H, I = a.I, Is = a.Is, m = a.m;
   const int DQ = a.down_dq, HT = DOWN_RD * DQ, h0 = tile * HT;
-  if constexpr (FUSED) {
-    if (!wg_wait(a.sync, SYNC_READY, 1u)) return;
-  }
-  if (threadIdx.x == 0) s_fail = 0;
-  __syncthreads();
-  const int nact = active_slots(a);
+  const int nact = clamp_i(a.active_count[0], 0, a.cap);
   const bool shared = (a.flags & SHARED) != 0;
   const int units = nact + (shared ? 1 : 0);
 
@@ -967,12 +904,6 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
     const int u = su / DQ, q = su - u * DQ;
     const int hb = h0 + q * DOWN_RD;             // first column of this row block
     if (u < nact) {
-      if constexpr (FUSED) {
-        if (!wave_wait(a.sync, SYNC_SLOT0 + u, (unsigned)a.gu_items_per_slot)) {
-          if (lane == 0) s_fail = 1;
-          continue;
-        }
-      }
       const int e = clamp_i(a.active[u], 0, a.E - 1);
       const int off = clamp_i(a.offsets[e], 0, a.te);
       const int np = clamp_i(a.offsets[e + 1], off, a.te) - off;
@@ -998,12 +929,6 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
         }
       }
     } else {
-      if constexpr (FUSED) {
-        if (!wave_wait(a.sync, SYNC_SHARED, (unsigned)a.n_shared_gu)) {
-          if (lane == 0) s_fail = 1;
-          continue;
-        }
-      }
       Row<ACT> rows[DOWN_RD];
 #pragma unroll
       for (int t = 0; t < DOWN_RD; ++t) rows[t] = make_row<ACT>(a.sdw, nullptr, nullptr, Is, min(hb + t, H - 1));
@@ -1027,101 +952,71 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   }
   __syncthreads();
 
-  if (s_fail == 0) {
-    const bool before = (a.flags & WEIGHT_BEFORE) != 0;
-    const bool gated = (a.flags & SHARED_GATED) != 0;
-    const bool out_f32 = (a.flags & OUT_F32) != 0 || ACT == F32;
-    const int k = a.K;
-    for (int t = threadIdx.x; t < m * HT; t += THREADS) {
-      const int r = t / HT, hl = t - r * HT, h = h0 + hl;
-      if (h >= H) continue;
-      float o = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int p = r * k + j;
-        const float c = before ? 1.0f : a.topk_w[p];
-        o = __builtin_fmaf(c, y_lds[clamp_i(a.pair_to_perm[p], 0, a.te - 1) * HT + hl], o);
-      }
-      if (shared) o = __builtin_fmaf(gated ? a.row_gate[r] : 1.0f, ys_lds[r * HT + hl], o);
-      if (out_f32)
-        reinterpret_cast<float *>(a.out)[(size_t)r * H + h] = o;
-      else
-        reinterpret_cast<uint16_t *>(a.out)[(size_t)r * H + h] = f32_to_bf16(o);
+  const bool before = (a.flags & WEIGHT_BEFORE) != 0;
+  const bool gated = (a.flags & SHARED_GATED) != 0;
+  const bool out_f32 = (a.flags & OUT_F32) != 0 || ACT == F32;
+  const int k = a.K;
+  for (int t = threadIdx.x; t < m * HT; t += THREADS) {
+    const int r = t / HT, hl = t - r * HT, h = h0 + hl;
+    if (h >= H) continue;
+    float o = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int p = r * k + j;
+      const float c = before ? 1.0f : a.topk_w[p];
+      o = __builtin_fmaf(c, y_lds[clamp_i(a.pair_to_perm[p], 0, a.te - 1) * HT + hl], o);
     }
+    if (shared) o = __builtin_fmaf(gated ? a.row_gate[r] : 1.0f, ys_lds[r * HT + hl], o);
+    if (out_f32)
+      reinterpret_cast<float *>(a.out)[(size_t)r * H + h] = o;
+    else
+      reinterpret_cast<uint16_t *>(a.out)[(size_t)r * H + h] = f32_to_bf16(o);
   }
-  __syncthreads();  // LDS is reused by the next item
 }
 
 // ------------------------------------------------------------------ kernels
 
-// The whole layer in one persistent launch (items claimed in queue order).
-// NOT LAUNCHED: on MI355X its first launch did not finish (twice, the second
-// time with every wait bounded in wall-clock time); the cause is not yet
-// identified, so the host refuses this arrangement and nothing instantiates
-// it.
-template <int EF, int ACT, int CR, int CS, int LPR>
-__global__ __launch_bounds__(THREADS) void fused_kernel(Args a) {
-  __shared__ int s_item;
-  for (;;) {
-    if (threadIdx.x == 0) s_item = (int)atomicAdd(word(a.sync, SYNC_NEXT), 1u);
-    __syncthreads();
-    int item = s_item;
-    __syncthreads();
-    if (item >= a.n_items) break;
-    if (item < a.n_router) {
-      router_item<ACT, true>(a, item);
-      continue;
-    }
-    item -= a.n_router;
-    if (item < a.n_shared_gu) {
-      shared_gu_item<ACT, CS, true>(a, item);
-      continue;
-    }
-    item -= a.n_shared_gu;
-    if (item < a.n_routed_gu) {
-      routed_gu_item<EF, ACT, CR, true>(a, item);
-      continue;
-    }
-    item -= a.n_routed_gu;
-    down_item<EF, ACT, CR, CS, LPR, true>(a, item);
-  }
-  // The last workgroup out resets the completion words for the next call
-  // (SYNC_ERR stays as it is).
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned done =
-        __hip_atomic_fetch_add(word(a.sync, SYNC_EXIT), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == gridDim.x - 1) {
-      *word(a.sync, SYNC_NEXT) = 0u;
-      *word(a.sync, SYNC_ROUTER) = 0u;
-      *word(a.sync, SYNC_READY) = 0u;
-      *word(a.sync, SYNC_EXIT) = 0u;
-      *word(a.sync, SYNC_SHARED) = 0u;
-      for (int s = 0; s < a.cap; ++s) *word(a.sync, SYNC_SLOT0 + s) = 0u;
-      release_agent();
-    }
-  }
-}
-
-// The items as three ordinary kernels.  The shared expert's gate/up does not
-// depend on routing, so its items run beside the router items in the first
-// launch.
+// Launch 1: router units (4 per workgroup, one per wave), then the shared
+// expert's gate/up items -- these need no routing, so they stream meanwhile.
 template <int ACT, int CS>
 __global__ __launch_bounds__(THREADS) void route_kernel(Args a) {
   const int item = blockIdx.x;
-  if (item < a.n_router)
-    router_item<ACT, false>(a, item);
-  else
-    shared_gu_item<ACT, CS, false>(a, item - a.n_router);
+  if (item < a.n_router) {
+    router_unit<ACT>(a, item * WPB + (threadIdx.x >> 6));
+    return;
+  }
+  constexpr int NI = gate_up_ni<ACT>();
+  const int i0 = ((item - a.n_router) * WPB + (threadIdx.x >> 6)) * NI;
+  if (i0 < a.Is)
+    gate_up_rows<ACT, ACT, CS, NI>(a, a.sgw, a.suw, nullptr, nullptr, nullptr, nullptr, a.Is, i0, 0,
+                                   a.m, nullptr, nullptr, a.sact, a.Is);
 }
 
+// Launch 2: every workgroup first rebuilds the routing from the logits
+// (block 0 publishes it), then takes the items (active slot s, row block b)
+// blockIdx, blockIdx + gridDim, ... of the nact * items_per_slot that exist;
+// its waves take row groups b * 4 + wave of slot s.
 template <int EF, int ACT, int CR, int CS>
 __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
-  routed_gu_item<EF, ACT, CR, false>(a, blockIdx.x);
+  constexpr int NI = gate_up_ni<EF>();
+  __shared__ RouteLDS L;
+  route_select(a, L, blockIdx.x == 0);
+  const int n = L.nact * a.gu_items_per_slot;
+  for (int it = blockIdx.x; it < n; it += gridDim.x) {
+    const int s = it / a.gu_items_per_slot, b = it - s * a.gu_items_per_slot;
+    const int e = clamp_i(L.active[s], 0, a.E - 1);
+    const int off = L.off[e], np = L.off[e + 1] - off;
+    const int i0 = (b * WPB + (threadIdx.x >> 6)) * NI;
+    if (i0 < a.I)
+      gate_up_rows<EF, ACT, CR, NI>(a, tbl(a.gw, e), tbl(a.uw, e), tbl(a.gs, e), tbl(a.us, e),
+                                    tbl(a.gb, e), tbl(a.ub, e), a.I, i0, off, np, L.sorted + off,
+                                    L.w, a.act, a.I);
+  }
 }
 
+// Launch 3: down tiles with the blend.
 template <int EF, int ACT, int CR, int CS, int LPR>
 __global__ __launch_bounds__(THREADS) void down_blend_kernel(Args a) {
-  down_item<EF, ACT, CR, CS, LPR, false>(a, blockIdx.x);
+  down_item<EF, ACT, CR, CS, LPR>(a, blockIdx.x);
 }
 
 }  // namespace moe

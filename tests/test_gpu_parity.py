@@ -44,17 +44,13 @@ def rms(a):
     return float(np.sqrt(np.mean(np.square(a))))
 
 
-SYNC_STRIDE = 32                 # one completion word per 128 bytes
-SYNC_WORDS = 272 * SYNC_STRIDE
-SYNC_ERR = 5 * SYNC_STRIDE       # the expired-wait flag
+SYNC_WORDS = 512                 # reserved completion words of the workspace
 
 
 def check_sync_words(dl):
-    """After a call every completion word is back to zero (and no bounded
-    wait expired)."""
+    """The reserved completion words are untouched (zero) after a call."""
     words = dl.ws_view("sync", torch.int32, SYNC_WORDS).cpu().numpy()
-    assert words[SYNC_ERR] == 0, "a bounded wait expired inside the kernel"
-    assert not words.any(), f"completion words not reset: {np.nonzero(words)[0][:8]}"
+    assert not words.any(), f"completion words not zero: {np.nonzero(words)[0][:8]}"
 
 
 def run(dl: DeviceLayer, x_np: np.ndarray, m: int):
