@@ -13,9 +13,10 @@ Calls rotate over R device copies of the layer, each with its own input rows
 (so its own expert selection), with R chosen so that at least 600 MB of other
 weights stream between two uses of a copy: no call finds its weights in the
 256 MB Infinity Cache or the L2.  The headline is HIP-graph replay (decode
-steps run graph-captured); stream-launched numbers are reported too, and the
-per-kernel HIP-event timing of that stream loop gives the roofline of the
-dominant kernel.
+steps run graph-captured); stream-launched numbers are reported too.  In that
+stream loop every kernel is launched with its own start/stop HIP events
+(hipExtLaunchKernelGGL), whose average for the dominant kernel gives the
+roofline entry.
 
 Effective bandwidth counts ALGORITHMIC bytes: the experts each call actually
 selected (from a one-time readback of the exported indices), router, bias,
@@ -39,7 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "µs per MoE decode layer and effective HBM GB/s (% of peak) at m=1,8"
 PEAK_HBM_GBPS = 8000.0
 DEFAULT_WORKLOAD = "qwen3_30b_a3b_bf16"
-KERNEL_SRC = os.path.join(ROOT, "mixture_experts_decode_amd", "csrc", "moe_kernels.hpp")
+KERNEL_SRC_DIR = os.path.join(ROOT, "mixture_experts_decode_amd", "csrc")
 COUNTERS = os.path.join(ROOT, "profiles", "gate_up_counters.json")
 
 
@@ -54,8 +55,6 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--all", action="store_true", help="one line per workload and m (analysis)")
-    p.add_argument("--copy-mb", type=int, default=0,
-                   help="also run a plain device copy of this size (counter calibration)")
     return p.parse_args()
 
 
@@ -144,30 +143,38 @@ def time_workload(name: str, m: int, steps: int, warmup: int, extra_rows=(), wan
         distinct = sum(b["distinct"] for b in bytes_c) / R
 
         stream = torch.cuda.Stream()
-        # Graph per copy.
-        graphs = []
-        with torch.cuda.stream(stream):
-            for c in range(R):
-                g = torch.cuda.CUDAGraph()
+        # One graph holds R consecutive forwards (one per weight copy), as a
+        # decode step's graph holds consecutive layers; a second graph holds
+        # the remainder, so that exactly `steps` forwards are timed.
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
                 with torch.cuda.graph(g, stream=stream):
-                    dl.forward(xs[c], mm, outs[c], copy=c, stream=stream.cuda_stream)
-                graphs.append(g)
+                    for c in range(n):
+                        dl.forward(xs[c], mm, outs[c], copy=c, stream=stream.cuda_stream)
+            return g
+
+        g_full = capture(R)
+        rem = steps % R
+        g_rem = capture(rem) if rem else None
         torch.cuda.synchronize()
-        for i in range(warmup):
-            graphs[i % R].replay()
+        for _ in range(max(1, warmup // R)):
+            g_full.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            graphs[i % R].replay()
+        for _ in range(steps // R):
+            g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
         torch.cuda.synchronize()
         t_graph = (time.perf_counter() - t0) / steps
 
-        # Stream-launched, with HIP events around every kernel.
+        # Stream-launched; every kernel carries its own start/stop HIP events.
         nst = md.moe_decode_num_stages(dl.plan)
         evs = []
         with torch.cuda.stream(stream):
             for _ in range(steps):
-                row = [torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+                row = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)]
                 for e in row:
                     e.record(stream)          # materialise the hipEvent_t
                 evs.append(row)
@@ -185,9 +192,9 @@ def time_workload(name: str, m: int, steps: int, warmup: int, extra_rows=(), wan
         stage_ms = [0.0] * nst
         for row in evs:
             for s in range(nst):
-                stage_ms[s] += row[s].elapsed_time(row[s + 1])
+                stage_ms[s] += row[2 * s].elapsed_time(row[2 * s + 1])
         stage_us = {md.moe_decode_stage_name(dl.plan, s): 1e3 * stage_ms[s] / steps for s in range(nst)}
-        del graphs
+        del g_full, g_rem
         results[mm] = {
             "us_graph": t_graph * 1e6, "us_stream": t_stream * 1e6, "bytes": B,
             "bytes_gate_up": B_gu, "distinct_experts": distinct, "copies": R,
@@ -218,28 +225,60 @@ def cpu_baseline(layer, m: int, seconds: float):
             "us_per_layer": round(dt * 1e6, 1)}
 
 
+def kernel_source_sha256() -> str:
+    """Hash of every file under csrc/ (name and contents, sorted by name)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
+        h.update(name.encode())
+        with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_entry():
-    """HBM bytes per gate_up launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
+    """Calibrated HBM bytes per gate_up launch (rocprofv3 FETCH_SIZE and
+    WRITE_SIZE, scaled by what they read for the plain copy kernel) from the
+    committed counter summary, if it was taken on the current kernel sources;
+    else None."""
     try:
         data = json.load(open(COUNTERS))
     except (OSError, ValueError):
         return None
-    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if data.get("kernel_source_sha256") != src:
+    if data.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     return data.get("traffic_bytes_per_launch")
 
 
-def copy_calibration(mb: int):
+def stream_read_gbps(gib: int = 4) -> dict:
+    """Achievable HBM bandwidth with the library's plain streaming kernels:
+    a read of a 4 GiB buffer (moe_decode_bench_read) and a 1 GiB copy
+    (moe_decode_bench_copy, 2 GiB moved).  The copy is also the known-size
+    reference for the HBM byte counters (one launch reads and writes 1 GiB)."""
     import torch
-    n = mb * (1 << 20) // 4
-    a = torch.ones(n, dtype=torch.float32, device="cuda")
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": n * 4}), flush=True)
+    from mixture_experts_decode_amd import moe_decode as md
+
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    half = 1 << 30
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n=10):
+        for _ in range(2):
+            fn()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n / 1e3
+
+    t_read = timed(lambda: md.moe_decode_bench_read(buf.data_ptr(), nbytes, sink.data_ptr(), st))
+    t_copy = timed(lambda: md.moe_decode_bench_copy(buf.data_ptr(), buf.data_ptr() + 2 * half, half, st))
+    del buf
+    torch.cuda.empty_cache()
+    return {"read": nbytes / t_read / 1e9, "copy": 2 * half / t_copy / 1e9}
 
 
 def main():
@@ -255,9 +294,6 @@ def main():
         sys.exit(1)
     from mixture_experts_decode_amd import synth
 
-    if args.copy_mb:
-        copy_calibration(args.copy_mb)
-
     if args.all:
         for name, spec in synth.WORKLOADS.items():
             layer, res = time_workload(name, spec.rows[0], args.steps, args.warmup, spec.rows[1:])
@@ -272,6 +308,8 @@ def main():
     spec = synth.WORKLOADS[args.workload]
     layer, res = time_workload(args.workload, args.rows, args.steps, args.warmup, extra)
     head = res[args.rows]
+    sol = stream_read_gbps()
+    read_gbps = sol["read"]
     gu_us = head["stage_us"]["gate_up"]
     achieved = head["bytes_gate_up"] / (gu_us * 1e-6) / 1e9
     cpu = None if args.no_cpu_baseline else cpu_baseline(layer, args.rows, args.cpu_seconds)
@@ -281,6 +319,7 @@ def main():
             "us_per_layer_graph": round(r["us_graph"], 2), "us_per_layer_stream": round(r["us_stream"], 2),
             "gbps_graph": round(r["gbps_graph"], 1), "gbps_stream": round(r["gbps_stream"], 1),
             "pct_of_peak_graph": round(100 * r["gbps_graph"] / PEAK_HBM_GBPS, 1),
+            "pct_of_stream_read": round(100 * r["gbps_graph"] / read_gbps, 1),
             "bytes_per_call": int(r["bytes"]), "distinct_experts": r["distinct_experts"],
             "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
             "copies_rotated": r["copies"],
@@ -303,7 +342,7 @@ def main():
                         f"top-{spec.top_k} I={spec.inter} experts={spec.expert_fmt} "
                         f"routing={spec.routing}" + (f" shared Is={spec.shared_inter}" if spec.shared else ""),
             "rows": args.rows,
-            "timing": "HIP graph replay, weights rotated over device copies (cold caches)",
+            "timing": "HIP graph of consecutive forwards over rotated weight copies (cold caches)",
         },
         "roofline": {
             "bound": "hbm", "kernel": "gate_up", "achieved": round(achieved, 1),
@@ -314,6 +353,8 @@ def main():
         },
         "cpu_baseline": cpu,
         "detail": detail,
+        "stream_read_gbps": round(read_gbps, 1),
+        "stream_copy_gbps": round(sol["copy"], 1),
     }
     print(json.dumps(line), flush=True)
 

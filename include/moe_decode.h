@@ -182,10 +182,13 @@ moe_status moe_decode_forward(const moe_decode_plan_t *plan, const moe_decode_we
 int32_t moe_decode_num_stages(const moe_decode_plan_t *plan);
 const char *moe_decode_stage_name(const moe_decode_plan_t *plan, int32_t i);
 
-/* As moe_decode_forward, and records events[i] (hipEvent_t) on `stream`
- * right before stage i is launched and events[num_stages] after the last:
- * the per-stage timing hook used by the bench.  n_events must equal
- * moe_decode_num_stages(plan) + 1. */
+/* As moe_decode_forward, with per-stage timing: stage i is launched with
+ * hipExtLaunchKernelGGL so that events[2i] and events[2i+1] (hipEvent_t,
+ * created with timing enabled) take that kernel's own start and end
+ * timestamps; hipEventElapsedTime(events[2i], events[2i+1]) is then the
+ * kernel's duration without launch gaps.  n_events must equal
+ * 2 * moe_decode_num_stages(plan); no entry may be NULL.  Not for stream
+ * capture (use moe_decode_forward there). */
 moe_status moe_decode_forward_timed(const moe_decode_plan_t *plan, const moe_decode_weights *w,
                                     const void *x, int32_t m, void *out, int32_t *idx_out,
                                     float *w_out, void *workspace, size_t workspace_bytes,
@@ -196,6 +199,17 @@ const char *moe_decode_last_error(void);
 
 /* Library version string. */
 const char *moe_decode_version(void);
+
+/* Measurement utilities (not part of the layer).  Plain streaming kernels
+ * with the layer's 16-byte-per-lane access pattern, used as known-size
+ * references for HBM byte counters and for achievable bandwidth.
+ *   moe_decode_bench_copy  dst[0..bytes) = src[0..bytes)   (device buffers)
+ *   moe_decode_bench_read  reads src[0..bytes) once; sink is a device uint32
+ *                          that is (practically) never written
+ * bytes must be a multiple of 16 and the buffers 16-byte aligned; launched on
+ * `stream`; MOE_EINVAL otherwise. */
+moe_status moe_decode_bench_copy(const void *src, void *dst, size_t bytes, void *stream);
+moe_status moe_decode_bench_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -228,7 +228,7 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   if (workspace_bytes < L.total)
     return fail(MOE_EWORKSPACE, "workspace has %zu bytes, the plan needs %zu", workspace_bytes, L.total);
   const int nst = num_stages(plan->variant);
-  if (events && n_events != nst + 1) return fail(MOE_EINVAL, "n_events must be %d", nst + 1);
+  if (events && n_events != 2 * nst) return fail(MOE_EINVAL, "n_events must be %d", 2 * nst);
   moe_status st = check_weights(d, w);
   if (st != MOE_OK) return st;
 
@@ -299,22 +299,16 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  auto rec = [&](int i) -> hipError_t {
-    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
-  };
+  auto ev = [&](int i) -> hipEvent_t { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
   hipError_t e;
-  if ((e = rec(0)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if ((e = moe::launch_route(d.act_fmt, cs, a, a.n_router + a.n_shared_gu, s)) != hipSuccess)
+  if ((e = moe::launch_route(d.act_fmt, cs, a, a.n_router + a.n_shared_gu, s, ev(0), ev(1))) != hipSuccess)
     return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
-  if ((e = rec(1)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
   // gate_up: a grid-stride launch; every workgroup pays one routing prologue.
   const int gu_blocks = a.n_routed_gu < kGateUpMaxBlocks ? a.n_routed_gu : kGateUpMaxBlocks;
-  if ((e = plan->gate_up[m](a, gu_blocks, s)) != hipSuccess)
+  if ((e = plan->gate_up[m](a, gu_blocks, s, ev(2), ev(3))) != hipSuccess)
     return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
-  if ((e = rec(2)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if ((e = kv.down_blend(a, a.n_down, s)) != hipSuccess)
+  if ((e = kv.down_blend(a, a.n_down, s, ev(4), ev(5))) != hipSuccess)
     return fail(MOE_EHIP, "down_blend launch: %s", hipGetErrorString(e));
-  if ((e = rec(3)) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -396,5 +390,21 @@ const char *moe_decode_stage_name(const moe_decode_plan_t *plan, int32_t i) {
 const char *moe_decode_last_error(void) { return g_err.c_str(); }
 
 const char *moe_decode_version(void) { return "moe_decode 0.1 (gfx950)"; }
+
+moe_status moe_decode_bench_copy(const void *src, void *dst, size_t bytes, void *stream) {
+  if (!src || !dst || bytes % 16 || !aligned(src, 16) || !aligned(dst, 16))
+    return fail(MOE_EINVAL, "bench_copy needs 16-byte aligned buffers and a multiple of 16 bytes");
+  hipError_t e = moe::launch_bench_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_EHIP, "bench_copy launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+moe_status moe_decode_bench_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+  if (!src || !sink || bytes % 16 || !aligned(src, 16))
+    return fail(MOE_EINVAL, "bench_read needs a 16-byte aligned buffer, a multiple of 16 bytes and a sink");
+  hipError_t e = moe::launch_bench_read(src, bytes, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_EHIP, "bench_read launch: %s", hipGetErrorString(e));
+  return ok();
+}
 
 }  // extern "C"

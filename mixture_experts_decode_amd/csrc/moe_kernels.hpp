@@ -187,6 +187,39 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_u32(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Wave maximum of an unsigned value, wave-uniform result.
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+  v = max(v, dpp_u32<DPP_XOR1>(v));
+  v = max(v, dpp_u32<DPP_XOR2>(v));
+  v = max(v, dpp_u32<DPP_HALF_MIRROR>(v));
+  v = max(v, dpp_u32<DPP_MIRROR>(v));
+  const unsigned a = max((unsigned)__builtin_amdgcn_readlane((int)v, 0), (unsigned)__builtin_amdgcn_readlane((int)v, 16));
+  const unsigned b = max((unsigned)__builtin_amdgcn_readlane((int)v, 32), (unsigned)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
+}
+
+// Exclusive prefix sum over the wave's lanes of v (0 <= v < 2^BITS), from
+// one ballot per bit plane and the count of set lanes below this one.  The
+// wave total goes to *total.
+template <int BITS>
+__device__ __forceinline__ int wave_excl_scan(unsigned v, int *total) {
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
+    const unsigned long long m = __builtin_amdgcn_ballot_w64((v >> b) & 1u);
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+    pre += below << b;
+    tot += __builtin_popcountll(m) << b;
+  }
+  *total = tot;
+  return pre;
+}
+
 // Wave maximum (NaN-ignoring, like fmax).
 __device__ __forceinline__ double wave_max_f64(double v) {
   v = fmax(v, dpp_f64<DPP_XOR1>(v));
@@ -639,64 +672,77 @@ struct RouteLDS {
   int nact;
 };
 
+// Order-preserving image of a double as an unsigned 64-bit integer.
+__device__ __forceinline__ unsigned long long order_key(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
 // Compare-exchange for (key descending, index ascending).
-__device__ __forceinline__ void cx(double &ka, int &ia, double &la, double &kb, int &ib, double &lb) {
+__device__ __forceinline__ void cx(unsigned long long &ka, int &ia, double &la, unsigned long long &kb,
+                                   int &ib, double &lb) {
   const bool sw = kb > ka || (kb == ka && ib < ia);
   if (sw) {
-    const double tk = ka, tl = la;
+    const unsigned long long tk = ka;
+    const double tl = la;
     const int ti = ia;
     ka = kb; la = lb; ia = ib;
     kb = tk; lb = tl; ib = ti;
   }
 }
 
-// Top-k of row r by one wave.  Lane l holds experts 4l..4l+3 (E <= 256),
-// sorts them locally by (key desc, index asc), and each round the wave takes
-// the best head: its key by a DPP max, its lane by a ballot -- the lowest
-// lane holding the maximum also holds the lowest index, because lanes own
-// ascending index ranges.  Slot j's expert and weight end up in lane j.
+// Top-k of row r by one wave.  Keys are compared as order-preserving 64-bit
+// integers, which is exactly the order of the double keys.  Lane l holds
+// experts 4l..4l+3 (E <= 256), sorts them locally by (key desc, index asc),
+// and each round the wave takes the best head: the high 32 key bits by an
+// integer DPP max (the low 32 only when heads tie on the high half), the lane
+// by a ballot -- the lowest lane holding the maximum also holds the lowest
+// index, because lanes own ascending index ranges.  Slot j's expert and
+// weight end up in lane j.
 __device__ __forceinline__ void row_topk(const Args &a, int r, int &my_e, double &my_w) {
   const int lane = threadIdx.x & 63, E = a.E, k = a.K;
   const double *lr = a.logits + (size_t)r * (E + 1);
-  double key[4], lg[4];
+  unsigned long long key[4];
+  double lg[4];
   int id[4];
-  bool ok[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = 4 * lane + i;
-    ok[i] = e < E;
-    id[i] = e;
-    lg[i] = ok[i] ? lr[e] : 0.0;
-    key[i] = lg[i];
-    if (ok[i] && a.routing == ROUTE_SIGMOID_BIAS) key[i] = sigmoid_d(lg[i]) + (double)a.ebias[e];
-    if (!ok[i]) key[i] = -__builtin_inf();
+    const bool ok = e < E;
+    lg[i] = ok ? lr[e] : 0.0;
+    double kd = lg[i];
+    if (ok && a.routing == ROUTE_SIGMOID_BIAS) kd = sigmoid_d(lg[i]) + (double)a.ebias[e];
+    key[i] = ok ? order_key(kd) : 0ull;        // below every real key
+    id[i] = ok ? e : 0x7FFFFFFF - (3 - i);     // and after them
   }
-  // Entries past E sort last: give them the largest indices.
+  int nvalid = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (!ok[i]) id[i] = 0x7FFFFFFF - (3 - i);
+  for (int i = 0; i < 4; ++i) nvalid += (4 * lane + i < E) ? 1 : 0;
   cx(key[0], id[0], lg[0], key[1], id[1], lg[1]);
   cx(key[2], id[2], lg[2], key[3], id[3], lg[3]);
   cx(key[0], id[0], lg[0], key[2], id[2], lg[2]);
   cx(key[1], id[1], lg[1], key[3], id[3], lg[3]);
   cx(key[1], id[1], lg[1], key[2], id[2], lg[2]);
   int left = 0;  // entries of this lane already taken
-  int nvalid = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) nvalid += (id[i] < E) ? 1 : 0;
   double lmax = 0.0, my_l = 0.0;
   my_e = 0;
   for (int j = 0; j < k; ++j) {
     const bool have = left < nvalid;
-    const double head = have ? key[0] : -__builtin_inf();
-    const double mx = wave_max_f64(head);
-    unsigned long long b = __builtin_amdgcn_ballot_w64(have && head == mx);
-    if (b == 0) b = __builtin_amdgcn_ballot_w64(have);   // only NaN keys left
+    const unsigned hh = have ? (unsigned)(key[0] >> 32) : 0u;
+    const unsigned mh = wave_max_u32(hh);
+    bool cand = have && hh == mh;
+    unsigned long long b = __builtin_amdgcn_ballot_w64(cand);
+    if (__builtin_popcountll(b) > 1) {  // tie on the high half: settle on the low half
+      const unsigned hl = cand ? (unsigned)key[0] : 0u;
+      const unsigned ml = wave_max_u32(hl);
+      cand = cand && hl == ml;
+      b = __builtin_amdgcn_ballot_w64(cand);
+    }
     const int wl = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(b));
     const int win = __builtin_amdgcn_readlane(id[0], wl);
     const double lw = readlane_f64(lg[0], wl);
     if (lane == wl) {  // pop the head
-      key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = -__builtin_inf();
+      key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0ull;
       lg[0] = lg[1]; lg[1] = lg[2]; lg[2] = lg[3];
       id[0] = id[1]; id[1] = id[2]; id[2] = id[3];
       ++left;
@@ -775,16 +821,10 @@ __device__ __forceinline__ void route_select(const Args &a, RouteLDS &L, bool pu
       ct += cnt[i];
       at += act[i];
     }
-    int ci = ct, ai = at;
-#pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) {
-      const int oc = __shfl_up(ci, d, WAVE), oa = __shfl_up(ai, d, WAVE);
-      if (lane >= d) {
-        ci += oc;
-        ai += oa;
-      }
-    }
-    int co = ci - ct, ao = ai - at;
+    int ci, ai;                          // wave totals
+    const int cpre = wave_excl_scan<8>((unsigned)ct, &ci);   // ct <= 4 * 32
+    const int apre = wave_excl_scan<3>((unsigned)at, &ai);   // at <= 4
+    int co = cpre, ao = apre;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;

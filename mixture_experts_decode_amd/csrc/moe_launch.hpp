@@ -4,13 +4,27 @@
 // its format pair needs and exposes them through a FormatKernels table; the
 // host picks a (CR, CS, LPR) present in the table.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 namespace moe {
 
 struct Args;
 
-typedef hipError_t (*launch_fn)(const Args &a, int blocks, hipStream_t st);
+// start/stop: events that take the kernel's own start and end timestamps
+// (hipExtLaunchKernelGGL), or null.
+typedef hipError_t (*launch_fn)(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop);
+
+// Launches kernel K with the layer's block size, timed when start/stop are given.
+template <typename K, typename... P>
+inline hipError_t launch_timed(K kernel, int blocks, int threads, hipStream_t st, hipEvent_t start, hipEvent_t stop,
+                               P... p) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, dim3(blocks), dim3(threads), 0, st, start, stop, 0u, p...);
+  else
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(threads), 0, st, p...);
+  return hipGetLastError();
+}
 
 // (CR, CS): input vectors per pass for routed and shared rows; LPR: lanes
 // per down row.
@@ -30,8 +44,11 @@ struct FormatKernels {
 };
 
 // First launch: router items plus the shared expert's gate/up items.
-hipError_t launch_route(int act, int cs, const Args &a, int blocks, hipStream_t st);
+hipError_t launch_route(int act, int cs, const Args &a, int blocks, hipStream_t st, hipEvent_t start,
+                        hipEvent_t stop);
 hipError_t launch_clear_sync(unsigned *sync, int n, hipStream_t st);
+hipError_t launch_bench_copy(const void *src, void *dst, size_t bytes, hipStream_t st);
+hipError_t launch_bench_read(const void *src, size_t bytes, unsigned *sink, hipStream_t st);
 
 const FormatKernels &kernels_f32_f32();
 const FormatKernels &kernels_f32_bf16();
@@ -44,14 +61,12 @@ const FormatKernels &kernels_bf16_mxfp4();
 
 #ifdef MOE_KERNELS_HPP_INCLUDED
 template <int EF, int ACT, int CR, int CS, int LPR>
-hipError_t launch_down_blend_t(const Args &a, int blocks, hipStream_t st) {
-  hipLaunchKernelGGL((down_blend_kernel<EF, ACT, CR, CS, LPR>), dim3(blocks), dim3(THREADS), 0, st, a);
-  return hipGetLastError();
+hipError_t launch_down_blend_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  return launch_timed(down_blend_kernel<EF, ACT, CR, CS, LPR>, blocks, THREADS, st, start, stop, a);
 }
 template <int EF, int ACT, int CR, int CS>
-hipError_t launch_gate_up_t(const Args &a, int blocks, hipStream_t st) {
-  hipLaunchKernelGGL((gate_up_kernel<EF, ACT, CR, CS>), dim3(blocks), dim3(THREADS), 0, st, a);
-  return hipGetLastError();
+hipError_t launch_gate_up_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  return launch_timed(gate_up_kernel<EF, ACT, CR, CS>, blocks, THREADS, st, start, stop, a);
 }
 #endif
 

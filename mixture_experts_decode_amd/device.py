@@ -6,6 +6,7 @@ itself is ``moe_decode.moe_decode_forward`` (libmoe_decode.so).
 """
 from __future__ import annotations
 
+import weakref
 from typing import Optional
 
 import numpy as np
@@ -98,6 +99,9 @@ class DeviceLayer:
         self.max_rows = max_rows or spec.max_rows
         self.desc = desc_of(spec, self.max_rows, out_f32)
         self.plan, self.ws_bytes = md.moe_decode_plan(self.desc)
+        # Destroyed with the object, or at interpreter exit before the
+        # binding module is torn down.
+        self._release = weakref.finalize(self, md.lib().moe_decode_plan_destroy, self.plan)
         self.layout = md.moe_decode_workspace_layout(self.plan)
         base = {
             "router": to_device(layer.router, device), "bias": to_device(layer.expert_bias, device),
@@ -118,12 +122,6 @@ class DeviceLayer:
         assert self.workspace.data_ptr() % 256 == 0
         md.moe_decode_workspace_init(self.plan, self.workspace.data_ptr(), self.ws_bytes,
                                      torch.cuda.current_stream(self.device).cuda_stream)
-
-    def __del__(self):
-        plan = getattr(self, "plan", None)
-        if plan:
-            md.moe_decode_plan_destroy(plan)
-            self.plan = None
 
     @property
     def weights(self) -> md.moe_decode_weights:

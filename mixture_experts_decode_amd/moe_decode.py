@@ -95,6 +95,10 @@ def lib() -> C.CDLL:
         L.moe_decode_last_error.argtypes = []
         L.moe_decode_version.restype = C.c_char_p
         L.moe_decode_version.argtypes = []
+        L.moe_decode_bench_copy.restype = st
+        L.moe_decode_bench_copy.argtypes = [vp, vp, C.c_size_t, vp]
+        L.moe_decode_bench_read.restype = st
+        L.moe_decode_bench_read.argtypes = [vp, C.c_size_t, vp, vp]
         _lib = L
     return _lib
 
@@ -162,3 +166,11 @@ def moe_decode_num_stages(plan) -> int:
 
 def moe_decode_stage_name(plan, i: int) -> str:
     return lib().moe_decode_stage_name(plan, i).decode()
+
+
+def moe_decode_bench_copy(src: int, dst: int, nbytes: int, stream: int) -> None:
+    _check(lib().moe_decode_bench_copy(src, dst, nbytes, stream))
+
+
+def moe_decode_bench_read(src: int, nbytes: int, sink: int, stream: int) -> None:
+    _check(lib().moe_decode_bench_read(src, nbytes, sink, stream))

@@ -139,7 +139,7 @@ def test_forward_rejects_bad_pointers_and_workspace():
                                       None) == md.MOE_EINVAL
         assert lib.moe_decode_forward(None, C.byref(_weights_stub()), 4096, 1, 4096, None, None,
                                       4096 * 256, ws, None) == md.MOE_EINVAL
-        # An event count no arrangement uses (1 or 3 stages -> 2 or 4 events).
+        # An event count no arrangement uses (a start and a stop event per stage).
         ev = (C.c_void_p * 7)(*([4096] * 7))
         assert lib.moe_decode_forward_timed(plan, C.byref(_weights_stub()), 4096, 1, 4096, None,
                                             None, 4096 * 256, ws, None, ev, 7) == md.MOE_EINVAL
@@ -170,3 +170,15 @@ def test_single_launch_arrangement_is_refused(monkeypatch):
     with pytest.raises(md.MoeDecodeError) as ei:
         md.moe_decode_plan(desc_of(synth.WORKLOADS["qwen3_30b_a3b_bf16"]))
     assert ei.value.status == md.MOE_EUNSUPPORTED
+
+
+def test_measurement_utilities_reject_bad_arguments():
+    """Validation runs before anything is launched (no GPU needed)."""
+    for args in ((4096, 8192, 100), (4100, 8192, 4096), (4096, 8200, 4096), (None, 8192, 4096)):
+        with pytest.raises(md.MoeDecodeError) as ei:
+            md.moe_decode_bench_copy(args[0], args[1], args[2], None)
+        assert ei.value.status == md.MOE_EINVAL
+    for args in ((4096, 100, 8192), (4100, 4096, 8192), (4096, 4096, None)):
+        with pytest.raises(md.MoeDecodeError) as ei:
+            md.moe_decode_bench_read(args[0], args[1], args[2], None)
+        assert ei.value.status == md.MOE_EINVAL

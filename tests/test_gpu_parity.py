@@ -294,3 +294,17 @@ def test_graph_replay_matches_eager():
         check_sync_words(dl)
         dl.forward(x, m, dl.new_out(m))      # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_measurement_utilities():
+    """The copy reference copies exactly; the read reference leaves its sink alone."""
+    n = (3 << 20) + 4                               # bytes: several grid strides and a tail
+    src = torch.randint(-2**31, 2**31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    say("bench_copy / bench_read", n)
+    md.moe_decode_bench_copy(src.data_ptr(), dst.data_ptr(), n - 4, 0)
+    md.moe_decode_bench_read(src.data_ptr(), n - 4, sink.data_ptr(), 0)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:-1], src[:-1]) and int(dst[-1]) == 0
+    assert int(sink[0]) in (7, 0x9E3779B9 - 2**32)
