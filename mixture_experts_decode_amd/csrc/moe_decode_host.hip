@@ -160,6 +160,16 @@ moe_status check_desc(const moe_decode_desc &d) {
     if (d.shared_inter <= 0 || d.shared_inter % 8)
       return fail(MOE_EUNSUPPORTED, "shared_inter must be a positive multiple of 8");
   }
+  // Weight matrices are read through buffer resources with 32-bit byte
+  // ranges: each projection (one expert's, or the shared expert's) must be
+  // under 2 GiB.
+  const double ebytes = d.expert_fmt == MOE_F32 ? 4.0 : d.expert_fmt == MOE_BF16 ? 2.0 : 0.5;
+  const double abytes = d.act_fmt == MOE_F32 ? 4.0 : 2.0;
+  const double lim = 2147483647.0;
+  if ((double)d.hidden * d.inter * ebytes >= lim)
+    return fail(MOE_EUNSUPPORTED, "an expert projection of %d x %d exceeds 2 GiB", d.inter, d.hidden);
+  if ((d.flags & MOE_SHARED) && (double)d.hidden * d.shared_inter * abytes >= lim)
+    return fail(MOE_EUNSUPPORTED, "a shared projection of %d x %d exceeds 2 GiB", d.shared_inter, d.hidden);
   return MOE_OK;
 }
 
@@ -283,7 +293,9 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   a.n_shared_gu = shared ? ((a.Is + ni_s - 1) / ni_s + wpb - 1) / wpb : 0;
   a.gu_items_per_slot = ((d.inter + ni_r - 1) / ni_r + wpb - 1) / wpb;
   a.n_routed_gu = a.cap * a.gu_items_per_slot;
-  a.down_dq = (a.cap + (shared ? 1 : 0)) < wpb ? 2 : 1;
+  // Two row blocks per down tile when the units would leave waves idle and
+  // the halved tile count still gives every CU a workgroup.
+  a.down_dq = ((a.cap + (shared ? 1 : 0)) < moe::DOWN_WPB && d.hidden / (2 * moe::DOWN_RD) >= 256) ? 2 : 1;
   a.n_down = (d.hidden + moe::DOWN_RD * a.down_dq - 1) / (moe::DOWN_RD * a.down_dq);
 
   static thread_local bool logged = false;

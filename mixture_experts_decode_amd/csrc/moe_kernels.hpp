@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe {
 
 enum : int { F32 = 0, BF16 = 1, AFF4 = 2, MXFP4 = 3 };
@@ -35,8 +37,10 @@ enum : int { ROUTE_SOFTMAX = 0, ROUTE_SIGMOID_BIAS = 1, ROUTE_SIGMOID_LOGIT = 2 
 enum : unsigned { NORM_TOPK = 1u, WEIGHT_BEFORE = 2u, SHARED = 4u, SHARED_GATED = 8u, OUT_F32 = 16u };
 
 constexpr int WAVE = 64;
-constexpr int THREADS = 256;            // every kernel: 4 waves per workgroup
+constexpr int THREADS = 256;            // route and gate/up: 4 waves per workgroup
 constexpr int WPB = THREADS / WAVE;
+constexpr int DOWN_THREADS = 512;       // down + blend: 8 waves, one active slot each at m = 1
+constexpr int DOWN_WPB = DOWN_THREADS / WAVE;
 constexpr int MAX_ROWS = 32;
 constexpr int MAX_TOPK = 16;
 constexpr int MAX_EXPERTS = 256;
@@ -236,6 +240,11 @@ __device__ __forceinline__ double wave_max_f64(double v) {
 // A chunk is 16 bytes of one weight row: 4 f32, 8 bf16 or 32 packed 4-bit
 // codes.  Lane `li` of a row group handles chunks li, li+LPR, ...  XF is the
 // storage format of the vector the row is dotted with (F32 or BF16).
+//
+// A chunk is consumed in SUB sub-steps.  Sub-step g needs only the x
+// elements it covers (8 of them for the 4-bit formats, whose chunk spans 32),
+// loaded from cache right before use, so the registers x takes stay small
+// whatever the number of vectors in a pass.
 
 template <int WF> struct Fmt;
 template <> struct Fmt<F32> { static constexpr int EPC = 4; };
@@ -243,258 +252,268 @@ template <> struct Fmt<BF16> { static constexpr int EPC = 8; };
 template <> struct Fmt<AFF4> { static constexpr int EPC = 32; };
 template <> struct Fmt<MXFP4> { static constexpr int EPC = 32; };
 
-// One weight row: data, and for 4-bit formats its scale (and bias) row.
+// One weight row, addressed through buffer resources: the matrix's data
+// resource (and, for the 4-bit formats, its scale and bias resources) and the
+// row's byte offset in the data.  A 4-bit row of K codes is K/2 bytes and its
+// scale row K/32 bytes (aff4: K/64 bf16; mxfp4: K/32 E8M0), so the scale
+// row's offset is off / 16 for both.
 template <int WF> struct Row {
-  const char *w;
-  const void *s;
-  const void *b;
+  __amdgpu_buffer_rsrc_t w, s, b;
+  int off;
 };
 
-// Weight chunk plus its per-chunk dequant constants.
+// Weight chunk plus the raw bits of its dequant constants (converted where
+// they are used, so that no load has to complete before the compute starts).
 template <int WF> struct WChunk {
   u32x4 q;
-  float s, b;
+  uint32_t s, b;
 };
 
-template <int WF>
+// VGPRs one loaded chunk holds.
+template <int WF> constexpr int wchunk_regs() { return WF == AFF4 ? 6 : WF == MXFP4 ? 5 : 4; }
+
+constexpr int BUF_NT = 2;        // cache policy: nontemporal (weights are read once per call)
+
+// UNI: the row is the same for the whole wave, its offset goes in the
+// scalar offset operand; else it is added to the lane's offset.
+template <int WF, bool UNI>
 __device__ __forceinline__ WChunk<WF> load_wchunk(const Row<WF> &r, int ch) {
   WChunk<WF> c;
-  c.q = ld_stream16(r.w + (size_t)ch * 16);
+  const int vo = UNI ? 0 : r.off, so = UNI ? r.off : 0;
+  c.q = __builtin_amdgcn_raw_buffer_load_b128(r.w, vo + ch * 16, so, BUF_NT);
   if constexpr (WF == AFF4) {
     // One bf16 scale and bias per 64 elements = per 2 chunks.
-    c.s = bf16_to_f32(reinterpret_cast<const uint16_t *>(r.s)[ch >> 1]);
-    c.b = bf16_to_f32(reinterpret_cast<const uint16_t *>(r.b)[ch >> 1]);
+    c.s = __builtin_amdgcn_raw_buffer_load_b16(r.s, vo / 16 + (ch >> 1) * 2, so / 16, 0);
+    c.b = __builtin_amdgcn_raw_buffer_load_b16(r.b, vo / 16 + (ch >> 1) * 2, so / 16, 0);
   } else if constexpr (WF == MXFP4) {
-    c.s = e8m0_to_f32(reinterpret_cast<const uint8_t *>(r.s)[ch]);
-    c.b = 0.f;
+    c.s = __builtin_amdgcn_raw_buffer_load_b8(r.s, vo / 16 + ch, so / 16, 0);
+    c.b = 0u;
   } else {
-    c.s = c.b = 0.f;
+    c.s = c.b = 0u;
   }
   return c;
 }
 
-// The x elements matching one weight chunk: fetch() issues the loads, prep()
-// turns them into the form dot() needs (kept apart so that the loads of
-// several chunk steps can be in flight together).
-template <int WF, int XF> struct XChunk;
+// XOps<WF, XF>: the arithmetic of one chunk against one vector.
+//   SUB, XS        sub-steps per chunk; x registers of one sub-step
+//   X              x values of one sub-step: X::fetch(xrow, ch, g)
+//   xsum(x, s)     running sum of the vector over the chunk (aff4 only)
+//   step(w, x, g, p)  adds sub-step g to the chunk partial p
+//   finish(w, p, xs, acc)  folds the chunk partial into the row total
+// For the 8- and 4-element formats the partial is the row total itself.
+template <int WF, int XF> struct XOps;
 
 // bf16 weights . bf16 x: raw bf16 pairs, v_dot2.
-template <> struct XChunk<BF16, BF16> {
-  uint32_t d[4];
-  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
-    u32x4 v = ld16(xrow + (size_t)ch * 16);
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+template <> struct XOps<BF16, BF16> {
+  static constexpr int SUB = 1, XS = 4;
+  struct X {
+    u32x4 d;
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int) { d = ld16(xrow + (size_t)ch * 16); }
+  };
+  static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
+  static __device__ __forceinline__ float start(float acc) { return acc; }
+  static __device__ __forceinline__ float step(const WChunk<BF16> &w, const X &x, int, float p) {
+    p = dot2(w.q.x, x.d.x, p);
+    p = dot2(w.q.y, x.d.y, p);
+    p = dot2(w.q.z, x.d.z, p);
+    return dot2(w.q.w, x.d.w, p);
   }
-  __device__ __forceinline__ void prep() {}
-  __device__ __forceinline__ float dot(const WChunk<BF16> &w, float acc) const {
-    acc = dot2(w.q.x, d[0], acc);
-    acc = dot2(w.q.y, d[1], acc);
-    acc = dot2(w.q.z, d[2], acc);
-    return dot2(w.q.w, d[3], acc);
-  }
+  static __device__ __forceinline__ float finish(const WChunk<BF16> &, float p, float, float) { return p; }
 };
 
 // bf16 weights . f32 x.
-template <> struct XChunk<BF16, F32> {
-  float f[8];
-  __device__ __forceinline__ void prep() {}
-  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
-    u32x4 a = ld16(xrow + (size_t)ch * 32), b = ld16(xrow + (size_t)ch * 32 + 16);
-    f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y);
-    f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
-    f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y);
-    f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
-  }
-  __device__ __forceinline__ float dot(const WChunk<BF16> &w, float acc) const {
-    const uint32_t q[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = __builtin_fmaf(bf_lo(q[i]), f[2 * i], acc);
-      acc = __builtin_fmaf(bf_hi(q[i]), f[2 * i + 1], acc);
+template <> struct XOps<BF16, F32> {
+  static constexpr int SUB = 1, XS = 8;
+  struct X {
+    u32x4 a, b;
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int) {
+      a = ld16(xrow + (size_t)ch * 32);
+      b = ld16(xrow + (size_t)ch * 32 + 16);
     }
-    return acc;
+  };
+  static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
+  static __device__ __forceinline__ float start(float acc) { return acc; }
+  static __device__ __forceinline__ float step(const WChunk<BF16> &w, const X &x, int, float p) {
+    p = __builtin_fmaf(bf_lo(w.q.x), __uint_as_float(x.a.x), p);
+    p = __builtin_fmaf(bf_hi(w.q.x), __uint_as_float(x.a.y), p);
+    p = __builtin_fmaf(bf_lo(w.q.y), __uint_as_float(x.a.z), p);
+    p = __builtin_fmaf(bf_hi(w.q.y), __uint_as_float(x.a.w), p);
+    p = __builtin_fmaf(bf_lo(w.q.z), __uint_as_float(x.b.x), p);
+    p = __builtin_fmaf(bf_hi(w.q.z), __uint_as_float(x.b.y), p);
+    p = __builtin_fmaf(bf_lo(w.q.w), __uint_as_float(x.b.z), p);
+    return __builtin_fmaf(bf_hi(w.q.w), __uint_as_float(x.b.w), p);
   }
+  static __device__ __forceinline__ float finish(const WChunk<BF16> &, float p, float, float) { return p; }
 };
 
 // f32 weights . f32 x.
-template <> struct XChunk<F32, F32> {
-  float f[4];
-  __device__ __forceinline__ void prep() {}
-  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
-    u32x4 a = ld16(xrow + (size_t)ch * 16);
-    f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y);
-    f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+template <> struct XOps<F32, F32> {
+  static constexpr int SUB = 1, XS = 4;
+  struct X {
+    u32x4 a;
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int) { a = ld16(xrow + (size_t)ch * 16); }
+  };
+  static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
+  static __device__ __forceinline__ float start(float acc) { return acc; }
+  static __device__ __forceinline__ float step(const WChunk<F32> &w, const X &x, int, float p) {
+    p = __builtin_fmaf(__uint_as_float(w.q.x), __uint_as_float(x.a.x), p);
+    p = __builtin_fmaf(__uint_as_float(w.q.y), __uint_as_float(x.a.y), p);
+    p = __builtin_fmaf(__uint_as_float(w.q.z), __uint_as_float(x.a.z), p);
+    return __builtin_fmaf(__uint_as_float(w.q.w), __uint_as_float(x.a.w), p);
   }
-  __device__ __forceinline__ float dot(const WChunk<F32> &w, float acc) const {
-    acc = __builtin_fmaf(__uint_as_float(w.q.x), f[0], acc);
-    acc = __builtin_fmaf(__uint_as_float(w.q.y), f[1], acc);
-    acc = __builtin_fmaf(__uint_as_float(w.q.z), f[2], acc);
-    return __builtin_fmaf(__uint_as_float(w.q.w), f[3], acc);
-  }
+  static __device__ __forceinline__ float finish(const WChunk<F32> &, float p, float, float) { return p; }
 };
 
 // f32 weights . bf16 x.
-template <> struct XChunk<F32, BF16> {
-  float f[4];
-  u32x2 raw;
-  __device__ __forceinline__ void fetch(const char *xrow, int ch) { raw = ld8(xrow + (size_t)ch * 8); }
-  __device__ __forceinline__ void prep() {
-    f[0] = bf_lo(raw.x); f[1] = bf_hi(raw.x); f[2] = bf_lo(raw.y); f[3] = bf_hi(raw.y);
+template <> struct XOps<F32, BF16> {
+  static constexpr int SUB = 1, XS = 2;
+  struct X {
+    u32x2 raw;
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int) { raw = ld8(xrow + (size_t)ch * 8); }
+  };
+  static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
+  static __device__ __forceinline__ float start(float acc) { return acc; }
+  static __device__ __forceinline__ float step(const WChunk<F32> &w, const X &x, int, float p) {
+    p = __builtin_fmaf(__uint_as_float(w.q.x), bf_lo(x.raw.x), p);
+    p = __builtin_fmaf(__uint_as_float(w.q.y), bf_hi(x.raw.x), p);
+    p = __builtin_fmaf(__uint_as_float(w.q.z), bf_lo(x.raw.y), p);
+    return __builtin_fmaf(__uint_as_float(w.q.w), bf_hi(x.raw.y), p);
   }
-  __device__ __forceinline__ float dot(const WChunk<F32> &w, float acc) const {
-    acc = __builtin_fmaf(__uint_as_float(w.q.x), f[0], acc);
-    acc = __builtin_fmaf(__uint_as_float(w.q.y), f[1], acc);
-    acc = __builtin_fmaf(__uint_as_float(w.q.z), f[2], acc);
-    return __builtin_fmaf(__uint_as_float(w.q.w), f[3], acc);
-  }
+  static __device__ __forceinline__ float finish(const WChunk<F32> &, float p, float, float) { return p; }
 };
 
-// aff4 weights . bf16 x.  A code dword holds elements e0..e7 (nibble i at
+__device__ __forceinline__ uint32_t code_dword(const u32x4 &q, int g) {
+  return g == 0 ? q.x : g == 1 ? q.y : g == 2 ? q.z : q.w;
+}
+
+// aff4 weights . bf16 x.  Code dword g holds elements 8g..8g+7 (nibble i at
 // bits 4i).  OR-ing a nibble into the mantissa of bf16 128.0 (0x4300) gives
 // 128 + q exactly, so (u >> 4t) & 0x000F000F | 0x43004300 is the bf16 pair
 // (128 + q_t, 128 + q_{t+4}); x is re-paired to (x_t, x_{t+4}) to match.
 //   sum q x = sum (128+q) x - 128 sum x, and w = s q + b, so the chunk adds
 //   s * D + (b - 128 s) * X  with D = sum (128+q) x, X = sum x.
-template <> struct XChunk<AFF4, BF16> {
-  uint32_t d[16];
-  float xs;
-  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
-    const char *p = xrow + (size_t)ch * 64;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x4 r = ld16(p + 16 * g);  // (x0,x1) (x2,x3) (x4,x5) (x6,x7)
-      d[4 * g + 0] = r.x; d[4 * g + 1] = r.y; d[4 * g + 2] = r.z; d[4 * g + 3] = r.w;
+template <> struct XOps<AFF4, BF16> {
+  static constexpr int SUB = 4, XS = 4;
+  struct X {
+    uint32_t d[4];   // (x0,x4) (x1,x5) (x2,x6) (x3,x7) of the sub-step
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g) {
+      const u32x4 v = ld16(xrow + (size_t)ch * 64 + 16 * g);  // (x0,x1) (x2,x3) (x4,x5) (x6,x7)
+      d[0] = (v.x & 0xFFFFu) | (v.z << 16);
+      d[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
+      d[2] = (v.y & 0xFFFFu) | (v.w << 16);
+      d[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
     }
+  };
+  static __device__ __forceinline__ float xsum(const X &x, float s) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s = dot2(x.d[t], 0x3F803F80u, s);
+    return s;
   }
-  __device__ __forceinline__ void prep() {
-    float s = 0.f;
+  static __device__ __forceinline__ float start(float) { return 0.f; }
+  static __device__ __forceinline__ float step(const WChunk<AFF4> &w, const X &x, int g, float D) {
+    const uint32_t q = code_dword(w.q, g);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t rx = d[4 * g], ry = d[4 * g + 1], rz = d[4 * g + 2], rw = d[4 * g + 3];
-      d[4 * g + 0] = (rx & 0xFFFFu) | (rz << 16);
-      d[4 * g + 1] = (rx >> 16) | (rz & 0xFFFF0000u);
-      d[4 * g + 2] = (ry & 0xFFFFu) | (rw << 16);
-      d[4 * g + 3] = (ry >> 16) | (rw & 0xFFFF0000u);
-      s = dot2(rx, 0x3F803F80u, s);
-      s = dot2(ry, 0x3F803F80u, s);
-      s = dot2(rz, 0x3F803F80u, s);
-      s = dot2(rw, 0x3F803F80u, s);
-    }
-    xs = s;
+    for (int t = 0; t < 4; ++t) D = dot2(((q >> (4 * t)) & 0x000F000Fu) | 0x43004300u, x.d[t], D);
+    return D;
   }
-  __device__ __forceinline__ float dot(const WChunk<AFF4> &w, float acc) const {
-    const uint32_t q[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
-    float D = 0.f;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uint32_t n = ((q[g] >> (4 * t)) & 0x000F000Fu) | 0x43004300u;
-        D = dot2(n, d[4 * g + t], D);
-      }
-    }
-    acc = __builtin_fmaf(w.s, D, acc);
-    return __builtin_fmaf(__builtin_fmaf(-128.0f, w.s, w.b), xs, acc);
+  static __device__ __forceinline__ float finish(const WChunk<AFF4> &w, float D, float xs, float acc) {
+    const float sc = __uint_as_float(w.s << 16), bi = __uint_as_float(w.b << 16);
+    acc = __builtin_fmaf(sc, D, acc);
+    return __builtin_fmaf(__builtin_fmaf(-128.0f, sc, bi), xs, acc);
   }
 };
 
-// aff4 weights . f32 x.
-template <> struct XChunk<AFF4, F32> {
-  float f[32];
-  float xs;
-  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
-    const char *p = xrow + (size_t)ch * 128;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      u32x4 r = ld16(p + 16 * g);
-      f[4 * g + 0] = __uint_as_float(r.x); f[4 * g + 1] = __uint_as_float(r.y);
-      f[4 * g + 2] = __uint_as_float(r.z); f[4 * g + 3] = __uint_as_float(r.w);
+// aff4 weights . f32 x: w = s q + b, the chunk adds s * sum q x + b * sum x.
+template <> struct XOps<AFF4, F32> {
+  static constexpr int SUB = 4, XS = 8;
+  struct X {
+    u32x4 a, b;      // x 8g .. 8g+7
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g) {
+      a = ld16(xrow + (size_t)ch * 128 + 32 * g);
+      b = ld16(xrow + (size_t)ch * 128 + 32 * g + 16);
     }
-  }
-  __device__ __forceinline__ void prep() {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) s += f[i];
-    xs = s;
-  }
-  __device__ __forceinline__ float dot(const WChunk<AFF4> &w, float acc) const {
-    const uint32_t q[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
-    float D = 0.f;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint32_t lo = q[g] & 0x0F0F0F0Fu, hi = (q[g] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        D = __builtin_fmaf((float)((lo >> (8 * b)) & 0xFFu), f[8 * g + 2 * b], D);
-        D = __builtin_fmaf((float)((hi >> (8 * b)) & 0xFFu), f[8 * g + 2 * b + 1], D);
-      }
+    __device__ __forceinline__ float f(int i) const {
+      const u32x4 &v = i < 4 ? a : b;
+      const int j = i & 3;
+      return __uint_as_float(j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w);
     }
-    acc = __builtin_fmaf(w.s, D, acc);
-    return __builtin_fmaf(w.b, xs, acc);
+  };
+  static __device__ __forceinline__ float xsum(const X &x, float s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += x.f(i);
+    return s;
+  }
+  static __device__ __forceinline__ float start(float) { return 0.f; }
+  static __device__ __forceinline__ float step(const WChunk<AFF4> &w, const X &x, int g, float D) {
+    const uint32_t q = code_dword(w.q, g);
+    const uint32_t lo = q & 0x0F0F0F0Fu, hi = (q >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      D = __builtin_fmaf((float)((lo >> (8 * b)) & 0xFFu), x.f(2 * b), D);
+      D = __builtin_fmaf((float)((hi >> (8 * b)) & 0xFFu), x.f(2 * b + 1), D);
+    }
+    return D;
+  }
+  static __device__ __forceinline__ float finish(const WChunk<AFF4> &w, float D, float xs, float acc) {
+    acc = __builtin_fmaf(__uint_as_float(w.s << 16), D, acc);
+    return __builtin_fmaf(__uint_as_float(w.b << 16), xs, acc);
   }
 };
 
 // mxfp4 weights . bf16 x: v_cvt_scalef32_pk_bf16_fp4 turns byte t of a code
 // dword (elements 2t, 2t+1, low nibble first) into an exact bf16 pair that
 // lines up with the raw x pair; the E8M0 scale multiplies the chunk sum.
-template <> struct XChunk<MXFP4, BF16> {
-  uint32_t d[16];
-  __device__ __forceinline__ void prep() {}
-  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
-    const char *p = xrow + (size_t)ch * 64;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x4 r = ld16(p + 16 * g);
-      d[4 * g + 0] = r.x; d[4 * g + 1] = r.y; d[4 * g + 2] = r.z; d[4 * g + 3] = r.w;
-    }
+template <> struct XOps<MXFP4, BF16> {
+  static constexpr int SUB = 4, XS = 4;
+  struct X {
+    u32x4 d;
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g) { d = ld16(xrow + (size_t)ch * 64 + 16 * g); }
+  };
+  static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
+  static __device__ __forceinline__ float start(float) { return 0.f; }
+  static __device__ __forceinline__ float step(const WChunk<MXFP4> &w, const X &x, int g, float S) {
+    const uint32_t q = code_dword(w.q, g);
+    S = dot2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0)), x.d.x, S);
+    S = dot2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1)), x.d.y, S);
+    S = dot2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2)), x.d.z, S);
+    return dot2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3)), x.d.w, S);
   }
-  __device__ __forceinline__ float dot(const WChunk<MXFP4> &w, float acc) const {
-    const uint32_t q[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
-    float S = 0.f;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      S = dot2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[g], 1.0f, 0)), d[4 * g + 0], S);
-      S = dot2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[g], 1.0f, 1)), d[4 * g + 1], S);
-      S = dot2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[g], 1.0f, 2)), d[4 * g + 2], S);
-      S = dot2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[g], 1.0f, 3)), d[4 * g + 3], S);
-    }
-    return __builtin_fmaf(S, w.s, acc);
+  static __device__ __forceinline__ float finish(const WChunk<MXFP4> &w, float S, float, float acc) {
+    return __builtin_fmaf(S, e8m0_to_f32(w.s), acc);
   }
 };
 
 // mxfp4 weights . f32 x.
-template <> struct XChunk<MXFP4, F32> {
-  float f[32];
-  __device__ __forceinline__ void prep() {}
-  __device__ __forceinline__ void fetch(const char *xrow, int ch) {
-    const char *p = xrow + (size_t)ch * 128;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      u32x4 r = ld16(p + 16 * g);
-      f[4 * g + 0] = __uint_as_float(r.x); f[4 * g + 1] = __uint_as_float(r.y);
-      f[4 * g + 2] = __uint_as_float(r.z); f[4 * g + 3] = __uint_as_float(r.w);
+template <> struct XOps<MXFP4, F32> {
+  static constexpr int SUB = 4, XS = 8;
+  struct X {
+    u32x4 a, b;
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g) {
+      a = ld16(xrow + (size_t)ch * 128 + 32 * g);
+      b = ld16(xrow + (size_t)ch * 128 + 32 * g + 16);
     }
+  };
+  static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
+  static __device__ __forceinline__ float start(float) { return 0.f; }
+  static __device__ __forceinline__ float step(const WChunk<MXFP4> &w, const X &x, int g, float S) {
+    const uint32_t q = code_dword(w.q, g);
+    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+    S = __builtin_fmaf(v0.x, __uint_as_float(x.a.x), S);
+    S = __builtin_fmaf(v0.y, __uint_as_float(x.a.y), S);
+    S = __builtin_fmaf(v1.x, __uint_as_float(x.a.z), S);
+    S = __builtin_fmaf(v1.y, __uint_as_float(x.a.w), S);
+    S = __builtin_fmaf(v2.x, __uint_as_float(x.b.x), S);
+    S = __builtin_fmaf(v2.y, __uint_as_float(x.b.y), S);
+    S = __builtin_fmaf(v3.x, __uint_as_float(x.b.z), S);
+    return __builtin_fmaf(v3.y, __uint_as_float(x.b.w), S);
   }
-  __device__ __forceinline__ float dot(const WChunk<MXFP4> &w, float acc) const {
-    const uint32_t q[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
-    float S = 0.f;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f32x2 v;
-        if (t == 0) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[g], 1.0f, 0);
-        if (t == 1) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[g], 1.0f, 1);
-        if (t == 2) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[g], 1.0f, 2);
-        if (t == 3) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[g], 1.0f, 3);
-        S = __builtin_fmaf(v.x, f[8 * g + 2 * t], S);
-        S = __builtin_fmaf(v.y, f[8 * g + 2 * t + 1], S);
-      }
-    }
-    return __builtin_fmaf(S, w.s, acc);
+  static __device__ __forceinline__ float finish(const WChunk<MXFP4> &w, float S, float, float acc) {
+    return __builtin_fmaf(S, e8m0_to_f32(w.s), acc);
   }
 };
-
 
 // ------------------------------------------------------ wave row x vector
 //
@@ -502,16 +521,31 @@ template <> struct XChunk<MXFP4, F32> {
 // vectors (xrow[c]).  The wave is split into 64/LPR lane groups; the caller
 // passes in `rows` the RG rows of the calling lane's group.  Lane li of a
 // group takes chunks li, li + LPR, ...; the weight loads of U chunk steps --
-// and, where registers allow, their x loads -- are issued together before any
-// of them is used.  On return acc[t][c] holds, in every lane of the group,
-// the full dot product of rows[t] with vector c.  The per-(row, vector)
-// arithmetic does not depend on C, U or the other rows, so results are the
-// same for every m.
-template <int WF, int XF, int RG, int C, int LPR, int U>
+// and, for the one-sub-step formats where registers allow, their x loads --
+// are issued together before any of them is used.  On return acc[t][c]
+// holds, in every lane of the group, the full dot product of rows[t] with
+// vector c.  The per-(row, vector) arithmetic does not depend on C, U or the
+// other rows, so results are the same for every m.
+
+// Chunk steps issued together: as many as fit, with the RG x C totals and
+// the x values in use, in about 128 VGPRs.
+template <int WF, int XF, int RG, int C> struct Unroll {
+  static constexpr int clampu(int v) { return v < 1 ? 1 : (v > 4 ? 4 : v); }
+  static constexpr int W = RG * wchunk_regs<WF>();
+  static constexpr int XS = XOps<WF, XF>::XS;
+  static constexpr int A = RG * C + 2 * XS;
+  static constexpr int U0 = clampu((128 - A) / W);
+  static constexpr bool XPF = XOps<WF, XF>::SUB == 1 && U0 * C * XS <= 32;
+  static constexpr int U = XPF ? clampu((128 - RG * C) / (W + C * XS)) : U0;
+};
+
+template <int WF, int XF, int RG, int C, int LPR>
 __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const char *const (&xrow)[C],
                                               int nchunks, float (&acc)[RG][C]) {
-  constexpr bool XPF = U * C * (int)(sizeof(XChunk<WF, XF>) / 4) <= 64;  // prefetch x too
-  constexpr int XU = XPF ? U : 1;
+  using O = XOps<WF, XF>;
+  using X = typename O::X;
+  constexpr int U = Unroll<WF, XF, RG, C>::U;
+  constexpr bool XPF = Unroll<WF, XF, RG, C>::XPF;
   const int li = threadIdx.x % LPR;
 #pragma unroll
   for (int t = 0; t < RG; ++t)
@@ -519,16 +553,16 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
     for (int c = 0; c < C; ++c) acc[t][c] = 0.f;
   for (int base = 0; base < nchunks; base += LPR * U) {
     WChunk<WF> w[U][RG];
-    XChunk<WF, XF> xc[XU][C];
+    X xp[XPF ? U : 1][XPF ? C : 1];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ch = base + li + u * LPR;
       if (ch < nchunks) {
 #pragma unroll
-        for (int t = 0; t < RG; ++t) w[u][t] = load_wchunk<WF>(rows[t], ch);
+        for (int t = 0; t < RG; ++t) w[u][t] = load_wchunk<WF, LPR == WAVE>(rows[t], ch);
         if constexpr (XPF) {
 #pragma unroll
-          for (int c = 0; c < C; ++c) xc[u][c].fetch(xrow[c], ch);
+          for (int c = 0; c < C; ++c) xp[u][c].fetch(xrow[c], ch, 0);
         }
       }
     }
@@ -536,14 +570,46 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
     for (int u = 0; u < U; ++u) {
       const int ch = base + li + u * LPR;
       if (ch < nchunks) {
+        // Sub-step, then row, then vector: a row's expanded codes serve every
+        // vector right away and are dead before the next row's are made.
+        float p[RG][C], xs[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-          XChunk<WF, XF> &x = xc[XPF ? u : 0][c];
-          if constexpr (!XPF) x.fetch(xrow[c], ch);
-          x.prep();
+          xs[c] = 0.f;
 #pragma unroll
-          for (int t = 0; t < RG; ++t) acc[t][c] = x.dot(w[u][t], acc[t][c]);
+          for (int t = 0; t < RG; ++t) p[t][c] = O::start(acc[t][c]);
         }
+        // x of sub-step g + 1 is requested before sub-step g is computed.
+        X xn[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          if constexpr (XPF) xn[c] = xp[u][c];
+          else xn[c].fetch(xrow[c], ch, 0);
+        }
+#pragma unroll
+        for (int g = 0; g < O::SUB; ++g) {
+          X x[C];
+#pragma unroll
+          for (int c = 0; c < C; ++c) x[c] = xn[c];
+          if (g + 1 < O::SUB) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) xn[c].fetch(xrow[c], ch, g + 1);
+          }
+#pragma unroll
+          for (int c = 0; c < C; ++c) xs[c] = O::xsum(x[c], xs[c]);
+#pragma unroll
+          for (int t = 0; t < RG; ++t) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) p[t][c] = O::step(w[u][t], x[c], g, p[t][c]);
+            // 4-bit codes expand to several registers per dword: expand
+            // each row's right where it is used, not all rows up front.
+            if constexpr (O::SUB > 1) __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < RG; ++t)
+#pragma unroll
+          for (int c = 0; c < C; ++c) acc[t][c] = O::finish(w[u][t], p[t][c], xs[c], acc[t][c]);
       }
     }
   }
@@ -553,34 +619,74 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
     for (int c = 0; c < C; ++c) acc[t][c] = group_total<LPR>(acc[t][c]);
 }
 
-// Chunk steps issued together: about 16 loads of 16 bytes per lane.
-template <int RG> constexpr int unroll_for() { return RG >= 8 ? 2 : 4; }
-
-template <int WF>
-__device__ __forceinline__ size_t row_bytes(int K) {
-  return (size_t)K * (WF == F32 ? 4 : WF == BF16 ? 2 : 1) / (WF >= AFF4 ? 2 : 1);
+// Calls f(integral_constant<C>, c0) over pairs [0, n) in passes of the
+// widest power of two up to CMAX that the pairs left fill, so that no pass
+// computes a vector twice.
+template <int CMAX, typename F>
+__device__ __forceinline__ void for_passes(int n, F &&f) {
+  int c0 = 0;
+  if constexpr (CMAX >= 8)
+    for (; n - c0 >= 8; c0 += 8) f(std::integral_constant<int, 8>(), c0);
+  if constexpr (CMAX >= 4)
+    for (; n - c0 >= 4; c0 += 4) f(std::integral_constant<int, 4>(), c0);
+  if constexpr (CMAX >= 2)
+    for (; n - c0 >= 2; c0 += 2) f(std::integral_constant<int, 2>(), c0);
+  for (; c0 < n; ++c0) f(std::integral_constant<int, 1>(), c0);
 }
 
 template <int WF>
-__device__ __forceinline__ Row<WF> make_row(const void *w, const void *s, const void *b, int K, int n) {
-  Row<WF> r;
-  r.w = reinterpret_cast<const char *>(w) + (size_t)n * row_bytes<WF>(K);
-  if constexpr (WF == AFF4) {
-    r.s = reinterpret_cast<const uint16_t *>(s) + (size_t)n * (K / 64);
-    r.b = reinterpret_cast<const uint16_t *>(b) + (size_t)n * (K / 64);
-  } else if constexpr (WF == MXFP4) {
-    r.s = reinterpret_cast<const uint8_t *>(s) + (size_t)n * (K / 32);
-    r.b = nullptr;
+__device__ __forceinline__ int row_bytes(int K) {
+  return K * (WF == F32 ? 4 : WF == BF16 ? 2 : 1) / (WF >= AFF4 ? 2 : 1);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+
+// The matrix [N, K] at w (scales s, biases b for 4-bit formats): one
+// resource per array, bounded to the array's bytes.
+template <int WF> struct Mat {
+  __amdgpu_buffer_rsrc_t w, s, b;
+  int rb;  // bytes per row
+};
+
+template <int WF>
+__device__ __forceinline__ Mat<WF> make_mat(const void *w, const void *s, const void *b, int N, int K) {
+  Mat<WF> m;
+  m.rb = row_bytes<WF>(K);
+  m.w = buf_rsrc(w, N * m.rb);
+  if constexpr (WF >= AFF4) {
+    m.s = buf_rsrc(s, N * m.rb / 16);
+    m.b = WF == AFF4 ? buf_rsrc(b, N * m.rb / 16) : m.s;
   } else {
-    r.s = r.b = nullptr;
+    m.s = m.b = m.w;
   }
+  return m;
+}
+
+// Row n of the matrix.  UNI: n is the same for the whole wave.
+template <int WF, bool UNI>
+__device__ __forceinline__ Row<WF> make_row(const Mat<WF> &m, int n) {
+  Row<WF> r;
+  r.w = m.w;
+  r.s = m.s;
+  r.b = m.b;
+  r.off = n * m.rb;
+  if constexpr (UNI) r.off = __builtin_amdgcn_readfirstlane(r.off);
   return r;
 }
 
 __device__ __forceinline__ size_t act_bytes(int fmt) { return fmt == F32 ? 4 : 2; }
 
+__device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Entry e (wave-uniform) of a device pointer table, as a wave-uniform pointer.
 __device__ __forceinline__ const void *tbl(const uint64_t *t, int e) {
-  return t ? reinterpret_cast<const void *>(t[e]) : nullptr;
+  if (!t) return nullptr;
+  const uint64_t v = t[uniform_i(e)];
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ int clamp_i(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -867,7 +973,7 @@ __device__ __forceinline__ void route_select(const Args &a, RouteLDS &L, bool pu
 // pairs pair[0..np-1] (routed: row = pair / k, routing weight w[pair]) or
 // input rows 0..np-1 (shared), in passes of C; writes silu(g) * v at
 // dst[(off + c) * ld + i].
-template <int EF, int ACT, int C, int NI>
+template <int EF, int ACT, int CMAX, int NI>
 __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, const void *uw,
                                              const void *gs, const void *us, const void *gb,
                                              const void *ub, int N, int i0, int off, int np,
@@ -877,46 +983,44 @@ __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, cons
   const size_t xstride = (size_t)H * act_bytes(ACT);
   const char *x = reinterpret_cast<const char *>(a.x);
   const bool routed = pairs != nullptr;
+  const bool scale = routed && (a.flags & WEIGHT_BEFORE);
+  const Mat<EF> mg = make_mat<EF>(gw, gs, gb, N, H), mu = make_mat<EF>(uw, us, ub, N, H);
   Row<EF> rows[RG];
 #pragma unroll
   for (int t = 0; t < NI; ++t) {
     const int i = min(i0 + t, N - 1);
-    rows[t] = make_row<EF>(gw, gs, gb, H, i);
-    rows[NI + t] = make_row<EF>(uw, us, ub, H, i);
+    rows[t] = make_row<EF, true>(mg, i);
+    rows[NI + t] = make_row<EF, true>(mu, i);
   }
-  for (int c0 = 0; c0 < np; c0 += C) {
-    const int nc = min(C, np - c0);
+  for_passes<CMAX>(np, [&](auto cc, int c0) {
+    constexpr int C = decltype(cc)::value;
     const char *xrow[C];
     int pair[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const int q = c0 + min(c, nc - 1);
-      pair[c] = routed ? pairs[q] : q;
-      xrow[c] = x + (size_t)(routed ? pair[c] / k : q) * xstride;
+      pair[c] = routed ? pairs[c0 + c] : c0 + c;
+      xrow[c] = x + (size_t)(routed ? pair[c] / k : c0 + c) * xstride;
     }
     float acc[RG][C];
-    wave_rows_dot<EF, ACT, RG, C, WAVE, unroll_for<RG>()>(rows, xrow, H / Fmt<EF>::EPC, acc);
+    wave_rows_dot<EF, ACT, RG, C, WAVE>(rows, xrow, H / Fmt<EF>::EPC, acc);
     if ((threadIdx.x & 63) == 0) {
-      const bool scale = routed && (a.flags & WEIGHT_BEFORE);
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        if (c < nc) {
-          const float w = scale ? pw[pair[c]] : 1.0f;
+        const float w = scale ? pw[pair[c]] : 1.0f;
 #pragma unroll
-          for (int t = 0; t < NI; ++t) {
-            if (i0 + t < N) {
-              float g = acc[t][c], v = acc[NI + t][c];
-              if (scale) {  // W(w x) = w (W x): scale both pre-activations
-                g *= w;
-                v *= w;
-              }
-              dst[(size_t)(off + c0 + c) * ld + i0 + t] = silu_mul(g, v);
+        for (int t = 0; t < NI; ++t) {
+          if (i0 + t < N) {
+            float g = acc[t][c], v = acc[NI + t][c];
+            if (scale) {  // W(w x) = w (W x): scale both pre-activations
+              g *= w;
+              v *= w;
             }
+            dst[(size_t)(off + c0 + c) * ld + i0 + t] = silu_mul(g, v);
           }
         }
       }
     }
-  }
+  });
 }
 
 // --------------------------------------------------------- down + blend
@@ -933,14 +1037,14 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   static_assert(DOWN_RD % GR == 0, "down rows must split over lane groups");
   __shared__ float y_lds[MAX_PAIRS * MAX_DOWN_TILE];
   __shared__ float ys_lds[MAX_ROWS * MAX_DOWN_TILE];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int H = a.H, I = a.I, Is = a.Is, m = a.m;
   const int DQ = a.down_dq, HT = DOWN_RD * DQ, h0 = tile * HT;
   const int nact = clamp_i(a.active_count[0], 0, a.cap);
   const bool shared = (a.flags & SHARED) != 0;
   const int units = nact + (shared ? 1 : 0);
 
-  for (int su = wave; su < units * DQ; su += WPB) {
+  for (int su = wave; su < units * DQ; su += DOWN_WPB) {
     const int u = su / DQ, q = su - u * DQ;
     const int hb = h0 + q * DOWN_RD;             // first column of this row block
     if (u < nact) {
@@ -949,45 +1053,43 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
       const int np = clamp_i(a.offsets[e + 1], off, a.te) - off;
       const void *dw = tbl(a.dw, e), *ds = tbl(a.ds, e), *db = tbl(a.db, e);
       const int grp = lane / LPR;
+      const Mat<EF> md = make_mat<EF>(dw, ds, db, H, I);
       Row<EF> rows[RGR];
 #pragma unroll
-      for (int t = 0; t < RGR; ++t) rows[t] = make_row<EF>(dw, ds, db, I, min(hb + grp + GR * t, H - 1));
-      for (int c0 = 0; c0 < np; c0 += CR) {
-        const int nc = min(CR, np - c0);
-        const char *xrow[CR];
+      for (int t = 0; t < RGR; ++t) rows[t] = make_row<EF, LPR == WAVE>(md, min(hb + grp + GR * t, H - 1));
+      for_passes<CR>(np, [&](auto cc, int c0) {
+        constexpr int C = decltype(cc)::value;
+        const char *xrow[C];
 #pragma unroll
-        for (int c = 0; c < CR; ++c)
-          xrow[c] = reinterpret_cast<const char *>(a.act + (size_t)(off + c0 + min(c, nc - 1)) * I);
-        float acc[RGR][CR];
-        wave_rows_dot<EF, F32, RGR, CR, LPR, unroll_for<RGR>()>(rows, xrow, I / Fmt<EF>::EPC, acc);
+        for (int c = 0; c < C; ++c) xrow[c] = reinterpret_cast<const char *>(a.act + (size_t)(off + c0 + c) * I);
+        float acc[RGR][C];
+        wave_rows_dot<EF, F32, RGR, C, LPR>(rows, xrow, I / Fmt<EF>::EPC, acc);
         if (lane % LPR == 0) {
 #pragma unroll
           for (int t = 0; t < RGR; ++t)
 #pragma unroll
-            for (int c = 0; c < CR; ++c)
-              if (c < nc) y_lds[(off + c0 + c) * HT + q * DOWN_RD + grp + GR * t] = acc[t][c];
+            for (int c = 0; c < C; ++c) y_lds[(off + c0 + c) * HT + q * DOWN_RD + grp + GR * t] = acc[t][c];
         }
-      }
+      });
     } else {
+      const Mat<ACT> ms = make_mat<ACT>(a.sdw, nullptr, nullptr, H, Is);
       Row<ACT> rows[DOWN_RD];
 #pragma unroll
-      for (int t = 0; t < DOWN_RD; ++t) rows[t] = make_row<ACT>(a.sdw, nullptr, nullptr, Is, min(hb + t, H - 1));
-      for (int c0 = 0; c0 < m; c0 += CS) {
-        const int nc = min(CS, m - c0);
-        const char *xrow[CS];
+      for (int t = 0; t < DOWN_RD; ++t) rows[t] = make_row<ACT, true>(ms, min(hb + t, H - 1));
+      for_passes<CS>(m, [&](auto cc, int c0) {
+        constexpr int C = decltype(cc)::value;
+        const char *xrow[C];
 #pragma unroll
-        for (int c = 0; c < CS; ++c)
-          xrow[c] = reinterpret_cast<const char *>(a.sact + (size_t)(c0 + min(c, nc - 1)) * Is);
-        float acc[DOWN_RD][CS];
-        wave_rows_dot<ACT, F32, DOWN_RD, CS, WAVE, unroll_for<DOWN_RD>()>(rows, xrow, Is / Fmt<ACT>::EPC, acc);
+        for (int c = 0; c < C; ++c) xrow[c] = reinterpret_cast<const char *>(a.sact + (size_t)(c0 + c) * Is);
+        float acc[DOWN_RD][C];
+        wave_rows_dot<ACT, F32, DOWN_RD, C, WAVE>(rows, xrow, Is / Fmt<ACT>::EPC, acc);
         if (lane == 0) {
 #pragma unroll
           for (int t = 0; t < DOWN_RD; ++t)
 #pragma unroll
-            for (int c = 0; c < CS; ++c)
-              if (c < nc) ys_lds[(c0 + c) * HT + q * DOWN_RD + t] = acc[t][c];
+            for (int c = 0; c < C; ++c) ys_lds[(c0 + c) * HT + q * DOWN_RD + t] = acc[t][c];
         }
-      }
+      });
     }
   }
   __syncthreads();
@@ -996,7 +1098,7 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   const bool gated = (a.flags & SHARED_GATED) != 0;
   const bool out_f32 = (a.flags & OUT_F32) != 0 || ACT == F32;
   const int k = a.K;
-  for (int t = threadIdx.x; t < m * HT; t += THREADS) {
+  for (int t = threadIdx.x; t < m * HT; t += DOWN_THREADS) {
     const int r = t / HT, hl = t - r * HT, h = h0 + hl;
     if (h >= H) continue;
     float o = 0.f;
@@ -1025,7 +1127,7 @@ __global__ __launch_bounds__(THREADS) void route_kernel(Args a) {
     return;
   }
   constexpr int NI = gate_up_ni<ACT>();
-  const int i0 = ((item - a.n_router) * WPB + (threadIdx.x >> 6)) * NI;
+  const int i0 = ((item - a.n_router) * WPB + uniform_i(threadIdx.x >> 6)) * NI;
   if (i0 < a.Is)
     gate_up_rows<ACT, ACT, CS, NI>(a, a.sgw, a.suw, nullptr, nullptr, nullptr, nullptr, a.Is, i0, 0,
                                    a.m, nullptr, nullptr, a.sact, a.Is);
@@ -1043,9 +1145,9 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
   const int n = L.nact * a.gu_items_per_slot;
   for (int it = blockIdx.x; it < n; it += gridDim.x) {
     const int s = it / a.gu_items_per_slot, b = it - s * a.gu_items_per_slot;
-    const int e = clamp_i(L.active[s], 0, a.E - 1);
-    const int off = L.off[e], np = L.off[e + 1] - off;
-    const int i0 = (b * WPB + (threadIdx.x >> 6)) * NI;
+    const int e = uniform_i(clamp_i(L.active[s], 0, a.E - 1));
+    const int off = uniform_i(L.off[e]), np = uniform_i(L.off[e + 1]) - off;
+    const int i0 = (b * WPB + uniform_i(threadIdx.x >> 6)) * NI;
     if (i0 < a.I)
       gate_up_rows<EF, ACT, CR, NI>(a, tbl(a.gw, e), tbl(a.uw, e), tbl(a.gs, e), tbl(a.us, e),
                                     tbl(a.gb, e), tbl(a.ub, e), a.I, i0, off, np, L.sorted + off,
@@ -1055,7 +1157,7 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
 
 // Launch 3: down tiles with the blend.
 template <int EF, int ACT, int CR, int CS, int LPR>
-__global__ __launch_bounds__(THREADS) void down_blend_kernel(Args a) {
+__global__ __launch_bounds__(DOWN_THREADS) void down_blend_kernel(Args a) {
   down_item<EF, ACT, CR, CS, LPR>(a, blockIdx.x);
 }
 

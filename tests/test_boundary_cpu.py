@@ -46,6 +46,7 @@ def _desc(**kw):
     ("flags", 1 << 10, md.MOE_EINVAL),
     ("flags", md.MOE_SHARED_GATED, md.MOE_EINVAL),
     ("inter", 100, md.MOE_EUNSUPPORTED),
+    ("inter", 1 << 19, md.MOE_EUNSUPPORTED),       # 2048 x 524288 bf16 = 2 GiB: past 32-bit ranges
 ])
 def test_plan_rejects(field, value, status):
     with pytest.raises(md.MoeDecodeError) as ei:
