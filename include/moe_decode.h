@@ -138,6 +138,9 @@ typedef struct {
   size_t pair_to_perm;    /* int32 [te]: position of pair p in sorted_pair */
   size_t active_experts;  /* int32 [cap]: experts with at least one pair, ascending */
   size_t active_count;    /* int32 [1] */
+  size_t slot_info;       /* [cap] 64-byte records, one per active slot u < active_count:
+                             int32 expert, first position in sorted_pair, pair count, 0;
+                             then the expert's down_w, down_s, down_b entries (uint64) */
   size_t act;             /* float [te, I]: routed SwiGLU activations, sorted order */
   size_t shared_act;      /* float [max_rows, Is] */
   size_t sync;            /* uint32 [512]: reserved completion words, kept zero */

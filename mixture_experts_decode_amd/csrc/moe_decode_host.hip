@@ -195,6 +195,7 @@ void layout_for(const moe_decode_desc &d, moe_decode_ws_layout *L) {
   L->pair_to_perm = take(te * 4);
   L->active_experts = take(cap * 4);
   L->active_count = take(4);
+  L->slot_info = take(cap * sizeof(moe::SlotRec));
   L->act = take(te * (size_t)d.inter * 4);
   L->shared_act = take(R * Is * 4);
   L->total = o;
@@ -277,6 +278,7 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   a.pair_to_perm = reinterpret_cast<int32_t *>(ws + L.pair_to_perm);
   a.active = reinterpret_cast<int32_t *>(ws + L.active_experts);
   a.active_count = reinterpret_cast<int32_t *>(ws + L.active_count);
+  a.slots = reinterpret_cast<moe::SlotRec *>(ws + L.slot_info);
   a.act = reinterpret_cast<float *>(ws + L.act);
   a.sact = reinterpret_cast<float *>(ws + L.shared_act);
   a.sync = reinterpret_cast<unsigned *>(ws + L.sync);

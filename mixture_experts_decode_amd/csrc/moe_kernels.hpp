@@ -61,6 +61,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Per active slot: what the down launch needs to start streaming, in one
+// 64-byte record (the routing publishes it).
+struct alignas(64) SlotRec {
+  int32_t e, off, np, pad;
+  uint64_t dw, ds, db, pad2;
+  uint64_t pad3[2];
+};
+static_assert(sizeof(SlotRec) == 64, "slot records are 64 bytes");
+
 // Everything a forward's kernels read or write (kernel argument, by value).
 struct Args {
   int H, E, K, I, Is, m, te, cap, act_fmt, expert_fmt, routing;
@@ -85,6 +94,7 @@ struct Args {
   int32_t *pair_to_perm;   // [te]
   int32_t *active;         // [cap]
   int32_t *active_count;   // [1]
+  SlotRec *slots;          // [cap]
   float *act;              // [te, I]
   float *sact;             // [m, Is]
   unsigned *sync;          // [SYNC_WORDS]
@@ -964,6 +974,22 @@ __device__ __forceinline__ void route_select(const Args &a, RouteLDS &L, bool pu
       a.pair_to_perm[p] = pos;
     }
   }
+  if (publish) {
+    for (int u = tid; u < L.nact; u += THREADS) {
+      const int e = L.active[u];
+      SlotRec r;
+      r.e = e;
+      r.off = L.off[e];
+      r.np = L.off[e + 1] - L.off[e];
+      r.pad = 0;
+      r.dw = a.dw ? a.dw[e] : 0ull;
+      r.ds = a.ds ? a.ds[e] : 0ull;
+      r.db = a.db ? a.db[e] : 0ull;
+      r.pad2 = 0ull;
+      r.pad3[0] = r.pad3[1] = 0ull;
+      a.slots[u] = r;
+    }
+  }
   __syncthreads();
 }
 
@@ -1037,21 +1063,44 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   static_assert(DOWN_RD % GR == 0, "down rows must split over lane groups");
   __shared__ float y_lds[MAX_PAIRS * MAX_DOWN_TILE];
   __shared__ float ys_lds[MAX_ROWS * MAX_DOWN_TILE];
-  const int wave = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int H = a.H, I = a.I, Is = a.Is, m = a.m;
+  __shared__ float s_c[MAX_PAIRS];               // blend coefficient of pair p
+  __shared__ int s_perm[MAX_PAIRS];              // sorted position of pair p
+  __shared__ float s_gamma[MAX_ROWS];
+  const int wave = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int H = a.H, I = a.I, Is = a.Is, m = a.m, te = a.te;
   const int DQ = a.down_dq, HT = DOWN_RD * DQ, h0 = tile * HT;
-  const int nact = clamp_i(a.active_count[0], 0, a.cap);
   const bool shared = (a.flags & SHARED) != 0;
-  const int units = nact + (shared ? 1 : 0);
+  const int sh = shared ? 1 : 0;                 // the shared expert is unit 0
+  const bool before = (a.flags & WEIGHT_BEFORE) != 0;
+  const bool gated = (a.flags & SHARED_GATED) != 0;
+
+  // Blend operands, requested now and used after the streaming.
+  float my_c = 0.f, my_g = 0.f;
+  int my_perm = 0;
+  if (tid < te) {
+    my_c = before ? 1.0f : a.topk_w[tid];
+    my_perm = clamp_i(a.pair_to_perm[tid], 0, te - 1);
+  }
+  if (tid < m) my_g = gated ? a.row_gate[tid] : 1.0f;
+  // This wave's first routed record, requested together with the count (the
+  // record array always has cap entries; a stale one is never used).
+  const int slot0 = clamp_i(wave / DQ - sh, 0, a.cap - 1);
+  const SlotRec pre = a.slots[slot0];
+  const int nact = clamp_i(a.active_count[0], 0, a.cap);
+  const int units = nact + sh;
 
   for (int su = wave; su < units * DQ; su += DOWN_WPB) {
     const int u = su / DQ, q = su - u * DQ;
     const int hb = h0 + q * DOWN_RD;             // first column of this row block
-    if (u < nact) {
-      const int e = clamp_i(a.active[u], 0, a.E - 1);
-      const int off = clamp_i(a.offsets[e], 0, a.te);
-      const int np = clamp_i(a.offsets[e + 1], off, a.te) - off;
-      const void *dw = tbl(a.dw, e), *ds = tbl(a.ds, e), *db = tbl(a.db, e);
+    if (u >= sh) {
+      const SlotRec rec = su == wave ? pre : a.slots[u - sh];
+      const int e = uniform_i(clamp_i(rec.e, 0, a.E - 1));
+      const int off = uniform_i(clamp_i(rec.off, 0, te));
+      const int np = uniform_i(clamp_i(rec.np, 0, te - off));
+      const void *dw = reinterpret_cast<const void *>(rec.dw);
+      const void *ds = reinterpret_cast<const void *>(rec.ds);
+      const void *db = reinterpret_cast<const void *>(rec.db);
+      (void)e;
       const int grp = lane / LPR;
       const Mat<EF> md = make_mat<EF>(dw, ds, db, H, I);
       Row<EF> rows[RGR];
@@ -1092,10 +1141,13 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
       });
     }
   }
+  if (tid < te) {
+    s_c[tid] = my_c;
+    s_perm[tid] = my_perm;
+  }
+  if (tid < m) s_gamma[tid] = my_g;
   __syncthreads();
 
-  const bool before = (a.flags & WEIGHT_BEFORE) != 0;
-  const bool gated = (a.flags & SHARED_GATED) != 0;
   const bool out_f32 = (a.flags & OUT_F32) != 0 || ACT == F32;
   const int k = a.K;
   for (int t = threadIdx.x; t < m * HT; t += DOWN_THREADS) {
@@ -1104,10 +1156,9 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
     float o = 0.f;
     for (int j = 0; j < k; ++j) {
       const int p = r * k + j;
-      const float c = before ? 1.0f : a.topk_w[p];
-      o = __builtin_fmaf(c, y_lds[clamp_i(a.pair_to_perm[p], 0, a.te - 1) * HT + hl], o);
+      o = __builtin_fmaf(s_c[p], y_lds[s_perm[p] * HT + hl], o);
     }
-    if (shared) o = __builtin_fmaf(gated ? a.row_gate[r] : 1.0f, ys_lds[r * HT + hl], o);
+    if (shared) o = __builtin_fmaf(s_gamma[r], ys_lds[r * HT + hl], o);
     if (out_f32)
       reinterpret_cast<float *>(a.out)[(size_t)r * H + h] = o;
     else
