@@ -29,6 +29,7 @@ struct moe_decode_plan {
   int variant;  // kSplit
   const moe::Variant *kv[moe::MAX_ROWS + 1];   // per m
   moe::launch_fn gate_up[moe::MAX_ROWS + 1];   // per m (split arrangement)
+  bool route_in_gu[moe::MAX_ROWS + 1];         // per m: where the routing is computed
 };
 
 namespace {
@@ -74,6 +75,18 @@ constexpr int kGateUpMaxBlocks = 1024;
 bool fused_requested() {
   const char *v = getenv("MOE_DECODE_VARIANT");
   return v && strcmp(v, "fused") == 0;
+}
+
+// Where a forward of m rows computes the routing.  Every gate/up workgroup
+// (from the logits, in LDS) starts the expert streaming soonest when the
+// routing is small; for more rows the router workgroup that finishes last
+// computes it once and publishes it.  MOE_DECODE_ROUTE=gate_up|once forces
+// one placement (both give identical results; the tests run both).
+bool route_in_gate_up(int m) {
+  const char *v = getenv("MOE_DECODE_ROUTE");
+  if (v && strcmp(v, "gate_up") == 0) return true;
+  if (v && strcmp(v, "once") == 0) return false;
+  return m == 1;
 }
 
 // Input vectors handled per pass over a weight tile: routed rows (pairs of
@@ -291,8 +304,10 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   const int ni_r = d.expert_fmt >= MOE_AFF4_G64 ? 4 : 2;   // gate_up_ni<EF>()
   const int ni_s = 2;                                       // gate_up_ni<ACT>()
   const int nrb = (m + 7) / 8;                               // input-row blocks per router row
-  a.n_router = ((d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0)) * nrb + wpb - 1) / wpb;
-  a.n_shared_gu = shared ? ((a.Is + ni_s - 1) / ni_s + wpb - 1) / wpb : 0;
+  a.route_in_gu = plan->route_in_gu[m] ? 1 : 0;
+  a.n_router = (d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0)) * nrb;   // router units
+  a.n_router_wg = (a.n_router + moe::ROUTE_UNITS_PER_WG - 1) / moe::ROUTE_UNITS_PER_WG;
+  a.n_shared_gu = shared ? ((a.Is + ni_s - 1) / ni_s + moe::ROUTE_WPB - 1) / moe::ROUTE_WPB : 0;
   a.gu_items_per_slot = ((d.inter + ni_r - 1) / ni_r + wpb - 1) / wpb;
   a.n_routed_gu = a.cap * a.gu_items_per_slot;
   // Two row blocks per down tile when the units would leave waves idle and
@@ -315,9 +330,9 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto ev = [&](int i) -> hipEvent_t { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
   hipError_t e;
-  if ((e = moe::launch_route(d.act_fmt, cs, a, a.n_router + a.n_shared_gu, s, ev(0), ev(1))) != hipSuccess)
+  if ((e = moe::launch_route(d.act_fmt, cs, a, a.n_router_wg + a.n_shared_gu, s, ev(0), ev(1))) != hipSuccess)
     return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
-  // gate_up: a grid-stride launch; every workgroup pays one routing prologue.
+  // gate_up: a grid-stride launch over the active slots' items.
   const int gu_blocks = a.n_routed_gu < kGateUpMaxBlocks ? a.n_routed_gu : kGateUpMaxBlocks;
   if ((e = plan->gate_up[m](a, gu_blocks, s, ev(2), ev(3))) != hipSuccess)
     return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
@@ -350,6 +365,7 @@ moe_status moe_decode_plan(const moe_decode_desc *desc, moe_decode_plan_t **plan
       delete p;
       return fail(MOE_EUNSUPPORTED, "no kernel variant for m = %d", m);
     }
+    p->route_in_gu[m] = route_in_gate_up(m);
   }
   layout_for(p->d, &p->L);
   *plan = p;

@@ -41,6 +41,10 @@ constexpr int THREADS = 256;            // route and gate/up: 4 waves per workgr
 constexpr int WPB = THREADS / WAVE;
 constexpr int DOWN_THREADS = 512;       // down + blend: 8 waves, one active slot each at m = 1
 constexpr int DOWN_WPB = DOWN_THREADS / WAVE;
+constexpr int ROUTE_THREADS = 512;      // route launch: 8 waves
+constexpr int ROUTE_WPB = ROUTE_THREADS / WAVE;
+constexpr int RSPLIT = 4;               // waves per router row (its H is split in 4)
+constexpr int ROUTE_UNITS_PER_WG = ROUTE_WPB / RSPLIT;
 constexpr int MAX_ROWS = 32;
 constexpr int MAX_TOPK = 16;
 constexpr int MAX_EXPERTS = 256;
@@ -48,9 +52,11 @@ constexpr int MAX_PAIRS = MAX_ROWS * MAX_TOPK;
 constexpr int DOWN_RD = 8;              // down rows per wave sub-unit
 constexpr int MAX_DOWN_TILE = 2 * DOWN_RD;
 
-// Reserved completion words in the workspace (zeroed by
-// moe_decode_workspace_init; unused by the current kernels).
+// Reserved words in the workspace (zeroed by moe_decode_workspace_init).
+// Word 0 counts the router workgroups that have stored their logits; the
+// last one resets it, so it is zero between calls.  Nothing ever waits on it.
 constexpr int SYNC_WORDS = 512;
+constexpr int SYNC_ROUTER_TICKET = 0;
 
 // Rows of intermediate per gate/up wave: 2 for 16-byte-per-8-or-4 element
 // formats, 4 for the 4-bit ones (their rows are 4x shorter).
@@ -61,14 +67,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Per active slot: what the down launch needs to start streaming, in one
-// 64-byte record (the routing publishes it).
-struct alignas(64) SlotRec {
+// Per active slot: what the gate/up and down launches need to start
+// streaming, in one 128-byte record (the routing publishes it).
+struct alignas(128) SlotRec {
   int32_t e, off, np, pad;
-  uint64_t dw, ds, db, pad2;
-  uint64_t pad3[2];
+  uint64_t gw, uw, gs, us, gb, ub, dw, ds, db;
+  uint64_t pad2[5];
 };
-static_assert(sizeof(SlotRec) == 64, "slot records are 64 bytes");
+static_assert(sizeof(SlotRec) == 128, "slot records are 128 bytes");
 
 // Everything a forward's kernels read or write (kernel argument, by value).
 struct Args {
@@ -76,7 +82,8 @@ struct Args {
   unsigned flags;
   float rsf;
   // work items
-  int n_router, n_shared_gu, gu_items_per_slot, n_routed_gu, n_down, down_dq;
+  int n_router, n_router_wg, n_shared_gu, gu_items_per_slot, n_routed_gu, n_down, down_dq;
+  int route_in_gu;         // 1: every gate/up workgroup routes; 0: the last router workgroup does
   const void *x;
   void *out;
   int32_t *idx_out;
@@ -108,6 +115,15 @@ __device__ __forceinline__ u32x4 ld_stream16(const void *p) {
 }
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
+
+// Device-coherent (agent-scope) accesses: they bypass the per-XCD caches'
+// non-coherent state, for data one workgroup hands to another in a launch.
+__device__ __forceinline__ void store_coherent(double *p, double v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double load_coherent(const double *p) {
+  return __hip_atomic_load(const_cast<double *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
@@ -705,32 +721,34 @@ __device__ __forceinline__ int clamp_i(int v, int lo, int hi) { return v < lo ? 
 //
 // Router unit u = (router row e, block of up to 8 input rows): logits[r, e] =
 // sum_h x[r,h] W[e,h], every product and sum in double.  Row E is the shared
-// expert's gate vector w_g.  The loads of a chunk step (the router chunk and
-// the 8 rows' x chunks) are issued before any is used.
+// expert's gate vector w_g.  RSPLIT waves share a unit, wave `part` taking the
+// part-th quarter of the chunks; each returns its per-row partial totals (in
+// every lane), which the caller adds in part order.  The loads of a chunk
+// step (the router chunk and the rows' x chunks) are issued before any is
+// used.
 template <int ACT>
-__device__ __forceinline__ void router_unit(const Args &a, int unit) {
+__device__ __forceinline__ void router_part(const Args &a, int unit, int part, double (&tot)[8]) {
   constexpr int EPC = ACT == F32 ? 4 : 8;
   constexpr int RU = 4;                      // chunk steps whose loads are in flight together
   const int lane = threadIdx.x & 63;
   const int nrows = a.E + ((a.flags & SHARED_GATED) ? 1 : 0);
   const int e = unit % nrows, r0 = (unit / nrows) * 8;
-  if (r0 >= a.m) return;
   const int nr = min(8, a.m - r0);           // input rows of this unit
   const int nchunks = a.H / EPC;
+  const int c0 = part * nchunks / RSPLIT, c1 = (part + 1) * nchunks / RSPLIT;
   const size_t xstride = (size_t)a.H * act_bytes(ACT);
   const char *wrow = e < a.E ? reinterpret_cast<const char *>(a.router) + (size_t)e * xstride
                              : reinterpret_cast<const char *>(a.sgv);
   const char *x = reinterpret_cast<const char *>(a.x) + (size_t)r0 * xstride;
-  const int LD = a.E + 1;
   double acc[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = 0.0;
-  for (int base = 0; base < nchunks; base += WAVE * RU) {
+  for (int base = c0; base < c1; base += WAVE * RU) {
     u32x4 q[RU];
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
       const int ch = base + lane + u * WAVE;
-      if (ch < nchunks) q[u] = ld16(wrow + (size_t)ch * 16);
+      if (ch < c1) q[u] = ld16(wrow + (size_t)ch * 16);
     }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -739,12 +757,12 @@ __device__ __forceinline__ void router_unit(const Args &a, int unit) {
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
           const int ch = base + lane + u * WAVE;
-          if (ch < nchunks) v[u] = ld16(x + (size_t)r * xstride + (size_t)ch * 16);
+          if (ch < c1) v[u] = ld16(x + (size_t)r * xstride + (size_t)ch * 16);
         }
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
           const int ch = base + lane + u * WAVE;
-          if (ch < nchunks) {
+          if (ch < c1) {
             float w[EPC], xv[EPC];
             if constexpr (ACT == F32) {
               w[0] = __uint_as_float(q[u].x); w[1] = __uint_as_float(q[u].y);
@@ -765,26 +783,33 @@ __device__ __forceinline__ void router_unit(const Args &a, int unit) {
     }
   }
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    if (r < nr) {
-      const double t = wave_sum_f64(acc[r]);
-      if (lane == 0) a.logits[(size_t)(r0 + r) * LD + e] = t;
-    }
-  }
+  for (int r = 0; r < 8; ++r) tot[r] = r < nr ? wave_sum_f64(acc[r]) : 0.0;
 }
 
 // --------------------------------------------------------- top-k and sort
 //
-// Routing state of one forward, rebuilt in LDS by every gate/up workgroup
-// from the logits (each computes the same result; block 0 also publishes it
-// to the workspace for the down/blend launch and the caller).
-struct RouteLDS {
+// Routing state of one forward, built in LDS by the router workgroup that
+// finishes last, then published to the workspace for the gate/up and down
+// launches and the caller.
+constexpr int RANK_MAX_CMP = 16;        // rank selection: at most this many comparisons per thread
+
+template <int NCAND> struct RankLDS {
+  unsigned long long key[NCAND];  // order key of candidate (r, i) at r * E + i
+  double lg[NCAND];               // its logit
+  int rank[NCAND];
+  double sel[MAX_PAIRS];          // logit of the expert in slot p
+};
+
+template <int NCAND> struct RouteLDS {
+  static constexpr int kCand = NCAND;   // rank selection serves at most NCAND = m * E candidates
+  RankLDS<NCAND> rk;
   int idx[MAX_PAIRS];        // selected expert of pair p = r*k + j
   float w[MAX_PAIRS];        // routing weight of pair p (times rsf)
   unsigned mask[MAX_EXPERTS];  // bit r: row r chose expert e
   int off[MAX_EXPERTS + 1];  // start of each expert's run in `sorted`
   int sorted[MAX_PAIRS];     // pairs sorted by expert, stable
   int active[MAX_EXPERTS];   // experts with a pair, ascending
+  int slot_of[MAX_EXPERTS];  // position of an active expert in `active`
   int nact;
 };
 
@@ -807,6 +832,34 @@ __device__ __forceinline__ void cx(unsigned long long &ka, int &ia, double &la, 
   }
 }
 
+// Routing weight of the slot held by this lane (lanes 0..k-1 hold slots
+// 0..k-1; `mine` marks them), in double: softmax over all experts -- with
+// norm_topk_prob the full denominator cancels and only the selected terms
+// remain -- or the unbiased sigmoid (the bias only selects), then the
+// normalisation.  lr: the row's logits; lmax: slot 0's logit (the row's
+// largest under softmax routing).  Every lane of the wave must call it.
+__device__ __forceinline__ double row_weights(const Args &a, const double *lr, bool mine, double my_l,
+                                              double lmax) {
+  const int lane = threadIdx.x & 63, E = a.E;
+  double w;
+  if (a.routing == ROUTE_SOFTMAX) {
+    const double num = mine ? exp(my_l - lmax) : 0.0;
+    double den;
+    if (a.flags & NORM_TOPK) {
+      den = wave_sum_f64(num);
+    } else {
+      double s = 0.0;
+      for (int e = lane; e < E; e += WAVE) s += exp(load_coherent(lr + e) - lmax);
+      den = wave_sum_f64(s);
+    }
+    w = num / den;
+  } else {
+    w = mine ? sigmoid_d(my_l) : 0.0;
+    if (a.flags & NORM_TOPK) w = w / wave_sum_f64(w);
+  }
+  return w;
+}
+
 // Top-k of row r by one wave.  Keys are compared as order-preserving 64-bit
 // integers, which is exactly the order of the double keys.  Lane l holds
 // experts 4l..4l+3 (E <= 256), sorts them locally by (key desc, index asc),
@@ -825,7 +878,7 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, int &my_e, double
   for (int i = 0; i < 4; ++i) {
     const int e = 4 * lane + i;
     const bool ok = e < E;
-    lg[i] = ok ? lr[e] : 0.0;
+    lg[i] = ok ? load_coherent(lr + e) : 0.0;
     double kd = lg[i];
     if (ok && a.routing == ROUTE_SIGMOID_BIAS) kd = sigmoid_d(lg[i]) + (double)a.ebias[e];
     key[i] = ok ? order_key(kd) : 0ull;        // below every real key
@@ -869,40 +922,90 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, int &my_e, double
       my_l = lw;
     }
   }
-  // Weights in double, slot j in lane j.
-  const bool mine = lane < k;
-  double w;
-  if (a.routing == ROUTE_SOFTMAX) {
-    // softmax over all experts; with norm_topk_prob the full denominator
-    // cancels and only the selected terms remain.
-    const double num = mine ? exp(my_l - lmax) : 0.0;
-    double den;
-    if (a.flags & NORM_TOPK) {
-      den = wave_sum_f64(num);
-    } else {
-      double s = 0.0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * lane + i < E) s += exp(lr[4 * lane + i] - lmax);
-      den = wave_sum_f64(s);
-    }
-    w = num / den;
-  } else {
-    w = mine ? sigmoid_d(my_l) : 0.0;   // unbiased: the bias only selects
-    if (a.flags & NORM_TOPK) w = w / wave_sum_f64(w);
-  }
-  my_w = w;
+  my_w = row_weights(a, lr, lane < k, my_l, lmax);
 }
 
-// Every thread of the workgroup: routing of all m rows into L.  publish:
-// also write the workspace arrays (and the caller's idx/w outputs).
-__device__ __forceinline__ void route_select(const Args &a, RouteLDS &L, bool publish) {
+// Every thread of a workgroup of NT threads: routing of all m rows into L,
+// published to the workspace (and the caller's idx/w outputs), with one
+// SlotRec per active slot.
+template <int NT, typename LDS>
+__device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish) {
+  constexpr int NW = NT / WAVE;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int E = a.E, k = a.K, m = a.m, te = m * k;
-  for (int r = wave; r < m; r += WPB) {
+  const int nc = m * E;
+  // Thread e < E requests expert e's table entries now; if e turns out
+  // active it writes that slot's record at the end.
+  uint64_t tb[9] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
+  if (tid < E) {
+    L.mask[tid] = 0u;
+    if (publish) {
+      tb[0] = a.gw[tid]; tb[1] = a.uw[tid]; tb[2] = a.dw[tid];
+      if (a.gs) { tb[3] = a.gs[tid]; tb[4] = a.us[tid]; tb[5] = a.ds[tid]; }
+      if (a.gb) { tb[6] = a.gb[tid]; tb[7] = a.ub[tid]; tb[8] = a.db[tid]; }
+    }
+  }
+  const bool by_rank = nc <= LDS::kCand && nc * E <= NT * RANK_MAX_CMP;
+  if (by_rank) {
+    // Selection by rank: candidate (r, i) is ranked by the number of the
+    // row's keys that beat it (a larger key, or an equal key with a lower
+    // index) -- a strict order, so ranks 0..k-1 are the slots in order.  S
+    // threads share a candidate's comparisons.
+    for (int c = tid; c < nc; c += NT) {
+      const int r = c / E, i = c - r * E;
+      const double l = load_coherent(a.logits + (size_t)r * (E + 1) + i);
+      const double kd = a.routing == ROUTE_SIGMOID_BIAS ? sigmoid_d(l) + (double)a.ebias[i] : l;
+      L.rk.key[c] = order_key(kd);
+      L.rk.lg[c] = l;
+      L.rk.rank[c] = 0;
+    }
+    __syncthreads();
+    int S = 1;
+    while (S < 64 && nc * S * 2 <= NT) S *= 2;
+    for (int t = tid; t < nc * S; t += NT) {
+      const int c = t / S, part = t - c * S;
+      const int r = c / E, i = c - r * E;
+      // Part `part` takes keys part, part + S, ...: the S threads of a
+      // candidate read adjacent words (distinct LDS banks).
+      const unsigned long long ki = L.rk.key[c];
+      const unsigned long long *kr = L.rk.key + r * E;
+      int cnt = 0;
+      int j = part;
+      for (; j + 7 * S < E; j += 8 * S) {
+        unsigned long long kj[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) kj[q] = kr[j + q * S];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) cnt += (kj[q] > ki || (kj[q] == ki && j + q * S < i)) ? 1 : 0;
+      }
+      for (; j < E; j += S) {
+        const unsigned long long kj = kr[j];
+        cnt += (kj > ki || (kj == ki && j < i)) ? 1 : 0;
+      }
+      if (cnt) atomicAdd(&L.rk.rank[c], cnt);
+    }
+    __syncthreads();
+    for (int c = tid; c < nc; c += NT) {
+      const int rank = L.rk.rank[c];
+      if (rank < k) {
+        const int r = c / E, p = r * k + rank;
+        L.idx[p] = c - r * E;
+        L.rk.sel[p] = L.rk.lg[c];
+      }
+    }
+    __syncthreads();
+  }
+  for (int r = wave; r < m; r += NW) {
     int e;
     double w;
-    row_topk(a, r, e, w);
+    if (by_rank) {
+      const bool mine = lane < k;
+      e = mine ? L.idx[r * k + lane] : 0;
+      const double my_l = mine ? L.rk.sel[r * k + lane] : 0.0;
+      w = row_weights(a, a.logits + (size_t)r * (E + 1), mine, my_l, L.rk.sel[r * k]);
+    } else {
+      row_topk(a, r, e, w);
+    }
     if (lane < k) {
       const float wf = (float)(w * (double)a.rsf);
       const int p = r * k + lane;
@@ -916,14 +1019,13 @@ __device__ __forceinline__ void route_select(const Args &a, RouteLDS &L, bool pu
       }
     }
     if (publish && lane == 0 && (a.flags & SHARED_GATED))
-      a.row_gate[r] = (float)sigmoid_d(a.logits[(size_t)r * (E + 1) + E]);
+      a.row_gate[r] = (float)sigmoid_d(load_coherent(a.logits + (size_t)r * (E + 1) + E));
   }
-  for (int e = tid; e < E; e += THREADS) L.mask[e] = 0u;
   __syncthreads();
-  // Stable counting sort by expert.  A row selects an expert at most once, so
+  // Stable counting sort by expert (mask zeroed at the start).  A row selects an expert at most once, so
   // bit r of mask[e] says whether row r chose e, and a pair's rank inside its
   // expert is the number of earlier rows that chose the same expert.
-  for (int p = tid; p < te; p += THREADS) atomicOr(&L.mask[L.idx[p]], 1u << (p / k));
+  for (int p = tid; p < te; p += NT) atomicOr(&L.mask[L.idx[p]], 1u << (p / k));
   __syncthreads();
   if (wave == 0) {
     // Lane l: experts 4l..4l+3; wave-wide exclusive scans of counts and of
@@ -949,6 +1051,7 @@ __device__ __forceinline__ void route_select(const Args &a, RouteLDS &L, bool pu
         if (publish) a.offsets[e] = co;
         if (act[i]) {
           L.active[ao] = e;
+          L.slot_of[e] = ao;
           if (publish) a.active[ao] = e;
         }
       }
@@ -965,7 +1068,7 @@ __device__ __forceinline__ void route_select(const Args &a, RouteLDS &L, bool pu
     }
   }
   __syncthreads();
-  for (int p = tid; p < te; p += THREADS) {
+  for (int p = tid; p < te; p += NT) {
     const int e = L.idx[p], r = p / k;
     const int pos = L.off[e] + __popc(L.mask[e] & ((1u << r) - 1u));
     L.sorted[pos] = p;
@@ -974,21 +1077,19 @@ __device__ __forceinline__ void route_select(const Args &a, RouteLDS &L, bool pu
       a.pair_to_perm[p] = pos;
     }
   }
-  if (publish) {
-    for (int u = tid; u < L.nact; u += THREADS) {
-      const int e = L.active[u];
-      SlotRec r;
-      r.e = e;
-      r.off = L.off[e];
-      r.np = L.off[e + 1] - L.off[e];
-      r.pad = 0;
-      r.dw = a.dw ? a.dw[e] : 0ull;
-      r.ds = a.ds ? a.ds[e] : 0ull;
-      r.db = a.db ? a.db[e] : 0ull;
-      r.pad2 = 0ull;
-      r.pad3[0] = r.pad3[1] = 0ull;
-      a.slots[u] = r;
-    }
+  if (publish && tid < E && L.mask[tid] != 0u) {
+    const int e = tid;
+    SlotRec rec;
+    rec.e = e;
+    rec.off = L.off[e];
+    rec.np = L.off[e + 1] - L.off[e];
+    rec.pad = 0;
+    rec.gw = tb[0]; rec.uw = tb[1]; rec.dw = tb[2];
+    rec.gs = tb[3]; rec.us = tb[4]; rec.ds = tb[5];
+    rec.gb = tb[6]; rec.ub = tb[7]; rec.db = tb[8];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) rec.pad2[i] = 0ull;
+    a.slots[L.slot_of[e]] = rec;
   }
   __syncthreads();
 }
@@ -1168,41 +1269,101 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
 
 // ------------------------------------------------------------------ kernels
 
-// Launch 1: router units (4 per workgroup, one per wave), then the shared
-// expert's gate/up items -- these need no routing, so they stream meanwhile.
+// Launch 1: router workgroups (ROUTE_UNITS_PER_WG units, RSPLIT waves each),
+// then the shared expert's gate/up items -- these need no routing, so they
+// stream meanwhile.  Each router workgroup stores its logits and takes a
+// ticket; the one that takes the last ticket (every other router workgroup
+// has stored and released its logits by then) computes the routing once for
+// the whole forward and resets the counter.  No workgroup waits for another.
 template <int ACT, int CS>
-__global__ __launch_bounds__(THREADS) void route_kernel(Args a) {
-  const int item = blockIdx.x;
-  if (item < a.n_router) {
-    router_unit<ACT>(a, item * WPB + (threadIdx.x >> 6));
+__global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
+  const int item = blockIdx.x, tid = threadIdx.x;
+  const int wave = uniform_i(threadIdx.x >> 6);
+  if (item < a.n_router_wg) {
+    __shared__ double s_part[ROUTE_WPB][8];
+    __shared__ unsigned s_ticket;
+    __shared__ RouteLDS<1024> L;
+    const int unit = item * ROUTE_UNITS_PER_WG + wave / RSPLIT, part = wave % RSPLIT;
+    const bool live = unit < a.n_router;
+    double tot[8];
+    if (live) router_part<ACT>(a, unit, part, tot);
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) s_part[wave][r] = live ? tot[r] : 0.0;
+    }
+    __syncthreads();
+    if (tid < ROUTE_UNITS_PER_WG * 8) {
+      const int ul = tid / 8, r = tid % 8, u = item * ROUTE_UNITS_PER_WG + ul;
+      const int nrows = a.E + ((a.flags & SHARED_GATED) ? 1 : 0);
+      const int e = u % nrows, rr = (u / nrows) * 8 + r;
+      if (u < a.n_router && rr < a.m) {
+        double t = s_part[ul * RSPLIT][r];
+#pragma unroll
+        for (int p = 1; p < RSPLIT; ++p) t += s_part[ul * RSPLIT + p][r];
+        store_coherent(a.logits + (size_t)rr * (a.E + 1) + e, t);
+      }
+    }
+    if (a.route_in_gu) return;   // every gate/up workgroup routes from the logits
+    // The logits travel only through device-coherent accesses, so completing
+    // the stores orders them before the ticket; no cache-wide fence needed.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      s_ticket = __hip_atomic_fetch_add(a.sync + SYNC_ROUTER_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_ticket != (unsigned)(a.n_router_wg - 1)) return;
+    route_all<ROUTE_THREADS>(a, L, true);
+    if (tid == 0) a.sync[SYNC_ROUTER_TICKET] = 0u;  // every ticket is taken
     return;
   }
   constexpr int NI = gate_up_ni<ACT>();
-  const int i0 = ((item - a.n_router) * WPB + uniform_i(threadIdx.x >> 6)) * NI;
+  const int i0 = ((item - a.n_router_wg) * ROUTE_WPB + wave) * NI;
   if (i0 < a.Is)
     gate_up_rows<ACT, ACT, CS, NI>(a, a.sgw, a.suw, nullptr, nullptr, nullptr, nullptr, a.Is, i0, 0,
                                    a.m, nullptr, nullptr, a.sact, a.Is);
 }
 
-// Launch 2: every workgroup first rebuilds the routing from the logits
-// (block 0 publishes it), then takes the items (active slot s, row block b)
-// blockIdx, blockIdx + gridDim, ... of the nact * items_per_slot that exist;
-// its waves take row groups b * 4 + wave of slot s.
+// Launch 2: items (active slot s, row block b), blockIdx, blockIdx +
+// gridDim, ... of the nact * items_per_slot that exist; its waves take row
+// groups b * 4 + wave of slot s.  Either the routing is published (the first
+// item's slot record is requested together with the active count), or --
+// route_in_gu, chosen for small m where it starts the streaming sooner --
+// every workgroup computes it from the logits in LDS and block 0 publishes.
 template <int EF, int ACT, int CR, int CS>
 __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
   constexpr int NI = gate_up_ni<EF>();
-  __shared__ RouteLDS L;
-  route_select(a, L, blockIdx.x == 0);
-  const int n = L.nact * a.gu_items_per_slot;
+  const int ips = a.gu_items_per_slot;
+  const int wave = uniform_i(threadIdx.x >> 6);
+  if (a.route_in_gu) {
+    __shared__ RouteLDS<256> L;
+    route_all<THREADS>(a, L, blockIdx.x == 0);
+    const int n = L.nact * ips;
+    for (int it = blockIdx.x; it < n; it += gridDim.x) {
+      const int s = it / ips, b = it - s * ips;
+      const int e = uniform_i(clamp_i(L.active[s], 0, a.E - 1));
+      const int off = uniform_i(L.off[e]), np = uniform_i(L.off[e + 1]) - off;
+      const int i0 = (b * WPB + wave) * NI;
+      if (i0 < a.I)
+        gate_up_rows<EF, ACT, CR, NI>(a, tbl(a.gw, e), tbl(a.uw, e), tbl(a.gs, e), tbl(a.us, e),
+                                      tbl(a.gb, e), tbl(a.ub, e), a.I, i0, off, np, L.sorted + off,
+                                      L.w, a.act, a.I);
+    }
+    return;
+  }
+  const SlotRec pre = a.slots[clamp_i((int)blockIdx.x / ips, 0, a.cap - 1)];
+  const int nact = clamp_i(a.active_count[0], 0, a.cap);
+  const int n = nact * ips;
   for (int it = blockIdx.x; it < n; it += gridDim.x) {
-    const int s = it / a.gu_items_per_slot, b = it - s * a.gu_items_per_slot;
-    const int e = uniform_i(clamp_i(L.active[s], 0, a.E - 1));
-    const int off = uniform_i(L.off[e]), np = uniform_i(L.off[e + 1]) - off;
-    const int i0 = (b * WPB + uniform_i(threadIdx.x >> 6)) * NI;
+    const int s = it / ips, b = it - s * ips;
+    const SlotRec rec = it == (int)blockIdx.x ? pre : a.slots[s];
+    const int off = uniform_i(clamp_i(rec.off, 0, a.te));
+    const int np = uniform_i(clamp_i(rec.np, 0, a.te - off));
+    const int i0 = (b * WPB + wave) * NI;
     if (i0 < a.I)
-      gate_up_rows<EF, ACT, CR, NI>(a, tbl(a.gw, e), tbl(a.uw, e), tbl(a.gs, e), tbl(a.us, e),
-                                    tbl(a.gb, e), tbl(a.ub, e), a.I, i0, off, np, L.sorted + off,
-                                    L.w, a.act, a.I);
+      gate_up_rows<EF, ACT, CR, NI>(a, reinterpret_cast<const void *>(rec.gw), reinterpret_cast<const void *>(rec.uw),
+                                    reinterpret_cast<const void *>(rec.gs), reinterpret_cast<const void *>(rec.us),
+                                    reinterpret_cast<const void *>(rec.gb), reinterpret_cast<const void *>(rec.ub),
+                                    a.I, i0, off, np, a.sorted_pair + off, a.topk_w, a.act, a.I);
   }
 }
 

@@ -10,7 +10,7 @@ __global__ void clear_sync_kernel(unsigned *sync, int n) {
 
 template <int ACT, int CS>
 static hipError_t route_launch(const Args &a, int blocks, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
-  return launch_timed(route_kernel<ACT, CS>, blocks, THREADS, st, t0, t1, a);
+  return launch_timed(route_kernel<ACT, CS>, blocks, ROUTE_THREADS, st, t0, t1, a);
 }
 
 // cs: shared-expert rows per pass, one of the values the host's pass

@@ -230,14 +230,18 @@ def test_largest_pair_count_and_dense_limit():
     check(spec2, got, idx, w, ref2, 4, TOL["bf16"], "k=E")
 
 
-def test_zero_input_and_ties():
-    spec = small(num_experts=8, top_k=3, routing="softmax")
+# (E, k, m): the first takes the rank selection (m * E small), the second the
+# round-by-round wave selection.
+@pytest.mark.parametrize("E,k,m", [(8, 3, 2), (256, 8, 8)])
+def test_zero_input_and_ties(E, k, m):
+    spec = small(num_experts=E, top_k=k, routing="softmax", rows=(m,))
     layer = synth.make_layer(spec, seed=13)
-    x = np.zeros((2, spec.hidden), np.uint16)
+    x = np.zeros((m, spec.hidden), np.uint16)
     dl = DeviceLayer(layer)
-    got, idx, w = run(dl, x, 2)
-    assert np.array_equal(idx, np.tile(np.arange(3, dtype=np.int32), (2, 1)))
-    assert np.all(w == np.float32(1.0 / 3.0)) and np.all(got == 0.0)
+    say(f"[gpu] ties E={E} k={k} m={m}")
+    got, idx, w = run(dl, x, m)
+    assert np.array_equal(idx, np.tile(np.arange(k, dtype=np.int32), (m, 1)))
+    assert np.all(w == np.float32(1.0 / k)) and np.all(got == 0.0)
     # Duplicate router rows: the lower index ranks first.
     x = layer.x(0)
     ref = oracle.forward(layer, x)
@@ -246,9 +250,9 @@ def test_zero_input_and_ties():
         layer.router[0] = layer.router[win]
         ref = oracle.forward(layer, x)
         dl = DeviceLayer(layer)
-        got, idx, w = run(dl, x, 1)
+        got, idx, w = run(dl, x, m)
         assert list(idx[0][:2]) == [0, win]
-        check(spec, got, idx, w, ref, 1, TOL["bf16"], "tie")
+        check(spec, got, idx, w, ref, m, TOL["bf16"], "tie")
 
 
 def test_errors_launch_nothing():
@@ -308,3 +312,29 @@ def test_measurement_utilities():
     torch.cuda.synchronize()
     assert torch.equal(dst[:-1], src[:-1]) and int(dst[-1]) == 0
     assert int(sink[0]) in (7, 0x9E3779B9 - 2**32)
+
+
+@pytest.mark.parametrize("name,rows", [("qwen3_30b_a3b_bf16", (1, 2, 8)),
+                                       ("qwen35_35b_a3b_mxfp4", (1, 8)),
+                                       ("lfm2_8b_a1b_aff4", (1, 4)), ("tiny_f32", (1,))])
+def test_routing_placements_agree(name, rows, monkeypatch):
+    """The routing computed by every gate/up workgroup and the routing computed
+    once by the last router workgroup give bitwise the same forward."""
+    spec = synth.WORKLOADS[name]
+    layer = synth.make_layer(spec, seed=5)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    res = {}
+    for mode in ("gate_up", "once"):
+        monkeypatch.setenv("MOE_DECODE_ROUTE", mode)
+        dl = DeviceLayer(layer)
+        for m in rows:
+            say(f"[gpu] routing placement {mode} {name} m={m}")
+            got, idx, w = run(dl, x, m)
+            order = dl.ws_view("sorted_pair", torch.int32, m * spec.top_k).cpu().numpy()
+            res[(mode, m)] = (got, idx, w, order)
+            check(spec, got, idx, w, ref, m, TOL[spec.act_fmt], f"{mode} m={m}")
+            check_sort(dl, m, idx)
+    for m in rows:
+        for a, b in zip(res[("gate_up", m)], res[("once", m)]):
+            assert np.array_equal(a, b), f"placements differ at m={m}"
