@@ -333,7 +333,8 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   if ((e = moe::launch_route(d.act_fmt, cs, a, a.n_router_wg + a.n_shared_gu, s, ev(0), ev(1))) != hipSuccess)
     return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
   // gate_up: a grid-stride launch over the active slots' items.
-  const int gu_blocks = a.n_routed_gu < kGateUpMaxBlocks ? a.n_routed_gu : kGateUpMaxBlocks;
+  // With the routing computed in gate/up, one more workgroup publishes it.
+  const int gu_blocks = (a.n_routed_gu < kGateUpMaxBlocks ? a.n_routed_gu : kGateUpMaxBlocks) + a.route_in_gu;
   if ((e = plan->gate_up[m](a, gu_blocks, s, ev(2), ev(3))) != hipSuccess)
     return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
   if ((e = kv.down_blend(a, a.n_down, s, ev(4), ev(5))) != hipSuccess)

@@ -1020,8 +1020,23 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish) {
     }
     if (publish && lane == 0 && (a.flags & SHARED_GATED))
       a.row_gate[r] = (float)sigmoid_d(load_coherent(a.logits + (size_t)r * (E + 1) + E));
+    if (m == 1 && !publish) {
+      // One row (nothing to publish): its k experts are distinct, so slot
+      // u of the ascending order holds the expert with u smaller selected
+      // experts, and pair j is that slot's only pair.
+      int pos = 0;
+      for (int i = 0; i < k; ++i) pos += __builtin_amdgcn_readlane(e, i) < e ? 1 : 0;
+      if (lane < k) {
+        L.active[pos] = e;
+        L.sorted[pos] = lane;
+        L.off[e] = pos;          // np = off[e + 1] - off[e] = 1; a selected e + 1
+        L.off[e + 1] = pos + 1;  // writes the same value here
+      }
+      if (lane == 0) L.nact = k;
+    }
   }
   __syncthreads();
+  if (m == 1 && !publish) return;
   // Stable counting sort by expert (mask zeroed at the start).  A row selects an expert at most once, so
   // bit r of mask[e] says whether row r chose e, and a pair's rank inside its
   // expert is the number of earlier rows that chose the same expert.
@@ -1328,17 +1343,22 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
 // groups b * 4 + wave of slot s.  Either the routing is published (the first
 // item's slot record is requested together with the active count), or --
 // route_in_gu, chosen for small m where it starts the streaming sooner --
-// every workgroup computes it from the logits in LDS and block 0 publishes.
+// every workgroup computes it from the logits in LDS and one extra
+// workgroup, the last, publishes it.
 template <int EF, int ACT, int CR, int CS>
 __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
   constexpr int NI = gate_up_ni<EF>();
   const int ips = a.gu_items_per_slot;
   const int wave = uniform_i(threadIdx.x >> 6);
   if (a.route_in_gu) {
+    // The last workgroup only publishes the routing; the others stream.
     __shared__ RouteLDS<256> L;
-    route_all<THREADS>(a, L, blockIdx.x == 0);
+    const int nb = gridDim.x - 1;
+    const bool publisher = (int)blockIdx.x == nb;
+    route_all<THREADS>(a, L, publisher);
+    if (publisher) return;
     const int n = L.nact * ips;
-    for (int it = blockIdx.x; it < n; it += gridDim.x) {
+    for (int it = blockIdx.x; it < n; it += nb) {
       const int s = it / ips, b = it - s * ips;
       const int e = uniform_i(clamp_i(L.active[s], 0, a.E - 1));
       const int off = uniform_i(L.off[e]), np = uniform_i(L.off[e + 1]) - off;
