@@ -143,6 +143,8 @@ typedef struct {
                              then the expert's down_w, down_s, down_b entries (uint64) */
   size_t act;             /* float [te, I]: routed SwiGLU activations, sorted order */
   size_t shared_act;      /* float [max_rows, Is] */
+  size_t shared_y;        /* float [P, max_rows, H]: shared-expert output in P parts of Is
+                             (matrix-core path; P = max(1, Is / 2048)) */
   size_t sync;            /* uint32 [512]: reserved completion words, kept zero */
   size_t total;           /* bytes a workspace must have */
 } moe_decode_ws_layout;

@@ -29,6 +29,7 @@ struct moe_decode_plan {
   int variant;  // kSplit
   const moe::Variant *kv[moe::MAX_ROWS + 1];   // per m
   moe::launch_fn gate_up[moe::MAX_ROWS + 1];   // per m (split arrangement)
+  moe::launch_fn gate_up_shd[moe::MAX_ROWS + 1];  // per m, with the shared down items
   bool route_in_gu[moe::MAX_ROWS + 1];         // per m: where the routing is computed
 };
 
@@ -123,7 +124,8 @@ const moe::FormatKernels &kernels_for(int act, int ef) {
 
 // The variant for m rows: the pass sizes pass_variant picks, with the lane
 // grouping down_lanes wants if instantiated, else the widest available.
-bool pick_variant(const moe_decode_desc &d, int m, const moe::Variant **v, moe::launch_fn *gate_up) {
+bool pick_variant(const moe_decode_desc &d, int m, const moe::Variant **v, moe::launch_fn *gate_up,
+                  moe::launch_fn *gate_up_shd) {
   int cr, cs;
   pass_variant(d, m, &cr, &cs);
   const int want = down_lanes(d.inter / elems_per_chunk(d.expert_fmt));
@@ -135,9 +137,12 @@ bool pick_variant(const moe_decode_desc &d, int m, const moe::Variant **v, moe::
     if (c.lpr == want) { best = &c; break; }
     if (!best || c.lpr > best->lpr) best = &c;
   }
-  *gate_up = nullptr;
+  *gate_up = *gate_up_shd = nullptr;
   for (int i = 0; i < k.ng; ++i)
-    if (k.g[i].cr == cr && k.g[i].cs == cs) *gate_up = k.g[i].gate_up;
+    if (k.g[i].cr == cr && k.g[i].cs == cs) {
+      *gate_up = k.g[i].gate_up;
+      *gate_up_shd = k.g[i].gate_up_shd;
+    }
   *v = best;
   return best && *gate_up;
 }
@@ -186,6 +191,14 @@ moe_status check_desc(const moe_decode_desc &d) {
   return MOE_OK;
 }
 
+// Parts of Is that the matrix-core shared down splits across workgroups
+// (about 2048 per part keeps every wave's stream short); 1 otherwise.
+int shared_down_parts(const moe_decode_desc &d) {
+  const int Is = (d.flags & MOE_SHARED) ? d.shared_inter : 0;
+  const int p = Is / 2048;
+  return p < 1 ? 1 : p;
+}
+
 void layout_for(const moe_decode_desc &d, moe_decode_ws_layout *L) {
   const size_t A = 256;
   const size_t R = (size_t)d.max_rows, E = (size_t)d.num_experts;
@@ -211,6 +224,7 @@ void layout_for(const moe_decode_desc &d, moe_decode_ws_layout *L) {
   L->slot_info = take(cap * sizeof(moe::SlotRec));
   L->act = take(te * (size_t)d.inter * 4);
   L->shared_act = take(R * Is * 4);
+  L->shared_y = take(Is ? (size_t)shared_down_parts(d) * R * (size_t)d.hidden * 4 : 0);
   L->total = o;
 }
 
@@ -294,6 +308,7 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   a.slots = reinterpret_cast<moe::SlotRec *>(ws + L.slot_info);
   a.act = reinterpret_cast<float *>(ws + L.act);
   a.sact = reinterpret_cast<float *>(ws + L.shared_act);
+  a.sy = reinterpret_cast<float *>(ws + L.shared_y);
   a.sync = reinterpret_cast<unsigned *>(ws + L.sync);
 
   const moe::Variant &kv = *plan->kv[m];
@@ -307,12 +322,33 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   a.route_in_gu = plan->route_in_gu[m] ? 1 : 0;
   a.n_router = (d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0)) * nrb;   // router units
   a.n_router_wg = (a.n_router + moe::ROUTE_UNITS_PER_WG - 1) / moe::ROUTE_UNITS_PER_WG;
-  a.n_shared_gu = shared ? ((a.Is + ni_s - 1) / ni_s + moe::ROUTE_WPB - 1) / moe::ROUTE_WPB : 0;
+  // The shared expert runs on the matrix cores (16-row tiles, gate/up in the
+  // route launch, down in the gate/up launch) for bf16 activations when H and
+  // Is are multiples of 32; on the vector units otherwise.
+  a.shared_mfma = shared && d.act_fmt == MOE_BF16 && d.hidden % 32 == 0 && a.Is % 32 == 0;
+  a.max_rows = d.max_rows;
+  a.sd_parts = shared_down_parts(d);
+  if (a.shared_mfma) {
+    a.n_shared_gu = (a.Is + 15) / 16;
+    a.n_shared_dn = (d.hidden + 15) / 16 * a.sd_parts;
+  } else {
+    a.n_shared_gu = shared ? ((a.Is + ni_s - 1) / ni_s + moe::ROUTE_WPB - 1) / moe::ROUTE_WPB : 0;
+    a.n_shared_dn = 0;
+  }
   a.gu_items_per_slot = ((d.inter + ni_r - 1) / ni_r + wpb - 1) / wpb;
   a.n_routed_gu = a.cap * a.gu_items_per_slot;
   // Two row blocks per down tile when the units would leave waves idle and
   // the halved tile count still gives every CU a workgroup.
-  a.down_dq = ((a.cap + (shared ? 1 : 0)) < moe::DOWN_WPB && d.hidden / (2 * moe::DOWN_RD) >= 256) ? 2 : 1;
+  // Long down rows are split along K into parts (fixed per layer, so the
+  // sums do not depend on m) so that one active expert still fills the
+  // workgroup's waves; the parts' partial y share the LDS y array.
+  a.down_parts = 1;
+  while (a.down_parts < 4 && d.inter / (2048 * (a.down_parts * 2)) >= 1 &&
+         (size_t)d.max_rows * d.top_k * moe::MAX_DOWN_TILE * (a.down_parts * 2) <= (size_t)moe::MAX_PAIRS * moe::MAX_DOWN_TILE &&
+         (d.inter / elems_per_chunk(d.expert_fmt)) % (a.down_parts * 2) == 0)
+    a.down_parts *= 2;
+  const int down_units = a.cap + (shared && !a.shared_mfma ? 1 : 0);
+  a.down_dq = (down_units < moe::DOWN_WPB && d.hidden / (2 * moe::DOWN_RD) >= 256) ? 2 : 1;
   a.n_down = (d.hidden + moe::DOWN_RD * a.down_dq - 1) / (moe::DOWN_RD * a.down_dq);
 
   static thread_local bool logged = false;
@@ -327,6 +363,8 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
             a.n_routed_gu, a.gu_items_per_slot, a.n_down, a.down_dq, cr, cs, lpr);
   }
 
+  const moe::launch_fn gu = a.shared_mfma ? plan->gate_up_shd[m] : plan->gate_up[m];
+  if (!gu) return fail(MOE_EUNSUPPORTED, "no gate_up variant for this shared-expert arrangement");
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto ev = [&](int i) -> hipEvent_t { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
   hipError_t e;
@@ -334,8 +372,9 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
     return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
   // gate_up: a grid-stride launch over the active slots' items.
   // With the routing computed in gate/up, one more workgroup publishes it.
-  const int gu_blocks = (a.n_routed_gu < kGateUpMaxBlocks ? a.n_routed_gu : kGateUpMaxBlocks) + a.route_in_gu;
-  if ((e = plan->gate_up[m](a, gu_blocks, s, ev(2), ev(3))) != hipSuccess)
+  const int gu_items = a.n_routed_gu + a.n_shared_dn;
+  const int gu_blocks = (gu_items < kGateUpMaxBlocks ? gu_items : kGateUpMaxBlocks) + a.route_in_gu;
+  if ((e = gu(a, gu_blocks, s, ev(2), ev(3))) != hipSuccess)
     return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
   if ((e = kv.down_blend(a, a.n_down, s, ev(4), ev(5))) != hipSuccess)
     return fail(MOE_EHIP, "down_blend launch: %s", hipGetErrorString(e));
@@ -362,7 +401,7 @@ moe_status moe_decode_plan(const moe_decode_desc *desc, moe_decode_plan_t **plan
   }
   p->variant = kSplit;
   for (int m = 1; m <= p->d.max_rows; ++m) {
-    if (!pick_variant(p->d, m, &p->kv[m], &p->gate_up[m])) {
+    if (!pick_variant(p->d, m, &p->kv[m], &p->gate_up[m], &p->gate_up_shd[m])) {
       delete p;
       return fail(MOE_EUNSUPPORTED, "no kernel variant for m = %d", m);
     }

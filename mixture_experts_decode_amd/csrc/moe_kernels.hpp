@@ -66,6 +66,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Per active slot: what the gate/up and down launches need to start
 // streaming, in one 128-byte record (the routing publishes it).
@@ -84,6 +86,11 @@ struct Args {
   // work items
   int n_router, n_router_wg, n_shared_gu, gu_items_per_slot, n_routed_gu, n_down, down_dq;
   int route_in_gu;         // 1: every gate/up workgroup routes; 0: the last router workgroup does
+  int shared_mfma;         // shared expert on the matrix cores (bf16 activations, H and Is multiples of 32)
+  int n_shared_dn;         // shared down items in the gate/up launch (matrix-core path)
+  int sd_parts;            // parts of Is the shared down items split (partials in sy[part])
+  int down_parts;          // parts of I each routed down row is split into (partials added in the blend)
+  int max_rows;
   const void *x;
   void *out;
   int32_t *idx_out;
@@ -104,6 +111,7 @@ struct Args {
   SlotRec *slots;          // [cap]
   float *act;              // [te, I]
   float *sact;             // [m, Is]
+  float *sy;               // [m, H]: shared-expert output (matrix-core path)
   unsigned *sync;          // [SYNC_WORDS]
 };
 
@@ -550,8 +558,8 @@ template <> struct XOps<MXFP4, F32> {
 // and, for the one-sub-step formats where registers allow, their x loads --
 // are issued together before any of them is used.  On return acc[t][c]
 // holds, in every lane of the group, the full dot product of rows[t] with
-// vector c.  The per-(row, vector) arithmetic does not depend on C, U or the
-// other rows, so results are the same for every m.
+// vector c over chunks [c0, nchunks).  The per-(row, vector) arithmetic does
+// not depend on C, U or the other rows, so results are the same for every m.
 
 // Chunk steps issued together: as many as fit, with the RG x C totals and
 // the x values in use, in about 128 VGPRs.
@@ -560,14 +568,15 @@ template <int WF, int XF, int RG, int C> struct Unroll {
   static constexpr int W = RG * wchunk_regs<WF>();
   static constexpr int XS = XOps<WF, XF>::XS;
   static constexpr int A = RG * C + 2 * XS;
-  static constexpr int U0 = clampu((128 - A) / W);
+  // 4-bit rows with 4+ vectors: one step (the expansion temporaries are large).
+  static constexpr int U0 = (WF >= AFF4 && C >= 4) ? 1 : clampu((128 - A) / W);
   static constexpr bool XPF = XOps<WF, XF>::SUB == 1 && U0 * C * XS <= 32;
   static constexpr int U = XPF ? clampu((128 - RG * C) / (W + C * XS)) : U0;
 };
 
 template <int WF, int XF, int RG, int C, int LPR>
 __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const char *const (&xrow)[C],
-                                              int nchunks, float (&acc)[RG][C]) {
+                                              int c0, int nchunks, float (&acc)[RG][C]) {
   using O = XOps<WF, XF>;
   using X = typename O::X;
   constexpr int U = Unroll<WF, XF, RG, C>::U;
@@ -577,7 +586,7 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
   for (int t = 0; t < RG; ++t)
 #pragma unroll
     for (int c = 0; c < C; ++c) acc[t][c] = 0.f;
-  for (int base = 0; base < nchunks; base += LPR * U) {
+  for (int base = c0; base < nchunks; base += LPR * U) {
     WChunk<WF> w[U][RG];
     X xp[XPF ? U : 1][XPF ? C : 1];
 #pragma unroll
@@ -701,6 +710,159 @@ __device__ __forceinline__ Row<WF> make_row(const Mat<WF> &m, int n) {
   if constexpr (UNI) r.off = __builtin_amdgcn_readfirstlane(r.off);
   return r;
 }
+
+// ------------------------------------------------------ matrix-core tiles
+//
+// v_mfma_f32_16x16x32_bf16 on one wave: A = 16 weight rows x 32 k (lane l
+// holds row l % 16 at k (l / 16) * 8 .. + 7), B = 32 k x 16 vectors (lane l
+// holds vector l % 16 at the same k), D = 16 x 16 f32 (lane l holds rows
+// (l / 16) * 4 + i, i < 4, of vector l % 16).  Rows past N and vectors past
+// nv repeat the last one; the callers drop their results.  Every (row,
+// vector) total is accumulated in the same order whatever the number of
+// vectors, so results do not depend on m.
+
+
+// 8 f32 values as two bf16 octets: hi = the top 16 bits, lo = the rest
+// rounded to bf16; hi + lo carries 16 significant bits, and the products
+// with bf16 weights are exact in the f32 accumulator.
+__device__ __forceinline__ void split_bf16(const u32x4 &a, const u32x4 &b, bf16x8 &hi, bf16x8 &lo) {
+  const uint32_t f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[4], r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t f0 = f[2 * i], f1 = f[2 * i + 1];
+    h[i] = (f0 >> 16) | (f1 & 0xFFFF0000u);
+    const float r0 = __uint_as_float(f0) - __uint_as_float(f0 & 0xFFFF0000u);
+    const float r1 = __uint_as_float(f1) - __uint_as_float(f1 & 0xFFFF0000u);
+    r[i] = (uint32_t)f32_to_bf16(r0) | ((uint32_t)f32_to_bf16(r1) << 16);
+  }
+  const u32x4 hv = {h[0], h[1], h[2], h[3]}, rv = {r[0], r[1], r[2], r[3]};
+  hi = __builtin_bit_cast(bf16x8, hv);
+  lo = __builtin_bit_cast(bf16x8, rv);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
+}
+
+// One wave: rows [n0, n0 + 16) of NA bf16 matrices [N, K] (rb bytes per row,
+// resources A[j]) against vectors 0..nv-1 of X (bf16 or f32 rows of xstride
+// bytes) over k in [kb, ke) (multiples of 32), into acc[j][ct] for vectors
+// 16 ct .. 16 ct + 15.
+//
+// The weights go through LDS: a batch of MF_U k-steps is 16 rows x 256
+// bytes per matrix, loaded with lane-linear 16-byte loads (each instruction
+// reads 4 rows x 256 contiguous bytes; the MFMA lane pattern itself would
+// read 16 rows x 64 bytes per instruction, which streams about a quarter
+// slower), written to this wave's own LDS region, and read back in the MFMA
+// layout.  The next batch's loads are in flight meanwhile.  `stage` is the
+// wave's region, NA * 16 * MF_ROW bytes.
+constexpr int MF_U = 4;                  // k-steps of 32 per batch
+constexpr int MF_ROW = MF_U * 64 + 16;   // bytes per staged row (16 bytes of padding)
+constexpr int MF_STAGE = 16 * MF_ROW;    // staged bytes per matrix per wave
+
+template <int XF, int NA, int NCT>
+__device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA], int rb, int n0, int N,
+                                           const char *x, size_t xstride, int nv, int kb, int ke,
+                                           char *stage, f32x4 (&acc)[NA][NCT]) {
+  constexpr int XB = XF == F32 ? 4 : 2;
+  constexpr int XL = XF == F32 ? 2 : 1;   // 16-byte x loads per step and column tile
+  const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
+  // Loader: instruction i brings rows 4 i + g, bytes rr * 16 .. + 16 of the batch.
+  int loff[MF_U];
+#pragma unroll
+  for (int i = 0; i < MF_U; ++i) loff[i] = min(n0 + 4 * i + g, N - 1) * rb + rr * 16;
+  const char *xv[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) xv[ct] = x + (size_t)min(16 * ct + rr, nv - 1) * xstride + (size_t)g * 8 * XB;
+#pragma unroll
+  for (int j = 0; j < NA; ++j)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (kb >= ke) return;
+  // Weights and x of the next batch are requested together, one batch ahead.
+  u32x4 nxt[NA][MF_U], nxb[MF_U][NCT][XL];
+  auto fetch = [&](int kq) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j)
+#pragma unroll
+      for (int i = 0; i < MF_U; ++i) nxt[j][i] = __builtin_amdgcn_raw_buffer_load_b128(A[j], loff[i] + kq * 2, 0, BUF_NT);
+#pragma unroll
+    for (int u = 0; u < MF_U; ++u) {
+      const int kk = min(kq + 32 * u, ke - 32);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int h = 0; h < XL; ++h) nxb[u][ct][h] = ld16(xv[ct] + (size_t)kk * XB + 16 * h);
+    }
+  };
+  fetch(kb);
+  for (int k0 = kb; k0 < ke; k0 += 32 * MF_U) {
+    u32x4 cur[NA][MF_U], bv[MF_U][NCT][XL];
+#pragma unroll
+    for (int j = 0; j < NA; ++j)
+#pragma unroll
+      for (int i = 0; i < MF_U; ++i) cur[j][i] = nxt[j][i];
+#pragma unroll
+    for (int u = 0; u < MF_U; ++u)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int h = 0; h < XL; ++h) bv[u][ct][h] = nxb[u][ct][h];
+    const int k1 = k0 + 32 * MF_U;
+    if (k1 < ke) fetch(k1);
+#pragma unroll
+    for (int j = 0; j < NA; ++j)
+#pragma unroll
+      for (int i = 0; i < MF_U; ++i)
+        *reinterpret_cast<u32x4 *>(stage + j * MF_STAGE + (4 * i + g) * MF_ROW + rr * 16) = cur[j][i];
+    // The region is this wave's alone; its LDS accesses complete in order.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int u = 0; u < MF_U; ++u) {
+      if (k0 + 32 * u < ke) {
+        u32x4 av[NA];
+#pragma unroll
+        for (int j = 0; j < NA; ++j)
+          av[j] = *reinterpret_cast<const u32x4 *>(stage + j * MF_STAGE + rr * MF_ROW + u * 64 + g * 16);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          if constexpr (XF == BF16) {
+            const bf16x8 bb = __builtin_bit_cast(bf16x8, bv[u][ct][0]);
+#pragma unroll
+            for (int j = 0; j < NA; ++j) acc[j][ct] = mfma16(av[j], bb, acc[j][ct]);
+          } else {
+            bf16x8 hi, lo;
+            split_bf16(bv[u][ct][0], bv[u][ct][XL - 1], hi, lo);
+#pragma unroll
+            for (int j = 0; j < NA; ++j) {
+              acc[j][ct] = mfma16(av[j], hi, acc[j][ct]);
+              acc[j][ct] = mfma16(av[j], lo, acc[j][ct]);
+            }
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// The k range of wave w when nw waves split K (a multiple of 32) evenly.
+__device__ __forceinline__ void k_slice(int K, int w, int nw, int &kb, int &ke) {
+  const int steps = K / 32, per = (steps + nw - 1) / nw;
+  kb = min(w * per, steps) * 32;
+  ke = min((w + 1) * per, steps) * 32;
+}
+
+// Partials of the NW waves of one matrix-core item, added in wave order.
+template <int NW, int NA> struct MfmaLDS {
+  float part[NW][NA][2][4][WAVE];   // [wave][matrix][column tile][i][lane]
+  alignas(16) char stage[NW][NA * MF_STAGE];   // each wave's weight staging
+};
 
 __device__ __forceinline__ size_t act_bytes(int fmt) { return fmt == F32 ? 4 : 2; }
 
@@ -1144,7 +1306,7 @@ __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, cons
       xrow[c] = x + (size_t)(routed ? pair[c] / k : c0 + c) * xstride;
     }
     float acc[RG][C];
-    wave_rows_dot<EF, ACT, RG, C, WAVE>(rows, xrow, H / Fmt<EF>::EPC, acc);
+    wave_rows_dot<EF, ACT, RG, C, WAVE>(rows, xrow, 0, H / Fmt<EF>::EPC, acc);
     if ((threadIdx.x & 63) == 0) {
 #pragma unroll
       for (int c = 0; c < C; ++c) {
@@ -1186,7 +1348,8 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   const int H = a.H, I = a.I, Is = a.Is, m = a.m, te = a.te;
   const int DQ = a.down_dq, HT = DOWN_RD * DQ, h0 = tile * HT;
   const bool shared = (a.flags & SHARED) != 0;
-  const int sh = shared ? 1 : 0;                 // the shared expert is unit 0
+  const bool sh_mfma = shared && a.shared_mfma;  // shared output already in sy
+  const int sh = shared && !sh_mfma ? 1 : 0;     // else the shared expert is unit 0
   const bool before = (a.flags & WEIGHT_BEFORE) != 0;
   const bool gated = (a.flags & SHARED_GATED) != 0;
 
@@ -1198,18 +1361,30 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
     my_perm = clamp_i(a.pair_to_perm[tid], 0, te - 1);
   }
   if (tid < m) my_g = gated ? a.row_gate[tid] : 1.0f;
+  float my_ys = 0.f;                             // this thread's shared output for the blend
+  if (sh_mfma && tid < m * HT) {
+    const int r = tid / HT, h = h0 + (tid - r * HT);
+    if (h < H)
+      for (int q = 0; q < a.sd_parts; ++q) my_ys += a.sy[((size_t)q * a.max_rows + r) * H + h];
+  }
   // This wave's first routed record, requested together with the count (the
   // record array always has cap entries; a stale one is never used).
-  const int slot0 = clamp_i(wave / DQ - sh, 0, a.cap - 1);
+  const int slot0 = clamp_i(wave / (DQ * a.down_parts) - sh, 0, a.cap - 1);
   const SlotRec pre = a.slots[slot0];
   const int nact = clamp_i(a.active_count[0], 0, a.cap);
   const int units = nact + sh;
 
-  for (int su = wave; su < units * DQ; su += DOWN_WPB) {
-    const int u = su / DQ, q = su - u * DQ;
+  // Sub-unit su = (unit, row block q, part pt of the down rows' K); the
+  // parts' totals are added in order in the blend.
+  const int NP = a.down_parts;
+  for (int su = wave; su < units * DQ * NP; su += DOWN_WPB) {
+    const int uq = su / NP, pt = su - uq * NP;
+    const int u = uq / DQ, q = uq - u * DQ;
     const int hb = h0 + q * DOWN_RD;             // first column of this row block
     if (u >= sh) {
       const SlotRec rec = su == wave ? pre : a.slots[u - sh];
+      const int nch = I / Fmt<EF>::EPC;
+      const int kc0 = pt * nch / NP, kc1 = (pt + 1) * nch / NP;
       const int e = uniform_i(clamp_i(rec.e, 0, a.E - 1));
       const int off = uniform_i(clamp_i(rec.off, 0, te));
       const int np = uniform_i(clamp_i(rec.np, 0, te - off));
@@ -1228,15 +1403,16 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
 #pragma unroll
         for (int c = 0; c < C; ++c) xrow[c] = reinterpret_cast<const char *>(a.act + (size_t)(off + c0 + c) * I);
         float acc[RGR][C];
-        wave_rows_dot<EF, F32, RGR, C, LPR>(rows, xrow, I / Fmt<EF>::EPC, acc);
+        wave_rows_dot<EF, F32, RGR, C, LPR>(rows, xrow, kc0, kc1, acc);
         if (lane % LPR == 0) {
 #pragma unroll
           for (int t = 0; t < RGR; ++t)
 #pragma unroll
-            for (int c = 0; c < C; ++c) y_lds[(off + c0 + c) * HT + q * DOWN_RD + grp + GR * t] = acc[t][c];
+            for (int c = 0; c < C; ++c)
+              y_lds[(pt * te + off + c0 + c) * HT + q * DOWN_RD + grp + GR * t] = acc[t][c];
         }
       });
-    } else {
+    } else if (pt == 0) {
       const Mat<ACT> ms = make_mat<ACT>(a.sdw, nullptr, nullptr, H, Is);
       Row<ACT> rows[DOWN_RD];
 #pragma unroll
@@ -1247,7 +1423,7 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
 #pragma unroll
         for (int c = 0; c < C; ++c) xrow[c] = reinterpret_cast<const char *>(a.sact + (size_t)(c0 + c) * Is);
         float acc[DOWN_RD][C];
-        wave_rows_dot<ACT, F32, DOWN_RD, C, WAVE>(rows, xrow, Is / Fmt<ACT>::EPC, acc);
+        wave_rows_dot<ACT, F32, DOWN_RD, C, WAVE>(rows, xrow, 0, Is / Fmt<ACT>::EPC, acc);
         if (lane == 0) {
 #pragma unroll
           for (int t = 0; t < DOWN_RD; ++t)
@@ -1272,13 +1448,88 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
     float o = 0.f;
     for (int j = 0; j < k; ++j) {
       const int p = r * k + j;
-      o = __builtin_fmaf(s_c[p], y_lds[s_perm[p] * HT + hl], o);
+      float y = y_lds[s_perm[p] * HT + hl];
+      for (int q2 = 1; q2 < NP; ++q2) y += y_lds[(q2 * te + s_perm[p]) * HT + hl];
+      o = __builtin_fmaf(s_c[p], y, o);
     }
-    if (shared) o = __builtin_fmaf(s_gamma[r], ys_lds[r * HT + hl], o);
+    if (shared) o = __builtin_fmaf(s_gamma[r], sh_mfma ? my_ys : ys_lds[r * HT + hl], o);
     if (out_f32)
       reinterpret_cast<float *>(a.out)[(size_t)r * H + h] = o;
     else
       reinterpret_cast<uint16_t *>(a.out)[(size_t)r * H + h] = f32_to_bf16(o);
+  }
+}
+
+// Shared expert gate/up on the matrix cores: item = 16 intermediate rows;
+// waves 0..3 take the gate rows and waves 4..7 the up rows, each a quarter
+// of H; writes silu(g) * u to sact.
+template <int NCT>
+__device__ __forceinline__ void shared_gu_mfma(const Args &a, int item, MfmaLDS<ROUTE_WPB, 1> &S) {
+  static_assert(ROUTE_WPB == 8, "gate and up take four waves each");
+  const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int H = a.H, Is = a.Is, m = a.m, n0 = item * 16;
+  const __amdgpu_buffer_rsrc_t A[1] = {buf_rsrc(w < 4 ? a.sgw : a.suw, Is * H * 2)};
+  int kb, ke;
+  k_slice(H, w & 3, 4, kb, ke);
+  f32x4 acc[1][NCT];
+  mfma_slice<BF16, 1, NCT>(A, H * 2, n0, Is, reinterpret_cast<const char *>(a.x), (size_t)H * 2, m, kb, ke,
+                           S.stage[w], acc);
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S.part[w][0][ct][i][lane] = acc[0][ct][i];
+  __syncthreads();
+  // Wave w finishes (column tile w / 4, element i = w % 4).
+  const int ct = w / 4, i = w % 4;
+  if (ct < NCT) {
+    float gs = 0.f, us = 0.f;
+    for (int p = 0; p < 4; ++p) {
+      gs += S.part[p][0][ct][i][lane];
+      us += S.part[4 + p][0][ct][i][lane];
+    }
+    const int row = n0 + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
+    if (row < Is && v < m) a.sact[(size_t)v * Is + row] = silu_mul(gs, us);
+  }
+}
+
+// Shared expert down on the matrix cores: item = (16 output columns, part q
+// of the a.sd_parts parts of Is); the WPB waves of the workgroup split the
+// part, and the part's total goes to sy[q] (the blend adds the parts in
+// order).
+template <int NCT>
+__device__ __forceinline__ void shared_dn_mfma(const Args &a, int item, MfmaLDS<WPB, 1> &S) {
+  const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int H = a.H, Is = a.Is, m = a.m, P = a.sd_parts;
+  const int tile = item / P, q = item - tile * P, n0 = tile * 16;
+  const __amdgpu_buffer_rsrc_t A[1] = {buf_rsrc(a.sdw, H * Is * 2)};
+  int pb, pe, kb, ke;
+  k_slice(Is, q, P, pb, pe);
+  k_slice(pe - pb, w, WPB, kb, ke);
+  f32x4 acc[1][NCT];
+  mfma_slice<F32, 1, NCT>(A, Is * 2, n0, H, reinterpret_cast<const char *>(a.sact), (size_t)Is * 4, m,
+                          pb + kb, pb + ke, S.stage[w], acc);
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S.part[w][0][ct][i][lane] = acc[0][ct][i];
+  __syncthreads();
+  const int i = w;   // WPB == 4: wave w finishes element i = w of every column tile
+  float *sy = a.sy + (size_t)q * a.max_rows * H;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    float y = 0.f;
+    for (int p = 0; p < WPB; ++p) y += S.part[p][0][ct][i][lane];
+    const int row = n0 + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
+    if (row < H && v < m) sy[(size_t)v * H + row] = y;
+  }
+  __syncthreads();   // S is reused by the workgroup's next item
+}
+
+template <int ACT>
+__device__ __forceinline__ void shared_dn_item(const Args &a, int item, MfmaLDS<WPB, 1> &S) {
+  if constexpr (ACT == BF16) {   // other activations never take the matrix-core path
+    if (a.m > 16) shared_dn_mfma<2>(a, item, S);
+    else shared_dn_mfma<1>(a, item, S);
   }
 }
 
@@ -1292,12 +1543,21 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
 // the whole forward and resets the counter.  No workgroup waits for another.
 template <int ACT, int CS>
 __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
+  struct RouterSmem {
+    double part[ROUTE_WPB][8];
+    unsigned ticket;
+    RouteLDS<1024> L;
+  };
+  __shared__ union {
+    RouterSmem r;
+    MfmaLDS<ROUTE_WPB, 1> mf;
+  } sm;
   const int item = blockIdx.x, tid = threadIdx.x;
   const int wave = uniform_i(threadIdx.x >> 6);
   if (item < a.n_router_wg) {
-    __shared__ double s_part[ROUTE_WPB][8];
-    __shared__ unsigned s_ticket;
-    __shared__ RouteLDS<1024> L;
+    double (&s_part)[ROUTE_WPB][8] = sm.r.part;
+    unsigned &s_ticket = sm.r.ticket;
+    RouteLDS<1024> &L = sm.r.L;
     const int unit = item * ROUTE_UNITS_PER_WG + wave / RSPLIT, part = wave % RSPLIT;
     const bool live = unit < a.n_router;
     double tot[8];
@@ -1331,8 +1591,14 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
     if (tid == 0) a.sync[SYNC_ROUTER_TICKET] = 0u;  // every ticket is taken
     return;
   }
+  const int sitem = item - a.n_router_wg;
+  if (ACT == BF16 && a.shared_mfma) {
+    if (a.m > 16) shared_gu_mfma<2>(a, sitem, sm.mf);
+    else shared_gu_mfma<1>(a, sitem, sm.mf);
+    return;
+  }
   constexpr int NI = gate_up_ni<ACT>();
-  const int i0 = ((item - a.n_router_wg) * ROUTE_WPB + wave) * NI;
+  const int i0 = (sitem * ROUTE_WPB + wave) * NI;
   if (i0 < a.Is)
     gate_up_rows<ACT, ACT, CS, NI>(a, a.sgw, a.suw, nullptr, nullptr, nullptr, nullptr, a.Is, i0, 0,
                                    a.m, nullptr, nullptr, a.sact, a.Is);
@@ -1345,11 +1611,12 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
 // route_in_gu, chosen for small m where it starts the streaming sooner --
 // every workgroup computes it from the logits in LDS and one extra
 // workgroup, the last, publishes it.
-template <int EF, int ACT, int CR, int CS>
+template <int EF, int ACT, int CR, int CS, bool SHD>
 __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
   constexpr int NI = gate_up_ni<EF>();
   const int ips = a.gu_items_per_slot;
   const int wave = uniform_i(threadIdx.x >> 6);
+  __shared__ MfmaLDS<WPB, 1> S;
   if (a.route_in_gu) {
     // The last workgroup only publishes the routing; the others stream.
     __shared__ RouteLDS<256> L;
@@ -1358,7 +1625,11 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
     route_all<THREADS>(a, L, publisher);
     if (publisher) return;
     const int n = L.nact * ips;
-    for (int it = blockIdx.x; it < n; it += nb) {
+    for (int it = blockIdx.x; it < n + (SHD ? a.n_shared_dn : 0); it += nb) {
+      if (SHD && it >= n) {
+        shared_dn_item<ACT>(a, it - n, S);
+        continue;
+      }
       const int s = it / ips, b = it - s * ips;
       const int e = uniform_i(clamp_i(L.active[s], 0, a.E - 1));
       const int off = uniform_i(L.off[e]), np = uniform_i(L.off[e + 1]) - off;
@@ -1373,7 +1644,11 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
   const SlotRec pre = a.slots[clamp_i((int)blockIdx.x / ips, 0, a.cap - 1)];
   const int nact = clamp_i(a.active_count[0], 0, a.cap);
   const int n = nact * ips;
-  for (int it = blockIdx.x; it < n; it += gridDim.x) {
+  for (int it = blockIdx.x; it < n + (SHD ? a.n_shared_dn : 0); it += gridDim.x) {
+    if (SHD && it >= n) {
+      shared_dn_item<ACT>(a, it - n, S);
+      continue;
+    }
     const int s = it / ips, b = it - s * ips;
     const SlotRec rec = it == (int)blockIdx.x ? pre : a.slots[s];
     const int off = uniform_i(clamp_i(rec.off, 0, a.te));

@@ -81,7 +81,9 @@ def test_plan_and_layout_for_every_workload(name):
                   (L.pair_to_perm, te * 4), (L.active_experts, min(te, spec.num_experts) * 4),
                   (L.active_count, 4), (L.slot_info, min(te, spec.num_experts) * 64),
                   (L.act, te * spec.inter * 4),
-                  (L.shared_act, spec.max_rows * (spec.shared_inter if spec.shared else 0) * 4)]
+                  (L.shared_act, spec.max_rows * (spec.shared_inter if spec.shared else 0) * 4),
+                  (L.shared_y, max(1, spec.shared_inter // 2048) * spec.max_rows
+                   * (spec.hidden if spec.shared else 0) * 4)]
         spans = sorted((o, o + max(n, 1)) for o, n in fields)
         for (a0, a1), (b0, _) in zip(spans, spans[1:]):
             assert a1 <= b0, "workspace arrays overlap"

@@ -194,9 +194,11 @@ def test_every_row_count_and_pass_variant():
         assert np.array_equal(got, full[:m])
 
 
+# Long rows (I >= 4096) also take the split of each down row into parts.
 @pytest.mark.parametrize("fmt,inter", [("bf16", 64), ("bf16", 256), ("bf16", 768), ("bf16", 1024),
                                        ("mxfp4", 512), ("mxfp4", 1024), ("aff4", 1792),
-                                       ("aff4", 128), ("f32", 32)])
+                                       ("aff4", 128), ("f32", 32), ("bf16", 4096),
+                                       ("aff4", 8192), ("mxfp4", 4096)])
 def test_down_lane_grouping(fmt, inter):
     spec = small(expert_fmt=fmt, inter=inter, hidden=512, num_experts=8, top_k=2,
                  act_fmt="f32" if fmt == "f32" else "bf16")
