@@ -141,7 +141,7 @@ bool pick_variant(const moe_decode_desc &d, int m, const moe::Variant **v, moe::
   for (int i = 0; i < k.ng; ++i)
     if (k.g[i].cr == cr && k.g[i].cs == cs) {
       *gate_up = k.g[i].gate_up;
-      *gate_up_shd = k.g[i].gate_up_shd;
+      *gate_up_shd = m > 16 ? k.g[i].gate_up_shd2 : k.g[i].gate_up_shd;
     }
   *v = best;
   return best && *gate_up;

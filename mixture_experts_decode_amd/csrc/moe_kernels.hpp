@@ -563,15 +563,19 @@ template <> struct XOps<MXFP4, F32> {
 
 // Chunk steps issued together: as many as fit, with the RG x C totals and
 // the x values in use, in about 128 VGPRs.
+// XPF: the x values of a step (all its sub-steps) are requested with its
+// weights -- one round trip per step -- when they fit: up to 32 registers
+// for one-sub-step formats, up to 64 (one step) for the 4-bit ones.
 template <int WF, int XF, int RG, int C> struct Unroll {
   static constexpr int clampu(int v) { return v < 1 ? 1 : (v > 4 ? 4 : v); }
   static constexpr int W = RG * wchunk_regs<WF>();
   static constexpr int XS = XOps<WF, XF>::XS;
+  static constexpr int SUB = XOps<WF, XF>::SUB;
   static constexpr int A = RG * C + 2 * XS;
   // 4-bit rows with 4+ vectors: one step (the expansion temporaries are large).
   static constexpr int U0 = (WF >= AFF4 && C >= 4) ? 1 : clampu((128 - A) / W);
-  static constexpr bool XPF = XOps<WF, XF>::SUB == 1 && U0 * C * XS <= 32;
-  static constexpr int U = XPF ? clampu((128 - RG * C) / (W + C * XS)) : U0;
+  static constexpr bool XPF = SUB == 1 ? U0 * C * XS <= 32 : C * SUB * XS <= 64;
+  static constexpr int U = !XPF ? U0 : SUB == 1 ? clampu((128 - RG * C) / (W + C * XS)) : 1;
 };
 
 template <int WF, int XF, int RG, int C, int LPR>
@@ -581,6 +585,7 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
   using X = typename O::X;
   constexpr int U = Unroll<WF, XF, RG, C>::U;
   constexpr bool XPF = Unroll<WF, XF, RG, C>::XPF;
+  constexpr int SUB = O::SUB;
   const int li = threadIdx.x % LPR;
 #pragma unroll
   for (int t = 0; t < RG; ++t)
@@ -588,7 +593,7 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
     for (int c = 0; c < C; ++c) acc[t][c] = 0.f;
   for (int base = c0; base < nchunks; base += LPR * U) {
     WChunk<WF> w[U][RG];
-    X xp[XPF ? U : 1][XPF ? C : 1];
+    X xp[XPF ? U : 1][XPF ? C : 1][XPF ? SUB : 1];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ch = base + li + u * LPR;
@@ -597,7 +602,9 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
         for (int t = 0; t < RG; ++t) w[u][t] = load_wchunk<WF, LPR == WAVE>(rows[t], ch);
         if constexpr (XPF) {
 #pragma unroll
-          for (int c = 0; c < C; ++c) xp[u][c].fetch(xrow[c], ch, 0);
+          for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int g = 0; g < SUB; ++g) xp[u][c][g].fetch(xrow[c], ch, g);
         }
       }
     }
@@ -614,19 +621,19 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
 #pragma unroll
           for (int t = 0; t < RG; ++t) p[t][c] = O::start(acc[t][c]);
         }
-        // x of sub-step g + 1 is requested before sub-step g is computed.
+        // Without XPF, x of sub-step g + 1 is requested before sub-step g
+        // is computed.
         X xn[C];
+        if constexpr (!XPF) {
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-          if constexpr (XPF) xn[c] = xp[u][c];
-          else xn[c].fetch(xrow[c], ch, 0);
+          for (int c = 0; c < C; ++c) xn[c].fetch(xrow[c], ch, 0);
         }
 #pragma unroll
         for (int g = 0; g < O::SUB; ++g) {
           X x[C];
 #pragma unroll
-          for (int c = 0; c < C; ++c) x[c] = xn[c];
-          if (g + 1 < O::SUB) {
+          for (int c = 0; c < C; ++c) x[c] = XPF ? xp[u][c][XPF ? g : 0] : xn[c];
+          if (!XPF && g + 1 < O::SUB) {
 #pragma unroll
             for (int c = 0; c < C; ++c) xn[c].fetch(xrow[c], ch, g + 1);
           }
@@ -1525,12 +1532,9 @@ __device__ __forceinline__ void shared_dn_mfma(const Args &a, int item, MfmaLDS<
   __syncthreads();   // S is reused by the workgroup's next item
 }
 
-template <int ACT>
+template <int ACT, int NCT>
 __device__ __forceinline__ void shared_dn_item(const Args &a, int item, MfmaLDS<WPB, 1> &S) {
-  if constexpr (ACT == BF16) {   // other activations never take the matrix-core path
-    if (a.m > 16) shared_dn_mfma<2>(a, item, S);
-    else shared_dn_mfma<1>(a, item, S);
-  }
+  if constexpr (ACT == BF16 && NCT > 0) shared_dn_mfma<NCT>(a, item, S);   // the matrix-core path
 }
 
 // ------------------------------------------------------------------ kernels
@@ -1611,7 +1615,9 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
 // route_in_gu, chosen for small m where it starts the streaming sooner --
 // every workgroup computes it from the logits in LDS and one extra
 // workgroup, the last, publishes it.
-template <int EF, int ACT, int CR, int CS, bool SHD>
+// SHD: 0, or the column tiles (1: m <= 16, 2: m <= 32) of the shared
+// expert's down items this variant also runs.
+template <int EF, int ACT, int CR, int CS, int SHD>
 __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
   constexpr int NI = gate_up_ni<EF>();
   const int ips = a.gu_items_per_slot;
@@ -1627,7 +1633,7 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
     const int n = L.nact * ips;
     for (int it = blockIdx.x; it < n + (SHD ? a.n_shared_dn : 0); it += nb) {
       if (SHD && it >= n) {
-        shared_dn_item<ACT>(a, it - n, S);
+        shared_dn_item<ACT, SHD>(a, it - n, S);
         continue;
       }
       const int s = it / ips, b = it - s * ips;
@@ -1646,7 +1652,7 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
   const int n = nact * ips;
   for (int it = blockIdx.x; it < n + (SHD ? a.n_shared_dn : 0); it += gridDim.x) {
     if (SHD && it >= n) {
-      shared_dn_item<ACT>(a, it - n, S);
+      shared_dn_item<ACT, SHD>(a, it - n, S);
       continue;
     }
     const int s = it / ips, b = it - s * ips;

@@ -35,7 +35,8 @@ struct Variant {
 struct GateUpVariant {
   int cr, cs;
   launch_fn gate_up;      // second launch
-  launch_fn gate_up_shd;  // the same, also running the shared expert's down on the matrix cores
+  launch_fn gate_up_shd;  // the same, also running the shared expert's down on the matrix cores (m <= 16)
+  launch_fn gate_up_shd2; // the same for m <= 32
 };
 struct FormatKernels {
   const Variant *v;
@@ -65,15 +66,15 @@ template <int EF, int ACT, int CR, int CS, int LPR>
 hipError_t launch_down_blend_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   return launch_timed(down_blend_kernel<EF, ACT, CR, CS, LPR>, blocks, DOWN_THREADS, st, start, stop, a);
 }
-template <int EF, int ACT, int CR, int CS, bool SHD>
+template <int EF, int ACT, int CR, int CS, int SHD>
 hipError_t launch_gate_up_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   return launch_timed(gate_up_kernel<EF, ACT, CR, CS, SHD>, blocks, THREADS, st, start, stop, a);
 }
 // The variant with the shared expert's down items exists for bf16
 // activations only (the matrix-core path).
-template <int EF, int ACT, int CR, int CS>
+template <int EF, int ACT, int CR, int CS, int NCT>
 constexpr launch_fn gate_up_shd_fn() {
-  if constexpr (ACT == BF16) return &launch_gate_up_t<EF, ACT, CR, CS, true>;
+  if constexpr (ACT == BF16) return &launch_gate_up_t<EF, ACT, CR, CS, NCT>;
   else return nullptr;
 }
 #endif
@@ -82,7 +83,8 @@ constexpr launch_fn gate_up_shd_fn() {
 
 // Inside an inst_*.hip unit, with constexpr int EFT and ACTT in scope.
 #define MOE_V(CR, CS, LPR) { CR, CS, LPR, &launch_down_blend_t<EFT, ACTT, CR, CS, LPR> }
-#define MOE_G(CR, CS) { CR, CS, &launch_gate_up_t<EFT, ACTT, CR, CS, false>, gate_up_shd_fn<EFT, ACTT, CR, CS>() }
+#define MOE_G(CR, CS) { CR, CS, &launch_gate_up_t<EFT, ACTT, CR, CS, 0>, gate_up_shd_fn<EFT, ACTT, CR, CS, 1>(), \
+                        gate_up_shd_fn<EFT, ACTT, CR, CS, 2>() }
 #define MOE_TABLE(NAME)                                                            \
   const FormatKernels &kernels_##NAME() {                                          \
     static const FormatKernels k{kV, (int)(sizeof kV / sizeof kV[0]), kG,         \
