@@ -141,7 +141,9 @@ typedef struct {
   size_t slot_info;       /* [cap] 64-byte records, one per active slot u < active_count:
                              int32 expert, first position in sorted_pair, pair count, 0;
                              then the expert's down_w, down_s, down_b entries (uint64) */
-  size_t act;             /* float [te, I]: routed SwiGLU activations, sorted order */
+  size_t act;             /* float [te, I]: routed SwiGLU activations, sorted order; for 4-bit
+                             experts each row is stored sub-step-major: element i at
+                             ((i % 32) / 8) * (I / 4) + (i / 32) * 8 + i % 8 */
   size_t shared_act;      /* float [max_rows, Is] */
   size_t shared_y;        /* float [P, max_rows, H]: shared-expert output in P parts of Is
                              (matrix-core path; P = max(1, Is / 2048)) */

@@ -33,6 +33,11 @@
 namespace moe {
 
 enum : int { F32 = 0, BF16 = 1, AFF4 = 2, MXFP4 = 3 };
+// x format of the down projection's input for 4-bit experts: f32, each row
+// stored sub-step-major (element i of the row at ((i % 32) / 8) * (I / 4) +
+// (i / 32) * 8 + i % 8), so that in sub-step g adjacent lanes (adjacent
+// 32-element chunks) read adjacent 32-byte blocks.
+enum : int { F32P = 4 };
 enum : int { ROUTE_SOFTMAX = 0, ROUTE_SIGMOID_BIAS = 1, ROUTE_SIGMOID_LOGIT = 2 };
 enum : unsigned { NORM_TOPK = 1u, WEIGHT_BEFORE = 2u, SHARED = 4u, SHARED_GATED = 8u, OUT_F32 = 16u };
 
@@ -342,7 +347,7 @@ template <> struct XOps<BF16, BF16> {
   static constexpr int SUB = 1, XS = 4;
   struct X {
     u32x4 d;
-    __device__ __forceinline__ void fetch(const char *xrow, int ch, int) { d = ld16(xrow + (size_t)ch * 16); }
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int, int) { d = ld16(xrow + (size_t)ch * 16); }
   };
   static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
   static __device__ __forceinline__ float start(float acc) { return acc; }
@@ -360,7 +365,7 @@ template <> struct XOps<BF16, F32> {
   static constexpr int SUB = 1, XS = 8;
   struct X {
     u32x4 a, b;
-    __device__ __forceinline__ void fetch(const char *xrow, int ch, int) {
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int, int) {
       a = ld16(xrow + (size_t)ch * 32);
       b = ld16(xrow + (size_t)ch * 32 + 16);
     }
@@ -385,7 +390,7 @@ template <> struct XOps<F32, F32> {
   static constexpr int SUB = 1, XS = 4;
   struct X {
     u32x4 a;
-    __device__ __forceinline__ void fetch(const char *xrow, int ch, int) { a = ld16(xrow + (size_t)ch * 16); }
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int, int) { a = ld16(xrow + (size_t)ch * 16); }
   };
   static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
   static __device__ __forceinline__ float start(float acc) { return acc; }
@@ -403,7 +408,7 @@ template <> struct XOps<F32, BF16> {
   static constexpr int SUB = 1, XS = 2;
   struct X {
     u32x2 raw;
-    __device__ __forceinline__ void fetch(const char *xrow, int ch, int) { raw = ld8(xrow + (size_t)ch * 8); }
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int, int) { raw = ld8(xrow + (size_t)ch * 8); }
   };
   static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
   static __device__ __forceinline__ float start(float acc) { return acc; }
@@ -430,7 +435,7 @@ template <> struct XOps<AFF4, BF16> {
   static constexpr int SUB = 4, XS = 4;
   struct X {
     uint32_t d[4];   // (x0,x4) (x1,x5) (x2,x6) (x3,x7) of the sub-step
-    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g) {
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g, int) {
       const u32x4 v = ld16(xrow + (size_t)ch * 64 + 16 * g);  // (x0,x1) (x2,x3) (x4,x5) (x6,x7)
       d[0] = (v.x & 0xFFFFu) | (v.z << 16);
       d[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
@@ -462,7 +467,7 @@ template <> struct XOps<AFF4, F32> {
   static constexpr int SUB = 4, XS = 8;
   struct X {
     u32x4 a, b;      // x 8g .. 8g+7
-    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g) {
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g, int) {
       a = ld16(xrow + (size_t)ch * 128 + 32 * g);
       b = ld16(xrow + (size_t)ch * 128 + 32 * g + 16);
     }
@@ -501,7 +506,7 @@ template <> struct XOps<MXFP4, BF16> {
   static constexpr int SUB = 4, XS = 4;
   struct X {
     u32x4 d;
-    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g) { d = ld16(xrow + (size_t)ch * 64 + 16 * g); }
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g, int) { d = ld16(xrow + (size_t)ch * 64 + 16 * g); }
   };
   static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
   static __device__ __forceinline__ float start(float) { return 0.f; }
@@ -522,7 +527,7 @@ template <> struct XOps<MXFP4, F32> {
   static constexpr int SUB = 4, XS = 8;
   struct X {
     u32x4 a, b;
-    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g) {
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g, int) {
       a = ld16(xrow + (size_t)ch * 128 + 32 * g);
       b = ld16(xrow + (size_t)ch * 128 + 32 * g + 16);
     }
@@ -547,6 +552,25 @@ template <> struct XOps<MXFP4, F32> {
   static __device__ __forceinline__ float finish(const WChunk<MXFP4> &w, float S, float, float acc) {
     return __builtin_fmaf(S, e8m0_to_f32(w.s), acc);
   }
+};
+
+// 4-bit weights . sub-step-major f32 x (the down input): the math of the
+// f32 case, sub-step g of chunk ch read at g * gs + ch * 32 bytes.
+template <> struct XOps<AFF4, F32P> : XOps<AFF4, F32> {
+  struct X : XOps<AFF4, F32>::X {
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g, int gs) {
+      a = ld16(xrow + (size_t)g * gs + (size_t)ch * 32);
+      b = ld16(xrow + (size_t)g * gs + (size_t)ch * 32 + 16);
+    }
+  };
+};
+template <> struct XOps<MXFP4, F32P> : XOps<MXFP4, F32> {
+  struct X : XOps<MXFP4, F32>::X {
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g, int gs) {
+      a = ld16(xrow + (size_t)g * gs + (size_t)ch * 32);
+      b = ld16(xrow + (size_t)g * gs + (size_t)ch * 32 + 16);
+    }
+  };
 };
 
 // ------------------------------------------------------ wave row x vector
@@ -580,7 +604,7 @@ template <int WF, int XF, int RG, int C> struct Unroll {
 
 template <int WF, int XF, int RG, int C, int LPR>
 __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const char *const (&xrow)[C],
-                                              int c0, int nchunks, float (&acc)[RG][C]) {
+                                              int c0, int nchunks, float (&acc)[RG][C], int gs = 0) {
   using O = XOps<WF, XF>;
   using X = typename O::X;
   constexpr int U = Unroll<WF, XF, RG, C>::U;
@@ -604,7 +628,7 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
 #pragma unroll
           for (int c = 0; c < C; ++c)
 #pragma unroll
-            for (int g = 0; g < SUB; ++g) xp[u][c][g].fetch(xrow[c], ch, g);
+            for (int g = 0; g < SUB; ++g) xp[u][c][g].fetch(xrow[c], ch, g, gs);
         }
       }
     }
@@ -626,7 +650,7 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
         X xn[C];
         if constexpr (!XPF) {
 #pragma unroll
-          for (int c = 0; c < C; ++c) xn[c].fetch(xrow[c], ch, 0);
+          for (int c = 0; c < C; ++c) xn[c].fetch(xrow[c], ch, 0, gs);
         }
 #pragma unroll
         for (int g = 0; g < O::SUB; ++g) {
@@ -635,7 +659,7 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
           for (int c = 0; c < C; ++c) x[c] = XPF ? xp[u][c][XPF ? g : 0] : xn[c];
           if (!XPF && g + 1 < O::SUB) {
 #pragma unroll
-            for (int c = 0; c < C; ++c) xn[c].fetch(xrow[c], ch, g + 1);
+            for (int c = 0; c < C; ++c) xn[c].fetch(xrow[c], ch, g + 1, gs);
           }
 #pragma unroll
           for (int c = 0; c < C; ++c) xs[c] = O::xsum(x[c], xs[c]);
@@ -1326,7 +1350,10 @@ __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, cons
               g *= w;
               v *= w;
             }
-            dst[(size_t)(off + c0 + c) * ld + i0 + t] = silu_mul(g, v);
+            const int i = i0 + t;
+            // 4-bit experts: the row is stored sub-step-major (F32P).
+            const int pos = (EF >= AFF4 && routed) ? ((i & 31) >> 3) * (ld >> 2) + (i >> 5) * 8 + (i & 7) : i;
+            dst[(size_t)(off + c0 + c) * ld + pos] = silu_mul(g, v);
           }
         }
       }
@@ -1410,7 +1437,7 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
 #pragma unroll
         for (int c = 0; c < C; ++c) xrow[c] = reinterpret_cast<const char *>(a.act + (size_t)(off + c0 + c) * I);
         float acc[RGR][C];
-        wave_rows_dot<EF, F32, RGR, C, LPR>(rows, xrow, kc0, kc1, acc);
+        wave_rows_dot<EF, (EF >= AFF4 ? F32P : F32), RGR, C, LPR>(rows, xrow, kc0, kc1, acc, I);
         if (lane % LPR == 0) {
 #pragma unroll
           for (int t = 0; t < RGR; ++t)
