@@ -1404,28 +1404,51 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   // This wave's first routed record, requested together with the count (the
   // record array always has cap entries; a stale one is never used).
   const int slot0 = clamp_i(wave / (DQ * a.down_parts) - sh, 0, a.cap - 1);
-  const SlotRec pre = a.slots[slot0];
+  // The fields a down sub-unit needs, of the wave's next routed sub-unit.
+  struct DownRec {
+    int off, np;
+    uint64_t dw, ds, db;
+  };
+  auto load_rec = [&](int slot) {
+    const SlotRec &r = a.slots[slot];
+    DownRec d;
+    d.off = r.off; d.np = r.np; d.dw = r.dw; d.ds = r.ds; d.db = r.db;
+    return d;
+  };
+  DownRec nxt = load_rec(slot0);
+  int nxt_slot = slot0;
   const int nact = clamp_i(a.active_count[0], 0, a.cap);
   const int units = nact + sh;
 
   // Sub-unit su = (unit, row block q, part pt of the down rows' K); the
   // parts' totals are added in order in the blend.
   const int NP = a.down_parts;
-  for (int su = wave; su < units * DQ * NP; su += DOWN_WPB) {
+  const int nsu = units * DQ * NP;
+  for (int su = wave; su < nsu; su += DOWN_WPB) {
     const int uq = su / NP, pt = su - uq * NP;
     const int u = uq / DQ, q = uq - u * DQ;
     const int hb = h0 + q * DOWN_RD;             // first column of this row block
     if (u >= sh) {
-      const SlotRec rec = su == wave ? pre : a.slots[u - sh];
+      if (nxt_slot != u - sh) {   // not requested ahead (only when the wave's first sub-unit was shared)
+        nxt = load_rec(u - sh);
+        nxt_slot = u - sh;
+      }
+      const DownRec rec = nxt;
+      const int su2 = su + DOWN_WPB;
+      if (su2 < nsu) {
+        const int s2 = (su2 / NP) / DQ - sh;
+        if (s2 >= 0 && s2 != nxt_slot) {
+          nxt = load_rec(s2);
+          nxt_slot = s2;
+        }
+      }
       const int nch = I / Fmt<EF>::EPC;
       const int kc0 = pt * nch / NP, kc1 = (pt + 1) * nch / NP;
-      const int e = uniform_i(clamp_i(rec.e, 0, a.E - 1));
       const int off = uniform_i(clamp_i(rec.off, 0, te));
       const int np = uniform_i(clamp_i(rec.np, 0, te - off));
       const void *dw = reinterpret_cast<const void *>(rec.dw);
       const void *ds = reinterpret_cast<const void *>(rec.ds);
       const void *db = reinterpret_cast<const void *>(rec.db);
-      (void)e;
       const int grp = lane / LPR;
       const Mat<EF> md = make_mat<EF>(dw, ds, db, H, I);
       Row<EF> rows[RGR];
@@ -1677,13 +1700,15 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
   const SlotRec pre = a.slots[clamp_i((int)blockIdx.x / ips, 0, a.cap - 1)];
   const int nact = clamp_i(a.active_count[0], 0, a.cap);
   const int n = nact * ips;
+  SlotRec nxt = pre;   // record of the next routed item, requested one item ahead
   for (int it = blockIdx.x; it < n + (SHD ? a.n_shared_dn : 0); it += gridDim.x) {
     if (SHD && it >= n) {
       shared_dn_item<ACT, SHD>(a, it - n, S);
       continue;
     }
     const int s = it / ips, b = it - s * ips;
-    const SlotRec rec = it == (int)blockIdx.x ? pre : a.slots[s];
+    const SlotRec rec = nxt;
+    if (it + (int)gridDim.x < n) nxt = a.slots[(it + (int)gridDim.x) / ips];
     const int off = uniform_i(clamp_i(rec.off, 0, a.te));
     const int np = uniform_i(clamp_i(rec.np, 0, a.te - off));
     const int i0 = (b * WPB + wave) * NI;
