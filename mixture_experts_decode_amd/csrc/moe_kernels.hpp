@@ -899,6 +899,12 @@ __device__ __forceinline__ size_t act_bytes(int fmt) { return fmt == F32 ? 4 : 2
 
 __device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Entry e (wave-uniform) of a device pointer table, as a wave-uniform pointer.
 __device__ __forceinline__ const void *tbl(const uint64_t *t, int e) {
   if (!t) return nullptr;
@@ -917,12 +923,12 @@ __device__ __forceinline__ int clamp_i(int v, int lo, int hi) { return v < lo ? 
 // expert's gate vector w_g.  RSPLIT waves share a unit, wave `part` taking the
 // part-th quarter of the chunks; each returns its per-row partial totals (in
 // every lane), which the caller adds in part order.  The loads of a chunk
-// step (the router chunk and the rows' x chunks) are issued before any is
-// used.
+// step (the router chunk and all 8 rows' x chunks) are issued before any is
+// used, so the rows cost one memory round trip, not eight.
 template <int ACT>
 __device__ __forceinline__ void router_part(const Args &a, int unit, int part, double (&tot)[8]) {
   constexpr int EPC = ACT == F32 ? 4 : 8;
-  constexpr int RU = 4;                      // chunk steps whose loads are in flight together
+  constexpr int RU = 1;                      // chunk steps whose loads are in flight together
   const int lane = threadIdx.x & 63;
   const int nrows = a.E + ((a.flags & SHARED_GATED) ? 1 : 0);
   const int e = unit % nrows, r0 = (unit / nrows) * 8;
@@ -937,7 +943,9 @@ __device__ __forceinline__ void router_part(const Args &a, int unit, int part, d
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = 0.0;
   for (int base = c0; base < c1; base += WAVE * RU) {
-    u32x4 q[RU];
+    // Every load of the step is issued before any is used.  Rows past nr
+    // repeat row nr - 1 (in bounds) and are not accumulated.
+    u32x4 q[RU], v[8][RU];
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
       const int ch = base + lane + u * WAVE;
@@ -945,13 +953,16 @@ __device__ __forceinline__ void router_part(const Args &a, int unit, int part, d
     }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      if (r < nr) {
-        u32x4 v[RU];
+      const int rr = min(r, nr - 1);
 #pragma unroll
-        for (int u = 0; u < RU; ++u) {
-          const int ch = base + lane + u * WAVE;
-          if (ch < c1) v[u] = ld16(x + (size_t)r * xstride + (size_t)ch * 16);
-        }
+      for (int u = 0; u < RU; ++u) {
+        const int ch = base + lane + u * WAVE;
+        if (ch < c1) v[r][u] = ld16(x + (size_t)rr * xstride + (size_t)ch * 16);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if (r < nr) {
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
           const int ch = base + lane + u * WAVE;
@@ -960,13 +971,13 @@ __device__ __forceinline__ void router_part(const Args &a, int unit, int part, d
             if constexpr (ACT == F32) {
               w[0] = __uint_as_float(q[u].x); w[1] = __uint_as_float(q[u].y);
               w[2] = __uint_as_float(q[u].z); w[3] = __uint_as_float(q[u].w);
-              xv[0] = __uint_as_float(v[u].x); xv[1] = __uint_as_float(v[u].y);
-              xv[2] = __uint_as_float(v[u].z); xv[3] = __uint_as_float(v[u].w);
+              xv[0] = __uint_as_float(v[r][u].x); xv[1] = __uint_as_float(v[r][u].y);
+              xv[2] = __uint_as_float(v[r][u].z); xv[3] = __uint_as_float(v[r][u].w);
             } else {
               w[0] = bf_lo(q[u].x); w[1] = bf_hi(q[u].x); w[2] = bf_lo(q[u].y); w[3] = bf_hi(q[u].y);
               w[4] = bf_lo(q[u].z); w[5] = bf_hi(q[u].z); w[6] = bf_lo(q[u].w); w[7] = bf_hi(q[u].w);
-              xv[0] = bf_lo(v[u].x); xv[1] = bf_hi(v[u].x); xv[2] = bf_lo(v[u].y); xv[3] = bf_hi(v[u].y);
-              xv[4] = bf_lo(v[u].z); xv[5] = bf_hi(v[u].z); xv[6] = bf_lo(v[u].w); xv[7] = bf_hi(v[u].w);
+              xv[0] = bf_lo(v[r][u].x); xv[1] = bf_hi(v[r][u].x); xv[2] = bf_lo(v[r][u].y); xv[3] = bf_hi(v[r][u].y);
+              xv[4] = bf_lo(v[r][u].z); xv[5] = bf_hi(v[r][u].z); xv[6] = bf_lo(v[r][u].w); xv[7] = bf_hi(v[r][u].w);
             }
 #pragma unroll
             for (int i = 0; i < EPC; ++i) acc[r] = __builtin_fma((double)w[i], (double)xv[i], acc[r]);
@@ -993,9 +1004,21 @@ template <int NCAND> struct RankLDS {
   double sel[MAX_PAIRS];          // logit of the expert in slot p
 };
 
-template <int NCAND> struct RouteLDS {
+// One wave's scratch for the top-k of one row (row_topk).
+struct alignas(16) TopkLDS {
+  unsigned hw[WAVE];              // high key words of the lanes' best entries
+  unsigned long long key[WAVE];   // candidates, then the selection
+  int id[WAVE];
+  double lg[WAVE];
+};
+
+template <int NCAND, int NWV> struct RouteLDS {
   static constexpr int kCand = NCAND;   // rank selection serves at most NCAND = m * E candidates
-  RankLDS<NCAND> rk;
+  static constexpr int kWaves = NWV;    // waves with a top-k scratch
+  union {
+    RankLDS<NCAND> rk;   // rank selection
+    TopkLDS tk[NWV];     // or per-wave selection
+  };
   int idx[MAX_PAIRS];        // selected expert of pair p = r*k + j
   float w[MAX_PAIRS];        // routing weight of pair p (times rsf)
   unsigned mask[MAX_EXPERTS];  // bit r: row r chose expert e
@@ -1004,6 +1027,7 @@ template <int NCAND> struct RouteLDS {
   int active[MAX_EXPERTS];   // experts with a pair, ascending
   int slot_of[MAX_EXPERTS];  // position of an active expert in `active`
   int nact;
+  uint64_t one_row[6][MAX_TOPK];  // one row, no publishing: slot u's gate, up, gate/up scales, biases
 };
 
 // Order-preserving image of a double as an unsigned 64-bit integer.
@@ -1041,8 +1065,14 @@ __device__ __forceinline__ double row_weights(const Args &a, const double *lr, b
     if (a.flags & NORM_TOPK) {
       den = wave_sum_f64(num);
     } else {
+      // Lane l adds experts l, l + 64, ... (E <= 256), all requested at once.
+      double v[MAX_EXPERTS / WAVE];
+#pragma unroll
+      for (int j = 0; j < MAX_EXPERTS / WAVE; ++j) v[j] = load_coherent(lr + min(lane + j * WAVE, E - 1));
       double s = 0.0;
-      for (int e = lane; e < E; e += WAVE) s += exp(load_coherent(lr + e) - lmax);
+#pragma unroll
+      for (int j = 0; j < MAX_EXPERTS / WAVE; ++j)
+        if (lane + j * WAVE < E) s += exp(v[j] - lmax);
       den = wave_sum_f64(s);
     }
     w = num / den;
@@ -1053,30 +1083,59 @@ __device__ __forceinline__ double row_weights(const Args &a, const double *lr, b
   return w;
 }
 
-// Top-k of row r by one wave.  Keys are compared as order-preserving 64-bit
-// integers, which is exactly the order of the double keys.  Lane l holds
-// experts 4l..4l+3 (E <= 256), sorts them locally by (key desc, index asc),
-// and each round the wave takes the best head: the high 32 key bits by an
-// integer DPP max (the low 32 only when heads tie on the high half), the lane
-// by a ballot -- the lowest lane holding the maximum also holds the lowest
-// index, because lanes own ascending index ranges.  Slot j's expert and
+// Lane l's four candidates of a row (experts 4l..4l+3; lr: the row's
+// logits): order keys, logits and indices; padding past E gets key 0 (below
+// every real key) and an index after every real one.  Every load is issued
+// before any is used -- one memory round trip; a lane past E loads entry
+// E - 1 and discards it.
+template <bool BIASED>
+__device__ __forceinline__ void lane_keys(const Args &a, const double *lr, unsigned long long (&key)[4],
+                                          double (&lg)[4], int (&id)[4]) {
+  const int lane = threadIdx.x & 63, E = a.E;
+  float bias[4];
+  if constexpr (BIASED) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias[i] = a.ebias[min(4 * lane + i, E - 1)];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lg[i] = load_coherent(lr + min(4 * lane + i, E - 1));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    const bool ok = e < E;
+    if (!ok) lg[i] = 0.0;
+    double kd = lg[i];
+    if constexpr (BIASED) kd = sigmoid_d(lg[i]) + (double)bias[i];
+    key[i] = ok ? order_key(kd) : 0ull;
+    id[i] = ok ? e : 0x7FFFFFFF - (3 - i);
+  }
+}
+
+// Top-k of row r by one wave (T: the wave's scratch).  Keys are compared as
+// order-preserving 64-bit integers, which is exactly the order of the double
+// keys; ties go to the lower index.  Lane l holds experts 4l..4l+3 (E <= 256)
+// and sorts them locally by (key desc, index asc).  Slot j's expert and
 // weight end up in lane j.
-__device__ __forceinline__ void row_topk(const Args &a, int r, int &my_e, double &my_w) {
+//
+// Selection by threshold: let t be the k-th largest of the lanes' best high
+// key words.  If only one lane's best has that high word, the k lanes whose
+// best reaches t hold every entry of the top k (at least k entries are >= that
+// lane's best), so the entries with high word >= t -- at most 4k -- are the
+// candidates, and each candidate's rank among them is its slot.  Otherwise
+// (a tie on the high word at the threshold) the wave takes the best head k
+// times: the high key word by an integer DPP max (the low word only when
+// heads tie on the high one), the lane by a ballot -- the lowest lane holding
+// the maximum also holds the lowest index, because lanes own ascending index
+// ranges.
+template <typename TL>
+__device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e, double &my_w) {
   const int lane = threadIdx.x & 63, E = a.E, k = a.K;
   const double *lr = a.logits + (size_t)r * (E + 1);
   unsigned long long key[4];
   double lg[4];
   int id[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = 4 * lane + i;
-    const bool ok = e < E;
-    lg[i] = ok ? load_coherent(lr + e) : 0.0;
-    double kd = lg[i];
-    if (ok && a.routing == ROUTE_SIGMOID_BIAS) kd = sigmoid_d(lg[i]) + (double)a.ebias[e];
-    key[i] = ok ? order_key(kd) : 0ull;        // below every real key
-    id[i] = ok ? e : 0x7FFFFFFF - (3 - i);     // and after them
-  }
+  if (a.routing == ROUTE_SIGMOID_BIAS) lane_keys<true>(a, lr, key, lg, id);
+  else lane_keys<false>(a, lr, key, lg, id);
   int nvalid = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) nvalid += (4 * lane + i < E) ? 1 : 0;
@@ -1085,9 +1144,61 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, int &my_e, double
   cx(key[0], id[0], lg[0], key[2], id[2], lg[2]);
   cx(key[1], id[1], lg[1], key[3], id[3], lg[3]);
   cx(key[1], id[1], lg[1], key[2], id[2], lg[2]);
-  int left = 0;  // entries of this lane already taken
   double lmax = 0.0, my_l = 0.0;
   my_e = 0;
+  // One wave: its LDS accesses complete in program order, so no barrier.
+  const unsigned myh = (unsigned)(key[0] >> 32);
+  T.hw[lane] = myh;
+  int gt = 0;   // lanes whose best has a larger high word
+#pragma unroll 4
+  for (int j = 0; j < WAVE; j += 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(T.hw + j);
+    gt += (v.x > myh ? 1 : 0) + (v.y > myh ? 1 : 0) + (v.z > myh ? 1 : 0) + (v.w > myh ? 1 : 0);
+  }
+  const unsigned long long at = __builtin_amdgcn_ballot_w64(gt == k - 1);
+  if (__builtin_popcountll(at) == 1) {
+    // t > 0: a real key's high word is never 0, so padding entries (key 0)
+    // are never candidates.
+    const unsigned t = (unsigned)__builtin_amdgcn_readlane((int)myh, (int)__builtin_ctzll(at));
+    int n = 0;   // this lane's candidates: a prefix of its sorted entries
+#pragma unroll
+    for (int i = 0; i < 4; ++i) n += (unsigned)(key[i] >> 32) >= t ? 1 : 0;
+    int nc;
+    const int pos = wave_excl_scan<3>((unsigned)n, &nc);   // nc <= 4k <= 64
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < n) {
+        T.key[pos + i] = key[i];
+        T.id[pos + i] = id[i];
+        T.lg[pos + i] = lg[i];
+      }
+    int rank = 0;
+    unsigned long long kc = 0ull;
+    int ic = 0;
+    double lc = 0.0;
+    if (lane < nc) {
+      kc = T.key[lane];
+      ic = T.id[lane];
+      lc = T.lg[lane];
+    }
+    for (int j = 0; j < nc; ++j) {
+      const unsigned long long kj = T.key[j];
+      const int ij = T.id[j];
+      rank += (kj > kc || (kj == kc && ij < ic)) ? 1 : 0;
+    }
+    if (lane < nc && rank < k) {   // slot `rank`
+      T.id[rank] = ic;
+      T.lg[rank] = lc;
+    }
+    if (lane < k) {
+      my_e = T.id[lane];
+      my_l = T.lg[lane];
+    }
+    lmax = T.lg[0];
+    my_w = row_weights(a, lr, lane < k, my_l, lmax);
+    return;
+  }
+  int left = 0;  // entries of this lane already taken
   for (int j = 0; j < k; ++j) {
     const bool have = left < nvalid;
     const unsigned hh = have ? (unsigned)(key[0] >> 32) : 0u;
@@ -1121,21 +1232,38 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, int &my_e, double
 // Every thread of a workgroup of NT threads: routing of all m rows into L,
 // published to the workspace (and the caller's idx/w outputs), with one
 // SlotRec per active slot.
-template <int NT, typename LDS>
-__device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish) {
+//
+// EARLY_TB: thread e < E requests expert e's table entries at the start,
+// together with the logits, and holds them until it writes the slot record
+// of an active e (the route kernel, where the records are on the critical
+// path); otherwise the records' entries are requested at the end.  With one
+// row and nothing to publish, waves 1.. copy every expert's gate/up entries
+// into tab ([6][MAX_EXPERTS], LDS) meanwhile, and each active slot's entries
+// end up in L.one_row; wave 0, which selects, holds none of them.
+template <int NT, bool EARLY_TB, typename LDS>
+__device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, uint64_t (*tab)[MAX_EXPERTS]) {
   constexpr int NW = NT / WAVE;
+  static_assert(NW <= LDS::kWaves, "a top-k scratch per wave");
+  static_assert(NW >= 2, "one_row: waves 1.. copy the tables");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int E = a.E, k = a.K, m = a.m, te = m * k;
   const int nc = m * E;
-  // Thread e < E requests expert e's table entries now; if e turns out
-  // active it writes that slot's record at the end.
+  const bool one_row = m == 1 && !publish;
   uint64_t tb[9] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
   if (tid < E) {
     L.mask[tid] = 0u;
-    if (publish) {
+    if (EARLY_TB && publish) {
       tb[0] = a.gw[tid]; tb[1] = a.uw[tid]; tb[2] = a.dw[tid];
       if (a.gs) { tb[3] = a.gs[tid]; tb[4] = a.us[tid]; tb[5] = a.ds[tid]; }
       if (a.gb) { tb[6] = a.gb[tid]; tb[7] = a.ub[tid]; tb[8] = a.db[tid]; }
+    }
+  }
+  if (one_row && wave > 0) {
+    for (int e = tid - WAVE; e < E; e += NT - WAVE) {
+      const uint64_t g = a.gw[e], u = a.uw[e];
+      const uint64_t gs = a.gs ? a.gs[e] : 0ull, us = a.gs ? a.us[e] : 0ull;
+      const uint64_t gb = a.gb ? a.gb[e] : 0ull, ub = a.gb ? a.ub[e] : 0ull;
+      tab[0][e] = g; tab[1][e] = u; tab[2][e] = gs; tab[3][e] = us; tab[4][e] = gb; tab[5][e] = ub;
     }
   }
   const bool by_rank = nc <= LDS::kCand && nc * E <= NT * RANK_MAX_CMP;
@@ -1144,10 +1272,18 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish) {
     // row's keys that beat it (a larger key, or an equal key with a lower
     // index) -- a strict order, so ranks 0..k-1 are the slots in order.  S
     // threads share a candidate's comparisons.
+    const bool biased = a.routing == ROUTE_SIGMOID_BIAS;
     for (int c = tid; c < nc; c += NT) {
       const int r = c / E, i = c - r * E;
-      const double l = load_coherent(a.logits + (size_t)r * (E + 1) + i);
-      const double kd = a.routing == ROUTE_SIGMOID_BIAS ? sigmoid_d(l) + (double)a.ebias[i] : l;
+      double l, kd;
+      if (biased) {   // both loads go out together
+        const float b = a.ebias[i];
+        l = load_coherent(a.logits + (size_t)r * (E + 1) + i);
+        kd = sigmoid_d(l) + (double)b;
+      } else {
+        l = load_coherent(a.logits + (size_t)r * (E + 1) + i);
+        kd = l;
+      }
       L.rk.key[c] = order_key(kd);
       L.rk.lg[c] = l;
       L.rk.rank[c] = 0;
@@ -1197,7 +1333,7 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish) {
       const double my_l = mine ? L.rk.sel[r * k + lane] : 0.0;
       w = row_weights(a, a.logits + (size_t)r * (E + 1), mine, my_l, L.rk.sel[r * k]);
     } else {
-      row_topk(a, r, e, w);
+      row_topk(a, r, L.tk[wave], e, w);
     }
     if (lane < k) {
       const float wf = (float)(w * (double)a.rsf);
@@ -1229,7 +1365,20 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish) {
     }
   }
   __syncthreads();
-  if (m == 1 && !publish) return;
+  if (one_row) {
+    // off[e] of an unselected e is stale or was written as a neighbour's
+    // end; active[] holds distinct experts, so active[off[e]] == e only for
+    // a selected e.
+    if (tid < E) {
+      const int pos = clamp_i(L.off[tid], 0, k - 1);
+      if (L.active[pos] == tid) {
+#pragma unroll
+        for (int j = 0; j < 6; ++j) L.one_row[j][pos] = tab[j][tid];
+      }
+    }
+    __syncthreads();
+    return;
+  }
   // Stable counting sort by expert (mask zeroed at the start).  A row selects an expert at most once, so
   // bit r of mask[e] says whether row r chose e, and a pair's rank inside its
   // expert is the number of earlier rows that chose the same expert.
@@ -1287,6 +1436,11 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish) {
   }
   if (publish && tid < E && L.mask[tid] != 0u) {
     const int e = tid;
+    if (!EARLY_TB) {
+      tb[0] = a.gw[e]; tb[1] = a.uw[e]; tb[2] = a.dw[e];
+      if (a.gs) { tb[3] = a.gs[e]; tb[4] = a.us[e]; tb[5] = a.ds[e]; }
+      if (a.gb) { tb[6] = a.gb[e]; tb[7] = a.ub[e]; tb[8] = a.db[e]; }
+    }
     SlotRec rec;
     rec.e = e;
     rec.off = L.off[e];
@@ -1589,6 +1743,17 @@ __device__ __forceinline__ void shared_dn_item(const Args &a, int item, MfmaLDS<
 
 // ------------------------------------------------------------------ kernels
 
+// gate_up's LDS: the shared down items' staging (variants that run them), or
+// -- one row, routing in every workgroup -- the experts' gate/up table
+// entries, which are consumed before any item starts.
+template <bool MF> union GateUpLDS {
+  MfmaLDS<WPB, 1> mf;
+  uint64_t tab[6][MAX_EXPERTS];
+};
+template <> union GateUpLDS<false> {
+  uint64_t tab[6][MAX_EXPERTS];
+};
+
 // Launch 1: router workgroups (ROUTE_UNITS_PER_WG units, RSPLIT waves each),
 // then the shared expert's gate/up items -- these need no routing, so they
 // stream meanwhile.  Each router workgroup stores its logits and takes a
@@ -1600,7 +1765,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
   struct RouterSmem {
     double part[ROUTE_WPB][8];
     unsigned ticket;
-    RouteLDS<1024> L;
+    RouteLDS<1024, ROUTE_WPB> L;
   };
   __shared__ union {
     RouterSmem r;
@@ -1611,7 +1776,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
   if (item < a.n_router_wg) {
     double (&s_part)[ROUTE_WPB][8] = sm.r.part;
     unsigned &s_ticket = sm.r.ticket;
-    RouteLDS<1024> &L = sm.r.L;
+    RouteLDS<1024, ROUTE_WPB> &L = sm.r.L;
     const int unit = item * ROUTE_UNITS_PER_WG + wave / RSPLIT, part = wave % RSPLIT;
     const bool live = unit < a.n_router;
     double tot[8];
@@ -1641,7 +1806,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
       s_ticket = __hip_atomic_fetch_add(a.sync + SYNC_ROUTER_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (s_ticket != (unsigned)(a.n_router_wg - 1)) return;
-    route_all<ROUTE_THREADS>(a, L, true);
+    route_all<ROUTE_THREADS, true>(a, L, true, nullptr);
     if (tid == 0) a.sync[SYNC_ROUTER_TICKET] = 0u;  // every ticket is taken
     return;
   }
@@ -1672,28 +1837,38 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
   constexpr int NI = gate_up_ni<EF>();
   const int ips = a.gu_items_per_slot;
   const int wave = uniform_i(threadIdx.x >> 6);
-  __shared__ MfmaLDS<WPB, 1> S;
+  __shared__ GateUpLDS<(SHD > 0)> GS;
   if (a.route_in_gu) {
     // The last workgroup only publishes the routing; the others stream.
-    __shared__ RouteLDS<256> L;
+    __shared__ RouteLDS<256, WPB> L;
     const int nb = gridDim.x - 1;
     const bool publisher = (int)blockIdx.x == nb;
-    route_all<THREADS>(a, L, publisher);
+    route_all<THREADS, false>(a, L, publisher, GS.tab);
     if (publisher) return;
     const int n = L.nact * ips;
     for (int it = blockIdx.x; it < n + (SHD ? a.n_shared_dn : 0); it += nb) {
-      if (SHD && it >= n) {
-        shared_dn_item<ACT, SHD>(a, it - n, S);
-        continue;
+      if constexpr (SHD > 0) {
+        if (it >= n) {
+          shared_dn_item<ACT, SHD>(a, it - n, GS.mf);
+          continue;
+        }
       }
       const int s = it / ips, b = it - s * ips;
       const int e = uniform_i(clamp_i(L.active[s], 0, a.E - 1));
       const int off = uniform_i(L.off[e]), np = uniform_i(L.off[e + 1]) - off;
       const int i0 = (b * WPB + wave) * NI;
-      if (i0 < a.I)
-        gate_up_rows<EF, ACT, CR, NI>(a, tbl(a.gw, e), tbl(a.uw, e), tbl(a.gs, e), tbl(a.us, e),
-                                      tbl(a.gb, e), tbl(a.ub, e), a.I, i0, off, np, L.sorted + off,
-                                      L.w, a.act, a.I);
+      if (i0 < a.I) {
+        const void *p[6];
+        if (a.m == 1) {   // entries requested with the logits
+#pragma unroll
+          for (int j = 0; j < 6; ++j) p[j] = reinterpret_cast<const void *>(uniform_u64(L.one_row[j][s]));
+        } else {
+          p[0] = tbl(a.gw, e); p[1] = tbl(a.uw, e); p[2] = tbl(a.gs, e);
+          p[3] = tbl(a.us, e); p[4] = tbl(a.gb, e); p[5] = tbl(a.ub, e);
+        }
+        gate_up_rows<EF, ACT, CR, NI>(a, p[0], p[1], p[2], p[3], p[4], p[5], a.I, i0, off, np,
+                                      L.sorted + off, L.w, a.act, a.I);
+      }
     }
     return;
   }
@@ -1702,9 +1877,11 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
   const int n = nact * ips;
   SlotRec nxt = pre;   // record of the next routed item, requested one item ahead
   for (int it = blockIdx.x; it < n + (SHD ? a.n_shared_dn : 0); it += gridDim.x) {
-    if (SHD && it >= n) {
-      shared_dn_item<ACT, SHD>(a, it - n, S);
-      continue;
+    if constexpr (SHD > 0) {
+      if (it >= n) {
+        shared_dn_item<ACT, SHD>(a, it - n, GS.mf);
+        continue;
+      }
     }
     const int s = it / ips, b = it - s * ips;
     const SlotRec rec = nxt;
