@@ -193,6 +193,12 @@ __device__ __forceinline__ double dpp_f64(double v) {
 __device__ __forceinline__ float readlane_f32(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 __device__ __forceinline__ double readlane_f64(double v, int l) {
   const unsigned long long b = (unsigned long long)__double_as_longlong(v);
   const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, l);
@@ -228,22 +234,6 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   v = v + dpp_f64<DPP_HALF_MIRROR>(v);
   v = v + dpp_f64<DPP_MIRROR>(v);
   return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
-}
-
-template <int CTRL>
-__device__ __forceinline__ unsigned dpp_u32(unsigned v) {
-  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-
-// Wave maximum of an unsigned value, wave-uniform result.
-__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
-  v = max(v, dpp_u32<DPP_XOR1>(v));
-  v = max(v, dpp_u32<DPP_XOR2>(v));
-  v = max(v, dpp_u32<DPP_HALF_MIRROR>(v));
-  v = max(v, dpp_u32<DPP_MIRROR>(v));
-  const unsigned a = max((unsigned)__builtin_amdgcn_readlane((int)v, 0), (unsigned)__builtin_amdgcn_readlane((int)v, 16));
-  const unsigned b = max((unsigned)__builtin_amdgcn_readlane((int)v, 32), (unsigned)__builtin_amdgcn_readlane((int)v, 48));
-  return max(a, b);
 }
 
 // Exclusive prefix sum over the wave's lanes of v (0 <= v < 2^BITS), from
@@ -1036,19 +1026,6 @@ __device__ __forceinline__ unsigned long long order_key(double v) {
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-// Compare-exchange for (key descending, index ascending).
-__device__ __forceinline__ void cx(unsigned long long &ka, int &ia, double &la, unsigned long long &kb,
-                                   int &ib, double &lb) {
-  const bool sw = kb > ka || (kb == ka && ib < ia);
-  if (sw) {
-    const unsigned long long tk = ka;
-    const double tl = la;
-    const int ti = ia;
-    ka = kb; la = lb; ia = ib;
-    kb = tk; lb = tl; ib = ti;
-  }
-}
-
 // Routing weight of the slot held by this lane (lanes 0..k-1 hold slots
 // 0..k-1; `mine` marks them), in double: softmax over all experts -- with
 // norm_topk_prob the full denominator cancels and only the selected terms
@@ -1085,7 +1062,7 @@ __device__ __forceinline__ double row_weights(const Args &a, const double *lr, b
 
 // Lane l's four candidates of a row (experts 4l..4l+3; lr: the row's
 // logits): order keys, logits and indices; padding past E gets key 0 (below
-// every real key) and an index after every real one.  Every load is issued
+// every real key) and a unique index after every real one.  Every load is issued
 // before any is used -- one memory round trip; a lane past E loads entry
 // E - 1 and discards it.
 template <bool BIASED>
@@ -1107,47 +1084,37 @@ __device__ __forceinline__ void lane_keys(const Args &a, const double *lr, unsig
     double kd = lg[i];
     if constexpr (BIASED) kd = sigmoid_d(lg[i]) + (double)bias[i];
     key[i] = ok ? order_key(kd) : 0ull;
-    id[i] = ok ? e : 0x7FFFFFFF - (3 - i);
+    id[i] = ok ? e : 0x40000000 + e;   // unique, after every real index
   }
 }
 
 // Top-k of row r by one wave (T: the wave's scratch).  Keys are compared as
 // order-preserving 64-bit integers, which is exactly the order of the double
-// keys; ties go to the lower index.  Lane l holds experts 4l..4l+3 (E <= 256)
-// and sorts them locally by (key desc, index asc).  Slot j's expert and
+// keys; ties go to the lower index, so (key desc, index asc) is a strict
+// order.  Lane l holds experts 4l..4l+3 (E <= 256).  Slot j's expert and
 // weight end up in lane j.
 //
-// Selection by threshold: let t be the k-th largest of the lanes' best high
-// key words.  If only one lane's best has that high word, the k lanes whose
-// best reaches t hold every entry of the top k (at least k entries are >= that
-// lane's best), so the entries with high word >= t -- at most 4k -- are the
-// candidates, and each candidate's rank among them is its slot.  Otherwise
-// (a tie on the high word at the threshold) the wave takes the best head k
-// times: the high key word by an integer DPP max (the low word only when
-// heads tie on the high one), the lane by a ballot -- the lowest lane holding
-// the maximum also holds the lowest index, because lanes own ascending index
-// ranges.
+// Selection by threshold: let T be the k-th best of the lanes' best entries.
+// Exactly k lanes have a best entry at least T, so at least k entries are,
+// and so is every entry of the top k; the entries at least T -- at most 4k,
+// all from those k lanes -- are the candidates, and each candidate's rank
+// among them (counted against every other candidate) is its slot.  T is
+// first sought on the high key words alone; when several lanes' best high
+// words tie at the k-th place, on the full (key, index) order.
 template <typename TL>
 __device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e, double &my_w) {
-  const int lane = threadIdx.x & 63, E = a.E, k = a.K;
-  const double *lr = a.logits + (size_t)r * (E + 1);
+  const int lane = threadIdx.x & 63, k = a.K;
+  const double *lr = a.logits + (size_t)r * (a.E + 1);
   unsigned long long key[4];
   double lg[4];
   int id[4];
   if (a.routing == ROUTE_SIGMOID_BIAS) lane_keys<true>(a, lr, key, lg, id);
   else lane_keys<false>(a, lr, key, lg, id);
-  int nvalid = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) nvalid += (4 * lane + i < E) ? 1 : 0;
-  cx(key[0], id[0], lg[0], key[1], id[1], lg[1]);
-  cx(key[2], id[2], lg[2], key[3], id[3], lg[3]);
-  cx(key[0], id[0], lg[0], key[2], id[2], lg[2]);
-  cx(key[1], id[1], lg[1], key[3], id[3], lg[3]);
-  cx(key[1], id[1], lg[1], key[2], id[2], lg[2]);
-  double lmax = 0.0, my_l = 0.0;
-  my_e = 0;
   // One wave: its LDS accesses complete in program order, so no barrier.
-  const unsigned myh = (unsigned)(key[0] >> 32);
+  unsigned hk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hk[i] = (unsigned)(key[i] >> 32);
+  const unsigned myh = max(max(hk[0], hk[1]), max(hk[2], hk[3]));   // the lane's best high word
   T.hw[lane] = myh;
   int gt = 0;   // lanes whose best has a larger high word
 #pragma unroll 4
@@ -1156,77 +1123,77 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e,
     gt += (v.x > myh ? 1 : 0) + (v.y > myh ? 1 : 0) + (v.z > myh ? 1 : 0) + (v.w > myh ? 1 : 0);
   }
   const unsigned long long at = __builtin_amdgcn_ballot_w64(gt == k - 1);
+  bool cand[4];
   if (__builtin_popcountll(at) == 1) {
-    // t > 0: a real key's high word is never 0, so padding entries (key 0)
-    // are never candidates.
+    // A real key's high word is never 0, so padding (key 0) is never a
+    // candidate.
     const unsigned t = (unsigned)__builtin_amdgcn_readlane((int)myh, (int)__builtin_ctzll(at));
-    int n = 0;   // this lane's candidates: a prefix of its sorted entries
 #pragma unroll
-    for (int i = 0; i < 4; ++i) n += (unsigned)(key[i] >> 32) >= t ? 1 : 0;
-    int nc;
-    const int pos = wave_excl_scan<3>((unsigned)n, &nc);   // nc <= 4k <= 64
+    for (int i = 0; i < 4; ++i) cand[i] = hk[i] >= t;
+  } else {
+    // The lane's best entry in the full order, and the lanes that beat it.
+    unsigned long long bk = key[0];
+    int bi = id[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i < n) {
-        T.key[pos + i] = key[i];
-        T.id[pos + i] = id[i];
-        T.lg[pos + i] = lg[i];
+    for (int i = 1; i < 4; ++i)
+      if (key[i] > bk || (key[i] == bk && id[i] < bi)) {
+        bk = key[i];
+        bi = id[i];
       }
-    int rank = 0;
-    unsigned long long kc = 0ull;
-    int ic = 0;
-    double lc = 0.0;
-    if (lane < nc) {
-      kc = T.key[lane];
-      ic = T.id[lane];
-      lc = T.lg[lane];
-    }
-    for (int j = 0; j < nc; ++j) {
+    T.key[lane] = bk;
+    T.id[lane] = bi;
+    int gf = 0;
+#pragma unroll 4
+    for (int j = 0; j < WAVE; ++j) {
       const unsigned long long kj = T.key[j];
       const int ij = T.id[j];
-      rank += (kj > kc || (kj == kc && ij < ic)) ? 1 : 0;
+      gf += (kj > bk || (kj == bk && ij < bi)) ? 1 : 0;
     }
-    if (lane < nc && rank < k) {   // slot `rank`
-      T.id[rank] = ic;
-      T.lg[rank] = lc;
-    }
-    if (lane < k) {
-      my_e = T.id[lane];
-      my_l = T.lg[lane];
-    }
-    lmax = T.lg[0];
-    my_w = row_weights(a, lr, lane < k, my_l, lmax);
-    return;
+    const int tl = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(gf == k - 1));   // exactly one lane
+    const unsigned long long tk = readlane_u64(bk, tl);
+    const int ti = __builtin_amdgcn_readlane(bi, tl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cand[i] = key[i] > tk || (key[i] == tk && id[i] <= ti);
   }
-  int left = 0;  // entries of this lane already taken
-  for (int j = 0; j < k; ++j) {
-    const bool have = left < nvalid;
-    const unsigned hh = have ? (unsigned)(key[0] >> 32) : 0u;
-    const unsigned mh = wave_max_u32(hh);
-    bool cand = have && hh == mh;
-    unsigned long long b = __builtin_amdgcn_ballot_w64(cand);
-    if (__builtin_popcountll(b) > 1) {  // tie on the high half: settle on the low half
-      const unsigned hl = cand ? (unsigned)key[0] : 0u;
-      const unsigned ml = wave_max_u32(hl);
-      cand = cand && hl == ml;
-      b = __builtin_amdgcn_ballot_w64(cand);
+  int n = 0;   // this lane's candidates
+#pragma unroll
+  for (int i = 0; i < 4; ++i) n += cand[i] ? 1 : 0;
+  int nc;
+  int q = wave_excl_scan<3>((unsigned)n, &nc);   // nc <= 4k <= 64
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (cand[i]) {
+      T.key[q] = key[i];
+      T.id[q] = id[i];
+      T.lg[q] = lg[i];
+      ++q;
     }
-    const int wl = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(b));
-    const int win = __builtin_amdgcn_readlane(id[0], wl);
-    const double lw = readlane_f64(lg[0], wl);
-    if (lane == wl) {  // pop the head
-      key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0ull;
-      lg[0] = lg[1]; lg[1] = lg[2]; lg[2] = lg[3];
-      id[0] = id[1]; id[1] = id[2]; id[2] = id[3];
-      ++left;
-    }
-    if (j == 0) lmax = lw;
-    if (lane == j) {
-      my_e = win;
-      my_l = lw;
-    }
+  // Lane c takes candidate c and counts the candidates that beat it.
+  unsigned long long kc = 0ull;
+  int ic = 0;
+  double lc = 0.0;
+  if (lane < nc) {
+    kc = T.key[lane];
+    ic = T.id[lane];
+    lc = T.lg[lane];
   }
-  my_w = row_weights(a, lr, lane < k, my_l, lmax);
+  int rank = 0;
+  for (int j = 0; j < nc; ++j) {
+    const unsigned long long kj = readlane_u64(kc, j);
+    const int ij = __builtin_amdgcn_readlane(ic, j);
+    rank += (kj > kc || (kj == kc && ij < ic)) ? 1 : 0;
+  }
+  if (lane < nc && rank < k) {   // slot `rank`
+    T.id[rank] = ic;
+    T.lg[rank] = lc;
+  }
+  double my_l = 0.0;
+  my_e = 0;
+  if (lane < k) {
+    my_e = T.id[lane];
+    my_l = T.lg[lane];
+  }
+  my_w = row_weights(a, lr, lane < k, my_l, T.lg[0]);
 }
 
 // Every thread of a workgroup of NT threads: routing of all m rows into L,
@@ -1244,8 +1211,11 @@ template <int NT, bool EARLY_TB, typename LDS>
 __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, uint64_t (*tab)[MAX_EXPERTS]) {
   constexpr int NW = NT / WAVE;
   static_assert(NW <= LDS::kWaves, "a top-k scratch per wave");
-  static_assert(NW >= 2, "one_row: waves 1.. copy the tables");
+  static_assert(NW >= 2, "one_row: the waves that select no row copy the tables");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
+  // Rows go to waves from vw = 0 on, where wave blockIdx % NW is vw 0: the
+  // workgroups sharing a compute unit then select on different SIMDs.
+  const int vw = (wave + NW - (int)(blockIdx.x % NW)) % NW;
   const int E = a.E, k = a.K, m = a.m, te = m * k;
   const int nc = m * E;
   const bool one_row = m == 1 && !publish;
@@ -1258,8 +1228,8 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, u
       if (a.gb) { tb[6] = a.gb[tid]; tb[7] = a.ub[tid]; tb[8] = a.db[tid]; }
     }
   }
-  if (one_row && wave > 0) {
-    for (int e = tid - WAVE; e < E; e += NT - WAVE) {
+  if (one_row && vw > 0) {
+    for (int e = (vw - 1) * WAVE + lane; e < E; e += NT - WAVE) {
       const uint64_t g = a.gw[e], u = a.uw[e];
       const uint64_t gs = a.gs ? a.gs[e] : 0ull, us = a.gs ? a.us[e] : 0ull;
       const uint64_t gb = a.gb ? a.gb[e] : 0ull, ub = a.gb ? a.ub[e] : 0ull;
@@ -1324,7 +1294,7 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, u
     }
     __syncthreads();
   }
-  for (int r = wave; r < m; r += NW) {
+  for (int r = vw; r < m; r += NW) {
     int e;
     double w;
     if (by_rank) {
