@@ -138,16 +138,18 @@ typedef struct {
   size_t pair_to_perm;    /* int32 [te]: position of pair p in sorted_pair */
   size_t active_experts;  /* int32 [cap]: experts with at least one pair, ascending */
   size_t active_count;    /* int32 [1] */
-  size_t slot_info;       /* [cap] 64-byte records, one per active slot u < active_count:
+  size_t slot_info;       /* [cap] 128-byte records, one per active slot u < active_count:
                              int32 expert, first position in sorted_pair, pair count, 0;
-                             then the expert's down_w, down_s, down_b entries (uint64) */
+                             then the expert's gate_w, up_w, gate_s, up_s, gate_b, up_b,
+                             down_w, down_s, down_b entries (uint64), then 40 zero bytes */
   size_t act;             /* float [te, I]: routed SwiGLU activations, sorted order; for 4-bit
                              experts each row is stored sub-step-major: element i at
                              ((i % 32) / 8) * (I / 4) + (i / 32) * 8 + i % 8 */
   size_t shared_act;      /* float [max_rows, Is] */
   size_t shared_y;        /* float [P, max_rows, H]: shared-expert output in P parts of Is
                              (matrix-core path; P = max(1, Is / 2048)) */
-  size_t sync;            /* uint32 [512]: reserved completion words, kept zero */
+  size_t sync;            /* uint32 [512]: reserved counters, zero between calls (word 0
+                             counts the router workgroups; the last arrival resets it) */
   size_t total;           /* bytes a workspace must have */
 } moe_decode_ws_layout;
 

@@ -1117,7 +1117,7 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e,
   const unsigned myh = max(max(hk[0], hk[1]), max(hk[2], hk[3]));   // the lane's best high word
   T.hw[lane] = myh;
   int gt = 0;   // lanes whose best has a larger high word
-#pragma unroll 4
+#pragma unroll 2
   for (int j = 0; j < WAVE; j += 4) {
     const u32x4 v = *reinterpret_cast<const u32x4 *>(T.hw + j);
     gt += (v.x > myh ? 1 : 0) + (v.y > myh ? 1 : 0) + (v.z > myh ? 1 : 0) + (v.w > myh ? 1 : 0);
@@ -1143,7 +1143,7 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e,
     T.key[lane] = bk;
     T.id[lane] = bi;
     int gf = 0;
-#pragma unroll 4
+#pragma unroll 2
     for (int j = 0; j < WAVE; ++j) {
       const unsigned long long kj = T.key[j];
       const int ij = T.id[j];

@@ -79,7 +79,7 @@ def test_plan_and_layout_for_every_workload(name):
                   (L.topk_idx, te * 4), (L.topk_w, te * 4), (L.row_gate, spec.max_rows * 4),
                   (L.sorted_pair, te * 4), (L.expert_offsets, (spec.num_experts + 1) * 4),
                   (L.pair_to_perm, te * 4), (L.active_experts, min(te, spec.num_experts) * 4),
-                  (L.active_count, 4), (L.slot_info, min(te, spec.num_experts) * 64),
+                  (L.active_count, 4), (L.slot_info, min(te, spec.num_experts) * 128),
                   (L.act, te * spec.inter * 4),
                   (L.shared_act, spec.max_rows * (spec.shared_inter if spec.shared else 0) * 4),
                   (L.shared_y, max(1, spec.shared_inter // 2048) * spec.max_rows

@@ -194,6 +194,29 @@ def test_every_row_count_and_pass_variant():
         assert np.array_equal(got, full[:m])
 
 
+# The matrix-core shared expert at several H and Is: short and long Is (a
+# long one splits the down over parts of Is), one and two column tiles
+# (m <= 16, m > 16).
+@pytest.mark.parametrize("hidden,shared_inter", [(1024, 512), (512, 1024), (256, 96), (512, 4096)])
+def test_shared_expert_shapes(hidden, shared_inter):
+    spec = small(hidden=hidden, num_experts=8, top_k=2, inter=64, shared=True, shared_gated=True,
+                 shared_inter=shared_inter, rows=(32,))
+    layer = synth.make_layer(spec, seed=hidden + shared_inter)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    dl = DeviceLayer(layer)
+    say(f"[gpu] shared H={hidden} Is={shared_inter} m=32")
+    full, idx, w = run(dl, x, 32)
+    check(spec, full, idx, w, ref, 32, TOL["bf16"], f"shared H={hidden} Is={shared_inter} m=32")
+    for m in (1, 5, 16, 17):
+        say(f"[gpu] shared H={hidden} Is={shared_inter} m={m}")
+        got, idx, w = run(dl, x, m)
+        check(spec, got, idx, w, ref, m, TOL["bf16"], f"shared H={hidden} Is={shared_inter} m={m}")
+        assert np.array_equal(got, full[:m])
+    del dl
+    torch.cuda.empty_cache()
+
+
 # Long rows (I >= 4096) also take the split of each down row into parts.
 @pytest.mark.parametrize("fmt,inter", [("bf16", 64), ("bf16", 256), ("bf16", 768), ("bf16", 1024),
                                        ("mxfp4", 512), ("mxfp4", 1024), ("aff4", 1792),
