@@ -64,8 +64,15 @@ constexpr int SYNC_WORDS = 512;
 constexpr int SYNC_ROUTER_TICKET = 0;
 
 // Rows of intermediate per gate/up wave: 2 for 16-byte-per-8-or-4 element
-// formats, 4 for the 4-bit ones (their rows are 4x shorter).
-template <int WF> constexpr int gate_up_ni() { return WF >= AFF4 ? 4 : 2; }
+// formats; 4 for the 4-bit ones (their rows are 4x shorter) with one vector
+// per pass, or next to the matrix-core shared down items, whose registers
+// bound the occupancy anyway.  4-bit passes of several vectors otherwise
+// take 2 rows: the registers then allow four waves per SIMD, which hide the
+// weights' latency behind each other's dequantisation better than twice the
+// rows per wave does.
+template <int WF, int CR = 1, int SHD = 0> constexpr int gate_up_ni() {
+  return WF >= AFF4 && (CR == 1 || SHD > 0) ? 4 : 2;
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -1804,7 +1811,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
 // expert's down items this variant also runs.
 template <int EF, int ACT, int CR, int CS, int SHD>
 __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
-  constexpr int NI = gate_up_ni<EF>();
+  constexpr int NI = gate_up_ni<EF, CR, SHD>();
   const int ips = a.gu_items_per_slot;
   const int wave = uniform_i(threadIdx.x >> 6);
   __shared__ GateUpLDS<(SHD > 0)> GS;

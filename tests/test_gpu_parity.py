@@ -89,6 +89,18 @@ def check_sort(dl, m, idx):
     assert np.array_equal(off, want["expert_offsets"])
     assert np.array_equal(p2p, want["pair_to_perm"])
     assert cnt == want["active_count"] and np.array_equal(act, want["active_experts"])
+    # One 128-byte record per active slot: expert, pair range, the expert's
+    # table entries, then zero padding.
+    recs = dl.ws_view("slot_info", torch.int32, max(cnt, 1) * 32).cpu().numpy().reshape(-1, 32)[:cnt]
+    ptrs = recs.view(np.int64)
+    tabs = {k: v.cpu().numpy() for k, v in dl.copies[0].tables.items()}
+    names = ("gate", "up", "gate_s", "up_s", "gate_b", "up_b", "down", "down_s", "down_b")
+    for u, e in enumerate(act):
+        n_e = off[e + 1] - off[e]
+        assert list(recs[u, :4]) == [e, off[e], n_e, 0], f"slot {u}: {recs[u, :4]}"
+        for f, name in enumerate(names):
+            assert ptrs[u, 2 + f] == (tabs[name][e] if name in tabs else 0), f"slot {u}: {name}"
+        assert not recs[u, 22:].any()
 
 
 # --------------------------------------------------------------- workloads
