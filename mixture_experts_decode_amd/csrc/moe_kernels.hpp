@@ -1003,7 +1003,6 @@ template <int NCAND> struct RankLDS {
 
 // One wave's scratch for the top-k of one row (row_topk).
 struct alignas(16) TopkLDS {
-  unsigned hw[WAVE];              // high key words of the lanes' best entries
   unsigned long long key[WAVE];   // candidates, then the selection
   int id[WAVE];
   double lg[WAVE];
@@ -1122,19 +1121,21 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e,
 #pragma unroll
   for (int i = 0; i < 4; ++i) hk[i] = (unsigned)(key[i] >> 32);
   const unsigned myh = max(max(hk[0], hk[1]), max(hk[2], hk[3]));   // the lane's best high word
-  T.hw[lane] = myh;
-  int gt = 0;   // lanes whose best has a larger high word
-#pragma unroll 2
-  for (int j = 0; j < WAVE; j += 4) {
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(T.hw + j);
-    gt += (v.x > myh ? 1 : 0) + (v.y > myh ? 1 : 0) + (v.z > myh ? 1 : 0) + (v.w > myh ? 1 : 0);
+  // t = the k-th largest of the lanes' best high words, bit by bit from the
+  // top: keep a bit when at least k lanes reach the value with it set.
+  unsigned t = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const unsigned c = t | (1u << b);
+    if (__builtin_popcountll(__builtin_amdgcn_ballot_w64(myh >= c)) >= k) t = c;
   }
-  const unsigned long long at = __builtin_amdgcn_ballot_w64(gt == k - 1);
+  // Exactly one lane's best has high word t when k lanes reach t and k - 1
+  // exceed it.
+  const bool unique = __builtin_popcountll(__builtin_amdgcn_ballot_w64(myh >= t)) == k &&
+                      __builtin_popcountll(__builtin_amdgcn_ballot_w64(myh > t)) == k - 1;
   bool cand[4];
-  if (__builtin_popcountll(at) == 1) {
+  if (unique) {
     // A real key's high word is never 0, so padding (key 0) is never a
     // candidate.
-    const unsigned t = (unsigned)__builtin_amdgcn_readlane((int)myh, (int)__builtin_ctzll(at));
 #pragma unroll
     for (int i = 0; i < 4; ++i) cand[i] = hk[i] >= t;
   } else {
