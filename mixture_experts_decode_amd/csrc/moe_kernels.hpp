@@ -599,14 +599,33 @@ template <int WF, int XF, int RG, int C> struct Unroll {
   static constexpr int U = !XPF ? U0 : SUB == 1 ? clampu((128 - RG * C) / (W + C * XS)) : 1;
 };
 
-template <int WF, int XF, int RG, int C, int LPR>
+// Issues the loads of the first chunk step of wave_rows_dot<..., U> over
+// chunks [c0, nchunks) into pre (used through PRE below).
+template <int WF, int RG, int U, int LPR>
+__device__ __forceinline__ void preload_step(const Row<WF> (&rows)[RG], int c0, int nchunks, WChunk<WF> (&pre)[U][RG]) {
+  const int li = threadIdx.x % LPR;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int ch = c0 + li + u * LPR;
+    if (ch < nchunks) {
+#pragma unroll
+      for (int t = 0; t < RG; ++t) pre[u][t] = load_wchunk<WF, LPR == WAVE>(rows[t], ch);
+    }
+  }
+}
+
+// PRE: pre holds the first chunk step, requested earlier by preload_step
+// with the same U; used when use_pre.
+template <int WF, int XF, int RG, int C, int LPR, bool PRE = false, int UP = 1>
 __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const char *const (&xrow)[C],
-                                              int c0, int nchunks, float (&acc)[RG][C], int gs = 0) {
+                                              int c0, int nchunks, float (&acc)[RG][C], int gs = 0,
+                                              const WChunk<WF> (*pre)[RG] = nullptr, bool use_pre = false) {
   using O = XOps<WF, XF>;
   using X = typename O::X;
   constexpr int U = Unroll<WF, XF, RG, C>::U;
   constexpr bool XPF = Unroll<WF, XF, RG, C>::XPF;
   constexpr int SUB = O::SUB;
+  static_assert(!PRE || U == UP, "the preloaded step has this pass's unroll");
   const int li = threadIdx.x % LPR;
 #pragma unroll
   for (int t = 0; t < RG; ++t)
@@ -619,8 +638,13 @@ __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const c
     for (int u = 0; u < U; ++u) {
       const int ch = base + li + u * LPR;
       if (ch < nchunks) {
+        if (PRE && use_pre && base == c0) {
 #pragma unroll
-        for (int t = 0; t < RG; ++t) w[u][t] = load_wchunk<WF, LPR == WAVE>(rows[t], ch);
+          for (int t = 0; t < RG; ++t) w[u][t] = pre[u][t];
+        } else {
+#pragma unroll
+          for (int t = 0; t < RG; ++t) w[u][t] = load_wchunk<WF, LPR == WAVE>(rows[t], ch);
+        }
         if constexpr (XPF) {
 #pragma unroll
           for (int c = 0; c < C; ++c)
@@ -702,8 +726,16 @@ __device__ __forceinline__ int row_bytes(int K) {
   return K * (WF == F32 ? 4 : WF == BF16 ? 2 : 1) / (WF >= AFF4 ? 2 : 1);
 }
 
+// Every array a wave reads through a resource is the same for the whole
+// wave; the base and size are made wave-uniform here so that the compiler
+// keeps the resource in scalar registers (a resource it cannot prove uniform
+// costs a loop over lanes around every load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  void *q = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 // The matrix [N, K] at w (scales s, biases b for 4-bit formats): one
@@ -1302,6 +1334,7 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, u
     }
     __syncthreads();
   }
+  int one_e = 0, one_pos = 0;   // one row: this lane's expert and its slot (lanes < k of vw 0)
   for (int r = vw; r < m; r += NW) {
     int e;
     double w;
@@ -1333,6 +1366,8 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, u
       // experts, and pair j is that slot's only pair.
       int pos = 0;
       for (int i = 0; i < k; ++i) pos += __builtin_amdgcn_readlane(e, i) < e ? 1 : 0;
+      one_e = e;
+      one_pos = pos;
       if (lane < k) {
         L.active[pos] = e;
         L.sorted[pos] = lane;
@@ -1344,15 +1379,11 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, u
   }
   __syncthreads();
   if (one_row) {
-    // off[e] of an unselected e is stale or was written as a neighbour's
-    // end; active[] holds distinct experts, so active[off[e]] == e only for
-    // a selected e.
-    if (tid < E) {
-      const int pos = clamp_i(L.off[tid], 0, k - 1);
-      if (L.active[pos] == tid) {
+    // The selecting wave's lanes j < k hold slot one_pos's expert one_e; the
+    // other waves' table copies are complete after the barrier above.
+    if (vw == 0 && lane < k) {
 #pragma unroll
-        for (int j = 0; j < 6; ++j) L.one_row[j][pos] = tab[j][tid];
-      }
+      for (int j = 0; j < 6; ++j) L.one_row[j][one_pos] = tab[j][clamp_i(one_e, 0, E - 1)];
     }
     __syncthreads();
     return;
