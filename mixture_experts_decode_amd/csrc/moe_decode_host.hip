@@ -325,9 +325,7 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   // route launch, down in the gate/up launch) for bf16 activations when H and
   // Is are multiples of 32; on the vector units otherwise.
   a.shared_mfma = shared && d.act_fmt == MOE_BF16 && d.hidden % 32 == 0 && a.Is % 32 == 0;
-  // gate_up_ni<EF, CR, SHD>(): the matrix-core shared expert runs the
-  // variants with shared down items (SHD > 0).
-  const int ni_r = d.expert_fmt >= MOE_AFF4_G64 && (cr == 1 || a.shared_mfma) ? 4 : 2;
+  const int ni_r = d.expert_fmt >= MOE_AFF4_G64 && cr == 1 ? 4 : 2;   // gate_up_ni<EF, CR>()
   a.max_rows = d.max_rows;
   a.sd_parts = shared_down_parts(d);
   if (a.shared_mfma) {

@@ -65,14 +65,10 @@ constexpr int SYNC_ROUTER_TICKET = 0;
 
 // Rows of intermediate per gate/up wave: 2 for 16-byte-per-8-or-4 element
 // formats; 4 for the 4-bit ones (their rows are 4x shorter) with one vector
-// per pass, or next to the matrix-core shared down items, whose registers
-// bound the occupancy anyway.  4-bit passes of several vectors otherwise
-// take 2 rows: the registers then allow four waves per SIMD, which hide the
-// weights' latency behind each other's dequantisation better than twice the
-// rows per wave does.
-template <int WF, int CR = 1, int SHD = 0> constexpr int gate_up_ni() {
-  return WF >= AFF4 && (CR == 1 || SHD > 0) ? 4 : 2;
-}
+// per pass.  4-bit passes of several vectors take 2 rows: the registers then
+// allow four waves per SIMD, which hide the weights' latency behind each
+// other's dequantisation better than twice the rows per wave does.
+template <int WF, int CR = 1> constexpr int gate_up_ni() { return WF >= AFF4 && CR == 1 ? 4 : 2; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -810,28 +806,35 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const bf16x8 &b, const f
 // bytes) over k in [kb, ke) (multiples of 32), into acc[j][ct] for vectors
 // 16 ct .. 16 ct + 15.
 //
-// The weights go through LDS: a batch of MF_U k-steps is 16 rows x 256
-// bytes per matrix, loaded with lane-linear 16-byte loads (each instruction
-// reads 4 rows x 256 contiguous bytes; the MFMA lane pattern itself would
-// read 16 rows x 64 bytes per instruction, which streams about a quarter
-// slower), written to this wave's own LDS region, and read back in the MFMA
-// layout.  The next batch's loads are in flight meanwhile.  `stage` is the
-// wave's region, NA * 16 * MF_ROW bytes.
+// The weights go through LDS: a batch of MU k-steps (MF_U by default) is 16
+// rows x MU * 64 bytes per matrix, loaded with lane-linear 16-byte loads
+// (with MU = 4 each instruction reads 4 rows x 256 contiguous bytes; the MFMA
+// lane pattern itself would read 16 rows x 64 bytes per instruction, which
+// streams about a quarter slower), written to this wave's own LDS region,
+// and read back in the MFMA layout.  The next batch's loads are in flight
+// meanwhile.  `stage` is the wave's region, NA * 16 * (MU * 64 + 16) bytes.
 constexpr int MF_U = 4;                  // k-steps of 32 per batch
 constexpr int MF_ROW = MF_U * 64 + 16;   // bytes per staged row (16 bytes of padding)
 constexpr int MF_STAGE = 16 * MF_ROW;    // staged bytes per matrix per wave
 
-template <int XF, int NA, int NCT>
+template <int XF, int NA, int NCT, int MU = MF_U>
 __device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA], int rb, int n0, int N,
                                            const char *x, size_t xstride, int nv, int kb, int ke,
                                            char *stage, f32x4 (&acc)[NA][NCT]) {
+  constexpr int ROW = MU * 64 + 16, STAGE = 16 * ROW;   // staging layout of MU k-steps
+  static_assert(MU <= MF_U, "the wave's staging region holds MF_U k-steps");
   constexpr int XB = XF == F32 ? 4 : 2;
   constexpr int XL = XF == F32 ? 2 : 1;   // 16-byte x loads per step and column tile
   const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
-  // Loader: instruction i brings rows 4 i + g, bytes rr * 16 .. + 16 of the batch.
-  int loff[MF_U];
+  // Loader: a staged row is MU * 64 bytes, LR = 4 MU lanes of 16 bytes;
+  // instruction i brings rows RI i + l / LR (RI = 16 / MU rows per
+  // instruction), bytes (l % LR) * 16 .. + 16 of the batch.
+  constexpr int LR = 4 * MU, RI = 16 / MU;
+  static_assert(MU == 1 || MU == 2 || MU == 4, "16 rows split evenly over the loads");
+  const int lrow = l / LR, lcol = l % LR;
+  int loff[MU];
 #pragma unroll
-  for (int i = 0; i < MF_U; ++i) loff[i] = min(n0 + 4 * i + g, N - 1) * rb + rr * 16;
+  for (int i = 0; i < MU; ++i) loff[i] = min(n0 + RI * i + lrow, N - 1) * rb + lcol * 16;
   const char *xv[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) xv[ct] = x + (size_t)min(16 * ct + rr, nv - 1) * xstride + (size_t)g * 8 * XB;
@@ -841,14 +844,14 @@ __device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA]
     for (int ct = 0; ct < NCT; ++ct) acc[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (kb >= ke) return;
   // Weights and x of the next batch are requested together, one batch ahead.
-  u32x4 nxt[NA][MF_U], nxb[MF_U][NCT][XL];
+  u32x4 nxt[NA][MU], nxb[MU][NCT][XL];
   auto fetch = [&](int kq) {
 #pragma unroll
     for (int j = 0; j < NA; ++j)
 #pragma unroll
-      for (int i = 0; i < MF_U; ++i) nxt[j][i] = __builtin_amdgcn_raw_buffer_load_b128(A[j], loff[i] + kq * 2, 0, BUF_NT);
+      for (int i = 0; i < MU; ++i) nxt[j][i] = __builtin_amdgcn_raw_buffer_load_b128(A[j], loff[i] + kq * 2, 0, BUF_NT);
 #pragma unroll
-    for (int u = 0; u < MF_U; ++u) {
+    for (int u = 0; u < MU; ++u) {
       const int kk = min(kq + 32 * u, ke - 32);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
@@ -857,36 +860,36 @@ __device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA]
     }
   };
   fetch(kb);
-  for (int k0 = kb; k0 < ke; k0 += 32 * MF_U) {
-    u32x4 cur[NA][MF_U], bv[MF_U][NCT][XL];
+  for (int k0 = kb; k0 < ke; k0 += 32 * MU) {
+    u32x4 cur[NA][MU], bv[MU][NCT][XL];
 #pragma unroll
     for (int j = 0; j < NA; ++j)
 #pragma unroll
-      for (int i = 0; i < MF_U; ++i) cur[j][i] = nxt[j][i];
+      for (int i = 0; i < MU; ++i) cur[j][i] = nxt[j][i];
 #pragma unroll
-    for (int u = 0; u < MF_U; ++u)
+    for (int u = 0; u < MU; ++u)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int h = 0; h < XL; ++h) bv[u][ct][h] = nxb[u][ct][h];
-    const int k1 = k0 + 32 * MF_U;
+    const int k1 = k0 + 32 * MU;
     if (k1 < ke) fetch(k1);
 #pragma unroll
     for (int j = 0; j < NA; ++j)
 #pragma unroll
-      for (int i = 0; i < MF_U; ++i)
-        *reinterpret_cast<u32x4 *>(stage + j * MF_STAGE + (4 * i + g) * MF_ROW + rr * 16) = cur[j][i];
+      for (int i = 0; i < MU; ++i)
+        *reinterpret_cast<u32x4 *>(stage + j * STAGE + (RI * i + lrow) * ROW + lcol * 16) = cur[j][i];
     // The region is this wave's alone; its LDS accesses complete in order.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int u = 0; u < MF_U; ++u) {
+    for (int u = 0; u < MU; ++u) {
       if (k0 + 32 * u < ke) {
         u32x4 av[NA];
 #pragma unroll
         for (int j = 0; j < NA; ++j)
-          av[j] = *reinterpret_cast<const u32x4 *>(stage + j * MF_STAGE + rr * MF_ROW + u * 64 + g * 16);
+          av[j] = *reinterpret_cast<const u32x4 *>(stage + j * STAGE + rr * ROW + u * 64 + g * 16);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           if constexpr (XF == BF16) {
@@ -919,9 +922,10 @@ __device__ __forceinline__ void k_slice(int K, int w, int nw, int &kb, int &ke) 
 }
 
 // Partials of the NW waves of one matrix-core item, added in wave order.
-template <int NW, int NA> struct MfmaLDS {
+// MU: k-steps per staged batch (mfma_slice<..., MU>).
+template <int NW, int NA, int MU = MF_U> struct MfmaLDS {
   float part[NW][NA][2][4][WAVE];   // [wave][matrix][column tile][i][lane]
-  alignas(16) char stage[NW][NA * MF_STAGE];   // each wave's weight staging
+  alignas(16) char stage[NW][NA * 16 * (MU * 64 + 16)];   // each wave's weight staging
 };
 
 __device__ __forceinline__ size_t act_bytes(int fmt) { return fmt == F32 ? 4 : 2; }
@@ -1716,8 +1720,8 @@ __device__ __forceinline__ void shared_gu_mfma(const Args &a, int item, MfmaLDS<
 // of the a.sd_parts parts of Is); the WPB waves of the workgroup split the
 // part, and the part's total goes to sy[q] (the blend adds the parts in
 // order).
-template <int NCT>
-__device__ __forceinline__ void shared_dn_mfma(const Args &a, int item, MfmaLDS<WPB, 1> &S) {
+template <int NCT, int MU>
+__device__ __forceinline__ void shared_dn_mfma(const Args &a, int item, MfmaLDS<WPB, 1, MU> &S) {
   const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int H = a.H, Is = a.Is, m = a.m, P = a.sd_parts;
   const int tile = item / P, q = item - tile * P, n0 = tile * 16;
@@ -1726,7 +1730,7 @@ __device__ __forceinline__ void shared_dn_mfma(const Args &a, int item, MfmaLDS<
   k_slice(Is, q, P, pb, pe);
   k_slice(pe - pb, w, WPB, kb, ke);
   f32x4 acc[1][NCT];
-  mfma_slice<F32, 1, NCT>(A, Is * 2, n0, H, reinterpret_cast<const char *>(a.sact), (size_t)Is * 4, m,
+  mfma_slice<F32, 1, NCT, MU>(A, Is * 2, n0, H, reinterpret_cast<const char *>(a.sact), (size_t)Is * 4, m,
                           pb + kb, pb + ke, S.stage[w], acc);
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
@@ -1745,21 +1749,27 @@ __device__ __forceinline__ void shared_dn_mfma(const Args &a, int item, MfmaLDS<
   __syncthreads();   // S is reused by the workgroup's next item
 }
 
-template <int ACT, int NCT>
-__device__ __forceinline__ void shared_dn_item(const Args &a, int item, MfmaLDS<WPB, 1> &S) {
-  if constexpr (ACT == BF16 && NCT > 0) shared_dn_mfma<NCT>(a, item, S);   // the matrix-core path
+template <int ACT, int NCT, int MU>
+__device__ __forceinline__ void shared_dn_item(const Args &a, int item, MfmaLDS<WPB, 1, MU> &S) {
+  if constexpr (ACT == BF16 && NCT > 0) shared_dn_mfma<NCT, MU>(a, item, S);   // the matrix-core path
 }
+
+// k-steps per batch of the shared down items in a gate/up variant: 2 where
+// that lets the variant reach four waves per SIMD (registers and LDS) -- one
+// vector per pass, or 4-bit experts -- else 4, which streams a long shared
+// down faster.
+template <int EF, int CR> constexpr int shared_dn_mu() { return CR == 1 || EF >= AFF4 ? 2 : 4; }
 
 // ------------------------------------------------------------------ kernels
 
 // gate_up's LDS: the shared down items' staging (variants that run them), or
 // -- one row, routing in every workgroup -- the experts' gate/up table
 // entries, which are consumed before any item starts.
-template <bool MF> union GateUpLDS {
-  MfmaLDS<WPB, 1> mf;
+template <bool MF, int MU> union GateUpLDS {
+  MfmaLDS<WPB, 1, MU> mf;
   uint64_t tab[6][MAX_EXPERTS];
 };
-template <> union GateUpLDS<false> {
+template <int MU> union GateUpLDS<false, MU> {
   uint64_t tab[6][MAX_EXPERTS];
 };
 
@@ -1843,10 +1853,11 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
 // expert's down items this variant also runs.
 template <int EF, int ACT, int CR, int CS, int SHD>
 __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
-  constexpr int NI = gate_up_ni<EF, CR, SHD>();
+  constexpr int NI = gate_up_ni<EF, CR>();
   const int ips = a.gu_items_per_slot;
   const int wave = uniform_i(threadIdx.x >> 6);
-  __shared__ GateUpLDS<(SHD > 0)> GS;
+  constexpr int SDMU = shared_dn_mu<EF, CR>();
+  __shared__ GateUpLDS<(SHD > 0), SDMU> GS;
   if (a.route_in_gu) {
     // The last workgroup only publishes the routing; the others stream.
     __shared__ RouteLDS<256, WPB> L;
@@ -1858,7 +1869,7 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
     for (int it = blockIdx.x; it < n + (SHD ? a.n_shared_dn : 0); it += nb) {
       if constexpr (SHD > 0) {
         if (it >= n) {
-          shared_dn_item<ACT, SHD>(a, it - n, GS.mf);
+          shared_dn_item<ACT, SHD, SDMU>(a, it - n, GS.mf);
           continue;
         }
       }
@@ -1888,7 +1899,7 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
   for (int it = blockIdx.x; it < n + (SHD ? a.n_shared_dn : 0); it += gridDim.x) {
     if constexpr (SHD > 0) {
       if (it >= n) {
-        shared_dn_item<ACT, SHD>(a, it - n, GS.mf);
+        shared_dn_item<ACT, SHD, SDMU>(a, it - n, GS.mf);
         continue;
       }
     }
