@@ -368,7 +368,11 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto ev = [&](int i) -> hipEvent_t { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
   hipError_t e;
-  if ((e = moe::launch_route(d.act_fmt, cs, a, a.n_router_wg + a.n_shared_gu, s, ev(0), ev(1))) != hipSuccess)
+  // The pass width only shapes the vector-unit shared gate/up; with the
+  // matrix-core one the narrowest variant runs (fewest registers, so two
+  // workgroups share a CU).
+  const int route_cs = a.shared_mfma ? 1 : cs;
+  if ((e = moe::launch_route(d.act_fmt, route_cs, a, a.n_router_wg + a.n_shared_gu, s, ev(0), ev(1))) != hipSuccess)
     return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
   // gate_up: a grid-stride launch over the active slots' items.
   // With the routing computed in gate/up, one more workgroup publishes it.
