@@ -18,7 +18,7 @@ of them can be regenerated alone and the experts can be drawn in parallel):
     stream key [seed, 7, b]      activation block b: x [max_rows, H]
 
 Each weight is ``f32(z * std)`` with ``z`` a float32 standard normal, then
-stored as f32, bf16 (RNE) or quantized (aff4 / mxfp4 below).  ``x`` is
+stored as f32, bf16 (RNE) or quantized (aff4 / mxfp4 / nvfp4 below).  ``x`` is
 ``f32(z * x_std)`` stored in the activation format.
 
 Formats (stored codes):
@@ -32,6 +32,13 @@ Formats (stored codes):
     and one E8M0 byte per 32 elements, ``scale [N, K/32]``.  Quantizer:
     ``e = clamp(floor(log2(amax)) - 2 + 127, 1, 254)``, code = nearest E2M1
     value of ``w / 2^(e-127)``, ties to the even code, saturating at 6.
+  * ``nvfp4``: E2M1 codes packed like mxfp4, one OCP E4M3 byte per 16
+    elements, ``scale [N, K/16]``, and one float32 second-level scale per
+    expert projection, ``scale2 [E]``.  Quantizer (per projection):
+    ``s2 = f32(amax / (6 * 448))`` (1 if amax = 0); per block the E4M3 value
+    nearest ``amax_block / (6 * s2)`` (ties to the even code); codes = nearest
+    E2M1 value of ``w / (E4M3(scale) * s2)``, ties to the even code,
+    saturating at 6 (all 0 where the block scale is 0).
 """
 from __future__ import annotations
 
@@ -43,12 +50,13 @@ from typing import Optional
 import numpy as np
 
 ACT_FORMATS = ("f32", "bf16")
-EXPERT_FORMATS = ("f32", "bf16", "aff4", "mxfp4")
+EXPERT_FORMATS = ("f32", "bf16", "aff4", "mxfp4", "nvfp4")
 ROUTINGS = ("softmax", "sigmoid_bias", "sigmoid_logit")
 
-# Group sizes of the two 4-bit formats along the reduction dimension K.
+# Group sizes of the 4-bit formats along the reduction dimension K.
 AFF4_GROUP = 64
 MXFP4_BLOCK = 32
+NVFP4_BLOCK = 16
 
 
 @dataclasses.dataclass(frozen=True)
@@ -173,6 +181,49 @@ def quantize_mxfp4(w: np.ndarray):
     return packed, e.astype(np.uint8)
 
 
+def _e4m3_positive_values() -> np.ndarray:
+    """Values of the E4M3 bytes 0x00..0x7E (the non-negative, non-NaN codes)."""
+    b = np.arange(0x7F)
+    ex, man = b >> 3, b & 7
+    return np.where(ex == 0, np.ldexp(man / 8.0, -6), np.ldexp(1.0 + man / 8.0, ex - 7))
+
+
+_E4M3_POS = _e4m3_positive_values()
+_E4M3_MIDPOINTS = 0.5 * (_E4M3_POS[1:] + _E4M3_POS[:-1])
+
+
+def _nearest_code(a: np.ndarray, midpoints: np.ndarray) -> np.ndarray:
+    """Index of the nearest table value for a >= 0 (ties to the even index,
+    saturating at the last one)."""
+    code = np.searchsorted(midpoints, a, side="left")
+    last = len(midpoints)
+    tie = (code < last) & (a == midpoints[np.minimum(code, last - 1)])
+    code = np.where(tie & (code % 2 == 1), code + 1, code)
+    return np.minimum(code, last)
+
+
+def quantize_nvfp4(w: np.ndarray):
+    """NVFP4 quantizer -> (packed [N, K/2], E4M3 scale bytes [N, K/16], float32 s2)."""
+    n, k = w.shape
+    assert k % NVFP4_BLOCK == 0
+    w64 = w.astype(np.float64)
+    amax = float(np.abs(w64).max()) if w64.size else 0.0
+    s2 = np.float32(amax / (6.0 * 448.0)) if amax > 0 else np.float32(1.0)
+    if s2 == 0:
+        s2 = np.float32(1.0)
+    g = w64.reshape(n, k // NVFP4_BLOCK, NVFP4_BLOCK)
+    target = np.abs(g).max(axis=2) / (6.0 * float(s2))
+    sc = _nearest_code(np.minimum(target, 448.0), _E4M3_MIDPOINTS).astype(np.uint8)
+    denom = _E4M3_POS[sc] * float(s2)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        scaled = np.where(denom[..., None] > 0, g / denom[..., None], 0.0)
+    code = _nearest_code(np.abs(scaled), _E2M1_MIDPOINTS)
+    code = code | np.where(scaled < 0, 8, 0)
+    code = code.astype(np.uint8).reshape(n, k)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sc, s2
+
+
 # ----------------------------------------------------------------------------
 # Layer generation.
 # ----------------------------------------------------------------------------
@@ -200,7 +251,8 @@ class Projection:
     """All E experts' copies of one projection, stacked on axis 0.
 
     ``data`` is [E, N, K] (f32 / bf16 bits) or [E, N, K/2] packed 4-bit codes;
-    ``scale`` / ``bias`` are [E, N, K/G] or None.
+    ``scale`` / ``bias`` are [E, N, K/G] or None; ``scale2`` is the nvfp4
+    second-level scale of each expert's copy, [E] float32, else None.
     """
 
     fmt: str
@@ -209,6 +261,7 @@ class Projection:
     data: np.ndarray
     scale: Optional[np.ndarray] = None
     bias: Optional[np.ndarray] = None
+    scale2: Optional[np.ndarray] = None
 
 
 @dataclasses.dataclass
@@ -237,6 +290,8 @@ class Layer:
                 tot += p.scale[0].nbytes
             if p.bias is not None:
                 tot += p.bias[0].nbytes
+            if p.scale2 is not None:
+                tot += p.scale2[0].nbytes
         return tot
 
 
@@ -252,6 +307,10 @@ def _alloc_projection(fmt: str, e: int, n: int, k: int) -> Projection:
     if fmt == "mxfp4":
         return Projection(fmt, n, k, np.empty((e, n, k // 2), np.uint8),
                           np.empty((e, n, k // MXFP4_BLOCK), np.uint8))
+    if fmt == "nvfp4":
+        return Projection(fmt, n, k, np.empty((e, n, k // 2), np.uint8),
+                          np.empty((e, n, k // NVFP4_BLOCK), np.uint8),
+                          scale2=np.empty((e,), np.float32))
     raise ValueError(fmt)
 
 
@@ -264,6 +323,8 @@ def _fill_expert(proj: Projection, e: int, w: np.ndarray) -> None:
         proj.data[e], proj.scale[e], proj.bias[e] = quantize_aff4(w)
     elif proj.fmt == "mxfp4":
         proj.data[e], proj.scale[e] = quantize_mxfp4(w)
+    elif proj.fmt == "nvfp4":
+        proj.data[e], proj.scale[e], proj.scale2[e] = quantize_nvfp4(w)
 
 
 def check_spec(spec: LayerSpec) -> None:
@@ -275,6 +336,8 @@ def check_spec(spec: LayerSpec) -> None:
         raise ValueError("aff4 needs H and I multiples of 64")
     if spec.expert_fmt == "mxfp4" and (spec.hidden % MXFP4_BLOCK or spec.inter % MXFP4_BLOCK):
         raise ValueError("mxfp4 needs H and I multiples of 32")
+    if spec.expert_fmt == "nvfp4" and (spec.hidden % 32 or spec.inter % 32):
+        raise ValueError("nvfp4 needs H and I multiples of 32")
 
 
 def make_layer(spec: LayerSpec, seed: int = 0, threads: Optional[int] = None) -> Layer:

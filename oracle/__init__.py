@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 
-FMT = {"f32": 0, "bf16": 1, "aff4": 2, "mxfp4": 3}
+FMT = {"f32": 0, "bf16": 1, "aff4": 2, "mxfp4": 3, "nvfp4": 4}
 ROUTING = {"softmax": 0, "sigmoid_bias": 1, "sigmoid_logit": 2}
 
 
@@ -66,6 +66,8 @@ def lib():
         L.orc_forward.restype = C.c_int32
         L.orc_forward.argtypes = [C.POINTER(_Desc), C.POINTER(_Weights), C.c_void_p, C.c_int32,
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+        L.orc_e4m3_value.restype = C.c_double
+        L.orc_e4m3_value.argtypes = [C.c_uint8]
         L.orc_decode_act.restype = C.c_double
         L.orc_decode_act.argtypes = [C.c_int32, C.c_void_p, C.c_int64]
         L.orc_decode_row.restype = None
@@ -125,7 +127,9 @@ class _Bound:
         w.expert_bias = _ptr(layer.expert_bias)
         for name in ("gate", "up", "down"):
             p = getattr(layer, name)
-            for suffix, arr in (("", p.data), ("_s", p.scale), ("_b", p.bias)):
+            # nvfp4: the "_b" entry of expert e points to its second-level scale.
+            second = p.scale2 if p.scale2 is not None else p.bias
+            for suffix, arr in (("", p.data), ("_s", p.scale), ("_b", second)):
                 t = _table(arr)
                 self.keep.append(t)
                 setattr(w, name + suffix, C.cast(t, _PP) if t is not None else None)
@@ -221,6 +225,11 @@ def decode_row(fmt: str, w: np.ndarray, s: Optional[np.ndarray], b: Optional[np.
                          _ptr(None if s is None else np.ascontiguousarray(s)),
                          _ptr(None if b is None else np.ascontiguousarray(b)), K, n, _ptr(out))
     return out
+
+
+def e4m3_value(b: int) -> float:
+    """One OCP FP8 E4M3 byte as a float (NaN for the NaN codes)."""
+    return float(lib().orc_e4m3_value(int(b)))
 
 
 def decode_act(fmt: str, a: np.ndarray) -> np.ndarray:

@@ -18,7 +18,9 @@
  *    where the routing weight multiplies a routed expert (input or output);
  *    the raw-logit top-k of the weight-before-FFN model.
  *  - "helpers_a.rs" (metrale): transpose_for_prefill_impl -- the E8M0 scale
- *    block of 32; packed [N, K/2] weights with [N, K/group] scales.
+ *    block of 32; packed [N, K/2] weights with [N, K/group] scales; the
+ *    NVFP4 scale block of 16, and the per-expert second-level scale
+ *    (weight_scale_2, the scale2 values) each projection carries.
  *
  * Every stored value is decoded exactly to double; every dot product,
  * exponential, normalisation and sum is taken in double, in the order the
@@ -29,7 +31,12 @@
  *  - normalisation (sum of the selected weights, no epsilon) comes before
  *    routed_scaling_factor;
  *  - the shared expert reads the unscaled row; its gate is sigmoid(x . w_g);
- *  - the blend sums the slots in slot order, then adds the shared term.
+ *  - the blend sums the slots in slot order, then adds the shared term;
+ *  - NVFP4 weights are the NVIDIA NVFP4 encoding the page names: E2M1 codes,
+ *    one E4M3 block scale per 16 elements along K, times the projection's
+ *    fp32 second-level scale; the activations stay in their own format
+ *    (weight-only dequantisation; the page's input_scale, which quantises
+ *    activations for a 4-bit GEMM, has no part in it).
  */
 #include "moe_oracle.h"
 
@@ -64,6 +71,17 @@ static double e2m1_value(unsigned code) {
 /* OCP MX E8M0 scale: 2^(e - 127). */
 static double e8m0_value(uint8_t e) { return ldexp(1.0, (int)e - 127); }
 
+/* OCP FP8 E4M3 (the "FN" variant: no infinities): sign bit 7, exponent
+ * bits 6..3 (bias 7), mantissa bits 2..0; exponent 0 is subnormal
+ * (mantissa/8 * 2^-6); exponent and mantissa all ones is NaN. */
+double orc_e4m3_value(uint8_t b) {
+  double sign = (b & 0x80u) ? -1.0 : 1.0;
+  unsigned ex = (b >> 3) & 15u, man = b & 7u;
+  if (ex == 15u && man == 7u) return NAN;
+  double mag = ex == 0 ? ldexp((double)man / 8.0, -6) : ldexp(1.0 + (double)man / 8.0, (int)ex - 7);
+  return sign * mag;
+}
+
 /* The 4-bit code of element k of row n of a packed [N, K/2] array: element
  * 2t in the low nibble of byte t. */
 static unsigned nibble(const uint8_t *packed, int32_t K, int32_t n, int32_t k) {
@@ -92,6 +110,12 @@ void orc_decode_row(int32_t fmt, const void *w, const void *s, const void *b,
         size_t g = (size_t)n * (K / 32) + k / 32;
         out[k] = e2m1_value(nibble((const uint8_t *)w, K, n, k)) *
                  e8m0_value(((const uint8_t *)s)[g]);
+        break;
+      }
+      case ORC_NVFP4: { /* value = E2M1(code) * E4M3(s) * s2, one E4M3 per 16 */
+        size_t g = (size_t)n * (K / 16) + k / 16;
+        out[k] = e2m1_value(nibble((const uint8_t *)w, K, n, k)) *
+                 orc_e4m3_value(((const uint8_t *)s)[g]) * (double)*(const float *)b;
         break;
       }
       default:
@@ -261,10 +285,11 @@ static int valid_desc(const orc_desc *d) {
   if (d->hidden <= 0 || d->num_experts <= 0 || d->inter <= 0) return 0;
   if (d->top_k <= 0 || d->top_k > d->num_experts) return 0;
   if (d->act_fmt != ORC_F32 && d->act_fmt != ORC_BF16) return 0;
-  if (d->expert_fmt < ORC_F32 || d->expert_fmt > ORC_MXFP4) return 0;
+  if (d->expert_fmt < ORC_F32 || d->expert_fmt > ORC_NVFP4) return 0;
   if (d->routing < ORC_SOFTMAX || d->routing > ORC_SIGMOID_LOGIT) return 0;
   if (d->expert_fmt == ORC_AFF4 && (d->hidden % 64 || d->inter % 64)) return 0;
   if (d->expert_fmt == ORC_MXFP4 && (d->hidden % 32 || d->inter % 32)) return 0;
+  if (d->expert_fmt == ORC_NVFP4 && (d->hidden % 16 || d->inter % 16)) return 0;
   if (d->shared && d->shared_inter <= 0) return 0;
   return 1;
 }

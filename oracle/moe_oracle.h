@@ -17,14 +17,14 @@ extern "C" {
 #endif
 
 /* Storage formats (numbers chosen independently of the HIP library's). */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_AFF4 = 2, ORC_MXFP4 = 3 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_AFF4 = 2, ORC_MXFP4 = 3, ORC_NVFP4 = 4 };
 /* Routing modes. */
 enum { ORC_SOFTMAX = 0, ORC_SIGMOID_BIAS = 1, ORC_SIGMOID_LOGIT = 2 };
 
 typedef struct {
   int32_t hidden, num_experts, top_k, inter, shared_inter;
   int32_t act_fmt;      /* ORC_F32 / ORC_BF16: x, router, shared expert, w_g */
-  int32_t expert_fmt;   /* ORC_F32 / ORC_BF16 / ORC_AFF4 / ORC_MXFP4 */
+  int32_t expert_fmt;   /* ORC_F32 / ORC_BF16 / ORC_AFF4 / ORC_MXFP4 / ORC_NVFP4 */
   int32_t routing;
   int32_t norm_topk, weight_before_ffn, shared, shared_gated;
   double routed_scaling_factor;
@@ -35,7 +35,8 @@ typedef struct {
   const float *expert_bias;           /* [E] or NULL */
   /* Per-expert host pointers, [E] each.  f32/bf16: [N,K]; 4-bit: packed
    * [N,K/2] bytes, low nibble = even element; scale [N,K/G]; aff4 bias
-   * [N,K/64] bf16. */
+   * [N,K/64] bf16; nvfp4: the "bias" entry points to the projection's one
+   * fp32 second-level scale. */
   const void *const *gate, *const *up, *const *down;
   const void *const *gate_s, *const *up_s, *const *down_s;
   const void *const *gate_b, *const *up_b, *const *down_b;
@@ -43,6 +44,8 @@ typedef struct {
   const void *sh_gate_vec;               /* [H] act_fmt */
 } orc_weights;
 
+/* One OCP FP8 E4M3 byte decoded to double (NaN for the NaN codes). */
+double orc_e4m3_value(uint8_t b);
 /* One stored element decoded to double. */
 double orc_decode_act(int32_t fmt, const void *p, int64_t i);
 /* Row n of an [N,K] expert projection, decoded to double, out[K]. */

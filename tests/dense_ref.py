@@ -1,7 +1,8 @@
 """Brute-force dense evaluation of a decode MoE layer in NumPy fp64.
 
 A second, independent evaluation used only to pin the oracle on tiny inputs:
-it decodes stored codes with lookup tables (the oracle uses bit formulas),
+it decodes stored codes with lookup tables and, for the E4M3 block scales of
+nvfp4, with torch's float8_e4m3fn conversion (the oracle uses bit formulas),
 routes with a stable argsort (the oracle scans), and evaluates EVERY expert on
 every row, weighting by a mask that is zero for the experts a row did not
 select (the oracle evaluates only the selected ones, slot by slot).
@@ -45,7 +46,17 @@ def dense_weight(proj, e: int) -> np.ndarray:
     if proj.fmt == "mxfp4":
         sc = np.repeat(np.ldexp(1.0, proj.scale[e].astype(np.int64) - 127), 32, axis=1)
         return E2M1_TABLE[q] * sc
+    if proj.fmt == "nvfp4":
+        sc = np.repeat(e4m3_to_f64(proj.scale[e]), 16, axis=1)
+        return E2M1_TABLE[q] * sc * float(proj.scale2[e])
     raise ValueError(proj.fmt)
+
+
+def e4m3_to_f64(b: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 bytes -> float64 through torch's float8_e4m3fn dtype."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(b, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
 
 
 def _silu(v):

@@ -54,6 +54,65 @@ def test_e8m0_all_finite_codes():
         assert np.all(got == math.ldexp(1.0, n - 127)), n
 
 
+def test_e4m3_golden_values_of_the_standard():
+    g = json.load(open(os.path.join(GOLDEN, "e4m3_ocp.json")))
+    for b, v in g["byte_to_value"].items():
+        got = oracle.e4m3_value(int(b, 16))
+        assert got == v and math.copysign(1.0, got) == math.copysign(1.0, v), b
+    for b in g["nan_bytes"]:
+        assert math.isnan(oracle.e4m3_value(int(b, 16)))
+
+
+def test_e4m3_all_bytes_match_torch_float8():
+    want = dense_ref.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    got = np.array([oracle.e4m3_value(b) for b in range(256)])
+    nan = np.isnan(want)
+    assert list(np.flatnonzero(nan)) == [0x7F, 0xFF]
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_nvfp4_row_closed_form():
+    # Codes 0..15 then 15..0 over two blocks of 16; block scales 1.0 (0x38)
+    # and 2.0 (0x40); second-level scale 0.5 -> value = E2M1 * scale * 0.5.
+    table = json.load(open(os.path.join(GOLDEN, "e2m1_ocp.json")))["code_to_value"]
+    codes = np.concatenate([np.arange(16), np.arange(15, -1, -1)]).astype(np.uint8)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)[None, :]
+    scale = np.array([[0x38, 0x40]], np.uint8)
+    s2 = np.array([0.5], np.float32)
+    got = oracle.decode_row("nvfp4", packed, scale, s2, 32, 0)
+    want = np.array([table[c] * (1.0 if k < 16 else 2.0) * 0.5 for k, c in enumerate(codes)])
+    assert np.array_equal(got, want)
+    # Rows use their own scale row: row 1 of a two-row array.
+    packed2 = np.vstack([np.zeros_like(packed), packed])
+    scale2 = np.vstack([np.array([[0x7E, 0x7E]], np.uint8), scale])
+    assert np.array_equal(oracle.decode_row("nvfp4", packed2, scale2, s2, 32, 1), want)
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+def test_nvfp4_second_level_scale_is_linear_where_it_must_be(which):
+    # silu(g) * v is linear in v and the down projection in its weights, so
+    # multiplying the up or down second-level scale by 4 multiplies every
+    # routed output by 4, exactly (a power of two; no shared expert); the
+    # gate's is not linear.
+    spec = tiny(act_fmt="bf16", expert_fmt="nvfp4", top_k=3, w_std=0.05)
+    layer = synth.make_layer(spec, seed=21)
+    x = synth.make_x(spec, 21, rows=4)
+    r1 = oracle.forward(layer, x)
+    getattr(layer, which).scale2[:] *= np.float32(4.0)
+    oracle._bound_cache.clear()
+    r4 = oracle.forward(layer, x)
+    assert np.array_equal(r1.idx, r4.idx)
+    assert np.array_equal(r4.out, 4.0 * r1.out)
+    getattr(layer, which).scale2[:] /= np.float32(4.0)
+    layer.gate.scale2[:] *= np.float32(4.0)
+    oracle._bound_cache.clear()
+    rg = oracle.forward(layer, x)
+    assert np.max(np.abs(rg.out - 4.0 * r1.out)) > 1e-3 * rms(r1.out)
+    oracle._bound_cache.clear()
+
+
 def test_aff4_all_codes_random_scale_bias():
     rng = np.random.default_rng(1)
     for trial in range(20):
@@ -245,7 +304,7 @@ def test_identity_experts_give_silu_times_x(before):
 # ------------------------------------------ P-10 brute force, all variants
 
 VARIANTS = list(itertools.product(
-    ["f32", "bf16"], ["f32", "bf16", "aff4", "mxfp4"],
+    ["f32", "bf16"], ["f32", "bf16", "aff4", "mxfp4", "nvfp4"],
     ["softmax", "sigmoid_bias", "sigmoid_logit"], [False, True], [False, True],
     ["none", "plain", "gated"]))
 
@@ -375,10 +434,13 @@ def test_input_weight_commutes_with_projection():
 
 # ------------------------------------------- P-15 quantized decode is exact
 
-@pytest.mark.parametrize("fmt", ["aff4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["aff4", "mxfp4", "nvfp4"])
 def test_quantized_layer_equals_f32_layer_of_decoded_values(fmt):
     spec = tiny(act_fmt="bf16", expert_fmt=fmt, top_k=3, w_std=0.02)
     layer = synth.make_layer(spec, seed=18)
+    if fmt == "nvfp4":   # a power-of-two second-level scale keeps the values exact in f32
+        for name in ("gate", "up", "down"):
+            getattr(layer, name).scale2[:] = np.float32(2.0 ** -10)
     x = synth.make_x(spec, 18, rows=4)
     dense = synth.make_layer(spec.replace(expert_fmt="f32"), seed=18)
     for name in ("gate", "up", "down"):

@@ -65,3 +65,25 @@ def test_workloads_are_valid():
     for spec in synth.WORKLOADS.values():
         synth.check_spec(spec)
         assert spec.top_k <= spec.num_experts
+
+
+def test_nvfp4_quantizer_scales_and_error():
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((8, 64)) * 0.02).astype(np.float32)
+    w[2, 16:32] = 0.0                                   # an all-zero block
+    packed, sc, s2 = synth.quantize_nvfp4(w)
+    assert packed.shape == (8, 32) and sc.shape == (8, 4) and s2.dtype == np.float32
+    assert s2 == np.float32(np.abs(w).max() / (6.0 * 448.0))
+    assert sc.max() <= 0x7E and sc[2, 1] == 0          # E4M3 at most 448; zero block -> scale 0
+    codes = np.empty((8, 64), np.uint8)
+    codes[:, 0::2], codes[:, 1::2] = packed & 15, packed >> 4
+    assert not codes[2, 16:32].any()
+    proj = synth.Projection("nvfp4", 8, 64, packed[None], sc[None], scale2=np.array([s2]))
+    from tests import dense_ref
+    deq = dense_ref.dense_weight(proj, 0)
+    # Each element within half an E2M1 step of its block scale (plus the
+    # block scale's own rounding): a loose bound of 25% of the block maximum.
+    blk = np.abs(w.astype(np.float64)).reshape(8, 4, 16).max(axis=2)
+    err = np.abs(deq - w).reshape(8, 4, 16).max(axis=2)
+    assert np.all(err <= 0.25 * blk + 1e-12)
+    assert np.abs(deq - w).mean() < 0.1 * np.abs(w).mean()
