@@ -71,8 +71,15 @@ typedef enum {
  *                  ([N, K/64] each)
  *   MOE_MXFP4_B32  OCP MX FP4 E2M1 codes, packed like aff4; value =
  *                  E2M1(code) * 2^(e-127) with one E8M0 byte e per 32
- *                  elements along K ([N, K/32]); e = 255 (NaN) is not valid. */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_AFF4_G64 = 2, MOE_MXFP4_B32 = 3 } moe_format;
+ *                  elements along K ([N, K/32]); e = 255 (NaN) is not valid.
+ *   MOE_NVFP4_B16  NVFP4 (the same page: scale block 16, plus the per-expert
+ *                  second-level scale each projection carries): E2M1 codes
+ *                  packed like aff4; value = E2M1(code) * E4M3(s) * s2 with
+ *                  one OCP FP8 E4M3 byte s per 16 elements along K ([N, K/16])
+ *                  and one float32 s2 per expert projection (the *_scale2
+ *                  arrays below); the E4M3 NaN bytes 0x7F / 0xFF are not valid.
+ *                  The activations stay in act_fmt (weight-only dequantisation). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_AFF4_G64 = 2, MOE_MXFP4_B32 = 3, MOE_NVFP4_B16 = 4 } moe_format;
 
 typedef enum {
   MOE_ROUTE_SOFTMAX = 0,        /* select by logit, weight softmax(l) over all E */
@@ -89,7 +96,7 @@ enum {
 };
 
 typedef struct {
-  int32_t hidden;        /* H: multiple of 8 (f32/bf16), 64 (aff4), 32 (mxfp4) */
+  int32_t hidden;        /* H: multiple of 8 (f32/bf16), 64 (aff4), 32 (mxfp4, nvfp4) */
   int32_t num_experts;   /* E: 1..256 */
   int32_t top_k;         /* k: 1..min(E, 16) */
   int32_t inter;         /* I: routed expert intermediate size, same multiples as H */
@@ -111,9 +118,10 @@ typedef struct {
   const uint64_t *gate_w;      /* table: [I, H] (packed [I, H/2] for 4-bit) */
   const uint64_t *up_w;        /* table: [I, H] */
   const uint64_t *down_w;      /* table: [H, I] (packed [H, I/2]) */
-  const uint64_t *gate_s;      /* table of scales: aff4 bf16 [I, H/64], mxfp4 u8 [I, H/32]; else NULL */
+  const uint64_t *gate_s;      /* table of scales: aff4 bf16 [I, H/64], mxfp4 u8 [I, H/32],
+                                  nvfp4 u8 [I, H/16]; else NULL */
   const uint64_t *up_s;
-  const uint64_t *down_s;      /* aff4 bf16 [H, I/64], mxfp4 u8 [H, I/32] */
+  const uint64_t *down_s;      /* aff4 bf16 [H, I/64], mxfp4 u8 [H, I/32], nvfp4 u8 [H, I/16] */
   const uint64_t *gate_b;      /* table of aff4 biases, bf16 like the scales; else NULL */
   const uint64_t *up_b;
   const uint64_t *down_b;
@@ -121,6 +129,9 @@ typedef struct {
   const void *sh_up_w;         /* [Is, H] act_fmt */
   const void *sh_down_w;       /* [H, Is] act_fmt */
   const void *sh_gate_vec;     /* [H] act_fmt (MOE_SHARED_GATED) */
+  const float *gate_scale2;    /* nvfp4: [E] float32 second-level scale of each expert's gate; else ignored */
+  const float *up_scale2;      /* nvfp4: [E] float32, up */
+  const float *down_scale2;    /* nvfp4: [E] float32, down */
 } moe_decode_weights;
 
 typedef struct moe_decode_plan moe_decode_plan_t;

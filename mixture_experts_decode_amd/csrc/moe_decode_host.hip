@@ -116,9 +116,11 @@ int elems_per_chunk(int fmt) { return fmt == MOE_F32 ? 4 : fmt == MOE_BF16 ? 8 :
 
 const moe::FormatKernels &kernels_for(int act, int ef) {
   typedef const moe::FormatKernels &(*getter)();
-  static const getter t[2][4] = {
-      {moe::kernels_f32_f32, moe::kernels_f32_bf16, moe::kernels_f32_aff4, moe::kernels_f32_mxfp4},
-      {moe::kernels_bf16_f32, moe::kernels_bf16_bf16, moe::kernels_bf16_aff4, moe::kernels_bf16_mxfp4}};
+  static const getter t[2][5] = {
+      {moe::kernels_f32_f32, moe::kernels_f32_bf16, moe::kernels_f32_aff4, moe::kernels_f32_mxfp4,
+       moe::kernels_f32_nvfp4},
+      {moe::kernels_bf16_f32, moe::kernels_bf16_bf16, moe::kernels_bf16_aff4, moe::kernels_bf16_mxfp4,
+       moe::kernels_bf16_nvfp4}};
   return t[act][ef]();
 }
 
@@ -152,7 +154,7 @@ moe_status check_desc(const moe_decode_desc &d) {
     return fail(MOE_EINVAL, "hidden, num_experts, top_k, inter and max_rows must be positive");
   if (d.act_fmt != MOE_F32 && d.act_fmt != MOE_BF16)
     return fail(MOE_EINVAL, "act_fmt must be MOE_F32 or MOE_BF16 (got %d)", d.act_fmt);
-  if (d.expert_fmt < MOE_F32 || d.expert_fmt > MOE_MXFP4_B32)
+  if (d.expert_fmt < MOE_F32 || d.expert_fmt > MOE_NVFP4_B16)
     return fail(MOE_EINVAL, "unknown expert_fmt %d", d.expert_fmt);
   if (d.routing < MOE_ROUTE_SOFTMAX || d.routing > MOE_ROUTE_SIGMOID_LOGIT)
     return fail(MOE_EINVAL, "unknown routing %d", d.routing);
@@ -174,6 +176,8 @@ moe_status check_desc(const moe_decode_desc &d) {
     return fail(MOE_EUNSUPPORTED, "aff4-g64 experts need hidden and inter multiples of 64");
   if (d.expert_fmt == MOE_MXFP4_B32 && (d.hidden % 32 || d.inter % 32))
     return fail(MOE_EUNSUPPORTED, "mxfp4 experts need hidden and inter multiples of 32");
+  if (d.expert_fmt == MOE_NVFP4_B16 && (d.hidden % 32 || d.inter % 32))
+    return fail(MOE_EUNSUPPORTED, "nvfp4 experts need hidden and inter multiples of 32");
   if (d.flags & MOE_SHARED) {
     if (d.shared_inter <= 0 || d.shared_inter % 8)
       return fail(MOE_EUNSUPPORTED, "shared_inter must be a positive multiple of 8");
@@ -234,10 +238,12 @@ moe_status check_weights(const moe_decode_desc &d, const moe_decode_weights *w) 
     return fail(MOE_EINVAL, "router_w must be a non-null 16-byte aligned device pointer");
   if (!w->gate_w || !w->up_w || !w->down_w)
     return fail(MOE_EINVAL, "gate_w, up_w and down_w tables are required");
-  if (d.expert_fmt == MOE_AFF4_G64 || d.expert_fmt == MOE_MXFP4_B32) {
+  if (d.expert_fmt >= MOE_AFF4_G64) {
     if (!w->gate_s || !w->up_s || !w->down_s)
       return fail(MOE_EINVAL, "4-bit experts need gate_s, up_s and down_s tables");
   }
+  if (d.expert_fmt == MOE_NVFP4_B16 && (!w->gate_scale2 || !w->up_scale2 || !w->down_scale2))
+    return fail(MOE_EINVAL, "nvfp4 experts need gate_scale2, up_scale2 and down_scale2");
   if (d.expert_fmt == MOE_AFF4_G64 && (!w->gate_b || !w->up_b || !w->down_b))
     return fail(MOE_EINVAL, "aff4 experts need gate_b, up_b and down_b tables");
   if (d.routing == MOE_ROUTE_SIGMOID_BIAS && !w->expert_bias)
@@ -295,6 +301,9 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   a.gw = w->gate_w; a.uw = w->up_w; a.dw = w->down_w;
   a.gs = w->gate_s; a.us = w->up_s; a.ds = w->down_s;
   a.gb = w->gate_b; a.ub = w->up_b; a.db = w->down_b;
+  if (d.expert_fmt == MOE_NVFP4_B16) {
+    a.gs2 = w->gate_scale2; a.us2 = w->up_scale2; a.ds2 = w->down_scale2;
+  }
   a.sgw = w->sh_gate_w; a.suw = w->sh_up_w; a.sdw = w->sh_down_w; a.sgv = w->sh_gate_vec;
   a.logits = reinterpret_cast<double *>(ws + L.logits);
   a.topk_idx = reinterpret_cast<int32_t *>(ws + L.topk_idx);

@@ -32,12 +32,12 @@
 
 namespace moe {
 
-enum : int { F32 = 0, BF16 = 1, AFF4 = 2, MXFP4 = 3 };
+enum : int { F32 = 0, BF16 = 1, AFF4 = 2, MXFP4 = 3, NVFP4 = 4 };
 // x format of the down projection's input for 4-bit experts: f32, each row
 // stored sub-step-major (element i of the row at ((i % 32) / 8) * (I / 4) +
 // (i / 32) * 8 + i % 8), so that in sub-step g adjacent lanes (adjacent
 // 32-element chunks) read adjacent 32-byte blocks.
-enum : int { F32P = 4 };
+enum : int { F32P = 5 };
 enum : int { ROUTE_SOFTMAX = 0, ROUTE_SIGMOID_BIAS = 1, ROUTE_SIGMOID_LOGIT = 2 };
 enum : unsigned { NORM_TOPK = 1u, WEIGHT_BEFORE = 2u, SHARED = 4u, SHARED_GATED = 8u, OUT_F32 = 16u };
 
@@ -106,6 +106,7 @@ struct Args {
   const void *router;
   const float *ebias;
   const uint64_t *gw, *uw, *dw, *gs, *us, *ds, *gb, *ub, *db;
+  const float *gs2, *us2, *ds2;   // nvfp4: [E] second-level scale per projection
   const void *sgw, *suw, *sdw, *sgv;
   double *logits;          // [m, E+1]
   int32_t *topk_idx;       // [te]
@@ -283,12 +284,14 @@ template <> struct Fmt<F32> { static constexpr int EPC = 4; };
 template <> struct Fmt<BF16> { static constexpr int EPC = 8; };
 template <> struct Fmt<AFF4> { static constexpr int EPC = 32; };
 template <> struct Fmt<MXFP4> { static constexpr int EPC = 32; };
+template <> struct Fmt<NVFP4> { static constexpr int EPC = 32; };
 
 // One weight row, addressed through buffer resources: the matrix's data
 // resource (and, for the 4-bit formats, its scale and bias resources) and the
 // row's byte offset in the data.  A 4-bit row of K codes is K/2 bytes and its
 // scale row K/32 bytes (aff4: K/64 bf16; mxfp4: K/32 E8M0), so the scale
-// row's offset is off / 16 for both.
+// row's offset is off / 16 for both; the nvfp4 scale row is K/16 E4M3 bytes,
+// at off / 8.
 template <int WF> struct Row {
   __amdgpu_buffer_rsrc_t w, s, b;
   int off;
@@ -302,7 +305,7 @@ template <int WF> struct WChunk {
 };
 
 // VGPRs one loaded chunk holds.
-template <int WF> constexpr int wchunk_regs() { return WF == AFF4 ? 6 : WF == MXFP4 ? 5 : 4; }
+template <int WF> constexpr int wchunk_regs() { return WF == AFF4 ? 6 : WF >= MXFP4 ? 5 : 4; }
 
 constexpr int BUF_NT = 2;        // cache policy: nontemporal (weights are read once per call)
 
@@ -319,6 +322,10 @@ __device__ __forceinline__ WChunk<WF> load_wchunk(const Row<WF> &r, int ch) {
     c.b = __builtin_amdgcn_raw_buffer_load_b16(r.b, vo / 16 + (ch >> 1) * 2, so / 16, 0);
   } else if constexpr (WF == MXFP4) {
     c.s = __builtin_amdgcn_raw_buffer_load_b8(r.s, vo / 16 + ch, so / 16, 0);
+    c.b = 0u;
+  } else if constexpr (WF == NVFP4) {
+    // The two E4M3 block scales of the chunk (elements 0..15, then 16..31).
+    c.s = __builtin_amdgcn_raw_buffer_load_b16(r.s, vo / 8 + ch * 2, so / 8, 0);
     c.b = 0u;
   } else {
     c.s = c.b = 0u;
@@ -547,6 +554,74 @@ template <> struct XOps<MXFP4, F32> {
   }
 };
 
+// OCP FP8 E4M3 byte (bits 7..0 of b; no NaN allowed) to f32: sign bit 7,
+// exponent bits 6..3 with bias 7, mantissa bits 2..0, exponent 0 subnormal
+// (mantissa * 2^-9).  A normal value is the f32 with exponent field e + 120
+// and the mantissa in its top three bits.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t em = b & 0x7Fu;
+  const float v = em >= 8u ? __uint_as_float((em << 20) + (120u << 23)) : (float)em * 0x1p-9f;
+  return (b & 0x80u) ? -v : v;
+}
+
+// nvfp4 weights (E2M1 codes, an E4M3 scale per 16 elements) . bf16 x: sub-
+// step g is block g of the chunk (code dwords 2g, 2g + 1); its sum is taken
+// unscaled, then times the block's scale (low scale byte for block 0).  The
+// projection's second-level scale multiplies the row total outside.
+template <> struct XOps<NVFP4, BF16> {
+  static constexpr int SUB = 2, XS = 8;
+  struct X {
+    u32x4 a, b;      // x 16g .. 16g+7, 16g+8 .. 16g+15
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g, int) {
+      a = ld16(xrow + (size_t)ch * 64 + 32 * g);
+      b = ld16(xrow + (size_t)ch * 64 + 32 * g + 16);
+    }
+  };
+  static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
+  static __device__ __forceinline__ float start(float) { return 0.f; }
+  template <int SEL> static __device__ __forceinline__ uint32_t pk(uint32_t q) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, SEL));
+  }
+  static __device__ __forceinline__ float step(const WChunk<NVFP4> &w, const X &x, int g, float S) {
+    const uint32_t q0 = code_dword(w.q, 2 * g), q1 = code_dword(w.q, 2 * g + 1);
+    float t = dot2(pk<0>(q0), x.a.x, 0.f);
+    t = dot2(pk<1>(q0), x.a.y, t);
+    t = dot2(pk<2>(q0), x.a.z, t);
+    t = dot2(pk<3>(q0), x.a.w, t);
+    t = dot2(pk<0>(q1), x.b.x, t);
+    t = dot2(pk<1>(q1), x.b.y, t);
+    t = dot2(pk<2>(q1), x.b.z, t);
+    t = dot2(pk<3>(q1), x.b.w, t);
+    return __builtin_fmaf(t, e4m3_to_f32(g == 0 ? (w.s & 0xFFu) : (w.s >> 8) & 0xFFu), S);
+  }
+  static __device__ __forceinline__ float finish(const WChunk<NVFP4> &, float S, float, float acc) { return acc + S; }
+};
+
+// nvfp4 weights . f32 x.
+template <> struct XOps<NVFP4, F32> {
+  static constexpr int SUB = 4, XS = 8;
+  using X = XOps<MXFP4, F32>::X;
+  static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
+  static __device__ __forceinline__ float start(float) { return 0.f; }
+  static __device__ __forceinline__ float step(const WChunk<NVFP4> &w, const X &x, int g, float S) {
+    const uint32_t q = code_dword(w.q, g);
+    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+    float t = v0.x * __uint_as_float(x.a.x);
+    t = __builtin_fmaf(v0.y, __uint_as_float(x.a.y), t);
+    t = __builtin_fmaf(v1.x, __uint_as_float(x.a.z), t);
+    t = __builtin_fmaf(v1.y, __uint_as_float(x.a.w), t);
+    t = __builtin_fmaf(v2.x, __uint_as_float(x.b.x), t);
+    t = __builtin_fmaf(v2.y, __uint_as_float(x.b.y), t);
+    t = __builtin_fmaf(v3.x, __uint_as_float(x.b.z), t);
+    t = __builtin_fmaf(v3.y, __uint_as_float(x.b.w), t);
+    return __builtin_fmaf(t, e4m3_to_f32(g < 2 ? (w.s & 0xFFu) : (w.s >> 8) & 0xFFu), S);
+  }
+  static __device__ __forceinline__ float finish(const WChunk<NVFP4> &, float S, float, float acc) { return acc + S; }
+};
+
 // 4-bit weights . sub-step-major f32 x (the down input): the math of the
 // f32 case, sub-step g of chunk ch read at g * gs + ch * 32 bytes.
 template <> struct XOps<AFF4, F32P> : XOps<AFF4, F32> {
@@ -564,6 +639,9 @@ template <> struct XOps<MXFP4, F32P> : XOps<MXFP4, F32> {
       b = ld16(xrow + (size_t)g * gs + (size_t)ch * 32 + 16);
     }
   };
+};
+template <> struct XOps<NVFP4, F32P> : XOps<NVFP4, F32> {
+  using X = XOps<MXFP4, F32P>::X;
 };
 
 // ------------------------------------------------------ wave row x vector
@@ -747,7 +825,7 @@ __device__ __forceinline__ Mat<WF> make_mat(const void *w, const void *s, const 
   m.rb = row_bytes<WF>(K);
   m.w = buf_rsrc(w, N * m.rb);
   if constexpr (WF >= AFF4) {
-    m.s = buf_rsrc(s, N * m.rb / 16);
+    m.s = buf_rsrc(s, N * m.rb / (WF == NVFP4 ? 8 : 16));
     m.b = WF == AFF4 ? buf_rsrc(b, N * m.rb / 16) : m.s;
   } else {
     m.s = m.b = m.w;
@@ -1479,7 +1557,8 @@ template <int EF, int ACT, int CMAX, int NI>
 __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, const void *uw,
                                              const void *gs, const void *us, const void *gb,
                                              const void *ub, int N, int i0, int off, int np,
-                                             const int *pairs, const float *pw, float *dst, int ld) {
+                                             const int *pairs, const float *pw, float *dst, int ld,
+                                             float s2g = 1.0f, float s2u = 1.0f) {
   constexpr int RG = 2 * NI;
   const int H = a.H, k = a.K;
   const size_t xstride = (size_t)H * act_bytes(ACT);
@@ -1513,6 +1592,10 @@ __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, cons
         for (int t = 0; t < NI; ++t) {
           if (i0 + t < N) {
             float g = acc[t][c], v = acc[NI + t][c];
+            if constexpr (EF == NVFP4) {   // the projections' second-level scales
+              g *= s2g;
+              v *= s2u;
+            }
             if (scale) {  // W(w x) = w (W x): scale both pre-activations
               g *= w;
               v *= w;
@@ -1573,13 +1656,13 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   const int slot0 = clamp_i(wave / (DQ * a.down_parts) - sh, 0, a.cap - 1);
   // The fields a down sub-unit needs, of the wave's next routed sub-unit.
   struct DownRec {
-    int off, np;
+    int e, off, np;
     uint64_t dw, ds, db;
   };
   auto load_rec = [&](int slot) {
     const SlotRec &r = a.slots[slot];
     DownRec d;
-    d.off = r.off; d.np = r.np; d.dw = r.dw; d.ds = r.ds; d.db = r.db;
+    d.e = r.e; d.off = r.off; d.np = r.np; d.dw = r.dw; d.ds = r.ds; d.db = r.db;
     return d;
   };
   DownRec nxt = load_rec(slot0);
@@ -1617,6 +1700,8 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
       const void *ds = reinterpret_cast<const void *>(rec.ds);
       const void *db = reinterpret_cast<const void *>(rec.db);
       const int grp = lane / LPR;
+      float s2d = 1.0f;   // nvfp4: the down projection's second-level scale
+      if constexpr (EF == NVFP4) s2d = a.ds2[uniform_i(clamp_i(rec.e, 0, a.E - 1))];
       const Mat<EF> md = make_mat<EF>(dw, ds, db, H, I);
       Row<EF> rows[RGR];
 #pragma unroll
@@ -1633,7 +1718,8 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
           for (int t = 0; t < RGR; ++t)
 #pragma unroll
             for (int c = 0; c < C; ++c)
-              y_lds[(pt * te + off + c0 + c) * HT + q * DOWN_RD + grp + GR * t] = acc[t][c];
+              y_lds[(pt * te + off + c0 + c) * HT + q * DOWN_RD + grp + GR * t] =
+                  EF == NVFP4 ? acc[t][c] * s2d : acc[t][c];
         }
       });
     } else if (pt == 0) {
@@ -1886,8 +1972,13 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
           p[0] = tbl(a.gw, e); p[1] = tbl(a.uw, e); p[2] = tbl(a.gs, e);
           p[3] = tbl(a.us, e); p[4] = tbl(a.gb, e); p[5] = tbl(a.ub, e);
         }
+        float s2g = 1.0f, s2u = 1.0f;
+        if constexpr (EF == NVFP4) {
+          s2g = a.gs2[e];
+          s2u = a.us2[e];
+        }
         gate_up_rows<EF, ACT, CR, NI>(a, p[0], p[1], p[2], p[3], p[4], p[5], a.I, i0, off, np,
-                                      L.sorted + off, L.w, a.act, a.I);
+                                      L.sorted + off, L.w, a.act, a.I, s2g, s2u);
       }
     }
     return;
@@ -1909,11 +2000,18 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
     const int off = uniform_i(clamp_i(rec.off, 0, a.te));
     const int np = uniform_i(clamp_i(rec.np, 0, a.te - off));
     const int i0 = (b * WPB + wave) * NI;
-    if (i0 < a.I)
+    if (i0 < a.I) {
+      float s2g = 1.0f, s2u = 1.0f;
+      if constexpr (EF == NVFP4) {
+        const int e = uniform_i(clamp_i(rec.e, 0, a.E - 1));
+        s2g = a.gs2[e];
+        s2u = a.us2[e];
+      }
       gate_up_rows<EF, ACT, CR, NI>(a, reinterpret_cast<const void *>(rec.gw), reinterpret_cast<const void *>(rec.uw),
                                     reinterpret_cast<const void *>(rec.gs), reinterpret_cast<const void *>(rec.us),
                                     reinterpret_cast<const void *>(rec.gb), reinterpret_cast<const void *>(rec.ub),
-                                    a.I, i0, off, np, a.sorted_pair + off, a.topk_w, a.act, a.I);
+                                    a.I, i0, off, np, a.sorted_pair + off, a.topk_w, a.act, a.I, s2g, s2u);
+    }
   }
 }
 

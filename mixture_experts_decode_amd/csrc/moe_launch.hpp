@@ -60,6 +60,8 @@ const FormatKernels &kernels_bf16_f32();
 const FormatKernels &kernels_bf16_bf16();
 const FormatKernels &kernels_bf16_aff4();
 const FormatKernels &kernels_bf16_mxfp4();
+const FormatKernels &kernels_f32_nvfp4();
+const FormatKernels &kernels_bf16_nvfp4();
 
 #ifdef MOE_KERNELS_HPP_INCLUDED
 template <int EF, int ACT, int CR, int CS, int LPR>

@@ -80,7 +80,9 @@ class _Copy:
             down_s=p(self.tables.get("down_s")), gate_b=p(self.tables.get("gate_b")),
             up_b=p(self.tables.get("up_b")), down_b=p(self.tables.get("down_b")),
             sh_gate_w=p(tensors.get("sh_gate")), sh_up_w=p(tensors.get("sh_up")),
-            sh_down_w=p(tensors.get("sh_down")), sh_gate_vec=p(tensors.get("sh_gate_vec")))
+            sh_down_w=p(tensors.get("sh_down")), sh_gate_vec=p(tensors.get("sh_gate_vec")),
+            gate_scale2=p(tensors.get("gate_s2")), up_scale2=p(tensors.get("up_s2")),
+            down_scale2=p(tensors.get("down_s2")))
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in self.t.values() if t is not None)
@@ -114,6 +116,7 @@ class DeviceLayer:
             base[name] = to_device(proj.data, device)
             base[name + "_s"] = to_device(proj.scale, device)
             base[name + "_b"] = to_device(proj.bias, device)
+            base[name + "_s2"] = to_device(proj.scale2, device)
         self.copies = [_Copy(base, spec.num_experts, self.device)]
         for _ in range(copies - 1):
             cl = {k: (None if v is None else v.clone()) for k, v in base.items()}

@@ -21,8 +21,9 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWORKSPACE",
                 4: "MOE_EHIP"}
 # moe_format
-MOE_F32, MOE_BF16, MOE_AFF4_G64, MOE_MXFP4_B32 = range(4)
-FORMATS = {"f32": MOE_F32, "bf16": MOE_BF16, "aff4": MOE_AFF4_G64, "mxfp4": MOE_MXFP4_B32}
+MOE_F32, MOE_BF16, MOE_AFF4_G64, MOE_MXFP4_B32, MOE_NVFP4_B16 = range(5)
+FORMATS = {"f32": MOE_F32, "bf16": MOE_BF16, "aff4": MOE_AFF4_G64, "mxfp4": MOE_MXFP4_B32,
+           "nvfp4": MOE_NVFP4_B16}
 # moe_routing
 MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID_BIAS, MOE_ROUTE_SIGMOID_LOGIT = range(3)
 ROUTINGS = {"softmax": MOE_ROUTE_SOFTMAX, "sigmoid_bias": MOE_ROUTE_SIGMOID_BIAS,
@@ -51,7 +52,8 @@ class moe_decode_desc(C.Structure):
 class moe_decode_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "router_w", "expert_bias", "gate_w", "up_w", "down_w", "gate_s", "up_s", "down_s",
-        "gate_b", "up_b", "down_b", "sh_gate_w", "sh_up_w", "sh_down_w", "sh_gate_vec")]
+        "gate_b", "up_b", "down_b", "sh_gate_w", "sh_up_w", "sh_down_w", "sh_gate_vec",
+        "gate_scale2", "up_scale2", "down_scale2")]
 
 
 class moe_decode_ws_layout(C.Structure):

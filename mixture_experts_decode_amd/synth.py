@@ -90,8 +90,10 @@ class LayerSpec:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads: shapes and routing of real decode MoE layers, with
-# synthetic seeded weights.
+# The six workloads: shapes and routing of real decode MoE layers, with
+# synthetic seeded weights.  The nvfp4 one is the mxfp4 layer's shape with
+# the experts stored as NVFP4 (the format of the NVFP4 checkpoint of that
+# model family).
 WORKLOADS = {
     "tiny_f32": LayerSpec(
         name="tiny_f32", hidden=64, num_experts=8, top_k=2, inter=32,
@@ -108,6 +110,10 @@ WORKLOADS = {
     "qwen35_35b_a3b_mxfp4": LayerSpec(
         name="qwen35_35b_a3b_mxfp4", hidden=2048, num_experts=256, top_k=8, inter=512,
         shared_inter=512, act_fmt="bf16", expert_fmt="mxfp4", routing="softmax",
+        norm_topk=True, shared=True, shared_gated=True, rows=(1, 8, 16)),
+    "qwen35_35b_a3b_nvfp4": LayerSpec(
+        name="qwen35_35b_a3b_nvfp4", hidden=2048, num_experts=256, top_k=8, inter=512,
+        shared_inter=512, act_fmt="bf16", expert_fmt="nvfp4", routing="softmax",
         norm_topk=True, shared=True, shared_gated=True, rows=(1, 8, 16)),
     "llama4_wbf_bf16": LayerSpec(
         name="llama4_wbf_bf16", hidden=5120, num_experts=16, top_k=1, inter=8192,

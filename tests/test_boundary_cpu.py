@@ -167,6 +167,22 @@ def test_sigmoid_bias_needs_expert_bias():
         md.moe_decode_plan_destroy(plan)
 
 
+def test_nvfp4_needs_scales_and_second_level_scales():
+    plan, ws = md.moe_decode_plan(desc_of(synth.WORKLOADS["qwen35_35b_a3b_nvfp4"]))
+    try:
+        for field in ("gate_s", "down_s", "gate_scale2", "up_scale2", "down_scale2"):
+            w = _weights_stub()
+            setattr(w, field, None)
+            with pytest.raises(md.MoeDecodeError) as ei:
+                md.moe_decode_forward(plan, w, 4096, 1, 4096, None, None, 4096 * 256, ws, 0)
+            assert ei.value.status == md.MOE_EINVAL, field
+    finally:
+        md.moe_decode_plan_destroy(plan)
+    with pytest.raises(md.MoeDecodeError) as ei:
+        md.moe_decode_plan(_desc(expert_fmt=md.MOE_NVFP4_B16, hidden=2048 + 16))
+    assert ei.value.status == md.MOE_EUNSUPPORTED
+
+
 def test_single_launch_arrangement_is_refused(monkeypatch):
     # The persistent single-launch arrangement is switched off: asking for it
     # fails at plan time instead of launching it.

@@ -133,7 +133,8 @@ def test_workload_parity_all_rows(name):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["qwen3_30b_a3b_bf16", "qwen35_35b_a3b_mxfp4", "lfm2_8b_a1b_aff4",
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b_bf16", "qwen35_35b_a3b_mxfp4", "qwen35_35b_a3b_nvfp4",
+                                  "lfm2_8b_a1b_aff4",
                                   "llama4_wbf_bf16"])
 def test_workload_fp32_output_tight(name):
     spec = synth.WORKLOADS[name]
@@ -165,6 +166,9 @@ def small(**kw):
 _BASE = [(act, fmt, routing, before)
          for act in ("f32", "bf16") for fmt in ("f32", "bf16", "aff4", "mxfp4")
          for routing in ("softmax", "sigmoid_bias", "sigmoid_logit") for before in (False, True)]
+_BASE += [(act, "nvfp4", routing, before)
+          for act in ("f32", "bf16") for routing in ("softmax", "sigmoid_bias", "sigmoid_logit")
+          for before in (False, True)]
 VARIANTS = [b + (("none", "plain", "gated")[i % 3],) for i, b in enumerate(_BASE)]
 
 
@@ -233,7 +237,8 @@ def test_shared_expert_shapes(hidden, shared_inter):
 @pytest.mark.parametrize("fmt,inter", [("bf16", 64), ("bf16", 256), ("bf16", 768), ("bf16", 1024),
                                        ("mxfp4", 512), ("mxfp4", 1024), ("aff4", 1792),
                                        ("aff4", 128), ("f32", 32), ("bf16", 4096),
-                                       ("aff4", 8192), ("mxfp4", 4096)])
+                                       ("aff4", 8192), ("mxfp4", 4096), ("nvfp4", 96),
+                                       ("nvfp4", 512), ("nvfp4", 4096)])
 def test_down_lane_grouping(fmt, inter):
     spec = small(expert_fmt=fmt, inter=inter, hidden=512, num_experts=8, top_k=2,
                  act_fmt="f32" if fmt == "f32" else "bf16")
