@@ -29,6 +29,14 @@
  *   out[r]      = sum_j c_rj y_rj + gamma_r * shared(x_r), c = w or 1,
  *               gamma = sigmoid(x . w_g) (gated) or 1.
  *
+ * m = 1..32 is the fused decode path the page describes (three launches).
+ * m = 33..256 (prefill chunks, speculative-decoding verification) takes a
+ * grouped path of the same steps whose expert products run on the matrix
+ * cores (five launches); it needs bf16 activations, bf16 experts and H, I,
+ * Is multiples of 32, which moe_decode_plan checks when max_rows > 32.  Each
+ * path gives a row the same bits for every m it serves; the two paths agree
+ * within the tolerance of their accumulation orders.
+ *
  * Ownership: the caller owns every device buffer (weights, pointer tables,
  * x, out, idx/w outputs, workspace).  A plan owns host memory only; it is
  * immutable after moe_decode_plan and may be shared by threads and streams,
@@ -101,7 +109,7 @@ typedef struct {
   int32_t top_k;         /* k: 1..min(E, 16) */
   int32_t inter;         /* I: routed expert intermediate size, same multiples as H */
   int32_t shared_inter;  /* Is: shared expert intermediate (multiple of 8), 0 without MOE_SHARED */
-  int32_t max_rows;      /* largest m a forward will be given: 1..32 */
+  int32_t max_rows;      /* largest m a forward will be given: 1..256 (above 32: see the top) */
   int32_t act_fmt;       /* moe_format of x, out, router, shared expert, w_g: MOE_F32 or MOE_BF16 */
   int32_t expert_fmt;    /* moe_format of the routed experts: any */
   int32_t routing;       /* moe_routing */
@@ -159,8 +167,11 @@ typedef struct {
   size_t shared_act;      /* float [max_rows, Is] */
   size_t shared_y;        /* float [P, max_rows, H]: shared-expert output in P parts of Is
                              (matrix-core path; P = max(1, Is / 2048)) */
+  size_t routed_y;        /* float [te, H]: routed expert outputs per pair, sorted order
+                             (m > 32 only; a 4-byte placeholder when max_rows <= 32) */
   size_t sync;            /* uint32 [512]: reserved counters, zero between calls (word 0
-                             counts the router workgroups; the last arrival resets it) */
+                             counts the router workgroups, word 1 the top-k workgroups of
+                             the m > 32 path; the last arrival resets each) */
   size_t total;           /* bytes a workspace must have */
 } moe_decode_ws_layout;
 

@@ -168,8 +168,8 @@ moe_status check_desc(const moe_decode_desc &d) {
     return fail(MOE_EUNSUPPORTED, "num_experts %d > %d", d.num_experts, moe::MAX_EXPERTS);
   if (d.top_k > d.num_experts || d.top_k > moe::MAX_TOPK)
     return fail(MOE_EUNSUPPORTED, "top_k %d must be <= min(num_experts, %d)", d.top_k, moe::MAX_TOPK);
-  if (d.max_rows > moe::MAX_ROWS)
-    return fail(MOE_EUNSUPPORTED, "max_rows %d > %d", d.max_rows, moe::MAX_ROWS);
+  if (d.max_rows > moe::MAX_ROWS_G)
+    return fail(MOE_EUNSUPPORTED, "max_rows %d > %d", d.max_rows, moe::MAX_ROWS_G);
   if (d.hidden % 8 || d.inter % 8)
     return fail(MOE_EUNSUPPORTED, "hidden and inter must be multiples of 8");
   if (d.expert_fmt == MOE_AFF4_G64 && (d.hidden % 64 || d.inter % 64))
@@ -181,6 +181,14 @@ moe_status check_desc(const moe_decode_desc &d) {
   if (d.flags & MOE_SHARED) {
     if (d.shared_inter <= 0 || d.shared_inter % 8)
       return fail(MOE_EUNSUPPORTED, "shared_inter must be a positive multiple of 8");
+  }
+  if (d.max_rows > moe::MAX_ROWS) {
+    // The grouped path: bf16 matrix-core products over 32-wide k steps.
+    if (d.act_fmt != MOE_BF16 || !kernels_for(d.act_fmt, d.expert_fmt).gate_up_grouped)
+      return fail(MOE_EUNSUPPORTED, "max_rows above %d needs bf16 activations and bf16 experts", moe::MAX_ROWS);
+    if (d.hidden % 32 || d.inter % 32 || ((d.flags & MOE_SHARED) && d.shared_inter % 32))
+      return fail(MOE_EUNSUPPORTED, "max_rows above %d needs hidden, inter and shared_inter multiples of 32",
+                  moe::MAX_ROWS);
   }
   // Weight matrices are read through buffer resources with 32-bit byte
   // ranges: each projection (one expert's, or the shared expert's) must be
@@ -229,6 +237,7 @@ void layout_for(const moe_decode_desc &d, moe_decode_ws_layout *L) {
   L->act = take(te * (size_t)d.inter * 4);
   L->shared_act = take(R * Is * 4);
   L->shared_y = take(Is ? (size_t)shared_down_parts(d) * R * (size_t)d.hidden * 4 : 0);
+  L->routed_y = take(d.max_rows > moe::MAX_ROWS ? te * (size_t)d.hidden * 4 : 0);
   L->total = o;
 }
 
@@ -256,6 +265,41 @@ moe_status check_weights(const moe_decode_desc &d, const moe_decode_weights *w) 
   if ((d.flags & MOE_SHARED_GATED) && (!w->sh_gate_vec || !aligned(w->sh_gate_vec, 16)))
     return fail(MOE_EINVAL, "MOE_SHARED_GATED needs a 16-byte aligned sh_gate_vec");
   return MOE_OK;
+}
+
+// m > 32: router units, top-k with the sort, then the grouped gate/up and
+// down on the matrix cores and the blend (moe_kernels.hpp, grouped path).
+// The three timed stages are route (router + top-k/sort), gate_up, and
+// down_blend (down + blend).
+moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *stream, void *const *events) {
+  const moe_decode_desc &d = plan->d;
+  const moe::FormatKernels &k = kernels_for(d.act_fmt, d.expert_fmt);
+  const int m = a.m;
+  const bool shared = (d.flags & MOE_SHARED) != 0;
+  a.route_in_gu = 1;   // the route launch stops after the logits
+  a.n_router = (d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0)) * ((m + 7) / 8);
+  a.n_router_wg = (a.n_router + moe::ROUTE_UNITS_PER_WG - 1) / moe::ROUTE_UNITS_PER_WG;
+  a.n_shared_gu = 0;
+  a.shared_mfma = 0;
+  a.max_rows = d.max_rows;
+  a.sd_parts = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto ev = [&](int i) -> hipEvent_t { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
+  hipError_t e;
+  if ((e = moe::launch_route(d.act_fmt, 1, a, a.n_router_wg, s, ev(0), nullptr)) != hipSuccess)
+    return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
+  if ((e = moe::launch_topk_sort(a, (m + moe::ROUTE_WPB - 1) / moe::ROUTE_WPB, s, nullptr, ev(1))) != hipSuccess)
+    return fail(MOE_EHIP, "top-k launch: %s", hipGetErrorString(e));
+  const int gu_items = a.cap * ((d.inter + 15) / 16) + (shared ? (a.Is + 15) / 16 : 0);
+  if ((e = k.gate_up_grouped(a, gu_items, s, ev(2), ev(3))) != hipSuccess)
+    return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
+  const int dn_items = (a.cap + (shared ? 1 : 0)) * ((d.hidden + 15) / 16);
+  if ((e = k.down_grouped(a, dn_items, s, ev(4), nullptr)) != hipSuccess)
+    return fail(MOE_EHIP, "down launch: %s", hipGetErrorString(e));
+  const int bl_threads = m * (d.hidden / 4);
+  if ((e = moe::launch_blend_grouped(a, (bl_threads + 255) / 256, s, nullptr, ev(5))) != hipSuccess)
+    return fail(MOE_EHIP, "blend launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights *w, const void *x,
@@ -318,7 +362,9 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   a.act = reinterpret_cast<float *>(ws + L.act);
   a.sact = reinterpret_cast<float *>(ws + L.shared_act);
   a.sy = reinterpret_cast<float *>(ws + L.shared_y);
+  a.y = reinterpret_cast<float *>(ws + L.routed_y);
   a.sync = reinterpret_cast<unsigned *>(ws + L.sync);
+  if (m > moe::MAX_ROWS) return forward_grouped(plan, a, stream, events);
 
   const moe::Variant &kv = *plan->kv[m];
   const int cr = kv.cr, cs = kv.cs, lpr = kv.lpr;
@@ -413,7 +459,7 @@ moe_status moe_decode_plan(const moe_decode_desc *desc, moe_decode_plan_t **plan
     return fail(MOE_EUNSUPPORTED, "the single-launch arrangement is disabled");
   }
   p->variant = kSplit;
-  for (int m = 1; m <= p->d.max_rows; ++m) {
+  for (int m = 1; m <= p->d.max_rows && m <= moe::MAX_ROWS; ++m) {
     if (!pick_variant(p->d, m, &p->kv[m], &p->gate_up[m], &p->gate_up_shd[m])) {
       delete p;
       return fail(MOE_EUNSUPPORTED, "no kernel variant for m = %d", m);

@@ -62,6 +62,15 @@ constexpr int MAX_DOWN_TILE = 2 * DOWN_RD;
 // last one resets it, so it is zero between calls.  Nothing ever waits on it.
 constexpr int SYNC_WORDS = 512;
 constexpr int SYNC_ROUTER_TICKET = 0;
+constexpr int SYNC_TOPK_TICKET = 1;     // grouped path: top-k workgroups (reset by the last arrival)
+// Grouped path (33 <= m <= MAX_ROWS_G): one routing per row on one wave,
+// then the experts' products on the matrix cores, G_COLS pairs per pass.
+constexpr int MAX_ROWS_G = 256;
+constexpr int G_THREADS = 512;
+constexpr int G_WPB = G_THREADS / WAVE;
+constexpr int G_NCT = 2;                // column tiles of 16 pairs per pass
+constexpr int G_COLS = 16 * G_NCT;
+constexpr int G_MU = 2;                 // k steps of 32 per staged batch (registers: two workgroups per CU)
 
 // Rows of intermediate per gate/up wave: 2 for 16-byte-per-8-or-4 element
 // formats; 4 for the 4-bit ones (their rows are 4x shorter) with one vector
@@ -121,6 +130,7 @@ struct Args {
   float *act;              // [te, I]
   float *sact;             // [m, Is]
   float *sy;               // [m, H]: shared-expert output (matrix-core path)
+  float *y;                // [te, H]: grouped path, routed down output per pair in sorted order
   unsigned *sync;          // [SYNC_WORDS]
 };
 
@@ -895,10 +905,12 @@ constexpr int MF_U = 4;                  // k-steps of 32 per batch
 constexpr int MF_ROW = MF_U * 64 + 16;   // bytes per staged row (16 bytes of padding)
 constexpr int MF_STAGE = 16 * MF_ROW;    // staged bytes per matrix per wave
 
+// xv[ct]: where this lane's vector of column tile ct (vector 16 ct + l % 16)
+// starts, plus the lane's k offset (l / 16) * 8 elements.
 template <int XF, int NA, int NCT, int MU = MF_U>
-__device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA], int rb, int n0, int N,
-                                           const char *x, size_t xstride, int nv, int kb, int ke,
-                                           char *stage, f32x4 (&acc)[NA][NCT]) {
+__device__ __forceinline__ void mfma_slice_v(const __amdgpu_buffer_rsrc_t (&A)[NA], int rb, int n0, int N,
+                                             const char *const (&xv)[NCT], int kb, int ke, char *stage,
+                                             f32x4 (&acc)[NA][NCT]) {
   constexpr int ROW = MU * 64 + 16, STAGE = 16 * ROW;   // staging layout of MU k-steps
   static_assert(MU <= MF_U, "the wave's staging region holds MF_U k-steps");
   constexpr int XB = XF == F32 ? 4 : 2;
@@ -913,9 +925,6 @@ __device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA]
   int loff[MU];
 #pragma unroll
   for (int i = 0; i < MU; ++i) loff[i] = min(n0 + RI * i + lrow, N - 1) * rb + lcol * 16;
-  const char *xv[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) xv[ct] = x + (size_t)min(16 * ct + rr, nv - 1) * xstride + (size_t)g * 8 * XB;
 #pragma unroll
   for (int j = 0; j < NA; ++j)
 #pragma unroll
@@ -990,6 +999,19 @@ __device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA]
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
+}
+
+// Vectors at x + v * xstride, v < nv (vectors past nv repeat the last one).
+template <int XF, int NA, int NCT, int MU = MF_U>
+__device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA], int rb, int n0, int N,
+                                           const char *x, size_t xstride, int nv, int kb, int ke,
+                                           char *stage, f32x4 (&acc)[NA][NCT]) {
+  constexpr int XB = XF == F32 ? 4 : 2;
+  const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
+  const char *xv[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) xv[ct] = x + (size_t)min(16 * ct + rr, nv - 1) * xstride + (size_t)g * 8 * XB;
+  mfma_slice_v<XF, NA, NCT, MU>(A, rb, n0, N, xv, kb, ke, stage, acc);
 }
 
 // The k range of wave w when nw waves split K (a multiple of 32) evenly.
@@ -2019,6 +2041,291 @@ __global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
 template <int EF, int ACT, int CR, int CS, int LPR>
 __global__ __launch_bounds__(DOWN_THREADS) void down_blend_kernel(Args a) {
   down_item<EF, ACT, CR, CS, LPR>(a, blockIdx.x);
+}
+
+
+// ================================================== grouped path (m > 32)
+//
+// For 33..MAX_ROWS_G rows the pairs per active expert are many enough that
+// the experts' products are small GEMMs: five launches on the caller's stream.
+//   route_kernel         the router units only (the logits)
+//   topk_sort_kernel     one row per wave: top-k and weights; the workgroup
+//                        that takes the last ticket sorts the pairs by expert
+//   gate_up_grouped      item = (active slot, 16 intermediate rows) or a
+//                        shared-expert row tile: gate on waves 0..3, up on
+//                        waves 4..7, each a quarter of H, on the matrix cores,
+//                        G_COLS of the expert's pairs per pass
+//   down_grouped         item = (active slot, 16 output columns) or a shared
+//                        tile: the eight waves split K; y per pair to HBM
+//   blend_grouped        out[r] = sum_j c_rj y[perm(r, j)] + gamma_r ys[r]
+// The (row, vector) sums are accumulated in an order fixed by the layer's
+// shapes, so a row's result does not depend on m within this path.
+
+// Stable counting sort of the te pairs in one workgroup: bit r of
+// rows[e][r / 32] is set when row r selected expert e; a pair's position is
+// its expert's offset plus the number of earlier rows that selected it.
+struct SortLDS {
+  uint32_t rows[MAX_EXPERTS][MAX_ROWS_G / 32];
+  int off[MAX_EXPERTS + 1];
+  int slot[MAX_EXPERTS];
+  int wtot[2][ROUTE_WPB];
+};
+
+template <int ACT>
+__global__ __launch_bounds__(ROUTE_THREADS) void topk_sort_kernel(Args a) {
+  __shared__ union {
+    TopkLDS tk[ROUTE_WPB];
+    SortLDS s;
+  } sm;
+  __shared__ unsigned s_ticket;
+  const int wave = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int E = a.E, k = a.K, m = a.m, te = m * k;
+  const int r = (int)blockIdx.x * ROUTE_WPB + wave;
+  if (r < m) {
+    int e;
+    double w;
+    row_topk(a, r, sm.tk[wave], e, w);
+    if (lane < k) {
+      const float wf = (float)(w * (double)a.rsf);
+      const int p = r * k + lane;
+      a.topk_idx[p] = e;
+      a.topk_w[p] = wf;
+      if (a.idx_out) a.idx_out[p] = e;
+      if (a.w_out) a.w_out[p] = wf;
+    }
+    if (lane == 0 && (a.flags & SHARED_GATED))
+      a.row_gate[r] = (float)sigmoid_d(load_coherent(a.logits + (size_t)r * (E + 1) + E));
+  }
+  // Release this workgroup's selections, then take a ticket; only the
+  // workgroup that takes the last one goes on (nobody waits).
+  __threadfence();
+  __syncthreads();
+  if (tid == 0)
+    s_ticket = __hip_atomic_fetch_add(a.sync + SYNC_TOPK_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_ticket != gridDim.x - 1) return;
+  __threadfence();   // acquire: every other workgroup's selections
+  SortLDS &S = sm.s;
+  constexpr int RW = MAX_ROWS_G / 32;
+  for (int i = tid; i < MAX_EXPERTS * RW; i += ROUTE_THREADS) (&S.rows[0][0])[i] = 0u;
+  __syncthreads();
+  for (int p = tid; p < te; p += ROUTE_THREADS) {
+    const int e = clamp_i(a.topk_idx[p], 0, E - 1), rr = p / k;
+    atomicOr(&S.rows[e][rr >> 5], 1u << (rr & 31));
+  }
+  __syncthreads();
+  // Exclusive scans over the experts of the pair counts and of the active
+  // flags: waves 0..3 take 64 experts each.
+  int cnt = 0, pre_c = 0, pre_a = 0;
+  if (wave < 4) {
+    const int e = wave * WAVE + lane;
+    if (e < E) {
+#pragma unroll
+      for (int j = 0; j < RW; ++j) cnt += __popc(S.rows[e][j]);
+    }
+    int tc, ta;
+    pre_c = wave_excl_scan<9>((unsigned)cnt, &tc);
+    pre_a = wave_excl_scan<1>(cnt > 0 ? 1u : 0u, &ta);
+    if (lane == 0) {
+      S.wtot[0][wave] = tc;
+      S.wtot[1][wave] = ta;
+    }
+  }
+  __syncthreads();
+  if (wave < 4) {
+    const int e = wave * WAVE + lane;
+    for (int w2 = 0; w2 < wave; ++w2) {
+      pre_c += S.wtot[0][w2];
+      pre_a += S.wtot[1][w2];
+    }
+    if (e < E) {
+      S.off[e] = pre_c;
+      S.slot[e] = pre_a;
+      a.offsets[e] = pre_c;
+      if (cnt > 0) a.active[pre_a] = e;
+      if (e == E - 1) {
+        S.off[E] = pre_c + cnt;
+        a.offsets[E] = pre_c + cnt;
+        a.active_count[0] = pre_a + (cnt > 0 ? 1 : 0);
+      }
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < te; p += ROUTE_THREADS) {
+    const int e = clamp_i(a.topk_idx[p], 0, E - 1), rr = p / k;
+    int before = __popc(S.rows[e][rr >> 5] & ((1u << (rr & 31)) - 1u));
+    for (int j = 0; j < (rr >> 5); ++j) before += __popc(S.rows[e][j]);
+    const int pos = S.off[e] + before;
+    a.sorted_pair[pos] = p;
+    a.pair_to_perm[p] = pos;
+  }
+  if (tid == 0) a.sync[SYNC_TOPK_TICKET] = 0u;   // every ticket is taken
+}
+
+// The expert's pair range and weights of gate/up or down item `item` of a
+// routed slot, or of the shared expert past the routed items.
+struct GroupedItem {
+  bool live, routed;
+  int e, off, np, n0;
+};
+
+__device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int tiles) {
+  GroupedItem g;
+  const int nrout = a.cap * tiles;
+  if (item < nrout) {
+    const int s = item / tiles;
+    const int nact = clamp_i(a.active_count[0], 0, a.cap);
+    g.live = s < nact;
+    g.routed = true;
+    g.e = uniform_i(clamp_i(a.active[min(s, a.cap - 1)], 0, a.E - 1));
+    g.off = uniform_i(clamp_i(a.offsets[g.e], 0, a.te));
+    g.np = uniform_i(clamp_i(a.offsets[g.e + 1], g.off, a.te)) - g.off;
+    g.n0 = (item - s * tiles) * 16;
+  } else {
+    g.live = (a.flags & SHARED) != 0;
+    g.routed = false;
+    g.e = 0;
+    g.off = 0;
+    g.np = a.m;
+    g.n0 = (item - nrout) * 16;
+  }
+  return g;
+}
+
+// Gate/up: item = 16 intermediate rows of one active expert (or of the
+// shared expert); writes silu(g) * v per pair (act, sorted order) or per row
+// (sact).  Experts: bf16.
+template <int EF>
+__global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
+  static_assert(EF == BF16, "matrix-core experts: bf16");
+  static_assert(G_WPB == 8, "gate and up take four waves each");
+  __shared__ MfmaLDS<G_WPB, 1, G_MU> S;
+  const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int H = a.H, k = a.K;
+  const GroupedItem it = grouped_item(a, blockIdx.x, (a.I + 15) / 16);
+  if (!it.live) return;
+  const int N = it.routed ? a.I : a.Is;
+  const void *mat = it.routed ? tbl(w < 4 ? a.gw : a.uw, it.e) : (w < 4 ? a.sgw : a.suw);
+  const __amdgpu_buffer_rsrc_t A[1] = {buf_rsrc(mat, N * H * 2)};
+  int kb, ke;
+  k_slice(H, w & 3, 4, kb, ke);
+  const bool before = it.routed && (a.flags & WEIGHT_BEFORE);
+  const char *x = reinterpret_cast<const char *>(a.x);
+  const int g4 = lane >> 4, rr = lane & 15;
+  for (int c0 = 0; c0 < it.np; c0 += G_COLS) {
+    const int nv = min(G_COLS, it.np - c0);
+    const char *xv[G_NCT];
+#pragma unroll
+    for (int ct = 0; ct < G_NCT; ++ct) {
+      const int v = c0 + min(16 * ct + rr, nv - 1);
+      const int row = it.routed ? min(clamp_i(a.sorted_pair[it.off + v], 0, a.te - 1) / k, a.m - 1) : v;
+      xv[ct] = x + (size_t)row * H * 2 + (size_t)g4 * 16;
+    }
+    f32x4 acc[1][G_NCT];
+    mfma_slice_v<BF16, 1, G_NCT, G_MU>(A, H * 2, it.n0, N, xv, kb, ke, S.stage[w], acc);
+#pragma unroll
+    for (int ct = 0; ct < G_NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S.part[w][0][ct][i][lane] = acc[0][ct][i];
+    __syncthreads();
+    // Wave w finishes (column tile w / 4, element i = w % 4).
+    const int ct = w / 4, i = w % 4;
+    float gs = 0.f, us = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      gs += S.part[p][0][ct][i][lane];
+      us += S.part[4 + p][0][ct][i][lane];
+    }
+    const int row = it.n0 + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
+    if (row < N && v < nv) {
+      if (it.routed) {
+        if (before) {   // W(w x) = w (W x)
+          const float wt = a.topk_w[clamp_i(a.sorted_pair[it.off + c0 + v], 0, a.te - 1)];
+          gs *= wt;
+          us *= wt;
+        }
+        a.act[(size_t)(it.off + c0 + v) * a.I + row] = silu_mul(gs, us);
+      } else {
+        a.sact[(size_t)(c0 + v) * a.Is + row] = silu_mul(gs, us);
+      }
+    }
+    __syncthreads();   // the partials are reused by the next pass
+  }
+}
+
+// Down: item = 16 output columns of one active expert (or of the shared
+// expert); the eight waves split K; y per pair (sorted order) or ys per row.
+template <int EF>
+__global__ __launch_bounds__(G_THREADS) void down_grouped_kernel(Args a) {
+  static_assert(EF == BF16, "matrix-core experts: bf16");
+  __shared__ MfmaLDS<G_WPB, 1, G_MU> S;
+  const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int H = a.H;
+  const GroupedItem it = grouped_item(a, blockIdx.x, (H + 15) / 16);
+  if (!it.live) return;
+  const int K = it.routed ? a.I : a.Is;
+  const void *mat = it.routed ? tbl(a.dw, it.e) : a.sdw;
+  const __amdgpu_buffer_rsrc_t A[1] = {buf_rsrc(mat, H * K * 2)};
+  int kb, ke;
+  k_slice(K, w, G_WPB, kb, ke);
+  const char *xb = reinterpret_cast<const char *>(it.routed ? a.act + (size_t)it.off * K : a.sact);
+  float *dst = it.routed ? a.y + (size_t)it.off * H : a.sy;
+  for (int c0 = 0; c0 < it.np; c0 += G_COLS) {
+    const int nv = min(G_COLS, it.np - c0);
+    f32x4 acc[1][G_NCT];
+    mfma_slice<F32, 1, G_NCT, G_MU>(A, K * 2, it.n0, H, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
+                                    S.stage[w], acc);
+#pragma unroll
+    for (int ct = 0; ct < G_NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S.part[w][0][ct][i][lane] = acc[0][ct][i];
+    __syncthreads();
+    const int ct = w / 4, i = w % 4;
+    float t = 0.f;
+#pragma unroll
+    for (int p = 0; p < G_WPB; ++p) t += S.part[p][0][ct][i][lane];
+    const int row = it.n0 + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
+    if (row < H && v < nv) dst[(size_t)(c0 + v) * H + row] = t;
+    __syncthreads();
+  }
+}
+
+// Blend: thread = (row r, 4 output columns); slots in order, then the shared
+// term.
+template <int ACT>
+__global__ __launch_bounds__(256) void blend_grouped_kernel(Args a) {
+  const int H = a.H, k = a.K, q = H / 4;
+  const int t = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  const int r = t / q, h = (t - r * q) * 4;
+  if (r >= a.m) return;
+  const bool before = (a.flags & WEIGHT_BEFORE) != 0;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int p = r * k + j;
+    const float c = before ? 1.0f : a.topk_w[p];
+    const int pos = clamp_i(a.pair_to_perm[p], 0, a.te - 1);
+    const u32x4 y = ld16(a.y + (size_t)pos * H + h);
+    o[0] = __builtin_fmaf(c, __uint_as_float(y.x), o[0]);
+    o[1] = __builtin_fmaf(c, __uint_as_float(y.y), o[1]);
+    o[2] = __builtin_fmaf(c, __uint_as_float(y.z), o[2]);
+    o[3] = __builtin_fmaf(c, __uint_as_float(y.w), o[3]);
+  }
+  if (a.flags & SHARED) {
+    const float gm = (a.flags & SHARED_GATED) ? a.row_gate[r] : 1.0f;
+    const u32x4 ys = ld16(a.sy + (size_t)r * H + h);
+    o[0] = __builtin_fmaf(gm, __uint_as_float(ys.x), o[0]);
+    o[1] = __builtin_fmaf(gm, __uint_as_float(ys.y), o[1]);
+    o[2] = __builtin_fmaf(gm, __uint_as_float(ys.z), o[2]);
+    o[3] = __builtin_fmaf(gm, __uint_as_float(ys.w), o[3]);
+  }
+  if ((a.flags & OUT_F32) || ACT == F32) {
+    *reinterpret_cast<u32x4 *>(reinterpret_cast<float *>(a.out) + (size_t)r * H + h) =
+        u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+  } else {
+    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + (size_t)r * H + h) =
+        u32x2{(uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16),
+              (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16)};
+  }
 }
 
 }  // namespace moe

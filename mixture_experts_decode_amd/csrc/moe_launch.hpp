@@ -43,12 +43,17 @@ struct FormatKernels {
   int nv;
   const GateUpVariant *g;
   int ng;
+  launch_fn gate_up_grouped;   // m > 32 (matrix cores), or null where not served
+  launch_fn down_grouped;
 };
 
 // First launch: router items plus the shared expert's gate/up items.
 hipError_t launch_route(int act, int cs, const Args &a, int blocks, hipStream_t st, hipEvent_t start,
                         hipEvent_t stop);
 hipError_t launch_clear_sync(unsigned *sync, int n, hipStream_t st);
+// Grouped path (m > 32): top-k with the sort, and the blend.
+hipError_t launch_topk_sort(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop);
+hipError_t launch_blend_grouped(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_bench_copy(const void *src, void *dst, size_t bytes, hipStream_t st);
 hipError_t launch_bench_read(const void *src, size_t bytes, unsigned *sink, hipStream_t st);
 
@@ -67,6 +72,14 @@ const FormatKernels &kernels_bf16_nvfp4();
 template <int EF, int ACT, int CR, int CS, int LPR>
 hipError_t launch_down_blend_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   return launch_timed(down_blend_kernel<EF, ACT, CR, CS, LPR>, blocks, DOWN_THREADS, st, start, stop, a);
+}
+template <int EF>
+hipError_t launch_gate_up_grouped_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  return launch_timed(gate_up_grouped_kernel<EF>, blocks, G_THREADS, st, start, stop, a);
+}
+template <int EF>
+hipError_t launch_down_grouped_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  return launch_timed(down_grouped_kernel<EF>, blocks, G_THREADS, st, start, stop, a);
 }
 template <int EF, int ACT, int CR, int CS, int SHD>
 hipError_t launch_gate_up_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
@@ -90,6 +103,14 @@ constexpr launch_fn gate_up_shd_fn() {
 #define MOE_TABLE(NAME)                                                            \
   const FormatKernels &kernels_##NAME() {                                          \
     static const FormatKernels k{kV, (int)(sizeof kV / sizeof kV[0]), kG,         \
-                                 (int)(sizeof kG / sizeof kG[0])};                 \
+                                 (int)(sizeof kG / sizeof kG[0]), nullptr, nullptr}; \
+    return k;                                                                      \
+  }
+// The same with the grouped (m > 32) kernels of the unit's expert format.
+#define MOE_TABLE_GROUPED(NAME)                                                    \
+  const FormatKernels &kernels_##NAME() {                                          \
+    static const FormatKernels k{kV, (int)(sizeof kV / sizeof kV[0]), kG,         \
+                                 (int)(sizeof kG / sizeof kG[0]),                  \
+                                 &launch_gate_up_grouped_t<EFT>, &launch_down_grouped_t<EFT>}; \
     return k;                                                                      \
   }

@@ -27,6 +27,14 @@ hipError_t launch_route(int act, int cs, const Args &a, int blocks, hipStream_t 
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_topk_sort(const Args &a, int blocks, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
+  return launch_timed(topk_sort_kernel<BF16>, blocks, ROUTE_THREADS, st, t0, t1, a);
+}
+
+hipError_t launch_blend_grouped(const Args &a, int blocks, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
+  return launch_timed(blend_grouped_kernel<BF16>, blocks, 256, st, t0, t1, a);
+}
+
 hipError_t launch_clear_sync(unsigned *sync, int n, hipStream_t st) {
   hipLaunchKernelGGL(clear_sync_kernel, dim3(1), dim3(256), 0, st, sync, n);
   return hipGetLastError();

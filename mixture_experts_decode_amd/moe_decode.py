@@ -59,8 +59,8 @@ class moe_decode_weights(C.Structure):
 class moe_decode_ws_layout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in (
         "logits", "topk_idx", "topk_w", "row_gate", "sorted_pair", "expert_offsets",
-        "pair_to_perm", "active_experts", "active_count", "slot_info", "act", "shared_act", "shared_y", "sync",
-        "total")]
+        "pair_to_perm", "active_experts", "active_count", "slot_info", "act", "shared_act", "shared_y",
+        "routed_y", "sync", "total")]
 
 
 _lib = None

@@ -38,7 +38,7 @@ def _desc(**kw):
     ("num_experts", 257, md.MOE_EUNSUPPORTED),
     ("top_k", 17, md.MOE_EUNSUPPORTED),
     ("top_k", 0, md.MOE_EINVAL),
-    ("max_rows", 33, md.MOE_EUNSUPPORTED),
+    ("max_rows", 257, md.MOE_EUNSUPPORTED),
     ("max_rows", 0, md.MOE_EINVAL),
     ("act_fmt", md.MOE_AFF4_G64, md.MOE_EINVAL),
     ("expert_fmt", 7, md.MOE_EINVAL),
@@ -69,7 +69,28 @@ def test_plan_rejects_4bit_shapes():
 
 @pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
 def test_plan_and_layout_for_every_workload(name):
-    spec = synth.WORKLOADS[name]
+    _check_plan_and_layout(synth.WORKLOADS[name])
+
+
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b_bf16", "llama4_wbf_bf16"])
+def test_plan_and_layout_grouped_rows(name):
+    _check_plan_and_layout(synth.WORKLOADS[name].replace(rows=(256,)))
+
+
+def test_grouped_rows_limits():
+    for kw in (dict(act_fmt=md.MOE_F32, expert_fmt=md.MOE_F32), dict(expert_fmt=md.MOE_AFF4_G64),
+               dict(expert_fmt=md.MOE_MXFP4_B32), dict(hidden=2048 + 16), dict(inter=768 + 8)):
+        with pytest.raises(md.MoeDecodeError) as ei:
+            md.moe_decode_plan(_desc(max_rows=64, **kw))
+        assert ei.value.status == md.MOE_EUNSUPPORTED, kw
+    with pytest.raises(md.MoeDecodeError) as ei:
+        md.moe_decode_plan(_desc(max_rows=257))
+    assert ei.value.status == md.MOE_EUNSUPPORTED
+    plan, ws = md.moe_decode_plan(_desc(max_rows=256))
+    md.moe_decode_plan_destroy(plan)
+
+
+def _check_plan_and_layout(spec):
     plan, ws = md.moe_decode_plan(desc_of(spec))
     try:
         L = md.moe_decode_workspace_layout(plan)
@@ -83,7 +104,8 @@ def test_plan_and_layout_for_every_workload(name):
                   (L.act, te * spec.inter * 4),
                   (L.shared_act, spec.max_rows * (spec.shared_inter if spec.shared else 0) * 4),
                   (L.shared_y, max(1, spec.shared_inter // 2048) * spec.max_rows
-                   * (spec.hidden if spec.shared else 0) * 4)]
+                   * (spec.hidden if spec.shared else 0) * 4),
+                  (L.routed_y, te * spec.hidden * 4 if spec.max_rows > 32 else 0)]
         spans = sorted((o, o + max(n, 1)) for o, n in fields)
         for (a0, a1), (b0, _) in zip(spans, spans[1:]):
             assert a1 <= b0, "workspace arrays overlap"

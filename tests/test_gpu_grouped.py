@@ -1,0 +1,86 @@
+"""GPU parity of the grouped path (33 <= m <= 256 rows: matrix-core expert
+products) against the oracle, through the C ABI.
+
+Same bar as the fused decode path: expert indices equal bit for bit, weights
+to 1e-6 relative, outputs within tol * rms(oracle) (2e-2 with bf16 output,
+1e-4 with f32 output); the sort arrays equal the oracle's sort; and a row's
+result is bitwise the same for every m the path serves.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_decode_amd import synth
+from mixture_experts_decode_amd.device import DeviceLayer
+from tests.test_gpu_parity import TOL, TOL_OUT_F32, check, check_sort, run, say, small
+
+pytestmark = pytest.mark.gpu
+
+
+def grouped_rows(dl, layer, x, rows, what, out_f32=False):
+    spec = layer.spec
+    ref = oracle.forward(layer, x[:max(rows)])
+    outs = {}
+    for m in rows:
+        say(f"[gpu] grouped {what} m={m}")
+        got, idx, w = run(dl, x, m)
+        check(spec, got, idx, w, ref, m, TOL_OUT_F32 if out_f32 else TOL["bf16"], f"{what} m={m}")
+        check_sort(dl, m, idx, records=m <= 32)
+        outs[m] = got
+    mmax = max(m for m in rows if m > 32)
+    for m in rows:
+        if m > 32:
+            assert np.array_equal(outs[m], outs[mmax][:m]), f"{what}: rows differ between m={m} and m={mmax}"
+    return outs
+
+
+_GV = [(routing, before) for routing in ("softmax", "sigmoid_bias", "sigmoid_logit")
+       for before in (False, True)]
+G_VARIANTS = [v + (("none", "plain", "gated")[i % 3],) for i, v in enumerate(_GV)]
+
+
+@pytest.mark.parametrize("routing,before,shared", G_VARIANTS)
+def test_grouped_small_variant(routing, before, shared):
+    spec = small(hidden=256, num_experts=12, top_k=3, inter=192, shared_inter=160, routing=routing,
+                 weight_before_ffn=before, norm_topk=routing != "sigmoid_logit", routed_scaling_factor=1.25,
+                 shared=shared != "none", shared_gated=shared == "gated", rows=(256,))
+    seed = G_VARIANTS.index((routing, before, shared)) + 300
+    layer = synth.make_layer(spec, seed=seed, threads=4)
+    x = layer.x(0)
+    what = f"{routing}/before={before}/shared={shared}"
+    for out_f32 in (False, True):
+        dl = DeviceLayer(layer, out_f32=out_f32)
+        grouped_rows(dl, layer, x, (33, 64, 200, 256, 8), what + f" f32out={out_f32}", out_f32)
+        del dl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("E,k,inter,hidden", [(256, 16, 64, 128), (2, 1, 96, 160), (4, 4, 128, 64),
+                                              (1, 1, 64, 96)])
+def test_grouped_pair_extremes(E, k, inter, hidden):
+    # 4096 pairs over every expert; one or two experts holding all rows (the
+    # longest runs of passes); k = E (every row on every expert).
+    spec = small(hidden=hidden, num_experts=E, top_k=k, inter=inter, shared=True, shared_gated=True,
+                 shared_inter=96, rows=(256,), w_std=0.1)
+    layer = synth.make_layer(spec, seed=E * 100 + k)
+    x = layer.x(0)
+    dl = DeviceLayer(layer)
+    grouped_rows(dl, layer, x, (256, 97, 33), f"E={E} k={k}")
+    del dl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,rows", [("qwen3_30b_a3b_bf16", (256, 128, 64, 33)),
+                                       ("llama4_wbf_bf16", (64, 48))])
+def test_grouped_workload(name, rows):
+    spec = synth.WORKLOADS[name].replace(rows=(max(rows),))
+    say(f"[gpu] grouped workload {name}: generating")
+    layer = synth.make_layer(spec, seed=2)
+    x = layer.x(1)
+    dl = DeviceLayer(layer)
+    grouped_rows(dl, layer, x, rows, name)
+    dl32 = DeviceLayer(layer, out_f32=True)
+    grouped_rows(dl32, layer, x, (max(rows),), name + " f32out", out_f32=True)
+    del dl, dl32
+    torch.cuda.empty_cache()
