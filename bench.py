@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--all", action="store_true", help="one line per workload and m (analysis)")
+    p.add_argument("--grouped-rows", default="",
+                   help="with --all: comma list of m > 32 (the grouped path) for the bf16 workloads")
     return p.parse_args()
 
 
@@ -115,7 +117,8 @@ def copies_for(layer, m: int) -> int:
 
 # ------------------------------------------------------------------ timing
 
-def time_workload(name: str, m: int, steps: int, warmup: int, extra_rows=(), want_stages=True):
+def time_workload(name: str, m: int, steps: int, warmup: int, extra_rows=(), want_stages=True,
+                  max_rows=None):
     import numpy as np
     import torch
 
@@ -124,6 +127,8 @@ def time_workload(name: str, m: int, steps: int, warmup: int, extra_rows=(), wan
     from mixture_experts_decode_amd.device import DeviceLayer, to_device
 
     spec = synth.WORKLOADS[name]
+    if max_rows:
+        spec = spec.replace(rows=(max_rows,))
     layer = synth.make_layer(spec, seed=0)
     rows_all = [m] + [r for r in extra_rows if r != m and r <= spec.max_rows]
     R = max(copies_for(layer, r) for r in rows_all)
@@ -297,6 +302,17 @@ def main():
     if args.all:
         for name, spec in synth.WORKLOADS.items():
             layer, res = time_workload(name, spec.rows[0], args.steps, args.warmup, spec.rows[1:])
+            for mm, r in res.items():
+                print(json.dumps({"workload": name, "m": mm, **{k: (round(v, 3) if isinstance(v, float) else v)
+                                                               for k, v in r.items()}}), flush=True)
+            del layer
+            torch.cuda.empty_cache()
+        grows = [int(v) for v in args.grouped_rows.split(",") if v]
+        for name, spec in synth.WORKLOADS.items():
+            if not grows or spec.act_fmt != "bf16" or spec.expert_fmt != "bf16":
+                continue
+            layer, res = time_workload(name, grows[0], args.steps, args.warmup, grows[1:],
+                                       max_rows=max(grows))
             for mm, r in res.items():
                 print(json.dumps({"workload": name, "m": mm, **{k: (round(v, 3) if isinstance(v, float) else v)
                                                                for k, v in r.items()}}), flush=True)

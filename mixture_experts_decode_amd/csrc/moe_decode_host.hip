@@ -293,7 +293,12 @@ moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *st
   const int gu_items = a.cap * ((d.inter + 15) / 16) + (shared ? (a.Is + 15) / 16 : 0);
   if ((e = k.gate_up_grouped(a, gu_items, s, ev(2), ev(3))) != hipSuccess)
     return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
-  const int dn_items = (a.cap + (shared ? 1 : 0)) * ((d.hidden + 15) / 16);
+  // Down items: rows of at most 2048 (k split 8 ways: 8 k steps or fewer
+  // per wave) take four tiles per item, k split two ways; longer rows keep
+  // one tile per item, k split eight ways.
+  const int kmax = d.inter > a.Is ? d.inter : a.Is;
+  a.g_dt = kmax <= 2048 ? 4 : 1;
+  const int dn_items = (a.cap + (shared ? 1 : 0)) * ((d.hidden + 16 * a.g_dt - 1) / (16 * a.g_dt));
   if ((e = k.down_grouped(a, dn_items, s, ev(4), nullptr)) != hipSuccess)
     return fail(MOE_EHIP, "down launch: %s", hipGetErrorString(e));
   const int bl_threads = m * (d.hidden / 4);

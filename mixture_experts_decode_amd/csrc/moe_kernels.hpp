@@ -131,6 +131,7 @@ struct Args {
   float *sact;             // [m, Is]
   float *sy;               // [m, H]: shared-expert output (matrix-core path)
   float *y;                // [te, H]: grouped path, routed down output per pair in sorted order
+  int g_dt;                // grouped path: 16-column tiles per down item (1, 2 or 4)
   unsigned *sync;          // [SYNC_WORDS]
 };
 
@@ -2253,39 +2254,45 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
   }
 }
 
-// Down: item = 16 output columns of one active expert (or of the shared
-// expert); the eight waves split K; y per pair (sorted order) or ys per row.
+// Down: item = a.g_dt tiles of 16 output columns of one active expert (or
+// of the shared expert); wave w takes tile w % dt over part w / dt of K
+// (G_WPB / dt parts, added in part order); y per pair (sorted order) or ys
+// per row.  dt (1, 2 or 4) is fixed per layer: short rows take several tiles
+// per item so that each wave streams a longer run of k.
 template <int EF>
 __global__ __launch_bounds__(G_THREADS) void down_grouped_kernel(Args a) {
   static_assert(EF == BF16, "matrix-core experts: bf16");
   __shared__ MfmaLDS<G_WPB, 1, G_MU> S;
   const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int H = a.H;
-  const GroupedItem it = grouped_item(a, blockIdx.x, (H + 15) / 16);
+  const int H = a.H, dt = a.g_dt, KP = G_WPB / dt;
+  const GroupedItem it = grouped_item(a, blockIdx.x, (H + 16 * dt - 1) / (16 * dt));
   if (!it.live) return;
   const int K = it.routed ? a.I : a.Is;
   const void *mat = it.routed ? tbl(a.dw, it.e) : a.sdw;
   const __amdgpu_buffer_rsrc_t A[1] = {buf_rsrc(mat, H * K * 2)};
+  const int n0 = it.n0 * dt + 16 * (w % dt);   // this wave's 16 rows
   int kb, ke;
-  k_slice(K, w, G_WPB, kb, ke);
+  k_slice(K, w / dt, KP, kb, ke);
   const char *xb = reinterpret_cast<const char *>(it.routed ? a.act + (size_t)it.off * K : a.sact);
   float *dst = it.routed ? a.y + (size_t)it.off * H : a.sy;
   for (int c0 = 0; c0 < it.np; c0 += G_COLS) {
     const int nv = min(G_COLS, it.np - c0);
     f32x4 acc[1][G_NCT];
-    mfma_slice<F32, 1, G_NCT, G_MU>(A, K * 2, it.n0, H, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
+    mfma_slice<F32, 1, G_NCT, G_MU>(A, K * 2, n0, H, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
                                     S.stage[w], acc);
 #pragma unroll
     for (int ct = 0; ct < G_NCT; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) S.part[w][0][ct][i][lane] = acc[0][ct][i];
     __syncthreads();
-    const int ct = w / 4, i = w % 4;
-    float t = 0.f;
-#pragma unroll
-    for (int p = 0; p < G_WPB; ++p) t += S.part[p][0][ct][i][lane];
-    const int row = it.n0 + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
-    if (row < H && v < nv) dst[(size_t)(c0 + v) * H + row] = t;
+    // (tile t, column tile ct, element i) combinations, G_WPB at a time.
+    for (int c = w; c < dt * G_NCT * 4; c += G_WPB) {
+      const int t = c / (G_NCT * 4), ct = (c / 4) % G_NCT, i = c % 4;
+      float sum = 0.f;
+      for (int p = 0; p < KP; ++p) sum += S.part[p * dt + t][0][ct][i][lane];
+      const int row = it.n0 * dt + 16 * t + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
+      if (row < H && v < nv) dst[(size_t)(c0 + v) * H + row] = sum;
+    }
     __syncthreads();
   }
 }
