@@ -293,13 +293,16 @@ moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *st
   const int gu_items = a.cap * ((d.inter + 15) / 16) + (shared ? (a.Is + 15) / 16 : 0);
   if ((e = k.gate_up_grouped(a, gu_items, s, ev(2), ev(3))) != hipSuccess)
     return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
-  // Down items: rows of at most 2048 (k split 8 ways: 8 k steps or fewer
-  // per wave) take four tiles per item, k split two ways; longer rows keep
-  // one tile per item, k split eight ways.
+  // Down rows of at most 2048: items of 64 columns on four waves that each
+  // take all four tiles over a quarter of K (an input fragment serves four
+  // tiles); longer rows: items of 16 columns on eight waves, an eighth of K
+  // each.
   const int kmax = d.inter > a.Is ? d.inter : a.Is;
-  a.g_dt = kmax <= 2048 ? 4 : 1;
-  const int dn_items = (a.cap + (shared ? 1 : 0)) * ((d.hidden + 16 * a.g_dt - 1) / (16 * a.g_dt));
-  if ((e = k.down_grouped(a, dn_items, s, ev(4), nullptr)) != hipSuccess)
+  const bool wide = kmax <= 2048;
+  const moe::launch_fn dn = wide ? k.down_grouped : k.down_grouped_long;
+  const int cols = wide ? 16 * moe::G_DT : 16;
+  const int dn_items = (a.cap + (shared ? 1 : 0)) * ((d.hidden + cols - 1) / cols);
+  if ((e = dn(a, dn_items, s, ev(4), nullptr)) != hipSuccess)
     return fail(MOE_EHIP, "down launch: %s", hipGetErrorString(e));
   const int bl_threads = m * (d.hidden / 4);
   if ((e = moe::launch_blend_grouped(a, (bl_threads + 255) / 256, s, nullptr, ev(5))) != hipSuccess)

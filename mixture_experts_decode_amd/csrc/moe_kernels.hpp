@@ -131,7 +131,6 @@ struct Args {
   float *sact;             // [m, Is]
   float *sy;               // [m, H]: shared-expert output (matrix-core path)
   float *y;                // [te, H]: grouped path, routed down output per pair in sorted order
-  int g_dt;                // grouped path: 16-column tiles per down item (1, 2 or 4)
   unsigned *sync;          // [SYNC_WORDS]
 };
 
@@ -2053,11 +2052,12 @@ __global__ __launch_bounds__(DOWN_THREADS) void down_blend_kernel(Args a) {
 //   topk_sort_kernel     one row per wave: top-k and weights; the workgroup
 //                        that takes the last ticket sorts the pairs by expert
 //   gate_up_grouped      item = (active slot, 16 intermediate rows) or a
-//                        shared-expert row tile: gate on waves 0..3, up on
-//                        waves 4..7, each a quarter of H, on the matrix cores,
-//                        G_COLS of the expert's pairs per pass
-//   down_grouped         item = (active slot, 16 output columns) or a shared
-//                        tile: the eight waves split K; y per pair to HBM
+//                        shared-expert row tile: each wave both matrices over
+//                        an eighth of H, on the matrix cores, G_COLS of the
+//                        expert's pairs per pass
+//   down_grouped         item = (active slot, 16 to 64 output columns) or a
+//                        shared tile: the waves split the tiles and K; y per
+//                        pair to HBM
 //   blend_grouped        out[r] = sum_j c_rj y[perm(r, j)] + gamma_r ys[r]
 // The (row, vector) sums are accumulated in an order fixed by the layer's
 // shapes, so a row's result does not depend on m within this path.
@@ -2194,22 +2194,24 @@ __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int
 }
 
 // Gate/up: item = 16 intermediate rows of one active expert (or of the
-// shared expert); writes silu(g) * v per pair (act, sorted order) or per row
-// (sact).  Experts: bf16.
+// shared expert); every wave takes both matrices over one eighth of H, so a
+// pair's input fragment serves the gate and the up products; the eight
+// partials are added in wave order.  Writes silu(g) * v per pair (act,
+// sorted order) or per row (sact).  Experts: bf16.
 template <int EF>
 __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
   static_assert(EF == BF16, "matrix-core experts: bf16");
-  static_assert(G_WPB == 8, "gate and up take four waves each");
-  __shared__ MfmaLDS<G_WPB, 1, G_MU> S;
+  __shared__ MfmaLDS<G_WPB, 2, G_MU> S;
   const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int H = a.H, k = a.K;
   const GroupedItem it = grouped_item(a, blockIdx.x, (a.I + 15) / 16);
   if (!it.live) return;
   const int N = it.routed ? a.I : a.Is;
-  const void *mat = it.routed ? tbl(w < 4 ? a.gw : a.uw, it.e) : (w < 4 ? a.sgw : a.suw);
-  const __amdgpu_buffer_rsrc_t A[1] = {buf_rsrc(mat, N * H * 2)};
+  const void *mg = it.routed ? tbl(a.gw, it.e) : a.sgw;
+  const void *mu = it.routed ? tbl(a.uw, it.e) : a.suw;
+  const __amdgpu_buffer_rsrc_t A[2] = {buf_rsrc(mg, N * H * 2), buf_rsrc(mu, N * H * 2)};
   int kb, ke;
-  k_slice(H, w & 3, 4, kb, ke);
+  k_slice(H, w, G_WPB, kb, ke);
   const bool before = it.routed && (a.flags & WEIGHT_BEFORE);
   const char *x = reinterpret_cast<const char *>(a.x);
   const int g4 = lane >> 4, rr = lane & 15;
@@ -2222,20 +2224,22 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
       const int row = it.routed ? min(clamp_i(a.sorted_pair[it.off + v], 0, a.te - 1) / k, a.m - 1) : v;
       xv[ct] = x + (size_t)row * H * 2 + (size_t)g4 * 16;
     }
-    f32x4 acc[1][G_NCT];
-    mfma_slice_v<BF16, 1, G_NCT, G_MU>(A, H * 2, it.n0, N, xv, kb, ke, S.stage[w], acc);
+    f32x4 acc[2][G_NCT];
+    mfma_slice_v<BF16, 2, G_NCT, G_MU>(A, H * 2, it.n0, N, xv, kb, ke, S.stage[w], acc);
 #pragma unroll
-    for (int ct = 0; ct < G_NCT; ++ct)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S.part[w][0][ct][i][lane] = acc[0][ct][i];
+      for (int ct = 0; ct < G_NCT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S.part[w][j][ct][i][lane] = acc[j][ct][i];
     __syncthreads();
     // Wave w finishes (column tile w / 4, element i = w % 4).
     const int ct = w / 4, i = w % 4;
     float gs = 0.f, us = 0.f;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < G_WPB; ++p) {
       gs += S.part[p][0][ct][i][lane];
-      us += S.part[4 + p][0][ct][i][lane];
+      us += S.part[p][1][ct][i][lane];
     }
     const int row = it.n0 + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
     if (row < N && v < nv) {
@@ -2254,43 +2258,64 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
   }
 }
 
-// Down: item = a.g_dt tiles of 16 output columns of one active expert (or
-// of the shared expert); wave w takes tile w % dt over part w / dt of K
-// (G_WPB / dt parts, added in part order); y per pair (sorted order) or ys
-// per row.  dt (1, 2 or 4) is fixed per layer: short rows take several tiles
-// per item so that each wave streams a longer run of k.
-template <int EF>
-__global__ __launch_bounds__(G_THREADS) void down_grouped_kernel(Args a) {
+// Down: y per pair (sorted order) or ys per row, for one active expert (or
+// the shared expert):
+//   WIDE (rows of at most 2048): item = G_DT tiles of 16 output columns on
+//     four waves, each all the tiles over a quarter of K, so one input
+//     fragment serves G_DT tiles;
+//   else: item = one tile on eight waves, each an eighth of K (a long run
+//     of k per wave).
+// The parts of K are added in part order.
+constexpr int G_DT = 4;
+template <bool WIDE> constexpr int down_grouped_threads() { return WIDE ? 256 : G_THREADS; }
+template <bool WIDE> constexpr int down_grouped_cols() { return WIDE ? 16 * G_DT : 16; }
+template <int EF, bool WIDE>
+__global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Args a) {
   static_assert(EF == BF16, "matrix-core experts: bf16");
-  __shared__ MfmaLDS<G_WPB, 1, G_MU> S;
+  static_assert(down_grouped_threads<true>() == 256, "the launch bound above");
+  constexpr int NW = down_grouped_threads<WIDE>() / WAVE;   // waves = parts of K
+  constexpr int NA = WIDE ? G_DT : 1;                        // tiles per wave
+  constexpr int MU = WIDE ? 1 : G_MU;
+  constexpr int COLS = down_grouped_cols<WIDE>();
+  __shared__ MfmaLDS<NW, NA, MU> S;
   const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int H = a.H, dt = a.g_dt, KP = G_WPB / dt;
-  const GroupedItem it = grouped_item(a, blockIdx.x, (H + 16 * dt - 1) / (16 * dt));
+  const int H = a.H;
+  const GroupedItem it = grouped_item(a, blockIdx.x, (H + COLS - 1) / COLS);
   if (!it.live) return;
   const int K = it.routed ? a.I : a.Is;
-  const void *mat = it.routed ? tbl(a.dw, it.e) : a.sdw;
-  const __amdgpu_buffer_rsrc_t A[1] = {buf_rsrc(mat, H * K * 2)};
-  const int n0 = it.n0 * dt + 16 * (w % dt);   // this wave's 16 rows
+  const char *mat = reinterpret_cast<const char *>(it.routed ? tbl(a.dw, it.e) : a.sdw);
+  const int h0 = it.n0 / 16 * COLS;   // the item's first column
+  // One resource per tile, bounded to the tile's rows (a tile past H reads
+  // nothing).
+  __amdgpu_buffer_rsrc_t A[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int r0 = h0 + 16 * j;
+    A[j] = buf_rsrc(mat + (size_t)min(r0, H) * K * 2, max(0, min(16, H - r0)) * K * 2);
+  }
   int kb, ke;
-  k_slice(K, w / dt, KP, kb, ke);
+  k_slice(K, w, NW, kb, ke);
   const char *xb = reinterpret_cast<const char *>(it.routed ? a.act + (size_t)it.off * K : a.sact);
   float *dst = it.routed ? a.y + (size_t)it.off * H : a.sy;
   for (int c0 = 0; c0 < it.np; c0 += G_COLS) {
     const int nv = min(G_COLS, it.np - c0);
-    f32x4 acc[1][G_NCT];
-    mfma_slice<F32, 1, G_NCT, G_MU>(A, K * 2, n0, H, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
-                                    S.stage[w], acc);
+    f32x4 acc[NA][G_NCT];
+    mfma_slice<F32, NA, G_NCT, MU>(A, K * 2, 0, 16, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
+                                   S.stage[w], acc);
 #pragma unroll
-    for (int ct = 0; ct < G_NCT; ++ct)
+    for (int j = 0; j < NA; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S.part[w][0][ct][i][lane] = acc[0][ct][i];
+      for (int ct = 0; ct < G_NCT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S.part[w][j][ct][i][lane] = acc[j][ct][i];
     __syncthreads();
-    // (tile t, column tile ct, element i) combinations, G_WPB at a time.
-    for (int c = w; c < dt * G_NCT * 4; c += G_WPB) {
+    // (tile t, column tile ct, element i) combinations, NW at a time.
+    for (int c = w; c < NA * G_NCT * 4; c += NW) {
       const int t = c / (G_NCT * 4), ct = (c / 4) % G_NCT, i = c % 4;
       float sum = 0.f;
-      for (int p = 0; p < KP; ++p) sum += S.part[p * dt + t][0][ct][i][lane];
-      const int row = it.n0 * dt + 16 * t + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
+#pragma unroll
+      for (int p = 0; p < NW; ++p) sum += S.part[p][t][ct][i][lane];
+      const int row = h0 + 16 * t + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
       if (row < H && v < nv) dst[(size_t)(c0 + v) * H + row] = sum;
     }
     __syncthreads();

@@ -44,7 +44,8 @@ struct FormatKernels {
   const GateUpVariant *g;
   int ng;
   launch_fn gate_up_grouped;   // m > 32 (matrix cores), or null where not served
-  launch_fn down_grouped;
+  launch_fn down_grouped;      // down rows of at most 2048
+  launch_fn down_grouped_long; // longer down rows
 };
 
 // First launch: router items plus the shared expert's gate/up items.
@@ -77,9 +78,9 @@ template <int EF>
 hipError_t launch_gate_up_grouped_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   return launch_timed(gate_up_grouped_kernel<EF>, blocks, G_THREADS, st, start, stop, a);
 }
-template <int EF>
+template <int EF, bool WIDE>
 hipError_t launch_down_grouped_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  return launch_timed(down_grouped_kernel<EF>, blocks, G_THREADS, st, start, stop, a);
+  return launch_timed(down_grouped_kernel<EF, WIDE>, blocks, down_grouped_threads<WIDE>(), st, start, stop, a);
 }
 template <int EF, int ACT, int CR, int CS, int SHD>
 hipError_t launch_gate_up_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
@@ -103,7 +104,7 @@ constexpr launch_fn gate_up_shd_fn() {
 #define MOE_TABLE(NAME)                                                            \
   const FormatKernels &kernels_##NAME() {                                          \
     static const FormatKernels k{kV, (int)(sizeof kV / sizeof kV[0]), kG,         \
-                                 (int)(sizeof kG / sizeof kG[0]), nullptr, nullptr}; \
+                                 (int)(sizeof kG / sizeof kG[0]), nullptr, nullptr, nullptr}; \
     return k;                                                                      \
   }
 // The same with the grouped (m > 32) kernels of the unit's expert format.
@@ -111,6 +112,7 @@ constexpr launch_fn gate_up_shd_fn() {
   const FormatKernels &kernels_##NAME() {                                          \
     static const FormatKernels k{kV, (int)(sizeof kV / sizeof kV[0]), kG,         \
                                  (int)(sizeof kG / sizeof kG[0]),                  \
-                                 &launch_gate_up_grouped_t<EFT>, &launch_down_grouped_t<EFT>}; \
+                                 &launch_gate_up_grouped_t<EFT>, &launch_down_grouped_t<EFT, true>, \
+                                 &launch_down_grouped_t<EFT, false>};                \
     return k;                                                                      \
   }
