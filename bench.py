@@ -322,7 +322,10 @@ def main():
 
     extra = [int(v) for v in args.extra_rows.split(",") if v]
     spec = synth.WORKLOADS[args.workload]
-    layer, res = time_workload(args.workload, args.rows, args.steps, args.warmup, extra)
+    # Row counts above the workload's own take the grouped path (m > 32).
+    big = max([args.rows] + extra)
+    layer, res = time_workload(args.workload, args.rows, args.steps, args.warmup, extra,
+                               max_rows=big if big > spec.max_rows else None)
     head = res[args.rows]
     sol = stream_read_gbps()
     read_gbps = sol["read"]

@@ -921,6 +921,10 @@ __device__ __forceinline__ void mfma_slice_v(const __amdgpu_buffer_rsrc_t (&A)[N
   // instruction), bytes (l % LR) * 16 .. + 16 of the batch.
   constexpr int LR = 4 * MU, RI = 16 / MU;
   static_assert(MU == 1 || MU == 2 || MU == 4, "16 rows split evenly over the loads");
+  // Nontemporal loads bring whole 128-byte lines that are not kept: with
+  // 64 bytes per row per batch (MU = 1) the next batch's half would be
+  // fetched from HBM again, so those loads keep the default policy.
+  constexpr int POL = MU >= 2 ? BUF_NT : 0;
   const int lrow = l / LR, lcol = l % LR;
   int loff[MU];
 #pragma unroll
@@ -936,7 +940,7 @@ __device__ __forceinline__ void mfma_slice_v(const __amdgpu_buffer_rsrc_t (&A)[N
 #pragma unroll
     for (int j = 0; j < NA; ++j)
 #pragma unroll
-      for (int i = 0; i < MU; ++i) nxt[j][i] = __builtin_amdgcn_raw_buffer_load_b128(A[j], loff[i] + kq * 2, 0, BUF_NT);
+      for (int i = 0; i < MU; ++i) nxt[j][i] = __builtin_amdgcn_raw_buffer_load_b128(A[j], loff[i] + kq * 2, 0, POL);
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
       const int kk = min(kq + 32 * u, ke - 32);
