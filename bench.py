@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--all", action="store_true", help="one line per workload and m (analysis)")
     p.add_argument("--grouped-rows", default="",
-                   help="with --all: comma list of m > 32 (the grouped path) for the bf16 workloads")
+                   help="with --all: comma list of m > 32 (the grouped path) for the workloads it serves")
     return p.parse_args()
 
 
@@ -309,7 +309,7 @@ def main():
             torch.cuda.empty_cache()
         grows = [int(v) for v in args.grouped_rows.split(",") if v]
         for name, spec in synth.WORKLOADS.items():
-            if not grows or spec.act_fmt != "bf16" or spec.expert_fmt != "bf16":
+            if not grows or spec.act_fmt != "bf16" or spec.expert_fmt not in ("bf16", "mxfp4", "nvfp4"):
                 continue
             layer, res = time_workload(name, grows[0], args.steps, args.warmup, grows[1:],
                                        max_rows=max(grows))

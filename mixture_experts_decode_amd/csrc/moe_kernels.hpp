@@ -1018,6 +1018,167 @@ __device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA]
   mfma_slice_v<XF, NA, NCT, MU>(A, rb, n0, N, xv, kb, ke, stage, acc);
 }
 
+// 4-bit weights (MXFP4, NVFP4) on the matrix cores.  The loader brings a
+// batch of MU k steps of 16 rows as codes -- 16 bytes, one k step of one row,
+// per lane; lanes from 16 MU on load nothing -- with their block scales,
+// dequantises them to bf16 and stages them in the layout mfma_slice_v reads.
+// Both decodings are exact in bf16: E2M1 times a power of two (E8M0), and
+// E2M1 times E4M3 (at most 6 significant bits).  The NVFP4 second-level
+// scale is left to the caller.
+template <int WF> struct QMat {
+  __amdgpu_buffer_rsrc_t w, s;   // codes [N, K/2], scale bytes [N, K/32] or [N, K/16]
+};
+
+template <int WF>
+__device__ __forceinline__ QMat<WF> make_qmat(const void *w, const void *s, int N, int K) {
+  QMat<WF> m;
+  m.w = buf_rsrc(w, N * (K / 2));
+  m.s = buf_rsrc(s, N * (K / (WF == NVFP4 ? 16 : 32)));
+  return m;
+}
+
+// 32 codes of one row (code dword d: elements 8d .. 8d+7, low nibble first)
+// with their scale bits -> 32 bf16 values, o[d] = elements 8d .. 8d+7.
+template <int WF>
+__device__ __forceinline__ void dequant32(const u32x4 &q, uint32_t s, u32x4 (&o)[4]) {
+  float sc[2];
+  if constexpr (WF == MXFP4) {
+    sc[0] = sc[1] = e8m0_to_f32(s & 0xFFu);
+  } else {
+    sc[0] = e4m3_to_f32(s & 0xFFu);
+    sc[1] = e4m3_to_f32((s >> 8) & 0xFFu);
+  }
+  uint32_t pr[4][4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t qd = code_dword(q, d);
+    const float c = sc[d >> 1];
+    f32x2 v[4];
+    v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 0);
+    v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 1);
+    v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 2);
+    v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 3);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // The products are bf16 values: their low 16 bits are zero.
+      const uint32_t a = __float_as_uint(v[t].x * c), b = __float_as_uint(v[t].y * c);
+      pr[d][t] = (a >> 16) | (b & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = u32x4{pr[d][0], pr[d][1], pr[d][2], pr[d][3]};
+}
+
+// mfma_slice_v with 4-bit weights A[j] (K = the matrices' row length).
+template <int WF, int XF, int NA, int NCT, int MU>
+__device__ __forceinline__ void mfma_slice_q(const QMat<WF> (&A)[NA], int K, int n0, int N,
+                                             const char *const (&xv)[NCT], int kb, int ke, char *stage,
+                                             f32x4 (&acc)[NA][NCT]) {
+  constexpr int ROW = MU * 64 + 16, STAGE = 16 * ROW;
+  static_assert(MU <= MF_U, "the wave's staging region holds MF_U k-steps");
+  static_assert(WF == MXFP4 || WF == NVFP4, "4-bit formats");
+  constexpr int XB = XF == F32 ? 4 : 2;
+  constexpr int XL = XF == F32 ? 2 : 1;
+  const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
+  const bool loader = l < 16 * MU;
+  const int qrow = min(n0 + l / MU, N - 1), qk = l % MU;   // this lane's row and k step
+  const int qoff = qrow * (K / 2) + qk * 16;
+  const int soff = WF == NVFP4 ? qrow * (K / 16) + qk * 2 : qrow * (K / 32) + qk;
+#pragma unroll
+  for (int j = 0; j < NA; ++j)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (kb >= ke) return;
+  u32x4 nq[NA], nxb[MU][NCT][XL];
+  uint32_t ns[NA];
+  auto fetch = [&](int kq) {
+    if (loader) {
+#pragma unroll
+      for (int j = 0; j < NA; ++j) {
+        // Row batches of 16 MU bytes: the default policy keeps the rest of
+        // each line for the following batches.
+        nq[j] = __builtin_amdgcn_raw_buffer_load_b128(A[j].w, qoff + kq / 2, 0, 0);
+        if constexpr (WF == NVFP4)
+          ns[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].s, soff + kq / 16, 0, 0);
+        else
+          ns[j] = __builtin_amdgcn_raw_buffer_load_b8(A[j].s, soff + kq / 32, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int kk = min(kq + 32 * u, ke - 32);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int h = 0; h < XL; ++h) nxb[u][ct][h] = ld16(xv[ct] + (size_t)kk * XB + 16 * h);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    nq[j] = u32x4{0u, 0u, 0u, 0u};
+    ns[j] = 0u;
+  }
+  fetch(kb);
+  for (int k0 = kb; k0 < ke; k0 += 32 * MU) {
+    u32x4 cq[NA], bv[MU][NCT][XL];
+    uint32_t cs[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      cq[j] = nq[j];
+      cs[j] = ns[j];
+    }
+#pragma unroll
+    for (int u = 0; u < MU; ++u)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int h = 0; h < XL; ++h) bv[u][ct][h] = nxb[u][ct][h];
+    const int k1 = k0 + 32 * MU;
+    if (k1 < ke) fetch(k1);
+    if (loader) {
+#pragma unroll
+      for (int j = 0; j < NA; ++j) {
+        u32x4 o[4];
+        dequant32<WF>(cq[j], cs[j], o);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          *reinterpret_cast<u32x4 *>(stage + j * STAGE + (l / MU) * ROW + qk * 64 + 16 * t) = o[t];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      if (k0 + 32 * u < ke) {
+        u32x4 av[NA];
+#pragma unroll
+        for (int j = 0; j < NA; ++j)
+          av[j] = *reinterpret_cast<const u32x4 *>(stage + j * STAGE + rr * ROW + u * 64 + g * 16);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          if constexpr (XF == BF16) {
+            const bf16x8 bb = __builtin_bit_cast(bf16x8, bv[u][ct][0]);
+#pragma unroll
+            for (int j = 0; j < NA; ++j) acc[j][ct] = mfma16(av[j], bb, acc[j][ct]);
+          } else {
+            bf16x8 hi, lo;
+            split_bf16(bv[u][ct][0], bv[u][ct][XL - 1], hi, lo);
+#pragma unroll
+            for (int j = 0; j < NA; ++j) {
+              acc[j][ct] = mfma16(av[j], hi, acc[j][ct]);
+              acc[j][ct] = mfma16(av[j], lo, acc[j][ct]);
+            }
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // The k range of wave w when nw waves split K (a multiple of 32) evenly.
 __device__ __forceinline__ void k_slice(int K, int w, int nw, int &kb, int &ke) {
   const int steps = K / 32, per = (steps + nw - 1) / nw;
@@ -2204,7 +2365,7 @@ __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int
 // sorted order) or per row (sact).  Experts: bf16.
 template <int EF>
 __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
-  static_assert(EF == BF16, "matrix-core experts: bf16");
+  static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4, "matrix-core experts: bf16, mxfp4, nvfp4");
   __shared__ MfmaLDS<G_WPB, 2, G_MU> S;
   const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int H = a.H, k = a.K;
@@ -2213,7 +2374,24 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
   const int N = it.routed ? a.I : a.Is;
   const void *mg = it.routed ? tbl(a.gw, it.e) : a.sgw;
   const void *mu = it.routed ? tbl(a.uw, it.e) : a.suw;
-  const __amdgpu_buffer_rsrc_t A[2] = {buf_rsrc(mg, N * H * 2), buf_rsrc(mu, N * H * 2)};
+  // bf16 rows (the shared expert's always): one resource per matrix.
+  __amdgpu_buffer_rsrc_t A[2];
+  QMat<EF == BF16 ? MXFP4 : EF> Q[2];
+  const bool quant = EF != BF16 && it.routed;
+  if (quant) {
+    Q[0] = make_qmat<EF == BF16 ? MXFP4 : EF>(mg, tbl(a.gs, it.e), N, H);
+    Q[1] = make_qmat<EF == BF16 ? MXFP4 : EF>(mu, tbl(a.us, it.e), N, H);
+  } else {
+    A[0] = buf_rsrc(mg, N * H * 2);
+    A[1] = buf_rsrc(mu, N * H * 2);
+  }
+  float s2g = 1.0f, s2u = 1.0f;   // nvfp4: the projections' second-level scales
+  if constexpr (EF == NVFP4) {
+    if (it.routed) {
+      s2g = a.gs2[it.e];
+      s2u = a.us2[it.e];
+    }
+  }
   int kb, ke;
   k_slice(H, w, G_WPB, kb, ke);
   const bool before = it.routed && (a.flags & WEIGHT_BEFORE);
@@ -2229,7 +2407,14 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
       xv[ct] = x + (size_t)row * H * 2 + (size_t)g4 * 16;
     }
     f32x4 acc[2][G_NCT];
-    mfma_slice_v<BF16, 2, G_NCT, G_MU>(A, H * 2, it.n0, N, xv, kb, ke, S.stage[w], acc);
+    if constexpr (EF != BF16) {
+      if (quant)
+        mfma_slice_q<EF, BF16, 2, G_NCT, G_MU>(Q, H, it.n0, N, xv, kb, ke, S.stage[w], acc);
+      else
+        mfma_slice_v<BF16, 2, G_NCT, G_MU>(A, H * 2, it.n0, N, xv, kb, ke, S.stage[w], acc);
+    } else {
+      mfma_slice_v<BF16, 2, G_NCT, G_MU>(A, H * 2, it.n0, N, xv, kb, ke, S.stage[w], acc);
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -2245,6 +2430,8 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
       gs += S.part[p][0][ct][i][lane];
       us += S.part[p][1][ct][i][lane];
     }
+    gs *= s2g;
+    us *= s2u;
     const int row = it.n0 + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
     if (row < N && v < nv) {
       if (it.routed) {
@@ -2275,7 +2462,8 @@ template <bool WIDE> constexpr int down_grouped_threads() { return WIDE ? 256 : 
 template <bool WIDE> constexpr int down_grouped_cols() { return WIDE ? 16 * G_DT : 16; }
 template <int EF, bool WIDE>
 __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Args a) {
-  static_assert(EF == BF16, "matrix-core experts: bf16");
+  static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4, "matrix-core experts: bf16, mxfp4, nvfp4");
+  constexpr int QF = EF == BF16 ? MXFP4 : EF;                  // the 4-bit loader's format
   static_assert(down_grouped_threads<true>() == 256, "the launch bound above");
   constexpr int NW = down_grouped_threads<WIDE>() / WAVE;   // waves = parts of K
   constexpr int NA = WIDE ? G_DT : 1;                        // tiles per wave
@@ -2292,10 +2480,25 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
   // One resource per tile, bounded to the tile's rows (a tile past H reads
   // nothing).
   __amdgpu_buffer_rsrc_t A[NA];
+  QMat<QF> Q[NA];
+  const bool quant = EF != BF16 && it.routed;
+  float s2d = 1.0f;   // nvfp4: the down projection's second-level scale
+  if (quant) {
+    const char *smat = reinterpret_cast<const char *>(tbl(a.ds, it.e));
+    constexpr int SB = QF == NVFP4 ? 16 : 32;   // elements per scale byte
 #pragma unroll
-  for (int j = 0; j < NA; ++j) {
-    const int r0 = h0 + 16 * j;
-    A[j] = buf_rsrc(mat + (size_t)min(r0, H) * K * 2, max(0, min(16, H - r0)) * K * 2);
+    for (int j = 0; j < NA; ++j) {
+      const int r0 = h0 + 16 * j, nr = max(0, min(16, H - r0));
+      Q[j].w = buf_rsrc(mat + (size_t)min(r0, H) * (K / 2), nr * (K / 2));
+      Q[j].s = buf_rsrc(smat + (size_t)min(r0, H) * (K / SB), nr * (K / SB));
+    }
+    if constexpr (EF == NVFP4) s2d = a.ds2[it.e];
+  } else {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int r0 = h0 + 16 * j;
+      A[j] = buf_rsrc(mat + (size_t)min(r0, H) * K * 2, max(0, min(16, H - r0)) * K * 2);
+    }
   }
   int kb, ke;
   k_slice(K, w, NW, kb, ke);
@@ -2304,8 +2507,16 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
   for (int c0 = 0; c0 < it.np; c0 += G_COLS) {
     const int nv = min(G_COLS, it.np - c0);
     f32x4 acc[NA][G_NCT];
-    mfma_slice<F32, NA, G_NCT, MU>(A, K * 2, 0, 16, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
-                                   S.stage[w], acc);
+    if (quant) {
+      const char *xv[G_NCT];
+#pragma unroll
+      for (int ct = 0; ct < G_NCT; ++ct)
+        xv[ct] = xb + (size_t)(c0 + min(16 * ct + (lane & 15), nv - 1)) * K * 4 + (size_t)(lane >> 4) * 32;
+      mfma_slice_q<QF, F32, NA, G_NCT, MU>(Q, K, 0, 16, xv, kb, ke, S.stage[w], acc);
+    } else {
+      mfma_slice<F32, NA, G_NCT, MU>(A, K * 2, 0, 16, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
+                                     S.stage[w], acc);
+    }
 #pragma unroll
     for (int j = 0; j < NA; ++j)
 #pragma unroll
@@ -2320,7 +2531,7 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
 #pragma unroll
       for (int p = 0; p < NW; ++p) sum += S.part[p][t][ct][i][lane];
       const int row = h0 + 16 * t + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
-      if (row < H && v < nv) dst[(size_t)(c0 + v) * H + row] = sum;
+      if (row < H && v < nv) dst[(size_t)(c0 + v) * H + row] = sum * s2d;
     }
     __syncthreads();
   }

@@ -79,15 +79,17 @@ def test_plan_and_layout_grouped_rows(name):
 
 def test_grouped_rows_limits():
     for kw in (dict(act_fmt=md.MOE_F32, expert_fmt=md.MOE_F32), dict(expert_fmt=md.MOE_AFF4_G64),
-               dict(expert_fmt=md.MOE_MXFP4_B32), dict(hidden=2048 + 16), dict(inter=768 + 8)):
+               dict(act_fmt=md.MOE_F32, expert_fmt=md.MOE_MXFP4_B32), dict(hidden=2048 + 16),
+               dict(inter=768 + 8)):
         with pytest.raises(md.MoeDecodeError) as ei:
             md.moe_decode_plan(_desc(max_rows=64, **kw))
         assert ei.value.status == md.MOE_EUNSUPPORTED, kw
     with pytest.raises(md.MoeDecodeError) as ei:
         md.moe_decode_plan(_desc(max_rows=257))
     assert ei.value.status == md.MOE_EUNSUPPORTED
-    plan, ws = md.moe_decode_plan(_desc(max_rows=256))
-    md.moe_decode_plan_destroy(plan)
+    for fmt in (md.MOE_BF16, md.MOE_MXFP4_B32, md.MOE_NVFP4_B16):
+        plan, ws = md.moe_decode_plan(_desc(max_rows=256, expert_fmt=fmt))
+        md.moe_decode_plan_destroy(plan)
 
 
 def _check_plan_and_layout(spec):

@@ -56,6 +56,28 @@ def test_grouped_small_variant(routing, before, shared):
     torch.cuda.empty_cache()
 
 
+# 4-bit experts: the dequantising matrix-core loader, short (four tiles per
+# down wave) and long (I > 2048) down rows.
+_QV = [("mxfp4", "softmax", False, "gated", 192), ("mxfp4", "sigmoid_bias", True, "none", 4096),
+       ("nvfp4", "sigmoid_logit", False, "plain", 192), ("nvfp4", "softmax", True, "gated", 4096),
+       ("nvfp4", "sigmoid_bias", False, "none", 2048 + 32)]
+
+
+@pytest.mark.parametrize("fmt,routing,before,shared,inter", _QV)
+def test_grouped_4bit(fmt, routing, before, shared, inter):
+    spec = small(hidden=256, num_experts=12, top_k=3, inter=inter, shared_inter=160, expert_fmt=fmt,
+                 routing=routing, weight_before_ffn=before, norm_topk=routing != "sigmoid_logit",
+                 shared=shared != "none", shared_gated=shared == "gated", rows=(128,))
+    layer = synth.make_layer(spec, seed=_QV.index((fmt, routing, before, shared, inter)) + 400, threads=4)
+    x = layer.x(0)
+    what = f"{fmt}/{routing}/before={before}/shared={shared}/I={inter}"
+    for out_f32 in (False, True):
+        dl = DeviceLayer(layer, out_f32=out_f32)
+        grouped_rows(dl, layer, x, (33, 128, 70), what + f" f32out={out_f32}", out_f32)
+        del dl
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("E,k,inter,hidden", [(256, 16, 64, 128), (2, 1, 96, 160), (4, 4, 128, 64),
                                               (1, 1, 64, 96)])
 def test_grouped_pair_extremes(E, k, inter, hidden):
@@ -72,7 +94,9 @@ def test_grouped_pair_extremes(E, k, inter, hidden):
 
 
 @pytest.mark.parametrize("name,rows", [("qwen3_30b_a3b_bf16", (256, 128, 64, 33)),
-                                       ("llama4_wbf_bf16", (64, 48))])
+                                       ("llama4_wbf_bf16", (64, 48)),
+                                       ("qwen35_35b_a3b_mxfp4", (40, 33)),
+                                       ("qwen35_35b_a3b_nvfp4", (40, 33))])
 def test_grouped_workload(name, rows):
     spec = synth.WORKLOADS[name].replace(rows=(max(rows),))
     say(f"[gpu] grouped workload {name}: generating")
