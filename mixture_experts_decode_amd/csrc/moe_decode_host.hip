@@ -290,7 +290,8 @@ moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *st
     return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
   if ((e = moe::launch_topk_sort(a, (m + moe::ROUTE_WPB - 1) / moe::ROUTE_WPB, s, nullptr, ev(1))) != hipSuccess)
     return fail(MOE_EHIP, "top-k launch: %s", hipGetErrorString(e));
-  const int gu_items = a.cap * ((d.inter + 15) / 16) + (shared ? (a.Is + 15) / 16 : 0);
+  const int gr = k.gu_grouped_rows;
+  const int gu_items = a.cap * ((d.inter + gr - 1) / gr) + (shared ? (a.Is + gr - 1) / gr : 0);
   if ((e = k.gate_up_grouped(a, gu_items, s, ev(2), ev(3))) != hipSuccess)
     return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
   // Down rows of at most 2048: items of 64 columns on four waves that each

@@ -70,7 +70,8 @@ constexpr int G_THREADS = 512;
 constexpr int G_WPB = G_THREADS / WAVE;
 constexpr int G_NCT = 2;                // column tiles of 16 pairs per pass
 constexpr int G_COLS = 16 * G_NCT;
-constexpr int G_MU = 2;                 // k steps of 32 per staged batch (registers: two workgroups per CU)
+constexpr int G_MU = 2;
+constexpr bool G_QDIRECT = true;        // 4-bit grouped down: codes straight into the operands                 // k steps of 32 per staged batch (registers: two workgroups per CU)
 
 // Rows of intermediate per gate/up wave: 2 for 16-byte-per-8-or-4 element
 // formats; 4 for the 4-bit ones (their rows are 4x shorter) with one vector
@@ -1176,6 +1177,113 @@ __device__ __forceinline__ void mfma_slice_q(const QMat<WF> (&A)[NA], int K, int
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// The same products with the 4-bit codes loaded straight into the MFMA
+// operands (no LDS): a k-sum does not depend on the order of k, so within a
+// batch of MU k steps (32 MU elements) lane (row r, group g) takes elements
+// [8 MU g, 8 MU (g + 1)) -- 4 MU contiguous code bytes, one load -- and uses
+// elements 8 u .. 8 u + 7 of that range as its fragment of k step u; the
+// input vectors are read in the same order.  Fragments at or past ke are
+// zeroed (k ranges are multiples of 32, batches may run past them).
+// xr[ct]: the start of this lane's vector 16 ct + l % 16.
+template <int WF, int XF, int NA, int NCT, int MU>
+__device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, int n0, int N,
+                                              const char *const (&xr)[NCT], int kb, int ke,
+                                              f32x4 (&acc)[NA][NCT]) {
+  static_assert(WF == MXFP4 || WF == NVFP4, "4-bit formats");
+  static_assert(MU == 1 || MU == 2 || MU == 4, "a lane's range lies in one E8M0 block");
+  constexpr int CB = 4 * MU;                       // code bytes per lane per batch
+  constexpr int XB = XF == F32 ? 4 : 2;
+  constexpr int XQ = 8 * MU * XB / 16;             // 16-byte x loads per lane, batch and tile
+  const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
+  const int row = min(n0 + rr, N - 1);
+  const int qoff = row * (K / 2) + g * CB;
+  const int soff = WF == NVFP4 ? row * (K / 16) + (8 * MU * g) / 16 : row * (K / 32) + (8 * MU * g) / 32;
+#pragma unroll
+  for (int j = 0; j < NA; ++j)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (kb >= ke) return;
+  typedef uint32_t cvec __attribute__((ext_vector_type(MU)));
+  cvec nq[NA];
+  uint32_t ns[NA];
+  u32x4 nx[NCT][XQ];
+  auto fetch = [&](int kq) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      if constexpr (MU == 4) nq[j] = __builtin_bit_cast(cvec, __builtin_amdgcn_raw_buffer_load_b128(A[j].w, qoff + kq / 2, 0, 0));
+      else if constexpr (MU == 2) nq[j] = __builtin_bit_cast(cvec, __builtin_amdgcn_raw_buffer_load_b64(A[j].w, qoff + kq / 2, 0, 0));
+      else nq[j] = __builtin_bit_cast(cvec, __builtin_amdgcn_raw_buffer_load_b32(A[j].w, qoff + kq / 2, 0, 0));
+      if constexpr (WF == NVFP4 && MU == 4) ns[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].s, soff + kq / 16, 0, 0);
+      else if constexpr (WF == NVFP4) ns[j] = __builtin_amdgcn_raw_buffer_load_b8(A[j].s, soff + kq / 16, 0, 0);
+      else ns[j] = __builtin_amdgcn_raw_buffer_load_b8(A[j].s, soff + kq / 32, 0, 0);
+    }
+    // The lane's x range, clamped into the row (zeroed fragments cover the
+    // part past ke).
+    const int kx = min(kq + 8 * MU * g, K - 8 * MU);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int h = 0; h < XQ; ++h) nx[ct][h] = ld16(xr[ct] + (size_t)kx * XB + 16 * h);
+  };
+  fetch(kb);
+  for (int k0 = kb; k0 < ke; k0 += 32 * MU) {
+    cvec cq[NA];
+    uint32_t cs[NA];
+    u32x4 cx[NCT][XQ];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      cq[j] = nq[j];
+      cs[j] = ns[j];
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int h = 0; h < XQ; ++h) cx[ct][h] = nx[ct][h];
+    if (k0 + 32 * MU < ke) fetch(k0 + 32 * MU);
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const bool valid = k0 + 8 * MU * g + 8 * u < ke;
+      u32x4 av[NA];
+#pragma unroll
+      for (int j = 0; j < NA; ++j) {
+        float sc;
+        if constexpr (WF == MXFP4) sc = e8m0_to_f32(cs[j] & 0xFFu);
+        else sc = e4m3_to_f32(MU == 4 ? (cs[j] >> (8 * (u >> 1))) & 0xFFu : cs[j] & 0xFFu);
+        const uint32_t qd = cq[j][u];
+        uint32_t pr[4];
+        f32x2 v[4];
+        v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 0);
+        v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 1);
+        v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 2);
+        v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 3);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          // Exact bf16 products: their low 16 bits are zero.
+          const uint32_t a = __float_as_uint(v[t].x * sc), b = __float_as_uint(v[t].y * sc);
+          pr[t] = valid ? (a >> 16) | (b & 0xFFFF0000u) : 0u;
+        }
+        av[j] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        if constexpr (XF == BF16) {
+          const bf16x8 bb = __builtin_bit_cast(bf16x8, cx[ct][u]);
+#pragma unroll
+          for (int j = 0; j < NA; ++j) acc[j][ct] = mfma16(av[j], bb, acc[j][ct]);
+        } else {
+          bf16x8 hi, lo;
+          split_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
+#pragma unroll
+          for (int j = 0; j < NA; ++j) {
+            acc[j][ct] = mfma16(av[j], hi, acc[j][ct]);
+            acc[j][ct] = mfma16(av[j], lo, acc[j][ct]);
+          }
+        }
+      }
+    }
   }
 }
 
@@ -2358,29 +2466,36 @@ __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int
   return g;
 }
 
-// Gate/up: item = 16 intermediate rows of one active expert (or of the
-// shared expert); every wave takes both matrices over one eighth of H, so a
-// pair's input fragment serves the gate and the up products; the eight
-// partials are added in wave order.  Writes silu(g) * v per pair (act,
-// sorted order) or per row (sact).  Experts: bf16.
+// Gate/up: item = 16 GT intermediate rows (GT tiles of 16) of one active
+// expert (or of the shared expert); wave w takes both matrices of tile
+// w % GT over part w / GT of H, so a pair's input fragment serves the gate
+// and the up products; the parts are added in part order.  Writes
+// silu(g) * v per pair (act, sorted order) or per row (sact).  (Items of two
+// or four tiles were slower for every format.)  A pass of at most 16 pairs
+// takes one column tile.
+template <int EF> constexpr int gate_up_grouped_tiles() { return 1; }
 template <int EF>
 __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
   static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4, "matrix-core experts: bf16, mxfp4, nvfp4");
+  constexpr int GT = gate_up_grouped_tiles<EF>(), KP = G_WPB / GT;
+  constexpr int QF = EF == BF16 ? MXFP4 : EF;
   __shared__ MfmaLDS<G_WPB, 2, G_MU> S;
   const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int H = a.H, k = a.K;
-  const GroupedItem it = grouped_item(a, blockIdx.x, (a.I + 15) / 16);
+  const GroupedItem it = grouped_item(a, blockIdx.x, (a.I + 16 * GT - 1) / (16 * GT));
   if (!it.live) return;
   const int N = it.routed ? a.I : a.Is;
+  const int r0 = it.n0 * GT;                 // the item's first row
+  const int n0 = r0 + 16 * (w % GT);         // this wave's 16 rows
   const void *mg = it.routed ? tbl(a.gw, it.e) : a.sgw;
   const void *mu = it.routed ? tbl(a.uw, it.e) : a.suw;
   // bf16 rows (the shared expert's always): one resource per matrix.
   __amdgpu_buffer_rsrc_t A[2];
-  QMat<EF == BF16 ? MXFP4 : EF> Q[2];
+  QMat<QF> Q[2];
   const bool quant = EF != BF16 && it.routed;
   if (quant) {
-    Q[0] = make_qmat<EF == BF16 ? MXFP4 : EF>(mg, tbl(a.gs, it.e), N, H);
-    Q[1] = make_qmat<EF == BF16 ? MXFP4 : EF>(mu, tbl(a.us, it.e), N, H);
+    Q[0] = make_qmat<QF>(mg, tbl(a.gs, it.e), N, H);
+    Q[1] = make_qmat<QF>(mu, tbl(a.us, it.e), N, H);
   } else {
     A[0] = buf_rsrc(mg, N * H * 2);
     A[1] = buf_rsrc(mu, N * H * 2);
@@ -2393,56 +2508,61 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
     }
   }
   int kb, ke;
-  k_slice(H, w, G_WPB, kb, ke);
+  k_slice(H, w / GT, KP, kb, ke);
   const bool before = it.routed && (a.flags & WEIGHT_BEFORE);
   const char *x = reinterpret_cast<const char *>(a.x);
   const int g4 = lane >> 4, rr = lane & 15;
-  for (int c0 = 0; c0 < it.np; c0 += G_COLS) {
-    const int nv = min(G_COLS, it.np - c0);
-    const char *xv[G_NCT];
+  // One pass over the tile: NCT column tiles of 16 pairs from c0 on.
+  auto pass = [&](auto nct, int c0, int nv) {
+    constexpr int NCT = decltype(nct)::value;
+    const char *xv[NCT];
 #pragma unroll
-    for (int ct = 0; ct < G_NCT; ++ct) {
+    for (int ct = 0; ct < NCT; ++ct) {
       const int v = c0 + min(16 * ct + rr, nv - 1);
       const int row = it.routed ? min(clamp_i(a.sorted_pair[it.off + v], 0, a.te - 1) / k, a.m - 1) : v;
       xv[ct] = x + (size_t)row * H * 2 + (size_t)g4 * 16;
     }
-    f32x4 acc[2][G_NCT];
-    if constexpr (EF != BF16) {
-      if (quant)
-        mfma_slice_q<EF, BF16, 2, G_NCT, G_MU>(Q, H, it.n0, N, xv, kb, ke, S.stage[w], acc);
-      else
-        mfma_slice_v<BF16, 2, G_NCT, G_MU>(A, H * 2, it.n0, N, xv, kb, ke, S.stage[w], acc);
-    } else {
-      mfma_slice_v<BF16, 2, G_NCT, G_MU>(A, H * 2, it.n0, N, xv, kb, ke, S.stage[w], acc);
-    }
+    f32x4 acc[2][NCT];
+    if (quant)
+      mfma_slice_q<QF, BF16, 2, NCT, G_MU>(Q, H, n0, N, xv, kb, ke, S.stage[w], acc);
+    else
+      mfma_slice_v<BF16, 2, NCT, G_MU>(A, H * 2, n0, N, xv, kb, ke, S.stage[w], acc);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int ct = 0; ct < G_NCT; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S.part[w][j][ct][i][lane] = acc[j][ct][i];
+  };
+  for (int c0 = 0; c0 < it.np; c0 += G_COLS) {
+    const int nv = min(G_COLS, it.np - c0);
+    const int nct = nv > 16 ? 2 : 1;
+    if (nct == 2) pass(std::integral_constant<int, 2>(), c0, nv);
+    else pass(std::integral_constant<int, 1>(), c0, nv);
     __syncthreads();
-    // Wave w finishes (column tile w / 4, element i = w % 4).
-    const int ct = w / 4, i = w % 4;
-    float gs = 0.f, us = 0.f;
+    // (tile t, column tile ct, element i) combinations, G_WPB at a time.
+    for (int c = w; c < GT * nct * 4; c += G_WPB) {
+      const int t = c / (nct * 4), ct = (c / 4) % nct, i = c % 4;
+      float gs = 0.f, us = 0.f;
 #pragma unroll
-    for (int p = 0; p < G_WPB; ++p) {
-      gs += S.part[p][0][ct][i][lane];
-      us += S.part[p][1][ct][i][lane];
-    }
-    gs *= s2g;
-    us *= s2u;
-    const int row = it.n0 + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
-    if (row < N && v < nv) {
-      if (it.routed) {
-        if (before) {   // W(w x) = w (W x)
-          const float wt = a.topk_w[clamp_i(a.sorted_pair[it.off + c0 + v], 0, a.te - 1)];
-          gs *= wt;
-          us *= wt;
+      for (int p = 0; p < KP; ++p) {
+        gs += S.part[p * GT + t][0][ct][i][lane];
+        us += S.part[p * GT + t][1][ct][i][lane];
+      }
+      gs *= s2g;
+      us *= s2u;
+      const int row = r0 + 16 * t + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
+      if (row < N && v < nv) {
+        if (it.routed) {
+          if (before) {   // W(w x) = w (W x)
+            const float wt = a.topk_w[clamp_i(a.sorted_pair[it.off + c0 + v], 0, a.te - 1)];
+            gs *= wt;
+            us *= wt;
+          }
+          a.act[(size_t)(it.off + c0 + v) * a.I + row] = silu_mul(gs, us);
+        } else {
+          a.sact[(size_t)(c0 + v) * a.Is + row] = silu_mul(gs, us);
         }
-        a.act[(size_t)(it.off + c0 + v) * a.I + row] = silu_mul(gs, us);
-      } else {
-        a.sact[(size_t)(c0 + v) * a.Is + row] = silu_mul(gs, us);
       }
     }
     __syncthreads();   // the partials are reused by the next pass
@@ -2504,29 +2624,41 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
   k_slice(K, w, NW, kb, ke);
   const char *xb = reinterpret_cast<const char *>(it.routed ? a.act + (size_t)it.off * K : a.sact);
   float *dst = it.routed ? a.y + (size_t)it.off * H : a.sy;
-  for (int c0 = 0; c0 < it.np; c0 += G_COLS) {
-    const int nv = min(G_COLS, it.np - c0);
-    f32x4 acc[NA][G_NCT];
-    if (quant) {
-      const char *xv[G_NCT];
+  // One pass: NCT column tiles of 16 pairs from c0 on.
+  auto pass = [&](auto nct, int c0, int nv) {
+    constexpr int NCT = decltype(nct)::value;
+    f32x4 acc[NA][NCT];
+    if (quant && G_QDIRECT) {
+      const char *xr[NCT];
 #pragma unroll
-      for (int ct = 0; ct < G_NCT; ++ct)
+      for (int ct = 0; ct < NCT; ++ct) xr[ct] = xb + (size_t)(c0 + min(16 * ct + (lane & 15), nv - 1)) * K * 4;
+      mfma_slice_qd<QF, F32, NA, NCT, 2>(Q, K, 0, 16, xr, kb, ke, acc);
+    } else if (quant) {
+      const char *xv[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
         xv[ct] = xb + (size_t)(c0 + min(16 * ct + (lane & 15), nv - 1)) * K * 4 + (size_t)(lane >> 4) * 32;
-      mfma_slice_q<QF, F32, NA, G_NCT, MU>(Q, K, 0, 16, xv, kb, ke, S.stage[w], acc);
+      mfma_slice_q<QF, F32, NA, NCT, MU>(Q, K, 0, 16, xv, kb, ke, S.stage[w], acc);
     } else {
-      mfma_slice<F32, NA, G_NCT, MU>(A, K * 2, 0, 16, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
-                                     S.stage[w], acc);
+      mfma_slice<F32, NA, NCT, MU>(A, K * 2, 0, 16, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
+                                   S.stage[w], acc);
     }
 #pragma unroll
     for (int j = 0; j < NA; ++j)
 #pragma unroll
-      for (int ct = 0; ct < G_NCT; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S.part[w][j][ct][i][lane] = acc[j][ct][i];
+  };
+  for (int c0 = 0; c0 < it.np; c0 += G_COLS) {
+    const int nv = min(G_COLS, it.np - c0);
+    const int nct = nv > 16 ? 2 : 1;
+    if (nct == 2) pass(std::integral_constant<int, 2>(), c0, nv);
+    else pass(std::integral_constant<int, 1>(), c0, nv);
     __syncthreads();
     // (tile t, column tile ct, element i) combinations, NW at a time.
-    for (int c = w; c < NA * G_NCT * 4; c += NW) {
-      const int t = c / (G_NCT * 4), ct = (c / 4) % G_NCT, i = c % 4;
+    for (int c = w; c < NA * nct * 4; c += NW) {
+      const int t = c / (nct * 4), ct = (c / 4) % nct, i = c % 4;
       float sum = 0.f;
 #pragma unroll
       for (int p = 0; p < NW; ++p) sum += S.part[p][t][ct][i][lane];

@@ -46,6 +46,7 @@ struct FormatKernels {
   launch_fn gate_up_grouped;   // m > 32 (matrix cores), or null where not served
   launch_fn down_grouped;      // down rows of at most 2048
   launch_fn down_grouped_long; // longer down rows
+  int gu_grouped_rows;         // intermediate rows per grouped gate/up item
 };
 
 // First launch: router items plus the shared expert's gate/up items.
@@ -104,7 +105,7 @@ constexpr launch_fn gate_up_shd_fn() {
 #define MOE_TABLE(NAME)                                                            \
   const FormatKernels &kernels_##NAME() {                                          \
     static const FormatKernels k{kV, (int)(sizeof kV / sizeof kV[0]), kG,         \
-                                 (int)(sizeof kG / sizeof kG[0]), nullptr, nullptr, nullptr}; \
+                                 (int)(sizeof kG / sizeof kG[0]), nullptr, nullptr, nullptr, 0}; \
     return k;                                                                      \
   }
 // The same with the grouped (m > 32) kernels of the unit's expert format.
@@ -113,6 +114,6 @@ constexpr launch_fn gate_up_shd_fn() {
     static const FormatKernels k{kV, (int)(sizeof kV / sizeof kV[0]), kG,         \
                                  (int)(sizeof kG / sizeof kG[0]),                  \
                                  &launch_gate_up_grouped_t<EFT>, &launch_down_grouped_t<EFT, true>, \
-                                 &launch_down_grouped_t<EFT, false>};                \
+                                 &launch_down_grouped_t<EFT, false>, 16 * gate_up_grouped_tiles<EFT>()}; \
     return k;                                                                      \
   }
