@@ -52,6 +52,7 @@ import numpy as np
 ACT_FORMATS = ("f32", "bf16")
 EXPERT_FORMATS = ("f32", "bf16", "aff4", "mxfp4", "nvfp4")
 ROUTINGS = ("softmax", "sigmoid_bias", "sigmoid_logit")
+ACTIVATIONS = ("silu", "gelu")
 
 # Group sizes of the 4-bit formats along the reduction dimension K.
 AFF4_GROUP = 64
@@ -77,6 +78,7 @@ class LayerSpec:
     shared: bool = False
     shared_gated: bool = False
     routed_scaling_factor: float = 1.0
+    activation: str = "silu"        # expert activation: "silu" (SwiGLU) or "gelu" (GeGLU)
     w_std: float = 0.02
     x_std: float = 1.0
     bias_std: float = 0.1
@@ -338,6 +340,8 @@ def check_spec(spec: LayerSpec) -> None:
         raise ValueError("bad format")
     if spec.routing not in ROUTINGS:
         raise ValueError("bad routing")
+    if spec.activation not in ACTIVATIONS:
+        raise ValueError("bad activation")
     if spec.expert_fmt == "aff4" and (spec.hidden % AFF4_GROUP or spec.inter % AFF4_GROUP):
         raise ValueError("aff4 needs H and I multiples of 64")
     if spec.expert_fmt == "mxfp4" and (spec.hidden % MXFP4_BLOCK or spec.inter % MXFP4_BLOCK):

@@ -41,7 +41,7 @@ class _Desc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "hidden", "num_experts", "top_k", "inter", "shared_inter", "act_fmt", "expert_fmt",
         "routing", "norm_topk", "weight_before_ffn", "shared", "shared_gated")] + [
-        ("routed_scaling_factor", C.c_double)]
+        ("routed_scaling_factor", C.c_double), ("geglu", C.c_int32)]
 
 
 _PP = C.POINTER(C.c_void_p)
@@ -101,7 +101,7 @@ def desc_of(spec) -> _Desc:
                  spec.shared_inter if spec.shared else 0, FMT[spec.act_fmt],
                  FMT[spec.expert_fmt], ROUTING[spec.routing], int(spec.norm_topk),
                  int(spec.weight_before_ffn), int(spec.shared), int(spec.shared_gated),
-                 float(spec.routed_scaling_factor))
+                 float(spec.routed_scaling_factor), int(spec.activation == "gelu"))
 
 
 def _table(arr: Optional[np.ndarray]):

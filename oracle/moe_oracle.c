@@ -32,6 +32,10 @@
  *    routed_scaling_factor;
  *  - the shared expert reads the unscaled row; its gate is sigmoid(x . w_g);
  *  - the blend sums the slots in slot order, then adds the shared term;
+ *  - GeGLU ("helpers_a.rs", set_gelu_activation: the expert activation
+ *    kernel becomes gelu_mul) is gelu(gate) * up with the exact GELU,
+ *    gelu(v) = v * Phi(v) = v/2 * (1 + erf(v / sqrt 2)); the page names no
+ *    approximation.  It applies to the routed and the shared expert alike;
  *  - NVFP4 weights are the NVIDIA NVFP4 encoding the page names: E2M1 codes,
  *    one E4M3 block scale per 16 elements along K, times the projection's
  *    fp32 second-level scale; the activations stay in their own format
@@ -135,6 +139,9 @@ static double dot(const double *a, const double *b, int32_t n) {
 static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
 
 static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* GELU, exact: v * Phi(v) with Phi the standard normal distribution. */
+static double gelu(double v) { return 0.5 * v * (1.0 + erf(v / sqrt(2.0))); }
 
 /* ------------------------------------------------------- routing (S1-S3) */
 
@@ -259,9 +266,10 @@ void orc_sort_pairs(int32_t m, int32_t k, int32_t E, const int32_t *idx,
 
 /* ----------------------------------------------------- expert FFN (S4-S5) */
 
-/* One SwiGLU expert: y = down( silu(gate u) * (up u) ).  Each projection is
+/* One gated expert: y = down( act(gate u) * (up u) ), act = silu, or gelu
+ * with geglu (GeGLU).  Each projection is
  * row-major [N, K]; gate/up have (N, K) = (I, H), down (H, I). */
-static void swiglu_expert(int32_t fmt, const void *gw, const void *gs, const void *gb,
+static void swiglu_expert(int32_t fmt, int32_t geglu, const void *gw, const void *gs, const void *gb,
                           const void *uw, const void *us, const void *ub,
                           const void *dw, const void *ds, const void *db,
                           int32_t H, int32_t I, const double *u, double *y,
@@ -271,7 +279,7 @@ static void swiglu_expert(int32_t fmt, const void *gw, const void *gs, const voi
     double g = dot(row, u, H);
     orc_decode_row(fmt, uw, us, ub, H, i, row);
     double v = dot(row, u, H);
-    act[i] = silu(g) * v;
+    act[i] = (geglu ? gelu(g) : silu(g)) * v;
   }
   for (int32_t h = 0; h < H; ++h) {
     orc_decode_row(fmt, dw, ds, db, I, h, row);
@@ -328,7 +336,7 @@ int32_t orc_forward(const orc_desc *d, const orc_weights *wt, const void *x, int
       const int32_t e = sel[j];
       double c;
       orc_routed_slot(xr, H, sw[j], d->weight_before_ffn, u, &c);
-      swiglu_expert(d->expert_fmt, wt->gate[e], tbl(wt->gate_s, e), tbl(wt->gate_b, e),
+      swiglu_expert(d->expert_fmt, d->geglu, wt->gate[e], tbl(wt->gate_s, e), tbl(wt->gate_b, e),
                     wt->up[e], tbl(wt->up_s, e), tbl(wt->up_b, e), wt->down[e],
                     tbl(wt->down_s, e), tbl(wt->down_b, e), H, I, u, y, row, act);
       for (int32_t h = 0; h < H; ++h) acc[h] += c * y[h];
@@ -344,7 +352,7 @@ int32_t orc_forward(const orc_desc *d, const orc_weights *wt, const void *x, int
           s += xr[h] * orc_decode_act(d->act_fmt, wt->sh_gate_vec, h);
         gamma = sigmoid(s);
       }
-      swiglu_expert(d->act_fmt, wt->sh_gate, NULL, NULL, wt->sh_up, NULL, NULL,
+      swiglu_expert(d->act_fmt, d->geglu, wt->sh_gate, NULL, NULL, wt->sh_up, NULL, NULL,
                     wt->sh_down, NULL, NULL, H, Is, xr, y, row, act);
       for (int32_t h = 0; h < H; ++h) acc[h] += gamma * y[h];
     }

@@ -28,6 +28,7 @@ typedef struct {
   int32_t routing;
   int32_t norm_topk, weight_before_ffn, shared, shared_gated;
   double routed_scaling_factor;
+  int32_t geglu;        /* expert activation gelu(gate) * up instead of silu(gate) * up */
 } orc_desc;
 
 typedef struct {

@@ -67,6 +67,11 @@ def _sigmoid(v):
     return 1.0 / (1.0 + np.exp(-v))
 
 
+def _gelu(v):
+    from scipy.stats import norm
+    return v * norm.cdf(v)
+
+
 def dense_forward(layer, x: np.ndarray):
     """Returns (out [m,H], mask-weight matrix [m,E], selected index lists)."""
     spec = layer.spec
@@ -108,13 +113,15 @@ def dense_forward(layer, x: np.ndarray):
         else:
             U = X
             c = weights[:, e]
-        Y = (_silu(U @ Wg.T) * (U @ Wu.T)) @ Wd.T
+        act = _gelu if spec.activation == "gelu" else _silu
+        Y = (act(U @ Wg.T) * (U @ Wu.T)) @ Wd.T
         out += c[:, None] * Y
     if spec.shared:
         Sg = act_to_f64(layer.sh_gate, spec.act_fmt)
         Su = act_to_f64(layer.sh_up, spec.act_fmt)
         Sd = act_to_f64(layer.sh_down, spec.act_fmt)
-        ys = (_silu(X @ Sg.T) * (X @ Su.T)) @ Sd.T
+        act = _gelu if spec.activation == "gelu" else _silu
+        ys = (act(X @ Sg.T) * (X @ Su.T)) @ Sd.T
         if spec.shared_gated:
             g = _sigmoid(X @ act_to_f64(layer.sh_gate_vec, spec.act_fmt))
             ys = ys * g[:, None]

@@ -301,6 +301,39 @@ def test_identity_experts_give_silu_times_x(before):
         assert np.allclose(r.out[row], want, rtol=1e-15, atol=1e-300)
 
 
+def test_identity_experts_give_gelu_times_x_against_normal_table():
+    # GeGLU with identity experts: out = w * gelu(x) * x, gelu(v) = v Phi(v).
+    # Phi at +-1 and +-2 from the standard normal table; the rest through
+    # scipy's normal distribution, an independent implementation.
+    from scipy.stats import norm
+    table = {1.0: 0.8413447460685429, -1.0: 0.15865525393145707, 2.0: 0.9772498680518208,
+             -2.0: 0.022750131948179195}
+    for v, phi in table.items():
+        assert abs(norm.cdf(v) - phi) < 1e-15
+    spec = tiny(hidden=64, inter=64, top_k=1, routing="sigmoid_logit", norm_topk=False,
+                activation="gelu")
+    layer = synth.make_layer(spec, seed=12)
+    eye = np.eye(64, dtype=np.float32)
+    for p in (layer.gate, layer.up, layer.down):
+        p.data[:] = eye
+    x = synth.make_x(spec, 12, rows=3)
+    x[0, :4] = [1.0, -1.0, 2.0, -2.0]
+    r = oracle.forward(layer, x)
+    for row in range(3):
+        w = r.w[row, 0]
+        xs = x[row].astype(np.float64)
+        want = w * (xs * norm.cdf(xs) * xs)
+        # 1 + erf cancels for negative v: an absolute bound on the row's scale.
+        assert np.max(np.abs(r.out[row] - want)) <= 1e-14 * rms(want)
+    w0 = r.w[0, 0]
+    for i, (v, phi) in enumerate(table.items()):
+        assert abs(r.out[0, i] - w0 * v * phi * v) <= 1e-15 * abs(w0 * v * v)
+    # gelu(v) - gelu(-v) = v: out = w gelu(v) v, so out(1) + out(-1) = w and
+    # out(2) + out(-2) = 4 w.
+    assert abs(r.out[0, 0] + r.out[0, 1] - w0) <= 1e-15 * abs(w0)
+    assert abs(r.out[0, 2] + r.out[0, 3] - 4 * w0) <= 4e-15 * abs(w0)
+
+
 # ------------------------------------------ P-10 brute force, all variants
 
 VARIANTS = list(itertools.product(
@@ -323,6 +356,24 @@ def test_oracle_matches_dense_brute_force(act, fmt, routing, norm, before, share
     for row in range(4):
         assert list(r.idx[row]) == list(selected[row])
         assert np.allclose(r.w[row], weights[row, selected[row]], rtol=1e-14, atol=0)
+    assert np.max(np.abs(r.out - want)) <= 1e-12 * rms(want)
+
+
+GELU_VARIANTS = list(itertools.product(["f32", "bf16"], ["bf16", "mxfp4", "nvfp4"],
+                                       ["softmax", "sigmoid_logit"], [False, True]))
+
+
+@pytest.mark.parametrize("act,fmt,routing,before", GELU_VARIANTS)
+def test_oracle_geglu_matches_dense_brute_force(act, fmt, routing, before):
+    spec = tiny(act_fmt=act, expert_fmt=fmt, routing=routing, weight_before_ffn=before, top_k=3,
+                shared=True, shared_gated=True, shared_inter=32, activation="gelu", w_std=0.1)
+    seed = 900 + GELU_VARIANTS.index((act, fmt, routing, before))
+    layer = synth.make_layer(spec, seed=seed, threads=1)
+    x = synth.make_x(spec, seed, rows=4)
+    r = oracle.forward(layer, x)
+    want, _, selected = dense_ref.dense_forward(layer, x)
+    for row in range(4):
+        assert list(r.idx[row]) == list(selected[row])
     assert np.max(np.abs(r.out - want)) <= 1e-12 * rms(want)
 
 
