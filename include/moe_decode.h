@@ -100,7 +100,10 @@ enum {
   MOE_WEIGHT_BEFORE_FFN = 2,  /* the routing weight scales the expert input; output weight 1 */
   MOE_SHARED = 4,             /* add a shared SwiGLU expert on every row (unscaled input) */
   MOE_SHARED_GATED = 8,       /* ... times sigmoid(x . w_g) (requires MOE_SHARED) */
-  MOE_OUT_F32 = 16            /* write out as float32 instead of act_fmt */
+  MOE_OUT_F32 = 16,           /* write out as float32 instead of act_fmt */
+  MOE_GEGLU = 32              /* expert activation gelu(gate) * up (GeGLU, exact GELU
+                                 g * Phi(g)) instead of silu(gate) * up, routed and shared;
+                                 metrale "helpers_a.rs", set_gelu_activation */
 };
 
 typedef struct {

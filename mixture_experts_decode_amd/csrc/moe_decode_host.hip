@@ -158,7 +158,8 @@ moe_status check_desc(const moe_decode_desc &d) {
     return fail(MOE_EINVAL, "unknown expert_fmt %d", d.expert_fmt);
   if (d.routing < MOE_ROUTE_SOFTMAX || d.routing > MOE_ROUTE_SIGMOID_LOGIT)
     return fail(MOE_EINVAL, "unknown routing %d", d.routing);
-  const uint32_t known = MOE_NORM_TOPK | MOE_WEIGHT_BEFORE_FFN | MOE_SHARED | MOE_SHARED_GATED | MOE_OUT_F32;
+  const uint32_t known =
+      MOE_NORM_TOPK | MOE_WEIGHT_BEFORE_FFN | MOE_SHARED | MOE_SHARED_GATED | MOE_OUT_F32 | MOE_GEGLU;
   if (d.flags & ~known) return fail(MOE_EINVAL, "unknown flag bits 0x%x", d.flags & ~known);
   if ((d.flags & MOE_SHARED_GATED) && !(d.flags & MOE_SHARED))
     return fail(MOE_EINVAL, "MOE_SHARED_GATED requires MOE_SHARED");

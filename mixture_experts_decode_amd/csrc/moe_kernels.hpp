@@ -39,7 +39,7 @@ enum : int { F32 = 0, BF16 = 1, AFF4 = 2, MXFP4 = 3, NVFP4 = 4 };
 // 32-element chunks) read adjacent 32-byte blocks.
 enum : int { F32P = 5 };
 enum : int { ROUTE_SOFTMAX = 0, ROUTE_SIGMOID_BIAS = 1, ROUTE_SIGMOID_LOGIT = 2 };
-enum : unsigned { NORM_TOPK = 1u, WEIGHT_BEFORE = 2u, SHARED = 4u, SHARED_GATED = 8u, OUT_F32 = 16u };
+enum : unsigned { NORM_TOPK = 1u, WEIGHT_BEFORE = 2u, SHARED = 4u, SHARED_GATED = 8u, OUT_F32 = 16u, GEGLU = 32u };
 
 constexpr int WAVE = 64;
 constexpr int THREADS = 256;            // route and gate/up: 4 waves per workgroup
@@ -178,6 +178,28 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 
 __device__ __forceinline__ float silu_mul(float g, float v) {
   return g / (1.0f + __expf(-g)) * v;
+}
+
+// GeGLU's activation, the exact GELU g * Phi(g), Phi(g) = 1 - erfc(z) / 2
+// for g >= 0 and erfc(z) / 2 below, z = |g| / sqrt 2.  erfc from Abramowitz
+// and Stegun 7.1.26 (absolute error at most 1.5e-7; no cancellation for
+// negative g): erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^(-z^2),
+// t = 1 / (1 + p z).
+__device__ __forceinline__ float gelu_mul(float g, float v) {
+  const float z = __builtin_fabsf(g) * 0.70710678118654752f;
+  const float t = 1.0f / __builtin_fmaf(0.3275911f, z, 1.0f);
+  float q = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  q = __builtin_fmaf(q, t, 1.421413741f);
+  q = __builtin_fmaf(q, t, -0.284496736f);
+  q = __builtin_fmaf(q, t, 0.254829592f);
+  const float half_erfc = 0.5f * q * t * __expf(-z * z);
+  const float phi = g >= 0.f ? 1.0f - half_erfc : half_erfc;
+  return g * phi * v;
+}
+
+// The experts' activation: silu(g) * v, or gelu(g) * v with GEGLU.
+__device__ __forceinline__ float act_mul(unsigned flags, float g, float v) {
+  return (flags & GEGLU) ? gelu_mul(g, v) : silu_mul(g, v);
 }
 
 __device__ __forceinline__ double sigmoid_d(double v) { return 1.0 / (1.0 + exp(-v)); }
@@ -1898,7 +1920,7 @@ __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, cons
             const int i = i0 + t;
             // 4-bit experts: the row is stored sub-step-major (F32P).
             const int pos = (EF >= AFF4 && routed) ? ((i & 31) >> 3) * (ld >> 2) + (i >> 5) * 8 + (i & 7) : i;
-            dst[(size_t)(off + c0 + c) * ld + pos] = silu_mul(g, v);
+            dst[(size_t)(off + c0 + c) * ld + pos] = act_mul(a.flags, g, v);
           }
         }
       }
@@ -2093,7 +2115,7 @@ __device__ __forceinline__ void shared_gu_mfma(const Args &a, int item, MfmaLDS<
       us += S.part[4 + p][0][ct][i][lane];
     }
     const int row = n0 + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
-    if (row < Is && v < m) a.sact[(size_t)v * Is + row] = silu_mul(gs, us);
+    if (row < Is && v < m) a.sact[(size_t)v * Is + row] = act_mul(a.flags, gs, us);
   }
 }
 
@@ -2232,8 +2254,12 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
 // workgroup, the last, publishes it.
 // SHD: 0, or the column tiles (1: m <= 16, 2: m <= 32) of the shared
 // expert's down items this variant also runs.
+// The variants m = 1 runs (one vector per pass, at most one shared column
+// tile) are held to 128 registers, four waves per SIMD: their natural size is
+// within a few registers of it.  Argument: CR * 4 + SHD.
+template <int CRS> constexpr int gate_up_min_waves() { return CRS / 4 == 1 && CRS % 4 <= 1 ? 4 : 1; }
 template <int EF, int ACT, int CR, int CS, int SHD>
-__global__ __launch_bounds__(THREADS) void gate_up_kernel(Args a) {
+__global__ __launch_bounds__(THREADS, gate_up_min_waves<CR * 4 + SHD>()) void gate_up_kernel(Args a) {
   constexpr int NI = gate_up_ni<EF, CR>();
   const int ips = a.gu_items_per_slot;
   const int wave = uniform_i(threadIdx.x >> 6);
@@ -2559,9 +2585,9 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
             gs *= wt;
             us *= wt;
           }
-          a.act[(size_t)(it.off + c0 + v) * a.I + row] = silu_mul(gs, us);
+          a.act[(size_t)(it.off + c0 + v) * a.I + row] = act_mul(a.flags, gs, us);
         } else {
-          a.sact[(size_t)(c0 + v) * a.Is + row] = silu_mul(gs, us);
+          a.sact[(size_t)(c0 + v) * a.Is + row] = act_mul(a.flags, gs, us);
         }
       }
     }

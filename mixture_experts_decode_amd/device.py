@@ -28,6 +28,8 @@ def desc_of(spec: LayerSpec, max_rows: Optional[int] = None, out_f32: bool = Fal
         flags |= md.MOE_SHARED_GATED
     if out_f32:
         flags |= md.MOE_OUT_F32
+    if spec.activation == "gelu":
+        flags |= md.MOE_GEGLU
     return md.moe_decode_desc(
         hidden=spec.hidden, num_experts=spec.num_experts, top_k=spec.top_k, inter=spec.inter,
         shared_inter=spec.shared_inter if spec.shared else 0,

@@ -34,6 +34,7 @@ MOE_WEIGHT_BEFORE_FFN = 2
 MOE_SHARED = 4
 MOE_SHARED_GATED = 8
 MOE_OUT_F32 = 16
+MOE_GEGLU = 32
 
 
 class MoeDecodeError(RuntimeError):

@@ -78,6 +78,19 @@ def test_grouped_4bit(fmt, routing, before, shared, inter):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "nvfp4"])
+def test_grouped_geglu(fmt):
+    spec = small(hidden=256, num_experts=12, top_k=3, inter=192, shared_inter=160, expert_fmt=fmt,
+                 activation="gelu", shared=True, shared_gated=True, rows=(96,))
+    layer = synth.make_layer(spec, seed=600 + len(fmt), threads=4)
+    x = layer.x(0)
+    for out_f32 in (False, True):
+        dl = DeviceLayer(layer, out_f32=out_f32)
+        grouped_rows(dl, layer, x, (33, 96), f"geglu {fmt} f32out={out_f32}", out_f32)
+        del dl
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("E,k,inter,hidden", [(256, 16, 64, 128), (2, 1, 96, 160), (4, 4, 128, 64),
                                               (1, 1, 64, 96)])
 def test_grouped_pair_extremes(E, k, inter, hidden):
@@ -108,3 +121,22 @@ def test_grouped_workload(name, rows):
     grouped_rows(dl32, layer, x, (max(rows),), name + " f32out", out_f32=True)
     del dl, dl32
     torch.cuda.empty_cache()
+
+
+def test_paths_agree_at_the_boundary():
+    # m = 32 (fused decode path) and m = 33 (grouped path): the first 32 rows
+    # agree within the tolerance (different accumulation orders), with equal
+    # selections.
+    spec = small(hidden=512, num_experts=16, top_k=4, inter=256, shared=True, shared_gated=True,
+                 shared_inter=192, rows=(64,))
+    layer = synth.make_layer(spec, seed=77)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x[:33])
+    dl = DeviceLayer(layer, out_f32=True)
+    o32, i32, w32 = run(dl, x, 32)
+    o33, i33, w33 = run(dl, x, 33)
+    check(spec, o32, i32, w32, ref, 32, TOL_OUT_F32, "m=32")
+    check(spec, o33, i33, w33, ref, 33, TOL_OUT_F32, "m=33")
+    assert np.array_equal(i32, i33[:32]) and np.array_equal(w32, w33[:32])
+    r = np.abs(ref.out[:32])
+    assert np.max(np.abs(o32 - o33[:32])) <= 2 * TOL_OUT_F32 * float(np.sqrt(np.mean(r * r)))

@@ -196,6 +196,25 @@ def test_small_variant(act, fmt, routing, before, shared):
             check_sort(dl, m, idx)
 
 
+@pytest.mark.parametrize("act,fmt,routing", [("bf16", "bf16", "softmax"), ("bf16", "mxfp4", "sigmoid_bias"),
+                                            ("bf16", "nvfp4", "softmax"), ("bf16", "aff4", "sigmoid_logit"),
+                                            ("f32", "f32", "softmax"), ("f32", "nvfp4", "sigmoid_bias")])
+def test_small_geglu(act, fmt, routing):
+    # GeGLU experts (routed and shared): the exact GELU against the oracle's.
+    spec = small(act_fmt=act, expert_fmt=fmt, routing=routing, activation="gelu", shared=True,
+                 shared_gated=True, norm_topk=routing != "sigmoid_logit")
+    layer = synth.make_layer(spec, seed=500 + len(act) + len(fmt) + len(routing), threads=4)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    for out_f32 in (False, True):
+        dl = DeviceLayer(layer, out_f32=out_f32)
+        for m in (1, 5, 8):
+            say(f"[gpu] geglu {act}/{fmt}/{routing} m={m} f32out={out_f32}")
+            got, idx, w = run(dl, x, m)
+            tol = TOL[act] if not out_f32 else (TOL_OUT_F32 if act == "bf16" else TOL["f32"])
+            check(spec, got, idx, w, ref, m, tol, f"geglu {act}/{fmt} m={m}")
+
+
 def test_every_row_count_and_pass_variant():
     spec = small(hidden=256, num_experts=16, top_k=4, inter=128, shared=True, shared_gated=True,
                  shared_inter=96, rows=(32,))
