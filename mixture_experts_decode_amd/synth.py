@@ -16,6 +16,7 @@ of them can be regenerated alone and the experts can be drawn in parallel):
     stream key [seed, 5, j]      shared expert projection j (Is instead of I)
     stream key [seed, 6, 0]      shared-expert gate vector w_g [H]
     stream key [seed, 7, b]      activation block b: x [max_rows, H]
+    stream key [seed, 8, 0]      pre-expert norm weight [H]: 1 + z * 0.1
 
 Each weight is ``f32(z * std)`` with ``z`` a float32 standard normal, then
 stored as f32, bf16 (RNE) or quantized (aff4 / mxfp4 / nvfp4 below).  ``x`` is
@@ -79,6 +80,8 @@ class LayerSpec:
     shared_gated: bool = False
     routed_scaling_factor: float = 1.0
     activation: str = "silu"        # expert activation: "silu" (SwiGLU) or "gelu" (GeGLU)
+    pre_expert_norm: bool = False   # experts read the row RMS-normed (weight pre_norm_w); router: raw
+    norm_eps: float = 1e-6
     w_std: float = 0.02
     x_std: float = 1.0
     bias_std: float = 0.1
@@ -285,6 +288,7 @@ class Layer:
     sh_up: Optional[np.ndarray]         # [Is, H] act_fmt
     sh_down: Optional[np.ndarray]       # [H, Is] act_fmt
     sh_gate_vec: Optional[np.ndarray]   # [H] act_fmt
+    pre_norm_w: Optional[np.ndarray] = None   # [H] act_fmt (pre_expert_norm)
 
     def x(self, block: int = 0, rows: Optional[int] = None) -> np.ndarray:
         return make_x(self.spec, self.seed, block, rows)
@@ -384,7 +388,10 @@ def make_layer(spec: LayerSpec, seed: int = 0, threads: Optional[int] = None) ->
         sh_down = _store_act(_draw(seed, 5, 2, (H, Is), spec.w_std), spec.act_fmt)
         if spec.shared_gated:
             sh_vec = _store_act(_draw(seed, 6, 0, (H,), spec.w_std), spec.act_fmt)
-    return Layer(spec, seed, router, bias, gate, up, down, sh_gate, sh_up, sh_down, sh_vec)
+    norm_w = None
+    if spec.pre_expert_norm:
+        norm_w = _store_act(_draw(seed, 8, 0, (H,), 0.1) + np.float32(1.0), spec.act_fmt)
+    return Layer(spec, seed, router, bias, gate, up, down, sh_gate, sh_up, sh_down, sh_vec, norm_w)
 
 
 def make_x(spec: LayerSpec, seed: int = 0, block: int = 0, rows: Optional[int] = None) -> np.ndarray:

@@ -41,7 +41,8 @@ class _Desc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "hidden", "num_experts", "top_k", "inter", "shared_inter", "act_fmt", "expert_fmt",
         "routing", "norm_topk", "weight_before_ffn", "shared", "shared_gated")] + [
-        ("routed_scaling_factor", C.c_double), ("geglu", C.c_int32)]
+        ("routed_scaling_factor", C.c_double), ("geglu", C.c_int32), ("pre_norm", C.c_int32),
+        ("norm_eps", C.c_double)]
 
 
 _PP = C.POINTER(C.c_void_p)
@@ -51,7 +52,7 @@ class _Weights(C.Structure):
     _fields_ = [("router", C.c_void_p), ("expert_bias", C.c_void_p)] + [
         (n, _PP) for n in ("gate", "up", "down", "gate_s", "up_s", "down_s",
                            "gate_b", "up_b", "down_b")] + [
-        (n, C.c_void_p) for n in ("sh_gate", "sh_up", "sh_down", "sh_gate_vec")]
+        (n, C.c_void_p) for n in ("sh_gate", "sh_up", "sh_down", "sh_gate_vec", "pre_norm_w")]
 
 
 _lib = None
@@ -101,7 +102,8 @@ def desc_of(spec) -> _Desc:
                  spec.shared_inter if spec.shared else 0, FMT[spec.act_fmt],
                  FMT[spec.expert_fmt], ROUTING[spec.routing], int(spec.norm_topk),
                  int(spec.weight_before_ffn), int(spec.shared), int(spec.shared_gated),
-                 float(spec.routed_scaling_factor), int(spec.activation == "gelu"))
+                 float(spec.routed_scaling_factor), int(spec.activation == "gelu"),
+                 int(spec.pre_expert_norm), float(spec.norm_eps))
 
 
 def _table(arr: Optional[np.ndarray]):
@@ -137,6 +139,7 @@ class _Bound:
         w.sh_up = _ptr(layer.sh_up)
         w.sh_down = _ptr(layer.sh_down)
         w.sh_gate_vec = _ptr(layer.sh_gate_vec)
+        w.pre_norm_w = _ptr(layer.pre_norm_w)
         self.weights = w
 
 

@@ -36,6 +36,13 @@
  *    kernel becomes gelu_mul) is gelu(gate) * up with the exact GELU,
  *    gelu(v) = v * Phi(v) = v/2 * (1 + erf(v / sqrt 2)); the page names no
  *    approximation.  It applies to the routed and the shared expert alike;
+ *  - the pre-expert norm ("helpers_a.rs", set_pre_expert_norm: the router
+ *    reads the input as it is, the experts read it normed with the norm
+ *    weight) is the RMS norm xe = x * w / sqrt(mean(x^2) + eps) of each row,
+ *    stored in the activation format (rounded to nearest, ties to even) as
+ *    the experts' input; the routed experts (through the weight placement)
+ *    and the shared expert read xe, the router and the shared-expert gate
+ *    read x;
  *  - NVFP4 weights are the NVIDIA NVFP4 encoding the page names: E2M1 codes,
  *    one E4M3 block scale per 16 elements along K, times the projection's
  *    fp32 second-level scale; the activations stay in their own format
@@ -126,6 +133,28 @@ void orc_decode_row(int32_t fmt, const void *w, const void *s, const void *b,
         out[k] = NAN;
     }
   }
+}
+
+/* A double rounded to the activation format: float32 (to nearest), or bf16
+ * (8 significant bits, to nearest, ties to even; finite normal values). */
+static double round_act(int32_t fmt, double v) {
+  if (fmt == ORC_F32) return (double)(float)v;
+  if (v == 0.0 || !isfinite(v)) return v;
+  int e;
+  frexp(v, &e);                          /* |v| in [2^(e-1), 2^e) */
+  const double quantum = ldexp(1.0, e - 8);
+  return nearbyint(v / quantum) * quantum; /* default rounding: to nearest, ties to even */
+}
+
+/* "helpers_a.rs", set_pre_expert_norm: one row's expert input, the RMS norm
+ * x * w / sqrt(mean(x^2) + eps) in the activation format. */
+void orc_pre_expert_norm(const orc_desc *d, const void *norm_w, const double *x, double *xe) {
+  const int32_t H = d->hidden;
+  double ss = 0.0;
+  for (int32_t h = 0; h < H; ++h) ss += x[h] * x[h];
+  const double inv = 1.0 / sqrt(ss / (double)H + d->norm_eps);
+  for (int32_t h = 0; h < H; ++h)
+    xe[h] = round_act(d->act_fmt, x[h] * orc_decode_act(d->act_fmt, norm_w, h) * inv);
 }
 
 /* ------------------------------------------------------------ small math */
@@ -299,6 +328,7 @@ static int valid_desc(const orc_desc *d) {
   if (d->expert_fmt == ORC_MXFP4 && (d->hidden % 32 || d->inter % 32)) return 0;
   if (d->expert_fmt == ORC_NVFP4 && (d->hidden % 16 || d->inter % 16)) return 0;
   if (d->shared && d->shared_inter <= 0) return 0;
+  if (d->pre_norm && !(d->norm_eps >= 0.0)) return 0;
   return 1;
 }
 
@@ -309,6 +339,7 @@ int32_t orc_forward(const orc_desc *d, const orc_weights *wt, const void *x, int
   const int32_t Is = d->shared ? d->shared_inter : 0;
   const int32_t big = (H > I ? H : I) > Is ? (H > I ? H : I) : Is;
   double *xr = (double *)malloc(sizeof(double) * (size_t)H);
+  double *xe = (double *)malloc(sizeof(double) * (size_t)H);   /* the experts' input */
   double *u = (double *)malloc(sizeof(double) * (size_t)H);
   double *y = (double *)malloc(sizeof(double) * (size_t)H);
   double *acc = (double *)malloc(sizeof(double) * (size_t)H);
@@ -322,6 +353,10 @@ int32_t orc_forward(const orc_desc *d, const orc_weights *wt, const void *x, int
     /* Each row on its own: the result of a row does not depend on m. */
     const char *xrow = (const char *)x + (size_t)r * H * (d->act_fmt == ORC_F32 ? 4 : 2);
     for (int32_t h = 0; h < H; ++h) xr[h] = orc_decode_act(d->act_fmt, xrow, h);
+    if (d->pre_norm)
+      orc_pre_expert_norm(d, wt->pre_norm_w, xr, xe);
+    else
+      for (int32_t h = 0; h < H; ++h) xe[h] = xr[h];
     orc_router_logits(d, wt, xrow, lg);
     orc_select(d, wt->expert_bias, lg, sel, sw, margin ? &margin[r] : NULL);
     if (idx)
@@ -335,7 +370,7 @@ int32_t orc_forward(const orc_desc *d, const orc_weights *wt, const void *x, int
     for (int32_t j = 0; j < k; ++j) {
       const int32_t e = sel[j];
       double c;
-      orc_routed_slot(xr, H, sw[j], d->weight_before_ffn, u, &c);
+      orc_routed_slot(xe, H, sw[j], d->weight_before_ffn, u, &c);
       swiglu_expert(d->expert_fmt, d->geglu, wt->gate[e], tbl(wt->gate_s, e), tbl(wt->gate_b, e),
                     wt->up[e], tbl(wt->up_s, e), tbl(wt->up_b, e), wt->down[e],
                     tbl(wt->down_s, e), tbl(wt->down_b, e), H, I, u, y, row, act);
@@ -353,11 +388,11 @@ int32_t orc_forward(const orc_desc *d, const orc_weights *wt, const void *x, int
         gamma = sigmoid(s);
       }
       swiglu_expert(d->act_fmt, d->geglu, wt->sh_gate, NULL, NULL, wt->sh_up, NULL, NULL,
-                    wt->sh_down, NULL, NULL, H, Is, xr, y, row, act);
+                    wt->sh_down, NULL, NULL, H, Is, xe, y, row, act);
       for (int32_t h = 0; h < H; ++h) acc[h] += gamma * y[h];
     }
     for (int32_t h = 0; h < H; ++h) out[(size_t)r * H + h] = acc[h];
   }
-  free(xr); free(u); free(y); free(acc); free(row); free(act); free(lg); free(sel); free(sw);
+  free(xr); free(xe); free(u); free(y); free(acc); free(row); free(act); free(lg); free(sel); free(sw);
   return 0;
 }

@@ -29,6 +29,8 @@ typedef struct {
   int32_t norm_topk, weight_before_ffn, shared, shared_gated;
   double routed_scaling_factor;
   int32_t geglu;        /* expert activation gelu(gate) * up instead of silu(gate) * up */
+  int32_t pre_norm;     /* experts read the row RMS-normed with pre_norm_w (router: raw) */
+  double norm_eps;
 } orc_desc;
 
 typedef struct {
@@ -43,6 +45,7 @@ typedef struct {
   const void *const *gate_b, *const *up_b, *const *down_b;
   const void *sh_gate, *sh_up, *sh_down; /* [Is,H],[Is,H],[H,Is] act_fmt */
   const void *sh_gate_vec;               /* [H] act_fmt */
+  const void *pre_norm_w;                /* [H] act_fmt (pre_norm) */
 } orc_weights;
 
 /* One OCP FP8 E4M3 byte decoded to double (NaN for the NaN codes). */
@@ -52,6 +55,9 @@ double orc_decode_act(int32_t fmt, const void *p, int64_t i);
 /* Row n of an [N,K] expert projection, decoded to double, out[K]. */
 void orc_decode_row(int32_t fmt, const void *w, const void *s, const void *b,
                     int32_t K, int32_t n, double *out);
+
+/* One row's expert input under the pre-expert norm: xe[H] from x[H]. */
+void orc_pre_expert_norm(const orc_desc *d, const void *norm_w, const double *x, double *xe);
 
 /* One routed slot's expert input and output weight (weight placement). */
 void orc_routed_slot(const double *x, int32_t n, double w, int32_t before_ffn,

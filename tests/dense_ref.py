@@ -72,6 +72,16 @@ def _gelu(v):
     return v * norm.cdf(v)
 
 
+def round_to_act(v: np.ndarray, fmt: str) -> np.ndarray:
+    """Exact values rounded to the activation format (bf16: 8 significant
+    bits, to nearest, ties to even)."""
+    if fmt == "f32":
+        return v.astype(np.float32).astype(np.float64)
+    m, e = np.frexp(v)
+    q = np.ldexp(1.0, e - 8)
+    return np.where(v == 0, 0.0, np.rint(v / q) * q)
+
+
 def dense_forward(layer, x: np.ndarray):
     """Returns (out [m,H], mask-weight matrix [m,E], selected index lists)."""
     spec = layer.spec
@@ -102,16 +112,22 @@ def dense_forward(layer, x: np.ndarray):
     mask = np.zeros((m, E), bool)
     for r, order in enumerate(selected):
         mask[r, order] = True
+    # The experts' input: the row itself, or RMS-normed (the router above read X).
+    XE = X
+    if spec.pre_expert_norm:
+        w_n = act_to_f64(layer.pre_norm_w, spec.act_fmt)
+        inv = 1.0 / np.sqrt(np.mean(X * X, axis=1, keepdims=True) + spec.norm_eps)
+        XE = round_to_act(X * w_n[None, :] * inv, spec.act_fmt)
     out = np.zeros_like(X)
     for e in range(E):
         Wg = dense_weight(layer.gate, e)
         Wu = dense_weight(layer.up, e)
         Wd = dense_weight(layer.down, e)
         if spec.weight_before_ffn:
-            U = X * weights[:, e:e + 1]
+            U = XE * weights[:, e:e + 1]
             c = mask[:, e].astype(np.float64)
         else:
-            U = X
+            U = XE
             c = weights[:, e]
         act = _gelu if spec.activation == "gelu" else _silu
         Y = (act(U @ Wg.T) * (U @ Wu.T)) @ Wd.T
@@ -121,7 +137,7 @@ def dense_forward(layer, x: np.ndarray):
         Su = act_to_f64(layer.sh_up, spec.act_fmt)
         Sd = act_to_f64(layer.sh_down, spec.act_fmt)
         act = _gelu if spec.activation == "gelu" else _silu
-        ys = (act(X @ Sg.T) * (X @ Su.T)) @ Sd.T
+        ys = (act(XE @ Sg.T) * (XE @ Su.T)) @ Sd.T
         if spec.shared_gated:
             g = _sigmoid(X @ act_to_f64(layer.sh_gate_vec, spec.act_fmt))
             ys = ys * g[:, None]

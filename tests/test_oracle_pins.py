@@ -377,6 +377,75 @@ def test_oracle_geglu_matches_dense_brute_force(act, fmt, routing, before):
     assert np.max(np.abs(r.out - want)) <= 1e-12 * rms(want)
 
 
+# ----------------------------------------------- P-18 pre-expert norm
+
+NORM_VARIANTS = list(itertools.product(["f32", "bf16"], ["bf16", "aff4", "nvfp4"],
+                                       ["softmax", "sigmoid_bias"], [False, True]))
+
+
+@pytest.mark.parametrize("act,fmt,routing,before", NORM_VARIANTS)
+def test_pre_norm_matches_dense_brute_force(act, fmt, routing, before):
+    spec = tiny(act_fmt=act, expert_fmt=fmt, routing=routing, weight_before_ffn=before, top_k=3,
+                shared=True, shared_gated=True, shared_inter=32, pre_expert_norm=True, w_std=0.1)
+    seed = 950 + NORM_VARIANTS.index((act, fmt, routing, before))
+    layer = synth.make_layer(spec, seed=seed, threads=1)
+    x = synth.make_x(spec, seed, rows=4)
+    r = oracle.forward(layer, x)
+    want, _, selected = dense_ref.dense_forward(layer, x)
+    for row in range(4):
+        assert list(r.idx[row]) == list(selected[row])
+    assert np.max(np.abs(r.out - want)) <= 1e-12 * rms(want)
+
+
+def _identity_norm_layer(act, eps, seed=13, shared=False):
+    spec = tiny(act_fmt=act, hidden=64, inter=64, top_k=1, routing="softmax", norm_topk=True,
+                pre_expert_norm=True, norm_eps=eps, shared=shared, shared_gated=False,
+                shared_inter=64)
+    layer = synth.make_layer(spec, seed=seed)
+    eye = np.eye(64, dtype=np.float32)     # the routed experts are f32
+    for p in (layer.gate, layer.up, layer.down):
+        p.data[:] = eye
+    return spec, layer
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_pre_norm_constant_row_closed_form(act):
+    # x = c everywhere: mean(x^2) = c^2.  eps = 0 gives the expert input
+    # w * sign(c); eps = 3 c^2 gives w * sign(c) / 2 (both exact).  With one
+    # identity expert at weight 1 (top-1, normalised): out = silu(xe) * xe.
+    for eps, scale in ((0.0, 1.0), (3 * 0.75 ** 2, 0.5)):
+        spec, layer = _identity_norm_layer(act, eps)
+        x = np.full((2, 64), 0.75, np.float32)
+        x[1] = -0.75
+        if act == "bf16":
+            x = synth.f32_to_bf16_bits(x)
+        r = oracle.forward(layer, x)
+        w = dense_ref.act_to_f64(layer.pre_norm_w, act)
+        for row, sign in ((0, 1.0), (1, -1.0)):
+            xe = sign * scale * w
+            want = xe / (1 + np.exp(-xe)) * xe
+            assert r.w[row, 0] == 1.0
+            assert np.max(np.abs(r.out[row] - want)) <= 1e-15 * np.max(np.abs(want)), (eps, row)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_pre_norm_scale_invariant_and_router_reads_raw_input(act):
+    # eps = 0: 4 x has the same expert input as x, bit for bit; the router
+    # reads the raw row, so its logits scale by 4 (same top-1, weight 1).
+    spec, layer = _identity_norm_layer(act, 0.0, seed=14, shared=True)
+    x = synth.make_x(spec, 14, rows=3)
+    xf = dense_ref.act_to_f64(x, act)
+    x4 = (xf * 4).astype(np.float32)
+    if act == "bf16":
+        x4 = synth.f32_to_bf16_bits(x4)
+    r1, r4 = oracle.forward(layer, x), oracle.forward(layer, x4)
+    assert np.array_equal(r1.idx, r4.idx) and np.array_equal(r1.w, r4.w)
+    assert np.array_equal(r1.out, r4.out)
+    assert np.allclose(r4.logits, 4 * r1.logits, rtol=1e-14, atol=0)
+    plain = synth.make_layer(spec.replace(pre_expert_norm=False), seed=14)
+    assert np.array_equal(oracle.forward(plain, x).logits, r1.logits)
+
+
 # --------------------------------------------------------------- P-11 sort
 
 @pytest.mark.parametrize("m,k,E", [(1, 1, 1), (1, 8, 128), (8, 8, 128), (32, 1, 16),
