@@ -101,9 +101,14 @@ enum {
   MOE_SHARED = 4,             /* add a shared SwiGLU expert on every row (unscaled input) */
   MOE_SHARED_GATED = 8,       /* ... times sigmoid(x . w_g) (requires MOE_SHARED) */
   MOE_OUT_F32 = 16,           /* write out as float32 instead of act_fmt */
-  MOE_GEGLU = 32              /* expert activation gelu(gate) * up (GeGLU, exact GELU
+  MOE_GEGLU = 32,             /* expert activation gelu(gate) * up (GeGLU, exact GELU
                                  g * Phi(g)) instead of silu(gate) * up, routed and shared;
                                  metrale "helpers_a.rs", set_gelu_activation */
+  MOE_PRE_EXPERT_NORM = 64    /* the experts (routed and shared) read each row RMS-normed,
+                                 x * w / sqrt(mean(x^2) + norm_eps) with w = pre_norm_w,
+                                 stored in act_fmt (to nearest, ties to even); the router and
+                                 the shared-expert gate read the row as it is.  metrale
+                                 "helpers_a.rs", set_pre_expert_norm */
 };
 
 typedef struct {
@@ -118,6 +123,7 @@ typedef struct {
   int32_t routing;       /* moe_routing */
   uint32_t flags;        /* MOE_NORM_TOPK | MOE_WEIGHT_BEFORE_FFN | MOE_SHARED | ... */
   float routed_scaling_factor;
+  float norm_eps;        /* MOE_PRE_EXPERT_NORM: finite, >= 0; else ignored */
 } moe_decode_desc;
 
 /* Device pointers.  The per-expert tables are DEVICE arrays of E uint64
@@ -143,6 +149,7 @@ typedef struct {
   const float *gate_scale2;    /* nvfp4: [E] float32 second-level scale of each expert's gate; else ignored */
   const float *up_scale2;      /* nvfp4: [E] float32, up */
   const float *down_scale2;    /* nvfp4: [E] float32, down */
+  const void *pre_norm_w;      /* [H] act_fmt (MOE_PRE_EXPERT_NORM), 16-byte aligned */
 } moe_decode_weights;
 
 typedef struct moe_decode_plan moe_decode_plan_t;
@@ -172,6 +179,8 @@ typedef struct {
                              (matrix-core path; P = max(1, Is / 2048)) */
   size_t routed_y;        /* float [te, H]: routed expert outputs per pair, sorted order
                              (m > 32 only; a 4-byte placeholder when max_rows <= 32) */
+  size_t normed_x;        /* act_fmt [max_rows, H]: the experts' input under
+                             MOE_PRE_EXPERT_NORM (a 4-byte placeholder without it) */
   size_t sync;            /* uint32 [512]: reserved counters, zero between calls (word 0
                              counts the router workgroups, word 1 the top-k workgroups of
                              the m > 32 path; the last arrival resets each) */

@@ -158,13 +158,15 @@ moe_status check_desc(const moe_decode_desc &d) {
     return fail(MOE_EINVAL, "unknown expert_fmt %d", d.expert_fmt);
   if (d.routing < MOE_ROUTE_SOFTMAX || d.routing > MOE_ROUTE_SIGMOID_LOGIT)
     return fail(MOE_EINVAL, "unknown routing %d", d.routing);
-  const uint32_t known =
-      MOE_NORM_TOPK | MOE_WEIGHT_BEFORE_FFN | MOE_SHARED | MOE_SHARED_GATED | MOE_OUT_F32 | MOE_GEGLU;
+  const uint32_t known = MOE_NORM_TOPK | MOE_WEIGHT_BEFORE_FFN | MOE_SHARED | MOE_SHARED_GATED | MOE_OUT_F32 |
+                         MOE_GEGLU | MOE_PRE_EXPERT_NORM;
   if (d.flags & ~known) return fail(MOE_EINVAL, "unknown flag bits 0x%x", d.flags & ~known);
   if ((d.flags & MOE_SHARED_GATED) && !(d.flags & MOE_SHARED))
     return fail(MOE_EINVAL, "MOE_SHARED_GATED requires MOE_SHARED");
   if (!std::isfinite(d.routed_scaling_factor))
     return fail(MOE_EINVAL, "routed_scaling_factor must be finite");
+  if ((d.flags & MOE_PRE_EXPERT_NORM) && !(std::isfinite(d.norm_eps) && d.norm_eps >= 0.0f))
+    return fail(MOE_EINVAL, "norm_eps must be finite and >= 0");
   if (d.num_experts > moe::MAX_EXPERTS)
     return fail(MOE_EUNSUPPORTED, "num_experts %d > %d", d.num_experts, moe::MAX_EXPERTS);
   if (d.top_k > d.num_experts || d.top_k > moe::MAX_TOPK)
@@ -239,6 +241,7 @@ void layout_for(const moe_decode_desc &d, moe_decode_ws_layout *L) {
   L->shared_act = take(R * Is * 4);
   L->shared_y = take(Is ? (size_t)shared_down_parts(d) * R * (size_t)d.hidden * 4 : 0);
   L->routed_y = take(d.max_rows > moe::MAX_ROWS ? te * (size_t)d.hidden * 4 : 0);
+  L->normed_x = take((d.flags & MOE_PRE_EXPERT_NORM) ? R * (size_t)d.hidden * (d.act_fmt == MOE_F32 ? 4 : 2) : 0);
   L->total = o;
 }
 
@@ -265,6 +268,8 @@ moe_status check_weights(const moe_decode_desc &d, const moe_decode_weights *w) 
   }
   if ((d.flags & MOE_SHARED_GATED) && (!w->sh_gate_vec || !aligned(w->sh_gate_vec, 16)))
     return fail(MOE_EINVAL, "MOE_SHARED_GATED needs a 16-byte aligned sh_gate_vec");
+  if ((d.flags & MOE_PRE_EXPERT_NORM) && (!w->pre_norm_w || !aligned(w->pre_norm_w, 16)))
+    return fail(MOE_EINVAL, "MOE_PRE_EXPERT_NORM needs a 16-byte aligned pre_norm_w");
   return MOE_OK;
 }
 
@@ -272,7 +277,8 @@ moe_status check_weights(const moe_decode_desc &d, const moe_decode_weights *w) 
 // down on the matrix cores and the blend (moe_kernels.hpp, grouped path).
 // The three timed stages are route (router + top-k/sort), gate_up, and
 // down_blend (down + blend).
-moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *stream, void *const *events) {
+moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *stream, void *const *events,
+                           hipEvent_t route_start) {
   const moe_decode_desc &d = plan->d;
   const moe::FormatKernels &k = kernels_for(d.act_fmt, d.expert_fmt);
   const int m = a.m;
@@ -287,7 +293,7 @@ moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *st
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto ev = [&](int i) -> hipEvent_t { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
   hipError_t e;
-  if ((e = moe::launch_route(d.act_fmt, 1, a, a.n_router_wg, s, ev(0), nullptr)) != hipSuccess)
+  if ((e = moe::launch_route(d.act_fmt, 1, a, a.n_router_wg, s, route_start, nullptr)) != hipSuccess)
     return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
   if ((e = moe::launch_topk_sort(a, (m + moe::ROUTE_WPB - 1) / moe::ROUTE_WPB, s, nullptr, ev(1))) != hipSuccess)
     return fail(MOE_EHIP, "top-k launch: %s", hipGetErrorString(e));
@@ -347,6 +353,7 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   a.flags = d.flags;
   a.rsf = d.routed_scaling_factor;
   a.x = x;
+  a.xr = x;
   a.out = out;
   a.idx_out = idx_out;
   a.w_out = w_out;
@@ -374,7 +381,18 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   a.sy = reinterpret_cast<float *>(ws + L.shared_y);
   a.y = reinterpret_cast<float *>(ws + L.routed_y);
   a.sync = reinterpret_cast<unsigned *>(ws + L.sync);
-  if (m > moe::MAX_ROWS) return forward_grouped(plan, a, stream, events);
+  // Pre-expert norm: the experts read the normed rows, written first (its
+  // launch opens the route stage's timing).
+  hipEvent_t route_start = events ? static_cast<hipEvent_t>(events[0]) : nullptr;
+  if (d.flags & MOE_PRE_EXPERT_NORM) {
+    void *xe = ws + L.normed_x;
+    hipError_t e = moe::launch_pre_norm(d.act_fmt, a, w->pre_norm_w, d.norm_eps, xe,
+                                        static_cast<hipStream_t>(stream), route_start);
+    if (e != hipSuccess) return fail(MOE_EHIP, "pre-norm launch: %s", hipGetErrorString(e));
+    a.x = xe;
+    route_start = nullptr;
+  }
+  if (m > moe::MAX_ROWS) return forward_grouped(plan, a, stream, events, route_start);
 
   const moe::Variant &kv = *plan->kv[m];
   const int cr = kv.cr, cs = kv.cs, lpr = kv.lpr;
@@ -437,7 +455,7 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   // matrix-core one the narrowest variant runs (fewest registers, so two
   // workgroups share a CU).
   const int route_cs = a.shared_mfma ? 1 : cs;
-  if ((e = moe::launch_route(d.act_fmt, route_cs, a, a.n_router_wg + a.n_shared_gu, s, ev(0), ev(1))) != hipSuccess)
+  if ((e = moe::launch_route(d.act_fmt, route_cs, a, a.n_router_wg + a.n_shared_gu, s, route_start, ev(1))) != hipSuccess)
     return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
   // gate_up: a grid-stride launch over the active slots' items.
   // With the routing computed in gate/up, one more workgroup publishes it.

@@ -39,7 +39,8 @@ enum : int { F32 = 0, BF16 = 1, AFF4 = 2, MXFP4 = 3, NVFP4 = 4 };
 // 32-element chunks) read adjacent 32-byte blocks.
 enum : int { F32P = 5 };
 enum : int { ROUTE_SOFTMAX = 0, ROUTE_SIGMOID_BIAS = 1, ROUTE_SIGMOID_LOGIT = 2 };
-enum : unsigned { NORM_TOPK = 1u, WEIGHT_BEFORE = 2u, SHARED = 4u, SHARED_GATED = 8u, OUT_F32 = 16u, GEGLU = 32u };
+enum : unsigned { NORM_TOPK = 1u, WEIGHT_BEFORE = 2u, SHARED = 4u, SHARED_GATED = 8u, OUT_F32 = 16u, GEGLU = 32u,
+                  PRE_NORM = 64u };
 
 constexpr int WAVE = 64;
 constexpr int THREADS = 256;            // route and gate/up: 4 waves per workgroup
@@ -109,7 +110,8 @@ struct Args {
   int sd_parts;            // parts of Is the shared down items split (partials in sy[part])
   int down_parts;          // parts of I each routed down row is split into (partials added in the blend)
   int max_rows;
-  const void *x;
+  const void *x;           // the experts' input (the row, or its pre-expert norm)
+  const void *xr;          // the router's input (the row as given)
   void *out;
   int32_t *idx_out;
   float *w_out;
@@ -1366,7 +1368,7 @@ __device__ __forceinline__ void router_part(const Args &a, int unit, int part, d
   const size_t xstride = (size_t)a.H * act_bytes(ACT);
   const char *wrow = e < a.E ? reinterpret_cast<const char *>(a.router) + (size_t)e * xstride
                              : reinterpret_cast<const char *>(a.sgv);
-  const char *x = reinterpret_cast<const char *>(a.x) + (size_t)r0 * xstride;
+  const char *x = reinterpret_cast<const char *>(a.xr) + (size_t)r0 * xstride;
   double acc[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = 0.0;
@@ -2342,6 +2344,74 @@ __global__ __launch_bounds__(DOWN_THREADS) void down_blend_kernel(Args a) {
   down_item<EF, ACT, CR, CS, LPR>(a, blockIdx.x);
 }
 
+
+// ================================================== pre-expert norm
+//
+// One workgroup per row: xe = x * w / sqrt(mean(x^2) + eps), in double (the
+// squares and products of stored values are exact), rounded once to the
+// activation format (bf16: to nearest, ties to even, from the double).
+
+// A double to bf16 bits, rounded to nearest (ties to even) in one step:
+// the double's significand is rounded to 8 bits on its bit pattern, which is
+// then exact in float.  Finite values in bf16's normal range.
+__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lsb = (u >> 45) & 1ull;
+  u = (u + 0x00000FFFFFFFFFFFull + lsb) & ~0x00001FFFFFFFFFFFull;
+  return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)u)) >> 16);
+}
+
+template <int ACT>
+__global__ __launch_bounds__(256) void pre_norm_kernel(Args a, const void *w, float eps, void *xe) {
+  constexpr int EPC = ACT == F32 ? 4 : 8;   // elements per 16-byte chunk
+  __shared__ double s_part[4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, nch = H / EPC;
+  const size_t rb = (size_t)H * act_bytes(ACT);
+  const char *xrow = reinterpret_cast<const char *>(a.xr) + (size_t)r * rb;
+  auto elems = [&](const u32x4 &q, double (&v)[EPC]) {
+    if constexpr (ACT == F32) {
+      v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+      v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+    } else {
+      v[0] = bf_lo(q.x); v[1] = bf_hi(q.x); v[2] = bf_lo(q.y); v[3] = bf_hi(q.y);
+      v[4] = bf_lo(q.z); v[5] = bf_hi(q.z); v[6] = bf_lo(q.w); v[7] = bf_hi(q.w);
+    }
+  };
+  double ss = 0.0;
+  for (int c = tid; c < nch; c += 256) {
+    double v[EPC];
+    elems(ld16(xrow + (size_t)c * 16), v);
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) ss = __builtin_fma(v[i], v[i], ss);
+  }
+  ss = wave_sum_f64(ss);
+  if (lane == 0) s_part[wave] = ss;
+  __syncthreads();
+  const double tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+  const double inv = 1.0 / __builtin_sqrt(tot / (double)H + (double)eps);
+  char *orow = reinterpret_cast<char *>(xe) + (size_t)r * rb;
+  for (int c = tid; c < nch; c += 256) {
+    double v[EPC], g[EPC];
+    elems(ld16(xrow + (size_t)c * 16), v);
+    elems(ld16(reinterpret_cast<const char *>(w) + (size_t)c * 16), g);
+    if constexpr (ACT == F32) {
+      u32x4 o;
+      o.x = __float_as_uint((float)(v[0] * g[0] * inv));
+      o.y = __float_as_uint((float)(v[1] * g[1] * inv));
+      o.z = __float_as_uint((float)(v[2] * g[2] * inv));
+      o.w = __float_as_uint((float)(v[3] * g[3] * inv));
+      *reinterpret_cast<u32x4 *>(orow + (size_t)c * 16) = o;
+    } else {
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = (uint32_t)f64_to_bf16(v[2 * i] * g[2 * i] * inv) |
+               ((uint32_t)f64_to_bf16(v[2 * i + 1] * g[2 * i + 1] * inv) << 16);
+      *reinterpret_cast<u32x4 *>(orow + (size_t)c * 16) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  }
+}
 
 // ================================================== grouped path (m > 32)
 //

@@ -53,6 +53,9 @@ struct FormatKernels {
 hipError_t launch_route(int act, int cs, const Args &a, int blocks, hipStream_t st, hipEvent_t start,
                         hipEvent_t stop);
 hipError_t launch_clear_sync(unsigned *sync, int n, hipStream_t st);
+// The pre-expert norm of the m rows into xe (one workgroup per row).
+hipError_t launch_pre_norm(int act, const Args &a, const void *w, float eps, void *xe, hipStream_t st,
+                           hipEvent_t start);
 // Grouped path (m > 32): top-k with the sort, and the blend.
 hipError_t launch_topk_sort(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_blend_grouped(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop);

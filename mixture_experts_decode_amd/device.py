@@ -30,12 +30,14 @@ def desc_of(spec: LayerSpec, max_rows: Optional[int] = None, out_f32: bool = Fal
         flags |= md.MOE_OUT_F32
     if spec.activation == "gelu":
         flags |= md.MOE_GEGLU
+    if spec.pre_expert_norm:
+        flags |= md.MOE_PRE_EXPERT_NORM
     return md.moe_decode_desc(
         hidden=spec.hidden, num_experts=spec.num_experts, top_k=spec.top_k, inter=spec.inter,
         shared_inter=spec.shared_inter if spec.shared else 0,
         max_rows=max_rows or spec.max_rows, act_fmt=md.FORMATS[spec.act_fmt],
         expert_fmt=md.FORMATS[spec.expert_fmt], routing=md.ROUTINGS[spec.routing], flags=flags,
-        routed_scaling_factor=spec.routed_scaling_factor)
+        routed_scaling_factor=spec.routed_scaling_factor, norm_eps=spec.norm_eps)
 
 
 def to_device(a: Optional[np.ndarray], device) -> Optional[torch.Tensor]:
@@ -84,7 +86,7 @@ class _Copy:
             sh_gate_w=p(tensors.get("sh_gate")), sh_up_w=p(tensors.get("sh_up")),
             sh_down_w=p(tensors.get("sh_down")), sh_gate_vec=p(tensors.get("sh_gate_vec")),
             gate_scale2=p(tensors.get("gate_s2")), up_scale2=p(tensors.get("up_s2")),
-            down_scale2=p(tensors.get("down_s2")))
+            down_scale2=p(tensors.get("down_s2")), pre_norm_w=p(tensors.get("pre_norm_w")))
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in self.t.values() if t is not None)
@@ -112,6 +114,7 @@ class DeviceLayer:
             "sh_gate": to_device(layer.sh_gate, device), "sh_up": to_device(layer.sh_up, device),
             "sh_down": to_device(layer.sh_down, device),
             "sh_gate_vec": to_device(layer.sh_gate_vec, device),
+            "pre_norm_w": to_device(layer.pre_norm_w, device),
         }
         for name in ("gate", "up", "down"):
             proj = getattr(layer, name)

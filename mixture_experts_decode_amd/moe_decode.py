@@ -35,6 +35,7 @@ MOE_SHARED = 4
 MOE_SHARED_GATED = 8
 MOE_OUT_F32 = 16
 MOE_GEGLU = 32
+MOE_PRE_EXPERT_NORM = 64
 
 
 class MoeDecodeError(RuntimeError):
@@ -47,21 +48,21 @@ class moe_decode_desc(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("num_experts", C.c_int32), ("top_k", C.c_int32),
                 ("inter", C.c_int32), ("shared_inter", C.c_int32), ("max_rows", C.c_int32),
                 ("act_fmt", C.c_int32), ("expert_fmt", C.c_int32), ("routing", C.c_int32),
-                ("flags", C.c_uint32), ("routed_scaling_factor", C.c_float)]
+                ("flags", C.c_uint32), ("routed_scaling_factor", C.c_float), ("norm_eps", C.c_float)]
 
 
 class moe_decode_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "router_w", "expert_bias", "gate_w", "up_w", "down_w", "gate_s", "up_s", "down_s",
         "gate_b", "up_b", "down_b", "sh_gate_w", "sh_up_w", "sh_down_w", "sh_gate_vec",
-        "gate_scale2", "up_scale2", "down_scale2")]
+        "gate_scale2", "up_scale2", "down_scale2", "pre_norm_w")]
 
 
 class moe_decode_ws_layout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in (
         "logits", "topk_idx", "topk_w", "row_gate", "sorted_pair", "expert_offsets",
         "pair_to_perm", "active_experts", "active_count", "slot_info", "act", "shared_act", "shared_y",
-        "routed_y", "sync", "total")]
+        "routed_y", "normed_x", "sync", "total")]
 
 
 _lib = None

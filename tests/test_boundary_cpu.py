@@ -107,7 +107,9 @@ def _check_plan_and_layout(spec):
                   (L.shared_act, spec.max_rows * (spec.shared_inter if spec.shared else 0) * 4),
                   (L.shared_y, max(1, spec.shared_inter // 2048) * spec.max_rows
                    * (spec.hidden if spec.shared else 0) * 4),
-                  (L.routed_y, te * spec.hidden * 4 if spec.max_rows > 32 else 0)]
+                  (L.routed_y, te * spec.hidden * 4 if spec.max_rows > 32 else 0),
+                  (L.normed_x, spec.max_rows * spec.hidden * (4 if spec.act_fmt == "f32" else 2)
+                   if spec.pre_expert_norm else 0)]
         spans = sorted((o, o + max(n, 1)) for o, n in fields)
         for (a0, a1), (b0, _) in zip(spans, spans[1:]):
             assert a1 <= b0, "workspace arrays overlap"
@@ -205,6 +207,27 @@ def test_nvfp4_needs_scales_and_second_level_scales():
     with pytest.raises(md.MoeDecodeError) as ei:
         md.moe_decode_plan(_desc(expert_fmt=md.MOE_NVFP4_B16, hidden=2048 + 16))
     assert ei.value.status == md.MOE_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b_bf16", "tiny_f32"])
+def test_plan_and_layout_pre_expert_norm(name):
+    _check_plan_and_layout(synth.WORKLOADS[name].replace(pre_expert_norm=True))
+
+
+def test_pre_expert_norm_validation():
+    for eps in (-1.0, float("nan"), float("inf")):
+        with pytest.raises(md.MoeDecodeError) as ei:
+            md.moe_decode_plan(_desc(flags=md.MOE_NORM_TOPK | md.MOE_PRE_EXPERT_NORM, norm_eps=eps))
+        assert ei.value.status == md.MOE_EINVAL, eps
+    plan, ws = md.moe_decode_plan(_desc(flags=md.MOE_NORM_TOPK | md.MOE_PRE_EXPERT_NORM, norm_eps=1e-6))
+    try:
+        w = _weights_stub()
+        w.pre_norm_w = None
+        with pytest.raises(md.MoeDecodeError) as ei:
+            md.moe_decode_forward(plan, w, 4096, 1, 4096, None, None, 4096 * 256, ws, 0)
+        assert ei.value.status == md.MOE_EINVAL
+    finally:
+        md.moe_decode_plan_destroy(plan)
 
 
 def test_single_launch_arrangement_is_refused(monkeypatch):

@@ -91,6 +91,19 @@ def test_grouped_geglu(fmt):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+def test_grouped_pre_expert_norm(fmt):
+    spec = small(hidden=256, num_experts=12, top_k=3, inter=192, shared_inter=160, expert_fmt=fmt,
+                 pre_expert_norm=True, shared=True, shared_gated=True, rows=(80,))
+    layer = synth.make_layer(spec, seed=650 + len(fmt), threads=4)
+    x = layer.x(0)
+    for out_f32 in (False, True):
+        dl = DeviceLayer(layer, out_f32=out_f32)
+        grouped_rows(dl, layer, x, (33, 80), f"pre-norm {fmt} f32out={out_f32}", out_f32)
+        del dl
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("E,k,inter,hidden", [(256, 16, 64, 128), (2, 1, 96, 160), (4, 4, 128, 64),
                                               (1, 1, 64, 96)])
 def test_grouped_pair_extremes(E, k, inter, hidden):

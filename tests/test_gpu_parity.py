@@ -215,6 +215,28 @@ def test_small_geglu(act, fmt, routing):
             check(spec, got, idx, w, ref, m, tol, f"geglu {act}/{fmt} m={m}")
 
 
+@pytest.mark.parametrize("act,fmt,routing,before", [("bf16", "bf16", "softmax", False),
+                                                   ("bf16", "nvfp4", "sigmoid_bias", True),
+                                                   ("bf16", "aff4", "softmax", False),
+                                                   ("f32", "f32", "sigmoid_logit", True)])
+def test_small_pre_expert_norm(act, fmt, routing, before):
+    # The experts read the RMS-normed rows (written in the activation format),
+    # the router and the shared gate the raw rows.
+    spec = small(act_fmt=act, expert_fmt=fmt, routing=routing, weight_before_ffn=before,
+                 pre_expert_norm=True, shared=True, shared_gated=True,
+                 norm_topk=routing != "sigmoid_logit")
+    layer = synth.make_layer(spec, seed=700 + len(fmt) + len(routing) + before, threads=4)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    for out_f32 in (False, True):
+        dl = DeviceLayer(layer, out_f32=out_f32)
+        for m in (1, 5, 8):
+            say(f"[gpu] pre-norm {act}/{fmt}/{routing}/before={before} m={m} f32out={out_f32}")
+            got, idx, w = run(dl, x, m)
+            tol = TOL[act] if not out_f32 else (TOL_OUT_F32 if act == "bf16" else TOL["f32"])
+            check(spec, got, idx, w, ref, m, tol, f"pre-norm {act}/{fmt} m={m}")
+
+
 def test_every_row_count_and_pass_variant():
     spec = small(hidden=256, num_experts=16, top_k=4, inter=128, shared=True, shared_gated=True,
                  shared_inter=96, rows=(32,))
