@@ -283,8 +283,10 @@ moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *st
   const moe::FormatKernels &k = kernels_for(d.act_fmt, d.expert_fmt);
   const int m = a.m;
   const bool shared = (d.flags & MOE_SHARED) != 0;
-  a.route_in_gu = 1;   // the route launch stops after the logits
-  a.n_router = (d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0)) * ((m + 7) / 8);
+  a.route_in_gu = 1;
+  // Router tiles: RT_E router rows x 8 input rows per unit.
+  const int nrows = d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0);
+  a.n_router = (nrows + moe::RT_E - 1) / moe::RT_E * ((m + 7) / 8);
   a.n_router_wg = (a.n_router + moe::ROUTE_UNITS_PER_WG - 1) / moe::ROUTE_UNITS_PER_WG;
   a.n_shared_gu = 0;
   a.shared_mfma = 0;
@@ -293,7 +295,7 @@ moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *st
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto ev = [&](int i) -> hipEvent_t { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
   hipError_t e;
-  if ((e = moe::launch_route(d.act_fmt, 1, a, a.n_router_wg, s, route_start, nullptr)) != hipSuccess)
+  if ((e = moe::launch_route_tile(d.act_fmt, a, a.n_router_wg, s, route_start)) != hipSuccess)
     return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
   if ((e = moe::launch_topk_sort(a, (m + moe::ROUTE_WPB - 1) / moe::ROUTE_WPB, s, nullptr, ev(1))) != hipSuccess)
     return fail(MOE_EHIP, "top-k launch: %s", hipGetErrorString(e));

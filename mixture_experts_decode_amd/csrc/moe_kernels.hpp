@@ -1420,6 +1420,74 @@ __device__ __forceinline__ void router_part(const Args &a, int unit, int part, d
   for (int r = 0; r < 8; ++r) tot[r] = r < nr ? wave_sum_f64(acc[r]) : 0.0;
 }
 
+// Router tile for many rows (the grouped path): unit u = (block of RT_E
+// router rows, block of up to 8 input rows), so each input chunk serves RT_E
+// router rows; otherwise as router_part.  tot[j][r]: router row j of the
+// block, input row r (0 past the last row or router row).
+constexpr int RT_E = 4;
+template <int ACT>
+__device__ __forceinline__ void router_tile(const Args &a, int unit, int part, double (&tot)[RT_E][8]) {
+  constexpr int EPC = ACT == F32 ? 4 : 8;
+  const int lane = threadIdx.x & 63;
+  const int nrows = a.E + ((a.flags & SHARED_GATED) ? 1 : 0);
+  const int nbe = (nrows + RT_E - 1) / RT_E;
+  const int eb = unit % nbe, r0 = (unit / nbe) * 8;
+  const int nr = min(8, a.m - r0);
+  const int nchunks = a.H / EPC;
+  const int c0 = part * nchunks / RSPLIT, c1 = (part + 1) * nchunks / RSPLIT;
+  const size_t xstride = (size_t)a.H * act_bytes(ACT);
+  const char *wrow[RT_E];
+#pragma unroll
+  for (int j = 0; j < RT_E; ++j) {
+    const int e = min(eb * RT_E + j, nrows - 1);
+    wrow[j] = e < a.E ? reinterpret_cast<const char *>(a.router) + (size_t)e * xstride
+                      : reinterpret_cast<const char *>(a.sgv);
+  }
+  const char *x = reinterpret_cast<const char *>(a.xr) + (size_t)r0 * xstride;
+  double acc[RT_E][8];
+#pragma unroll
+  for (int j = 0; j < RT_E; ++j)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[j][r] = 0.0;
+  for (int base = c0; base < c1; base += WAVE) {
+    const int ch = base + lane;
+    if (ch < c1) {
+      u32x4 q[RT_E], v[8];
+#pragma unroll
+      for (int j = 0; j < RT_E; ++j) q[j] = ld16(wrow[j] + (size_t)ch * 16);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = ld16(x + (size_t)min(r, nr - 1) * xstride + (size_t)ch * 16);
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) {
+        double xv[8], wv[RT_E];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const u32x4 &u = v[r];
+          const uint32_t d = (ACT == F32) ? (i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w)
+                                          : ((i >> 1) == 0 ? u.x : (i >> 1) == 1 ? u.y : (i >> 1) == 2 ? u.z : u.w);
+          xv[r] = ACT == F32 ? (double)__uint_as_float(d) : (double)((i & 1) ? bf_hi(d) : bf_lo(d));
+        }
+#pragma unroll
+        for (int j = 0; j < RT_E; ++j) {
+          const u32x4 &u = q[j];
+          const uint32_t d = (ACT == F32) ? (i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w)
+                                          : ((i >> 1) == 0 ? u.x : (i >> 1) == 1 ? u.y : (i >> 1) == 2 ? u.z : u.w);
+          wv[j] = ACT == F32 ? (double)__uint_as_float(d) : (double)((i & 1) ? bf_hi(d) : bf_lo(d));
+        }
+#pragma unroll
+        for (int j = 0; j < RT_E; ++j)
+#pragma unroll
+          for (int r = 0; r < 8; ++r) acc[j][r] = __builtin_fma(wv[j], xv[r], acc[j][r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < RT_E; ++j)
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      tot[j][r] = (r < nr && eb * RT_E + j < nrows) ? wave_sum_f64(acc[j][r]) : 0.0;
+}
+
 // --------------------------------------------------------- top-k and sort
 //
 // Routing state of one forward, built in LDS by the router workgroup that
@@ -2247,6 +2315,39 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
                                    a.m, nullptr, nullptr, a.sact, a.Is);
 }
 
+// The router units only, as tiles of RT_E router rows (the grouped path).
+template <int ACT>
+__global__ __launch_bounds__(ROUTE_THREADS) void route_tile_kernel(Args a) {
+  __shared__ double s_part[ROUTE_WPB][RT_E * 8];
+  const int item = blockIdx.x, tid = threadIdx.x;
+  const int wave = uniform_i(threadIdx.x >> 6);
+  const int unit = item * ROUTE_UNITS_PER_WG + wave / RSPLIT, part = wave % RSPLIT;
+  const bool live = unit < a.n_router;
+  double tot[RT_E][8];
+  if (live) router_tile<ACT>(a, unit, part, tot);
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int j = 0; j < RT_E; ++j)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) s_part[wave][j * 8 + r] = live ? tot[j][r] : 0.0;
+  }
+  __syncthreads();
+  if (tid < ROUTE_UNITS_PER_WG * RT_E * 8) {
+    const int ul = tid / (RT_E * 8), o = tid % (RT_E * 8), j = o / 8, r = o % 8;
+    const int u = item * ROUTE_UNITS_PER_WG + ul;
+    const int nrows = a.E + ((a.flags & SHARED_GATED) ? 1 : 0);
+    const int nbe = (nrows + RT_E - 1) / RT_E;
+    const int e = (u % nbe) * RT_E + j, rr = (u / nbe) * 8 + r;
+    if (u < a.n_router && rr < a.m && e < nrows) {
+      double t = s_part[ul * RSPLIT][o];
+#pragma unroll
+      for (int p = 1; p < RSPLIT; ++p) t += s_part[ul * RSPLIT + p][o];
+      a.logits[(size_t)rr * (a.E + 1) + e] = t;
+    }
+  }
+}
+
+
 // Launch 2: items (active slot s, row block b), blockIdx, blockIdx +
 // gridDim, ... of the nact * items_per_slot that exist; its waves take row
 // groups b * 4 + wave of slot s.  Either the routing is published (the first
@@ -2458,7 +2559,9 @@ __global__ __launch_bounds__(ROUTE_THREADS) void topk_sort_kernel(Args a) {
     if (lane < k) {
       const float wf = (float)(w * (double)a.rsf);
       const int p = r * k + lane;
-      a.topk_idx[p] = e;
+      // The sort below reads the selections of every workgroup: they go
+      // through device-coherent stores.
+      __hip_atomic_store(a.topk_idx + p, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       a.topk_w[p] = wf;
       if (a.idx_out) a.idx_out[p] = e;
       if (a.w_out) a.w_out[p] = wf;
@@ -2466,21 +2569,22 @@ __global__ __launch_bounds__(ROUTE_THREADS) void topk_sort_kernel(Args a) {
     if (lane == 0 && (a.flags & SHARED_GATED))
       a.row_gate[r] = (float)sigmoid_d(load_coherent(a.logits + (size_t)r * (E + 1) + E));
   }
-  // Release this workgroup's selections, then take a ticket; only the
-  // workgroup that takes the last one goes on (nobody waits).
-  __threadfence();
+  // Complete this workgroup's stores, then take a ticket; only the workgroup
+  // that takes the last one goes on (nobody waits).  The selections travel
+  // only through device-coherent accesses, so no cache-wide fence is needed.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0)
     s_ticket = __hip_atomic_fetch_add(a.sync + SYNC_TOPK_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (s_ticket != gridDim.x - 1) return;
-  __threadfence();   // acquire: every other workgroup's selections
   SortLDS &S = sm.s;
   constexpr int RW = MAX_ROWS_G / 32;
   for (int i = tid; i < MAX_EXPERTS * RW; i += ROUTE_THREADS) (&S.rows[0][0])[i] = 0u;
   __syncthreads();
   for (int p = tid; p < te; p += ROUTE_THREADS) {
-    const int e = clamp_i(a.topk_idx[p], 0, E - 1), rr = p / k;
+    const int e = clamp_i(__hip_atomic_load(a.topk_idx + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0, E - 1);
+    const int rr = p / k;
     atomicOr(&S.rows[e][rr >> 5], 1u << (rr & 31));
   }
   __syncthreads();
@@ -2522,7 +2626,8 @@ __global__ __launch_bounds__(ROUTE_THREADS) void topk_sort_kernel(Args a) {
   }
   __syncthreads();
   for (int p = tid; p < te; p += ROUTE_THREADS) {
-    const int e = clamp_i(a.topk_idx[p], 0, E - 1), rr = p / k;
+    const int e = clamp_i(__hip_atomic_load(a.topk_idx + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0, E - 1);
+    const int rr = p / k;
     int before = __popc(S.rows[e][rr >> 5] & ((1u << (rr & 31)) - 1u));
     for (int j = 0; j < (rr >> 5); ++j) before += __popc(S.rows[e][j]);
     const int pos = S.off[e] + before;

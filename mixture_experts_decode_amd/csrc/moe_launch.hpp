@@ -53,6 +53,8 @@ struct FormatKernels {
 hipError_t launch_route(int act, int cs, const Args &a, int blocks, hipStream_t st, hipEvent_t start,
                         hipEvent_t stop);
 hipError_t launch_clear_sync(unsigned *sync, int n, hipStream_t st);
+// The grouped path's router: units of RT_E router rows x 8 input rows.
+hipError_t launch_route_tile(int act, const Args &a, int blocks, hipStream_t st, hipEvent_t start);
 // The pre-expert norm of the m rows into xe (one workgroup per row).
 hipError_t launch_pre_norm(int act, const Args &a, const void *w, float eps, void *xe, hipStream_t st,
                            hipEvent_t start);

@@ -27,6 +27,11 @@ hipError_t launch_route(int act, int cs, const Args &a, int blocks, hipStream_t 
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_route_tile(int act, const Args &a, int blocks, hipStream_t st, hipEvent_t t0) {
+  if (act == F32) return launch_timed(route_tile_kernel<F32>, blocks, ROUTE_THREADS, st, t0, nullptr, a);
+  return launch_timed(route_tile_kernel<BF16>, blocks, ROUTE_THREADS, st, t0, nullptr, a);
+}
+
 hipError_t launch_pre_norm(int act, const Args &a, const void *w, float eps, void *xe, hipStream_t st,
                            hipEvent_t t0) {
   if (act == F32) return launch_timed(pre_norm_kernel<F32>, a.m, 256, st, t0, nullptr, a, w, eps, xe);
