@@ -71,8 +71,7 @@ constexpr int G_THREADS = 512;
 constexpr int G_WPB = G_THREADS / WAVE;
 constexpr int G_NCT = 2;                // column tiles of 16 pairs per pass
 constexpr int G_COLS = 16 * G_NCT;
-constexpr int G_MU = 2;
-constexpr bool G_QDIRECT = true;        // 4-bit grouped down: codes straight into the operands                 // k steps of 32 per staged batch (registers: two workgroups per CU)
+constexpr int G_MU = 2;                 // k steps of 32 per staged batch (registers: two workgroups per CU)
 
 // Rows of intermediate per gate/up wave: 2 for 16-byte-per-8-or-4 element
 // formats; 4 for the 4-bit ones (their rows are 4x shorter) with one vector
@@ -1095,39 +1094,70 @@ __device__ __forceinline__ void dequant32(const u32x4 &q, uint32_t s, u32x4 (&o)
 }
 
 // mfma_slice_v with 4-bit weights A[j] (K = the matrices' row length).
+// A batch of two k steps is 16 rows x 64 codes = 512 bytes per matrix: lane
+// l loads 8 bytes (16 codes: row l / 4, k step (l / 2) % 2, half l % 2).
+template <int WF>
+__device__ __forceinline__ void dequant16(const u32x2 &q, uint32_t s, u32x4 (&o)[2]) {
+  if constexpr (WF == MXFP4) {
+    const float sc = e8m0_to_f32(s & 0xFFu);   // a power of two: the scaled conversion is exact
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const uint32_t qd = d == 0 ? q.x : q.y;
+      o[d] = u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(qd, sc, 0)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(qd, sc, 1)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(qd, sc, 2)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(qd, sc, 3))};
+    }
+  } else {
+    const float sc = e4m3_to_f32(s & 0xFFu);
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const uint32_t qd = d == 0 ? q.x : q.y;
+      uint32_t pr[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x2 v = t == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 0)
+                      : t == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 1)
+                      : t == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 2)
+                               : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 3);
+        const uint32_t x0 = __float_as_uint(v.x * sc), x1 = __float_as_uint(v.y * sc);
+        pr[t] = (x0 >> 16) | (x1 & 0xFFFF0000u);
+      }
+      o[d] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+    }
+  }
+}
+
 template <int WF, int XF, int NA, int NCT, int MU>
 __device__ __forceinline__ void mfma_slice_q(const QMat<WF> (&A)[NA], int K, int n0, int N,
                                              const char *const (&xv)[NCT], int kb, int ke, char *stage,
                                              f32x4 (&acc)[NA][NCT]) {
   constexpr int ROW = MU * 64 + 16, STAGE = 16 * ROW;
-  static_assert(MU <= MF_U, "the wave's staging region holds MF_U k-steps");
+  static_assert(MU == 2, "two k steps per batch");
   static_assert(WF == MXFP4 || WF == NVFP4, "4-bit formats");
   constexpr int XB = XF == F32 ? 4 : 2;
   constexpr int XL = XF == F32 ? 2 : 1;
   const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
-  const bool loader = l < 16 * MU;
-  const int qrow = min(n0 + l / MU, N - 1), qk = l % MU;   // this lane's row and k step
-  const int qoff = qrow * (K / 2) + qk * 16;
-  const int soff = WF == NVFP4 ? qrow * (K / 16) + qk * 2 : qrow * (K / 32) + qk;
+  const int lr = l >> 2, ks = (l >> 1) & 1, hh = l & 1;
+  const int qrow = min(n0 + lr, N - 1);
+  const int qoff = qrow * (K / 2) + ks * 16 + hh * 8;
+  const int soff = WF == NVFP4 ? qrow * (K / 16) + ks * 2 + hh : qrow * (K / 32) + ks;
 #pragma unroll
   for (int j = 0; j < NA; ++j)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (kb >= ke) return;
-  u32x4 nq[NA], nxb[MU][NCT][XL];
+  u32x2 nq[NA];
+  u32x4 nxb[MU][NCT][XL];
   uint32_t ns[NA];
   auto fetch = [&](int kq) {
-    if (loader) {
 #pragma unroll
-      for (int j = 0; j < NA; ++j) {
-        // Row batches of 16 MU bytes: the default policy keeps the rest of
-        // each line for the following batches.
-        nq[j] = __builtin_amdgcn_raw_buffer_load_b128(A[j].w, qoff + kq / 2, 0, 0);
-        if constexpr (WF == NVFP4)
-          ns[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].s, soff + kq / 16, 0, 0);
-        else
-          ns[j] = __builtin_amdgcn_raw_buffer_load_b8(A[j].s, soff + kq / 32, 0, 0);
-      }
+    for (int j = 0; j < NA; ++j) {
+      nq[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(A[j].w, qoff + kq / 2, 0, 0));
+      if constexpr (WF == NVFP4)
+        ns[j] = __builtin_amdgcn_raw_buffer_load_b8(A[j].s, soff + kq / 16, 0, 0);
+      else
+        ns[j] = __builtin_amdgcn_raw_buffer_load_b8(A[j].s, soff + kq / 32, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
@@ -1135,17 +1165,13 @@ __device__ __forceinline__ void mfma_slice_q(const QMat<WF> (&A)[NA], int K, int
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int h = 0; h < XL; ++h) nxb[u][ct][h] = ld16(xv[ct] + (size_t)kk * XB + 16 * h);
+        for (int hx = 0; hx < XL; ++hx) nxb[u][ct][hx] = ld16(xv[ct] + (size_t)kk * XB + 16 * hx);
     }
   };
-#pragma unroll
-  for (int j = 0; j < NA; ++j) {
-    nq[j] = u32x4{0u, 0u, 0u, 0u};
-    ns[j] = 0u;
-  }
   fetch(kb);
   for (int k0 = kb; k0 < ke; k0 += 32 * MU) {
-    u32x4 cq[NA], bv[MU][NCT][XL];
+    u32x2 cq[NA];
+    u32x4 bv[MU][NCT][XL];
     uint32_t cs[NA];
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
@@ -1157,18 +1183,16 @@ __device__ __forceinline__ void mfma_slice_q(const QMat<WF> (&A)[NA], int K, int
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int h = 0; h < XL; ++h) bv[u][ct][h] = nxb[u][ct][h];
+        for (int hx = 0; hx < XL; ++hx) bv[u][ct][hx] = nxb[u][ct][hx];
     const int k1 = k0 + 32 * MU;
     if (k1 < ke) fetch(k1);
-    if (loader) {
 #pragma unroll
-      for (int j = 0; j < NA; ++j) {
-        u32x4 o[4];
-        dequant32<WF>(cq[j], cs[j], o);
+    for (int j = 0; j < NA; ++j) {
+      u32x4 o[2];
+      dequant16<WF>(cq[j], cs[j], o);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          *reinterpret_cast<u32x4 *>(stage + j * STAGE + (l / MU) * ROW + qk * 64 + 16 * t) = o[t];
-      }
+      for (int t = 0; t < 2; ++t)
+        *reinterpret_cast<u32x4 *>(stage + j * STAGE + lr * ROW + ks * 64 + hh * 32 + 16 * t) = o[t];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -2829,17 +2853,11 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
   auto pass = [&](auto nct, int c0, int nv) {
     constexpr int NCT = decltype(nct)::value;
     f32x4 acc[NA][NCT];
-    if (quant && G_QDIRECT) {
+    if (quant) {   // 4-bit codes straight into the operands
       const char *xr[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) xr[ct] = xb + (size_t)(c0 + min(16 * ct + (lane & 15), nv - 1)) * K * 4;
       mfma_slice_qd<QF, F32, NA, NCT, 2>(Q, K, 0, 16, xr, kb, ke, acc);
-    } else if (quant) {
-      const char *xv[NCT];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        xv[ct] = xb + (size_t)(c0 + min(16 * ct + (lane & 15), nv - 1)) * K * 4 + (size_t)(lane >> 4) * 32;
-      mfma_slice_q<QF, F32, NA, NCT, MU>(Q, K, 0, 16, xv, kb, ke, S.stage[w], acc);
     } else {
       mfma_slice<F32, NA, NCT, MU>(A, K * 2, 0, 16, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
                                    S.stage[w], acc);
