@@ -1043,12 +1043,11 @@ __device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA]
 }
 
 // 4-bit weights (MXFP4, NVFP4) on the matrix cores.  The loader brings a
-// batch of MU k steps of 16 rows as codes -- 16 bytes, one k step of one row,
-// per lane; lanes from 16 MU on load nothing -- with their block scales,
-// dequantises them to bf16 and stages them in the layout mfma_slice_v reads.
-// Both decodings are exact in bf16: E2M1 times a power of two (E8M0), and
-// E2M1 times E4M3 (at most 6 significant bits).  The NVFP4 second-level
-// scale is left to the caller.
+// batch of two k steps of 16 rows as codes -- 8 bytes (16 codes) per lane --
+// with their block scales, dequantises them to bf16 and stages them in the
+// layout mfma_slice_v reads.  Both decodings are exact in bf16: E2M1 times a
+// power of two (E8M0), and E2M1 times E4M3 (at most 6 significant bits).
+// The NVFP4 second-level scale is left to the caller.
 template <int WF> struct QMat {
   __amdgpu_buffer_rsrc_t w, s;   // codes [N, K/2], scale bytes [N, K/32] or [N, K/16]
 };
@@ -1059,38 +1058,6 @@ __device__ __forceinline__ QMat<WF> make_qmat(const void *w, const void *s, int 
   m.w = buf_rsrc(w, N * (K / 2));
   m.s = buf_rsrc(s, N * (K / (WF == NVFP4 ? 16 : 32)));
   return m;
-}
-
-// 32 codes of one row (code dword d: elements 8d .. 8d+7, low nibble first)
-// with their scale bits -> 32 bf16 values, o[d] = elements 8d .. 8d+7.
-template <int WF>
-__device__ __forceinline__ void dequant32(const u32x4 &q, uint32_t s, u32x4 (&o)[4]) {
-  float sc[2];
-  if constexpr (WF == MXFP4) {
-    sc[0] = sc[1] = e8m0_to_f32(s & 0xFFu);
-  } else {
-    sc[0] = e4m3_to_f32(s & 0xFFu);
-    sc[1] = e4m3_to_f32((s >> 8) & 0xFFu);
-  }
-  uint32_t pr[4][4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t qd = code_dword(q, d);
-    const float c = sc[d >> 1];
-    f32x2 v[4];
-    v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 0);
-    v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 1);
-    v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 2);
-    v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 3);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      // The products are bf16 values: their low 16 bits are zero.
-      const uint32_t a = __float_as_uint(v[t].x * c), b = __float_as_uint(v[t].y * c);
-      pr[d][t] = (a >> 16) | (b & 0xFFFF0000u);
-    }
-  }
-#pragma unroll
-  for (int d = 0; d < 4; ++d) o[d] = u32x4{pr[d][0], pr[d][1], pr[d][2], pr[d][3]};
 }
 
 // mfma_slice_v with 4-bit weights A[j] (K = the matrices' row length).
@@ -1302,16 +1269,26 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
         else sc = e4m3_to_f32(MU == 4 ? (cs[j] >> (8 * (u >> 1))) & 0xFFu : cs[j] & 0xFFu);
         const uint32_t qd = cq[j][u];
         uint32_t pr[4];
-        f32x2 v[4];
-        v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 0);
-        v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 1);
-        v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 2);
-        v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 3);
+        if constexpr (WF == MXFP4) {
+          // The E8M0 scale is a power of two: the scaled conversion is exact.
+          pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(qd, sc, 0));
+          pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(qd, sc, 1));
+          pr[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(qd, sc, 2));
+          pr[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(qd, sc, 3));
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          // Exact bf16 products: their low 16 bits are zero.
-          const uint32_t a = __float_as_uint(v[t].x * sc), b = __float_as_uint(v[t].y * sc);
-          pr[t] = valid ? (a >> 16) | (b & 0xFFFF0000u) : 0u;
+          for (int t = 0; t < 4; ++t) pr[t] = valid ? pr[t] : 0u;
+        } else {
+          f32x2 v[4];
+          v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 0);
+          v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 1);
+          v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 2);
+          v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 3);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            // Exact bf16 products: their low 16 bits are zero.
+            const uint32_t a = __float_as_uint(v[t].x * sc), b = __float_as_uint(v[t].y * sc);
+            pr[t] = valid ? (a >> 16) | (b & 0xFFFF0000u) : 0u;
+          }
         }
         av[j] = u32x4{pr[0], pr[1], pr[2], pr[3]};
       }
