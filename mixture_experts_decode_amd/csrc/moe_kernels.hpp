@@ -2830,11 +2830,11 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
   auto pass = [&](auto nct, int c0, int nv) {
     constexpr int NCT = decltype(nct)::value;
     f32x4 acc[NA][NCT];
-    if (quant) {   // 4-bit codes straight into the operands
-      const char *xr[NCT];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) xr[ct] = xb + (size_t)(c0 + min(16 * ct + (lane & 15), nv - 1)) * K * 4;
-      mfma_slice_qd<QF, F32, NA, NCT, 2>(Q, K, 0, 16, xr, kb, ke, acc);
+    if (quant) {   // 4-bit codes straight into the operands; passes of one column tile
+      if constexpr (NCT == 1) {
+        const char *xr[1] = {xb + (size_t)(c0 + min(lane & 15, nv - 1)) * K * 4};
+        mfma_slice_qd<QF, F32, NA, 1, 2>(Q, K, 0, 16, xr, kb, ke, acc);
+      }
     } else {
       mfma_slice<F32, NA, NCT, MU>(A, K * 2, 0, 16, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
                                    S.stage[w], acc);
@@ -2846,8 +2846,12 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
 #pragma unroll
         for (int i = 0; i < 4; ++i) S.part[w][j][ct][i][lane] = acc[j][ct][i];
   };
-  for (int c0 = 0; c0 < it.np; c0 += G_COLS) {
-    const int nv = min(G_COLS, it.np - c0);
+  // 4-bit passes take 16 pairs (one column tile): two tiles' inputs would
+  // cost a wave per SIMD in registers.  A pair's sum does not depend on the
+  // pass it is in.
+  const int step = quant ? 16 : G_COLS;
+  for (int c0 = 0; c0 < it.np; c0 += step) {
+    const int nv = min(step, it.np - c0);
     const int nct = nv > 16 ? 2 : 1;
     if (nct == 2) pass(std::integral_constant<int, 2>(), c0, nv);
     else pass(std::integral_constant<int, 1>(), c0, nv);
