@@ -32,8 +32,9 @@
  * m = 1..32 is the fused decode path the page describes (three launches).
  * m = 33..256 (prefill chunks, speculative-decoding verification) takes a
  * grouped path of the same steps whose expert products run on the matrix
- * cores (five launches); it needs bf16 activations, bf16 experts and H, I,
- * Is multiples of 32, which moe_decode_plan checks when max_rows > 32.  Each
+ * cores (five launches); it needs bf16 activations, bf16, mxfp4 or nvfp4
+ * experts and H, I, Is multiples of 32, which moe_decode_plan checks when
+ * max_rows > 32.  Each
  * path gives a row the same bits for every m it serves; the two paths agree
  * within the tolerance of their accumulation orders.
  *
