@@ -2789,7 +2789,10 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
   static_assert(down_grouped_threads<true>() == 256, "the launch bound above");
   constexpr int NW = down_grouped_threads<WIDE>() / WAVE;   // waves = parts of K
   constexpr int NA = WIDE ? G_DT : 1;                        // tiles per wave
-  constexpr int MU = WIDE ? 1 : G_MU;
+  // bf16 rows of at most 2048: two k steps per staged batch (longer runs per
+  // row beat the wave per SIMD they cost); 4-bit kernels keep one, so their
+  // shared-expert items do not set their register count.
+  constexpr int MU = WIDE ? (EF == BF16 ? 2 : 1) : G_MU;
   constexpr int COLS = down_grouped_cols<WIDE>();
   __shared__ MfmaLDS<NW, NA, MU> S;
   const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
