@@ -2617,7 +2617,21 @@ __global__ __launch_bounds__(ROUTE_THREADS) void topk_sort_kernel(Args a) {
       S.off[e] = pre_c;
       S.slot[e] = pre_a;
       a.offsets[e] = pre_c;
-      if (cnt > 0) a.active[pre_a] = e;
+      if (cnt > 0) {
+        // The slot's record: what the gate/up and down items need, in one load.
+        a.active[pre_a] = e;
+        SlotRec rec;
+        rec.e = e;
+        rec.off = pre_c;
+        rec.np = cnt;
+        rec.pad = 0;
+        rec.gw = a.gw[e]; rec.uw = a.uw[e]; rec.dw = a.dw[e];
+        rec.gs = a.gs ? a.gs[e] : 0ull; rec.us = a.gs ? a.us[e] : 0ull; rec.ds = a.gs ? a.ds[e] : 0ull;
+        rec.gb = a.gb ? a.gb[e] : 0ull; rec.ub = a.gb ? a.ub[e] : 0ull; rec.db = a.gb ? a.db[e] : 0ull;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) rec.pad2[i] = 0ull;
+        a.slots[pre_a] = rec;
+      }
       if (e == E - 1) {
         S.off[E] = pre_c + cnt;
         a.offsets[E] = pre_c + cnt;
@@ -2643,6 +2657,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void topk_sort_kernel(Args a) {
 struct GroupedItem {
   bool live, routed;
   int e, off, np, n0;
+  const void *gw, *uw, *gs, *us, *dw, *ds;   // the routed expert's matrices
 };
 
 __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int tiles) {
@@ -2653,9 +2668,16 @@ __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int
     const int nact = clamp_i(a.active_count[0], 0, a.cap);
     g.live = s < nact;
     g.routed = true;
-    g.e = uniform_i(clamp_i(a.active[min(s, a.cap - 1)], 0, a.E - 1));
-    g.off = uniform_i(clamp_i(a.offsets[g.e], 0, a.te));
-    g.np = uniform_i(clamp_i(a.offsets[g.e + 1], g.off, a.te)) - g.off;
+    const SlotRec &r = a.slots[min(s, a.cap - 1)];   // one record, requested with the count
+    g.e = uniform_i(clamp_i(r.e, 0, a.E - 1));
+    g.off = uniform_i(clamp_i(r.off, 0, a.te));
+    g.np = uniform_i(clamp_i(r.np, 0, a.te - g.off));
+    g.gw = reinterpret_cast<const void *>(uniform_u64(r.gw));
+    g.uw = reinterpret_cast<const void *>(uniform_u64(r.uw));
+    g.gs = reinterpret_cast<const void *>(uniform_u64(r.gs));
+    g.us = reinterpret_cast<const void *>(uniform_u64(r.us));
+    g.dw = reinterpret_cast<const void *>(uniform_u64(r.dw));
+    g.ds = reinterpret_cast<const void *>(uniform_u64(r.ds));
     g.n0 = (item - s * tiles) * 16;
   } else {
     g.live = (a.flags & SHARED) != 0;
@@ -2664,6 +2686,7 @@ __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int
     g.off = 0;
     g.np = a.m;
     g.n0 = (item - nrout) * 16;
+    g.gw = g.uw = g.gs = g.us = g.dw = g.ds = nullptr;
   }
   return g;
 }
@@ -2689,15 +2712,15 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
   const int N = it.routed ? a.I : a.Is;
   const int r0 = it.n0 * GT;                 // the item's first row
   const int n0 = r0 + 16 * (w % GT);         // this wave's 16 rows
-  const void *mg = it.routed ? tbl(a.gw, it.e) : a.sgw;
-  const void *mu = it.routed ? tbl(a.uw, it.e) : a.suw;
+  const void *mg = it.routed ? it.gw : a.sgw;
+  const void *mu = it.routed ? it.uw : a.suw;
   // bf16 rows (the shared expert's always): one resource per matrix.
   __amdgpu_buffer_rsrc_t A[2];
   QMat<QF> Q[2];
   const bool quant = EF != BF16 && it.routed;
   if (quant) {
-    Q[0] = make_qmat<QF>(mg, tbl(a.gs, it.e), N, H);
-    Q[1] = make_qmat<QF>(mu, tbl(a.us, it.e), N, H);
+    Q[0] = make_qmat<QF>(mg, it.gs, N, H);
+    Q[1] = make_qmat<QF>(mu, it.us, N, H);
   } else {
     A[0] = buf_rsrc(mg, N * H * 2);
     A[1] = buf_rsrc(mu, N * H * 2);
@@ -2800,7 +2823,7 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
   const GroupedItem it = grouped_item(a, blockIdx.x, (H + COLS - 1) / COLS);
   if (!it.live) return;
   const int K = it.routed ? a.I : a.Is;
-  const char *mat = reinterpret_cast<const char *>(it.routed ? tbl(a.dw, it.e) : a.sdw);
+  const char *mat = reinterpret_cast<const char *>(it.routed ? it.dw : a.sdw);
   const int h0 = it.n0 / 16 * COLS;   // the item's first column
   // One resource per tile, bounded to the tile's rows (a tile past H reads
   // nothing).
@@ -2809,7 +2832,7 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
   const bool quant = EF != BF16 && it.routed;
   float s2d = 1.0f;   // nvfp4: the down projection's second-level scale
   if (quant) {
-    const char *smat = reinterpret_cast<const char *>(tbl(a.ds, it.e));
+    const char *smat = reinterpret_cast<const char *>(it.ds);
     constexpr int SB = QF == NVFP4 ? 16 : 32;   // elements per scale byte
 #pragma unroll
     for (int j = 0; j < NA; ++j) {

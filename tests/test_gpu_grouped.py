@@ -26,7 +26,7 @@ def grouped_rows(dl, layer, x, rows, what, out_f32=False):
         say(f"[gpu] grouped {what} m={m}")
         got, idx, w = run(dl, x, m)
         check(spec, got, idx, w, ref, m, TOL_OUT_F32 if out_f32 else TOL["bf16"], f"{what} m={m}")
-        check_sort(dl, m, idx, records=m <= 32)
+        check_sort(dl, m, idx)
         outs[m] = got
     mmax = max(m for m in rows if m > 32)
     for m in rows:
