@@ -188,7 +188,7 @@ moe_status check_desc(const moe_decode_desc &d) {
   if (d.max_rows > moe::MAX_ROWS) {
     // The grouped path: bf16 matrix-core products over 32-wide k steps.
     if (d.act_fmt != MOE_BF16 || !kernels_for(d.act_fmt, d.expert_fmt).gate_up_grouped)
-      return fail(MOE_EUNSUPPORTED, "max_rows above %d needs bf16 activations and bf16, mxfp4 or nvfp4 experts",
+      return fail(MOE_EUNSUPPORTED, "max_rows above %d needs bf16 activations and bf16 or 4-bit experts",
                   moe::MAX_ROWS);
     if (d.hidden % 32 || d.inter % 32 || ((d.flags & MOE_SHARED) && d.shared_inter % 32))
       return fail(MOE_EUNSUPPORTED, "max_rows above %d needs hidden, inter and shared_inter multiples of 32",

@@ -1049,14 +1049,17 @@ __device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA]
 // power of two (E8M0), and E2M1 times E4M3 (at most 6 significant bits).
 // The NVFP4 second-level scale is left to the caller.
 template <int WF> struct QMat {
-  __amdgpu_buffer_rsrc_t w, s;   // codes [N, K/2], scale bytes [N, K/32] or [N, K/16]
+  // codes [N, K/2]; scale bytes [N, K/32] (mxfp4) or [N, K/16] (nvfp4), or
+  // bf16 scales and biases [N, K/64] (aff4)
+  __amdgpu_buffer_rsrc_t w, s, b;
 };
 
 template <int WF>
-__device__ __forceinline__ QMat<WF> make_qmat(const void *w, const void *s, int N, int K) {
+__device__ __forceinline__ QMat<WF> make_qmat(const void *w, const void *s, const void *b, int N, int K) {
   QMat<WF> m;
   m.w = buf_rsrc(w, N * (K / 2));
-  m.s = buf_rsrc(s, N * (K / (WF == NVFP4 ? 16 : 32)));
+  m.s = buf_rsrc(s, WF == AFF4 ? N * (K / 64) * 2 : N * (K / (WF == NVFP4 ? 16 : 32)));
+  m.b = WF == AFF4 ? buf_rsrc(b, N * (K / 64) * 2) : m.s;
   return m;
 }
 
@@ -1207,15 +1210,17 @@ template <int WF, int XF, int NA, int NCT, int MU>
 __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, int n0, int N,
                                               const char *const (&xr)[NCT], int kb, int ke,
                                               f32x4 (&acc)[NA][NCT]) {
-  static_assert(WF == MXFP4 || WF == NVFP4, "4-bit formats");
-  static_assert(MU == 1 || MU == 2 || MU == 4, "a lane's range lies in one E8M0 block");
+  static_assert(WF == MXFP4 || WF == NVFP4 || WF == AFF4, "4-bit formats");
+  static_assert(MU == 1 || MU == 2 || MU == 4, "a lane's range lies in one scale block");
   constexpr int CB = 4 * MU;                       // code bytes per lane per batch
   constexpr int XB = XF == F32 ? 4 : 2;
   constexpr int XQ = 8 * MU * XB / 16;             // 16-byte x loads per lane, batch and tile
   const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
   const int row = min(n0 + rr, N - 1);
   const int qoff = row * (K / 2) + g * CB;
-  const int soff = WF == NVFP4 ? row * (K / 16) + (8 * MU * g) / 16 : row * (K / 32) + (8 * MU * g) / 32;
+  const int soff = WF == NVFP4 ? row * (K / 16) + (8 * MU * g) / 16
+                 : WF == AFF4  ? row * (K / 64) * 2   // + 2 * the group of the lane's range
+                               : row * (K / 32) + (8 * MU * g) / 32;
 #pragma unroll
   for (int j = 0; j < NA; ++j)
 #pragma unroll
@@ -1223,7 +1228,7 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
   if (kb >= ke) return;
   typedef uint32_t cvec __attribute__((ext_vector_type(MU)));
   cvec nq[NA];
-  uint32_t ns[NA];
+  uint32_t ns[NA], nb[NA];
   u32x4 nx[NCT][XQ];
   auto fetch = [&](int kq) {
 #pragma unroll
@@ -1231,7 +1236,11 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
       if constexpr (MU == 4) nq[j] = __builtin_bit_cast(cvec, __builtin_amdgcn_raw_buffer_load_b128(A[j].w, qoff + kq / 2, 0, 0));
       else if constexpr (MU == 2) nq[j] = __builtin_bit_cast(cvec, __builtin_amdgcn_raw_buffer_load_b64(A[j].w, qoff + kq / 2, 0, 0));
       else nq[j] = __builtin_bit_cast(cvec, __builtin_amdgcn_raw_buffer_load_b32(A[j].w, qoff + kq / 2, 0, 0));
-      if constexpr (WF == NVFP4 && MU == 4) ns[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].s, soff + kq / 16, 0, 0);
+      if constexpr (WF == AFF4) {   // a lane's range lies in one 64-element group
+        const int go = soff + ((kq + 8 * MU * g) >> 6) * 2;
+        ns[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].s, go, 0, 0);
+        nb[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].b, go, 0, 0);
+      } else if constexpr (WF == NVFP4 && MU == 4) ns[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].s, soff + kq / 16, 0, 0);
       else if constexpr (WF == NVFP4) ns[j] = __builtin_amdgcn_raw_buffer_load_b8(A[j].s, soff + kq / 16, 0, 0);
       else ns[j] = __builtin_amdgcn_raw_buffer_load_b8(A[j].s, soff + kq / 32, 0, 0);
     }
@@ -1246,12 +1255,13 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
   fetch(kb);
   for (int k0 = kb; k0 < ke; k0 += 32 * MU) {
     cvec cq[NA];
-    uint32_t cs[NA];
+    uint32_t cs[NA], cb[NA];
     u32x4 cx[NCT][XQ];
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       cq[j] = nq[j];
       cs[j] = ns[j];
+      cb[j] = nb[j];
     }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -1261,15 +1271,39 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
       const bool valid = k0 + 8 * MU * g + 8 * u < ke;
-      u32x4 av[NA];
+      u32x4 av[NA], am[NA], al[NA];   // aff4: w = hi + mid + lo (bf16 each, 24 bits)
 #pragma unroll
       for (int j = 0; j < NA; ++j) {
-        float sc;
-        if constexpr (WF == MXFP4) sc = e8m0_to_f32(cs[j] & 0xFFu);
-        else sc = e4m3_to_f32(MU == 4 ? (cs[j] >> (8 * (u >> 1))) & 0xFFu : cs[j] & 0xFFu);
         const uint32_t qd = cq[j][u];
         uint32_t pr[4];
-        if constexpr (WF == MXFP4) {
+        if constexpr (WF == AFF4) {
+          // w = s q + b in float (s q is exact).  hi = w's top 16 bits, mid =
+          // the top 16 bits of w - hi, lo = the rest rounded to bf16 (every
+          // difference is exact): hi + mid + lo carries w's 24 bits, so the
+          // products are those of the float weights the vector path uses.
+          const float sc = bf16_to_f32((uint16_t)cs[j]), bi = bf16_to_f32((uint16_t)cb[j]);
+          uint32_t md[4], lo[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            uint32_t hb[2], mb[2], lb[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const float w = __builtin_fmaf(sc, (float)((qd >> (8 * t + 4 * e)) & 0xFu), bi);
+              const uint32_t h = __float_as_uint(w) & 0xFFFF0000u;
+              const float r = w - __uint_as_float(h);
+              const uint32_t m = __float_as_uint(r) & 0xFFFF0000u;
+              hb[e] = h;
+              mb[e] = m;
+              lb[e] = (uint32_t)f32_to_bf16(r - __uint_as_float(m)) << 16;
+            }
+            pr[t] = valid ? (hb[0] >> 16) | hb[1] : 0u;
+            md[t] = valid ? (mb[0] >> 16) | mb[1] : 0u;
+            lo[t] = valid ? (lb[0] >> 16) | lb[1] : 0u;
+          }
+          am[j] = u32x4{md[0], md[1], md[2], md[3]};
+          al[j] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        } else if constexpr (WF == MXFP4) {
+          const float sc = e8m0_to_f32(cs[j] & 0xFFu);
           // The E8M0 scale is a power of two: the scaled conversion is exact.
           pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(qd, sc, 0));
           pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(qd, sc, 1));
@@ -1278,6 +1312,7 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
 #pragma unroll
           for (int t = 0; t < 4; ++t) pr[t] = valid ? pr[t] : 0u;
         } else {
+          const float sc = e4m3_to_f32(MU == 4 ? (cs[j] >> (8 * (u >> 1))) & 0xFFu : cs[j] & 0xFFu);
           f32x2 v[4];
           v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 0);
           v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qd, 1.0f, 1);
@@ -1297,7 +1332,13 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
         if constexpr (XF == BF16) {
           const bf16x8 bb = __builtin_bit_cast(bf16x8, cx[ct][u]);
 #pragma unroll
-          for (int j = 0; j < NA; ++j) acc[j][ct] = mfma16(av[j], bb, acc[j][ct]);
+          for (int j = 0; j < NA; ++j) {
+            acc[j][ct] = mfma16(av[j], bb, acc[j][ct]);
+            if constexpr (WF == AFF4) {
+              acc[j][ct] = mfma16(am[j], bb, acc[j][ct]);
+              acc[j][ct] = mfma16(al[j], bb, acc[j][ct]);
+            }
+          }
         } else {
           bf16x8 hi, lo;
           split_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
@@ -1305,6 +1346,11 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
           for (int j = 0; j < NA; ++j) {
             acc[j][ct] = mfma16(av[j], hi, acc[j][ct]);
             acc[j][ct] = mfma16(av[j], lo, acc[j][ct]);
+            if constexpr (WF == AFF4) {
+              acc[j][ct] = mfma16(am[j], hi, acc[j][ct]);
+              acc[j][ct] = mfma16(am[j], lo, acc[j][ct]);
+              acc[j][ct] = mfma16(al[j], hi, acc[j][ct]);
+            }
           }
         }
       }
@@ -2657,7 +2703,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void topk_sort_kernel(Args a) {
 struct GroupedItem {
   bool live, routed;
   int e, off, np, n0;
-  const void *gw, *uw, *gs, *us, *dw, *ds;   // the routed expert's matrices
+  const void *gw, *uw, *gs, *us, *dw, *ds, *gb, *ub, *db;   // the routed expert's matrices
 };
 
 __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int tiles) {
@@ -2678,6 +2724,9 @@ __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int
     g.us = reinterpret_cast<const void *>(uniform_u64(r.us));
     g.dw = reinterpret_cast<const void *>(uniform_u64(r.dw));
     g.ds = reinterpret_cast<const void *>(uniform_u64(r.ds));
+    g.gb = reinterpret_cast<const void *>(uniform_u64(r.gb));
+    g.ub = reinterpret_cast<const void *>(uniform_u64(r.ub));
+    g.db = reinterpret_cast<const void *>(uniform_u64(r.db));
     g.n0 = (item - s * tiles) * 16;
   } else {
     g.live = (a.flags & SHARED) != 0;
@@ -2686,7 +2735,7 @@ __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int
     g.off = 0;
     g.np = a.m;
     g.n0 = (item - nrout) * 16;
-    g.gw = g.uw = g.gs = g.us = g.dw = g.ds = nullptr;
+    g.gw = g.uw = g.gs = g.us = g.dw = g.ds = g.gb = g.ub = g.db = nullptr;
   }
   return g;
 }
@@ -2701,7 +2750,7 @@ __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int
 template <int EF> constexpr int gate_up_grouped_tiles() { return 1; }
 template <int EF>
 __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
-  static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4, "matrix-core experts: bf16, mxfp4, nvfp4");
+  static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4 || EF == AFF4, "matrix-core experts");
   constexpr int GT = gate_up_grouped_tiles<EF>(), KP = G_WPB / GT;
   constexpr int QF = EF == BF16 ? MXFP4 : EF;
   __shared__ MfmaLDS<G_WPB, 2, G_MU> S;
@@ -2719,8 +2768,8 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
   QMat<QF> Q[2];
   const bool quant = EF != BF16 && it.routed;
   if (quant) {
-    Q[0] = make_qmat<QF>(mg, it.gs, N, H);
-    Q[1] = make_qmat<QF>(mu, it.us, N, H);
+    Q[0] = make_qmat<QF>(mg, it.gs, it.gb, N, H);
+    Q[1] = make_qmat<QF>(mu, it.us, it.ub, N, H);
   } else {
     A[0] = buf_rsrc(mg, N * H * 2);
     A[1] = buf_rsrc(mu, N * H * 2);
@@ -2748,9 +2797,16 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
       xv[ct] = x + (size_t)row * H * 2 + (size_t)g4 * 16;
     }
     f32x4 acc[2][NCT];
-    if (quant)
-      mfma_slice_q<QF, BF16, 2, NCT, G_MU>(Q, H, n0, N, xv, kb, ke, S.stage[w], acc);
-    else
+    if (quant) {
+      if constexpr (QF == AFF4) {   // hi + lo weights, straight into the operands
+        const char *xr[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) xr[ct] = xv[ct] - (size_t)g4 * 16;
+        mfma_slice_qd<QF, BF16, 2, NCT, G_MU>(Q, H, n0, N, xr, kb, ke, acc);
+      } else {
+        mfma_slice_q<QF, BF16, 2, NCT, G_MU>(Q, H, n0, N, xv, kb, ke, S.stage[w], acc);
+      }
+    } else
       mfma_slice_v<BF16, 2, NCT, G_MU>(A, H * 2, n0, N, xv, kb, ke, S.stage[w], acc);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -2807,7 +2863,7 @@ template <bool WIDE> constexpr int down_grouped_threads() { return WIDE ? 256 : 
 template <bool WIDE> constexpr int down_grouped_cols() { return WIDE ? 16 * G_DT : 16; }
 template <int EF, bool WIDE>
 __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Args a) {
-  static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4, "matrix-core experts: bf16, mxfp4, nvfp4");
+  static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4 || EF == AFF4, "matrix-core experts");
   constexpr int QF = EF == BF16 ? MXFP4 : EF;                  // the 4-bit loader's format
   static_assert(down_grouped_threads<true>() == 256, "the launch bound above");
   constexpr int NW = down_grouped_threads<WIDE>() / WAVE;   // waves = parts of K
@@ -2833,12 +2889,15 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
   float s2d = 1.0f;   // nvfp4: the down projection's second-level scale
   if (quant) {
     const char *smat = reinterpret_cast<const char *>(it.ds);
-    constexpr int SB = QF == NVFP4 ? 16 : 32;   // elements per scale byte
+    const char *bmat = reinterpret_cast<const char *>(it.db);
+    // Scale bytes per row: K/16 (nvfp4), K/32 (mxfp4), K/64 bf16 (aff4).
+    const int sb = QF == NVFP4 ? K / 16 : QF == AFF4 ? K / 32 : K / 32;
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       const int r0 = h0 + 16 * j, nr = max(0, min(16, H - r0));
       Q[j].w = buf_rsrc(mat + (size_t)min(r0, H) * (K / 2), nr * (K / 2));
-      Q[j].s = buf_rsrc(smat + (size_t)min(r0, H) * (K / SB), nr * (K / SB));
+      Q[j].s = buf_rsrc(smat + (size_t)min(r0, H) * sb, nr * sb);
+      Q[j].b = QF == AFF4 ? buf_rsrc(bmat + (size_t)min(r0, H) * sb, nr * sb) : Q[j].s;
     }
     if constexpr (EF == NVFP4) s2d = a.ds2[it.e];
   } else {

@@ -78,7 +78,7 @@ def test_plan_and_layout_grouped_rows(name):
 
 
 def test_grouped_rows_limits():
-    for kw in (dict(act_fmt=md.MOE_F32, expert_fmt=md.MOE_F32), dict(expert_fmt=md.MOE_AFF4_G64),
+    for kw in (dict(act_fmt=md.MOE_F32, expert_fmt=md.MOE_F32), dict(expert_fmt=md.MOE_F32),
                dict(act_fmt=md.MOE_F32, expert_fmt=md.MOE_MXFP4_B32), dict(hidden=2048 + 16),
                dict(inter=768 + 8)):
         with pytest.raises(md.MoeDecodeError) as ei:
@@ -87,7 +87,7 @@ def test_grouped_rows_limits():
     with pytest.raises(md.MoeDecodeError) as ei:
         md.moe_decode_plan(_desc(max_rows=257))
     assert ei.value.status == md.MOE_EUNSUPPORTED
-    for fmt in (md.MOE_BF16, md.MOE_MXFP4_B32, md.MOE_NVFP4_B16):
+    for fmt in (md.MOE_BF16, md.MOE_MXFP4_B32, md.MOE_NVFP4_B16, md.MOE_AFF4_G64):
         plan, ws = md.moe_decode_plan(_desc(max_rows=256, expert_fmt=fmt))
         md.moe_decode_plan_destroy(plan)
 
