@@ -309,7 +309,7 @@ def main():
             torch.cuda.empty_cache()
         grows = [int(v) for v in args.grouped_rows.split(",") if v]
         for name, spec in synth.WORKLOADS.items():
-            if not grows or spec.act_fmt != "bf16" or spec.expert_fmt not in ("bf16", "mxfp4", "nvfp4"):
+            if not grows or spec.act_fmt != "bf16" or spec.expert_fmt not in ("bf16", "mxfp4", "nvfp4", "aff4"):
                 continue
             layer, res = time_workload(name, grows[0], args.steps, args.warmup, grows[1:],
                                        max_rows=max(grows))
