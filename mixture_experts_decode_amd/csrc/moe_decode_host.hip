@@ -306,12 +306,12 @@ moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *st
     return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
   // Down rows of at most 2048: items of 64 columns on four waves that each
   // take all four tiles over a quarter of K (an input fragment serves four
-  // tiles); longer rows: items of 16 columns on eight waves, an eighth of K
+  // tiles); longer rows: items of 32 columns on eight waves, an eighth of K
   // each.
   const int kmax = d.inter > a.Is ? d.inter : a.Is;
   const bool wide = kmax <= 2048;
   const moe::launch_fn dn = wide ? k.down_grouped : k.down_grouped_long;
-  const int cols = wide ? 16 * moe::G_DT : 16;
+  const int cols = wide ? 16 * moe::G_DT : 16 * moe::G_DTL;
   const int dn_items = (a.cap + (shared ? 1 : 0)) * ((d.hidden + cols - 1) / cols);
   if ((e = dn(a, dn_items, s, ev(4), nullptr)) != hipSuccess)
     return fail(MOE_EHIP, "down launch: %s", hipGetErrorString(e));

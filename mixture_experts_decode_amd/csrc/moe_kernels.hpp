@@ -2855,19 +2855,21 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
 //   WIDE (rows of at most 2048): item = G_DT tiles of 16 output columns on
 //     four waves, each all the tiles over a quarter of K, so one input
 //     fragment serves G_DT tiles;
-//   else: item = one tile on eight waves, each an eighth of K (a long run
-//     of k per wave).
+//   else: item = G_DTL tiles on eight waves, each both tiles over an eighth
+//     of K (a long run of k per wave; two tiles halve the input re-reads
+//     from L2 that dominate these rows, four cost a wave per SIMD in LDS).
 // The parts of K are added in part order.
 constexpr int G_DT = 4;
+constexpr int G_DTL = 2;
 template <bool WIDE> constexpr int down_grouped_threads() { return WIDE ? 256 : G_THREADS; }
-template <bool WIDE> constexpr int down_grouped_cols() { return WIDE ? 16 * G_DT : 16; }
+template <bool WIDE> constexpr int down_grouped_cols() { return WIDE ? 16 * G_DT : 16 * G_DTL; }
 template <int EF, bool WIDE>
 __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Args a) {
   static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4 || EF == AFF4, "matrix-core experts");
   constexpr int QF = EF == BF16 ? MXFP4 : EF;                  // the 4-bit loader's format
   static_assert(down_grouped_threads<true>() == 256, "the launch bound above");
   constexpr int NW = down_grouped_threads<WIDE>() / WAVE;   // waves = parts of K
-  constexpr int NA = WIDE ? G_DT : 1;                        // tiles per wave
+  constexpr int NA = WIDE ? G_DT : G_DTL;                        // tiles per wave
   // bf16 rows of at most 2048: two k steps per staged batch (longer runs per
   // row beat the wave per SIMD they cost); 4-bit kernels keep one, so their
   // shared-expert items do not set their register count.
