@@ -301,7 +301,7 @@ moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *st
   if ((e = moe::launch_topk_sort(a, (m + moe::ROUTE_WPB - 1) / moe::ROUTE_WPB, s, nullptr, ev(1))) != hipSuccess)
     return fail(MOE_EHIP, "top-k launch: %s", hipGetErrorString(e));
   const int gr = k.gu_grouped_rows;
-  const int gu_items = a.cap * ((d.inter + gr - 1) / gr) + (shared ? (a.Is + gr - 1) / gr : 0);
+  const int gu_items = moe::grouped_item_count(a.cap * ((d.inter + gr - 1) / gr), shared, (a.Is + gr - 1) / gr, m);
   if ((e = k.gate_up_grouped(a, gu_items, s, ev(2), ev(3))) != hipSuccess)
     return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
   // Down rows of at most 2048: items of 64 columns on four waves that each
@@ -312,7 +312,8 @@ moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *st
   const bool wide = kmax <= 2048;
   const moe::launch_fn dn = wide ? k.down_grouped : k.down_grouped_long;
   const int cols = wide ? 16 * moe::G_DT : 16 * moe::G_DTL;
-  const int dn_items = (a.cap + (shared ? 1 : 0)) * ((d.hidden + cols - 1) / cols);
+  const int dn_tiles = (d.hidden + cols - 1) / cols;
+  const int dn_items = moe::grouped_item_count(a.cap * dn_tiles, shared, dn_tiles, m);
   if ((e = dn(a, dn_items, s, ev(4), nullptr)) != hipSuccess)
     return fail(MOE_EHIP, "down launch: %s", hipGetErrorString(e));
   const int bl_threads = m * (d.hidden / 4);

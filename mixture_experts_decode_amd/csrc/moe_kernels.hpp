@@ -2706,7 +2706,18 @@ struct GroupedItem {
   const void *gw, *uw, *gs, *us, *dw, *ds, *gb, *ub, *db;   // the routed expert's matrices
 };
 
-__device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int tiles) {
+// Shared-expert items: one per (tile, block of G_COLS rows).  They start at
+// the first multiple of 8 at or after the routed items, in groups of 8 tiles:
+// the row blocks of one tile take block indices 8 apart, so the round-robin
+// dispatch puts them on one XCD one after another and the tile's weights are
+// read from HBM once and then from that XCD's L2.
+__host__ __device__ constexpr int shared_row_blocks(int m) { return (m + G_COLS - 1) / G_COLS; }
+__host__ __device__ constexpr int grouped_shared_base(int nrout) { return (nrout + 7) / 8 * 8; }
+__host__ __device__ constexpr int grouped_item_count(int nrout, bool shared, int stiles, int m) {
+  return shared ? grouped_shared_base(nrout) + (stiles + 7) / 8 * 8 * shared_row_blocks(m) : nrout;
+}
+
+__device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int tiles, int stiles) {
   GroupedItem g;
   const int nrout = a.cap * tiles;
   if (item < nrout) {
@@ -2729,12 +2740,15 @@ __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int
     g.db = reinterpret_cast<const void *>(uniform_u64(r.db));
     g.n0 = (item - s * tiles) * 16;
   } else {
-    g.live = (a.flags & SHARED) != 0;
+    const int P = shared_row_blocks(a.m), sidx = item - grouped_shared_base(nrout);
+    const int grp = sidx / (8 * P), r = sidx - grp * 8 * P;
+    const int tile = grp * 8 + (r & 7), blk = r >> 3;
+    g.live = (a.flags & SHARED) != 0 && sidx >= 0 && tile < stiles;
     g.routed = false;
     g.e = 0;
-    g.off = 0;
-    g.np = a.m;
-    g.n0 = (item - nrout) * 16;
+    g.off = blk * G_COLS;                       // the block's first row
+    g.np = max(0, min(G_COLS, a.m - g.off));
+    g.n0 = tile * 16;
     g.gw = g.uw = g.gs = g.us = g.dw = g.ds = g.gb = g.ub = g.db = nullptr;
   }
   return g;
@@ -2756,7 +2770,7 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
   __shared__ MfmaLDS<G_WPB, 2, G_MU> S;
   const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int H = a.H, k = a.K;
-  const GroupedItem it = grouped_item(a, blockIdx.x, (a.I + 16 * GT - 1) / (16 * GT));
+  const GroupedItem it = grouped_item(a, blockIdx.x, (a.I + 16 * GT - 1) / (16 * GT), (a.Is + 16 * GT - 1) / (16 * GT));
   if (!it.live) return;
   const int N = it.routed ? a.I : a.Is;
   const int r0 = it.n0 * GT;                 // the item's first row
@@ -2793,7 +2807,7 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int v = c0 + min(16 * ct + rr, nv - 1);
-      const int row = it.routed ? min(clamp_i(a.sorted_pair[it.off + v], 0, a.te - 1) / k, a.m - 1) : v;
+      const int row = it.routed ? min(clamp_i(a.sorted_pair[it.off + v], 0, a.te - 1) / k, a.m - 1) : it.off + v;
       xv[ct] = x + (size_t)row * H * 2 + (size_t)g4 * 16;
     }
     f32x4 acc[2][NCT];
@@ -2842,7 +2856,7 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
           }
           a.act[(size_t)(it.off + c0 + v) * a.I + row] = act_mul(a.flags, gs, us);
         } else {
-          a.sact[(size_t)(c0 + v) * a.Is + row] = act_mul(a.flags, gs, us);
+          a.sact[(size_t)(it.off + c0 + v) * a.Is + row] = act_mul(a.flags, gs, us);
         }
       }
     }
@@ -2878,7 +2892,7 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
   __shared__ MfmaLDS<NW, NA, MU> S;
   const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int H = a.H;
-  const GroupedItem it = grouped_item(a, blockIdx.x, (H + COLS - 1) / COLS);
+  const GroupedItem it = grouped_item(a, blockIdx.x, (H + COLS - 1) / COLS, (H + COLS - 1) / COLS);
   if (!it.live) return;
   const int K = it.routed ? a.I : a.Is;
   const char *mat = reinterpret_cast<const char *>(it.routed ? it.dw : a.sdw);
@@ -2911,8 +2925,8 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
   }
   int kb, ke;
   k_slice(K, w, NW, kb, ke);
-  const char *xb = reinterpret_cast<const char *>(it.routed ? a.act + (size_t)it.off * K : a.sact);
-  float *dst = it.routed ? a.y + (size_t)it.off * H : a.sy;
+  const char *xb = reinterpret_cast<const char *>((it.routed ? a.act : a.sact) + (size_t)it.off * K);
+  float *dst = (it.routed ? a.y : a.sy) + (size_t)it.off * H;
   // One pass: NCT column tiles of 16 pairs from c0 on.
   auto pass = [&](auto nct, int c0, int nv) {
     constexpr int NCT = decltype(nct)::value;
