@@ -1210,7 +1210,7 @@ template <int WF, int XF, int NA, int NCT, int MU>
 __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, int n0, int N,
                                               const char *const (&xr)[NCT], int kb, int ke,
                                               f32x4 (&acc)[NA][NCT]) {
-  static_assert(WF == MXFP4 || WF == NVFP4 || WF == AFF4, "4-bit formats");
+  static_assert(WF == MXFP4 || WF == NVFP4, "4-bit formats with one scale per code block");
   static_assert(MU == 1 || MU == 2 || MU == 4, "a lane's range lies in one scale block");
   constexpr int CB = 4 * MU;                       // code bytes per lane per batch
   constexpr int XB = XF == F32 ? 4 : 2;
@@ -1218,9 +1218,7 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
   const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
   const int row = min(n0 + rr, N - 1);
   const int qoff = row * (K / 2) + g * CB;
-  const int soff = WF == NVFP4 ? row * (K / 16) + (8 * MU * g) / 16
-                 : WF == AFF4  ? row * (K / 64) * 2   // + 2 * the group of the lane's range
-                               : row * (K / 32) + (8 * MU * g) / 32;
+  const int soff = WF == NVFP4 ? row * (K / 16) + (8 * MU * g) / 16 : row * (K / 32) + (8 * MU * g) / 32;
 #pragma unroll
   for (int j = 0; j < NA; ++j)
 #pragma unroll
@@ -1228,7 +1226,7 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
   if (kb >= ke) return;
   typedef uint32_t cvec __attribute__((ext_vector_type(MU)));
   cvec nq[NA];
-  uint32_t ns[NA], nb[NA];
+  uint32_t ns[NA];
   u32x4 nx[NCT][XQ];
   auto fetch = [&](int kq) {
 #pragma unroll
@@ -1236,11 +1234,7 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
       if constexpr (MU == 4) nq[j] = __builtin_bit_cast(cvec, __builtin_amdgcn_raw_buffer_load_b128(A[j].w, qoff + kq / 2, 0, 0));
       else if constexpr (MU == 2) nq[j] = __builtin_bit_cast(cvec, __builtin_amdgcn_raw_buffer_load_b64(A[j].w, qoff + kq / 2, 0, 0));
       else nq[j] = __builtin_bit_cast(cvec, __builtin_amdgcn_raw_buffer_load_b32(A[j].w, qoff + kq / 2, 0, 0));
-      if constexpr (WF == AFF4) {   // a lane's range lies in one 64-element group
-        const int go = soff + ((kq + 8 * MU * g) >> 6) * 2;
-        ns[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].s, go, 0, 0);
-        nb[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].b, go, 0, 0);
-      } else if constexpr (WF == NVFP4 && MU == 4) ns[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].s, soff + kq / 16, 0, 0);
+      if constexpr (WF == NVFP4 && MU == 4) ns[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].s, soff + kq / 16, 0, 0);
       else if constexpr (WF == NVFP4) ns[j] = __builtin_amdgcn_raw_buffer_load_b8(A[j].s, soff + kq / 16, 0, 0);
       else ns[j] = __builtin_amdgcn_raw_buffer_load_b8(A[j].s, soff + kq / 32, 0, 0);
     }
@@ -1255,13 +1249,12 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
   fetch(kb);
   for (int k0 = kb; k0 < ke; k0 += 32 * MU) {
     cvec cq[NA];
-    uint32_t cs[NA], cb[NA];
+    uint32_t cs[NA];
     u32x4 cx[NCT][XQ];
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       cq[j] = nq[j];
       cs[j] = ns[j];
-      cb[j] = nb[j];
     }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -1271,38 +1264,12 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
       const bool valid = k0 + 8 * MU * g + 8 * u < ke;
-      u32x4 av[NA], am[NA], al[NA];   // aff4: w = hi + mid + lo (bf16 each, 24 bits)
+      u32x4 av[NA];
 #pragma unroll
       for (int j = 0; j < NA; ++j) {
         const uint32_t qd = cq[j][u];
         uint32_t pr[4];
-        if constexpr (WF == AFF4) {
-          // w = s q + b in float (s q is exact).  hi = w's top 16 bits, mid =
-          // the top 16 bits of w - hi, lo = the rest rounded to bf16 (every
-          // difference is exact): hi + mid + lo carries w's 24 bits, so the
-          // products are those of the float weights the vector path uses.
-          const float sc = bf16_to_f32((uint16_t)cs[j]), bi = bf16_to_f32((uint16_t)cb[j]);
-          uint32_t md[4], lo[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            uint32_t hb[2], mb[2], lb[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const float w = __builtin_fmaf(sc, (float)((qd >> (8 * t + 4 * e)) & 0xFu), bi);
-              const uint32_t h = __float_as_uint(w) & 0xFFFF0000u;
-              const float r = w - __uint_as_float(h);
-              const uint32_t m = __float_as_uint(r) & 0xFFFF0000u;
-              hb[e] = h;
-              mb[e] = m;
-              lb[e] = (uint32_t)f32_to_bf16(r - __uint_as_float(m)) << 16;
-            }
-            pr[t] = valid ? (hb[0] >> 16) | hb[1] : 0u;
-            md[t] = valid ? (mb[0] >> 16) | mb[1] : 0u;
-            lo[t] = valid ? (lb[0] >> 16) | lb[1] : 0u;
-          }
-          am[j] = u32x4{md[0], md[1], md[2], md[3]};
-          al[j] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-        } else if constexpr (WF == MXFP4) {
+        if constexpr (WF == MXFP4) {
           const float sc = e8m0_to_f32(cs[j] & 0xFFu);
           // The E8M0 scale is a power of two: the scaled conversion is exact.
           pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(qd, sc, 0));
@@ -1332,13 +1299,7 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
         if constexpr (XF == BF16) {
           const bf16x8 bb = __builtin_bit_cast(bf16x8, cx[ct][u]);
 #pragma unroll
-          for (int j = 0; j < NA; ++j) {
-            acc[j][ct] = mfma16(av[j], bb, acc[j][ct]);
-            if constexpr (WF == AFF4) {
-              acc[j][ct] = mfma16(am[j], bb, acc[j][ct]);
-              acc[j][ct] = mfma16(al[j], bb, acc[j][ct]);
-            }
-          }
+          for (int j = 0; j < NA; ++j) acc[j][ct] = mfma16(av[j], bb, acc[j][ct]);
         } else {
           bf16x8 hi, lo;
           split_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
@@ -1346,11 +1307,6 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
           for (int j = 0; j < NA; ++j) {
             acc[j][ct] = mfma16(av[j], hi, acc[j][ct]);
             acc[j][ct] = mfma16(av[j], lo, acc[j][ct]);
-            if constexpr (WF == AFF4) {
-              acc[j][ct] = mfma16(am[j], hi, acc[j][ct]);
-              acc[j][ct] = mfma16(am[j], lo, acc[j][ct]);
-              acc[j][ct] = mfma16(al[j], hi, acc[j][ct]);
-            }
           }
         }
       }
@@ -1363,6 +1319,137 @@ __device__ __forceinline__ void k_slice(int K, int w, int nw, int &kb, int &ke) 
   const int steps = K / 32, per = (steps + nw - 1) / nw;
   kb = min(w * per, steps) * 32;
   ke = min((w + 1) * per, steps) * 32;
+}
+
+// The same in whole 64-element groups (K a multiple of 64).
+__device__ __forceinline__ void k_slice64(int K, int w, int nw, int &kb, int &ke) {
+  const int steps = K / 64, per = (steps + nw - 1) / nw;
+  kb = min(w * per, steps) * 64;
+  ke = min((w + 1) * per, steps) * 64;
+}
+
+// Lane (l & ~3) + I's value, for every lane l (a broadcast within quads).
+template <int I> __device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, I * 0x55, 0xF, 0xF, false);
+}
+
+// aff4 on the matrix cores.  A 64-element group's weights are s q + b, so
+// its sum over k is s (D - 128 X) + b X, with D the sum of (128 + q) x and X
+// the sum of x.  The codes enter the products as the bf16 values 128 + q
+// (bits 0x4300 | q, exact), X is a product with an all-ones operand, and
+// every product of two bf16 values is exact in the f32 accumulators; no
+// weight is rounded.  A batch is one group (k ranges are multiples of 64):
+// lane (row l % 16, g = l / 16) takes elements [16 g, 16 g + 16) of it, the
+// first 8 in k step 0 and the rest in k step 1 (a sum does not depend on the
+// order of k), and the input vectors are read in the same order.  D and X
+// start from zero in every group; the lane then adds s D + (b - 128 s) X for
+// its accumulator rows 4 g + i, whose scale and bias come from lane
+// (l & ~3) + i of its quad, which loaded those of row 4 g + i.
+// xr[ct]: the start of this lane's vector 16 ct + l % 16.
+template <int XF, int NA, int NCT>
+__device__ __forceinline__ void mfma_slice_aff4(const QMat<AFF4> (&A)[NA], int K, int n0, int N,
+                                                const char *const (&xr)[NCT], int kb, int ke,
+                                                f32x4 (&acc)[NA][NCT]) {
+  constexpr int XB = XF == F32 ? 4 : 2;
+  constexpr int XQ = XB;                           // 16-byte x loads per lane, group and tile
+  const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
+  const int qoff = min(n0 + rr, N - 1) * (K / 2) + g * 8;
+  const int soff = min(n0 + 4 * g + (l & 3), N - 1) * (K / 64) * 2;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NA; ++j)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[j][ct] = zero;
+  if (kb >= ke) return;
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  u32x2 nq[NA];
+  uint32_t ns[NA], nb[NA];
+  u32x4 nx[NCT][XQ];
+  auto fetch = [&](int kq) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      nq[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(A[j].w, qoff + kq / 2, 0, 0));
+      ns[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].s, soff + (kq >> 6) * 2, 0, 0);
+      nb[j] = __builtin_amdgcn_raw_buffer_load_b16(A[j].b, soff + (kq >> 6) * 2, 0, 0);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int h = 0; h < XQ; ++h) nx[ct][h] = ld16(xr[ct] + (size_t)(kq + 16 * g) * XB + 16 * h);
+  };
+  fetch(kb);
+  for (int k0 = kb; k0 < ke; k0 += 64) {
+    u32x2 cq[NA];
+    uint32_t cs[NA], cb[NA];
+    u32x4 cx[NCT][XQ];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      cq[j] = nq[j];
+      cs[j] = ns[j];
+      cb[j] = nb[j];
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int h = 0; h < XQ; ++h) cx[ct][h] = nx[ct][h];
+    if (k0 + 64 < ke) fetch(k0 + 64);
+    f32x4 D[NA][NCT], X[NCT];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      u32x4 av[NA];
+#pragma unroll
+      for (int j = 0; j < NA; ++j) {
+        const uint32_t q = cq[j][u], qs = q >> 4;
+        uint32_t pr[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          // byte t of q (low nibble: element 2t) to bits 0..7, byte t of
+          // q >> 4 (element 2t + 1) to bits 16..23, zeros elsewhere
+          const uint32_t p = __builtin_amdgcn_perm(qs, q, 0x0C000C00u | (uint32_t)((4 + t) << 16) | (uint32_t)t);
+          pr[t] = (p & 0x000F000Fu) | 0x43004300u;
+        }
+        av[j] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        if constexpr (XF == BF16) {
+          const bf16x8 bb = __builtin_bit_cast(bf16x8, cx[ct][u]);
+          X[ct] = mfma16(ones, bb, u ? X[ct] : zero);
+#pragma unroll
+          for (int j = 0; j < NA; ++j) D[j][ct] = mfma16(av[j], bb, u ? D[j][ct] : zero);
+        } else {
+          bf16x8 hi, lo;
+          split_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
+          X[ct] = mfma16(ones, hi, u ? X[ct] : zero);
+          X[ct] = mfma16(ones, lo, X[ct]);
+#pragma unroll
+          for (int j = 0; j < NA; ++j) {
+            D[j][ct] = mfma16(av[j], hi, u ? D[j][ct] : zero);
+            D[j][ct] = mfma16(av[j], lo, D[j][ct]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      float sc[4], bc[4];
+      sc[0] = bf16_to_f32((uint16_t)quad_bcast<0>(cs[j]));
+      sc[1] = bf16_to_f32((uint16_t)quad_bcast<1>(cs[j]));
+      sc[2] = bf16_to_f32((uint16_t)quad_bcast<2>(cs[j]));
+      sc[3] = bf16_to_f32((uint16_t)quad_bcast<3>(cs[j]));
+      bc[0] = bf16_to_f32((uint16_t)quad_bcast<0>(cb[j]));
+      bc[1] = bf16_to_f32((uint16_t)quad_bcast<1>(cb[j]));
+      bc[2] = bf16_to_f32((uint16_t)quad_bcast<2>(cb[j]));
+      bc[3] = bf16_to_f32((uint16_t)quad_bcast<3>(cb[j]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float bp = __builtin_fmaf(-128.0f, sc[i], bc[i]);   // b - 128 s, one rounding
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          acc[j][ct][i] = __builtin_fmaf(sc[i], D[j][ct][i], __builtin_fmaf(bp, X[ct][i], acc[j][ct][i]));
+      }
+    }
+  }
 }
 
 // Partials of the NW waves of one matrix-core item, added in wave order.
@@ -2796,7 +2883,8 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
     }
   }
   int kb, ke;
-  k_slice(H, w / GT, KP, kb, ke);
+  if (EF == AFF4 && quant) k_slice64(H, w / GT, KP, kb, ke);   // whole scale groups
+  else k_slice(H, w / GT, KP, kb, ke);
   const bool before = it.routed && (a.flags & WEIGHT_BEFORE);
   const char *x = reinterpret_cast<const char *>(a.x);
   const int g4 = lane >> 4, rr = lane & 15;
@@ -2812,11 +2900,11 @@ __global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
     }
     f32x4 acc[2][NCT];
     if (quant) {
-      if constexpr (QF == AFF4) {   // hi + lo weights, straight into the operands
+      if constexpr (QF == AFF4) {   // codes straight into the operands, group sums
         const char *xr[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) xr[ct] = xv[ct] - (size_t)g4 * 16;
-        mfma_slice_qd<QF, BF16, 2, NCT, G_MU>(Q, H, n0, N, xr, kb, ke, acc);
+        mfma_slice_aff4<BF16, 2, NCT>(Q, H, n0, N, xr, kb, ke, acc);
       } else {
         mfma_slice_q<QF, BF16, 2, NCT, G_MU>(Q, H, n0, N, xv, kb, ke, S.stage[w], acc);
       }
@@ -2924,7 +3012,8 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
     }
   }
   int kb, ke;
-  k_slice(K, w, NW, kb, ke);
+  if (EF == AFF4 && quant) k_slice64(K, w, NW, kb, ke);   // whole scale groups
+  else k_slice(K, w, NW, kb, ke);
   const char *xb = reinterpret_cast<const char *>((it.routed ? a.act : a.sact) + (size_t)it.off * K);
   float *dst = (it.routed ? a.y : a.sy) + (size_t)it.off * H;
   // One pass: NCT column tiles of 16 pairs from c0 on.
@@ -2934,7 +3023,8 @@ __global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Ar
     if (quant) {   // 4-bit codes straight into the operands; passes of one column tile
       if constexpr (NCT == 1) {
         const char *xr[1] = {xb + (size_t)(c0 + min(lane & 15, nv - 1)) * K * 4};
-        mfma_slice_qd<QF, F32, NA, 1, 2>(Q, K, 0, 16, xr, kb, ke, acc);
+        if constexpr (QF == AFF4) mfma_slice_aff4<F32, NA, 1>(Q, K, 0, 16, xr, kb, ke, acc);
+        else mfma_slice_qd<QF, F32, NA, 1, 2>(Q, K, 0, 16, xr, kb, ke, acc);
       }
     } else {
       mfma_slice<F32, NA, NCT, MU>(A, K * 2, 0, 16, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
