@@ -2849,8 +2849,9 @@ __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int
 // or four tiles were slower for every format.)  A pass of at most 16 pairs
 // takes one column tile.
 template <int EF> constexpr int gate_up_grouped_tiles() { return 1; }
+template <int EF> constexpr int gu_grouped_min_waves() { return EF == AFF4 ? 4 : 1; }
 template <int EF>
-__global__ __launch_bounds__(G_THREADS) void gate_up_grouped_kernel(Args a) {
+__global__ __launch_bounds__(G_THREADS, gu_grouped_min_waves<EF>()) void gate_up_grouped_kernel(Args a) {
   static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4 || EF == AFF4, "matrix-core experts");
   constexpr int GT = gate_up_grouped_tiles<EF>(), KP = G_WPB / GT;
   constexpr int QF = EF == BF16 ? MXFP4 : EF;
