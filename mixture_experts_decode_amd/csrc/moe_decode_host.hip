@@ -304,10 +304,10 @@ moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *st
   const int gu_items = moe::grouped_item_count(a.cap * ((d.inter + gr - 1) / gr), shared, (a.Is + gr - 1) / gr, m);
   if ((e = k.gate_up_grouped(a, gu_items, s, ev(2), ev(3))) != hipSuccess)
     return fail(MOE_EHIP, "gate_up launch: %s", hipGetErrorString(e));
-  // Down rows of at most 2048: items of 64 columns on four waves that each
-  // take all four tiles over a quarter of K (an input fragment serves four
-  // tiles); longer rows: items of 32 columns on eight waves, an eighth of K
-  // each.
+  // Down rows of at most 2048: items of 64 columns on two waves (four for
+  // aff4) that each take all four tiles over a part of K (an input fragment
+  // serves four tiles); longer rows: items of 32 columns on eight waves, an
+  // eighth of K each.
   const int kmax = d.inter > a.Is ? d.inter : a.Is;
   const bool wide = kmax <= 2048;
   const moe::launch_fn dn = wide ? k.down_grouped : k.down_grouped_long;

@@ -2956,22 +2956,26 @@ __global__ __launch_bounds__(G_THREADS, gu_grouped_min_waves<EF>()) void gate_up
 // Down: y per pair (sorted order) or ys per row, for one active expert (or
 // the shared expert):
 //   WIDE (rows of at most 2048): item = G_DT tiles of 16 output columns on
-//     four waves, each all the tiles over a quarter of K, so one input
-//     fragment serves G_DT tiles;
+//     two waves (four for aff4), each all the tiles over its part of K, so
+//     one input fragment serves G_DT tiles;
 //   else: item = G_DTL tiles on eight waves, each both tiles over an eighth
 //     of K (a long run of k per wave; two tiles halve the input re-reads
 //     from L2 that dominate these rows, four cost a wave per SIMD in LDS).
 // The parts of K are added in part order.
 constexpr int G_DT = 4;
 constexpr int G_DTL = 2;
-template <bool WIDE> constexpr int down_grouped_threads() { return WIDE ? 256 : G_THREADS; }
+// Wide items run on two waves (longer runs of k per wave), aff4's on
+// four: its products per byte are the most, and four parts of K were
+// 21-32 % faster than two.
+template <int EF, bool WIDE> constexpr int down_grouped_threads() {
+  return WIDE ? (EF == AFF4 ? 256 : 128) : G_THREADS;
+}
 template <bool WIDE> constexpr int down_grouped_cols() { return WIDE ? 16 * G_DT : 16 * G_DTL; }
 template <int EF, bool WIDE>
-__global__ __launch_bounds__(WIDE ? 256 : G_THREADS) void down_grouped_kernel(Args a) {
+__global__ __launch_bounds__((down_grouped_threads<EF, WIDE>())) void down_grouped_kernel(Args a) {
   static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4 || EF == AFF4, "matrix-core experts");
   constexpr int QF = EF == BF16 ? MXFP4 : EF;                  // the 4-bit loader's format
-  static_assert(down_grouped_threads<true>() == 256, "the launch bound above");
-  constexpr int NW = down_grouped_threads<WIDE>() / WAVE;   // waves = parts of K
+  constexpr int NW = down_grouped_threads<EF, WIDE>() / WAVE;   // waves = parts of K
   constexpr int NA = WIDE ? G_DT : G_DTL;                        // tiles per wave
   // bf16 rows of at most 2048: two k steps per staged batch (longer runs per
   // row beat the wave per SIMD they cost); 4-bit kernels keep one, so their

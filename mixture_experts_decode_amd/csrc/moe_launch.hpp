@@ -86,7 +86,7 @@ hipError_t launch_gate_up_grouped_t(const Args &a, int blocks, hipStream_t st, h
 }
 template <int EF, bool WIDE>
 hipError_t launch_down_grouped_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  return launch_timed(down_grouped_kernel<EF, WIDE>, blocks, down_grouped_threads<WIDE>(), st, start, stop, a);
+  return launch_timed(down_grouped_kernel<EF, WIDE>, blocks, down_grouped_threads<EF, WIDE>(), st, start, stop, a);
 }
 template <int EF, int ACT, int CR, int CS, int SHD>
 hipError_t launch_gate_up_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
