@@ -1556,11 +1556,13 @@ __device__ __forceinline__ void router_part(const Args &a, int unit, int part, d
 
 // Router tile for many rows (the grouped path): unit u = (block of RT_E
 // router rows, block of up to 8 input rows), so each input chunk serves RT_E
-// router rows; otherwise as router_part.  tot[j][r]: router row j of the
-// block, input row r (0 past the last row or router row).
+// router rows; otherwise as router_part.  Returns, in lanes 2o and 2o + 1,
+// the wave's sum for o = 8 j + r: router row j of the block, input row r (0
+// past the last row or router row).
 constexpr int RT_E = 4;
 template <int ACT>
-__device__ __forceinline__ void router_tile(const Args &a, int unit, int part, double (&tot)[RT_E][8]) {
+__device__ __forceinline__ double router_tile(const Args &a, int unit, int part) {
+  static_assert(RT_E * 8 == 32, "one sum per lane pair");
   constexpr int EPC = ACT == F32 ? 4 : 8;
   const int lane = threadIdx.x & 63;
   const int nrows = a.E + ((a.flags & SHARED_GATED) ? 1 : 0);
@@ -1615,11 +1617,28 @@ __device__ __forceinline__ void router_tile(const Args &a, int unit, int part, d
       }
     }
   }
+  // The 32 sums over the wave by halving: at each step a lane keeps half of
+  // its values, adding the partner's copy of that half, and sends the other
+  // half; five steps leave one value per lane (the sum over 32 lanes), and a
+  // last exchange adds the pair.  Lane l ends with o = l / 2.
+  double v[32];
 #pragma unroll
   for (int j = 0; j < RT_E; ++j)
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      tot[j][r] = (r < nr && eb * RT_E + j < nrows) ? wave_sum_f64(acc[j][r]) : 0.0;
+    for (int r = 0; r < 8; ++r) v[8 * j + r] = acc[j][r];
+#pragma unroll
+  for (int st = 0; st < 5; ++st) {
+    const int half = 16 >> st, off = 32 >> st;
+    const bool up = (lane & off) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const double keep = up ? v[half + i] : v[i], send = up ? v[i] : v[half + i];
+      v[i] = keep + __shfl_xor(send, off);
+    }
+  }
+  const double t = v[0] + __shfl_xor(v[0], 1);
+  const int o = lane >> 1, j = o >> 3, r = o & 7;
+  return (r < nr && eb * RT_E + j < nrows) ? t : 0.0;
 }
 
 // --------------------------------------------------------- top-k and sort
@@ -2457,14 +2476,8 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_tile_kernel(Args a) {
   const int wave = uniform_i(threadIdx.x >> 6);
   const int unit = item * ROUTE_UNITS_PER_WG + wave / RSPLIT, part = wave % RSPLIT;
   const bool live = unit < a.n_router;
-  double tot[RT_E][8];
-  if (live) router_tile<ACT>(a, unit, part, tot);
-  if ((threadIdx.x & 63) == 0) {
-#pragma unroll
-    for (int j = 0; j < RT_E; ++j)
-#pragma unroll
-      for (int r = 0; r < 8; ++r) s_part[wave][j * 8 + r] = live ? tot[j][r] : 0.0;
-  }
+  const double tot = live ? router_tile<ACT>(a, unit, part) : 0.0;
+  if ((threadIdx.x & 1) == 0) s_part[wave][(threadIdx.x & 63) >> 1] = tot;
   __syncthreads();
   if (tid < ROUTE_UNITS_PER_WG * RT_E * 8) {
     const int ul = tid / (RT_E * 8), o = tid % (RT_E * 8), j = o / 8, r = o % 8;
