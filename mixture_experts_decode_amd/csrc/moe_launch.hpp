@@ -82,7 +82,7 @@ hipError_t launch_down_blend_t(const Args &a, int blocks, hipStream_t st, hipEve
 }
 template <int EF>
 hipError_t launch_gate_up_grouped_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  return launch_timed(gate_up_grouped_kernel<EF>, blocks, G_THREADS, st, start, stop, a);
+  return launch_timed(gate_up_grouped_kernel<EF>, blocks, 64 * gu_grouped_waves<EF>(), st, start, stop, a);
 }
 template <int EF, bool WIDE>
 hipError_t launch_down_grouped_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
