@@ -2863,10 +2863,12 @@ __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int
 // takes one column tile.
 template <int EF> constexpr int gate_up_grouped_tiles() { return 1; }
 template <int EF> constexpr int gu_grouped_min_waves() { return EF == AFF4 ? 4 : 1; }
-// Waves per item, each a part of H: four for 4-bit experts (a 16-row item
-// holds a quarter of bf16's bytes, so longer runs of k per wave pay: -3 to
-// -11 %), eight for bf16.
-template <int EF> constexpr int gu_grouped_waves() { return EF == BF16 ? 8 : 4; }
+// Waves per item, each a part of H: four for MXFP4 and aff4 experts (a
+// 16-row item holds a quarter of bf16's bytes, so longer runs of k per wave
+// pay: -3 to -11 %), eight for bf16 and for NVFP4, whose dequantisation
+// (a float scale per 16 codes) takes the most work per code (-7 % at 256
+// rows against four).
+template <int EF> constexpr int gu_grouped_waves() { return EF == BF16 || EF == NVFP4 ? 8 : 4; }
 template <int EF>
 __global__ __launch_bounds__(64 * gu_grouped_waves<EF>(), gu_grouped_min_waves<EF>()) void gate_up_grouped_kernel(Args a) {
   constexpr int NWG = gu_grouped_waves<EF>();
