@@ -45,8 +45,13 @@ enum : unsigned { NORM_TOPK = 1u, WEIGHT_BEFORE = 2u, SHARED = 4u, SHARED_GATED 
 constexpr int WAVE = 64;
 constexpr int THREADS = 256;            // route and gate/up: 4 waves per workgroup
 constexpr int WPB = THREADS / WAVE;
-constexpr int DOWN_THREADS = 512;       // down + blend: 8 waves, one active slot each at m = 1
+constexpr int DOWN_THREADS = 512;       // down + blend of the widest passes: 8 waves
 constexpr int DOWN_WPB = DOWN_THREADS / WAVE;
+// Down + blend workgroup of the variant with passes of up to CS vectors: 12
+// waves (a tile's sub-units run in fewer rounds: -9 to -16 % on the down at
+// m = 2-4) where the registers fit three waves per SIMD, else 8 (the
+// eight-vector variants spill, and so would aff4's four-vector one: +9 %).
+template <int EF, int CS> constexpr int down_threads() { return CS >= 8 || EF == AFF4 ? DOWN_THREADS : 768; }
 constexpr int ROUTE_THREADS = 512;      // route launch: 8 waves
 constexpr int ROUTE_WPB = ROUTE_THREADS / WAVE;
 constexpr int RSPLIT = 4;               // waves per router row (its H is split in 4)
@@ -2162,6 +2167,7 @@ template <int EF, int ACT, int CR, int CS, int LPR>
 __device__ __forceinline__ void down_item(const Args &a, int tile) {
   constexpr int GR = WAVE / LPR;                 // routed rows in parallel per wave
   constexpr int RGR = DOWN_RD / GR;              // routed rows per lane group
+  constexpr int NWD = down_threads<EF, CS>() / WAVE; // waves of the workgroup
   static_assert(DOWN_RD % GR == 0, "down rows must split over lane groups");
   __shared__ float y_lds[MAX_PAIRS * MAX_DOWN_TILE];
   __shared__ float ys_lds[MAX_ROWS * MAX_DOWN_TILE];
@@ -2214,7 +2220,7 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   // parts' totals are added in order in the blend.
   const int NP = a.down_parts;
   const int nsu = units * DQ * NP;
-  for (int su = wave; su < nsu; su += DOWN_WPB) {
+  for (int su = wave; su < nsu; su += NWD) {
     const int uq = su / NP, pt = su - uq * NP;
     const int u = uq / DQ, q = uq - u * DQ;
     const int hb = h0 + q * DOWN_RD;             // first column of this row block
@@ -2224,7 +2230,7 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
         nxt_slot = u - sh;
       }
       const DownRec rec = nxt;
-      const int su2 = su + DOWN_WPB;
+      const int su2 = su + NWD;
       if (su2 < nsu) {
         const int s2 = (su2 / NP) / DQ - sh;
         if (s2 >= 0 && s2 != nxt_slot) {
@@ -2292,7 +2298,7 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
 
   const bool out_f32 = (a.flags & OUT_F32) != 0 || ACT == F32;
   const int k = a.K;
-  for (int t = threadIdx.x; t < m * HT; t += DOWN_THREADS) {
+  for (int t = threadIdx.x; t < m * HT; t += down_threads<EF, CS>()) {
     const int r = t / HT, hl = t - r * HT, h = h0 + hl;
     if (h >= H) continue;
     float o = 0.f;
@@ -2588,7 +2594,7 @@ __global__ __launch_bounds__(THREADS, gate_up_min_waves<CR * 4 + SHD>()) void ga
 
 // Launch 3: down tiles with the blend.
 template <int EF, int ACT, int CR, int CS, int LPR>
-__global__ __launch_bounds__(DOWN_THREADS) void down_blend_kernel(Args a) {
+__global__ __launch_bounds__((down_threads<EF, CS>())) void down_blend_kernel(Args a) {
   down_item<EF, ACT, CR, CS, LPR>(a, blockIdx.x);
 }
 

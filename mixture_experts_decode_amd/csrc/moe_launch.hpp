@@ -78,7 +78,7 @@ const FormatKernels &kernels_bf16_nvfp4();
 #ifdef MOE_KERNELS_HPP_INCLUDED
 template <int EF, int ACT, int CR, int CS, int LPR>
 hipError_t launch_down_blend_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  return launch_timed(down_blend_kernel<EF, ACT, CR, CS, LPR>, blocks, DOWN_THREADS, st, start, stop, a);
+  return launch_timed(down_blend_kernel<EF, ACT, CR, CS, LPR>, blocks, down_threads<EF, CS>(), st, start, stop, a);
 }
 template <int EF>
 hipError_t launch_gate_up_grouped_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
