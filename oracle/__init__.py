@@ -32,7 +32,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(LIB_PATH):
         tmp = LIB_PATH + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
-                               "-o", tmp, _SRC, "-lm"])
+                               "-fopenmp", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
@@ -69,6 +69,12 @@ def lib():
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
         L.orc_e4m3_value.restype = C.c_double
         L.orc_e4m3_value.argtypes = [C.c_uint8]
+        L.orc_set_threads.restype = None
+        L.orc_set_threads.argtypes = [C.c_int32]
+        L.orc_get_threads.restype = C.c_int32
+        L.orc_get_threads.argtypes = []
+        L.orc_round_act.restype = C.c_double
+        L.orc_round_act.argtypes = [C.c_int32, C.c_double]
         L.orc_decode_act.restype = C.c_double
         L.orc_decode_act.argtypes = [C.c_int32, C.c_void_p, C.c_int64]
         L.orc_decode_row.restype = None
@@ -233,6 +239,21 @@ def decode_row(fmt: str, w: np.ndarray, s: Optional[np.ndarray], b: Optional[np.
 def e4m3_value(b: int) -> float:
     """One OCP FP8 E4M3 byte as a float (NaN for the NaN codes)."""
     return float(lib().orc_e4m3_value(int(b)))
+
+
+def set_threads(n: int) -> None:
+    """Threads (OpenMP) over each projection's output neurons; results do not
+    depend on the count."""
+    lib().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().orc_get_threads())
+
+
+def round_act(fmt: str, v: float) -> float:
+    """v rounded to the activation format ("f32", or "bf16": to nearest, ties to even)."""
+    return float(lib().orc_round_act(FMT[fmt], float(v)))
 
 
 def decode_act(fmt: str, a: np.ndarray) -> np.ndarray:

@@ -52,6 +52,7 @@
 #include "moe_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdlib.h>
 #include <string.h>
@@ -136,14 +137,20 @@ void orc_decode_row(int32_t fmt, const void *w, const void *s, const void *b,
 }
 
 /* A double rounded to the activation format: float32 (to nearest), or bf16
- * (8 significant bits, to nearest, ties to even; finite normal values). */
-static double round_act(int32_t fmt, double v) {
+ * to nearest, ties to even.  bf16 keeps float32's exponent range with 8
+ * significant bits: the spacing of the values in [2^(e-1), 2^e) is 2^(e-8),
+ * and below the smallest normal 2^-126 the subnormals keep the spacing
+ * 2^-133 of the lowest binade; a result past the largest finite value
+ * (2^128 - 2^120) rounds to infinity. */
+double orc_round_act(int32_t fmt, double v) {
   if (fmt == ORC_F32) return (double)(float)v;
   if (v == 0.0 || !isfinite(v)) return v;
   int e;
   frexp(v, &e);                          /* |v| in [2^(e-1), 2^e) */
+  if (e < -125) e = -125;                /* subnormal: the spacing of [2^-126, 2^-125) */
   const double quantum = ldexp(1.0, e - 8);
-  return nearbyint(v / quantum) * quantum; /* default rounding: to nearest, ties to even */
+  const double r = nearbyint(v / quantum) * quantum; /* default rounding: to nearest, ties to even */
+  return fabs(r) >= ldexp(1.0, 128) ? copysign(INFINITY, v) : r;
 }
 
 /* "helpers_a.rs", set_pre_expert_norm: one row's expert input, the RMS norm
@@ -154,8 +161,17 @@ void orc_pre_expert_norm(const orc_desc *d, const void *norm_w, const double *x,
   for (int32_t h = 0; h < H; ++h) ss += x[h] * x[h];
   const double inv = 1.0 / sqrt(ss / (double)H + d->norm_eps);
   for (int32_t h = 0; h < H; ++h)
-    xe[h] = round_act(d->act_fmt, x[h] * orc_decode_act(d->act_fmt, norm_w, h) * inv);
+    xe[h] = orc_round_act(d->act_fmt, x[h] * orc_decode_act(d->act_fmt, norm_w, h) * inv);
 }
+
+/* Threads over output neurons (OpenMP).  Each neuron's dot product is taken
+ * by one thread in the order of the definition, so the results do not depend
+ * on the thread count; 1 unless orc_set_threads says otherwise. */
+static int g_threads = 1;
+
+void orc_set_threads(int32_t n) { g_threads = n < 1 ? 1 : n; }
+
+int32_t orc_get_threads(void) { return g_threads; }
 
 /* ------------------------------------------------------------ small math */
 
@@ -193,6 +209,7 @@ void orc_routed_slot(const double *x, int32_t n, double w, int32_t before_ffn,
 void orc_router_logits(const orc_desc *d, const orc_weights *wt, const void *x_row,
                        double *logits) {
   const int32_t H = d->hidden;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
   for (int32_t e = 0; e < d->num_experts; ++e) {
     double acc = 0.0;
     for (int32_t h = 0; h < H; ++h)
@@ -301,18 +318,24 @@ void orc_sort_pairs(int32_t m, int32_t k, int32_t E, const int32_t *idx,
 static void swiglu_expert(int32_t fmt, int32_t geglu, const void *gw, const void *gs, const void *gb,
                           const void *uw, const void *us, const void *ub,
                           const void *dw, const void *ds, const void *db,
-                          int32_t H, int32_t I, const double *u, double *y,
-                          double *row, double *act) {
-  for (int32_t i = 0; i < I; ++i) {
-    orc_decode_row(fmt, gw, gs, gb, H, i, row);
-    double g = dot(row, u, H);
-    orc_decode_row(fmt, uw, us, ub, H, i, row);
-    double v = dot(row, u, H);
-    act[i] = (geglu ? gelu(g) : silu(g)) * v;
-  }
-  for (int32_t h = 0; h < H; ++h) {
-    orc_decode_row(fmt, dw, ds, db, I, h, row);
-    y[h] = dot(row, act, I);
+                          int32_t H, int32_t I, const double *u, double *y, double *act) {
+#pragma omp parallel num_threads(g_threads)
+  {
+    double *row = (double *)malloc(sizeof(double) * (size_t)(H > I ? H : I));
+#pragma omp for schedule(static)
+    for (int32_t i = 0; i < I; ++i) {
+      orc_decode_row(fmt, gw, gs, gb, H, i, row);
+      double g = dot(row, u, H);
+      orc_decode_row(fmt, uw, us, ub, H, i, row);
+      double v = dot(row, u, H);
+      act[i] = (geglu ? gelu(g) : silu(g)) * v;
+    }
+#pragma omp for schedule(static)
+    for (int32_t h = 0; h < H; ++h) {
+      orc_decode_row(fmt, dw, ds, db, I, h, row);
+      y[h] = dot(row, act, I);
+    }
+    free(row);
   }
 }
 
@@ -337,13 +360,11 @@ int32_t orc_forward(const orc_desc *d, const orc_weights *wt, const void *x, int
   if (!valid_desc(d) || m < 0) return -1;
   const int32_t H = d->hidden, E = d->num_experts, k = d->top_k, I = d->inter;
   const int32_t Is = d->shared ? d->shared_inter : 0;
-  const int32_t big = (H > I ? H : I) > Is ? (H > I ? H : I) : Is;
   double *xr = (double *)malloc(sizeof(double) * (size_t)H);
   double *xe = (double *)malloc(sizeof(double) * (size_t)H);   /* the experts' input */
   double *u = (double *)malloc(sizeof(double) * (size_t)H);
   double *y = (double *)malloc(sizeof(double) * (size_t)H);
   double *acc = (double *)malloc(sizeof(double) * (size_t)H);
-  double *row = (double *)malloc(sizeof(double) * (size_t)big);
   double *act = (double *)malloc(sizeof(double) * (size_t)(I > Is ? I : Is));
   double *lg = (double *)malloc(sizeof(double) * (size_t)E);
   int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
@@ -373,7 +394,7 @@ int32_t orc_forward(const orc_desc *d, const orc_weights *wt, const void *x, int
       orc_routed_slot(xe, H, sw[j], d->weight_before_ffn, u, &c);
       swiglu_expert(d->expert_fmt, d->geglu, wt->gate[e], tbl(wt->gate_s, e), tbl(wt->gate_b, e),
                     wt->up[e], tbl(wt->up_s, e), tbl(wt->up_b, e), wt->down[e],
-                    tbl(wt->down_s, e), tbl(wt->down_b, e), H, I, u, y, row, act);
+                    tbl(wt->down_s, e), tbl(wt->down_b, e), H, I, u, y, act);
       for (int32_t h = 0; h < H; ++h) acc[h] += c * y[h];
     }
     if (d->shared) {
@@ -388,11 +409,11 @@ int32_t orc_forward(const orc_desc *d, const orc_weights *wt, const void *x, int
         gamma = sigmoid(s);
       }
       swiglu_expert(d->act_fmt, d->geglu, wt->sh_gate, NULL, NULL, wt->sh_up, NULL, NULL,
-                    wt->sh_down, NULL, NULL, H, Is, xe, y, row, act);
+                    wt->sh_down, NULL, NULL, H, Is, xe, y, act);
       for (int32_t h = 0; h < H; ++h) acc[h] += gamma * y[h];
     }
     for (int32_t h = 0; h < H; ++h) out[(size_t)r * H + h] = acc[h];
   }
-  free(xr); free(xe); free(u); free(y); free(acc); free(row); free(act); free(lg); free(sel); free(sw);
+  free(xr); free(xe); free(u); free(y); free(acc); free(act); free(lg); free(sel); free(sw);
   return 0;
 }

@@ -50,6 +50,14 @@ typedef struct {
 
 /* One OCP FP8 E4M3 byte decoded to double (NaN for the NaN codes). */
 double orc_e4m3_value(uint8_t b);
+/* Threads the oracle spreads a projection's output neurons over (OpenMP;
+ * default 1).  Results are the same for every count. */
+void orc_set_threads(int32_t n);
+int32_t orc_get_threads(void);
+
+/* v rounded to the activation format (float32, or bf16 to nearest, ties to
+ * even, subnormals included), as a double. */
+double orc_round_act(int32_t fmt, double v);
 /* One stored element decoded to double. */
 double orc_decode_act(int32_t fmt, const void *p, int64_t i);
 /* Row n of an [N,K] expert projection, decoded to double, out[K]. */

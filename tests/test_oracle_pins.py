@@ -146,6 +146,76 @@ def test_bf16_and_f32_decode():
     assert np.array_equal(oracle.decode_act("f32", f), f.astype(np.float64))
 
 
+# ------------------------------------------- P-2 rounding to the activation format
+
+def _bf16_by_torch(f32: np.ndarray) -> np.ndarray:
+    """torch's float32 -> bfloat16 cast (an implementation independent of the
+    oracle), back to float64."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(f32, dtype=np.float32)).to(torch.bfloat16)
+    return t.to(torch.float32).numpy().astype(np.float64)
+
+
+def _round_bf16_by_oracle(vals: np.ndarray) -> np.ndarray:
+    return np.array([oracle.round_act("bf16", float(v)) for v in vals])
+
+
+def test_bf16_rounding_matches_torch_on_ties_and_edges():
+    # Exact midpoints between two bf16 values: the low 16 bits of the float32
+    # are 0x8000.  A kept mantissa that is even stays; an odd one rounds up
+    # (into the next binade, or to infinity past the largest finite value).
+    rng = np.random.default_rng(21)
+    hi = rng.integers(0, 0x7F80, 2048).astype(np.uint32)
+    hi = np.concatenate([hi, [0x0000, 0x0001, 0x007F, 0x0080, 0x3F7F, 0x3F80, 0x7F7E, 0x7F7F]]).astype(np.uint32)
+    sign = (rng.integers(0, 2, hi.size).astype(np.uint32) << 31)
+    ties = ((hi << 16) | 0x8000 | sign).view(np.float32)
+    # Off-midpoint neighbours, random finite patterns, the float32
+    # subnormals and the smallest normals.
+    below = ((hi << 16) | 0x7FFF | sign).view(np.float32)
+    above = ((hi << 16) | 0x8001 | sign).view(np.float32)
+    rnd = rng.integers(0, 0x7F800000, 4096).astype(np.uint32).view(np.float32)
+    sub = np.array([1, 2, 0x7FFF, 0x8000, 0x8001, 0x18000, 0x7FFFFF, 0x800000, 0x807FFF, 0x808000],
+                   np.uint32).view(np.float32)
+    for vals in (ties, below, above, rnd, sub, -sub):
+        assert np.array_equal(_round_bf16_by_oracle(vals), _bf16_by_torch(vals))
+    assert oracle.round_act("bf16", float(np.uint32(0x7F7F8000).view(np.float32))) == math.inf
+
+
+def test_bf16_rounding_closed_forms():
+    # Around 1 the bf16 spacing is 2^-7: 1 + 2^-8 is a tie to the even 1;
+    # 1 + 3 * 2^-8 is a tie between 1 + 2^-7 (odd) and 1 + 2^-6 (even).
+    assert oracle.round_act("bf16", 1 + 2.0 ** -8) == 1.0
+    assert oracle.round_act("bf16", 1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6
+    assert oracle.round_act("bf16", 1 + 2.0 ** -8 + 2.0 ** -30) == 1 + 2.0 ** -7
+    assert oracle.round_act("bf16", -(2 - 2.0 ** -9)) == -2.0      # up into the next binade
+    assert oracle.round_act("bf16", 3 * 2.0 ** -135) == 2.0 ** -133  # subnormal spacing 2^-133
+    assert oracle.round_act("bf16", 2.0 ** -134) == 0.0                 # tie to the even 0
+
+
+def test_f32_rounding_matches_numpy():
+    rng = np.random.default_rng(22)
+    v = rng.standard_normal(2000) * np.exp(rng.uniform(-60, 60, 2000))
+    got = np.array([oracle.round_act("f32", float(t)) for t in v])
+    assert np.array_equal(got, v.astype(np.float32).astype(np.float64))
+
+
+def test_results_do_not_depend_on_thread_count():
+    # The oracle spreads output neurons over OpenMP threads (the CPU
+    # baseline's second leg); each neuron's sum keeps its order.
+    spec = tiny(hidden=128, inter=96, shared=True, shared_gated=True, expert_fmt="mxfp4", rows=(3,))
+    layer = synth.make_layer(spec, seed=23)
+    x = layer.x(0)
+    one = oracle.forward(layer, x)
+    try:
+        oracle.set_threads(4)
+        assert oracle.get_threads() == 4
+        four = oracle.forward(layer, x)
+    finally:
+        oracle.set_threads(1)
+    assert np.array_equal(one.out, four.out) and np.array_equal(one.idx, four.idx)
+    assert np.array_equal(one.w, four.w) and np.array_equal(one.logits, four.logits)
+
+
 # ------------------------------------------------------ P-3 page's worked example
 
 def test_routed_slot_worked_example():
