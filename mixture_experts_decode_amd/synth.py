@@ -17,6 +17,7 @@ of them can be regenerated alone and the experts can be drawn in parallel):
     stream key [seed, 6, 0]      shared-expert gate vector w_g [H]
     stream key [seed, 7, b]      activation block b: x [max_rows, H]
     stream key [seed, 8, 0]      pre-expert norm weight [H]: 1 + z * 0.1
+    stream key [seed, 9, 0]      router pre-norm weight [H]: 1 + z * 0.1
 
 Each weight is ``f32(z * std)`` with ``z`` a float32 standard normal, then
 stored as f32, bf16 (RNE) or quantized (aff4 / mxfp4 / nvfp4 below).  ``x`` is
@@ -52,7 +53,7 @@ import numpy as np
 
 ACT_FORMATS = ("f32", "bf16")
 EXPERT_FORMATS = ("f32", "bf16", "aff4", "mxfp4", "nvfp4")
-ROUTINGS = ("softmax", "sigmoid_bias", "sigmoid_logit")
+ROUTINGS = ("softmax", "sigmoid_bias", "sigmoid_logit", "sqrtsoftplus")
 ACTIVATIONS = ("silu", "gelu")
 
 # Group sizes of the 4-bit formats along the reduction dimension K.
@@ -81,6 +82,8 @@ class LayerSpec:
     routed_scaling_factor: float = 1.0
     activation: str = "silu"        # expert activation: "silu" (SwiGLU) or "gelu" (GeGLU)
     pre_expert_norm: bool = False   # experts read the row RMS-normed (weight pre_norm_w); router: raw
+    router_pre_norm: bool = False   # the router reads the row RMS-normed (weight router_norm_w)
+    route_bias: Optional[bool] = None  # an expert bias [E] for selection (default: sigmoid_bias only)
     norm_eps: float = 1e-6
     w_std: float = 0.02
     x_std: float = 1.0
@@ -90,6 +93,11 @@ class LayerSpec:
     @property
     def max_rows(self) -> int:
         return max(self.rows)
+
+    @property
+    def biased(self) -> bool:
+        """Whether the layer has an expert bias (required by sigmoid_bias)."""
+        return self.routing == "sigmoid_bias" if self.route_bias is None else bool(self.route_bias)
 
     def replace(self, **kw) -> "LayerSpec":
         return dataclasses.replace(self, **kw)
@@ -289,6 +297,7 @@ class Layer:
     sh_down: Optional[np.ndarray]       # [H, Is] act_fmt
     sh_gate_vec: Optional[np.ndarray]   # [H] act_fmt
     pre_norm_w: Optional[np.ndarray] = None   # [H] act_fmt (pre_expert_norm)
+    router_norm_w: Optional[np.ndarray] = None   # [H] act_fmt (router_pre_norm)
 
     def x(self, block: int = 0, rows: Optional[int] = None) -> np.ndarray:
         return make_x(self.spec, self.seed, block, rows)
@@ -346,6 +355,10 @@ def check_spec(spec: LayerSpec) -> None:
         raise ValueError("bad routing")
     if spec.activation not in ACTIVATIONS:
         raise ValueError("bad activation")
+    if spec.routing == "sigmoid_bias" and not spec.biased:
+        raise ValueError("sigmoid_bias routing needs the expert bias")
+    if spec.biased and spec.routing not in ("sigmoid_bias", "sqrtsoftplus"):
+        raise ValueError("an expert bias serves sigmoid_bias and sqrtsoftplus routing only")
     if spec.expert_fmt == "aff4" and (spec.hidden % AFF4_GROUP or spec.inter % AFF4_GROUP):
         raise ValueError("aff4 needs H and I multiples of 64")
     if spec.expert_fmt == "mxfp4" and (spec.hidden % MXFP4_BLOCK or spec.inter % MXFP4_BLOCK):
@@ -360,7 +373,7 @@ def make_layer(spec: LayerSpec, seed: int = 0, threads: Optional[int] = None) ->
     H, E, I, Is = spec.hidden, spec.num_experts, spec.inter, spec.shared_inter
     router = _store_act(_draw(seed, 0, 0, (E, H), spec.w_std), spec.act_fmt)
     bias = None
-    if spec.routing == "sigmoid_bias":
+    if spec.biased:
         bias = _draw(seed, 1, 0, (E,), spec.bias_std).astype(np.float32)
     gate = _alloc_projection(spec.expert_fmt, E, I, H)
     up = _alloc_projection(spec.expert_fmt, E, I, H)
@@ -388,10 +401,12 @@ def make_layer(spec: LayerSpec, seed: int = 0, threads: Optional[int] = None) ->
         sh_down = _store_act(_draw(seed, 5, 2, (H, Is), spec.w_std), spec.act_fmt)
         if spec.shared_gated:
             sh_vec = _store_act(_draw(seed, 6, 0, (H,), spec.w_std), spec.act_fmt)
-    norm_w = None
+    norm_w = rnorm_w = None
     if spec.pre_expert_norm:
         norm_w = _store_act(_draw(seed, 8, 0, (H,), 0.1) + np.float32(1.0), spec.act_fmt)
-    return Layer(spec, seed, router, bias, gate, up, down, sh_gate, sh_up, sh_down, sh_vec, norm_w)
+    if spec.router_pre_norm:
+        rnorm_w = _store_act(_draw(seed, 9, 0, (H,), 0.1) + np.float32(1.0), spec.act_fmt)
+    return Layer(spec, seed, router, bias, gate, up, down, sh_gate, sh_up, sh_down, sh_vec, norm_w, rnorm_w)
 
 
 def make_x(spec: LayerSpec, seed: int = 0, block: int = 0, rows: Optional[int] = None) -> np.ndarray:

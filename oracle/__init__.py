@@ -24,7 +24,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 
 FMT = {"f32": 0, "bf16": 1, "aff4": 2, "mxfp4": 3, "nvfp4": 4}
-ROUTING = {"softmax": 0, "sigmoid_bias": 1, "sigmoid_logit": 2}
+ROUTING = {"softmax": 0, "sigmoid_bias": 1, "sigmoid_logit": 2, "sqrtsoftplus": 3}
 
 
 def build(force: bool = True) -> str:
@@ -42,7 +42,7 @@ class _Desc(C.Structure):
         "hidden", "num_experts", "top_k", "inter", "shared_inter", "act_fmt", "expert_fmt",
         "routing", "norm_topk", "weight_before_ffn", "shared", "shared_gated")] + [
         ("routed_scaling_factor", C.c_double), ("geglu", C.c_int32), ("pre_norm", C.c_int32),
-        ("norm_eps", C.c_double)]
+        ("norm_eps", C.c_double), ("router_pre_norm", C.c_int32)]
 
 
 _PP = C.POINTER(C.c_void_p)
@@ -52,7 +52,8 @@ class _Weights(C.Structure):
     _fields_ = [("router", C.c_void_p), ("expert_bias", C.c_void_p)] + [
         (n, _PP) for n in ("gate", "up", "down", "gate_s", "up_s", "down_s",
                            "gate_b", "up_b", "down_b")] + [
-        (n, C.c_void_p) for n in ("sh_gate", "sh_up", "sh_down", "sh_gate_vec", "pre_norm_w")]
+        (n, C.c_void_p) for n in ("sh_gate", "sh_up", "sh_down", "sh_gate_vec", "pre_norm_w",
+                                  "router_norm_w")]
 
 
 _lib = None
@@ -67,6 +68,8 @@ def lib():
         L.orc_forward.restype = C.c_int32
         L.orc_forward.argtypes = [C.POINTER(_Desc), C.POINTER(_Weights), C.c_void_p, C.c_int32,
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+        L.orc_sqrtsoftplus.restype = C.c_double
+        L.orc_sqrtsoftplus.argtypes = [C.c_double]
         L.orc_e4m3_value.restype = C.c_double
         L.orc_e4m3_value.argtypes = [C.c_uint8]
         L.orc_set_threads.restype = None
@@ -109,7 +112,7 @@ def desc_of(spec) -> _Desc:
                  FMT[spec.expert_fmt], ROUTING[spec.routing], int(spec.norm_topk),
                  int(spec.weight_before_ffn), int(spec.shared), int(spec.shared_gated),
                  float(spec.routed_scaling_factor), int(spec.activation == "gelu"),
-                 int(spec.pre_expert_norm), float(spec.norm_eps))
+                 int(spec.pre_expert_norm), float(spec.norm_eps), int(spec.router_pre_norm))
 
 
 def _table(arr: Optional[np.ndarray]):
@@ -146,6 +149,7 @@ class _Bound:
         w.sh_down = _ptr(layer.sh_down)
         w.sh_gate_vec = _ptr(layer.sh_gate_vec)
         w.pre_norm_w = _ptr(layer.pre_norm_w)
+        w.router_norm_w = _ptr(layer.router_norm_w)
         self.weights = w
 
 
@@ -234,6 +238,11 @@ def decode_row(fmt: str, w: np.ndarray, s: Optional[np.ndarray], b: Optional[np.
                          _ptr(None if s is None else np.ascontiguousarray(s)),
                          _ptr(None if b is None else np.ascontiguousarray(b)), K, n, _ptr(out))
     return out
+
+
+def sqrtsoftplus(v: float) -> float:
+    """The sqrt-softplus router score sqrt(log(1 + e^v))."""
+    return float(lib().orc_sqrtsoftplus(float(v)))
 
 
 def e4m3_value(b: int) -> float:

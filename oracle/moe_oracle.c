@@ -43,6 +43,20 @@
  *    the experts' input; the routed experts (through the weight placement)
  *    and the shared expert read xe, the router and the shared-expert gate
  *    read x;
+ *  - the sqrt-softplus router ("refactor(gemm): split the gemv_q8 grab-bag by
+ *    family", commit message: router_sqrtsoftplus among the routers, next to
+ *    the biased router that selects by the biased score and weights by the
+ *    unbiased one) scores an expert s = sqrt(softplus(l)), softplus(l) =
+ *    log(1 + e^l); it selects by s, or by s + bias when an expert bias is
+ *    given, and weights a slot by its unbiased s (then norm_topk_prob and
+ *    routed_scaling_factor as for the other routers);
+ *  - the router pre-norm ("forward_bf16_grouped_decode.rs", the predicate
+ *    refuses weights.router_pre_norm: a norm the router's input goes through)
+ *    is the RMS norm of each row with its own weight router_norm_w, stored in
+ *    the activation format like the pre-expert norm, with the same eps; only
+ *    the router's logits read it -- the experts, the shared expert and the
+ *    shared-expert gate read the row as it is (or, for the experts and the
+ *    shared expert, the pre-expert norm);
  *  - NVFP4 weights are the NVIDIA NVFP4 encoding the page names: E2M1 codes,
  *    one E4M3 block scale per 16 elements along K, times the projection's
  *    fp32 second-level scale; the activations stay in their own format
@@ -154,7 +168,8 @@ double orc_round_act(int32_t fmt, double v) {
 }
 
 /* "helpers_a.rs", set_pre_expert_norm: one row's expert input, the RMS norm
- * x * w / sqrt(mean(x^2) + eps) in the activation format. */
+ * x * w / sqrt(mean(x^2) + eps) in the activation format.  With the router's
+ * weight it is also the router pre-norm. */
 void orc_pre_expert_norm(const orc_desc *d, const void *norm_w, const double *x, double *xe) {
   const int32_t H = d->hidden;
   double ss = 0.0;
@@ -205,27 +220,41 @@ void orc_routed_slot(const double *x, int32_t n, double w, int32_t before_ffn,
 }
 
 /* "forward_bf16_grouped_decode.rs": the per-row router GEMV,
- * logits[e] = sum_h x[h] * Wr[e, h]. */
-void orc_router_logits(const orc_desc *d, const orc_weights *wt, const void *x_row,
-                       double *logits) {
+ * logits[e] = sum_h x[h] * Wr[e, h], of a decoded row x[H]. */
+static void router_logits(const orc_desc *d, const orc_weights *wt, const double *x, double *logits) {
   const int32_t H = d->hidden;
 #pragma omp parallel for num_threads(g_threads) schedule(static)
   for (int32_t e = 0; e < d->num_experts; ++e) {
     double acc = 0.0;
-    for (int32_t h = 0; h < H; ++h)
-      acc += orc_decode_act(d->act_fmt, x_row, h) *
-             orc_decode_act(d->act_fmt, wt->router, (int64_t)e * H + h);
+    for (int32_t h = 0; h < H; ++h) acc += x[h] * orc_decode_act(d->act_fmt, wt->router, (int64_t)e * H + h);
     logits[e] = acc;
   }
+}
+
+void orc_router_logits(const orc_desc *d, const orc_weights *wt, const void *x_row,
+                       double *logits) {
+  double *x = (double *)malloc(sizeof(double) * (size_t)d->hidden);
+  for (int32_t h = 0; h < d->hidden; ++h) x[h] = orc_decode_act(d->act_fmt, x_row, h);
+  router_logits(d, wt, x, logits);
+  free(x);
+}
+
+/* softplus(l) = log(1 + e^l), taken as l + log(1 + e^-l) for l > 0 so that
+ * e^l never overflows; the score is its square root. */
+double orc_sqrtsoftplus(double l) {
+  const double sp = l > 0.0 ? l + log1p(exp(-l)) : log1p(exp(l));
+  return sqrt(sp);
 }
 
 /* Selection key of expert e.  Softmax: the logit (same order as the
  * probability).  Sigmoid with bias ("wire lfm2" Summary; iron #24 commit:
  * select by the biased score): sigmoid(logit) + bias.  Raw-logit sigmoid
  * ("routed_weight_site.rs" module doc: top-k on the raw logits, a monotone
- * map of the sigmoid): the logit. */
+ * map of the sigmoid): the logit.  Sqrt-softplus: the score, plus the bias
+ * when one is given. */
 static double select_key(const orc_desc *d, const float *bias, const double *l, int32_t e) {
   if (d->routing == ORC_SIGMOID_BIAS) return sigmoid(l[e]) + (double)bias[e];
+  if (d->routing == ORC_SQRTSOFTPLUS) return orc_sqrtsoftplus(l[e]) + (bias ? (double)bias[e] : 0.0);
   return l[e];
 }
 
@@ -269,6 +298,9 @@ void orc_select(const orc_desc *d, const float *expert_bias, const double *logit
     double den = 0.0;
     for (int32_t e = 0; e < E; ++e) den += exp(logits[e] - lmax);
     for (int32_t j = 0; j < k; ++j) w[j] = exp(logits[idx[j]] - lmax) / den;
+  } else if (d->routing == ORC_SQRTSOFTPLUS) {
+    /* The unbiased score of the selected expert. */
+    for (int32_t j = 0; j < k; ++j) w[j] = orc_sqrtsoftplus(logits[idx[j]]);
   } else {
     /* Both sigmoid modes weight by the unbiased sigmoid of the logit. */
     for (int32_t j = 0; j < k; ++j) w[j] = sigmoid(logits[idx[j]]);
@@ -346,12 +378,12 @@ static int valid_desc(const orc_desc *d) {
   if (d->top_k <= 0 || d->top_k > d->num_experts) return 0;
   if (d->act_fmt != ORC_F32 && d->act_fmt != ORC_BF16) return 0;
   if (d->expert_fmt < ORC_F32 || d->expert_fmt > ORC_NVFP4) return 0;
-  if (d->routing < ORC_SOFTMAX || d->routing > ORC_SIGMOID_LOGIT) return 0;
+  if (d->routing < ORC_SOFTMAX || d->routing > ORC_SQRTSOFTPLUS) return 0;
   if (d->expert_fmt == ORC_AFF4 && (d->hidden % 64 || d->inter % 64)) return 0;
   if (d->expert_fmt == ORC_MXFP4 && (d->hidden % 32 || d->inter % 32)) return 0;
   if (d->expert_fmt == ORC_NVFP4 && (d->hidden % 16 || d->inter % 16)) return 0;
   if (d->shared && d->shared_inter <= 0) return 0;
-  if (d->pre_norm && !(d->norm_eps >= 0.0)) return 0;
+  if ((d->pre_norm || d->router_pre_norm) && !(d->norm_eps >= 0.0)) return 0;
   return 1;
 }
 
@@ -362,6 +394,7 @@ int32_t orc_forward(const orc_desc *d, const orc_weights *wt, const void *x, int
   const int32_t Is = d->shared ? d->shared_inter : 0;
   double *xr = (double *)malloc(sizeof(double) * (size_t)H);
   double *xe = (double *)malloc(sizeof(double) * (size_t)H);   /* the experts' input */
+  double *xn = (double *)malloc(sizeof(double) * (size_t)H);   /* the router's input */
   double *u = (double *)malloc(sizeof(double) * (size_t)H);
   double *y = (double *)malloc(sizeof(double) * (size_t)H);
   double *acc = (double *)malloc(sizeof(double) * (size_t)H);
@@ -378,7 +411,11 @@ int32_t orc_forward(const orc_desc *d, const orc_weights *wt, const void *x, int
       orc_pre_expert_norm(d, wt->pre_norm_w, xr, xe);
     else
       for (int32_t h = 0; h < H; ++h) xe[h] = xr[h];
-    orc_router_logits(d, wt, xrow, lg);
+    if (d->router_pre_norm)
+      orc_pre_expert_norm(d, wt->router_norm_w, xr, xn);   /* the same RMS norm, the router's weight */
+    else
+      for (int32_t h = 0; h < H; ++h) xn[h] = xr[h];
+    router_logits(d, wt, xn, lg);
     orc_select(d, wt->expert_bias, lg, sel, sw, margin ? &margin[r] : NULL);
     if (idx)
       for (int32_t j = 0; j < k; ++j) idx[(size_t)r * k + j] = sel[j];
@@ -414,6 +451,6 @@ int32_t orc_forward(const orc_desc *d, const orc_weights *wt, const void *x, int
     }
     for (int32_t h = 0; h < H; ++h) out[(size_t)r * H + h] = acc[h];
   }
-  free(xr); free(xe); free(u); free(y); free(acc); free(act); free(lg); free(sel); free(sw);
+  free(xr); free(xe); free(xn); free(u); free(y); free(acc); free(act); free(lg); free(sel); free(sw);
   return 0;
 }

@@ -19,7 +19,7 @@ extern "C" {
 /* Storage formats (numbers chosen independently of the HIP library's). */
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_AFF4 = 2, ORC_MXFP4 = 3, ORC_NVFP4 = 4 };
 /* Routing modes. */
-enum { ORC_SOFTMAX = 0, ORC_SIGMOID_BIAS = 1, ORC_SIGMOID_LOGIT = 2 };
+enum { ORC_SOFTMAX = 0, ORC_SIGMOID_BIAS = 1, ORC_SIGMOID_LOGIT = 2, ORC_SQRTSOFTPLUS = 3 };
 
 typedef struct {
   int32_t hidden, num_experts, top_k, inter, shared_inter;
@@ -31,6 +31,7 @@ typedef struct {
   int32_t geglu;        /* expert activation gelu(gate) * up instead of silu(gate) * up */
   int32_t pre_norm;     /* experts read the row RMS-normed with pre_norm_w (router: raw) */
   double norm_eps;
+  int32_t router_pre_norm; /* the router reads the row RMS-normed with router_norm_w */
 } orc_desc;
 
 typedef struct {
@@ -46,6 +47,7 @@ typedef struct {
   const void *sh_gate, *sh_up, *sh_down; /* [Is,H],[Is,H],[H,Is] act_fmt */
   const void *sh_gate_vec;               /* [H] act_fmt */
   const void *pre_norm_w;                /* [H] act_fmt (pre_norm) */
+  const void *router_norm_w;             /* [H] act_fmt (router_pre_norm) */
 } orc_weights;
 
 /* One OCP FP8 E4M3 byte decoded to double (NaN for the NaN codes). */
@@ -71,11 +73,16 @@ void orc_pre_expert_norm(const orc_desc *d, const void *norm_w, const double *x,
 void orc_routed_slot(const double *x, int32_t n, double w, int32_t before_ffn,
                      double *x_out, double *w_out);
 
-/* Router logits of one row: logits[E]. */
+/* Router logits of one row: logits[E] (x_row stored in act_fmt, read as it
+ * is: the router pre-norm is applied by orc_forward). */
 void orc_router_logits(const orc_desc *d, const orc_weights *wt, const void *x_row,
                        double *logits);
 
-/* Selection and weights of one row from its logits. idx[k], w[k]; margin =
+/* The sqrt-softplus score sqrt(log(1 + e^l)). */
+double orc_sqrtsoftplus(double l);
+
+/* Selection and weights of one row from its logits (expert_bias: [E], or NULL
+ * where the routing takes none). idx[k], w[k]; margin =
  * smallest gap between consecutive keys among the top min(k+1,E) keys. */
 void orc_select(const orc_desc *d, const float *expert_bias, const double *logits,
                 int32_t *idx, double *w, double *margin);

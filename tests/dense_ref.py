@@ -82,15 +82,29 @@ def round_to_act(v: np.ndarray, fmt: str) -> np.ndarray:
     return np.where(v == 0, 0.0, np.rint(v / q) * q)
 
 
+def _sqrtsoftplus(v):
+    return np.sqrt(np.logaddexp(0.0, v))                 # log(e^0 + e^v)
+
+
+def _rms_normed(X, w_bits, spec):
+    w = act_to_f64(w_bits, spec.act_fmt)
+    inv = 1.0 / np.sqrt(np.mean(X * X, axis=1, keepdims=True) + spec.norm_eps)
+    return round_to_act(X * w[None, :] * inv, spec.act_fmt)
+
+
 def dense_forward(layer, x: np.ndarray):
     """Returns (out [m,H], mask-weight matrix [m,E], selected index lists)."""
     spec = layer.spec
     E, k = spec.num_experts, spec.top_k
     X = act_to_f64(x, spec.act_fmt)                      # [m, H]
     Wr = act_to_f64(layer.router, spec.act_fmt)          # [E, H]
-    L = X @ Wr.T                                         # [m, E]
+    XR = _rms_normed(X, layer.router_norm_w, spec) if spec.router_pre_norm else X
+    L = XR @ Wr.T                                        # [m, E]
+    bias = 0.0 if layer.expert_bias is None else layer.expert_bias.astype(np.float64)[None, :]
     if spec.routing == "sigmoid_bias":
-        key = _sigmoid(L) + layer.expert_bias.astype(np.float64)[None, :]
+        key = _sigmoid(L) + bias
+    elif spec.routing == "sqrtsoftplus":
+        key = _sqrtsoftplus(L) + bias
     else:
         key = L
     m = X.shape[0]
@@ -103,6 +117,8 @@ def dense_forward(layer, x: np.ndarray):
             p = np.exp(L[r] - L[r].max())
             p = p / p.sum()
             wsel = p[order]
+        elif spec.routing == "sqrtsoftplus":
+            wsel = _sqrtsoftplus(L[r][order])
         else:
             wsel = _sigmoid(L[r][order])
         if spec.norm_topk:
@@ -113,11 +129,7 @@ def dense_forward(layer, x: np.ndarray):
     for r, order in enumerate(selected):
         mask[r, order] = True
     # The experts' input: the row itself, or RMS-normed (the router above read X).
-    XE = X
-    if spec.pre_expert_norm:
-        w_n = act_to_f64(layer.pre_norm_w, spec.act_fmt)
-        inv = 1.0 / np.sqrt(np.mean(X * X, axis=1, keepdims=True) + spec.norm_eps)
-        XE = round_to_act(X * w_n[None, :] * inv, spec.act_fmt)
+    XE = _rms_normed(X, layer.pre_norm_w, spec) if spec.pre_expert_norm else X
     out = np.zeros_like(X)
     for e in range(E):
         Wg = dense_weight(layer.gate, e)

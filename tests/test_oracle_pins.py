@@ -648,3 +648,142 @@ def test_invalid_description_rejected():
     spec = tiny(expert_fmt="aff4", inter=32)      # aff4 needs I % 64 == 0
     with pytest.raises(ValueError):
         synth.check_spec(spec)
+
+
+# ------------------------------------- P-19 the sqrt-softplus router score
+
+def test_sqrtsoftplus_closed_forms():
+    # softplus(0) = ln 2; softplus(l) -> l for large l and -> e^l for very
+    # negative l; against NumPy's log(e^0 + e^l) on a grid.
+    assert oracle.sqrtsoftplus(0.0) == math.sqrt(math.log(2.0))
+    assert math.isclose(oracle.sqrtsoftplus(40.0), math.sqrt(40.0), rel_tol=1e-15)
+    assert math.isclose(oracle.sqrtsoftplus(-40.0), math.exp(-20.0), rel_tol=1e-12)
+    grid = np.linspace(-30, 30, 601)
+    got = np.array([oracle.sqrtsoftplus(float(v)) for v in grid])
+    assert np.allclose(got, np.sqrt(np.logaddexp(0.0, grid)), rtol=1e-14, atol=0)
+    assert np.all(np.diff(got) > 0)                        # strictly increasing
+
+
+@pytest.mark.parametrize("norm", [False, True])
+def test_sqrtsoftplus_zero_input_ties(norm):
+    # x = 0: every score is sqrt(ln 2), a tie everywhere: experts 0..k-1;
+    # weights 1/k normalised, else sqrt(ln 2) times the scaling factor.
+    spec = tiny(routing="sqrtsoftplus", top_k=3, norm_topk=norm, routed_scaling_factor=1.5)
+    layer = synth.make_layer(spec, seed=31)
+    r = oracle.forward(layer, np.zeros((2, 64), np.float32))
+    assert np.array_equal(r.idx, np.tile(np.arange(3), (2, 1)))
+    want = 1.5 / 3 if norm else 1.5 * math.sqrt(math.log(2.0))
+    assert np.allclose(r.w, want, rtol=1e-15, atol=0)
+    assert np.all(r.out == 0.0)
+
+
+def test_sqrtsoftplus_selects_like_the_raw_logits_without_bias():
+    # A strictly increasing score selects the same experts, in the same
+    # order, as the raw-logit router on the same logits.
+    for seed in range(6):
+        spec = tiny(routing="sqrtsoftplus", num_experts=32, top_k=4)
+        layer = synth.make_layer(spec, seed=40 + seed)
+        x = synth.make_x(spec, 40 + seed, rows=4)
+        raw = synth.make_layer(spec.replace(routing="sigmoid_logit"), seed=40 + seed)
+        a, b = oracle.forward(layer, x), oracle.forward(raw, x)
+        assert np.array_equal(a.logits, b.logits) and np.array_equal(a.idx, b.idx)
+        sel = np.take_along_axis(a.logits, a.idx.astype(np.int64), axis=1)
+        want = np.sqrt(np.logaddexp(0.0, sel))
+        assert np.allclose(a.w, want / want.sum(axis=1, keepdims=True), rtol=1e-14, atol=0)
+
+
+def test_sqrtsoftplus_bias_selects_unbiased_weights():
+    # With an expert bias the selection is the top k of score + bias (ties to
+    # the lower index), the weights the unbiased scores normalised.
+    spec = tiny(routing="sqrtsoftplus", num_experts=16, top_k=4, route_bias=True, bias_std=0.5)
+    layer = synth.make_layer(spec, seed=44)
+    x = synth.make_x(spec, 44, rows=4)
+    r = oracle.forward(layer, x)
+    score = np.sqrt(np.logaddexp(0.0, r.logits))
+    key = score + layer.expert_bias.astype(np.float64)[None, :]
+    for row in range(4):
+        order = np.argsort(-key[row], kind="stable")[:4]
+        assert list(r.idx[row]) == list(order)
+        w = score[row, order]
+        assert np.allclose(r.w[row], w / w.sum(), rtol=1e-14, atol=0)
+    # ...and it differs from the unbiased selection somewhere.
+    plain = oracle.forward(synth.make_layer(spec.replace(route_bias=False), seed=44), x)
+    assert not np.array_equal(plain.idx, r.idx)
+
+
+SQSP_VARIANTS = list(itertools.product(["f32", "bf16"], ["bf16", "mxfp4"], [False, True], [False, True]))
+
+
+@pytest.mark.parametrize("act,fmt,bias,before", SQSP_VARIANTS)
+def test_sqrtsoftplus_matches_dense_brute_force(act, fmt, bias, before):
+    spec = tiny(act_fmt=act, expert_fmt=fmt, routing="sqrtsoftplus", route_bias=bias,
+                weight_before_ffn=before, top_k=3, routed_scaling_factor=1.5, shared=True,
+                shared_gated=True, shared_inter=32, w_std=0.1)
+    seed = 1100 + SQSP_VARIANTS.index((act, fmt, bias, before))
+    layer = synth.make_layer(spec, seed=seed, threads=1)
+    x = synth.make_x(spec, seed, rows=4)
+    r = oracle.forward(layer, x)
+    want, weights, selected = dense_ref.dense_forward(layer, x)
+    for row in range(4):
+        assert list(r.idx[row]) == list(selected[row])
+        assert np.allclose(r.w[row], weights[row, selected[row]], rtol=1e-14, atol=0)
+    assert np.max(np.abs(r.out - want)) <= 1e-12 * rms(want)
+
+
+# --------------------------------------------------- P-20 the router pre-norm
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_router_pre_norm_logits_are_those_of_the_normed_row(act):
+    # The logits equal the router's logits of the row normed outside the
+    # oracle (NumPy RMS norm, torch's rounding to bf16).
+    spec = tiny(act_fmt=act, routing="softmax", router_pre_norm=True, norm_eps=1e-5, top_k=2,
+                shared=True, shared_gated=True, shared_inter=32)
+    layer = synth.make_layer(spec, seed=51)
+    x = synth.make_x(spec, 51, rows=4)
+    r = oracle.forward(layer, x)
+    X = dense_ref.act_to_f64(x, act)
+    w = dense_ref.act_to_f64(layer.router_norm_w, act)
+    xn = X * w[None, :] / np.sqrt(np.mean(X * X, axis=1, keepdims=True) + 1e-5)
+    if act == "bf16":
+        import torch
+        xn_bits = torch.from_numpy(xn.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        # (xn rounded to float32 first: a double-rounding difference would show as a mismatch)
+    else:
+        xn_bits = xn.astype(np.float32)
+    for row in range(4):
+        assert np.array_equal(oracle.router_logits(layer, xn_bits[row]), r.logits[row])
+    # ...and not those of the raw row.
+    assert not np.array_equal(oracle.router_logits(layer, x[0]), r.logits[0])
+
+
+def test_router_pre_norm_scale_invariant_shared_gate_raw():
+    # eps = 0: x and 4 x give the router the same normed row (same logits,
+    # bit for bit); the shared-expert gate reads the raw row, so the output
+    # changes with the scale.
+    spec = tiny(act_fmt="f32", routing="softmax", router_pre_norm=True, norm_eps=0.0, top_k=2,
+                shared=True, shared_gated=True, shared_inter=32)
+    layer = synth.make_layer(spec, seed=52)
+    x = synth.make_x(spec, 52, rows=3)
+    r1, r4 = oracle.forward(layer, x), oracle.forward(layer, (x * 4).astype(np.float32))
+    assert np.array_equal(r1.logits, r4.logits) and np.array_equal(r1.idx, r4.idx)
+    assert not np.allclose(r1.out * 4, r4.out)
+
+
+RPN_VARIANTS = list(itertools.product(["f32", "bf16"], ["bf16", "aff4"], ["softmax", "sqrtsoftplus"],
+                                      [False, True]))
+
+
+@pytest.mark.parametrize("act,fmt,routing,expert_norm", RPN_VARIANTS)
+def test_router_pre_norm_matches_dense_brute_force(act, fmt, routing, expert_norm):
+    spec = tiny(act_fmt=act, expert_fmt=fmt, routing=routing, router_pre_norm=True,
+                pre_expert_norm=expert_norm, top_k=3, shared=True, shared_gated=True, shared_inter=32,
+                w_std=0.1)
+    seed = 1200 + RPN_VARIANTS.index((act, fmt, routing, expert_norm))
+    layer = synth.make_layer(spec, seed=seed, threads=1)
+    x = synth.make_x(spec, seed, rows=4)
+    r = oracle.forward(layer, x)
+    want, weights, selected = dense_ref.dense_forward(layer, x)
+    for row in range(4):
+        assert list(r.idx[row]) == list(selected[row])
+        assert np.allclose(r.w[row], weights[row, selected[row]], rtol=1e-14, atol=0)
+    assert np.max(np.abs(r.out - want)) <= 1e-12 * rms(want)
