@@ -32,11 +32,11 @@
  * m = 1..32 is the fused decode path the page describes (three launches).
  * m = 33..256 (prefill chunks, speculative-decoding verification) takes a
  * grouped path of the same steps whose expert products run on the matrix
- * cores (five launches); it needs bf16 activations, bf16, mxfp4 or nvfp4
- * experts and H, I, Is multiples of 32, which moe_decode_plan checks when
- * max_rows > 32.  Each
- * path gives a row the same bits for every m it serves; the two paths agree
- * within the tolerance of their accumulation orders.
+ * cores (five launches); it needs bf16 activations, bf16, aff4, mxfp4 or
+ * nvfp4 experts and H, I, Is multiples of 32, which moe_decode_plan checks
+ * when max_rows > 32.  Each path gives a row the same bits for every m it
+ * serves; the two paths agree within the tolerance of their accumulation
+ * orders.
  *
  * Ownership: the caller owns every device buffer (weights, pointer tables,
  * x, out, idx/w outputs, workspace).  A plan owns host memory only; it is
@@ -93,7 +93,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_AFF4_G64 = 2, MOE_MXFP4_B32 = 3, M
 typedef enum {
   MOE_ROUTE_SOFTMAX = 0,        /* select by logit, weight softmax(l) over all E */
   MOE_ROUTE_SIGMOID_BIAS = 1,   /* select by sigmoid(l)+bias, weight sigmoid(l) */
-  MOE_ROUTE_SIGMOID_LOGIT = 2   /* select by logit, weight sigmoid(l) */
+  MOE_ROUTE_SIGMOID_LOGIT = 2,  /* select by logit, weight sigmoid(l) */
+  MOE_ROUTE_SQRTSOFTPLUS = 3    /* score s = sqrt(log(1 + e^l)): select by s, or by s + bias when
+                                   expert_bias is given; weight s (iron page "refactor(gemm): split
+                                   the gemv_q8 grab-bag by family", commit message: router_sqrtsoftplus) */
 } moe_routing;
 
 enum {
@@ -105,11 +108,15 @@ enum {
   MOE_GEGLU = 32,             /* expert activation gelu(gate) * up (GeGLU, exact GELU
                                  g * Phi(g)) instead of silu(gate) * up, routed and shared;
                                  metrale "helpers_a.rs", set_gelu_activation */
-  MOE_PRE_EXPERT_NORM = 64    /* the experts (routed and shared) read each row RMS-normed,
+  MOE_PRE_EXPERT_NORM = 64,   /* the experts (routed and shared) read each row RMS-normed,
                                  x * w / sqrt(mean(x^2) + norm_eps) with w = pre_norm_w,
                                  stored in act_fmt (to nearest, ties to even); the router and
                                  the shared-expert gate read the row as it is.  metrale
                                  "helpers_a.rs", set_pre_expert_norm */
+  MOE_ROUTER_PRE_NORM = 128   /* the router reads each row RMS-normed with router_norm_w (same
+                                 form, norm_eps and rounding as the pre-expert norm); the experts
+                                 and the shared-expert gate do not.  metrale
+                                 "forward_bf16_grouped_decode.rs" (weights.router_pre_norm) */
 };
 
 typedef struct {
@@ -124,7 +131,7 @@ typedef struct {
   int32_t routing;       /* moe_routing */
   uint32_t flags;        /* MOE_NORM_TOPK | MOE_WEIGHT_BEFORE_FFN | MOE_SHARED | ... */
   float routed_scaling_factor;
-  float norm_eps;        /* MOE_PRE_EXPERT_NORM: finite, >= 0; else ignored */
+  float norm_eps;        /* MOE_PRE_EXPERT_NORM, MOE_ROUTER_PRE_NORM: finite, >= 0; else ignored */
 } moe_decode_desc;
 
 /* Device pointers.  The per-expert tables are DEVICE arrays of E uint64
@@ -132,7 +139,8 @@ typedef struct {
  * 16-byte aligned, which the library documents but does not check. */
 typedef struct {
   const void *router_w;        /* [E, H] act_fmt */
-  const float *expert_bias;    /* [E] float32; MOE_ROUTE_SIGMOID_BIAS only, else NULL */
+  const float *expert_bias;    /* [E] float32; required by MOE_ROUTE_SIGMOID_BIAS, optional with
+                                  MOE_ROUTE_SQRTSOFTPLUS, ignored otherwise */
   const uint64_t *gate_w;      /* table: [I, H] (packed [I, H/2] for 4-bit) */
   const uint64_t *up_w;        /* table: [I, H] */
   const uint64_t *down_w;      /* table: [H, I] (packed [H, I/2]) */
@@ -151,6 +159,7 @@ typedef struct {
   const float *up_scale2;      /* nvfp4: [E] float32, up */
   const float *down_scale2;    /* nvfp4: [E] float32, down */
   const void *pre_norm_w;      /* [H] act_fmt (MOE_PRE_EXPERT_NORM), 16-byte aligned */
+  const void *router_norm_w;   /* [H] act_fmt (MOE_ROUTER_PRE_NORM), 16-byte aligned */
 } moe_decode_weights;
 
 typedef struct moe_decode_plan moe_decode_plan_t;
@@ -160,6 +169,8 @@ typedef struct moe_decode_plan moe_decode_plan_t;
  * te = max_rows * top_k, cap = min(te, E). */
 typedef struct {
   size_t logits;          /* double [max_rows, E+1]: router logits; column E = x . w_g */
+  size_t scores;          /* double [max_rows, E]: sqrt-softplus scores of the logits
+                             (MOE_ROUTE_SQRTSOFTPLUS; a 4-byte placeholder otherwise) */
   size_t topk_idx;        /* int32 [te]: selected experts, row-major [m, k] */
   size_t topk_w;          /* float [te]: routing weights (before placement) */
   size_t row_gate;        /* float [max_rows]: shared-expert gate gamma_r */
@@ -169,7 +180,8 @@ typedef struct {
   size_t active_experts;  /* int32 [cap]: experts with at least one pair, ascending */
   size_t active_count;    /* int32 [1] */
   size_t slot_info;       /* [cap] 128-byte records, one per active slot u < active_count:
-                             int32 expert, first position in sorted_pair, pair count, 0;
+                             int32 expert, first position in sorted_pair, pair count, and a
+                             tag (odd) that hashes the call's tables, x, workspace and m;
                              then the expert's gate_w, up_w, gate_s, up_s, gate_b, up_b,
                              down_w, down_s, down_b entries (uint64), then 40 zero bytes */
   size_t act;             /* float [te, I]: routed SwiGLU activations, sorted order; for 4-bit
@@ -182,15 +194,27 @@ typedef struct {
                              (m > 32 only; a 4-byte placeholder when max_rows <= 32) */
   size_t normed_x;        /* act_fmt [max_rows, H]: the experts' input under
                              MOE_PRE_EXPERT_NORM (a 4-byte placeholder without it) */
-  size_t sync;            /* uint32 [512]: reserved counters, zero between calls (word 0
-                             counts the router workgroups, word 1 the top-k workgroups of
-                             the m > 32 path; the last arrival resets each) */
+  size_t router_x;        /* act_fmt [max_rows, H]: the router's input under
+                             MOE_ROUTER_PRE_NORM (a 4-byte placeholder without it) */
+  size_t sync;            /* uint32 [512]: reserved words.  Word 0 counts the router
+                             workgroups, word 1 the top-k workgroups of the m > 32 path;
+                             the last arrival resets each and the forward's next launch
+                             resets it again, so a forward leaves them zero whatever it
+                             found there.  Word 2 holds the tag of the last call whose
+                             routing was published: the launches that read the slot records
+                             take routed work only when it is their call's.  The rest stay
+                             zero. */
   size_t total;           /* bytes a workspace must have */
 } moe_decode_ws_layout;
 
-/* Validate a layer description and build a plan.  MOE_EUNSUPPORTED for shapes
- * or format combinations the kernels do not serve; *workspace_bytes receives
- * the workspace size (alignment 256 bytes). */
+/* Validate a layer description and build a plan: the predicate of the metrale
+ * page "forward_bf16_grouped_decode.rs" (fn bf16_grouped_decode_arena_ok and
+ * bf16_grouped_decode_ok: the shape, weight, kernel and arena terms decided
+ * before anything runs, the m cap, the arena need of grouped_decode_buffer_need
+ * here returned as the workspace size).  MOE_EUNSUPPORTED for shapes or format
+ * combinations the kernels do not serve, MOE_EINVAL for malformed fields;
+ * *workspace_bytes receives the workspace size (alignment 256 bytes).  The
+ * plan is host memory the caller releases with moe_decode_plan_destroy. */
 moe_status moe_decode_plan(const moe_decode_desc *desc, moe_decode_plan_t **plan,
                            size_t *workspace_bytes);
 
@@ -202,11 +226,20 @@ moe_status moe_decode_workspace_layout(const moe_decode_plan_t *plan,
 
 /* Prepare a freshly allocated workspace (zeroes its reserved completion words
  * with a kernel on `stream`).  Call once before the first forward on a
- * workspace; forwards leave them zero. */
+ * workspace; forwards leave them zero.  Without it, the first forward on the
+ * workspace may route from an incomplete set of logits (its output is then
+ * wrong; it reads only in-range memory) and every later forward is correct. */
 moe_status moe_decode_workspace_init(const moe_decode_plan_t *plan, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
-/* The layer on m rows.
+/* The layer on m rows: fn forward_bf16_grouped_decode of the metrale page
+ * "forward_bf16_grouped_decode.rs" -- the per-row router, the sort of the
+ * (row, slot) pairs by expert, gate+up with the activation, down, and the blend
+ * with the shared expert, the output landing in rows 0..m of `out`, an error
+ * returned with nothing launched when the predicate fails; the routing of the
+ * mlxcel page "perf(moe): wire lfm2 to the fused decode-MoE kernel" (Summary)
+ * and the weight placement of the frink page "routed_weight_site.rs"
+ * (fn routed_slot) as described at the top of this file.
  *   x          device [m, H] act_fmt
  *   out        device [m, H] act_fmt (float32 with MOE_OUT_F32)
  *   idx_out    device int32 [m, k] selected experts, or NULL

@@ -62,9 +62,9 @@ bool log_enabled() {
 }
 
 // Kernel arrangement: the work items as three launches ordered by the
-// stream.  (A single persistent launch is written but not enabled: its first
-// launches on MI355X did not finish and the cause is not identified, so a
-// plan asking for it with MOE_DECODE_VARIANT=fused is refused.)
+// stream.  (A single persistent launch that chained the steps through
+// completion words and bounded waits did not finish on MI355X; it was removed,
+// and a plan asking for it with MOE_DECODE_VARIANT=fused is refused.)
 constexpr int kSplit = 1;
 const char *const kSplitStages[] = {"route", "gate_up", "down_blend"};
 int num_stages(int) { return 3; }
@@ -78,14 +78,14 @@ bool fused_requested() {
   return v && strcmp(v, "fused") == 0;
 }
 
-// Where a forward of m rows computes the routing.  Every gate/up workgroup
-// (from the logits, in LDS) starts the expert streaming soonest when the
-// routing is small; for more rows the router workgroup that finishes last
-// computes it once and publishes it.  MOE_DECODE_ROUTE=gate_up|once forces
-// one placement (both give identical results; the tests run both).
+// Where a forward of m rows computes the routing.  For one row every gate/up
+// workgroup computes it (from the logits, in LDS), which starts the expert
+// streaming soonest; for more rows the router workgroup that finishes last
+// computes it once and publishes it (the only placement the variants of
+// m > 1 carry).  MOE_DECODE_ROUTE=once forces the published placement at
+// m = 1 too (both give identical results; the tests run both).
 bool route_in_gate_up(int m) {
   const char *v = getenv("MOE_DECODE_ROUTE");
-  if (v && strcmp(v, "gate_up") == 0) return true;
   if (v && strcmp(v, "once") == 0) return false;
   return m == 1;
 }
@@ -126,18 +126,44 @@ const moe::FormatKernels &kernels_for(int act, int ef) {
   return t[act][ef]();
 }
 
+// Whether the shared expert runs on the matrix cores: bf16 activations with
+// H and Is multiples of 32 (gate/up in the route launch, down in the gate/up
+// launch); on the vector units otherwise.
+bool shared_on_matrix_cores(const moe_decode_desc &d) {
+  return (d.flags & MOE_SHARED) && d.act_fmt == MOE_BF16 && d.hidden % 32 == 0 && d.shared_inter % 32 == 0;
+}
+
+// Parts of K each routed down row is split into: up to 4 for long rows (at
+// least 2048 elements each), so that one active expert still fills a tile's
+// waves; fixed per layer (from max_rows, not m), so that a row's sums do not
+// depend on m.  The parts' partial y share the down's LDS y array.
+int down_parts_of(const moe_decode_desc &d) {
+  int parts = 1;
+  while (parts < 4 && d.inter / (2048 * (parts * 2)) >= 1 &&
+         (size_t)d.max_rows * d.top_k * moe::MAX_DOWN_TILE * (parts * 2) <= (size_t)moe::MAX_PAIRS * moe::MAX_DOWN_TILE &&
+         (d.inter / elems_per_chunk(d.expert_fmt)) % (parts * 2) == 0)
+    parts *= 2;
+  return parts;
+}
+
 // The variant for m rows: the pass sizes pass_variant picks, with the lane
-// grouping down_lanes wants if instantiated, else the widest available.
+// grouping down_lanes wants if instantiated, else the widest available; at
+// m = 1 the narrow down when a tile's sub-units (k experts times the parts of
+// K) fit its 4 waves and it is instantiated.
 bool pick_variant(const moe_decode_desc &d, int m, const moe::Variant **v, moe::launch_fn *gate_up,
                   moe::launch_fn *gate_up_shd) {
   int cr, cs;
   pass_variant(d, m, &cr, &cs);
   const int want = down_lanes(d.inter / elems_per_chunk(d.expert_fmt));
+  const bool shared_vu = (d.flags & MOE_SHARED) && !shared_on_matrix_cores(d);
+  const int narrow = m == 1 && d.top_k * down_parts_of(d) + (shared_vu ? 1 : 0) <= 4 ? 1 : 0;
   const moe::FormatKernels &k = kernels_for(d.act_fmt, d.expert_fmt);
   const moe::Variant *best = nullptr;
+  for (int pass = 0; pass < 2 && !best; ++pass)
   for (int i = 0; i < k.nv; ++i) {
     const moe::Variant &c = k.v[i];
-    if (c.cr != cr || c.cs != cs) continue;
+    // First pass: the narrow flag wanted; second: any (narrow not instantiated).
+    if (c.cr != cr || c.cs != cs || (pass == 0 && c.narrow != narrow) || (pass == 1 && c.narrow)) continue;
     if (c.lpr == want) { best = &c; break; }
     if (!best || c.lpr > best->lpr) best = &c;
   }
@@ -151,6 +177,12 @@ bool pick_variant(const moe_decode_desc &d, int m, const moe::Variant **v, moe::
   return best && *gate_up;
 }
 
+// Router rows of the route launch: the experts, plus the shared-expert gate
+// vector unless the pre-norm launch takes it (router pre-norm).
+int router_rows(const moe_decode_desc &d) {
+  return d.num_experts + ((d.flags & MOE_SHARED_GATED) && !(d.flags & MOE_ROUTER_PRE_NORM) ? 1 : 0);
+}
+
 moe_status check_desc(const moe_decode_desc &d) {
   if (d.hidden <= 0 || d.num_experts <= 0 || d.top_k <= 0 || d.inter <= 0 || d.max_rows <= 0)
     return fail(MOE_EINVAL, "hidden, num_experts, top_k, inter and max_rows must be positive");
@@ -158,16 +190,16 @@ moe_status check_desc(const moe_decode_desc &d) {
     return fail(MOE_EINVAL, "act_fmt must be MOE_F32 or MOE_BF16 (got %d)", d.act_fmt);
   if (d.expert_fmt < MOE_F32 || d.expert_fmt > MOE_NVFP4_B16)
     return fail(MOE_EINVAL, "unknown expert_fmt %d", d.expert_fmt);
-  if (d.routing < MOE_ROUTE_SOFTMAX || d.routing > MOE_ROUTE_SIGMOID_LOGIT)
+  if (d.routing < MOE_ROUTE_SOFTMAX || d.routing > MOE_ROUTE_SQRTSOFTPLUS)
     return fail(MOE_EINVAL, "unknown routing %d", d.routing);
   const uint32_t known = MOE_NORM_TOPK | MOE_WEIGHT_BEFORE_FFN | MOE_SHARED | MOE_SHARED_GATED | MOE_OUT_F32 |
-                         MOE_GEGLU | MOE_PRE_EXPERT_NORM;
+                         MOE_GEGLU | MOE_PRE_EXPERT_NORM | MOE_ROUTER_PRE_NORM;
   if (d.flags & ~known) return fail(MOE_EINVAL, "unknown flag bits 0x%x", d.flags & ~known);
   if ((d.flags & MOE_SHARED_GATED) && !(d.flags & MOE_SHARED))
     return fail(MOE_EINVAL, "MOE_SHARED_GATED requires MOE_SHARED");
   if (!std::isfinite(d.routed_scaling_factor))
     return fail(MOE_EINVAL, "routed_scaling_factor must be finite");
-  if ((d.flags & MOE_PRE_EXPERT_NORM) && !(std::isfinite(d.norm_eps) && d.norm_eps >= 0.0f))
+  if ((d.flags & (MOE_PRE_EXPERT_NORM | MOE_ROUTER_PRE_NORM)) && !(std::isfinite(d.norm_eps) && d.norm_eps >= 0.0f))
     return fail(MOE_EINVAL, "norm_eps must be finite and >= 0");
   if (d.num_experts > moe::MAX_EXPERTS)
     return fail(MOE_EUNSUPPORTED, "num_experts %d > %d", d.num_experts, moe::MAX_EXPERTS);
@@ -231,6 +263,7 @@ void layout_for(const moe_decode_desc &d, moe_decode_ws_layout *L) {
   };
   L->sync = take(moe::SYNC_WORDS * sizeof(uint32_t));
   L->logits = take(R * (E + 1) * sizeof(double));
+  L->scores = take(d.routing == MOE_ROUTE_SQRTSOFTPLUS ? R * E * sizeof(double) : 0);
   L->topk_idx = take(te * 4);
   L->topk_w = take(te * 4);
   L->row_gate = take(R * 4);
@@ -245,6 +278,7 @@ void layout_for(const moe_decode_desc &d, moe_decode_ws_layout *L) {
   L->shared_y = take(Is ? (size_t)shared_down_parts(d) * R * (size_t)d.hidden * 4 : 0);
   L->routed_y = take(d.max_rows > moe::MAX_ROWS ? te * (size_t)d.hidden * 4 : 0);
   L->normed_x = take((d.flags & MOE_PRE_EXPERT_NORM) ? R * (size_t)d.hidden * (d.act_fmt == MOE_F32 ? 4 : 2) : 0);
+  L->router_x = take((d.flags & MOE_ROUTER_PRE_NORM) ? R * (size_t)d.hidden * (d.act_fmt == MOE_F32 ? 4 : 2) : 0);
   L->total = o;
 }
 
@@ -273,6 +307,8 @@ moe_status check_weights(const moe_decode_desc &d, const moe_decode_weights *w) 
     return fail(MOE_EINVAL, "MOE_SHARED_GATED needs a 16-byte aligned sh_gate_vec");
   if ((d.flags & MOE_PRE_EXPERT_NORM) && (!w->pre_norm_w || !aligned(w->pre_norm_w, 16)))
     return fail(MOE_EINVAL, "MOE_PRE_EXPERT_NORM needs a 16-byte aligned pre_norm_w");
+  if ((d.flags & MOE_ROUTER_PRE_NORM) && (!w->router_norm_w || !aligned(w->router_norm_w, 16)))
+    return fail(MOE_EINVAL, "MOE_ROUTER_PRE_NORM needs a 16-byte aligned router_norm_w");
   return MOE_OK;
 }
 
@@ -288,7 +324,7 @@ moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *st
   const bool shared = (d.flags & MOE_SHARED) != 0;
   a.route_in_gu = 1;
   // Router tiles: RT_E router rows x 8 input rows per unit.
-  const int nrows = d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0);
+  const int nrows = router_rows(d);
   a.n_router = (nrows + moe::RT_E - 1) / moe::RT_E * ((m + 7) / 8);
   a.n_router_wg = (a.n_router + moe::ROUTE_UNITS_PER_WG - 1) / moe::ROUTE_UNITS_PER_WG;
   a.n_shared_gu = 0;
@@ -322,6 +358,24 @@ moe_status forward_grouped(const moe_decode_plan_t *plan, moe::Args &a, void *st
   if ((e = moe::launch_blend_grouped(a, (bl_threads + 255) / 256, s, nullptr, ev(5))) != hipSuccess)
     return fail(MOE_EHIP, "blend launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+// The tag this call's slot records carry: a hash of its per-expert tables,
+// expert input, workspace and row count, odd so that it is never the zero
+// of a cleared record.  The kernels use a record only if it carries the tag.
+int32_t call_tag(const moe::Args &a) {
+  const uint64_t v[13] = {(uint64_t)(uintptr_t)a.gw, (uint64_t)(uintptr_t)a.uw, (uint64_t)(uintptr_t)a.dw,
+                          (uint64_t)(uintptr_t)a.gs, (uint64_t)(uintptr_t)a.us, (uint64_t)(uintptr_t)a.ds,
+                          (uint64_t)(uintptr_t)a.gb, (uint64_t)(uintptr_t)a.ub, (uint64_t)(uintptr_t)a.db,
+                          (uint64_t)(uintptr_t)a.x, (uint64_t)(uintptr_t)a.sync, (uint64_t)a.m,
+                          (uint64_t)(uint32_t)a.E};
+  uint64_t h = 0x243F6A8885A308D3ull;
+  for (int i = 0; i < 13; ++i) {
+    h ^= v[i];
+    h *= 0x9E3779B97F4A7C15ull;
+    h ^= h >> 29;
+  }
+  return (int32_t)((uint32_t)(h >> 32) | 1u);
 }
 
 moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights *w, const void *x,
@@ -364,7 +418,7 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   a.idx_out = idx_out;
   a.w_out = w_out;
   a.router = w->router_w;
-  a.ebias = w->expert_bias;
+  a.ebias = (d.routing == MOE_ROUTE_SIGMOID_BIAS || d.routing == MOE_ROUTE_SQRTSOFTPLUS) ? w->expert_bias : nullptr;
   a.gw = w->gate_w; a.uw = w->up_w; a.dw = w->down_w;
   a.gs = w->gate_s; a.us = w->up_s; a.ds = w->down_s;
   a.gb = w->gate_b; a.ub = w->up_b; a.db = w->down_b;
@@ -373,6 +427,7 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   }
   a.sgw = w->sh_gate_w; a.suw = w->sh_up_w; a.sdw = w->sh_down_w; a.sgv = w->sh_gate_vec;
   a.logits = reinterpret_cast<double *>(ws + L.logits);
+  a.scores = reinterpret_cast<double *>(ws + L.scores);
   a.topk_idx = reinterpret_cast<int32_t *>(ws + L.topk_idx);
   a.topk_w = reinterpret_cast<float *>(ws + L.topk_w);
   a.row_gate = reinterpret_cast<float *>(ws + L.row_gate);
@@ -387,17 +442,22 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   a.sy = reinterpret_cast<float *>(ws + L.shared_y);
   a.y = reinterpret_cast<float *>(ws + L.routed_y);
   a.sync = reinterpret_cast<unsigned *>(ws + L.sync);
-  // Pre-expert norm: the experts read the normed rows, written first (its
-  // launch opens the route stage's timing).
+  // Pre-norms: the experts read the rows normed with the pre-expert norm, the
+  // router the rows normed with the router pre-norm; one launch writes both
+  // first (it opens the route stage's timing).
   hipEvent_t route_start = events ? static_cast<hipEvent_t>(events[0]) : nullptr;
-  if (d.flags & MOE_PRE_EXPERT_NORM) {
-    void *xe = ws + L.normed_x;
-    hipError_t e = moe::launch_pre_norm(d.act_fmt, a, w->pre_norm_w, d.norm_eps, xe,
+  if (d.flags & (MOE_PRE_EXPERT_NORM | MOE_ROUTER_PRE_NORM)) {
+    const bool pe = (d.flags & MOE_PRE_EXPERT_NORM) != 0, pr = (d.flags & MOE_ROUTER_PRE_NORM) != 0;
+    void *xe = ws + L.normed_x, *xrn = ws + L.router_x;
+    hipError_t e = moe::launch_pre_norm(d.act_fmt, a, x, pe ? w->pre_norm_w : nullptr,
+                                        pr ? w->router_norm_w : nullptr, d.norm_eps, xe, xrn,
                                         static_cast<hipStream_t>(stream), route_start);
     if (e != hipSuccess) return fail(MOE_EHIP, "pre-norm launch: %s", hipGetErrorString(e));
-    a.x = xe;
+    if (pe) a.x = xe;
+    if (pr) a.xr = xrn;
     route_start = nullptr;
   }
+  a.tag = call_tag(a);   // after a.x is final
   if (m > moe::MAX_ROWS) return forward_grouped(plan, a, stream, events, route_start);
 
   const moe::Variant &kv = *plan->kv[m];
@@ -408,12 +468,12 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   const int ni_s = 2;                                       // gate_up_ni<ACT>()
   const int nrb = (m + 7) / 8;                               // input-row blocks per router row
   a.route_in_gu = plan->route_in_gu[m] ? 1 : 0;
-  a.n_router = (d.num_experts + ((d.flags & MOE_SHARED_GATED) ? 1 : 0)) * nrb;   // router units
+  a.n_router = router_rows(d) * nrb;   // router units
   a.n_router_wg = (a.n_router + moe::ROUTE_UNITS_PER_WG - 1) / moe::ROUTE_UNITS_PER_WG;
   // The shared expert runs on the matrix cores (16-row tiles, gate/up in the
   // route launch, down in the gate/up launch) for bf16 activations when H and
   // Is are multiples of 32; on the vector units otherwise.
-  a.shared_mfma = shared && d.act_fmt == MOE_BF16 && d.hidden % 32 == 0 && a.Is % 32 == 0;
+  a.shared_mfma = shared_on_matrix_cores(d);
   const int ni_r = d.expert_fmt >= MOE_AFF4_G64 && cr == 1 ? 4 : 2;   // gate_up_ni<EF, CR>()
   a.max_rows = d.max_rows;
   a.sd_parts = shared_down_parts(d);
@@ -426,19 +486,13 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   }
   a.gu_items_per_slot = ((d.inter + ni_r - 1) / ni_r + wpb - 1) / wpb;
   a.n_routed_gu = a.cap * a.gu_items_per_slot;
-  // Two row blocks per down tile when the units would leave waves idle and
-  // the halved tile count still gives every CU a workgroup.
-  // Long down rows are split along K into parts (fixed per layer, so the
-  // sums do not depend on m) so that one active expert still fills the
-  // workgroup's waves; the parts' partial y share the LDS y array.
-  a.down_parts = 1;
-  while (a.down_parts < 4 && d.inter / (2048 * (a.down_parts * 2)) >= 1 &&
-         (size_t)d.max_rows * d.top_k * moe::MAX_DOWN_TILE * (a.down_parts * 2) <= (size_t)moe::MAX_PAIRS * moe::MAX_DOWN_TILE &&
-         (d.inter / elems_per_chunk(d.expert_fmt)) % (a.down_parts * 2) == 0)
-    a.down_parts *= 2;
+  a.down_parts = down_parts_of(d);
   const int down_units = a.cap + (shared && !a.shared_mfma ? 1 : 0);
-  a.down_dq = (down_units < moe::DOWN_WPB && d.hidden / (2 * moe::DOWN_RD) >= 256) ? 2 : 1;
-  a.n_down = (d.hidden + moe::DOWN_RD * a.down_dq - 1) / (moe::DOWN_RD * a.down_dq);
+  // Two row blocks per tile when a tile's sub-units would leave waves idle
+  // and the halved tile count still gives every CU a workgroup.
+  const int down_waves = kv.down_threads / moe::WAVE;
+  a.down_dq = (down_units * a.down_parts < down_waves && d.hidden / (2 * kv.rd) >= 256) ? 2 : 1;
+  a.n_down = (d.hidden + kv.rd * a.down_dq - 1) / (kv.rd * a.down_dq);
 
   static thread_local bool logged = false;
   if (!logged && log_enabled()) {

@@ -38,9 +38,9 @@ enum : int { F32 = 0, BF16 = 1, AFF4 = 2, MXFP4 = 3, NVFP4 = 4 };
 // (i / 32) * 8 + i % 8), so that in sub-step g adjacent lanes (adjacent
 // 32-element chunks) read adjacent 32-byte blocks.
 enum : int { F32P = 5 };
-enum : int { ROUTE_SOFTMAX = 0, ROUTE_SIGMOID_BIAS = 1, ROUTE_SIGMOID_LOGIT = 2 };
+enum : int { ROUTE_SOFTMAX = 0, ROUTE_SIGMOID_BIAS = 1, ROUTE_SIGMOID_LOGIT = 2, ROUTE_SQRTSOFTPLUS = 3 };
 enum : unsigned { NORM_TOPK = 1u, WEIGHT_BEFORE = 2u, SHARED = 4u, SHARED_GATED = 8u, OUT_F32 = 16u, GEGLU = 32u,
-                  PRE_NORM = 64u };
+                  PRE_NORM = 64u, ROUTER_NORM = 128u };
 
 constexpr int WAVE = 64;
 constexpr int THREADS = 256;            // route and gate/up: 4 waves per workgroup
@@ -51,7 +51,33 @@ constexpr int DOWN_WPB = DOWN_THREADS / WAVE;
 // waves (a tile's sub-units run in fewer rounds: -9 to -16 % on the down at
 // m = 2-4) where the registers fit three waves per SIMD, else 8 (the
 // eight-vector variants spill, and so would aff4's four-vector one: +9 %).
-template <int EF, int CS> constexpr int down_threads() { return CS >= 8 || EF == AFF4 ? DOWN_THREADS : 768; }
+constexpr int DOWN_RD = 8;              // down rows per wave sub-unit
+constexpr int MAX_DOWN_TILE = 2 * DOWN_RD;
+// One vector per pass (m = 1): 8 waves; for f32 and bf16 experts held to 128
+// registers, so that two workgroups share a CU.  The 4-bit formats'
+// expansion does not fit 128 without spilling; their m = 1 grids have at
+// most 256 tiles at the workloads' shapes.
+// NW ("narrow", m = 1 with f32 or bf16 experts and at most 4 sub-units per
+// tile, e.g. one expert with its rows in 4 parts of K): tiles of 4 rows on 4
+// waves, each wave's sub-unit (4 rows, one part of K) issued as one batch of
+// loads.  Against 8-row sub-units in two batches on 8 waves (320 tiles) a
+// probe of the 5120 x 8192 bf16 down streamed 17.2 us instead of 24.0 (a
+// plain read of the same bytes: 15.9 us); with 8 experts per row it was
+// slower (two rounds of sub-units per wave), so the host takes it only for
+// few sub-units.
+// The 4-vector variants with 64 lanes per row for f32 and bf16 experts, and
+// with 16 lanes per row or 64 for the fp4 formats, run 12 waves only with a
+// smaller register budget for the row loop (below 104 they spilled); the
+// fp4 formats with 64 lanes keep 8 waves.
+template <int EF, int CS, int NW> constexpr int down_rd() { return NW ? 4 : DOWN_RD; }
+template <int EF, int CS, int LPR, int NW = 0> constexpr int down_threads() {
+  return NW ? 256 : CS == 1 || CS >= 8 || EF == AFF4 || (EF >= MXFP4 && LPR == WAVE) ? DOWN_THREADS : 768;
+}
+template <int EF, int CS, int NW> constexpr int down_min_waves() { return CS == 1 && EF <= BF16 ? 4 : 1; }
+// VGPRs the down's row-by-vector loop may plan for (wave_rows_dot's budget).
+template <int EF, int CS, int NW> constexpr int down_vgpr_budget() {
+  return NW ? 100 : CS == 1 && EF <= BF16 ? 88 : CS == 4 ? 104 : 128;
+}
 constexpr int ROUTE_THREADS = 512;      // route launch: 8 waves
 constexpr int ROUTE_WPB = ROUTE_THREADS / WAVE;
 constexpr int RSPLIT = 4;               // waves per router row (its H is split in 4)
@@ -60,15 +86,15 @@ constexpr int MAX_ROWS = 32;
 constexpr int MAX_TOPK = 16;
 constexpr int MAX_EXPERTS = 256;
 constexpr int MAX_PAIRS = MAX_ROWS * MAX_TOPK;
-constexpr int DOWN_RD = 8;              // down rows per wave sub-unit
-constexpr int MAX_DOWN_TILE = 2 * DOWN_RD;
 
 // Reserved words in the workspace (zeroed by moe_decode_workspace_init).
 // Word 0 counts the router workgroups that have stored their logits; the
-// last one resets it, so it is zero between calls.  Nothing ever waits on it.
+// last one resets it, and so does the next launch of the forward, so it is
+// zero between calls whatever a call found there.  Nothing ever waits on it.
 constexpr int SYNC_WORDS = 512;
 constexpr int SYNC_ROUTER_TICKET = 0;
 constexpr int SYNC_TOPK_TICKET = 1;     // grouped path: top-k workgroups (reset by the last arrival)
+constexpr int SYNC_PUBLISHED = 2;       // the tag of the call whose routing the records hold
 // Grouped path (33 <= m <= MAX_ROWS_G): one routing per row on one wave,
 // then the experts' products on the matrix cores, G_COLS pairs per pass.
 constexpr int MAX_ROWS_G = 256;
@@ -95,7 +121,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // Per active slot: what the gate/up and down launches need to start
 // streaming, in one 128-byte record (the routing publishes it).
 struct alignas(128) SlotRec {
-  int32_t e, off, np, pad;
+  int32_t e, off, np, tag;       // tag: Args::tag of the forward that wrote it
   uint64_t gw, uw, gs, us, gb, ub, dw, ds, db;
   uint64_t pad2[5];
 };
@@ -114,8 +140,9 @@ struct Args {
   int sd_parts;            // parts of Is the shared down items split (partials in sy[part])
   int down_parts;          // parts of I each routed down row is split into (partials added in the blend)
   int max_rows;
+  int tag;                 // this call's slot-record tag (odd; a hash of its tables, x, workspace and m)
   const void *x;           // the experts' input (the row, or its pre-expert norm)
-  const void *xr;          // the router's input (the row as given)
+  const void *xr;          // the router's input (the row, or its router pre-norm)
   void *out;
   int32_t *idx_out;
   float *w_out;
@@ -125,6 +152,7 @@ struct Args {
   const float *gs2, *us2, *ds2;   // nvfp4: [E] second-level scale per projection
   const void *sgw, *suw, *sdw, *sgv;
   double *logits;          // [m, E+1]
+  double *scores;          // [m, E]: sqrt-softplus scores of the logits (that routing only)
   int32_t *topk_idx;       // [te]
   float *topk_w;           // [te]
   float *row_gate;         // [m]
@@ -209,6 +237,35 @@ __device__ __forceinline__ float act_mul(unsigned flags, float g, float v) {
 }
 
 __device__ __forceinline__ double sigmoid_d(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+// The sqrt-softplus router score sqrt(log(1 + e^v)), with log(1 + e^v) taken
+// as v + log(1 + e^-v) above 0 (no overflow).
+__device__ __forceinline__ double sqrtsoftplus_d(double v) {
+  return sqrt(v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v)));
+}
+
+// Whether the routing reads the expert bias: sigmoid+bias always,
+// sqrt-softplus when one is given.
+__device__ __forceinline__ bool routing_biased(int routing, const float *ebias) {
+  return routing == ROUTE_SIGMOID_BIAS || (routing == ROUTE_SQRTSOFTPLUS && ebias != nullptr);
+}
+
+// Selection key of logit l (sc: its sqrt-softplus score, b: its bias):
+// sigmoid(l) + b (sigmoid+bias), sc + b (sqrt-softplus with a bias), else the
+// logit itself (softmax, raw-logit, and sqrt-softplus without a bias, whose
+// strictly increasing score orders the experts as the logits do).
+template <bool BIASED>
+__device__ __forceinline__ double select_key_d(int routing, double l, double sc, double b) {
+  if constexpr (BIASED) return routing == ROUTE_SIGMOID_BIAS ? sigmoid_d(l) + b : sc + b;
+  return l;
+}
+
+// Router rows of the route launch: the experts, and the shared-expert gate
+// vector w_g as row E -- unless the router reads a pre-normed row, when the
+// pre-norm launch (which reads the raw row) takes the gate instead.
+__device__ __forceinline__ int router_rows(const Args &a) {
+  return a.E + ((a.flags & SHARED_GATED) && !(a.flags & ROUTER_NORM) ? 1 : 0);
+}
 
 // ------------------------------------------------ cross-lane reductions
 //
@@ -700,16 +757,16 @@ template <> struct XOps<NVFP4, F32P> : XOps<NVFP4, F32> {
 // XPF: the x values of a step (all its sub-steps) are requested with its
 // weights -- one round trip per step -- when they fit: up to 32 registers
 // for one-sub-step formats, up to 64 (one step) for the 4-bit ones.
-template <int WF, int XF, int RG, int C> struct Unroll {
+template <int WF, int XF, int RG, int C, int VB = 128> struct Unroll {
   static constexpr int clampu(int v) { return v < 1 ? 1 : (v > 4 ? 4 : v); }
   static constexpr int W = RG * wchunk_regs<WF>();
   static constexpr int XS = XOps<WF, XF>::XS;
   static constexpr int SUB = XOps<WF, XF>::SUB;
   static constexpr int A = RG * C + 2 * XS;
   // 4-bit rows with 4+ vectors: one step (the expansion temporaries are large).
-  static constexpr int U0 = (WF >= AFF4 && C >= 4) ? 1 : clampu((128 - A) / W);
+  static constexpr int U0 = (WF >= AFF4 && C >= 4) ? 1 : clampu((VB - A) / W);
   static constexpr bool XPF = SUB == 1 ? U0 * C * XS <= 32 : C * SUB * XS <= 64;
-  static constexpr int U = !XPF ? U0 : SUB == 1 ? clampu((128 - RG * C) / (W + C * XS)) : 1;
+  static constexpr int U = !XPF ? U0 : SUB == 1 ? clampu((VB - RG * C) / (W + C * XS)) : 1;
 };
 
 // Issues the loads of the first chunk step of wave_rows_dot<..., U> over
@@ -729,14 +786,14 @@ __device__ __forceinline__ void preload_step(const Row<WF> (&rows)[RG], int c0, 
 
 // PRE: pre holds the first chunk step, requested earlier by preload_step
 // with the same U; used when use_pre.
-template <int WF, int XF, int RG, int C, int LPR, bool PRE = false, int UP = 1>
+template <int WF, int XF, int RG, int C, int LPR, bool PRE = false, int UP = 1, int VB = 128>
 __device__ __forceinline__ void wave_rows_dot(const Row<WF> (&rows)[RG], const char *const (&xrow)[C],
                                               int c0, int nchunks, float (&acc)[RG][C], int gs = 0,
                                               const WChunk<WF> (*pre)[RG] = nullptr, bool use_pre = false) {
   using O = XOps<WF, XF>;
   using X = typename O::X;
-  constexpr int U = Unroll<WF, XF, RG, C>::U;
-  constexpr bool XPF = Unroll<WF, XF, RG, C>::XPF;
+  constexpr int U = Unroll<WF, XF, RG, C, VB>::U;
+  constexpr bool XPF = Unroll<WF, XF, RG, C, VB>::XPF;
   constexpr int SUB = O::SUB;
   static_assert(!PRE || U == UP, "the preloaded step has this pass's unroll");
   const int li = threadIdx.x % LPR;
@@ -1485,6 +1542,48 @@ __device__ __forceinline__ const void *tbl(const uint64_t *t, int e) {
 
 __device__ __forceinline__ int clamp_i(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// The routing a forward publishes is used only if the publishing workgroup
+// wrote this call's tag (Args::tag: the host's hash of the call's tables,
+// input, workspace and row count) into the workspace word SYNC_PUBLISHED
+// after the slot records and the active count.  A consumer reads the word
+// with the count (one memory round trip) and takes no routed work when it
+// differs: records another call left behind are never streamed from.
+__device__ __forceinline__ int published_count(const Args &a) {
+  const int n = a.active_count[0];
+  const unsigned pub = a.sync[SYNC_PUBLISHED];
+  return pub == (unsigned)a.tag ? clamp_i(n, 0, a.cap) : 0;
+}
+
+// Cross-workgroup hand-off inside one launch.  Every workgroup completes its
+// stores and takes a ticket from *ctr; the one that takes ticket n - 1 (every
+// other has stored by then) returns true.  Nobody waits.  Every thread of the
+// workgroup calls it; tk is a __shared__ word.
+//
+// FENCES: the workgroups release their stores at agent scope before the
+// ticket and the last one acquires after it, which orders them under the
+// HIP memory model.  Without: the data handed over must be written and read
+// only with agent-scope atomics (device-coherent stores and loads, which
+// skip the non-coherent state of the per-XCD L2s); s_waitcnt(0) completes the
+// stores, at the device-coherent level, before the ticket's atomic is
+// issued, so the last arrival's loads find them.  The route launch takes
+// this second form: every router workgroup's release fence writes back its
+// XCD's L2, where the launch's shared-expert items keep their output, and
+// cost up to 5 us of the route stage (256 experts, 16 rows).
+template <bool FENCES>
+__device__ __forceinline__ bool last_arrival(unsigned *ctr, unsigned n, unsigned &tk) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if constexpr (FENCES) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    tk = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (FENCES) {
+      if (tk == n - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+  }
+  __syncthreads();
+  return tk == n - 1;
+}
+
 // ------------------------------------------------------------------ router
 //
 // Router unit u = (router row e, block of up to 8 input rows): logits[r, e] =
@@ -1499,7 +1598,7 @@ __device__ __forceinline__ void router_part(const Args &a, int unit, int part, d
   constexpr int EPC = ACT == F32 ? 4 : 8;
   constexpr int RU = 1;                      // chunk steps whose loads are in flight together
   const int lane = threadIdx.x & 63;
-  const int nrows = a.E + ((a.flags & SHARED_GATED) ? 1 : 0);
+  const int nrows = router_rows(a);
   const int e = unit % nrows, r0 = (unit / nrows) * 8;
   const int nr = min(8, a.m - r0);           // input rows of this unit
   const int nchunks = a.H / EPC;
@@ -1570,7 +1669,7 @@ __device__ __forceinline__ double router_tile(const Args &a, int unit, int part)
   static_assert(RT_E * 8 == 32, "one sum per lane pair");
   constexpr int EPC = ACT == F32 ? 4 : 8;
   const int lane = threadIdx.x & 63;
-  const int nrows = a.E + ((a.flags & SHARED_GATED) ? 1 : 0);
+  const int nrows = router_rows(a);
   const int nbe = (nrows + RT_E - 1) / RT_E;
   const int eb = unit % nbe, r0 = (unit / nbe) * 8;
   const int nr = min(8, a.m - r0);
@@ -1695,8 +1794,10 @@ __device__ __forceinline__ unsigned long long order_key(double v) {
 // 0..k-1; `mine` marks them), in double: softmax over all experts -- with
 // norm_topk_prob the full denominator cancels and only the selected terms
 // remain -- or the unbiased sigmoid (the bias only selects), then the
-// normalisation.  lr: the row's logits; lmax: slot 0's logit (the row's
-// largest under softmax routing).  Every lane of the wave must call it.
+// normalisation; the sqrt-softplus router weights by its unbiased score the
+// same way (for it my_l holds that score, which the router units computed).
+// lr: the row's logits; lmax: slot 0's logit (the row's largest under softmax
+// routing).  Every lane of the wave must call it.
 __device__ __forceinline__ double row_weights(const Args &a, const double *lr, bool mine, double my_l,
                                               double lmax) {
   const int lane = threadIdx.x & 63, E = a.E;
@@ -1719,14 +1820,14 @@ __device__ __forceinline__ double row_weights(const Args &a, const double *lr, b
     }
     w = num / den;
   } else {
-    w = mine ? sigmoid_d(my_l) : 0.0;
+    w = mine ? (a.routing == ROUTE_SQRTSOFTPLUS ? my_l : sigmoid_d(my_l)) : 0.0;
     if (a.flags & NORM_TOPK) w = w / wave_sum_f64(w);
   }
   return w;
 }
 
 // Lane l's four candidates of a row (experts 4l..4l+3; lr: the row's
-// logits): order keys, logits and indices; padding past E gets key 0 (below
+// logits): order keys, logits (sqrt-softplus: scores) and indices; padding past E gets key 0 (below
 // every real key) and a unique index after every real one.  Every load is issued
 // before any is used -- one memory round trip; a lane past E loads entry
 // E - 1 and discards it.
@@ -1734,22 +1835,29 @@ template <bool BIASED>
 __device__ __forceinline__ void lane_keys(const Args &a, const double *lr, unsigned long long (&key)[4],
                                           double (&lg)[4], int (&id)[4]) {
   const int lane = threadIdx.x & 63, E = a.E;
-  float bias[4];
+  const bool sqsp = a.routing == ROUTE_SQRTSOFTPLUS;
+  const int r = (int)((lr - a.logits) / (E + 1));
+  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  double sc[4] = {0.0, 0.0, 0.0, 0.0};
   if constexpr (BIASED) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) bias[i] = a.ebias[min(4 * lane + i, E - 1)];
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) lg[i] = load_coherent(lr + min(4 * lane + i, E - 1));
+  if (sqsp) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = load_coherent(a.scores + (size_t)r * E + min(4 * lane + i, E - 1));
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = 4 * lane + i;
     const bool ok = e < E;
     if (!ok) lg[i] = 0.0;
-    double kd = lg[i];
-    if constexpr (BIASED) kd = sigmoid_d(lg[i]) + (double)bias[i];
+    const double kd = select_key_d<BIASED>(a.routing, lg[i], sc[i], (double)bias[i]);
     key[i] = ok ? order_key(kd) : 0ull;
     id[i] = ok ? e : 0x40000000 + e;   // unique, after every real index
+    if (sqsp) lg[i] = sc[i];            // the weights read the score
   }
 }
 
@@ -1773,7 +1881,7 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e,
   unsigned long long key[4];
   double lg[4];
   int id[4];
-  if (a.routing == ROUTE_SIGMOID_BIAS) lane_keys<true>(a, lr, key, lg, id);
+  if (routing_biased(a.routing, a.ebias)) lane_keys<true>(a, lr, key, lg, id);
   else lane_keys<false>(a, lr, key, lg, id);
   // One wave: its LDS accesses complete in program order, so no barrier.
   unsigned hk[4];
@@ -1909,20 +2017,23 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, u
     // row's keys that beat it (a larger key, or an equal key with a lower
     // index) -- a strict order, so ranks 0..k-1 are the slots in order.  S
     // threads share a candidate's comparisons.
-    const bool biased = a.routing == ROUTE_SIGMOID_BIAS;
+    const bool biased = routing_biased(a.routing, a.ebias);
+    const bool sqsp = a.routing == ROUTE_SQRTSOFTPLUS;
     for (int c = tid; c < nc; c += NT) {
       const int r = c / E, i = c - r * E;
-      double l, kd;
-      if (biased) {   // both loads go out together
+      double l, kd, sc = 0.0;
+      if (biased) {   // the loads go out together
         const float b = a.ebias[i];
         l = load_coherent(a.logits + (size_t)r * (E + 1) + i);
-        kd = sigmoid_d(l) + (double)b;
+        if (sqsp) sc = load_coherent(a.scores + (size_t)r * E + i);
+        kd = select_key_d<true>(a.routing, l, sc, (double)b);
       } else {
         l = load_coherent(a.logits + (size_t)r * (E + 1) + i);
-        kd = l;
+        if (sqsp) sc = load_coherent(a.scores + (size_t)r * E + i);
+        kd = select_key_d<false>(a.routing, l, sc, 0.0);
       }
       L.rk.key[c] = order_key(kd);
-      L.rk.lg[c] = l;
+      L.rk.lg[c] = sqsp ? sc : l;   // what the weights read
       L.rk.rank[c] = 0;
     }
     __syncthreads();
@@ -2081,7 +2192,7 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, u
     rec.e = e;
     rec.off = L.off[e];
     rec.np = L.off[e + 1] - L.off[e];
-    rec.pad = 0;
+    rec.tag = a.tag;
     rec.gw = tb[0]; rec.uw = tb[1]; rec.dw = tb[2];
     rec.gs = tb[3]; rec.us = tb[4]; rec.ds = tb[5];
     rec.gb = tb[6]; rec.ub = tb[7]; rec.db = tb[8];
@@ -2090,6 +2201,7 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, u
     a.slots[L.slot_of[e]] = rec;
   }
   __syncthreads();
+  if (publish && tid == 0) a.sync[SYNC_PUBLISHED] = (unsigned)a.tag;   // after the records and the count
 }
 
 // ---------------------------------------------------------------- gate/up
@@ -2158,25 +2270,29 @@ __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, cons
 
 // --------------------------------------------------------- down + blend
 //
-// Down tile `tile`: output columns [h0, h0 + HT), HT = DOWN_RD * down_dq.
+// Down tile `tile`: output columns [h0, h0 + HT), HT = RD * down_dq with RD
+// rows per sub-unit (down_rd).
 // Sub-unit (u, q) is unit u (an active slot, or the shared expert last) and
 // row block q; waves take sub-units round-robin, y per pair goes to LDS, then
 //   out[r, h] = sum_j c_rj y[perm(r, j), h] + gamma_r ys[r, h]
 // in slot order.
-template <int EF, int ACT, int CR, int CS, int LPR>
+template <int EF, int ACT, int CR, int CS, int LPR, int NW>
 __device__ __forceinline__ void down_item(const Args &a, int tile) {
   constexpr int GR = WAVE / LPR;                 // routed rows in parallel per wave
-  constexpr int RGR = DOWN_RD / GR;              // routed rows per lane group
-  constexpr int NWD = down_threads<EF, CS>() / WAVE; // waves of the workgroup
-  static_assert(DOWN_RD % GR == 0, "down rows must split over lane groups");
-  __shared__ float y_lds[MAX_PAIRS * MAX_DOWN_TILE];
-  __shared__ float ys_lds[MAX_ROWS * MAX_DOWN_TILE];
+  constexpr int RGR = down_rd<EF, CS, NW>() / GR;     // routed rows per lane group
+  constexpr int NWD = down_threads<EF, CS, LPR, NW>() / WAVE; // waves of the workgroup
+  constexpr int RD = down_rd<EF, CS, NW>();
+  static_assert(RD % GR == 0, "down rows must split over lane groups");
+  // One row: at most 4 parts of K times k pairs, one row of the shared expert.
+  constexpr bool NARROW = CR == 1 && CS == 1;
+  __shared__ float y_lds[(NARROW ? 4 * MAX_TOPK : MAX_PAIRS) * MAX_DOWN_TILE];
+  __shared__ float ys_lds[(NARROW ? 1 : MAX_ROWS) * MAX_DOWN_TILE];
   __shared__ float s_c[MAX_PAIRS];               // blend coefficient of pair p
   __shared__ int s_perm[MAX_PAIRS];              // sorted position of pair p
   __shared__ float s_gamma[MAX_ROWS];
   const int wave = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63, tid = threadIdx.x;
   const int H = a.H, I = a.I, Is = a.Is, m = a.m, te = a.te;
-  const int DQ = a.down_dq, HT = DOWN_RD * DQ, h0 = tile * HT;
+  const int DQ = a.down_dq, HT = RD * DQ, h0 = tile * HT;
   const bool shared = (a.flags & SHARED) != 0;
   const bool sh_mfma = shared && a.shared_mfma;  // shared output already in sy
   const int sh = shared && !sh_mfma ? 1 : 0;     // else the shared expert is unit 0
@@ -2213,7 +2329,7 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   };
   DownRec nxt = load_rec(slot0);
   int nxt_slot = slot0;
-  const int nact = clamp_i(a.active_count[0], 0, a.cap);
+  const int nact = published_count(a);
   const int units = nact + sh;
 
   // Sub-unit su = (unit, row block q, part pt of the down rows' K); the
@@ -2223,7 +2339,7 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   for (int su = wave; su < nsu; su += NWD) {
     const int uq = su / NP, pt = su - uq * NP;
     const int u = uq / DQ, q = uq - u * DQ;
-    const int hb = h0 + q * DOWN_RD;             // first column of this row block
+    const int hb = h0 + q * RD;                  // first column of this row block
     if (u >= sh) {
       if (nxt_slot != u - sh) {   // not requested ahead (only when the wave's first sub-unit was shared)
         nxt = load_rec(u - sh);
@@ -2258,33 +2374,35 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
 #pragma unroll
         for (int c = 0; c < C; ++c) xrow[c] = reinterpret_cast<const char *>(a.act + (size_t)(off + c0 + c) * I);
         float acc[RGR][C];
-        wave_rows_dot<EF, (EF >= AFF4 ? F32P : F32), RGR, C, LPR>(rows, xrow, kc0, kc1, acc, I);
+        wave_rows_dot<EF, (EF >= AFF4 ? F32P : F32), RGR, C, LPR, false, 1, down_vgpr_budget<EF, CS, NW>()>(
+            rows, xrow, kc0, kc1, acc, I);
         if (lane % LPR == 0) {
 #pragma unroll
           for (int t = 0; t < RGR; ++t)
 #pragma unroll
             for (int c = 0; c < C; ++c)
-              y_lds[(pt * te + off + c0 + c) * HT + q * DOWN_RD + grp + GR * t] =
+              y_lds[(pt * te + off + c0 + c) * HT + q * RD + grp + GR * t] =
                   EF == NVFP4 ? acc[t][c] * s2d : acc[t][c];
         }
       });
     } else if (pt == 0) {
       const Mat<ACT> ms = make_mat<ACT>(a.sdw, nullptr, nullptr, H, Is);
-      Row<ACT> rows[DOWN_RD];
+      Row<ACT> rows[RD];
 #pragma unroll
-      for (int t = 0; t < DOWN_RD; ++t) rows[t] = make_row<ACT, true>(ms, min(hb + t, H - 1));
+      for (int t = 0; t < RD; ++t) rows[t] = make_row<ACT, true>(ms, min(hb + t, H - 1));
       for_passes<CS>(m, [&](auto cc, int c0) {
         constexpr int C = decltype(cc)::value;
         const char *xrow[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) xrow[c] = reinterpret_cast<const char *>(a.sact + (size_t)(c0 + c) * Is);
-        float acc[DOWN_RD][C];
-        wave_rows_dot<ACT, F32, DOWN_RD, C, WAVE>(rows, xrow, 0, Is / Fmt<ACT>::EPC, acc);
+        float acc[RD][C];
+        wave_rows_dot<ACT, F32, RD, C, WAVE, false, 1, down_vgpr_budget<EF, CS, NW>()>(rows, xrow, 0,
+                                                                                   Is / Fmt<ACT>::EPC, acc);
         if (lane == 0) {
 #pragma unroll
-          for (int t = 0; t < DOWN_RD; ++t)
+          for (int t = 0; t < RD; ++t)
 #pragma unroll
-            for (int c = 0; c < C; ++c) ys_lds[(c0 + c) * HT + q * DOWN_RD + t] = acc[t][c];
+            for (int c = 0; c < C; ++c) ys_lds[(c0 + c) * HT + q * RD + t] = acc[t][c];
         }
       });
     }
@@ -2298,7 +2416,7 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
 
   const bool out_f32 = (a.flags & OUT_F32) != 0 || ACT == F32;
   const int k = a.K;
-  for (int t = threadIdx.x; t < m * HT; t += down_threads<EF, CS>()) {
+  for (int t = threadIdx.x; t < m * HT; t += down_threads<EF, CS, LPR, NW>()) {
     const int r = t / HT, hl = t - r * HT, h = h0 + hl;
     if (h >= H) continue;
     float o = 0.f;
@@ -2411,8 +2529,11 @@ template <int MU> union GateUpLDS<false, MU> {
 // ticket; the one that takes the last ticket (every other router workgroup
 // has stored and released its logits by then) computes the routing once for
 // the whole forward and resets the counter.  No workgroup waits for another.
+// Held to 128 registers (two workgroups per CU) but for the 8-vector passes
+// of the vector-unit shared gate/up, which spill there.
+template <int CS> constexpr int route_min_waves() { return CS >= 8 ? 1 : 4; }
 template <int ACT, int CS>
-__global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
+__global__ __launch_bounds__(ROUTE_THREADS, route_min_waves<CS>()) void route_kernel(Args a) {
   struct RouterSmem {
     double part[ROUTE_WPB][8];
     unsigned ticket;
@@ -2439,24 +2560,20 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(Args a) {
     __syncthreads();
     if (tid < ROUTE_UNITS_PER_WG * 8) {
       const int ul = tid / 8, r = tid % 8, u = item * ROUTE_UNITS_PER_WG + ul;
-      const int nrows = a.E + ((a.flags & SHARED_GATED) ? 1 : 0);
+      const int nrows = router_rows(a);
       const int e = u % nrows, rr = (u / nrows) * 8 + r;
       if (u < a.n_router && rr < a.m) {
         double t = s_part[ul * RSPLIT][r];
 #pragma unroll
         for (int p = 1; p < RSPLIT; ++p) t += s_part[ul * RSPLIT + p][r];
         store_coherent(a.logits + (size_t)rr * (a.E + 1) + e, t);
+        if (a.routing == ROUTE_SQRTSOFTPLUS && e < a.E) store_coherent(a.scores + (size_t)rr * a.E + e, sqrtsoftplus_d(t));
       }
     }
     if (a.route_in_gu) return;   // every gate/up workgroup routes from the logits
-    // The logits travel only through device-coherent accesses, so completing
-    // the stores orders them before the ticket; no cache-wide fence needed.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0)
-      s_ticket = __hip_atomic_fetch_add(a.sync + SYNC_ROUTER_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (s_ticket != (unsigned)(a.n_router_wg - 1)) return;
+    // The logits go out through store_coherent and come back through
+    // load_coherent (agent-scope atomics): the hand-off without fences.
+    if (!last_arrival<false>(a.sync + SYNC_ROUTER_TICKET, (unsigned)a.n_router_wg, s_ticket)) return;
     route_all<ROUTE_THREADS, true>(a, L, true, nullptr);
     if (tid == 0) a.sync[SYNC_ROUTER_TICKET] = 0u;  // every ticket is taken
     return;
@@ -2488,7 +2605,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_tile_kernel(Args a) {
   if (tid < ROUTE_UNITS_PER_WG * RT_E * 8) {
     const int ul = tid / (RT_E * 8), o = tid % (RT_E * 8), j = o / 8, r = o % 8;
     const int u = item * ROUTE_UNITS_PER_WG + ul;
-    const int nrows = a.E + ((a.flags & SHARED_GATED) ? 1 : 0);
+    const int nrows = router_rows(a);
     const int nbe = (nrows + RT_E - 1) / RT_E;
     const int e = (u % nbe) * RT_E + j, rr = (u / nbe) * 8 + r;
     if (u < a.n_router && rr < a.m && e < nrows) {
@@ -2496,47 +2613,61 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_tile_kernel(Args a) {
 #pragma unroll
       for (int p = 1; p < RSPLIT; ++p) t += s_part[ul * RSPLIT + p][o];
       a.logits[(size_t)rr * (a.E + 1) + e] = t;
+      if (a.routing == ROUTE_SQRTSOFTPLUS && e < a.E) a.scores[(size_t)rr * a.E + e] = sqrtsoftplus_d(t);
     }
   }
 }
 
 
-// Launch 2: items (active slot s, row block b), blockIdx, blockIdx +
-// gridDim, ... of the nact * items_per_slot that exist; its waves take row
-// groups b * 4 + wave of slot s.  Either the routing is published (the first
-// item's slot record is requested together with the active count), or --
-// route_in_gu, chosen for small m where it starts the streaming sooner --
+// Launch 2: items blockIdx, blockIdx + gridDim, ... of a list of the routed
+// items (active slot s, row block b) of the nact * items_per_slot that exist,
+// whose waves take row groups b * 4 + wave of slot s, and of the shared
+// expert's down items (SHD > 0).  Either the routing is published (the first
+// routed item's slot record is requested together with the active count), or
+// -- route_in_gu, chosen for small m where it starts the streaming sooner --
 // every workgroup computes it from the logits in LDS and one extra
-// workgroup, the last, publishes it.
+// workgroup, the last, publishes it; then the shared items come first in the
+// list, since they need no routing: a workgroup streams them before it takes
+// the routing (-6 % on the gate/up of the weight-before workload at m = 1).
 // SHD: 0, or the column tiles (1: m <= 16, 2: m <= 32) of the shared
 // expert's down items this variant also runs.
 // The variants m = 1 runs (one vector per pass, at most one shared column
 // tile) are held to 128 registers, four waves per SIMD: their natural size is
 // within a few registers of it.  Argument: CR * 4 + SHD.
-template <int CRS> constexpr int gate_up_min_waves() { return CRS / 4 == 1 && CRS % 4 <= 1 ? 4 : 1; }
+// (f32 activations, the latency-bound tiny layer's, spill at 128 and keep
+// no bound.)
+template <int CRS, bool F32Q = false> constexpr int gate_up_min_waves() {
+  return !F32Q && CRS / 4 == 1 && CRS % 4 <= 1 ? 4 : 1;
+}
 template <int EF, int ACT, int CR, int CS, int SHD>
-__global__ __launch_bounds__(THREADS, gate_up_min_waves<CR * 4 + SHD>()) void gate_up_kernel(Args a) {
+__global__ __launch_bounds__(THREADS, (gate_up_min_waves<CR * 4 + SHD, ACT == F32>()))
+void gate_up_kernel(Args a) {
   constexpr int NI = gate_up_ni<EF, CR>();
   const int ips = a.gu_items_per_slot;
   const int wave = uniform_i(threadIdx.x >> 6);
   constexpr int SDMU = shared_dn_mu<EF, CR>();
   __shared__ GateUpLDS<(SHD > 0), SDMU> GS;
-  if (a.route_in_gu) {
+  // The route launch is over: its ticket word starts the next forward at 0,
+  // whatever this forward found in it.
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.sync[SYNC_ROUTER_TICKET] = 0u;
+  const int S = SHD > 0 ? a.n_shared_dn : 0;   // shared down items
+  // Only the one-vector variants (m = 1) carry the routing: the top-k's
+  // registers would cost the streaming variants of m > 1 occupancy.
+  if (CR == 1 && a.route_in_gu) {
     // The last workgroup only publishes the routing; the others stream.
     __shared__ RouteLDS<256, WPB> L;
     const int nb = gridDim.x - 1;
     const bool publisher = (int)blockIdx.x == nb;
+    int it = blockIdx.x;
+    if constexpr (SHD > 0) {
+      for (; !publisher && it < S; it += nb) shared_dn_item<ACT, SHD, SDMU>(a, it, GS.mf);
+    }
     route_all<THREADS, false>(a, L, publisher, GS.tab);
     if (publisher) return;
     const int n = L.nact * ips;
-    for (int it = blockIdx.x; it < n + (SHD ? a.n_shared_dn : 0); it += nb) {
-      if constexpr (SHD > 0) {
-        if (it >= n) {
-          shared_dn_item<ACT, SHD, SDMU>(a, it - n, GS.mf);
-          continue;
-        }
-      }
-      const int s = it / ips, b = it - s * ips;
+    for (; it < S + n; it += nb) {
+      const int ri = it - S;
+      const int s = ri / ips, b = ri - s * ips;
       const int e = uniform_i(clamp_i(L.active[s], 0, a.E - 1));
       const int off = uniform_i(L.off[e]), np = uniform_i(L.off[e + 1]) - off;
       const int i0 = (b * WPB + wave) * NI;
@@ -2560,20 +2691,24 @@ __global__ __launch_bounds__(THREADS, gate_up_min_waves<CR * 4 + SHD>()) void ga
     }
     return;
   }
+  // With the routing published the list runs routed items first (the larger
+  // ones: shared items last balance the workgroups' ends; shared items first
+  // made the gate/up 6 % slower at m = 8 and 32 on the weight-before
+  // workload).  The first item's record is requested with the active count.
   const SlotRec pre = a.slots[clamp_i((int)blockIdx.x / ips, 0, a.cap - 1)];
-  const int nact = clamp_i(a.active_count[0], 0, a.cap);
+  const int nact = published_count(a);
   const int n = nact * ips;
   SlotRec nxt = pre;   // record of the next routed item, requested one item ahead
-  for (int it = blockIdx.x; it < n + (SHD ? a.n_shared_dn : 0); it += gridDim.x) {
+  for (int ri = blockIdx.x; ri < n + S; ri += gridDim.x) {
     if constexpr (SHD > 0) {
-      if (it >= n) {
-        shared_dn_item<ACT, SHD, SDMU>(a, it - n, GS.mf);
+      if (ri >= n) {
+        shared_dn_item<ACT, SHD, SDMU>(a, ri - n, GS.mf);
         continue;
       }
     }
-    const int s = it / ips, b = it - s * ips;
+    const int s = ri / ips, b = ri - s * ips;
     const SlotRec rec = nxt;
-    if (it + (int)gridDim.x < n) nxt = a.slots[(it + (int)gridDim.x) / ips];
+    if (ri + (int)gridDim.x < n) nxt = a.slots[(ri + (int)gridDim.x) / ips];
     const int off = uniform_i(clamp_i(rec.off, 0, a.te));
     const int np = uniform_i(clamp_i(rec.np, 0, a.te - off));
     const int i0 = (b * WPB + wave) * NI;
@@ -2593,17 +2728,21 @@ __global__ __launch_bounds__(THREADS, gate_up_min_waves<CR * 4 + SHD>()) void ga
 }
 
 // Launch 3: down tiles with the blend.
-template <int EF, int ACT, int CR, int CS, int LPR>
-__global__ __launch_bounds__((down_threads<EF, CS>())) void down_blend_kernel(Args a) {
-  down_item<EF, ACT, CR, CS, LPR>(a, blockIdx.x);
+template <int EF, int ACT, int CR, int CS, int LPR, int NW>
+__global__ __launch_bounds__((down_threads<EF, CS, LPR, NW>()), (down_min_waves<EF, CS, NW>())) void down_blend_kernel(Args a) {
+  down_item<EF, ACT, CR, CS, LPR, NW>(a, blockIdx.x);
 }
 
 
-// ================================================== pre-expert norm
+// ================================================== pre-norms
 //
-// One workgroup per row: xe = x * w / sqrt(mean(x^2) + eps), in double (the
-// squares and products of stored values are exact), rounded once to the
-// activation format (bf16: to nearest, ties to even, from the double).
+// One workgroup per row: the RMS norm x * w / sqrt(mean(x^2) + eps) of the
+// raw row, in double (the squares and products of stored values are exact),
+// rounded once to the activation format (bf16: to nearest, ties to even, from
+// the double) -- with the experts' weight into xe (pre-expert norm) and with
+// the router's weight into xrn (router pre-norm).  With the router pre-norm
+// and a gated shared expert it also takes the gate's logit x . w_g of the raw
+// row (the router units then read the normed row only).
 
 // A double to bf16 bits, rounded to nearest (ties to even) in one step:
 // the double's significand is rounded to 8 bits on its bit pattern, which is
@@ -2616,13 +2755,15 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double v) {
 }
 
 template <int ACT>
-__global__ __launch_bounds__(256) void pre_norm_kernel(Args a, const void *w, float eps, void *xe) {
+__global__ __launch_bounds__(256) void pre_norm_kernel(Args a, const void *x, const void *w, const void *wr,
+                                                       float eps, void *xe, void *xrn) {
   constexpr int EPC = ACT == F32 ? 4 : 8;   // elements per 16-byte chunk
-  __shared__ double s_part[4];
+  __shared__ double s_part[2][4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, nch = H / EPC;
   const size_t rb = (size_t)H * act_bytes(ACT);
-  const char *xrow = reinterpret_cast<const char *>(a.xr) + (size_t)r * rb;
+  const char *xrow = reinterpret_cast<const char *>(x) + (size_t)r * rb;
+  const bool gate = (a.flags & ROUTER_NORM) && (a.flags & SHARED_GATED);
   auto elems = [&](const u32x4 &q, double (&v)[EPC]) {
     if constexpr (ACT == F32) {
       v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
@@ -2632,37 +2773,53 @@ __global__ __launch_bounds__(256) void pre_norm_kernel(Args a, const void *w, fl
       v[4] = bf_lo(q.z); v[5] = bf_hi(q.z); v[6] = bf_lo(q.w); v[7] = bf_hi(q.w);
     }
   };
-  double ss = 0.0;
+  double ss = 0.0, gd = 0.0;
   for (int c = tid; c < nch; c += 256) {
     double v[EPC];
     elems(ld16(xrow + (size_t)c * 16), v);
 #pragma unroll
     for (int i = 0; i < EPC; ++i) ss = __builtin_fma(v[i], v[i], ss);
+    if (gate) {
+      double g[EPC];
+      elems(ld16(reinterpret_cast<const char *>(a.sgv) + (size_t)c * 16), g);
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) gd = __builtin_fma(v[i], g[i], gd);
+    }
   }
   ss = wave_sum_f64(ss);
-  if (lane == 0) s_part[wave] = ss;
+  gd = wave_sum_f64(gd);
+  if (lane == 0) {
+    s_part[0][wave] = ss;
+    s_part[1][wave] = gd;
+  }
   __syncthreads();
-  const double tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+  const double tot = (s_part[0][0] + s_part[0][1]) + (s_part[0][2] + s_part[0][3]);
+  if (gate && tid == 0)
+    store_coherent(a.logits + (size_t)r * (a.E + 1) + a.E, (s_part[1][0] + s_part[1][1]) + (s_part[1][2] + s_part[1][3]));
   const double inv = 1.0 / __builtin_sqrt(tot / (double)H + (double)eps);
-  char *orow = reinterpret_cast<char *>(xe) + (size_t)r * rb;
-  for (int c = tid; c < nch; c += 256) {
-    double v[EPC], g[EPC];
-    elems(ld16(xrow + (size_t)c * 16), v);
-    elems(ld16(reinterpret_cast<const char *>(w) + (size_t)c * 16), g);
-    if constexpr (ACT == F32) {
-      u32x4 o;
-      o.x = __float_as_uint((float)(v[0] * g[0] * inv));
-      o.y = __float_as_uint((float)(v[1] * g[1] * inv));
-      o.z = __float_as_uint((float)(v[2] * g[2] * inv));
-      o.w = __float_as_uint((float)(v[3] * g[3] * inv));
-      *reinterpret_cast<u32x4 *>(orow + (size_t)c * 16) = o;
-    } else {
-      uint32_t o[4];
+  for (int o = 0; o < 2; ++o) {
+    const void *nw = o == 0 ? w : wr;
+    if (!nw) continue;
+    char *orow = reinterpret_cast<char *>(o == 0 ? xe : xrn) + (size_t)r * rb;
+    for (int c = tid; c < nch; c += 256) {
+      double v[EPC], g[EPC];
+      elems(ld16(xrow + (size_t)c * 16), v);
+      elems(ld16(reinterpret_cast<const char *>(nw) + (size_t)c * 16), g);
+      if constexpr (ACT == F32) {
+        u32x4 q;
+        q.x = __float_as_uint((float)(v[0] * g[0] * inv));
+        q.y = __float_as_uint((float)(v[1] * g[1] * inv));
+        q.z = __float_as_uint((float)(v[2] * g[2] * inv));
+        q.w = __float_as_uint((float)(v[3] * g[3] * inv));
+        *reinterpret_cast<u32x4 *>(orow + (size_t)c * 16) = q;
+      } else {
+        uint32_t q[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[i] = (uint32_t)f64_to_bf16(v[2 * i] * g[2 * i] * inv) |
-               ((uint32_t)f64_to_bf16(v[2 * i + 1] * g[2 * i + 1] * inv) << 16);
-      *reinterpret_cast<u32x4 *>(orow + (size_t)c * 16) = u32x4{o[0], o[1], o[2], o[3]};
+        for (int i = 0; i < 4; ++i)
+          q[i] = (uint32_t)f64_to_bf16(v[2 * i] * g[2 * i] * inv) |
+                 ((uint32_t)f64_to_bf16(v[2 * i + 1] * g[2 * i + 1] * inv) << 16);
+        *reinterpret_cast<u32x4 *>(orow + (size_t)c * 16) = u32x4{q[0], q[1], q[2], q[3]};
+      }
     }
   }
 }
@@ -2722,15 +2879,8 @@ __global__ __launch_bounds__(ROUTE_THREADS) void topk_sort_kernel(Args a) {
     if (lane == 0 && (a.flags & SHARED_GATED))
       a.row_gate[r] = (float)sigmoid_d(load_coherent(a.logits + (size_t)r * (E + 1) + E));
   }
-  // Complete this workgroup's stores, then take a ticket; only the workgroup
-  // that takes the last one goes on (nobody waits).  The selections travel
-  // only through device-coherent accesses, so no cache-wide fence is needed.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0)
-    s_ticket = __hip_atomic_fetch_add(a.sync + SYNC_TOPK_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (s_ticket != gridDim.x - 1) return;
+  // Only the workgroup that takes the last ticket goes on (nobody waits).
+  if (!last_arrival<true>(a.sync + SYNC_TOPK_TICKET, gridDim.x, s_ticket)) return;
   SortLDS &S = sm.s;
   constexpr int RW = MAX_ROWS_G / 32;
   for (int i = tid; i < MAX_EXPERTS * RW; i += ROUTE_THREADS) (&S.rows[0][0])[i] = 0u;
@@ -2776,7 +2926,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void topk_sort_kernel(Args a) {
         rec.e = e;
         rec.off = pre_c;
         rec.np = cnt;
-        rec.pad = 0;
+        rec.tag = a.tag;
         rec.gw = a.gw[e]; rec.uw = a.uw[e]; rec.dw = a.dw[e];
         rec.gs = a.gs ? a.gs[e] : 0ull; rec.us = a.gs ? a.us[e] : 0ull; rec.ds = a.gs ? a.ds[e] : 0ull;
         rec.gb = a.gb ? a.gb[e] : 0ull; rec.ub = a.gb ? a.ub[e] : 0ull; rec.db = a.gb ? a.db[e] : 0ull;
@@ -2801,7 +2951,10 @@ __global__ __launch_bounds__(ROUTE_THREADS) void topk_sort_kernel(Args a) {
     a.sorted_pair[pos] = p;
     a.pair_to_perm[p] = pos;
   }
-  if (tid == 0) a.sync[SYNC_TOPK_TICKET] = 0u;   // every ticket is taken
+  if (tid == 0) {
+    a.sync[SYNC_TOPK_TICKET] = 0u;   // every ticket is taken
+    a.sync[SYNC_PUBLISHED] = (unsigned)a.tag;
+  }
 }
 
 // The expert's pair range and weights of gate/up or down item `item` of a
@@ -2828,7 +2981,7 @@ __device__ __forceinline__ GroupedItem grouped_item(const Args &a, int item, int
   const int nrout = a.cap * tiles;
   if (item < nrout) {
     const int s = item / tiles;
-    const int nact = clamp_i(a.active_count[0], 0, a.cap);
+    const int nact = published_count(a);
     g.live = s < nact;
     g.routed = true;
     const SlotRec &r = a.slots[min(s, a.cap - 1)];   // one record, requested with the count
@@ -2884,6 +3037,8 @@ __global__ __launch_bounds__(64 * gu_grouped_waves<EF>(), gu_grouped_min_waves<E
   __shared__ MfmaLDS<NWG, 2, G_MU> S;
   const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int H = a.H, k = a.K;
+  // The top-k launch is over: its ticket word starts the next forward at 0.
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.sync[SYNC_TOPK_TICKET] = 0u;
   const GroupedItem it = grouped_item(a, blockIdx.x, (a.I + 16 * GT - 1) / (16 * GT), (a.Is + 16 * GT - 1) / (16 * GT));
   if (!it.live) return;
   const int N = it.routed ? a.I : a.Is;

@@ -30,6 +30,8 @@ inline hipError_t launch_timed(K kernel, int blocks, int threads, hipStream_t st
 // per down row.
 struct Variant {
   int cr, cs, lpr;
+  int narrow;             // the m = 1 down of few sub-units per tile (tiles of 4 rows on 4 waves)
+  int rd, down_threads;   // down rows per wave sub-unit, threads per down workgroup
   launch_fn down_blend;   // third launch
 };
 struct GateUpVariant {
@@ -55,9 +57,12 @@ hipError_t launch_route(int act, int cs, const Args &a, int blocks, hipStream_t 
 hipError_t launch_clear_sync(unsigned *sync, int n, hipStream_t st);
 // The grouped path's router: units of RT_E router rows x 8 input rows.
 hipError_t launch_route_tile(int act, const Args &a, int blocks, hipStream_t st, hipEvent_t start);
-// The pre-expert norm of the m rows into xe (one workgroup per row).
-hipError_t launch_pre_norm(int act, const Args &a, const void *w, float eps, void *xe, hipStream_t st,
-                           hipEvent_t start);
+// The pre-norms of the m raw rows x (one workgroup per row): with weight w
+// into xe (the experts' input) and with weight wr into xrn (the router's);
+// a null weight skips its output.  With the router pre-norm and a gated
+// shared expert, also the gate's logit of the raw row.
+hipError_t launch_pre_norm(int act, const Args &a, const void *x, const void *w, const void *wr, float eps,
+                           void *xe, void *xrn, hipStream_t st, hipEvent_t start);
 // Grouped path (m > 32): top-k with the sort, and the blend.
 hipError_t launch_topk_sort(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_blend_grouped(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop);
@@ -76,9 +81,10 @@ const FormatKernels &kernels_f32_nvfp4();
 const FormatKernels &kernels_bf16_nvfp4();
 
 #ifdef MOE_KERNELS_HPP_INCLUDED
-template <int EF, int ACT, int CR, int CS, int LPR>
+template <int EF, int ACT, int CR, int CS, int LPR, int NW>
 hipError_t launch_down_blend_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  return launch_timed(down_blend_kernel<EF, ACT, CR, CS, LPR>, blocks, down_threads<EF, CS>(), st, start, stop, a);
+  return launch_timed(down_blend_kernel<EF, ACT, CR, CS, LPR, NW>, blocks, down_threads<EF, CS, LPR, NW>(), st,
+                      start, stop, a);
 }
 template <int EF>
 hipError_t launch_gate_up_grouped_t(const Args &a, int blocks, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
@@ -104,7 +110,11 @@ constexpr launch_fn gate_up_shd_fn() {
 }  // namespace moe
 
 // Inside an inst_*.hip unit, with constexpr int EFT and ACTT in scope.
-#define MOE_V(CR, CS, LPR) { CR, CS, LPR, &launch_down_blend_t<EFT, ACTT, CR, CS, LPR> }
+#define MOE_V(CR, CS, LPR) { CR, CS, LPR, 0, down_rd<EFT, CS, 0>(), down_threads<EFT, CS, LPR, 0>(), \
+                            &launch_down_blend_t<EFT, ACTT, CR, CS, LPR, 0> }
+// The narrow m = 1 down (f32 and bf16 experts).
+#define MOE_VN(LPR) { 1, 1, LPR, 1, down_rd<EFT, 1, 1>(), down_threads<EFT, 1, LPR, 1>(), \
+                      &launch_down_blend_t<EFT, ACTT, 1, 1, LPR, 1> }
 #define MOE_G(CR, CS) { CR, CS, &launch_gate_up_t<EFT, ACTT, CR, CS, 0>, gate_up_shd_fn<EFT, ACTT, CR, CS, 1>(), \
                         gate_up_shd_fn<EFT, ACTT, CR, CS, 2>() }
 #define MOE_TABLE(NAME)                                                            \

@@ -32,10 +32,10 @@ hipError_t launch_route_tile(int act, const Args &a, int blocks, hipStream_t st,
   return launch_timed(route_tile_kernel<BF16>, blocks, ROUTE_THREADS, st, t0, nullptr, a);
 }
 
-hipError_t launch_pre_norm(int act, const Args &a, const void *w, float eps, void *xe, hipStream_t st,
-                           hipEvent_t t0) {
-  if (act == F32) return launch_timed(pre_norm_kernel<F32>, a.m, 256, st, t0, nullptr, a, w, eps, xe);
-  return launch_timed(pre_norm_kernel<BF16>, a.m, 256, st, t0, nullptr, a, w, eps, xe);
+hipError_t launch_pre_norm(int act, const Args &a, const void *x, const void *w, const void *wr, float eps,
+                           void *xe, void *xrn, hipStream_t st, hipEvent_t t0) {
+  if (act == F32) return launch_timed(pre_norm_kernel<F32>, a.m, 256, st, t0, nullptr, a, x, w, wr, eps, xe, xrn);
+  return launch_timed(pre_norm_kernel<BF16>, a.m, 256, st, t0, nullptr, a, x, w, wr, eps, xe, xrn);
 }
 
 hipError_t launch_topk_sort(const Args &a, int blocks, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {

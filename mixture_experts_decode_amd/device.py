@@ -32,6 +32,8 @@ def desc_of(spec: LayerSpec, max_rows: Optional[int] = None, out_f32: bool = Fal
         flags |= md.MOE_GEGLU
     if spec.pre_expert_norm:
         flags |= md.MOE_PRE_EXPERT_NORM
+    if spec.router_pre_norm:
+        flags |= md.MOE_ROUTER_PRE_NORM
     return md.moe_decode_desc(
         hidden=spec.hidden, num_experts=spec.num_experts, top_k=spec.top_k, inter=spec.inter,
         shared_inter=spec.shared_inter if spec.shared else 0,
@@ -86,7 +88,8 @@ class _Copy:
             sh_gate_w=p(tensors.get("sh_gate")), sh_up_w=p(tensors.get("sh_up")),
             sh_down_w=p(tensors.get("sh_down")), sh_gate_vec=p(tensors.get("sh_gate_vec")),
             gate_scale2=p(tensors.get("gate_s2")), up_scale2=p(tensors.get("up_s2")),
-            down_scale2=p(tensors.get("down_s2")), pre_norm_w=p(tensors.get("pre_norm_w")))
+            down_scale2=p(tensors.get("down_s2")), pre_norm_w=p(tensors.get("pre_norm_w")),
+            router_norm_w=p(tensors.get("router_norm_w")))
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in self.t.values() if t is not None)
@@ -115,6 +118,7 @@ class DeviceLayer:
             "sh_down": to_device(layer.sh_down, device),
             "sh_gate_vec": to_device(layer.sh_gate_vec, device),
             "pre_norm_w": to_device(layer.pre_norm_w, device),
+            "router_norm_w": to_device(layer.router_norm_w, device),
         }
         for name in ("gate", "up", "down"):
             proj = getattr(layer, name)
@@ -126,6 +130,7 @@ class DeviceLayer:
         for _ in range(copies - 1):
             cl = {k: (None if v is None else v.clone()) for k, v in base.items()}
             self.copies.append(_Copy(cl, spec.num_experts, self.device))
+        self._plan_other = None      # the same layer with the other output format, made on demand
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         assert self.workspace.data_ptr() % 256 == 0
         md.moe_decode_workspace_init(self.plan, self.workspace.data_ptr(), self.ws_bytes,
@@ -135,18 +140,32 @@ class DeviceLayer:
     def weights(self) -> md.moe_decode_weights:
         return self.copies[0].weights
 
-    def new_out(self, m: int) -> torch.Tensor:
-        dt = torch.float32 if (self.out_f32 or self.spec.act_fmt == "f32") else torch.int16
+    def _plan(self, out_f32: Optional[bool]):
+        """The plan for the requested output format: this layer's own, or a
+        second plan of the same layer with MOE_OUT_F32 toggled (same workspace)."""
+        if out_f32 is None or bool(out_f32) == self.out_f32:
+            return self.plan
+        if self._plan_other is None:
+            plan, ws = md.moe_decode_plan(desc_of(self.spec, self.max_rows, bool(out_f32)))
+            weakref.finalize(self, md.lib().moe_decode_plan_destroy, plan)
+            assert ws == self.ws_bytes
+            self._plan_other = plan
+        return self._plan_other
+
+    def new_out(self, m: int, out_f32: Optional[bool] = None) -> torch.Tensor:
+        f32 = self.out_f32 if out_f32 is None else bool(out_f32)
+        dt = torch.float32 if (f32 or self.spec.act_fmt == "f32") else torch.int16
         return torch.empty((m, self.spec.hidden), dtype=dt, device=self.device)
 
     def forward(self, x: torch.Tensor, m: Optional[int] = None, out: Optional[torch.Tensor] = None,
                 idx: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
-                copy: int = 0, stream: Optional[int] = None, events=None) -> torch.Tensor:
+                copy: int = 0, stream: Optional[int] = None, events=None,
+                out_f32: Optional[bool] = None) -> torch.Tensor:
         m = x.shape[0] if m is None else m
         if out is None:
-            out = self.new_out(m)
+            out = self.new_out(m, out_f32)
         st = torch.cuda.current_stream(self.device).cuda_stream if stream is None else stream
-        args = (self.plan, self.copies[copy].weights, x.data_ptr(), m, out.data_ptr(),
+        args = (self._plan(out_f32), self.copies[copy].weights, x.data_ptr(), m, out.data_ptr(),
                 None if idx is None else idx.data_ptr(), None if w is None else w.data_ptr(),
                 self.workspace.data_ptr(), self.ws_bytes, st)
         if events is None:

@@ -25,9 +25,9 @@ MOE_F32, MOE_BF16, MOE_AFF4_G64, MOE_MXFP4_B32, MOE_NVFP4_B16 = range(5)
 FORMATS = {"f32": MOE_F32, "bf16": MOE_BF16, "aff4": MOE_AFF4_G64, "mxfp4": MOE_MXFP4_B32,
            "nvfp4": MOE_NVFP4_B16}
 # moe_routing
-MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID_BIAS, MOE_ROUTE_SIGMOID_LOGIT = range(3)
+MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID_BIAS, MOE_ROUTE_SIGMOID_LOGIT, MOE_ROUTE_SQRTSOFTPLUS = range(4)
 ROUTINGS = {"softmax": MOE_ROUTE_SOFTMAX, "sigmoid_bias": MOE_ROUTE_SIGMOID_BIAS,
-            "sigmoid_logit": MOE_ROUTE_SIGMOID_LOGIT}
+            "sigmoid_logit": MOE_ROUTE_SIGMOID_LOGIT, "sqrtsoftplus": MOE_ROUTE_SQRTSOFTPLUS}
 # flags
 MOE_NORM_TOPK = 1
 MOE_WEIGHT_BEFORE_FFN = 2
@@ -36,6 +36,7 @@ MOE_SHARED_GATED = 8
 MOE_OUT_F32 = 16
 MOE_GEGLU = 32
 MOE_PRE_EXPERT_NORM = 64
+MOE_ROUTER_PRE_NORM = 128
 
 
 class MoeDecodeError(RuntimeError):
@@ -55,14 +56,14 @@ class moe_decode_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "router_w", "expert_bias", "gate_w", "up_w", "down_w", "gate_s", "up_s", "down_s",
         "gate_b", "up_b", "down_b", "sh_gate_w", "sh_up_w", "sh_down_w", "sh_gate_vec",
-        "gate_scale2", "up_scale2", "down_scale2", "pre_norm_w")]
+        "gate_scale2", "up_scale2", "down_scale2", "pre_norm_w", "router_norm_w")]
 
 
 class moe_decode_ws_layout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in (
-        "logits", "topk_idx", "topk_w", "row_gate", "sorted_pair", "expert_offsets",
+        "logits", "scores", "topk_idx", "topk_w", "row_gate", "sorted_pair", "expert_offsets",
         "pair_to_perm", "active_experts", "active_count", "slot_info", "act", "shared_act", "shared_y",
-        "routed_y", "normed_x", "sync", "total")]
+        "routed_y", "normed_x", "router_x", "sync", "total")]
 
 
 _lib = None
