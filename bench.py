@@ -5,9 +5,12 @@
 
 A step is one forward of the whole layer (route, top-k, sort, gate/up,
 down, blend) over one batch of m synthetic rows, through the C ABI.  The
-default workload is the Qwen3-30B-A3B-shaped bf16 layer (H 2048, 128
-experts, top-8, I 768) at m = 1; m = 8 is measured too and reported under
-"detail".  Weights and inputs are resident in HBM before timing starts.
+headline workload is the largest one, the Llama-4-shaped weight-before-FFN
+bf16 layer (H 5120, 16 experts, top-1, I 8192, plus a shared expert of
+8192) at m = 1; its other row counts (8, 32) and every other workload at
+every row count it lists are timed too and reported under "detail" (skip
+them with --only).  Weights and inputs are resident in HBM before timing
+starts.
 
 Calls rotate over R device copies of the layer, each with its own input rows
 (so its own expert selection), with R chosen so that at least 600 MB of other
@@ -16,13 +19,14 @@ weights stream between two uses of a copy: no call finds its weights in the
 steps run graph-captured); stream-launched numbers are reported too.  In that
 stream loop every kernel is launched with its own start/stop HIP events
 (hipExtLaunchKernelGGL), whose average for the dominant kernel gives the
-roofline entry.
+roofline entry: the dominant kernel is the stage with the longest average
+duration, and its algorithmic bytes per launch are counted per stage.
 
 Effective bandwidth counts ALGORITHMIC bytes: the experts each call actually
 selected (from a one-time readback of the exported indices), router, bias,
-shared expert, input and output rows.  The oracle (plain fp64 C, one host
-thread) is timed on a bounded sample of the same workload as the CPU
-baseline.
+shared expert, input and output rows.  The oracle (plain fp64 C) is timed on
+the host as the CPU baseline: the median of 3 calls after 1 warm-up on one
+row of each workload, on one thread and with OpenMP over output neurons.
 """
 from __future__ import annotations
 
@@ -39,9 +43,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs per MoE decode layer and effective HBM GB/s (% of peak) at m=1,8"
 PEAK_HBM_GBPS = 8000.0
-DEFAULT_WORKLOAD = "qwen3_30b_a3b_bf16"
+DEFAULT_WORKLOAD = "llama4_wbf_bf16"
 KERNEL_SRC_DIR = os.path.join(ROOT, "mixture_experts_decode_amd", "csrc")
-COUNTERS = os.path.join(ROOT, "profiles", "gate_up_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def parse():
@@ -51,8 +55,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--rows", type=int, default=1, help="m of the headline step")
-    p.add_argument("--extra-rows", default="8", help="comma list of other m to report")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--extra-rows", default=None,
+                   help="comma list of other m of the headline workload (default: the ones it lists)")
+    p.add_argument("--only", action="store_true", help="time the headline workload only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--all", action="store_true", help="one line per workload and m (analysis)")
     p.add_argument("--grouped-rows", default="",
@@ -76,8 +81,17 @@ def proj_bytes(p) -> int:
     return b
 
 
+def shared_on_matrix_cores(spec) -> bool:
+    """Where the library runs the shared expert: on the matrix cores (bf16
+    activations, H and Is multiples of 32; gate/up in the route launch, down in
+    the gate/up launch), else on the vector units (gate/up in the route launch,
+    down in the down launch)."""
+    return spec.shared and spec.act_fmt == "bf16" and spec.hidden % 32 == 0 and spec.shared_inter % 32 == 0
+
+
 def layer_bytes(layer, idx, m: int) -> dict:
-    """Algorithmic bytes of one call on m rows that selected experts `idx`."""
+    """Algorithmic bytes of one call on m rows that selected experts `idx`,
+    in total and per launch of the decode path (m <= 32)."""
     spec = layer.spec
     ab = act_bytes(spec)
     distinct = len(set(int(e) for e in idx.reshape(-1)))
@@ -91,11 +105,23 @@ def layer_bytes(layer, idx, m: int) -> dict:
     x_in = m * H * ab
     out = m * H * ab
     te = m * spec.top_k
+    act = te * spec.inter * 4            # routed activations, f32: written by gate_up, read by down
+    sact = m * Is * 4                    # shared activations, f32
     total = distinct * (gu + dn) + router + shared_gu + shared_dn + gate_vec + x_in + out
-    # gate_up kernel: the active experts' gate+up rows and the shared
-    # expert's, the input rows, and the activations it writes.
-    gate_up = distinct * gu + shared_gu + x_in + te * spec.inter * 4 + m * Is * 4
-    return {"total": total, "distinct": distinct, "gate_up": gate_up,
+    mf = shared_on_matrix_cores(spec)
+    parts = max(1, Is // 2048)
+    stages = {
+        # router rows (and w_g), the input rows, and the shared gate/up
+        "route": router + gate_vec + x_in + shared_gu + sact,
+        # the active experts' gate+up rows, the input rows, the activations
+        # written; with the matrix-core shared expert also its down
+        "gate_up": distinct * gu + x_in + act + ((shared_dn + sact + parts * m * H * 4) if mf else 0),
+        # the active experts' down rows, the activations read, the output;
+        # the vector-unit shared down, or the matrix-core one's partials
+        "down_blend": distinct * dn + act + out + ((shared_dn + sact) if (spec.shared and not mf)
+                                                    else (parts * m * H * 4 if mf else 0)),
+    }
+    return {"total": total, "distinct": distinct, "stages": stages,
             "routed_weights": distinct * (gu + dn), "per_expert_gate_up": gu}
 
 
@@ -144,7 +170,7 @@ def time_workload(name: str, m: int, steps: int, warmup: int, extra_rows=(), wan
             torch.cuda.synchronize()
             bytes_c.append(layer_bytes(layer, idx.cpu().numpy(), mm))
         B = sum(b["total"] for b in bytes_c) / R
-        B_gu = sum(b["gate_up"] for b in bytes_c) / R
+        B_stage = {k: sum(b["stages"][k] for b in bytes_c) / R for k in bytes_c[0]["stages"]}
         distinct = sum(b["distinct"] for b in bytes_c) / R
 
         stream = torch.cuda.Stream()
@@ -202,32 +228,66 @@ def time_workload(name: str, m: int, steps: int, warmup: int, extra_rows=(), wan
         del g_full, g_rem
         results[mm] = {
             "us_graph": t_graph * 1e6, "us_stream": t_stream * 1e6, "bytes": B,
-            "bytes_gate_up": B_gu, "distinct_experts": distinct, "copies": R,
+            "bytes_stage": B_stage, "distinct_experts": distinct, "copies": R,
             "gbps_graph": B / t_graph / 1e9, "gbps_stream": B / t_stream / 1e9,
             "stage_us": stage_us,
         }
+    del dl
     return layer, results
 
 
-def cpu_baseline(layer, m: int, seconds: float):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    """The host threads this process may use: OMP_NUM_THREADS if set, else the
+    CPUs of its affinity mask."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_time(layer, m: int, threads: int):
+    """The oracle on the first m rows of input block 0: median seconds of 3
+    calls after 1 warm-up, on `threads` threads, and the selected experts."""
     import oracle
 
     x = layer.x(0)[:m]
-    oracle.forward(layer, x)                     # warm-up
-    n, t0 = 0, time.perf_counter()
-    idx = None
-    while True:
-        r = oracle.forward(layer, x)
-        idx = r.idx
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = (time.perf_counter() - t0) / n
+    oracle.set_threads(threads)
+    try:
+        oracle.forward(layer, x)                 # warm-up
+        ts, idx = [], None
+        for _ in range(3):
+            t0 = time.perf_counter()
+            idx = oracle.forward(layer, x).idx
+            ts.append(time.perf_counter() - t0)
+    finally:
+        oracle.set_threads(1)
+    return sorted(ts)[1], idx
+
+
+def cpu_baseline(layer, m: int):
+    """The oracle as the CPU baseline: one thread, and OpenMP over output
+    neurons on every host thread; `value` is the OpenMP leg."""
+    nt = host_threads()
+    t1, idx = cpu_time(layer, m, 1)
+    tn, _ = cpu_time(layer, m, nt)
     B = layer_bytes(layer, idx, m)["total"]
-    return {"value": round(B / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} oracle calls of the same layer on input block 0, m={m} "
-                      f"({dt * 1e3:.1f} ms per call, fp64, single host thread)",
-            "us_per_layer": round(dt * 1e6, 1)}
+    return {"value": round(B / tn / 1e9, 4), "unit": "GB/s", "cores": nt, "kind": "oracle",
+            "sample": f"the oracle (fp64 C, gcc -O2, OpenMP over output neurons) on one layer call, "
+                      f"m={m} row(s) of input block 0: median of 3 calls after 1 warm-up, on {nt} threads "
+                      f"and on 1 thread",
+            "us_per_layer": round(tn * 1e6, 1),
+            "single_thread": {"value": round(B / t1 / 1e9, 4), "unit": "GB/s", "us_per_layer": round(t1 * 1e6, 1)},
+            "cpu_model": cpu_model()}
 
 
 def kernel_source_sha256() -> str:
@@ -240,18 +300,19 @@ def kernel_source_sha256() -> str:
     return h.hexdigest()
 
 
-def traffic_entry():
-    """Calibrated HBM bytes per gate_up launch (rocprofv3 FETCH_SIZE and
+def traffic_entry(workload: str, m: int, stage: str):
+    """Calibrated HBM bytes per launch of one stage (rocprofv3 FETCH_SIZE and
     WRITE_SIZE, scaled by what they read for the plain copy kernel) from the
-    committed counter summary, if it was taken on the current kernel sources;
-    else None."""
+    committed counter summaries, if taken on the current kernel sources; else
+    None."""
     try:
         data = json.load(open(COUNTERS))
     except (OSError, ValueError):
         return None
-    if data.get("kernel_source_sha256") != kernel_source_sha256():
+    ent = data.get(f"{workload}/m{m}/{stage}")
+    if not ent or ent.get("kernel_source_sha256") != kernel_source_sha256():
         return None
-    return data.get("traffic_bytes_per_launch")
+    return ent.get("traffic_bytes_per_launch")
 
 
 def stream_read_gbps(gib: int = 4) -> dict:
@@ -284,6 +345,39 @@ def stream_read_gbps(gib: int = 4) -> dict:
     del buf
     torch.cuda.empty_cache()
     return {"read": nbytes / t_read / 1e9, "copy": 2 * half / t_copy / 1e9}
+
+
+def stage_roofline(res: dict) -> dict:
+    """The dominant kernel of one timed (workload, m): the stage with the
+    longest average launch, its algorithmic bytes per launch and the rate."""
+    st = max(res["stage_us"], key=lambda k: res["stage_us"][k])
+    us = res["stage_us"][st]
+    b = res["bytes_stage"].get(st, 0.0)
+    achieved = b / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": st, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "bytes_per_launch": int(b), "avg_launch_us": round(us, 3)}
+
+
+def detail_entry(r: dict, read_gbps: float) -> dict:
+    return {
+        "us_per_layer_graph": round(r["us_graph"], 2), "us_per_layer_stream": round(r["us_stream"], 2),
+        "gbps_graph": round(r["gbps_graph"], 1), "gbps_stream": round(r["gbps_stream"], 1),
+        "pct_of_peak_graph": round(100 * r["gbps_graph"] / PEAK_HBM_GBPS, 1),
+        "pct_of_stream_read": round(100 * r["gbps_graph"] / read_gbps, 1),
+        "bytes_per_call": int(r["bytes"]), "distinct_experts": r["distinct_experts"],
+        "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
+        "stage_bytes": {k: int(v) for k, v in r["bytes_stage"].items()},
+        "dominant": stage_roofline(r),
+        "copies_rotated": r["copies"],
+    }
+
+
+def describe(name: str, spec) -> str:
+    return (f"{name}: decode MoE layer H={spec.hidden} E={spec.num_experts} top-{spec.top_k} "
+            f"I={spec.inter} experts={spec.expert_fmt} routing={spec.routing}"
+            + (" weight-before-FFN" if spec.weight_before_ffn else "")
+            + (f" shared Is={spec.shared_inter}" + (" gated" if spec.shared_gated else "") if spec.shared else ""))
 
 
 def main():
@@ -320,29 +414,48 @@ def main():
             torch.cuda.empty_cache()
         return
 
-    extra = [int(v) for v in args.extra_rows.split(",") if v]
     spec = synth.WORKLOADS[args.workload]
+    if args.extra_rows is None:
+        extra = [r for r in spec.rows if r != args.rows]
+    else:
+        extra = [int(v) for v in args.extra_rows.split(",") if v]
     # Row counts above the workload's own take the grouped path (m > 32).
     big = max([args.rows] + extra)
+    print(f"[bench] {args.workload}: m = {[args.rows] + extra}", file=sys.stderr, flush=True)
     layer, res = time_workload(args.workload, args.rows, args.steps, args.warmup, extra,
                                max_rows=big if big > spec.max_rows else None)
+    torch.cuda.empty_cache()
     head = res[args.rows]
     sol = stream_read_gbps()
     read_gbps = sol["read"]
-    gu_us = head["stage_us"]["gate_up"]
-    achieved = head["bytes_gate_up"] / (gu_us * 1e-6) / 1e9
-    cpu = None if args.no_cpu_baseline else cpu_baseline(layer, args.rows, args.cpu_seconds)
-    detail = {}
-    for mm, r in res.items():
-        detail[f"m{mm}"] = {
-            "us_per_layer_graph": round(r["us_graph"], 2), "us_per_layer_stream": round(r["us_stream"], 2),
-            "gbps_graph": round(r["gbps_graph"], 1), "gbps_stream": round(r["gbps_stream"], 1),
-            "pct_of_peak_graph": round(100 * r["gbps_graph"] / PEAK_HBM_GBPS, 1),
-            "pct_of_stream_read": round(100 * r["gbps_graph"] / read_gbps, 1),
-            "bytes_per_call": int(r["bytes"]), "distinct_experts": r["distinct_experts"],
-            "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
-            "copies_rotated": r["copies"],
-        }
+    roof = stage_roofline(head)
+    roof["traffic"] = traffic_entry(args.workload, args.rows, roof["kernel"])
+    cpu = None
+    cpu_other = {}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(layer, args.rows)
+    del layer
+    detail = {f"m{mm}": detail_entry(r, read_gbps) for mm, r in res.items()}
+    others = {}
+    if not args.only:
+        for name, ospec in synth.WORKLOADS.items():
+            if name == args.workload:
+                continue
+            print(f"[bench] {name}: m = {list(ospec.rows)}", file=sys.stderr, flush=True)
+            olayer, ores = time_workload(name, ospec.rows[0], args.steps, args.warmup, ospec.rows[1:])
+            ent = {"config": describe(name, ospec)}
+            ent.update({f"m{mm}": detail_entry(r, read_gbps) for mm, r in ores.items()})
+            if not args.no_cpu_baseline:
+                t1, idx = cpu_time(olayer, 1, 1)
+                tn, _ = cpu_time(olayer, 1, host_threads())
+                B = layer_bytes(olayer, idx, 1)["total"]
+                ent["cpu_oracle_m1"] = {"us_single_thread": round(t1 * 1e6, 1),
+                                        "us_threads": round(tn * 1e6, 1), "threads": host_threads(),
+                                        "gbps_threads": round(B / tn / 1e9, 4)}
+            others[name] = ent
+            del olayer
+            torch.cuda.empty_cache()
     line = {
         "metric": METRIC,
         "value": round(head["gbps_graph"], 1),
@@ -357,21 +470,14 @@ def main():
         "dtype": spec.expert_fmt if spec.expert_fmt != "f32" else "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: decode MoE layer H={spec.hidden} E={spec.num_experts} "
-                        f"top-{spec.top_k} I={spec.inter} experts={spec.expert_fmt} "
-                        f"routing={spec.routing}" + (f" shared Is={spec.shared_inter}" if spec.shared else ""),
+            "workload": describe(args.workload, spec),
             "rows": args.rows,
             "timing": "HIP graph of consecutive forwards over rotated weight copies (cold caches)",
         },
-        "roofline": {
-            "bound": "hbm", "kernel": "gate_up", "achieved": round(achieved, 1),
-            "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": traffic_entry(),
-            "bytes_per_launch": int(head["bytes_gate_up"]),
-            "avg_launch_us": round(gu_us, 3),
-        },
+        "roofline": roof,
         "cpu_baseline": cpu,
         "detail": detail,
+        "other_workloads": others,
         "stream_read_gbps": round(read_gbps, 1),
         "stream_copy_gbps": round(sol["copy"], 1),
     }

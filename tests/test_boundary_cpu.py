@@ -42,7 +42,7 @@ def _desc(**kw):
     ("max_rows", 0, md.MOE_EINVAL),
     ("act_fmt", md.MOE_AFF4_G64, md.MOE_EINVAL),
     ("expert_fmt", 7, md.MOE_EINVAL),
-    ("routing", 3, md.MOE_EINVAL),
+    ("routing", 4, md.MOE_EINVAL),
     ("flags", 1 << 10, md.MOE_EINVAL),
     ("flags", md.MOE_SHARED_GATED, md.MOE_EINVAL),
     ("inter", 100, md.MOE_EUNSUPPORTED),

@@ -105,6 +105,21 @@ def test_grouped_pre_expert_norm(fmt):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("fmt,routing,bias", [("bf16", "sqrtsoftplus", True), ("mxfp4", "sqrtsoftplus", False),
+                                            ("aff4", "softmax", None)])
+def test_grouped_router_pre_norm_and_sqrtsoftplus(fmt, routing, bias):
+    spec = small(hidden=256, num_experts=12, top_k=3, inter=192, shared_inter=160, expert_fmt=fmt,
+                 routing=routing, route_bias=bias, router_pre_norm=True, shared=True, shared_gated=True,
+                 rows=(80,))
+    layer = synth.make_layer(spec, seed=670 + len(fmt) + len(routing), threads=4)
+    x = layer.x(0)
+    for out_f32 in (False, True):
+        dl = DeviceLayer(layer, out_f32=out_f32)
+        grouped_rows(dl, layer, x, (33, 80, 8), f"router pre-norm {fmt}/{routing} f32out={out_f32}", out_f32)
+        del dl
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("E,k,inter,hidden", [(256, 16, 64, 128), (2, 1, 96, 160), (4, 4, 128, 64),
                                               (1, 1, 64, 96)])
 def test_grouped_pair_extremes(E, k, inter, hidden):
