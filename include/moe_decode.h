@@ -254,6 +254,20 @@ moe_status moe_decode_forward(const moe_decode_plan_t *plan, const moe_decode_we
                               float *w_out, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/* The same forward with no workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): it allocates nothing and uses a library-owned device
+ * array of 32 MiB, one per GPU, held until the process ends.  A plan whose
+ * workspace (moe_decode_plan's *workspace_bytes) exceeds 32 MiB is rejected
+ * with MOE_EWORKSPACE, launching nothing.  Every such call on a GPU shares
+ * that GPU's array, which keeps the last call's contents: calls that overlap
+ * on one GPU race.  The first call on a GPU also launches a kernel that
+ * clears the array's reserved words.  Other arguments and errors as
+ * moe_decode_forward. */
+moe_status moe_decode_forward_noalloc(const moe_decode_plan_t *plan, const moe_decode_weights *w,
+                                      const void *x, int32_t m, void *out, int32_t *idx_out,
+                                      float *w_out, void *stream);
+
 /* Number of kernel launches (stages) one forward makes, and the name of
  * stage i ("route", "gate_up", "down_blend", ...). */
 int32_t moe_decode_num_stages(const moe_decode_plan_t *plan);

@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -528,6 +529,40 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   return ok();
 }
 
+// ------------------------------------------- the allocation-free forward
+//
+// Its workspace is a file-scope device array, one per GPU the library runs
+// on, held until the process ends.  In host code `scratch` only names the
+// array: its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device and kept in g_scratch.  Every
+// allocation-free call on a GPU shares that GPU's array, so such calls must
+// not overlap there.  Its reserved words are cleared once, by a kernel, on
+// the device's first call; every forward leaves them cleared.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];   // per device: the address of `scratch` there, or null
+
+moe_status device_scratch(const moe_decode_plan_t *plan, hipStream_t stream, void **ws) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EUNSUPPORTED, "device %d past the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(MOE_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    e = moe::launch_clear_sync(reinterpret_cast<unsigned *>(static_cast<char *>(p) + plan->L.sync), moe::SYNC_WORDS,
+                               stream);
+    if (e != hipSuccess) return fail(MOE_EHIP, "scratch clear launch: %s", hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *ws = g_scratch[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -584,6 +619,21 @@ moe_status moe_decode_forward(const moe_decode_plan_t *plan, const moe_decode_we
                               int32_t m, void *out, int32_t *idx_out, float *w_out, void *workspace,
                               size_t workspace_bytes, void *stream) {
   return forward_impl(plan, w, x, m, out, idx_out, w_out, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+moe_status moe_decode_forward_noalloc(const moe_decode_plan_t *plan, const moe_decode_weights *w,
+                                      const void *x, int32_t m, void *out, int32_t *idx_out, float *w_out,
+                                      void *stream) {
+  if (!plan) return fail(MOE_EINVAL, "plan is NULL");
+  if (plan->L.total > kScratchBytes)
+    return fail(MOE_EWORKSPACE,
+                "the plan needs %zu bytes of workspace; the allocation-free forward holds %zu (use "
+                "moe_decode_forward with a workspace of the caller's)",
+                plan->L.total, kScratchBytes);
+  void *ws = nullptr;
+  moe_status st = device_scratch(plan, static_cast<hipStream_t>(stream), &ws);
+  if (st != MOE_OK) return st;
+  return forward_impl(plan, w, x, m, out, idx_out, w_out, ws, kScratchBytes, stream, nullptr, 0);
 }
 
 moe_status moe_decode_forward_timed(const moe_decode_plan_t *plan, const moe_decode_weights *w,

@@ -91,6 +91,8 @@ def lib() -> C.CDLL:
         fwd = [vp, C.POINTER(moe_decode_weights), vp, C.c_int32, vp, vp, vp, vp, C.c_size_t, vp]
         L.moe_decode_forward.restype = st
         L.moe_decode_forward.argtypes = fwd
+        L.moe_decode_forward_noalloc.restype = st
+        L.moe_decode_forward_noalloc.argtypes = [vp, C.POINTER(moe_decode_weights), vp, C.c_int32, vp, vp, vp, vp]
         L.moe_decode_forward_timed.restype = st
         L.moe_decode_forward_timed.argtypes = fwd + [C.POINTER(vp), C.c_int32]
         L.moe_decode_num_stages.restype = C.c_int32
@@ -156,6 +158,11 @@ def moe_decode_forward(plan, weights: moe_decode_weights, x: int, m: int, out: i
                        workspace_bytes: int, stream: int) -> None:
     _check(lib().moe_decode_forward(plan, C.byref(weights), x, m, out, idx_out, w_out,
                                     workspace, workspace_bytes, stream))
+
+
+def moe_decode_forward_noalloc(plan, weights: moe_decode_weights, x: int, m: int, out: int,
+                               idx_out: int | None, w_out: int | None, stream: int) -> None:
+    _check(lib().moe_decode_forward_noalloc(plan, C.byref(weights), x, m, out, idx_out, w_out, stream))
 
 
 def moe_decode_forward_timed(plan, weights: moe_decode_weights, x: int, m: int, out: int,

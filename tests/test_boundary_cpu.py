@@ -249,3 +249,20 @@ def test_measurement_utilities_reject_bad_arguments():
         with pytest.raises(md.MoeDecodeError) as ei:
             md.moe_decode_bench_read(args[0], args[1], args[2], None)
         assert ei.value.status == md.MOE_EINVAL
+
+
+def test_noalloc_forward_rejects_a_plan_past_its_array():
+    # 16 experts of 8192 x 8192, top-16, 256 rows: the activations alone need
+    # 256 * 16 * 8192 * 4 bytes, far past the 32 MiB array; rejected before
+    # any device call.
+    d = _desc(hidden=8192, num_experts=16, top_k=16, inter=8192, max_rows=256)
+    plan, ws = md.moe_decode_plan(d)
+    try:
+        assert ws > 32 << 20
+        w = md.moe_decode_weights()
+        with pytest.raises(md.MoeDecodeError) as ei:
+            md.moe_decode_forward_noalloc(plan, w, 256, 1, 256, None, None, 0)
+        assert ei.value.status == md.MOE_EWORKSPACE
+        assert "32" in md.moe_decode_last_error() or "33554432" in md.moe_decode_last_error()
+    finally:
+        md.lib().moe_decode_plan_destroy(plan)
