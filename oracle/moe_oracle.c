@@ -47,9 +47,10 @@
  *    family", commit message: router_sqrtsoftplus among the routers, next to
  *    the biased router that selects by the biased score and weights by the
  *    unbiased one) scores an expert s = sqrt(softplus(l)), softplus(l) =
- *    log(1 + e^l); it selects by s, or by s + bias when an expert bias is
- *    given, and weights a slot by its unbiased s (then norm_topk_prob and
- *    routed_scaling_factor as for the other routers);
+ *    log(1 + e^l); it selects by s + bias when an expert bias is given, else
+ *    by s -- taken as the logit, which s orders the same way -- and weights
+ *    a slot by its unbiased s (then norm_topk_prob and routed_scaling_factor
+ *    as for the other routers);
  *  - the router pre-norm ("forward_bf16_grouped_decode.rs", the predicate
  *    refuses weights.router_pre_norm: a norm the router's input goes through)
  *    is the RMS norm of each row with its own weight router_norm_w, stored in
@@ -250,11 +251,13 @@ double orc_sqrtsoftplus(double l) {
  * probability).  Sigmoid with bias ("wire lfm2" Summary; iron #24 commit:
  * select by the biased score): sigmoid(logit) + bias.  Raw-logit sigmoid
  * ("routed_weight_site.rs" module doc: top-k on the raw logits, a monotone
- * map of the sigmoid): the logit.  Sqrt-softplus: the score, plus the bias
- * when one is given. */
+ * map of the sigmoid): the logit.  Sqrt-softplus: the score plus the bias
+ * when one is given; without one, the logit (the score is strictly
+ * increasing in it: the same order, with no rounding of the score to tie
+ * two different logits). */
 static double select_key(const orc_desc *d, const float *bias, const double *l, int32_t e) {
   if (d->routing == ORC_SIGMOID_BIAS) return sigmoid(l[e]) + (double)bias[e];
-  if (d->routing == ORC_SQRTSOFTPLUS) return orc_sqrtsoftplus(l[e]) + (bias ? (double)bias[e] : 0.0);
+  if (d->routing == ORC_SQRTSOFTPLUS && bias) return orc_sqrtsoftplus(l[e]) + (double)bias[e];
   return l[e];
 }
 
