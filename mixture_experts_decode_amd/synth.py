@@ -41,6 +41,11 @@ Formats (stored codes):
     nearest ``amax_block / (6 * s2)`` (ties to the even code); codes = nearest
     E2M1 value of ``w / (E4M3(scale) * s2)``, ties to the even code,
     saturating at 6 (all 0 where the block scale is 0).
+  * ``fp8``: one OCP E4M3 byte per element, ``data [N, K]`` uint8, and one
+    float32 scale per 128 x 128 block, ``scale [ceil(N/128), ceil(K/128)]``
+    (the last blocks ragged).  Quantizer (per block): ``s = f32(amax / 448)``
+    (1 if amax = 0); code = nearest E4M3 value of ``w / s``, ties to the even
+    code, saturating at 448, sign in bit 7.
 """
 from __future__ import annotations
 
@@ -52,7 +57,7 @@ from typing import Optional
 import numpy as np
 
 ACT_FORMATS = ("f32", "bf16")
-EXPERT_FORMATS = ("f32", "bf16", "aff4", "mxfp4", "nvfp4")
+EXPERT_FORMATS = ("f32", "bf16", "aff4", "mxfp4", "nvfp4", "fp8")
 ROUTINGS = ("softmax", "sigmoid_bias", "sigmoid_logit", "sqrtsoftplus")
 ACTIVATIONS = ("silu", "gelu")
 
@@ -60,6 +65,8 @@ ACTIVATIONS = ("silu", "gelu")
 AFF4_GROUP = 64
 MXFP4_BLOCK = 32
 NVFP4_BLOCK = 16
+# The fp8 scale block: FP8_BLOCK x FP8_BLOCK elements of [N, K].
+FP8_BLOCK = 128
 
 
 @dataclasses.dataclass(frozen=True)
@@ -243,6 +250,27 @@ def quantize_nvfp4(w: np.ndarray):
     return packed, sc, s2
 
 
+def quantize_fp8(w: np.ndarray):
+    """FP8 quantizer -> (E4M3 bytes [N, K], float32 scales [ceil(N/128), ceil(K/128)])."""
+    n, k = w.shape
+    nb, kb = -(-n // FP8_BLOCK), -(-k // FP8_BLOCK)
+    w64 = w.astype(np.float64)
+    scale = np.ones((nb, kb), np.float32)
+    codes = np.zeros((n, k), np.uint8)
+    for bi in range(nb):
+        for bj in range(kb):
+            blk = w64[bi * FP8_BLOCK:(bi + 1) * FP8_BLOCK, bj * FP8_BLOCK:(bj + 1) * FP8_BLOCK]
+            amax = float(np.abs(blk).max()) if blk.size else 0.0
+            s = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+            if s == 0:
+                s = np.float32(1.0)
+            scale[bi, bj] = s
+            scaled = blk / float(s)
+            c = _nearest_code(np.abs(scaled), _E4M3_MIDPOINTS) | np.where(scaled < 0, 0x80, 0)
+            codes[bi * FP8_BLOCK:(bi + 1) * FP8_BLOCK, bj * FP8_BLOCK:(bj + 1) * FP8_BLOCK] = c
+    return codes, scale
+
+
 # ----------------------------------------------------------------------------
 # Layer generation.
 # ----------------------------------------------------------------------------
@@ -269,8 +297,9 @@ def _store_act(w: np.ndarray, fmt: str) -> np.ndarray:
 class Projection:
     """All E experts' copies of one projection, stacked on axis 0.
 
-    ``data`` is [E, N, K] (f32 / bf16 bits) or [E, N, K/2] packed 4-bit codes;
-    ``scale`` / ``bias`` are [E, N, K/G] or None; ``scale2`` is the nvfp4
+    ``data`` is [E, N, K] (f32 / bf16 bits / fp8 bytes) or [E, N, K/2] packed
+    4-bit codes; ``scale`` / ``bias`` are [E, N, K/G] (fp8: [E, ceil(N/128),
+    ceil(K/128)] float32) or None; ``scale2`` is the nvfp4
     second-level scale of each expert's copy, [E] float32, else None.
     """
 
@@ -332,6 +361,9 @@ def _alloc_projection(fmt: str, e: int, n: int, k: int) -> Projection:
         return Projection(fmt, n, k, np.empty((e, n, k // 2), np.uint8),
                           np.empty((e, n, k // NVFP4_BLOCK), np.uint8),
                           scale2=np.empty((e,), np.float32))
+    if fmt == "fp8":
+        return Projection(fmt, n, k, np.empty((e, n, k), np.uint8),
+                          np.empty((e, -(-n // FP8_BLOCK), -(-k // FP8_BLOCK)), np.float32))
     raise ValueError(fmt)
 
 
@@ -346,6 +378,8 @@ def _fill_expert(proj: Projection, e: int, w: np.ndarray) -> None:
         proj.data[e], proj.scale[e] = quantize_mxfp4(w)
     elif proj.fmt == "nvfp4":
         proj.data[e], proj.scale[e], proj.scale2[e] = quantize_nvfp4(w)
+    elif proj.fmt == "fp8":
+        proj.data[e], proj.scale[e] = quantize_fp8(w)
 
 
 def check_spec(spec: LayerSpec) -> None:

@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 
-FMT = {"f32": 0, "bf16": 1, "aff4": 2, "mxfp4": 3, "nvfp4": 4}
+FMT = {"f32": 0, "bf16": 1, "aff4": 2, "mxfp4": 3, "nvfp4": 4, "fp8": 5}
 ROUTING = {"softmax": 0, "sigmoid_bias": 1, "sigmoid_logit": 2, "sqrtsoftplus": 3}
 
 

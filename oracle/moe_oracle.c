@@ -62,7 +62,16 @@
  *    one E4M3 block scale per 16 elements along K, times the projection's
  *    fp32 second-level scale; the activations stay in their own format
  *    (weight-only dequantisation; the page's input_scale, which quantises
- *    activations for a 4-bit GEMM, has no part in it).
+ *    activations for a 4-bit GEMM, has no part in it);
+ *  - FP8 weights ("forward_bf16_grouped_decode.rs": the grouped decode
+ *    dispatch serves NVFP4, then FP8, then BF16 experts, the FP8 one in its
+ *    own forward_fp8_grouped_decode; the page fixes neither the encoding nor
+ *    the scales) are OCP FP8 E4M3 codes, one byte per element in the [N, K]
+ *    order of the other formats, with one fp32 scale per 128 x 128 block of
+ *    the projection (row-major [ceil(N/128), ceil(K/128)], the last blocks
+ *    ragged): the value is E4M3(code) * scale.  E4M3 is the FP8 weight
+ *    encoding of block-scaled checkpoints and 128 x 128 their usual block;
+ *    the activations stay in their own format (weight-only dequantisation).
  */
 #include "moe_oracle.h"
 
@@ -143,6 +152,11 @@ void orc_decode_row(int32_t fmt, const void *w, const void *s, const void *b,
         size_t g = (size_t)n * (K / 16) + k / 16;
         out[k] = e2m1_value(nibble((const uint8_t *)w, K, n, k)) *
                  orc_e4m3_value(((const uint8_t *)s)[g]) * (double)*(const float *)b;
+        break;
+      }
+      case ORC_FP8: { /* value = E4M3(code) * scale, one fp32 scale per 128 x 128 */
+        size_t g = (size_t)(n / 128) * (size_t)((K + 127) / 128) + (size_t)(k / 128);
+        out[k] = orc_e4m3_value(((const uint8_t *)w)[(size_t)n * K + k]) * (double)((const float *)s)[g];
         break;
       }
       default:
@@ -380,7 +394,7 @@ static int valid_desc(const orc_desc *d) {
   if (d->hidden <= 0 || d->num_experts <= 0 || d->inter <= 0) return 0;
   if (d->top_k <= 0 || d->top_k > d->num_experts) return 0;
   if (d->act_fmt != ORC_F32 && d->act_fmt != ORC_BF16) return 0;
-  if (d->expert_fmt < ORC_F32 || d->expert_fmt > ORC_NVFP4) return 0;
+  if (d->expert_fmt < ORC_F32 || d->expert_fmt > ORC_FP8) return 0;
   if (d->routing < ORC_SOFTMAX || d->routing > ORC_SQRTSOFTPLUS) return 0;
   if (d->expert_fmt == ORC_AFF4 && (d->hidden % 64 || d->inter % 64)) return 0;
   if (d->expert_fmt == ORC_MXFP4 && (d->hidden % 32 || d->inter % 32)) return 0;

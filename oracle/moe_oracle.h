@@ -17,14 +17,14 @@ extern "C" {
 #endif
 
 /* Storage formats (numbers chosen independently of the HIP library's). */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_AFF4 = 2, ORC_MXFP4 = 3, ORC_NVFP4 = 4 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_AFF4 = 2, ORC_MXFP4 = 3, ORC_NVFP4 = 4, ORC_FP8 = 5 };
 /* Routing modes. */
 enum { ORC_SOFTMAX = 0, ORC_SIGMOID_BIAS = 1, ORC_SIGMOID_LOGIT = 2, ORC_SQRTSOFTPLUS = 3 };
 
 typedef struct {
   int32_t hidden, num_experts, top_k, inter, shared_inter;
   int32_t act_fmt;      /* ORC_F32 / ORC_BF16: x, router, shared expert, w_g */
-  int32_t expert_fmt;   /* ORC_F32 / ORC_BF16 / ORC_AFF4 / ORC_MXFP4 / ORC_NVFP4 */
+  int32_t expert_fmt;   /* ORC_F32 / ORC_BF16 / ORC_AFF4 / ORC_MXFP4 / ORC_NVFP4 / ORC_FP8 */
   int32_t routing;
   int32_t norm_topk, weight_before_ffn, shared, shared_gated;
   double routed_scaling_factor;
@@ -40,7 +40,8 @@ typedef struct {
   /* Per-expert host pointers, [E] each.  f32/bf16: [N,K]; 4-bit: packed
    * [N,K/2] bytes, low nibble = even element; scale [N,K/G]; aff4 bias
    * [N,K/64] bf16; nvfp4: the "bias" entry points to the projection's one
-   * fp32 second-level scale. */
+   * fp32 second-level scale.  fp8: one E4M3 byte per element, [N,K], and
+   * one fp32 scale per 128 x 128 block, [ceil(N/128), ceil(K/128)]. */
   const void *const *gate, *const *up, *const *down;
   const void *const *gate_s, *const *up_s, *const *down_s;
   const void *const *gate_b, *const *up_b, *const *down_b;

@@ -2,7 +2,8 @@
 
 A second, independent evaluation used only to pin the oracle on tiny inputs:
 it decodes stored codes with lookup tables and, for the E4M3 block scales of
-nvfp4, with torch's float8_e4m3fn conversion (the oracle uses bit formulas),
+nvfp4 and the fp8 weights, with torch's float8_e4m3fn conversion (the oracle
+uses bit formulas),
 routes with a stable argsort (the oracle scans), and evaluates EVERY expert on
 every row, weighting by a mask that is zero for the experts a row did not
 select (the oracle evaluates only the selected ones, slot by slot).
@@ -38,6 +39,11 @@ def dense_weight(proj, e: int) -> np.ndarray:
         return proj.data[e].astype(np.float64)
     if proj.fmt == "bf16":
         return bf16_to_f64(proj.data[e])
+    if proj.fmt == "fp8":
+        # Each 128 x 128 block's scale tiled over it with a Kronecker product.
+        n, k = proj.data[e].shape
+        sc = np.kron(proj.scale[e].astype(np.float64), np.ones((128, 128)))[:n, :k]
+        return e4m3_to_f64(proj.data[e]) * sc
     q = _unpack_nibbles(proj.data[e])
     if proj.fmt == "aff4":
         s = np.repeat(bf16_to_f64(proj.scale[e]), 64, axis=1)

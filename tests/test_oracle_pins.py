@@ -90,6 +90,43 @@ def test_nvfp4_row_closed_form():
     assert np.array_equal(oracle.decode_row("nvfp4", packed2, scale2, s2, 32, 1), want)
 
 
+def test_fp8_row_every_byte_against_torch_float8():
+    # Row of 256 bytes 0x00..0xFF over two 128-wide blocks with scales 2 and
+    # 0.5: each element is torch's float8_e4m3fn value times its block's
+    # scale (NaN for 0x7F and 0xFF).
+    codes = np.arange(256, dtype=np.uint8)[None, :]
+    scale = np.array([[2.0, 0.5]], np.float32)
+    got = oracle.decode_row("fp8", codes, scale, None, 256, 0)
+    want = dense_ref.e4m3_to_f64(codes[0]) * np.repeat([2.0, 0.5], 128)
+    nan = np.isnan(want)
+    assert list(np.flatnonzero(nan)) == [0x7F, 0xFF]
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_fp8_row_closed_form():
+    # 0x38 is 1.0 and 0xC0 is -2.0: with block scales 0.25 and 3, the row is
+    # 0.25 on its first 128 elements and -6 on the next 128.
+    codes = np.concatenate([np.full(128, 0x38), np.full(128, 0xC0)]).astype(np.uint8)[None, :]
+    got = oracle.decode_row("fp8", codes, np.array([[0.25, 3.0]], np.float32), None, 256, 0)
+    assert np.array_equal(got, np.concatenate([np.full(128, 0.25), np.full(128, -6.0)]))
+
+
+def test_fp8_block_scale_index_with_ragged_blocks():
+    # A 300 x 300 projection has 3 x 3 scale blocks, the last ones 44 wide.
+    # All codes 1.0 and block (i, j) scaled 1 + 10 i + j: row n reads the
+    # scales of row block n // 128, one per 128 columns -- a transposed or
+    # floor-sized scale index reads other values.
+    N = K = 300
+    codes = np.full((N, K), 0x38, np.uint8)
+    scale = np.array([[1 + 10 * i + j for j in range(3)] for i in range(3)], np.float32)
+    for n in (0, 127, 128, 255, 256, 299):
+        i = n // 128
+        want = np.concatenate([np.full(128, 1 + 10 * i), np.full(128, 2 + 10 * i), np.full(44, 3 + 10 * i)])
+        assert np.array_equal(oracle.decode_row("fp8", codes, scale, None, K, n), want), n
+
+
 @pytest.mark.parametrize("which", ["up", "down"])
 def test_nvfp4_second_level_scale_is_linear_where_it_must_be(which):
     # silu(g) * v is linear in v and the down projection in its weights, so
@@ -407,7 +444,7 @@ def test_identity_experts_give_gelu_times_x_against_normal_table():
 # ------------------------------------------ P-10 brute force, all variants
 
 VARIANTS = list(itertools.product(
-    ["f32", "bf16"], ["f32", "bf16", "aff4", "mxfp4", "nvfp4"],
+    ["f32", "bf16"], ["f32", "bf16", "aff4", "mxfp4", "nvfp4", "fp8"],
     ["softmax", "sigmoid_bias", "sigmoid_logit"], [False, True], [False, True],
     ["none", "plain", "gated"]))
 
@@ -624,13 +661,16 @@ def test_input_weight_commutes_with_projection():
 
 # ------------------------------------------- P-15 quantized decode is exact
 
-@pytest.mark.parametrize("fmt", ["aff4", "mxfp4", "nvfp4"])
+@pytest.mark.parametrize("fmt", ["aff4", "mxfp4", "nvfp4", "fp8"])
 def test_quantized_layer_equals_f32_layer_of_decoded_values(fmt):
     spec = tiny(act_fmt="bf16", expert_fmt=fmt, top_k=3, w_std=0.02)
     layer = synth.make_layer(spec, seed=18)
     if fmt == "nvfp4":   # a power-of-two second-level scale keeps the values exact in f32
         for name in ("gate", "up", "down"):
             getattr(layer, name).scale2[:] = np.float32(2.0 ** -10)
+    if fmt == "fp8":     # so do power-of-two block scales
+        for name in ("gate", "up", "down"):
+            getattr(layer, name).scale[:] = np.float32(2.0 ** -12)
     x = synth.make_x(spec, 18, rows=4)
     dense = synth.make_layer(spec.replace(expert_fmt="f32"), seed=18)
     for name in ("gate", "up", "down"):
@@ -648,6 +688,22 @@ def test_invalid_description_rejected():
     spec = tiny(expert_fmt="aff4", inter=32)      # aff4 needs I % 64 == 0
     with pytest.raises(ValueError):
         synth.check_spec(spec)
+
+
+@pytest.mark.parametrize("act,before", [("f32", False), ("bf16", True)])
+def test_fp8_layer_with_ragged_blocks_matches_dense_brute_force(act, before):
+    # H = 320 and I = 200: 128 x 128 scale blocks with ragged last blocks
+    # along both dimensions of every projection.
+    spec = tiny(act_fmt=act, expert_fmt="fp8", hidden=320, inter=200, num_experts=6, top_k=2,
+                weight_before_ffn=before, shared=True, shared_gated=True, shared_inter=64, w_std=0.05)
+    layer = synth.make_layer(spec, seed=31 + before, threads=1)
+    assert layer.gate.scale.shape == (6, 2, 3) and layer.down.scale.shape == (6, 3, 2)
+    x = synth.make_x(spec, 31, rows=4)
+    r = oracle.forward(layer, x)
+    want, weights, selected = dense_ref.dense_forward(layer, x)
+    for row in range(4):
+        assert list(r.idx[row]) == list(selected[row])
+    assert np.max(np.abs(r.out - want)) <= 1e-12 * rms(want)
 
 
 # ------------------------------------- P-19 the sqrt-softplus router score

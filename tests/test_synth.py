@@ -87,3 +87,28 @@ def test_nvfp4_quantizer_scales_and_error():
     err = np.abs(deq - w).reshape(8, 4, 16).max(axis=2)
     assert np.all(err <= 0.25 * blk + 1e-12)
     assert np.abs(deq - w).mean() < 0.1 * np.abs(w).mean()
+
+
+def test_fp8_quantizer_scales_and_error():
+    # Blocks of 128 x 128 with ragged edges (200 x 300 -> 2 x 3 blocks); each
+    # block's scale maps its largest magnitude to 448 (the E4M3 maximum); an
+    # all-zero block keeps scale 1 and code 0; every element is within half
+    # an E4M3 step (relative 2^-4 of the element, or the subnormal step).
+    rng = np.random.default_rng(4)
+    w = (rng.standard_normal((200, 300)) * 0.02).astype(np.float32)
+    w[128:, 256:] = 0.0
+    codes, sc = synth.quantize_fp8(w)
+    assert codes.shape == (200, 300) and sc.shape == (2, 3) and sc.dtype == np.float32
+    for i in range(2):
+        for j in range(3):
+            blk = np.abs(w[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]).max()
+            assert sc[i, j] == (np.float32(blk / 448.0) if blk > 0 else np.float32(1.0))
+    assert not codes[128:, 256:].any()
+    assert not np.any((codes & 0x7F) == 0x7F)            # no NaN codes: saturation at 448
+    proj = synth.Projection("fp8", 200, 300, codes[None], sc[None])
+    from tests import dense_ref
+    deq = dense_ref.dense_weight(proj, 0)
+    s_full = np.kron(sc.astype(np.float64), np.ones((128, 128)))[:200, :300]
+    step = np.maximum(np.abs(w) * 2.0 ** -4, s_full * 2.0 ** -10)   # half a step, normal / subnormal
+    assert np.all(np.abs(deq - w) <= step * (1 + 1e-6))
+    assert np.array_equal(np.signbit(deq[w != 0]), np.signbit(w[w != 0]))
