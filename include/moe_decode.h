@@ -33,7 +33,7 @@
  * m = 33..256 (prefill chunks, speculative-decoding verification) takes a
  * grouped path of the same steps whose expert products run on the matrix
  * cores (five launches); it needs bf16 activations, bf16, aff4, mxfp4 or
- * nvfp4 experts and H, I, Is multiples of 32, which moe_decode_plan checks
+ * nvfp4 experts (not fp8) and H, I, Is multiples of 32, which moe_decode_plan checks
  * when max_rows > 32.  Each path gives a row the same bits for every m it
  * serves; the two paths agree within the tolerance of their accumulation
  * orders.
@@ -87,8 +87,17 @@ typedef enum {
  *                  one OCP FP8 E4M3 byte s per 16 elements along K ([N, K/16])
  *                  and one float32 s2 per expert projection (the *_scale2
  *                  arrays below); the E4M3 NaN bytes 0x7F / 0xFF are not valid.
- *                  The activations stay in act_fmt (weight-only dequantisation). */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_AFF4_G64 = 2, MOE_MXFP4_B32 = 3, MOE_NVFP4_B16 = 4 } moe_format;
+ *                  The activations stay in act_fmt (weight-only dequantisation).
+ *   MOE_FP8_B128   FP8 experts (metrale "forward_bf16_grouped_decode.rs": the
+ *                  grouped decode serves NVFP4, FP8 and BF16 experts; the
+ *                  page fixes no layout, this is the library's reading): one
+ *                  OCP FP8 E4M3 byte per element, [N, K]; value = E4M3(code)
+ *                  * s with one float32 s per 128 x 128 block of the matrix
+ *                  ([N/128, K/128], row-major); H and I must be multiples of
+ *                  128; the NaN bytes 0x7F / 0xFF are not valid.  Weight-only
+ *                  dequantisation like NVFP4; m = 1..32 only. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_AFF4_G64 = 2, MOE_MXFP4_B32 = 3, MOE_NVFP4_B16 = 4,
+               MOE_FP8_B128 = 5 } moe_format;
 
 typedef enum {
   MOE_ROUTE_SOFTMAX = 0,        /* select by logit, weight softmax(l) over all E */
@@ -141,13 +150,14 @@ typedef struct {
   const void *router_w;        /* [E, H] act_fmt */
   const float *expert_bias;    /* [E] float32; required by MOE_ROUTE_SIGMOID_BIAS, optional with
                                   MOE_ROUTE_SQRTSOFTPLUS, ignored otherwise */
-  const uint64_t *gate_w;      /* table: [I, H] (packed [I, H/2] for 4-bit) */
+  const uint64_t *gate_w;      /* table: [I, H] (packed [I, H/2] for 4-bit; bytes for fp8) */
   const uint64_t *up_w;        /* table: [I, H] */
   const uint64_t *down_w;      /* table: [H, I] (packed [H, I/2]) */
   const uint64_t *gate_s;      /* table of scales: aff4 bf16 [I, H/64], mxfp4 u8 [I, H/32],
-                                  nvfp4 u8 [I, H/16]; else NULL */
+                                  nvfp4 u8 [I, H/16], fp8 float32 [I/128, H/128]; else NULL */
   const uint64_t *up_s;
-  const uint64_t *down_s;      /* aff4 bf16 [H, I/64], mxfp4 u8 [H, I/32], nvfp4 u8 [H, I/16] */
+  const uint64_t *down_s;      /* aff4 bf16 [H, I/64], mxfp4 u8 [H, I/32], nvfp4 u8 [H, I/16],
+                                  fp8 float32 [H/128, I/128] */
   const uint64_t *gate_b;      /* table of aff4 biases, bf16 like the scales; else NULL */
   const uint64_t *up_b;
   const uint64_t *down_b;

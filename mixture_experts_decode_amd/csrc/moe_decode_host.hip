@@ -115,15 +115,15 @@ int down_lanes(int chunks) {
   return 64;
 }
 
-int elems_per_chunk(int fmt) { return fmt == MOE_F32 ? 4 : fmt == MOE_BF16 ? 8 : 32; }
+int elems_per_chunk(int fmt) { return fmt == MOE_F32 ? 4 : fmt == MOE_BF16 ? 8 : fmt == MOE_FP8_B128 ? 16 : 32; }
 
 const moe::FormatKernels &kernels_for(int act, int ef) {
   typedef const moe::FormatKernels &(*getter)();
-  static const getter t[2][5] = {
+  static const getter t[2][6] = {
       {moe::kernels_f32_f32, moe::kernels_f32_bf16, moe::kernels_f32_aff4, moe::kernels_f32_mxfp4,
-       moe::kernels_f32_nvfp4},
+       moe::kernels_f32_nvfp4, moe::kernels_f32_fp8},
       {moe::kernels_bf16_f32, moe::kernels_bf16_bf16, moe::kernels_bf16_aff4, moe::kernels_bf16_mxfp4,
-       moe::kernels_bf16_nvfp4}};
+       moe::kernels_bf16_nvfp4, moe::kernels_bf16_fp8}};
   return t[act][ef]();
 }
 
@@ -189,7 +189,7 @@ moe_status check_desc(const moe_decode_desc &d) {
     return fail(MOE_EINVAL, "hidden, num_experts, top_k, inter and max_rows must be positive");
   if (d.act_fmt != MOE_F32 && d.act_fmt != MOE_BF16)
     return fail(MOE_EINVAL, "act_fmt must be MOE_F32 or MOE_BF16 (got %d)", d.act_fmt);
-  if (d.expert_fmt < MOE_F32 || d.expert_fmt > MOE_NVFP4_B16)
+  if (d.expert_fmt < MOE_F32 || d.expert_fmt > MOE_FP8_B128)
     return fail(MOE_EINVAL, "unknown expert_fmt %d", d.expert_fmt);
   if (d.routing < MOE_ROUTE_SOFTMAX || d.routing > MOE_ROUTE_SQRTSOFTPLUS)
     return fail(MOE_EINVAL, "unknown routing %d", d.routing);
@@ -216,6 +216,8 @@ moe_status check_desc(const moe_decode_desc &d) {
     return fail(MOE_EUNSUPPORTED, "mxfp4 experts need hidden and inter multiples of 32");
   if (d.expert_fmt == MOE_NVFP4_B16 && (d.hidden % 32 || d.inter % 32))
     return fail(MOE_EUNSUPPORTED, "nvfp4 experts need hidden and inter multiples of 32");
+  if (d.expert_fmt == MOE_FP8_B128 && (d.hidden % 128 || d.inter % 128))
+    return fail(MOE_EUNSUPPORTED, "fp8 experts need hidden and inter multiples of 128");
   if (d.flags & MOE_SHARED) {
     if (d.shared_inter <= 0 || d.shared_inter % 8)
       return fail(MOE_EUNSUPPORTED, "shared_inter must be a positive multiple of 8");
@@ -223,7 +225,7 @@ moe_status check_desc(const moe_decode_desc &d) {
   if (d.max_rows > moe::MAX_ROWS) {
     // The grouped path: bf16 matrix-core products over 32-wide k steps.
     if (d.act_fmt != MOE_BF16 || !kernels_for(d.act_fmt, d.expert_fmt).gate_up_grouped)
-      return fail(MOE_EUNSUPPORTED, "max_rows above %d needs bf16 activations and bf16 or 4-bit experts",
+      return fail(MOE_EUNSUPPORTED, "max_rows above %d needs bf16 activations and bf16 or 4-bit experts (not fp8)",
                   moe::MAX_ROWS);
     if (d.hidden % 32 || d.inter % 32 || ((d.flags & MOE_SHARED) && d.shared_inter % 32))
       return fail(MOE_EUNSUPPORTED, "max_rows above %d needs hidden, inter and shared_inter multiples of 32",
@@ -232,7 +234,8 @@ moe_status check_desc(const moe_decode_desc &d) {
   // Weight matrices are read through buffer resources with 32-bit byte
   // ranges: each projection (one expert's, or the shared expert's) must be
   // under 2 GiB.
-  const double ebytes = d.expert_fmt == MOE_F32 ? 4.0 : d.expert_fmt == MOE_BF16 ? 2.0 : 0.5;
+  const double ebytes = d.expert_fmt == MOE_F32 ? 4.0 : d.expert_fmt == MOE_BF16 ? 2.0
+                       : d.expert_fmt == MOE_FP8_B128 ? 1.0 : 0.5;
   const double abytes = d.act_fmt == MOE_F32 ? 4.0 : 2.0;
   const double lim = 2147483647.0;
   if ((double)d.hidden * d.inter * ebytes >= lim)
@@ -291,7 +294,7 @@ moe_status check_weights(const moe_decode_desc &d, const moe_decode_weights *w) 
     return fail(MOE_EINVAL, "gate_w, up_w and down_w tables are required");
   if (d.expert_fmt >= MOE_AFF4_G64) {
     if (!w->gate_s || !w->up_s || !w->down_s)
-      return fail(MOE_EINVAL, "4-bit experts need gate_s, up_s and down_s tables");
+      return fail(MOE_EINVAL, "4-bit and fp8 experts need gate_s, up_s and down_s tables");
   }
   if (d.expert_fmt == MOE_NVFP4_B16 && (!w->gate_scale2 || !w->up_scale2 || !w->down_scale2))
     return fail(MOE_EINVAL, "nvfp4 experts need gate_scale2, up_scale2 and down_scale2");

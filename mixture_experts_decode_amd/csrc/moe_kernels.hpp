@@ -32,12 +32,16 @@
 
 namespace moe {
 
-enum : int { F32 = 0, BF16 = 1, AFF4 = 2, MXFP4 = 3, NVFP4 = 4 };
+enum : int { F32 = 0, BF16 = 1, AFF4 = 2, MXFP4 = 3, NVFP4 = 4, FP8 = 5 };
 // x format of the down projection's input for 4-bit experts: f32, each row
 // stored sub-step-major (element i of the row at ((i % 32) / 8) * (I / 4) +
 // (i / 32) * 8 + i % 8), so that in sub-step g adjacent lanes (adjacent
 // 32-element chunks) read adjacent 32-byte blocks.
-enum : int { F32P = 5 };
+enum : int { F32P = 16 };
+// The packed 4-bit formats (two codes per byte, per-row block scales).
+constexpr bool is_fp4(int f) { return f == AFF4 || f == MXFP4 || f == NVFP4; }
+// Formats whose chunks carry dequant constants beside the codes.
+constexpr bool is_quant(int f) { return is_fp4(f) || f == FP8; }
 enum : int { ROUTE_SOFTMAX = 0, ROUTE_SIGMOID_BIAS = 1, ROUTE_SIGMOID_LOGIT = 2, ROUTE_SQRTSOFTPLUS = 3 };
 enum : unsigned { NORM_TOPK = 1u, WEIGHT_BEFORE = 2u, SHARED = 4u, SHARED_GATED = 8u, OUT_F32 = 16u, GEGLU = 32u,
                   PRE_NORM = 64u, ROUTER_NORM = 128u };
@@ -105,11 +109,14 @@ constexpr int G_COLS = 16 * G_NCT;
 constexpr int G_MU = 2;                 // k steps of 32 per staged batch (registers: two workgroups per CU)
 
 // Rows of intermediate per gate/up wave: 2 for 16-byte-per-8-or-4 element
-// formats; 4 for the 4-bit ones (their rows are 4x shorter) with one vector
+// formats; 4 for the 4-bit and fp8 ones (their rows are 4x and 2x shorter) with one vector
 // per pass.  4-bit passes of several vectors take 2 rows: the registers then
 // allow four waves per SIMD, which hide the weights' latency behind each
 // other's dequantisation better than twice the rows per wave does.
-template <int WF, int CR = 1> constexpr int gate_up_ni() { return WF >= AFF4 && CR == 1 ? 4 : 2; }
+template <int WF, int CR = 1> constexpr int gate_up_ni() { return is_quant(WF) && CR == 1 ? 4 : 2; }
+// Register budget of a gate/up wave's row loop: fp8 rows with one vector
+// take one chunk step of 8 rows (two steps spill beside the routing's state).
+template <int WF, int CR> constexpr int gate_up_vb() { return WF == FP8 && CR == 1 ? 96 : 128; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -381,6 +388,7 @@ template <> struct Fmt<BF16> { static constexpr int EPC = 8; };
 template <> struct Fmt<AFF4> { static constexpr int EPC = 32; };
 template <> struct Fmt<MXFP4> { static constexpr int EPC = 32; };
 template <> struct Fmt<NVFP4> { static constexpr int EPC = 32; };
+template <> struct Fmt<FP8> { static constexpr int EPC = 16; };
 
 // One weight row, addressed through buffer resources: the matrix's data
 // resource (and, for the 4-bit formats, its scale and bias resources) and the
@@ -391,6 +399,12 @@ template <> struct Fmt<NVFP4> { static constexpr int EPC = 32; };
 template <int WF> struct Row {
   __amdgpu_buffer_rsrc_t w, s, b;
   int off;
+};
+// fp8: one fp32 scale per 128 x 128 block; soff is the byte offset of the
+// row's block row in the [N / 128, K / 128] scale array.
+template <> struct Row<FP8> {
+  __amdgpu_buffer_rsrc_t w, s, b;
+  int off, soff;
 };
 
 // Weight chunk plus the raw bits of its dequant constants (converted where
@@ -422,6 +436,11 @@ __device__ __forceinline__ WChunk<WF> load_wchunk(const Row<WF> &r, int ch) {
   } else if constexpr (WF == NVFP4) {
     // The two E4M3 block scales of the chunk (elements 0..15, then 16..31).
     c.s = __builtin_amdgcn_raw_buffer_load_b16(r.s, vo / 8 + ch * 2, so / 8, 0);
+    c.b = 0u;
+  } else if constexpr (WF == FP8) {
+    // The fp32 scale of the chunk's 128-column block (chunks of 16 codes).
+    const int svo = UNI ? 0 : r.soff, sso = UNI ? r.soff : 0;
+    c.s = __builtin_amdgcn_raw_buffer_load_b32(r.s, svo + (ch >> 3) * 4, sso, 0);
     c.b = 0u;
   } else {
     c.s = c.b = 0u;
@@ -718,6 +737,71 @@ template <> struct XOps<NVFP4, F32> {
   static __device__ __forceinline__ float finish(const WChunk<NVFP4> &, float S, float, float acc) { return acc + S; }
 };
 
+// fp8 weights (OCP E4M3 codes, an fp32 scale per 128 x 128 block) . bf16
+// x: v_cvt_scalef32_pk_bf16_fp8 turns half of a code dword (elements 2t,
+// 2t + 1 of the dword, low byte first) into an exact bf16 pair that lines up
+// with the raw x pair; the chunk's 16 products are summed unscaled, then
+// times its block's scale.
+template <> struct XOps<FP8, BF16> {
+  static constexpr int SUB = 1, XS = 8;
+  struct X {
+    u32x4 a, b;      // x 0..7, 8..15 of the chunk
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int, int) {
+      a = ld16(xrow + (size_t)ch * 32);
+      b = ld16(xrow + (size_t)ch * 32 + 16);
+    }
+  };
+  template <bool HI> static __device__ __forceinline__ uint32_t pk(uint32_t q) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, 1.0f, HI));
+  }
+  static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
+  static __device__ __forceinline__ float start(float acc) { return acc; }
+  static __device__ __forceinline__ float step(const WChunk<FP8> &w, const X &x, int, float acc) {
+    float t = dot2(pk<false>(w.q.x), x.a.x, 0.f);
+    t = dot2(pk<true>(w.q.x), x.a.y, t);
+    t = dot2(pk<false>(w.q.y), x.a.z, t);
+    t = dot2(pk<true>(w.q.y), x.a.w, t);
+    t = dot2(pk<false>(w.q.z), x.b.x, t);
+    t = dot2(pk<true>(w.q.z), x.b.y, t);
+    t = dot2(pk<false>(w.q.w), x.b.z, t);
+    t = dot2(pk<true>(w.q.w), x.b.w, t);
+    return __builtin_fmaf(t, __uint_as_float(w.s), acc);
+  }
+  static __device__ __forceinline__ float finish(const WChunk<FP8> &, float acc, float, float) { return acc; }
+};
+
+// fp8 weights . f32 x: sub-step g is code dwords 2g, 2g + 1 (8 elements).
+template <> struct XOps<FP8, F32> {
+  static constexpr int SUB = 2, XS = 8;
+  struct X {
+    u32x4 a, b;      // x 8g .. 8g+7
+    __device__ __forceinline__ void fetch(const char *xrow, int ch, int g, int) {
+      a = ld16(xrow + (size_t)ch * 64 + 32 * g);
+      b = ld16(xrow + (size_t)ch * 64 + 32 * g + 16);
+    }
+  };
+  static __device__ __forceinline__ float xsum(const X &, float s) { return s; }
+  static __device__ __forceinline__ float start(float) { return 0.f; }
+  static __device__ __forceinline__ float step(const WChunk<FP8> &w, const X &x, int g, float S) {
+    const uint32_t q0 = code_dword(w.q, 2 * g), q1 = code_dword(w.q, 2 * g + 1);
+    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q0, 1.0f, false);
+    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q0, 1.0f, true);
+    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q1, 1.0f, false);
+    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q1, 1.0f, true);
+    S = __builtin_fmaf(v0.x, __uint_as_float(x.a.x), S);
+    S = __builtin_fmaf(v0.y, __uint_as_float(x.a.y), S);
+    S = __builtin_fmaf(v1.x, __uint_as_float(x.a.z), S);
+    S = __builtin_fmaf(v1.y, __uint_as_float(x.a.w), S);
+    S = __builtin_fmaf(v2.x, __uint_as_float(x.b.x), S);
+    S = __builtin_fmaf(v2.y, __uint_as_float(x.b.y), S);
+    S = __builtin_fmaf(v3.x, __uint_as_float(x.b.z), S);
+    return __builtin_fmaf(v3.y, __uint_as_float(x.b.w), S);
+  }
+  static __device__ __forceinline__ float finish(const WChunk<FP8> &w, float S, float, float acc) {
+    return __builtin_fmaf(S, __uint_as_float(w.s), acc);
+  }
+};
+
 // 4-bit weights . sub-step-major f32 x (the down input): the math of the
 // f32 case, sub-step g of chunk ch read at g * gs + ch * 32 bytes.
 template <> struct XOps<AFF4, F32P> : XOps<AFF4, F32> {
@@ -893,7 +977,7 @@ __device__ __forceinline__ void for_passes(int n, F &&f) {
 
 template <int WF>
 __device__ __forceinline__ int row_bytes(int K) {
-  return K * (WF == F32 ? 4 : WF == BF16 ? 2 : 1) / (WF >= AFF4 ? 2 : 1);
+  return K * (WF == F32 ? 4 : WF == BF16 ? 2 : 1) / (is_fp4(WF) ? 2 : 1);
 }
 
 // Every array a wave reads through a resource is the same for the whole
@@ -920,7 +1004,10 @@ __device__ __forceinline__ Mat<WF> make_mat(const void *w, const void *s, const 
   Mat<WF> m;
   m.rb = row_bytes<WF>(K);
   m.w = buf_rsrc(w, N * m.rb);
-  if constexpr (WF >= AFF4) {
+  if constexpr (WF == FP8) {
+    m.s = buf_rsrc(s, (N + 127) / 128 * (K / 128) * 4);
+    m.b = m.s;
+  } else if constexpr (is_fp4(WF)) {
     m.s = buf_rsrc(s, N * m.rb / (WF == NVFP4 ? 8 : 16));
     m.b = WF == AFF4 ? buf_rsrc(b, N * m.rb / 16) : m.s;
   } else {
@@ -938,6 +1025,10 @@ __device__ __forceinline__ Row<WF> make_row(const Mat<WF> &m, int n) {
   r.b = m.b;
   r.off = n * m.rb;
   if constexpr (UNI) r.off = __builtin_amdgcn_readfirstlane(r.off);
+  if constexpr (WF == FP8) {   // K = rb for fp8: (n / 128) block rows of K / 128 scales
+    r.soff = (n >> 7) * (m.rb >> 5);
+    if constexpr (UNI) r.soff = __builtin_amdgcn_readfirstlane(r.soff);
+  }
   return r;
 }
 
@@ -2240,7 +2331,7 @@ __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, cons
       xrow[c] = x + (size_t)(routed ? pair[c] / k : c0 + c) * xstride;
     }
     float acc[RG][C];
-    wave_rows_dot<EF, ACT, RG, C, WAVE>(rows, xrow, 0, H / Fmt<EF>::EPC, acc);
+    wave_rows_dot<EF, ACT, RG, C, WAVE, false, 1, gate_up_vb<EF, CMAX>()>(rows, xrow, 0, H / Fmt<EF>::EPC, acc);
     if ((threadIdx.x & 63) == 0) {
 #pragma unroll
       for (int c = 0; c < C; ++c) {
@@ -2259,7 +2350,7 @@ __device__ __forceinline__ void gate_up_rows(const Args &a, const void *gw, cons
             }
             const int i = i0 + t;
             // 4-bit experts: the row is stored sub-step-major (F32P).
-            const int pos = (EF >= AFF4 && routed) ? ((i & 31) >> 3) * (ld >> 2) + (i >> 5) * 8 + (i & 7) : i;
+            const int pos = (is_fp4(EF) && routed) ? ((i & 31) >> 3) * (ld >> 2) + (i >> 5) * 8 + (i & 7) : i;
             dst[(size_t)(off + c0 + c) * ld + pos] = act_mul(a.flags, g, v);
           }
         }
@@ -2374,7 +2465,7 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
 #pragma unroll
         for (int c = 0; c < C; ++c) xrow[c] = reinterpret_cast<const char *>(a.act + (size_t)(off + c0 + c) * I);
         float acc[RGR][C];
-        wave_rows_dot<EF, (EF >= AFF4 ? F32P : F32), RGR, C, LPR, false, 1, down_vgpr_budget<EF, CS, NW>()>(
+        wave_rows_dot<EF, (is_fp4(EF) ? F32P : F32), RGR, C, LPR, false, 1, down_vgpr_budget<EF, CS, NW>()>(
             rows, xrow, kc0, kc1, acc, I);
         if (lane % LPR == 0) {
 #pragma unroll

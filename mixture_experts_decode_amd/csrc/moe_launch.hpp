@@ -79,6 +79,8 @@ const FormatKernels &kernels_bf16_aff4();
 const FormatKernels &kernels_bf16_mxfp4();
 const FormatKernels &kernels_f32_nvfp4();
 const FormatKernels &kernels_bf16_nvfp4();
+const FormatKernels &kernels_f32_fp8();
+const FormatKernels &kernels_bf16_fp8();
 
 #ifdef MOE_KERNELS_HPP_INCLUDED
 template <int EF, int ACT, int CR, int CS, int LPR, int NW>

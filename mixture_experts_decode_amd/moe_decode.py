@@ -21,9 +21,9 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWORKSPACE",
                 4: "MOE_EHIP"}
 # moe_format
-MOE_F32, MOE_BF16, MOE_AFF4_G64, MOE_MXFP4_B32, MOE_NVFP4_B16 = range(5)
+MOE_F32, MOE_BF16, MOE_AFF4_G64, MOE_MXFP4_B32, MOE_NVFP4_B16, MOE_FP8_B128 = range(6)
 FORMATS = {"f32": MOE_F32, "bf16": MOE_BF16, "aff4": MOE_AFF4_G64, "mxfp4": MOE_MXFP4_B32,
-           "nvfp4": MOE_NVFP4_B16}
+           "nvfp4": MOE_NVFP4_B16, "fp8": MOE_FP8_B128}
 # moe_routing
 MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID_BIAS, MOE_ROUTE_SIGMOID_LOGIT, MOE_ROUTE_SQRTSOFTPLUS = range(4)
 ROUTINGS = {"softmax": MOE_ROUTE_SOFTMAX, "sigmoid_bias": MOE_ROUTE_SIGMOID_BIAS,

@@ -42,6 +42,7 @@ def _desc(**kw):
     ("max_rows", 0, md.MOE_EINVAL),
     ("act_fmt", md.MOE_AFF4_G64, md.MOE_EINVAL),
     ("expert_fmt", 7, md.MOE_EINVAL),
+    ("expert_fmt", 6, md.MOE_EINVAL),
     ("routing", 4, md.MOE_EINVAL),
     ("flags", 1 << 10, md.MOE_EINVAL),
     ("flags", md.MOE_SHARED_GATED, md.MOE_EINVAL),
@@ -53,6 +54,17 @@ def test_plan_rejects(field, value, status):
         md.moe_decode_plan(_desc(**{field: value}))
     assert ei.value.status == status
     assert md.moe_decode_last_error()
+
+
+def test_plan_rejects_fp8_shapes():
+    # Scale blocks of 128 x 128: H and I multiples of 128; the decode path only.
+    for kw in (dict(inter=768 + 64), dict(hidden=2048 + 32), dict(max_rows=33)):
+        with pytest.raises(md.MoeDecodeError) as ei:
+            md.moe_decode_plan(_desc(expert_fmt=md.MOE_FP8_B128, **kw))
+        assert ei.value.status == md.MOE_EUNSUPPORTED, kw
+    plan, ws = md.moe_decode_plan(_desc(expert_fmt=md.MOE_FP8_B128))
+    assert ws > 0
+    md.lib().moe_decode_plan_destroy(plan)
 
 
 def test_plan_rejects_4bit_shapes():
@@ -207,6 +219,19 @@ def test_nvfp4_needs_scales_and_second_level_scales():
     with pytest.raises(md.MoeDecodeError) as ei:
         md.moe_decode_plan(_desc(expert_fmt=md.MOE_NVFP4_B16, hidden=2048 + 16))
     assert ei.value.status == md.MOE_EUNSUPPORTED
+
+
+def test_fp8_needs_scale_tables():
+    plan, ws = md.moe_decode_plan(desc_of(synth.WORKLOADS["qwen35_35b_a3b_fp8"]))
+    try:
+        for field in ("gate_s", "up_s", "down_s"):
+            w = _weights_stub()
+            setattr(w, field, None)
+            with pytest.raises(md.MoeDecodeError) as ei:
+                md.moe_decode_forward(plan, w, 4096, 1, 4096, None, None, 4096 * 256, ws, 0)
+            assert ei.value.status == md.MOE_EINVAL, field
+    finally:
+        md.moe_decode_plan_destroy(plan)
 
 
 @pytest.mark.parametrize("name", ["qwen3_30b_a3b_bf16", "tiny_f32"])

@@ -190,7 +190,7 @@ def test_workload_parity_all_rows(name):
 
 
 @pytest.mark.parametrize("name", ["qwen3_30b_a3b_bf16", "qwen35_35b_a3b_mxfp4", "qwen35_35b_a3b_nvfp4",
-                                  "lfm2_8b_a1b_aff4",
+                                  "qwen35_35b_a3b_fp8", "lfm2_8b_a1b_aff4",
                                   "llama4_wbf_bf16"])
 def test_workload_fp32_output_tight(name):
     spec = synth.WORKLOADS[name]
@@ -230,6 +230,36 @@ _BASE += [(act, fmt, "sqrtsoftplus", before)
           for act in ("f32", "bf16") for fmt in ("f32", "bf16", "aff4", "mxfp4", "nvfp4")
           for before in (False, True)]
 VARIANTS = [b + (("none", "plain", "gated")[i % 3],) for i, b in enumerate(_BASE)]
+
+# fp8 experts (H and I multiples of 128: 3 x 2 scale blocks per gate/up
+# matrix, 2 x 3 per down) over every routing, with the expert activation,
+# the pre-expert norm and the router pre-norm rotating through the cases.
+_FP8 = [(act, routing, before) for act in ("f32", "bf16")
+        for routing in ("softmax", "sigmoid_bias", "sigmoid_logit", "sqrtsoftplus") for before in (False, True)]
+
+
+@pytest.mark.parametrize("act,routing,before", _FP8)
+def test_small_fp8(act, routing, before):
+    i = _FP8.index((act, routing, before))
+    shared = ("none", "plain", "gated")[i % 3]
+    spec = small(act_fmt=act, expert_fmt="fp8", hidden=384, inter=256, shared_inter=136, routing=routing,
+                 weight_before_ffn=before, norm_topk=routing != "sigmoid_logit", routed_scaling_factor=1.25,
+                 shared=shared != "none", shared_gated=shared == "gated",
+                 route_bias=(i % 2 == 0) if routing == "sqrtsoftplus" else None,
+                 activation="gelu" if i % 4 == 1 else "silu", pre_expert_norm=i % 5 == 2,
+                 router_pre_norm=i % 5 == 3)
+    layer = synth.make_layer(spec, seed=700 + i, threads=4)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    what = f"fp8 {act}/{routing}/before={before}/shared={shared}/{spec.activation}"
+    say(f"[gpu] small {what}")
+    for out_f32 in (False, True):
+        dl = DeviceLayer(layer, out_f32=out_f32)
+        for m in (1, 5, 8):
+            got, idx, w = run(dl, x, m)
+            tol = TOL[act] if not out_f32 else (TOL_OUT_F32 if act == "bf16" else TOL["f32"])
+            check(spec, got, idx, w, ref, m, tol, f"{what} m={m} f32out={out_f32}")
+            check_sort(dl, m, idx)
 
 
 @pytest.mark.parametrize("act,fmt,routing,before,shared", VARIANTS)
@@ -376,7 +406,8 @@ def test_shared_expert_shapes(hidden, shared_inter):
                                        ("mxfp4", 512), ("mxfp4", 1024), ("aff4", 1792),
                                        ("aff4", 128), ("f32", 32), ("bf16", 4096),
                                        ("aff4", 8192), ("mxfp4", 4096), ("nvfp4", 96),
-                                       ("nvfp4", 512), ("nvfp4", 4096)])
+                                       ("nvfp4", 512), ("nvfp4", 4096), ("fp8", 128), ("fp8", 512),
+                                       ("fp8", 1024), ("fp8", 4096)])
 def test_down_lane_grouping(fmt, inter):
     spec = small(expert_fmt=fmt, inter=inter, hidden=512, num_experts=8, top_k=2,
                  act_fmt="f32" if fmt == "f32" else "bf16")
@@ -494,7 +525,7 @@ def test_row_sweep_many_experts(shared_inter):
 
 
 # The 4-bit workloads with 256 experts, up to the decode path's 32 rows.
-@pytest.mark.parametrize("name", ["qwen35_35b_a3b_mxfp4", "qwen35_35b_a3b_nvfp4"])
+@pytest.mark.parametrize("name", ["qwen35_35b_a3b_mxfp4", "qwen35_35b_a3b_nvfp4", "qwen35_35b_a3b_fp8"])
 def test_workload_rows_to_32(name):
     spec = synth.WORKLOADS[name].replace(rows=(1, 8, 16, 17, 32))
     layer = synth.make_layer(spec, seed=0)
