@@ -147,6 +147,10 @@ int down_parts_of(const moe_decode_desc &d) {
   return parts;
 }
 
+// Narrow down tiles (4 waves, occupancy 4 per SIMD) resident at once on the
+// 256 compute units.
+constexpr int kNarrowResident = 4 * 256;
+
 // The variant for m rows: the pass sizes pass_variant picks, with the lane
 // grouping down_lanes wants if instantiated, else the widest available; at
 // m = 1 the narrow down when a tile's sub-units (k experts times the parts of
@@ -157,16 +161,28 @@ bool pick_variant(const moe_decode_desc &d, int m, const moe::Variant **v, moe::
   pass_variant(d, m, &cr, &cs);
   const int want = down_lanes(d.inter / elems_per_chunk(d.expert_fmt));
   const bool shared_vu = (d.flags & MOE_SHARED) && !shared_on_matrix_cores(d);
-  const int narrow = m == 1 && d.top_k * down_parts_of(d) + (shared_vu ? 1 : 0) <= 4 ? 1 : 0;
+  const bool narrow = m == 1 && d.top_k * down_parts_of(d) + (shared_vu ? 1 : 0) <= 4;
   const moe::FormatKernels &k = kernels_for(d.act_fmt, d.expert_fmt);
   const moe::Variant *best = nullptr;
+  // A narrow variant's tiles are c.narrow rows high: the lowest tiles whose
+  // grid still fits one round of resident workgroups (a second round of a
+  // few tiles would add a whole tile's latency at the end).
+  auto fits = [&](const moe::Variant &c) { return (d.hidden + c.narrow - 1) / c.narrow <= kNarrowResident; };
+  auto better = [&](const moe::Variant &c, const moe::Variant *b) {
+    if (!b) return true;
+    if ((c.lpr == want) != (b->lpr == want)) return c.lpr == want;
+    if (c.lpr != b->lpr) return c.lpr > b->lpr;
+    if (!c.narrow) return false;
+    if (fits(c) != fits(*b)) return fits(c);
+    return fits(c) ? c.narrow < b->narrow : c.narrow > b->narrow;
+  };
   for (int pass = 0; pass < 2 && !best; ++pass)
   for (int i = 0; i < k.nv; ++i) {
     const moe::Variant &c = k.v[i];
-    // First pass: the narrow flag wanted; second: any (narrow not instantiated).
-    if (c.cr != cr || c.cs != cs || (pass == 0 && c.narrow != narrow) || (pass == 1 && c.narrow)) continue;
-    if (c.lpr == want) { best = &c; break; }
-    if (!best || c.lpr > best->lpr) best = &c;
+    // First pass: a narrow variant where wanted; second: the others (no
+    // narrow one instantiated).
+    if (c.cr != cr || c.cs != cs || (pass == 0 && (c.narrow > 0) != narrow) || (pass == 1 && c.narrow)) continue;
+    if (better(c, best)) best = &c;
   }
   *gate_up = *gate_up_shd = nullptr;
   for (int i = 0; i < k.ng; ++i)

@@ -73,7 +73,7 @@ constexpr int MAX_DOWN_TILE = 2 * DOWN_RD;
 // with 16 lanes per row or 64 for the fp4 formats, run 12 waves only with a
 // smaller register budget for the row loop (below 104 they spilled); the
 // fp4 formats with 64 lanes keep 8 waves.
-template <int EF, int CS, int NW> constexpr int down_rd() { return NW ? 4 : DOWN_RD; }
+template <int EF, int CS, int NW> constexpr int down_rd() { return NW ? NW : DOWN_RD; }
 template <int EF, int CS, int LPR, int NW = 0> constexpr int down_threads() {
   return NW ? 256 : CS == 1 || CS >= 8 || EF == AFF4 || (EF >= MXFP4 && LPR == WAVE) ? DOWN_THREADS : 768;
 }

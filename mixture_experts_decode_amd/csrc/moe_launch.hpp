@@ -30,7 +30,7 @@ inline hipError_t launch_timed(K kernel, int blocks, int threads, hipStream_t st
 // per down row.
 struct Variant {
   int cr, cs, lpr;
-  int narrow;             // the m = 1 down of few sub-units per tile (tiles of 4 rows on 4 waves)
+  int narrow;             // the m = 1 down of few sub-units per tile: its tile height (rows on 4 waves); 0 if not
   int rd, down_threads;   // down rows per wave sub-unit, threads per down workgroup
   launch_fn down_blend;   // third launch
 };
@@ -114,9 +114,9 @@ constexpr launch_fn gate_up_shd_fn() {
 // Inside an inst_*.hip unit, with constexpr int EFT and ACTT in scope.
 #define MOE_V(CR, CS, LPR) { CR, CS, LPR, 0, down_rd<EFT, CS, 0>(), down_threads<EFT, CS, LPR, 0>(), \
                             &launch_down_blend_t<EFT, ACTT, CR, CS, LPR, 0> }
-// The narrow m = 1 down (f32 and bf16 experts).
-#define MOE_VN(LPR) { 1, 1, LPR, 1, down_rd<EFT, 1, 1>(), down_threads<EFT, 1, LPR, 1>(), \
-                      &launch_down_blend_t<EFT, ACTT, 1, 1, LPR, 1> }
+// The narrow m = 1 down (f32 and bf16 experts), tiles of RD rows.
+#define MOE_VN(LPR, RD) { 1, 1, LPR, RD, down_rd<EFT, 1, RD>(), down_threads<EFT, 1, LPR, RD>(), \
+                          &launch_down_blend_t<EFT, ACTT, 1, 1, LPR, RD> }
 #define MOE_G(CR, CS) { CR, CS, &launch_gate_up_t<EFT, ACTT, CR, CS, 0>, gate_up_shd_fn<EFT, ACTT, CR, CS, 1>(), \
                         gate_up_shd_fn<EFT, ACTT, CR, CS, 2>() }
 #define MOE_TABLE(NAME)                                                            \
