@@ -109,7 +109,7 @@ def layer_bytes(layer, idx, m: int) -> dict:
     sact = m * Is * 4                    # shared activations, f32
     total = distinct * (gu + dn) + router + shared_gu + shared_dn + gate_vec + x_in + out
     mf = shared_on_matrix_cores(spec)
-    parts = max(1, Is // 2048)
+    parts = max(1, min(Is // 2048, 16))   # the plan's shared-down parts
     stages = {
         # router rows (and w_g), the input rows, and the shared gate/up
         "route": router + gate_vec + x_in + shared_gu + sact,

@@ -32,8 +32,8 @@
  * m = 1..32 is the fused decode path the page describes (three launches).
  * m = 33..256 (prefill chunks, speculative-decoding verification) takes a
  * grouped path of the same steps whose expert products run on the matrix
- * cores (five launches); it needs bf16 activations, bf16, aff4, mxfp4 or
- * nvfp4 experts (not fp8) and H, I, Is multiples of 32, which moe_decode_plan checks
+ * cores (five launches); it needs bf16 activations, bf16, aff4, mxfp4,
+ * nvfp4 or fp8 experts and H, I, Is multiples of 32, which moe_decode_plan checks
  * when max_rows > 32.  Each path gives a row the same bits for every m it
  * serves; the two paths agree within the tolerance of their accumulation
  * orders.
@@ -95,7 +95,7 @@ typedef enum {
  *                  * s with one float32 s per 128 x 128 block of the matrix
  *                  ([N/128, K/128], row-major); H and I must be multiples of
  *                  128; the NaN bytes 0x7F / 0xFF are not valid.  Weight-only
- *                  dequantisation like NVFP4; m = 1..32 only. */
+ *                  dequantisation like NVFP4. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_AFF4_G64 = 2, MOE_MXFP4_B32 = 3, MOE_NVFP4_B16 = 4,
                MOE_FP8_B128 = 5 } moe_format;
 
@@ -129,7 +129,7 @@ enum {
 };
 
 typedef struct {
-  int32_t hidden;        /* H: multiple of 8 (f32/bf16), 64 (aff4), 32 (mxfp4, nvfp4) */
+  int32_t hidden;        /* H: multiple of 8 (f32/bf16), 64 (aff4), 32 (mxfp4, nvfp4), 128 (fp8) */
   int32_t num_experts;   /* E: 1..256 */
   int32_t top_k;         /* k: 1..min(E, 16) */
   int32_t inter;         /* I: routed expert intermediate size, same multiples as H */
@@ -199,7 +199,7 @@ typedef struct {
                              ((i % 32) / 8) * (I / 4) + (i / 32) * 8 + i % 8 */
   size_t shared_act;      /* float [max_rows, Is] */
   size_t shared_y;        /* float [P, max_rows, H]: shared-expert output in P parts of Is
-                             (matrix-core path; P = max(1, Is / 2048)) */
+                             (matrix-core path; P = max(1, min(Is / 2048, 16))) */
   size_t routed_y;        /* float [te, H]: routed expert outputs per pair, sorted order
                              (m > 32 only; a 4-byte placeholder when max_rows <= 32) */
   size_t normed_x;        /* act_fmt [max_rows, H]: the experts' input under

@@ -241,7 +241,7 @@ moe_status check_desc(const moe_decode_desc &d) {
   if (d.max_rows > moe::MAX_ROWS) {
     // The grouped path: bf16 matrix-core products over 32-wide k steps.
     if (d.act_fmt != MOE_BF16 || !kernels_for(d.act_fmt, d.expert_fmt).gate_up_grouped)
-      return fail(MOE_EUNSUPPORTED, "max_rows above %d needs bf16 activations and bf16 or 4-bit experts (not fp8)",
+      return fail(MOE_EUNSUPPORTED, "max_rows above %d needs bf16 activations and bf16, 4-bit or fp8 experts",
                   moe::MAX_ROWS);
     if (d.hidden % 32 || d.inter % 32 || ((d.flags & MOE_SHARED) && d.shared_inter % 32))
       return fail(MOE_EUNSUPPORTED, "max_rows above %d needs hidden, inter and shared_inter multiples of 32",
@@ -262,11 +262,14 @@ moe_status check_desc(const moe_decode_desc &d) {
 }
 
 // Parts of Is that the matrix-core shared down splits across workgroups
-// (about 2048 per part keeps every wave's stream short); 1 otherwise.
+// (about 2048 per part keeps every wave's stream short; at most
+// MAX_SD_PARTS); 1 otherwise.  (Fewer parts on the 5120-wide layer -- one
+// item per gate/up workgroup instead of 1.25 -- made its gate/up launch
+// slower at m = 1 and 8: longer items.)
 int shared_down_parts(const moe_decode_desc &d) {
   const int Is = (d.flags & MOE_SHARED) ? d.shared_inter : 0;
   const int p = Is / 2048;
-  return p < 1 ? 1 : p;
+  return p < 1 ? 1 : p > moe::MAX_SD_PARTS ? moe::MAX_SD_PARTS : p;
 }
 
 void layout_for(const moe_decode_desc &d, moe_decode_ws_layout *L) {

@@ -80,7 +80,7 @@ template <int EF, int CS, int LPR, int NW = 0> constexpr int down_threads() {
 template <int EF, int CS, int NW> constexpr int down_min_waves() { return CS == 1 && EF <= BF16 ? 4 : 1; }
 // VGPRs the down's row-by-vector loop may plan for (wave_rows_dot's budget).
 template <int EF, int CS, int NW> constexpr int down_vgpr_budget() {
-  return NW ? 100 : CS == 1 && EF <= BF16 ? 88 : CS == 4 ? 104 : 128;
+  return NW ? (NW == 4 ? 96 : 100) : CS == 1 && EF <= BF16 ? 88 : CS == 4 ? 104 : 128;
 }
 constexpr int ROUTE_THREADS = 512;      // route launch: 8 waves
 constexpr int ROUTE_WPB = ROUTE_THREADS / WAVE;
@@ -90,6 +90,7 @@ constexpr int MAX_ROWS = 32;
 constexpr int MAX_TOPK = 16;
 constexpr int MAX_EXPERTS = 256;
 constexpr int MAX_PAIRS = MAX_ROWS * MAX_TOPK;
+constexpr int MAX_SD_PARTS = 16;        // parts of Is the matrix-core shared down splits into, at most
 
 // Reserved words in the workspace (zeroed by moe_decode_workspace_init).
 // Word 0 counts the router workgroups that have stored their logits; the
@@ -1203,16 +1204,23 @@ __device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA]
 // The NVFP4 second-level scale is left to the caller.
 template <int WF> struct QMat {
   // codes [N, K/2]; scale bytes [N, K/32] (mxfp4) or [N, K/16] (nvfp4), or
-  // bf16 scales and biases [N, K/64] (aff4)
+  // bf16 scales and biases [N, K/64] (aff4); fp8: codes [N, K], fp32
+  // scales [N/128, K/128]
   __amdgpu_buffer_rsrc_t w, s, b;
 };
 
 template <int WF>
 __device__ __forceinline__ QMat<WF> make_qmat(const void *w, const void *s, const void *b, int N, int K) {
   QMat<WF> m;
-  m.w = buf_rsrc(w, N * (K / 2));
-  m.s = buf_rsrc(s, WF == AFF4 ? N * (K / 64) * 2 : N * (K / (WF == NVFP4 ? 16 : 32)));
-  m.b = WF == AFF4 ? buf_rsrc(b, N * (K / 64) * 2) : m.s;
+  if constexpr (WF == FP8) {
+    m.w = buf_rsrc(w, N * K);
+    m.s = buf_rsrc(s, (N + 127) / 128 * (K / 128) * 4);
+    m.b = m.s;
+  } else {
+    m.w = buf_rsrc(w, N * (K / 2));
+    m.s = buf_rsrc(s, WF == AFF4 ? N * (K / 64) * 2 : N * (K / (WF == NVFP4 ? 16 : 32)));
+    m.b = WF == AFF4 ? buf_rsrc(b, N * (K / 64) * 2) : m.s;
+  }
   return m;
 }
 
@@ -1481,6 +1489,13 @@ __device__ __forceinline__ void k_slice64(int K, int w, int nw, int &kb, int &ke
   ke = min((w + 1) * per, steps) * 64;
 }
 
+// The same in whole 128-element blocks (K a multiple of 128).
+__device__ __forceinline__ void k_slice128(int K, int w, int nw, int &kb, int &ke) {
+  const int steps = K / 128, per = (steps + nw - 1) / nw;
+  kb = min(w * per, steps) * 128;
+  ke = min((w + 1) * per, steps) * 128;
+}
+
 // Lane (l & ~3) + I's value, for every lane l (a broadcast within quads).
 template <int I> __device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, I * 0x55, 0xF, 0xF, false);
@@ -1600,6 +1615,106 @@ __device__ __forceinline__ void mfma_slice_aff4(const QMat<AFF4> (&A)[NA], int K
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
           acc[j][ct][i] = __builtin_fmaf(sc[i], D[j][ct][i], __builtin_fmaf(bp, X[ct][i], acc[j][ct][i]));
+      }
+    }
+  }
+}
+
+// FP8 (E4M3 codes, one fp32 scale per 128 x 128 block) on the matrix cores.
+// Every E4M3 value is exact in bf16, so the codes enter the products as
+// bf16 (v_cvt_scalef32_pk_bf16_fp8 with scale 1); a 128-element group's sum
+// starts from zero and is then added to the total times the group's scale,
+// which the 16 rows of a tile share (tiles start at multiples of 16, blocks
+// at multiples of 128, N is a multiple of 128).  A batch is half a group
+// (two k steps): lane (row l % 16, g = l / 16) takes elements
+// [16 g, 16 g + 16) of it -- 16 contiguous code bytes, one load -- the first
+// 8 as its fragment of k step 0 and the rest of k step 1 (a sum does not
+// depend on the order of k), and the input vectors are read in the same
+// order.  K, kb and ke are multiples of 128.
+// xr[ct]: the start of this lane's vector 16 ct + l % 16.
+template <int XF, int NA, int NCT>
+__device__ __forceinline__ void mfma_slice_f8(const QMat<FP8> (&A)[NA], int K, int n0, int N,
+                                              const char *const (&xr)[NCT], int kb, int ke,
+                                              f32x4 (&acc)[NA][NCT]) {
+  constexpr int XB = XF == F32 ? 4 : 2;
+  constexpr int XQ = XB;                           // 16-byte x loads per lane, batch and tile
+  const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
+  const int qoff = min(n0 + rr, N - 1) * K + g * 16;
+  const int srow = __builtin_amdgcn_readfirstlane((min(n0, N - 1) >> 7) * (K >> 7) * 4);   // the tile's scale row
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NA; ++j)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[j][ct] = zero;
+  if (kb >= ke) return;
+  u32x4 nq[NA];
+  uint32_t ns[NA];
+  u32x4 nx[NCT][XQ];
+  auto fetch = [&](int kq) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      nq[j] = __builtin_amdgcn_raw_buffer_load_b128(A[j].w, qoff + kq, 0, 0);
+      ns[j] = __builtin_amdgcn_raw_buffer_load_b32(A[j].s, 0, srow + (kq >> 7) * 4, 0);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int h = 0; h < XQ; ++h) nx[ct][h] = ld16(xr[ct] + (size_t)(kq + 16 * g) * XB + 16 * h);
+  };
+  fetch(kb);
+  f32x4 D[NA][NCT];
+  for (int k0 = kb; k0 < ke; k0 += 64) {
+    u32x4 cq[NA];
+    uint32_t cs[NA];
+    u32x4 cx[NCT][XQ];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      cq[j] = nq[j];
+      cs[j] = ns[j];
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int h = 0; h < XQ; ++h) cx[ct][h] = nx[ct][h];
+    if (k0 + 64 < ke) fetch(k0 + 64);
+    const bool first = (k0 & 127) == 0;   // the group's first half
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      u32x4 av[NA];
+#pragma unroll
+      for (int j = 0; j < NA; ++j) {
+        const uint32_t q0 = u ? cq[j].z : cq[j].x, q1 = u ? cq[j].w : cq[j].y;
+        av[j] = u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q0, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q0, 1.0f, true)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q1, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q1, 1.0f, true))};
+      }
+      const bool fresh = first && u == 0;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        if constexpr (XF == BF16) {
+          const bf16x8 bb = __builtin_bit_cast(bf16x8, cx[ct][u]);
+#pragma unroll
+          for (int j = 0; j < NA; ++j) D[j][ct] = mfma16(av[j], bb, fresh ? zero : D[j][ct]);
+        } else {
+          bf16x8 hi, lo;
+          split_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
+#pragma unroll
+          for (int j = 0; j < NA; ++j) {
+            D[j][ct] = mfma16(av[j], hi, fresh ? zero : D[j][ct]);
+            D[j][ct] = mfma16(av[j], lo, D[j][ct]);
+          }
+        }
+      }
+    }
+    if (!first) {   // the group is complete: add it, scaled
+#pragma unroll
+      for (int j = 0; j < NA; ++j) {
+        const float sc = __uint_as_float(cs[j]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[j][ct][i] = __builtin_fmaf(sc, D[j][ct][i], acc[j][ct][i]);
       }
     }
   }
@@ -1843,11 +1958,11 @@ __device__ __forceinline__ double router_tile(const Args &a, int unit, int part)
 // launches and the caller.
 constexpr int RANK_MAX_CMP = 16;        // rank selection: at most this many comparisons per thread
 
-template <int NCAND> struct RankLDS {
+template <int NCAND, int NPAIRS> struct RankLDS {
   unsigned long long key[NCAND];  // order key of candidate (r, i) at r * E + i
   double lg[NCAND];               // its logit
   int rank[NCAND];
-  double sel[MAX_PAIRS];          // logit of the expert in slot p
+  double sel[NPAIRS];             // logit of the expert in slot p
 };
 
 // One wave's scratch for the top-k of one row (row_topk).
@@ -1857,23 +1972,56 @@ struct alignas(16) TopkLDS {
   double lg[WAVE];
 };
 
-template <int NCAND, int NWV> struct RouteLDS {
+// NPAIRS: the most (row, slot) pairs the routing holds (MAX_TOPK for the
+// one-row routing of the m = 1 gate/up).
+template <int NCAND, int NWV, int NPAIRS = MAX_PAIRS> struct RouteLDS {
   static constexpr int kCand = NCAND;   // rank selection serves at most NCAND = m * E candidates
   static constexpr int kWaves = NWV;    // waves with a top-k scratch
   union {
-    RankLDS<NCAND> rk;   // rank selection
+    RankLDS<NCAND, NPAIRS> rk;   // rank selection
     TopkLDS tk[NWV];     // or per-wave selection
   };
-  int idx[MAX_PAIRS];        // selected expert of pair p = r*k + j
-  float w[MAX_PAIRS];        // routing weight of pair p (times rsf)
+  int idx[NPAIRS];           // selected expert of pair p = r*k + j
+  float w[NPAIRS];           // routing weight of pair p (times rsf)
   unsigned mask[MAX_EXPERTS];  // bit r: row r chose expert e
   int off[MAX_EXPERTS + 1];  // start of each expert's run in `sorted`
-  int sorted[MAX_PAIRS];     // pairs sorted by expert, stable
+  int sorted[NPAIRS];        // pairs sorted by expert, stable
   int active[MAX_EXPERTS];   // experts with a pair, ascending
   int slot_of[MAX_EXPERTS];  // position of an active expert in `active`
   int nact;
   uint64_t one_row[6][MAX_TOPK];  // one row, no publishing: slot u's gate, up, gate/up scales, biases
 };
+
+// One row's routing inputs held in LDS: the logits, the sqrt-softplus
+// scores and the expert biases, by expert.  The m = 1 gate/up requests them
+// before its shared-expert items and routes from here afterwards.
+struct RowStash {
+  double lg[MAX_EXPERTS];
+  double sc[MAX_EXPERTS];
+  float b[MAX_EXPERTS];
+};
+
+// Requests row 0's logits, scores (sqrt-softplus) and biases (when the
+// routing reads them) into st with loads that write LDS directly: lane l of
+// a wave writes 16 (4) bytes at the wave's LDS base + 16 l (4 l).  Waves 0, 1
+// take the logits of experts 0..127 and 128..255, waves 2, 3 the scores,
+// every wave 64 biases.  A pair of doubles ending at E reads logit column E
+// (the shared gate's) or, for the scores, 8 bytes of the array's alignment
+// padding.  256 threads.
+__device__ __forceinline__ void stash_row0(const Args &a, RowStash &st) {
+  typedef __attribute__((address_space(3))) void *lds_ptr;
+  const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63, E = a.E;
+  const int half = w & 1, e0 = half * 128 + 2 * lane;
+  if (w < 2) {
+    if (e0 < E) __builtin_amdgcn_global_load_lds(a.logits + e0, (lds_ptr)(st.lg + half * 128), 16, 0, 0);
+  } else if (a.routing == ROUTE_SQRTSOFTPLUS) {
+    if (e0 < E) __builtin_amdgcn_global_load_lds(a.scores + e0, (lds_ptr)(st.sc + half * 128), 16, 0, 0);
+  }
+  if (routing_biased(a.routing, a.ebias)) {
+    const int e = w * 64 + lane;
+    if (e < E) __builtin_amdgcn_global_load_lds(a.ebias + e, (lds_ptr)(st.b + w * 64), 4, 0, 0);
+  }
+}
 
 // Order-preserving image of a double as an unsigned 64-bit integer.
 __device__ __forceinline__ unsigned long long order_key(double v) {
@@ -1889,8 +2037,9 @@ __device__ __forceinline__ unsigned long long order_key(double v) {
 // same way (for it my_l holds that score, which the router units computed).
 // lr: the row's logits; lmax: slot 0's logit (the row's largest under softmax
 // routing).  Every lane of the wave must call it.
+template <bool STASH>
 __device__ __forceinline__ double row_weights(const Args &a, const double *lr, bool mine, double my_l,
-                                              double lmax) {
+                                              double lmax, const RowStash *st) {
   const int lane = threadIdx.x & 63, E = a.E;
   double w;
   if (a.routing == ROUTE_SOFTMAX) {
@@ -1902,7 +2051,10 @@ __device__ __forceinline__ double row_weights(const Args &a, const double *lr, b
       // Lane l adds experts l, l + 64, ... (E <= 256), all requested at once.
       double v[MAX_EXPERTS / WAVE];
 #pragma unroll
-      for (int j = 0; j < MAX_EXPERTS / WAVE; ++j) v[j] = load_coherent(lr + min(lane + j * WAVE, E - 1));
+      for (int j = 0; j < MAX_EXPERTS / WAVE; ++j) {
+        const int e = min(lane + j * WAVE, E - 1);
+        v[j] = STASH ? st->lg[e] : load_coherent(lr + e);
+      }
       double s = 0.0;
 #pragma unroll
       for (int j = 0; j < MAX_EXPERTS / WAVE; ++j)
@@ -1922,23 +2074,33 @@ __device__ __forceinline__ double row_weights(const Args &a, const double *lr, b
 // every real key) and a unique index after every real one.  Every load is issued
 // before any is used -- one memory round trip; a lane past E loads entry
 // E - 1 and discards it.
-template <bool BIASED>
+template <bool BIASED, bool STASH>
 __device__ __forceinline__ void lane_keys(const Args &a, const double *lr, unsigned long long (&key)[4],
-                                          double (&lg)[4], int (&id)[4]) {
+                                          double (&lg)[4], int (&id)[4], const RowStash *st) {
   const int lane = threadIdx.x & 63, E = a.E;
   const bool sqsp = a.routing == ROUTE_SQRTSOFTPLUS;
   const int r = (int)((lr - a.logits) / (E + 1));
   float bias[4] = {0.f, 0.f, 0.f, 0.f};
   double sc[4] = {0.0, 0.0, 0.0, 0.0};
-  if constexpr (BIASED) {
+  if constexpr (STASH) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bias[i] = a.ebias[min(4 * lane + i, E - 1)];
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int e = min(4 * lane + i, E - 1);
+      lg[i] = st->lg[e];
+      if (sqsp) sc[i] = st->sc[e];
+      if constexpr (BIASED) bias[i] = st->b[e];
+    }
+  } else {
+    if constexpr (BIASED) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lg[i] = load_coherent(lr + min(4 * lane + i, E - 1));
-  if (sqsp) {
+      for (int i = 0; i < 4; ++i) bias[i] = a.ebias[min(4 * lane + i, E - 1)];
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = load_coherent(a.scores + (size_t)r * E + min(4 * lane + i, E - 1));
+    for (int i = 0; i < 4; ++i) lg[i] = load_coherent(lr + min(4 * lane + i, E - 1));
+    if (sqsp) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = load_coherent(a.scores + (size_t)r * E + min(4 * lane + i, E - 1));
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1965,15 +2127,16 @@ __device__ __forceinline__ void lane_keys(const Args &a, const double *lr, unsig
 // among them (counted against every other candidate) is its slot.  T is
 // first sought on the high key words alone; when several lanes' best high
 // words tie at the k-th place, on the full (key, index) order.
-template <typename TL>
-__device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e, double &my_w) {
+template <bool STASH, typename TL>
+__device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e, double &my_w,
+                                         const RowStash *st) {
   const int lane = threadIdx.x & 63, k = a.K;
   const double *lr = a.logits + (size_t)r * (a.E + 1);
   unsigned long long key[4];
   double lg[4];
   int id[4];
-  if (routing_biased(a.routing, a.ebias)) lane_keys<true>(a, lr, key, lg, id);
-  else lane_keys<false>(a, lr, key, lg, id);
+  if (routing_biased(a.routing, a.ebias)) lane_keys<true, STASH>(a, lr, key, lg, id, st);
+  else lane_keys<false, STASH>(a, lr, key, lg, id, st);
   // One wave: its LDS accesses complete in program order, so no barrier.
   unsigned hk[4];
 #pragma unroll
@@ -2059,7 +2222,7 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e,
     my_e = T.id[lane];
     my_l = T.lg[lane];
   }
-  my_w = row_weights(a, lr, lane < k, my_l, T.lg[0]);
+  my_w = row_weights<STASH>(a, lr, lane < k, my_l, T.lg[0], st);
 }
 
 // Every thread of a workgroup of NT threads: routing of all m rows into L,
@@ -2073,8 +2236,10 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e,
 // row and nothing to publish, waves 1.. copy every expert's gate/up entries
 // into tab ([6][MAX_EXPERTS], LDS) meanwhile, and each active slot's entries
 // end up in L.one_row; wave 0, which selects, holds none of them.
-template <int NT, bool EARLY_TB, typename LDS>
-__device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, uint64_t (*tab)[MAX_EXPERTS]) {
+// STASH: one row, whose routing inputs are in st (LDS).
+template <int NT, bool EARLY_TB, bool STASH = false, typename LDS>
+__device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, uint64_t (*tab)[MAX_EXPERTS],
+                                          const RowStash *st = nullptr) {
   constexpr int NW = NT / WAVE;
   static_assert(NW <= LDS::kWaves, "a top-k scratch per wave");
   static_assert(NW >= 2, "one_row: the waves that select no row copy the tables");
@@ -2113,7 +2278,11 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, u
     for (int c = tid; c < nc; c += NT) {
       const int r = c / E, i = c - r * E;
       double l, kd, sc = 0.0;
-      if (biased) {   // the loads go out together
+      if constexpr (STASH) {   // one row, from LDS
+        l = st->lg[i];
+        if (sqsp) sc = st->sc[i];
+        kd = biased ? select_key_d<true>(a.routing, l, sc, (double)st->b[i]) : select_key_d<false>(a.routing, l, sc, 0.0);
+      } else if (biased) {   // the loads go out together
         const float b = a.ebias[i];
         l = load_coherent(a.logits + (size_t)r * (E + 1) + i);
         if (sqsp) sc = load_coherent(a.scores + (size_t)r * E + i);
@@ -2171,9 +2340,9 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, u
       const bool mine = lane < k;
       e = mine ? L.idx[r * k + lane] : 0;
       const double my_l = mine ? L.rk.sel[r * k + lane] : 0.0;
-      w = row_weights(a, a.logits + (size_t)r * (E + 1), mine, my_l, L.rk.sel[r * k]);
+      w = row_weights<STASH>(a, a.logits + (size_t)r * (E + 1), mine, my_l, L.rk.sel[r * k], st);
     } else {
-      row_topk(a, r, L.tk[wave], e, w);
+      row_topk<STASH>(a, r, L.tk[wave], e, w, st);
     }
     if (lane < k) {
       const float wf = (float)(w * (double)a.rsf);
@@ -2381,6 +2550,10 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   __shared__ float s_c[MAX_PAIRS];               // blend coefficient of pair p
   __shared__ int s_perm[MAX_PAIRS];              // sorted position of pair p
   __shared__ float s_gamma[MAX_ROWS];
+  // The narrow tiles' prologue (one row, few sub-units: its latency is the
+  // launch's) takes the shared output's parts through LDS.
+  constexpr bool LDS_YS = NW > 0;
+  __shared__ float ys_parts[LDS_YS ? MAX_SD_PARTS : 1][WAVE];
   const int wave = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63, tid = threadIdx.x;
   const int H = a.H, I = a.I, Is = a.Is, m = a.m, te = a.te;
   const int DQ = a.down_dq, HT = RD * DQ, h0 = tile * HT;
@@ -2390,23 +2563,6 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   const bool before = (a.flags & WEIGHT_BEFORE) != 0;
   const bool gated = (a.flags & SHARED_GATED) != 0;
 
-  // Blend operands, requested now and used after the streaming.
-  float my_c = 0.f, my_g = 0.f;
-  int my_perm = 0;
-  if (tid < te) {
-    my_c = before ? 1.0f : a.topk_w[tid];
-    my_perm = clamp_i(a.pair_to_perm[tid], 0, te - 1);
-  }
-  if (tid < m) my_g = gated ? a.row_gate[tid] : 1.0f;
-  float my_ys = 0.f;                             // this thread's shared output for the blend
-  if (sh_mfma && tid < m * HT) {
-    const int r = tid / HT, h = h0 + (tid - r * HT);
-    if (h < H)
-      for (int q = 0; q < a.sd_parts; ++q) my_ys += a.sy[((size_t)q * a.max_rows + r) * H + h];
-  }
-  // This wave's first routed record, requested together with the count (the
-  // record array always has cap entries; a stale one is never used).
-  const int slot0 = clamp_i(wave / (DQ * a.down_parts) - sh, 0, a.cap - 1);
   // The fields a down sub-unit needs, of the wave's next routed sub-unit.
   struct DownRec {
     int e, off, np;
@@ -2418,9 +2574,54 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
     d.e = r.e; d.off = r.off; d.np = r.np; d.dw = r.dw; d.ds = r.ds; d.db = r.db;
     return d;
   };
-  DownRec nxt = load_rec(slot0);
+  // This wave's first routed record (the record array always has cap
+  // entries; a stale one is never used).
+  const int slot0 = clamp_i(wave / (DQ * a.down_parts) - sh, 0, a.cap - 1);
+  float my_c = 0.f, my_g = 0.f;
+  float my_ys = 0.f;                             // wider variants: this thread's shared output for the blend
+  int my_perm = 0;                               // clamped where it is used
+  DownRec nxt;
+  int nact;
+  if constexpr (LDS_YS) {
+    // One row: every load of the prologue goes out before any is used (one
+    // memory round trip, not one per dependent use) -- the record, the
+    // published tag and count, the blend operands, and the shared output's
+    // parts, which go straight to LDS (lane t of wave 0 writes column t of
+    // part q at ys_parts[q][t]) and are added after the streaming.
+    nxt = load_rec(slot0);
+    const int cnt = a.active_count[0];
+    const unsigned pub = a.sync[SYNC_PUBLISHED];
+    if (tid < te) {
+      my_c = before ? 1.0f : a.topk_w[tid];
+      my_perm = a.pair_to_perm[tid];
+    }
+    if (tid < m) my_g = gated ? a.row_gate[tid] : 1.0f;
+    if (sh_mfma && wave == 0 && tid < HT && h0 + tid < H) {
+      typedef __attribute__((address_space(3))) void *lds_ptr;
+      for (int q = 0; q < a.sd_parts; ++q)
+        __builtin_amdgcn_global_load_lds(a.sy + (size_t)q * a.max_rows * H + h0 + tid, (lds_ptr)ys_parts[q], 4, 0, 0);
+    }
+    // The count and tag are needed before the first sub-unit; holding them
+    // here keeps the count's load from sinking behind the tag's comparison.
+    asm volatile("" ::"s"(cnt), "s"(pub));
+    nact = pub == (unsigned)a.tag ? clamp_i(cnt, 0, a.cap) : 0;
+  } else {
+    // Blend operands, requested now and used after the streaming.
+    if (tid < te) {
+      my_c = before ? 1.0f : a.topk_w[tid];
+      my_perm = a.pair_to_perm[tid];
+    }
+    if (tid < m) my_g = gated ? a.row_gate[tid] : 1.0f;
+    if (sh_mfma && tid < m * HT) {
+      const int r = tid / HT, h = h0 + (tid - r * HT);
+      if (h < H)
+        for (int q = 0; q < a.sd_parts; ++q) my_ys += a.sy[((size_t)q * a.max_rows + r) * H + h];
+    }
+    // The record, requested together with the count.
+    nxt = load_rec(slot0);
+    nact = published_count(a);
+  }
   int nxt_slot = slot0;
-  const int nact = published_count(a);
   const int units = nact + sh;
 
   // Sub-unit su = (unit, row block q, part pt of the down rows' K); the
@@ -2500,9 +2701,10 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   }
   if (tid < te) {
     s_c[tid] = my_c;
-    s_perm[tid] = my_perm;
+    s_perm[tid] = clamp_i(my_perm, 0, te - 1);
   }
   if (tid < m) s_gamma[tid] = my_g;
+  if constexpr (LDS_YS) __builtin_amdgcn_s_waitcnt(0);   // the parts' loads have written LDS
   __syncthreads();
 
   const bool out_f32 = (a.flags & OUT_F32) != 0 || ACT == F32;
@@ -2517,7 +2719,18 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
       for (int q2 = 1; q2 < NP; ++q2) y += y_lds[(q2 * te + s_perm[p]) * HT + hl];
       o = __builtin_fmaf(s_c[p], y, o);
     }
-    if (shared) o = __builtin_fmaf(s_gamma[r], sh_mfma ? my_ys : ys_lds[r * HT + hl], o);
+    if (shared) {
+      float ys;
+      if (!sh_mfma) {
+        ys = ys_lds[r * HT + hl];
+      } else if constexpr (LDS_YS) {   // the parts in order, as the other variants add them
+        ys = 0.f;
+        for (int q = 0; q < a.sd_parts; ++q) ys += ys_parts[q][hl];
+      } else {
+        ys = my_ys;
+      }
+      o = __builtin_fmaf(s_gamma[r], ys, o);
+    }
     if (out_f32)
       reinterpret_cast<float *>(a.out)[(size_t)r * H + h] = o;
     else
@@ -2746,14 +2959,21 @@ void gate_up_kernel(Args a) {
   // registers would cost the streaming variants of m > 1 occupancy.
   if (CR == 1 && a.route_in_gu) {
     // The last workgroup only publishes the routing; the others stream.
-    __shared__ RouteLDS<256, WPB> L;
+    __shared__ RouteLDS<256, WPB, MAX_TOPK> L;
+    __shared__ RowStash ST;
     const int nb = gridDim.x - 1;
     const bool publisher = (int)blockIdx.x == nb;
+    // The row's logits (scores, biases) go straight to LDS, requested before
+    // the shared-expert items: their round trip overlaps the items'
+    // streaming instead of following it, and holds no registers.
+    stash_row0(a, ST);
     int it = blockIdx.x;
     if constexpr (SHD > 0) {
       for (; !publisher && it < S; it += nb) shared_dn_item<ACT, SHD, SDMU>(a, it, GS.mf);
     }
-    route_all<THREADS, false>(a, L, publisher, GS.tab);
+    __builtin_amdgcn_s_waitcnt(0);   // the stash's loads have written LDS
+    __syncthreads();
+    route_all<THREADS, false, true>(a, L, publisher, GS.tab, &ST);
     if (publisher) return;
     const int n = L.nact * ips;
     for (; it < S + n; it += nb) {
@@ -2956,7 +3176,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void topk_sort_kernel(Args a) {
   if (r < m) {
     int e;
     double w;
-    row_topk(a, r, sm.tk[wave], e, w);
+    row_topk<false>(a, r, sm.tk[wave], e, w, nullptr);
     if (lane < k) {
       const float wf = (float)(w * (double)a.rsf);
       const int p = r * k + lane;
@@ -3119,10 +3339,11 @@ template <int EF> constexpr int gu_grouped_min_waves() { return EF == AFF4 ? 4 :
 // (a float scale per 16 codes) takes the most work per code (-7 % at 256
 // rows against four).
 template <int EF> constexpr int gu_grouped_waves() { return EF == BF16 || EF == NVFP4 ? 8 : 4; }
+// fp8 items hold half of bf16's bytes: four waves, like the 4-bit ones.
 template <int EF>
 __global__ __launch_bounds__(64 * gu_grouped_waves<EF>(), gu_grouped_min_waves<EF>()) void gate_up_grouped_kernel(Args a) {
   constexpr int NWG = gu_grouped_waves<EF>();
-  static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4 || EF == AFF4, "matrix-core experts");
+  static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4 || EF == AFF4 || EF == FP8, "matrix-core experts");
   constexpr int GT = gate_up_grouped_tiles<EF>(), KP = NWG / GT;
   constexpr int QF = EF == BF16 ? MXFP4 : EF;
   __shared__ MfmaLDS<NWG, 2, G_MU> S;
@@ -3157,6 +3378,7 @@ __global__ __launch_bounds__(64 * gu_grouped_waves<EF>(), gu_grouped_min_waves<E
   }
   int kb, ke;
   if (EF == AFF4 && quant) k_slice64(H, w / GT, KP, kb, ke);   // whole scale groups
+  else if (EF == FP8 && quant) k_slice128(H, w / GT, KP, kb, ke);
   else k_slice(H, w / GT, KP, kb, ke);
   const bool before = it.routed && (a.flags & WEIGHT_BEFORE);
   const char *x = reinterpret_cast<const char *>(a.x);
@@ -3173,11 +3395,12 @@ __global__ __launch_bounds__(64 * gu_grouped_waves<EF>(), gu_grouped_min_waves<E
     }
     f32x4 acc[2][NCT];
     if (quant) {
-      if constexpr (QF == AFF4) {   // codes straight into the operands, group sums
+      if constexpr (QF == AFF4 || QF == FP8) {   // codes straight into the operands, group sums
         const char *xr[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) xr[ct] = xv[ct] - (size_t)g4 * 16;
-        mfma_slice_aff4<BF16, 2, NCT>(Q, H, n0, N, xr, kb, ke, acc);
+        if constexpr (QF == AFF4) mfma_slice_aff4<BF16, 2, NCT>(Q, H, n0, N, xr, kb, ke, acc);
+        else mfma_slice_f8<BF16, 2, NCT>(Q, H, n0, N, xr, kb, ke, acc);
       } else {
         mfma_slice_q<QF, BF16, 2, NCT, G_MU>(Q, H, n0, N, xv, kb, ke, S.stage[w], acc);
       }
@@ -3245,8 +3468,8 @@ template <int EF, bool WIDE> constexpr int down_grouped_threads() {
 template <bool WIDE> constexpr int down_grouped_cols() { return WIDE ? 16 * G_DT : 16 * G_DTL; }
 template <int EF, bool WIDE>
 __global__ __launch_bounds__((down_grouped_threads<EF, WIDE>())) void down_grouped_kernel(Args a) {
-  static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4 || EF == AFF4, "matrix-core experts");
-  constexpr int QF = EF == BF16 ? MXFP4 : EF;                  // the 4-bit loader's format
+  static_assert(EF == BF16 || EF == MXFP4 || EF == NVFP4 || EF == AFF4 || EF == FP8, "matrix-core experts");
+  constexpr int QF = EF == BF16 ? MXFP4 : EF;                  // the quantised loader's format
   constexpr int NW = down_grouped_threads<EF, WIDE>() / WAVE;   // waves = parts of K
   constexpr int NA = WIDE ? G_DT : G_DTL;                        // tiles per wave
   // bf16 rows of at most 2048: two k steps per staged batch (longer runs per
@@ -3271,14 +3494,21 @@ __global__ __launch_bounds__((down_grouped_threads<EF, WIDE>())) void down_group
   if (quant) {
     const char *smat = reinterpret_cast<const char *>(it.ds);
     const char *bmat = reinterpret_cast<const char *>(it.db);
-    // Scale bytes per row: K/16 (nvfp4), K/32 (mxfp4), K/64 bf16 (aff4).
+    // Scale bytes per row: K/16 (nvfp4), K/32 (mxfp4), K/64 bf16 (aff4);
+    // fp8: the tile's 128-row block row of K/128 fp32 scales.
     const int sb = QF == NVFP4 ? K / 16 : QF == AFF4 ? K / 32 : K / 32;
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       const int r0 = h0 + 16 * j, nr = max(0, min(16, H - r0));
-      Q[j].w = buf_rsrc(mat + (size_t)min(r0, H) * (K / 2), nr * (K / 2));
-      Q[j].s = buf_rsrc(smat + (size_t)min(r0, H) * sb, nr * sb);
-      Q[j].b = QF == AFF4 ? buf_rsrc(bmat + (size_t)min(r0, H) * sb, nr * sb) : Q[j].s;
+      if constexpr (QF == FP8) {
+        Q[j].w = buf_rsrc(mat + (size_t)min(r0, H) * K, nr * K);
+        Q[j].s = buf_rsrc(smat + (size_t)(min(r0, H - 1) / 128) * (K / 128) * 4, nr > 0 ? (K / 128) * 4 : 0);
+        Q[j].b = Q[j].s;
+      } else {
+        Q[j].w = buf_rsrc(mat + (size_t)min(r0, H) * (K / 2), nr * (K / 2));
+        Q[j].s = buf_rsrc(smat + (size_t)min(r0, H) * sb, nr * sb);
+        Q[j].b = QF == AFF4 ? buf_rsrc(bmat + (size_t)min(r0, H) * sb, nr * sb) : Q[j].s;
+      }
     }
     if constexpr (EF == NVFP4) s2d = a.ds2[it.e];
   } else {
@@ -3290,6 +3520,7 @@ __global__ __launch_bounds__((down_grouped_threads<EF, WIDE>())) void down_group
   }
   int kb, ke;
   if (EF == AFF4 && quant) k_slice64(K, w, NW, kb, ke);   // whole scale groups
+  else if (EF == FP8 && quant) k_slice128(K, w, NW, kb, ke);
   else k_slice(K, w, NW, kb, ke);
   const char *xb = reinterpret_cast<const char *>((it.routed ? a.act : a.sact) + (size_t)it.off * K);
   float *dst = (it.routed ? a.y : a.sy) + (size_t)it.off * H;
@@ -3301,6 +3532,7 @@ __global__ __launch_bounds__((down_grouped_threads<EF, WIDE>())) void down_group
       if constexpr (NCT == 1) {
         const char *xr[1] = {xb + (size_t)(c0 + min(lane & 15, nv - 1)) * K * 4};
         if constexpr (QF == AFF4) mfma_slice_aff4<F32, NA, 1>(Q, K, 0, 16, xr, kb, ke, acc);
+        else if constexpr (QF == FP8) mfma_slice_f8<F32, NA, 1>(Q, K, 0, 16, xr, kb, ke, acc);
         else mfma_slice_qd<QF, F32, NA, 1, 2>(Q, K, 0, 16, xr, kb, ke, acc);
       }
     } else {

@@ -88,8 +88,8 @@ int main() {
             plan_case(desc(2048, 256, 8, 512, 512, rows, act, ef, routing, flags), true);
             plan_case(desc(5120, 16, 1, 8192, 8192, rows, act, ef, routing, flags), true);
           }
-          // The grouped path: bf16 activations with bf16 or 4-bit experts.
-          const bool grouped = act == MOE_BF16 && ef != MOE_F32 && ef != MOE_FP8_B128;
+          // The grouped path: bf16 activations with bf16, 4-bit or fp8 experts.
+          const bool grouped = act == MOE_BF16 && ef != MOE_F32;
           plan_case(desc(2048, 128, 8, 768, 512, 256, act, ef, routing, flags), grouped);
         }
   // Malformed and unsupported descriptors.

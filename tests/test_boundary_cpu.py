@@ -57,14 +57,16 @@ def test_plan_rejects(field, value, status):
 
 
 def test_plan_rejects_fp8_shapes():
-    # Scale blocks of 128 x 128: H and I multiples of 128; the decode path only.
-    for kw in (dict(inter=768 + 64), dict(hidden=2048 + 32), dict(max_rows=33)):
+    # Scale blocks of 128 x 128: H and I multiples of 128; above 32 rows bf16
+    # activations only (the matrix-core path).
+    for kw in (dict(inter=768 + 64), dict(hidden=2048 + 32), dict(max_rows=33, act_fmt=md.MOE_F32)):
         with pytest.raises(md.MoeDecodeError) as ei:
             md.moe_decode_plan(_desc(expert_fmt=md.MOE_FP8_B128, **kw))
         assert ei.value.status == md.MOE_EUNSUPPORTED, kw
-    plan, ws = md.moe_decode_plan(_desc(expert_fmt=md.MOE_FP8_B128))
-    assert ws > 0
-    md.lib().moe_decode_plan_destroy(plan)
+    for rows in (1, 32, 256):
+        plan, ws = md.moe_decode_plan(_desc(expert_fmt=md.MOE_FP8_B128, max_rows=rows))
+        assert ws > 0
+        md.lib().moe_decode_plan_destroy(plan)
 
 
 def test_plan_rejects_4bit_shapes():
@@ -99,9 +101,22 @@ def test_grouped_rows_limits():
     with pytest.raises(md.MoeDecodeError) as ei:
         md.moe_decode_plan(_desc(max_rows=257))
     assert ei.value.status == md.MOE_EUNSUPPORTED
-    for fmt in (md.MOE_BF16, md.MOE_MXFP4_B32, md.MOE_NVFP4_B16, md.MOE_AFF4_G64):
+    for fmt in (md.MOE_BF16, md.MOE_MXFP4_B32, md.MOE_NVFP4_B16, md.MOE_AFF4_G64, md.MOE_FP8_B128):
         plan, ws = md.moe_decode_plan(_desc(max_rows=256, expert_fmt=fmt))
         md.moe_decode_plan_destroy(plan)
+
+
+def _shared_parts(spec):
+    # About 2048 of Is per part, at most 16 parts.
+    return max(1, min(spec.shared_inter // 2048, 16))
+
+
+def test_shared_down_parts():
+    assert _shared_parts(synth.WORKLOADS["llama4_wbf_bf16"]) == 4
+    assert _shared_parts(synth.WORKLOADS["qwen35_35b_a3b_mxfp4"]) == 1
+    spec = synth.WORKLOADS["qwen3_30b_a3b_bf16"].replace(shared=True, shared_inter=65536, hidden=256)
+    assert _shared_parts(spec) == 16
+    _check_plan_and_layout(spec)
 
 
 def _check_plan_and_layout(spec):
@@ -117,8 +132,7 @@ def _check_plan_and_layout(spec):
                   (L.active_count, 4), (L.slot_info, min(te, spec.num_experts) * 128),
                   (L.act, te * spec.inter * 4),
                   (L.shared_act, spec.max_rows * (spec.shared_inter if spec.shared else 0) * 4),
-                  (L.shared_y, max(1, spec.shared_inter // 2048) * spec.max_rows
-                   * (spec.hidden if spec.shared else 0) * 4),
+                  (L.shared_y, _shared_parts(spec) * spec.max_rows * (spec.hidden if spec.shared else 0) * 4),
                   (L.routed_y, te * spec.hidden * 4 if spec.max_rows > 32 else 0),
                   (L.normed_x, spec.max_rows * spec.hidden * (4 if spec.act_fmt == "f32" else 2)
                    if spec.pre_expert_norm else 0)]

@@ -56,12 +56,14 @@ def test_grouped_small_variant(routing, before, shared):
     torch.cuda.empty_cache()
 
 
-# 4-bit experts: the dequantising matrix-core loader, short (four tiles per
-# down wave) and long (I > 2048) down rows.
+# 4-bit and fp8 experts: the dequantising matrix-core loaders, short (four
+# tiles per down wave) and long (I > 2048) down rows.
 _QV = [("mxfp4", "softmax", False, "gated", 192), ("mxfp4", "sigmoid_bias", True, "none", 4096),
        ("nvfp4", "sigmoid_logit", False, "plain", 192), ("nvfp4", "softmax", True, "gated", 4096),
        ("nvfp4", "sigmoid_bias", False, "none", 2048 + 32),
-       ("aff4", "sigmoid_bias", False, "gated", 192), ("aff4", "softmax", True, "none", 4096)]
+       ("aff4", "sigmoid_bias", False, "gated", 192), ("aff4", "softmax", True, "none", 4096),
+       ("fp8", "softmax", False, "gated", 256), ("fp8", "sigmoid_bias", True, "none", 4096),
+       ("fp8", "sigmoid_logit", False, "plain", 2048 + 128)]
 
 
 @pytest.mark.parametrize("fmt,routing,before,shared,inter", _QV)
@@ -139,6 +141,7 @@ def test_grouped_pair_extremes(E, k, inter, hidden):
                                        ("llama4_wbf_bf16", (64, 48)),
                                        ("qwen35_35b_a3b_mxfp4", (40, 33)),
                                        ("qwen35_35b_a3b_nvfp4", (40, 33)),
+                                       ("qwen35_35b_a3b_fp8", (64, 33)),
                                        ("lfm2_8b_a1b_aff4", (64, 33))])
 def test_grouped_workload(name, rows):
     spec = synth.WORKLOADS[name].replace(rows=(max(rows),))

@@ -421,6 +421,31 @@ def test_down_lane_grouping(fmt, inter):
         check(spec, got, idx, w, ref, m, TOL[spec.act_fmt], f"{fmt} I={inter} m={m}")
 
 
+def test_down_parts_are_a_plan_constant():
+    # I = 8192, k = 8: a plan for one row splits each down row into 4 parts
+    # of K, a plan for 32 rows into 2 (their partials share one LDS array).
+    # Each plan gives a row the same bits for every m it serves; the two
+    # plans agree with the oracle, and with each other within the tolerance.
+    spec = small(hidden=256, num_experts=16, top_k=8, inter=8192, rows=(32,), shared=True, shared_gated=True,
+                 shared_inter=256)
+    layer = synth.make_layer(spec, seed=91)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    outs = {}
+    for max_rows in (1, 32):
+        dl = DeviceLayer(layer, max_rows=max_rows, out_f32=True)
+        for m in sorted({1, max_rows}):
+            say(f"[gpu] down parts: plan for {max_rows} rows, m={m}")
+            got, idx, w = run(dl, x, m)
+            check(spec, got, idx, w, ref, m, TOL_OUT_F32, f"plan {max_rows} m={m}")
+            outs[(max_rows, m)] = got
+        del dl
+    assert np.array_equal(outs[(32, 1)], outs[(32, 32)][:1])
+    r = ref.out[:1]
+    assert np.max(np.abs(outs[(1, 1)] - outs[(32, 1)])) <= 2 * TOL_OUT_F32 * float(np.sqrt(np.mean(r * r)))
+    torch.cuda.empty_cache()
+
+
 def test_largest_pair_count_and_dense_limit():
     # E = 256, k = 16, m = 32: te = 512 pairs, the most the sort handles.
     spec = small(hidden=128, num_experts=256, top_k=16, inter=64, rows=(32,), w_std=0.1)
