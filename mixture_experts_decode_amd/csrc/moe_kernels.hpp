@@ -2069,11 +2069,13 @@ __device__ __forceinline__ double row_weights(const Args &a, const double *lr, b
   return w;
 }
 
-// Lane l's four candidates of a row (experts 4l..4l+3; lr: the row's
-// logits): order keys, logits (sqrt-softplus: scores) and indices; padding past E gets key 0 (below
-// every real key) and a unique index after every real one.  Every load is issued
-// before any is used -- one memory round trip; a lane past E loads entry
-// E - 1 and discards it.
+// Lane l's four candidates of a row (experts l, l + 64, l + 128, l + 192; lr:
+// the row's logits): order keys, logits (sqrt-softplus: scores) and indices;
+// padding past E gets key 0 (below every real key) and a unique index after
+// every real one.  Every load is issued before any is used -- one memory
+// round trip; a lane past E loads entry E - 1 and discards it.  Adjacent
+// lanes read adjacent entries (coalesced, and free of LDS bank conflicts
+// from the stash; 4 entries apart cost 8-way conflicts).
 template <bool BIASED, bool STASH>
 __device__ __forceinline__ void lane_keys(const Args &a, const double *lr, unsigned long long (&key)[4],
                                           double (&lg)[4], int (&id)[4], const RowStash *st) {
@@ -2085,7 +2087,7 @@ __device__ __forceinline__ void lane_keys(const Args &a, const double *lr, unsig
   if constexpr (STASH) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = min(4 * lane + i, E - 1);
+      const int e = min(lane + WAVE * i, E - 1);
       lg[i] = st->lg[e];
       if (sqsp) sc[i] = st->sc[e];
       if constexpr (BIASED) bias[i] = st->b[e];
@@ -2093,18 +2095,18 @@ __device__ __forceinline__ void lane_keys(const Args &a, const double *lr, unsig
   } else {
     if constexpr (BIASED) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bias[i] = a.ebias[min(4 * lane + i, E - 1)];
+      for (int i = 0; i < 4; ++i) bias[i] = a.ebias[min(lane + WAVE * i, E - 1)];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lg[i] = load_coherent(lr + min(4 * lane + i, E - 1));
+    for (int i = 0; i < 4; ++i) lg[i] = load_coherent(lr + min(lane + WAVE * i, E - 1));
     if (sqsp) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[i] = load_coherent(a.scores + (size_t)r * E + min(4 * lane + i, E - 1));
+      for (int i = 0; i < 4; ++i) sc[i] = load_coherent(a.scores + (size_t)r * E + min(lane + WAVE * i, E - 1));
     }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int e = 4 * lane + i;
+    const int e = lane + WAVE * i;
     const bool ok = e < E;
     if (!ok) lg[i] = 0.0;
     const double kd = select_key_d<BIASED>(a.routing, lg[i], sc[i], (double)bias[i]);
@@ -2117,7 +2119,7 @@ __device__ __forceinline__ void lane_keys(const Args &a, const double *lr, unsig
 // Top-k of row r by one wave (T: the wave's scratch).  Keys are compared as
 // order-preserving 64-bit integers, which is exactly the order of the double
 // keys; ties go to the lower index, so (key desc, index asc) is a strict
-// order.  Lane l holds experts 4l..4l+3 (E <= 256).  Slot j's expert and
+// order.  Lane l holds experts l + 64 i, i < 4 (E <= 256).  Slot j's expert and
 // weight end up in lane j.
 //
 // Selection by threshold: let T be the k-th best of the lanes' best entries.
@@ -2143,7 +2145,8 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e,
   for (int i = 0; i < 4; ++i) hk[i] = (unsigned)(key[i] >> 32);
   const unsigned myh = max(max(hk[0], hk[1]), max(hk[2], hk[3]));   // the lane's best high word
   // t = the k-th largest of the lanes' best high words, bit by bit from the
-  // top: keep a bit when at least k lanes reach the value with it set.
+  // top: keep a bit when at least k lanes reach the value with it set.  (Two
+  // bits per step, three independent ballots each, took more cycles.)
   unsigned t = 0u;
   for (int b = 31; b >= 0; --b) {
     const unsigned c = t | (1u << b);
@@ -2206,11 +2209,20 @@ __device__ __forceinline__ void row_topk(const Args &a, int r, TL &T, int &my_e,
     ic = T.id[lane];
     lc = T.lg[lane];
   }
+  // The candidates come back from LDS as broadcasts, eight requested at a
+  // time (entries past nc are in bounds and not counted), instead of a chain
+  // of readlanes.
   int rank = 0;
-  for (int j = 0; j < nc; ++j) {
-    const unsigned long long kj = readlane_u64(kc, j);
-    const int ij = __builtin_amdgcn_readlane(ic, j);
-    rank += (kj > kc || (kj == kc && ij < ic)) ? 1 : 0;
+  for (int j0 = 0; j0 < nc; j0 += 8) {
+    unsigned long long kj[8];
+    int ij[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      kj[q] = T.key[j0 + q];
+      ij[q] = T.id[j0 + q];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) rank += (j0 + q < nc && (kj[q] > kc || (kj[q] == kc && ij[q] < ic))) ? 1 : 0;
   }
   if (lane < nc && rank < k) {   // slot `rank`
     T.id[rank] = ic;
@@ -2361,9 +2373,19 @@ __device__ __forceinline__ void route_all(const Args &a, LDS &L, bool publish, u
     if (m == 1 && !publish) {
       // One row (nothing to publish): its k experts are distinct, so slot
       // u of the ascending order holds the expert with u smaller selected
-      // experts, and pair j is that slot's only pair.
+      // experts, and pair j is that slot's only pair.  The selection is read
+      // back from LDS as broadcasts (by rank: L.idx; else the wave's top-k
+      // scratch, slots 0..k-1), four at a time (past k: in bounds, not
+      // counted).
+      const int *sel = by_rank ? L.idx + r * k : L.tk[wave].id;
       int pos = 0;
-      for (int i = 0; i < k; ++i) pos += __builtin_amdgcn_readlane(e, i) < e ? 1 : 0;
+      for (int i0 = 0; i0 < k; i0 += 4) {
+        int si[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) si[q] = sel[i0 + q];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pos += (i0 + q < k && si[q] < e) ? 1 : 0;
+      }
       one_e = e;
       one_pos = pos;
       if (lane < k) {
