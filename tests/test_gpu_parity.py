@@ -491,6 +491,45 @@ def test_zero_input_and_ties(E, k, m):
         check(spec, got, idx, w, ref, m, TOL["bf16"], "tie")
 
 
+# Top-1 of many experts: the one-wave selection takes the wave maximum of the
+# lanes' best high key words.  Random rows in every routing mode, then a tie
+# on the winner (a duplicated router row: the lower index wins, through the
+# full-order threshold) and x = 0 (every key equal: expert 0).
+@pytest.mark.parametrize("routing", ["softmax", "sigmoid_bias", "sigmoid_logit", "sqrtsoftplus"])
+def test_top1_many_experts(routing):
+    spec = small(num_experts=256, top_k=1, routing=routing, norm_topk=routing != "sigmoid_logit",
+                 weight_before_ffn=routing == "sigmoid_logit", rows=(1, 3, 8))
+    layer = synth.make_layer(spec, seed=23)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    dl = DeviceLayer(layer)
+    for m in (1, 3, 8):
+        say(f"[gpu] top-1 of 256 {routing} m={m}")
+        got, idx, w = run(dl, x, m)
+        check(spec, got, idx, w, ref, m, TOL["bf16"], f"top-1 {routing} m={m}")
+    win = int(ref.idx[0, 0])
+    if win != 0:
+        layer.router[0] = layer.router[win]
+        if layer.expert_bias is not None:
+            layer.expert_bias[0] = layer.expert_bias[win]
+        ref = oracle.forward(layer, x)
+        assert ref.idx[0, 0] == 0
+        dl = DeviceLayer(layer)
+        for m in (1, 3):
+            say(f"[gpu] top-1 duplicated winner {routing} m={m}")
+            got, idx, w = run(dl, x, m)
+            check(spec, got, idx, w, ref, m, TOL["bf16"], f"top-1 tie {routing} m={m}")
+    z = np.zeros((2, spec.hidden), np.uint16)
+    if layer.expert_bias is not None:
+        layer.expert_bias[:] = np.float32(0.25)
+    dl = DeviceLayer(layer)
+    for m in (1, 2):
+        say(f"[gpu] top-1 x=0 {routing} m={m}")
+        got, idx, w = run(dl, z, m)
+        assert np.array_equal(idx, np.zeros((m, 1), np.int32)), idx
+        assert np.array_equal(idx, oracle.forward(layer, z).idx[:m])
+
+
 # Ties in the two sigmoid modes, at x = 0 (every logit 0).  (E, k, m) as
 # above, plus m = 1, where every gate/up workgroup selects.
 @pytest.mark.parametrize("E,k,m", [(8, 3, 1), (8, 3, 2), (256, 8, 1), (256, 8, 8)])
