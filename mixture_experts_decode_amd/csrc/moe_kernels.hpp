@@ -1196,6 +1196,88 @@ __device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA]
   mfma_slice_v<XF, NA, NCT, MU>(A, rb, n0, N, xv, kb, ke, stage, acc);
 }
 
+// One vector's product with 16 bf16 rows on the matrix cores (the shared
+// down at m = 1), with the weights and the f32 input brought into LDS by the
+// loads themselves (buffer loads that write LDS).  The wave owns DMA_NB slots
+// of one batch each -- 16 rows x 64 k of weights (2 KB) and the input's 64
+// values (256 B) -- and keeps DMA_NB - 1 batches in flight while it consumes
+// one: twice the bytes in flight of mfma_slice_v's register prefetch, and no
+// register holds a weight in flight.  Chunk c (16 bytes) of row r sits at
+// chunk r * 8 + (c ^ (r >> 1)) of the slot, so the operand reads of 16 rows at
+// one chunk fall in 16 distinct 16-byte bank groups.  The MFMA sequence --
+// k steps in order, the input's high then low bf16 part -- is mfma_slice_v's
+// with every column reading the one vector, so the sums are bitwise the same.
+constexpr int DMA_NB = 3;
+constexpr int DMA_SLOT = 2048 + 256;
+struct SharedDnRing {
+  float part[WPB][4][WAVE];
+  alignas(16) char slot[WPB][DMA_NB * DMA_SLOT];
+};
+
+__device__ __forceinline__ void mfma_slice_dma(__amdgpu_buffer_rsrc_t A, int rb, int n0, int N,
+                                               __amdgpu_buffer_rsrc_t X, int kb, int ke, char *ring,
+                                               f32x4 &acc) {
+  typedef __attribute__((address_space(3))) void *lds_ptr;
+  const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
+  acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (kb >= ke) return;
+  const int nb = (ke - kb + 63) / 64;
+  // Lane l brings chunk positions l and 64 + l of a batch.
+  int voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = 64 * i + l, r = p >> 3, c = (p & 7) ^ (r >> 1);
+    voff[i] = min(n0 + r, N - 1) * rb + c * 16;
+  }
+  // Three loads per batch: two of weights, one of input (lanes 0..15).
+  auto issue = [&](int b) {
+    char *sl = ring + (b % DMA_NB) * DMA_SLOT;
+    const int kq = kb + 64 * b;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(A, (lds_ptr)(sl + 1024 * i), 16, voff[i] + kq * 2, 0, 0, BUF_NT);
+    if (l < 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(X, (lds_ptr)(sl + 2048), 16, kq * 4 + l * 16, 0, 0, 0);
+  };
+  for (int b = 0; b < DMA_NB - 1 && b < nb; ++b) issue(b);
+  for (int b = 0; b < nb; ++b) {
+    if (b + DMA_NB - 1 < nb) issue(b + DMA_NB - 1);
+    // Batch b's loads are done once no more than the later batches' remain
+    // outstanding (vector memory loads complete in order for the count).
+    const int later = min(nb - 1 - b, DMA_NB - 1);
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 6);
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | 3);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+    // The slot is read with LDS loads written out here, each batch's three
+    // waited for in the same statement: the compiler would otherwise wait for
+    // every load into LDS in flight (it cannot tell the slots apart) before
+    // any LDS read, which would leave one batch in flight.
+    const unsigned sl = (unsigned)(uintptr_t)(lds_ptr)(ring + (b % DMA_NB) * DMA_SLOT);
+    const int k0 = kb + 64 * b;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (k0 + 32 * u < ke) {
+        const int c = 4 * u + g;
+        const unsigned pa = sl + (rr * 8 + (c ^ (rr >> 1))) * 16, px = sl + 2048 + (32 * u + 8 * g) * 4;
+        u32x4 av, b0, b1;
+        asm volatile(
+            "ds_read_b128 %0, %3\n\t"
+            "ds_read_b128 %1, %4\n\t"
+            "ds_read_b128 %2, %4 offset:16\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=v"(av), "=v"(b0), "=v"(b1)
+            : "v"(pa), "v"(px)
+            : "memory");
+        bf16x8 hi, lo;
+        split_bf16(b0, b1, hi, lo);
+        acc = mfma16(av, hi, acc);
+        acc = mfma16(av, lo, acc);
+      }
+    }
+    asm volatile("" ::: "memory");   // the slot's reads precede its next load
+  }
+}
+
 // 4-bit weights (MXFP4, NVFP4) on the matrix cores.  The loader brings a
 // batch of two k steps of 16 rows as codes -- 8 bytes (16 codes) per lane --
 // with their block scales, dequantises them to bf16 and stages them in the
@@ -2825,6 +2907,30 @@ __device__ __forceinline__ void shared_dn_mfma(const Args &a, int item, MfmaLDS<
   __syncthreads();   // S is reused by the workgroup's next item
 }
 
+// The same item at m = 1 through mfma_slice_dma (one vector, so one column
+// tile); the waves' partials are added in the same order.
+__device__ __forceinline__ void shared_dn_ring(const Args &a, int item, SharedDnRing &S) {
+  const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int H = a.H, Is = a.Is, P = a.sd_parts;
+  const int tile = item / P, q = item - tile * P, n0 = tile * 16;
+  const __amdgpu_buffer_rsrc_t A = buf_rsrc(a.sdw, H * Is * 2);
+  const __amdgpu_buffer_rsrc_t X = buf_rsrc(a.sact, Is * 4);
+  int pb, pe, kb, ke;
+  k_slice(Is, q, P, pb, pe);
+  k_slice(pe - pb, w, WPB, kb, ke);
+  f32x4 acc;
+  mfma_slice_dma(A, Is * 2, n0, H, X, pb + kb, pb + ke, S.slot[w], acc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) S.part[w][i][lane] = acc[i];
+  __syncthreads();
+  const int i = w;   // WPB == 4: wave w finishes element i = w
+  float y = 0.f;
+  for (int p = 0; p < WPB; ++p) y += S.part[p][i][lane];
+  const int row = n0 + (lane >> 4) * 4 + i, v = lane & 15;
+  if (row < H && v < 1) a.sy[(size_t)q * a.max_rows * H + row] = y;
+  __syncthreads();   // S is reused by the workgroup's next item
+}
+
 template <int ACT, int NCT, int MU>
 __device__ __forceinline__ void shared_dn_item(const Args &a, int item, MfmaLDS<WPB, 1, MU> &S) {
   if constexpr (ACT == BF16 && NCT > 0) shared_dn_mfma<NCT, MU>(a, item, S);   // the matrix-core path
@@ -2847,6 +2953,17 @@ template <bool MF, int MU> union GateUpLDS {
 };
 template <int MU> union GateUpLDS<false, MU> {
   uint64_t tab[6][MAX_EXPERTS];
+};
+
+// One row with bf16 experts: the shared down items' LDS ring -- their items
+// come first -- then the routing's table entries and arrays, which the
+// routed items read after it.
+union GateUpRingLDS {
+  SharedDnRing ring;
+  struct {
+    uint64_t tab[6][MAX_EXPERTS];
+    RouteLDS<256, WPB, MAX_TOPK> L;
+  } rt;
 };
 
 // Launch 1: router workgroups (ROUTE_UNITS_PER_WG units, RSPLIT waves each),
@@ -2972,57 +3089,80 @@ void gate_up_kernel(Args a) {
   const int ips = a.gu_items_per_slot;
   const int wave = uniform_i(threadIdx.x >> 6);
   constexpr int SDMU = shared_dn_mu<EF, CR>();
-  __shared__ GateUpLDS<(SHD > 0), SDMU> GS;
+  // One vector per pass (CR == 1) is m = 1: the host picks these variants
+  // for one row only.
+  // At m = 1 the bf16-expert variants stream the shared down items through
+  // the LDS ring (the same sums).  (With both paths in one kernel the 4-bit
+  // variants spilled; on the 512-wide shared expert of the 4-bit layers,
+  // whose waves take two batches each, the ring was 0.4 us slower.)
+  constexpr bool RING = CR == 1 && ACT == BF16 && EF == BF16 && SHD == 1;
+  __shared__ std::conditional_t<RING, GateUpRingLDS, GateUpLDS<(SHD > 0), SDMU>> G;
+  auto shared_item = [&](int it) {
+    if constexpr (RING) shared_dn_ring(a, it, G.ring);
+    else if constexpr (SHD > 0) shared_dn_item<ACT, SHD, SDMU>(a, it, G.mf);
+  };
   // The route launch is over: its ticket word starts the next forward at 0,
   // whatever this forward found in it.
   if (blockIdx.x == 0 && threadIdx.x == 0) a.sync[SYNC_ROUTER_TICKET] = 0u;
   const int S = SHD > 0 ? a.n_shared_dn : 0;   // shared down items
   // Only the one-vector variants (m = 1) carry the routing: the top-k's
   // registers would cost the streaming variants of m > 1 occupancy.
-  if (CR == 1 && a.route_in_gu) {
-    // The last workgroup only publishes the routing; the others stream.
-    __shared__ RouteLDS<256, WPB, MAX_TOPK> L;
-    __shared__ RowStash ST;
-    const int nb = gridDim.x - 1;
-    const bool publisher = (int)blockIdx.x == nb;
-    // The row's logits (scores, biases) go straight to LDS, requested before
-    // the shared-expert items: their round trip overlaps the items'
-    // streaming instead of following it, and holds no registers.
-    stash_row0(a, ST);
-    int it = blockIdx.x;
-    if constexpr (SHD > 0) {
-      for (; !publisher && it < S; it += nb) shared_dn_item<ACT, SHD, SDMU>(a, it, GS.mf);
-    }
-    __builtin_amdgcn_s_waitcnt(0);   // the stash's loads have written LDS
-    __syncthreads();
-    route_all<THREADS, false, true>(a, L, publisher, GS.tab, &ST);
-    if (publisher) return;
-    const int n = L.nact * ips;
-    for (; it < S + n; it += nb) {
-      const int ri = it - S;
-      const int s = ri / ips, b = ri - s * ips;
-      const int e = uniform_i(clamp_i(L.active[s], 0, a.E - 1));
-      const int off = uniform_i(L.off[e]), np = uniform_i(L.off[e + 1]) - off;
-      const int i0 = (b * WPB + wave) * NI;
-      if (i0 < a.I) {
-        const void *p[6];
-        if (a.m == 1) {   // entries requested with the logits
-#pragma unroll
-          for (int j = 0; j < 6; ++j) p[j] = reinterpret_cast<const void *>(uniform_u64(L.one_row[j][s]));
-        } else {
-          p[0] = tbl(a.gw, e); p[1] = tbl(a.uw, e); p[2] = tbl(a.gs, e);
-          p[3] = tbl(a.us, e); p[4] = tbl(a.gb, e); p[5] = tbl(a.ub, e);
-        }
-        float s2g = 1.0f, s2u = 1.0f;
-        if constexpr (EF == NVFP4) {
-          s2g = a.gs2[e];
-          s2u = a.us2[e];
-        }
-        gate_up_rows<EF, ACT, CR, NI>(a, p[0], p[1], p[2], p[3], p[4], p[5], a.I, i0, off, np,
-                                      L.sorted + off, L.w, a.act, a.I, s2g, s2u);
+  if constexpr (CR == 1) {
+    if (a.route_in_gu) {
+      // The last workgroup only publishes the routing; the others stream.
+      RouteLDS<256, WPB, MAX_TOPK> *Lp;
+      uint64_t (*tab)[MAX_EXPERTS];
+      if constexpr (RING) {
+        Lp = &G.rt.L;
+        tab = G.rt.tab;
+      } else {
+        __shared__ RouteLDS<256, WPB, MAX_TOPK> L0;
+        Lp = &L0;
+        tab = G.tab;
       }
+      RouteLDS<256, WPB, MAX_TOPK> &L = *Lp;
+      __shared__ RowStash ST;
+      const int nb = gridDim.x - 1;
+      const bool publisher = (int)blockIdx.x == nb;
+      // The row's logits (scores, biases) go straight to LDS, requested
+      // before the shared-expert items: their round trip overlaps the items'
+      // streaming instead of following it, and holds no registers.
+      stash_row0(a, ST);
+      int it = blockIdx.x;
+      if constexpr (SHD > 0) {
+        for (; !publisher && it < S; it += nb) shared_item(it);
+      }
+      __builtin_amdgcn_s_waitcnt(0);   // the stash's loads have written LDS
+      __syncthreads();
+      route_all<THREADS, false, true>(a, L, publisher, tab, &ST);
+      if (publisher) return;
+      const int n = L.nact * ips;
+      for (; it < S + n; it += nb) {
+        const int ri = it - S;
+        const int s = ri / ips, b = ri - s * ips;
+        const int e = uniform_i(clamp_i(L.active[s], 0, a.E - 1));
+        const int off = uniform_i(L.off[e]), np = uniform_i(L.off[e + 1]) - off;
+        const int i0 = (b * WPB + wave) * NI;
+        if (i0 < a.I) {
+          const void *p[6];
+          if (a.m == 1) {   // entries requested with the logits
+#pragma unroll
+            for (int j = 0; j < 6; ++j) p[j] = reinterpret_cast<const void *>(uniform_u64(L.one_row[j][s]));
+          } else {
+            p[0] = tbl(a.gw, e); p[1] = tbl(a.uw, e); p[2] = tbl(a.gs, e);
+            p[3] = tbl(a.us, e); p[4] = tbl(a.gb, e); p[5] = tbl(a.ub, e);
+          }
+          float s2g = 1.0f, s2u = 1.0f;
+          if constexpr (EF == NVFP4) {
+            s2g = a.gs2[e];
+            s2u = a.us2[e];
+          }
+          gate_up_rows<EF, ACT, CR, NI>(a, p[0], p[1], p[2], p[3], p[4], p[5], a.I, i0, off, np,
+                                        L.sorted + off, L.w, a.act, a.I, s2g, s2u);
+        }
+      }
+      return;
     }
-    return;
   }
   // With the routing published the list runs routed items first (the larger
   // ones: shared items last balance the workgroups' ends; shared items first
@@ -3035,7 +3175,7 @@ void gate_up_kernel(Args a) {
   for (int ri = blockIdx.x; ri < n + S; ri += gridDim.x) {
     if constexpr (SHD > 0) {
       if (ri >= n) {
-        shared_dn_item<ACT, SHD, SDMU>(a, ri - n, GS.mf);
+        shared_item(ri - n);
         continue;
       }
     }

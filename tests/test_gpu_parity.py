@@ -379,9 +379,11 @@ def test_every_row_count_and_pass_variant():
 
 
 # The matrix-core shared expert at several H and Is: short and long Is (a
-# long one splits the down over parts of Is), one and two column tiles
-# (m <= 16, m > 16).
-@pytest.mark.parametrize("hidden,shared_inter", [(1024, 512), (512, 1024), (256, 96), (512, 4096)])
+# long one splits the down over parts of Is; at m = 1 a wave's share of at
+# least 256 goes through the LDS ring, 1056 with a partial last batch), one
+# and two column tiles (m <= 16, m > 16).
+@pytest.mark.parametrize("hidden,shared_inter", [(1024, 512), (512, 1024), (256, 96), (512, 4096),
+                                                 (256, 1056)])
 def test_shared_expert_shapes(hidden, shared_inter):
     spec = small(hidden=hidden, num_experts=8, top_k=2, inter=64, shared=True, shared_gated=True,
                  shared_inter=shared_inter, rows=(32,))
