@@ -87,6 +87,7 @@ constexpr int ROUTE_WPB = ROUTE_THREADS / WAVE;
 constexpr int RSPLIT = 4;               // waves per router row (its H is split in 4)
 constexpr int ROUTE_UNITS_PER_WG = ROUTE_WPB / RSPLIT;
 constexpr int MAX_ROWS = 32;
+constexpr int CU_COUNT = 256;            // compute units of an MI355X (dispatch-slot heuristics)
 constexpr int MAX_TOPK = 16;
 constexpr int MAX_EXPERTS = 256;
 constexpr int MAX_PAIRS = MAX_ROWS * MAX_TOPK;
@@ -2955,6 +2956,16 @@ template <int MU> union GateUpLDS<false, MU> {
   uint64_t tab[6][MAX_EXPERTS];
 };
 
+// The routing of one row as the routed items read it: per active slot the
+// expert, its pair range and its gate/up table entries, and the pairs and
+// weights in sorted order.
+struct OneRowRouting {
+  int nact;
+  int e[MAX_TOPK], off[MAX_TOPK], np[MAX_TOPK], sorted[MAX_TOPK];
+  float w[MAX_TOPK];
+  uint64_t p[6][MAX_TOPK];
+};
+
 // One row with bf16 experts: the shared down items' LDS ring -- their items
 // come first -- then the routing's table entries and arrays, which the
 // routed items read after it.
@@ -3129,13 +3140,57 @@ void gate_up_kernel(Args a) {
       // streaming instead of following it, and holds no registers.
       stash_row0(a, ST);
       int it = blockIdx.x;
+      // With the ring, the workgroups dispatched second on each CU route
+      // before their shared item, the others after: the routing (a few us
+      // with no weights streaming) then overlaps the other workgroups of the
+      // CU streaming, instead of three of the four routing at once.  Their
+      // routing result is copied out of the LDS the ring reuses.
+      const bool route_first = RING && (int)blockIdx.x / CU_COUNT == 1;
       if constexpr (SHD > 0) {
-        for (; !publisher && it < S; it += nb) shared_item(it);
+        if (!route_first)
+          for (; !publisher && it < S; it += nb) shared_item(it);
       }
       __builtin_amdgcn_s_waitcnt(0);   // the stash's loads have written LDS
       __syncthreads();
       route_all<THREADS, false, true>(a, L, publisher, tab, &ST);
       if (publisher) return;
+      if constexpr (RING) {
+        __shared__ OneRowRouting R1;
+        const int tid = threadIdx.x;
+        if (tid == 0) R1.nact = L.nact;
+        if (tid < a.K) {
+          R1.sorted[tid] = L.sorted[tid];
+          R1.w[tid] = L.w[tid];
+        }
+        if (tid < L.nact) {
+          const int e = clamp_i(L.active[tid], 0, a.E - 1);
+          R1.e[tid] = e;
+          R1.off[tid] = L.off[e];
+          R1.np[tid] = L.off[e + 1] - L.off[e];
+#pragma unroll
+          for (int j = 0; j < 6; ++j) R1.p[j][tid] = L.one_row[j][tid];
+        }
+        __syncthreads();
+        if constexpr (SHD > 0) {
+          if (route_first)
+            for (; it < S; it += nb) shared_item(it);
+        }
+        const int n = R1.nact * ips;
+        for (; it < S + n; it += nb) {
+          const int ri = it - S;
+          const int s = ri / ips, b = ri - s * ips;
+          const int off = uniform_i(R1.off[s]), np = uniform_i(R1.np[s]);
+          const int i0 = (b * WPB + wave) * NI;
+          if (i0 < a.I) {
+            const void *p[6];
+#pragma unroll
+            for (int j = 0; j < 6; ++j) p[j] = reinterpret_cast<const void *>(uniform_u64(R1.p[j][s]));
+            gate_up_rows<EF, ACT, CR, NI>(a, p[0], p[1], p[2], p[3], p[4], p[5], a.I, i0, off, np,
+                                          R1.sorted + off, R1.w, a.act, a.I);
+          }
+        }
+        return;
+      }
       const int n = L.nact * ips;
       for (; it < S + n; it += nb) {
         const int ri = it - S;
