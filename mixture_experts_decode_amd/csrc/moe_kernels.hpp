@@ -117,8 +117,10 @@ constexpr int G_MU = 2;                 // k steps of 32 per staged batch (regis
 // other's dequantisation better than twice the rows per wave does.
 template <int WF, int CR = 1> constexpr int gate_up_ni() { return is_quant(WF) && CR == 1 ? 4 : 2; }
 // Register budget of a gate/up wave's row loop: fp8 rows with one vector
-// take one chunk step of 8 rows (two steps spill beside the routing's state).
-template <int WF, int CR> constexpr int gate_up_vb() { return WF == FP8 && CR == 1 ? 96 : 128; }
+// take one chunk step of 8 rows (two steps spill beside the routing's state);
+// with several vectors, 64 registers leave room for four or five waves per
+// SIMD instead of two or three (the fp8 layer: -6 to -12 % at m = 2-16).
+template <int WF, int CR> constexpr int gate_up_vb() { return WF == FP8 ? (CR == 1 ? 96 : 64) : 128; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
