@@ -671,7 +671,8 @@ def test_measurement_utilities():
 
 
 @pytest.mark.parametrize("name,rows", [("qwen3_30b_a3b_bf16", (1,)), ("qwen35_35b_a3b_mxfp4", (1,)),
-                                       ("lfm2_8b_a1b_aff4", (1,)), ("tiny_f32", (1,))])
+                                       ("lfm2_8b_a1b_aff4", (1,)), ("tiny_f32", (1,)),
+                                       ("llama4_wbf_bf16", (1,))])
 def test_routing_placements_agree(name, rows, monkeypatch):
     """For one row, the routing computed by every gate/up workgroup and the
     routing computed once by the last router workgroup (the placement of
@@ -697,3 +698,4 @@ def test_routing_placements_agree(name, rows, monkeypatch):
     for m in rows:
         for a, b in zip(res[("gate_up", m)], res[("once", m)]):
             assert np.array_equal(a, b), f"placements differ at m={m}"
+
