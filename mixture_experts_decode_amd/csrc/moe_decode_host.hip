@@ -73,6 +73,9 @@ const char *stage_name(int, int i) { return kSplitStages[i]; }
 
 // Workgroups of the gate/up launch: a few per CU; each loops over items.
 constexpr int kGateUpMaxBlocks = 1024;
+// Compute units of MI355X, and the router units of a 16-wave route workgroup.
+constexpr int kCUs = 256;
+constexpr int kRouterUnitsWide = moe::ROUTE_THREADS_WIDE / moe::WAVE / moe::RSPLIT;
 
 bool fused_requested() {
   const char *v = getenv("MOE_DECODE_VARIANT");
@@ -133,6 +136,7 @@ const moe::FormatKernels &kernels_for(int act, int ef) {
 bool shared_on_matrix_cores(const moe_decode_desc &d) {
   return (d.flags & MOE_SHARED) && d.act_fmt == MOE_BF16 && d.hidden % 32 == 0 && d.shared_inter % 32 == 0;
 }
+
 
 // Parts of K each routed down row is split into: up to 4 for long rows (at
 // least 2048 elements each), so that one active expert still fills a tile's
@@ -492,7 +496,6 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   const int nrb = (m + 7) / 8;                               // input-row blocks per router row
   a.route_in_gu = plan->route_in_gu[m] ? 1 : 0;
   a.n_router = router_rows(d) * nrb;   // router units
-  a.n_router_wg = (a.n_router + moe::ROUTE_UNITS_PER_WG - 1) / moe::ROUTE_UNITS_PER_WG;
   // The shared expert runs on the matrix cores (16-row tiles, gate/up in the
   // route launch, down in the gate/up launch) for bf16 activations when H and
   // Is are multiples of 32; on the vector units otherwise.
@@ -507,6 +510,18 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
     a.n_shared_gu = shared ? ((a.Is + ni_s - 1) / ni_s + moe::ROUTE_WPB - 1) / moe::ROUTE_WPB : 0;
     a.n_shared_dn = 0;
   }
+  // Above 8 rows the route launch takes 16-wave workgroups (the routing's
+  // top-k runs 16 rows at once) when they fit one round, one per CU: bf16
+  // activations, and the shared expert, if any, on the matrix cores (two
+  // of its 8-wave items per workgroup, the same sums).  Router units and
+  // items compute the same values either way.
+  const int router_wg_wide = (a.n_router + kRouterUnitsWide - 1) / kRouterUnitsWide;
+  const int shared_wg_wide = a.shared_mfma ? (a.n_shared_gu + 1) / 2 : 0;
+  const bool route_wide = m > 8 && d.act_fmt == MOE_BF16 && (a.shared_mfma || !shared) &&
+                          router_wg_wide + shared_wg_wide <= kCUs;
+  a.n_router_wg = route_wide ? router_wg_wide
+                             : (a.n_router + moe::ROUTE_UNITS_PER_WG - 1) / moe::ROUTE_UNITS_PER_WG;
+  const int route_blocks = a.n_router_wg + (route_wide ? shared_wg_wide : a.n_shared_gu);
   a.gu_items_per_slot = ((d.inter + ni_r - 1) / ni_r + wpb - 1) / wpb;
   a.n_routed_gu = a.cap * a.gu_items_per_slot;
   a.down_parts = down_parts_of(d);
@@ -538,7 +553,7 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   // matrix-core one the narrowest variant runs (fewest registers, so two
   // workgroups share a CU).
   const int route_cs = a.shared_mfma ? 1 : cs;
-  if ((e = moe::launch_route(d.act_fmt, route_cs, a, a.n_router_wg + a.n_shared_gu, s, route_start, ev(1))) != hipSuccess)
+  if ((e = moe::launch_route(d.act_fmt, route_cs, a, route_blocks, s, route_start, ev(1), route_wide)) != hipSuccess)
     return fail(MOE_EHIP, "route launch: %s", hipGetErrorString(e));
   // gate_up: a grid-stride launch over the active slots' items.
   // With the routing computed in gate/up, one more workgroup publishes it.

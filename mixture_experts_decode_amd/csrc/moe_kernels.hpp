@@ -83,6 +83,7 @@ template <int EF, int CS, int NW> constexpr int down_vgpr_budget() {
   return NW ? (NW == 4 ? 96 : 100) : CS == 1 && EF <= BF16 ? 88 : CS == 4 ? 104 : 128;
 }
 constexpr int ROUTE_THREADS = 512;      // route launch: 8 waves
+constexpr int ROUTE_THREADS_WIDE = 1024; // route launch of a narrow matrix-core shared expert: 16 waves
 constexpr int ROUTE_WPB = ROUTE_THREADS / WAVE;
 constexpr int RSPLIT = 4;               // waves per router row (its H is split in 4)
 constexpr int ROUTE_UNITS_PER_WG = ROUTE_WPB / RSPLIT;
@@ -2845,32 +2846,36 @@ __device__ __forceinline__ void down_item(const Args &a, int tile) {
   }
 }
 
-// Shared expert gate/up on the matrix cores: item = 16 intermediate rows;
-// waves 0..3 take the gate rows and waves 4..7 the up rows, each a quarter
-// of H; writes silu(g) * u to sact.
-template <int NCT>
-__device__ __forceinline__ void shared_gu_mfma(const Args &a, int item, MfmaLDS<ROUTE_WPB, 1> &S) {
-  static_assert(ROUTE_WPB == 8, "gate and up take four waves each");
-  const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
+// Shared expert gate/up on the matrix cores: item = 16 intermediate rows on
+// the eight waves wb..wb+7; waves wb..wb+3 take the gate rows and the others
+// the up rows, each a quarter of H; writes silu(g) * u to sact.  Every wave
+// of the workgroup calls it (one barrier); live: the item exists.
+template <int NCT, int WPB = ROUTE_WPB>
+__device__ __forceinline__ void shared_gu_mfma(const Args &a, int item, MfmaLDS<WPB, 1> &S, int wb = 0,
+                                               bool live = true) {
+  static_assert(WPB % 8 == 0, "items of eight waves");
+  const int w = uniform_i(threadIdx.x >> 6), wl = w - wb, lane = threadIdx.x & 63;
   const int H = a.H, Is = a.Is, m = a.m, n0 = item * 16;
-  const __amdgpu_buffer_rsrc_t A[1] = {buf_rsrc(w < 4 ? a.sgw : a.suw, Is * H * 2)};
-  int kb, ke;
-  k_slice(H, w & 3, 4, kb, ke);
-  f32x4 acc[1][NCT];
-  mfma_slice<BF16, 1, NCT>(A, H * 2, n0, Is, reinterpret_cast<const char *>(a.x), (size_t)H * 2, m, kb, ke,
-                           S.stage[w], acc);
+  if (live) {
+    const __amdgpu_buffer_rsrc_t A[1] = {buf_rsrc(wl < 4 ? a.sgw : a.suw, Is * H * 2)};
+    int kb, ke;
+    k_slice(H, wl & 3, 4, kb, ke);
+    f32x4 acc[1][NCT];
+    mfma_slice<BF16, 1, NCT>(A, H * 2, n0, Is, reinterpret_cast<const char *>(a.x), (size_t)H * 2, m, kb, ke,
+                             S.stage[w], acc);
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S.part[w][0][ct][i][lane] = acc[0][ct][i];
+      for (int i = 0; i < 4; ++i) S.part[w][0][ct][i][lane] = acc[0][ct][i];
+  }
   __syncthreads();
-  // Wave w finishes (column tile w / 4, element i = w % 4).
-  const int ct = w / 4, i = w % 4;
-  if (ct < NCT) {
+  // Wave wb + j finishes (column tile j / 4, element i = j % 4).
+  const int ct = wl / 4, i = wl % 4;
+  if (live && ct < NCT) {
     float gs = 0.f, us = 0.f;
     for (int p = 0; p < 4; ++p) {
-      gs += S.part[p][0][ct][i][lane];
-      us += S.part[4 + p][0][ct][i][lane];
+      gs += S.part[wb + p][0][ct][i][lane];
+      us += S.part[wb + 4 + p][0][ct][i][lane];
     }
     const int row = n0 + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
     if (row < Is && v < m) a.sact[(size_t)v * Is + row] = act_mul(a.flags, gs, us);
@@ -2988,24 +2993,31 @@ union GateUpRingLDS {
 // Held to 128 registers (two workgroups per CU) but for the 8-vector passes
 // of the vector-unit shared gate/up, which spill there.
 template <int CS> constexpr int route_min_waves() { return CS >= 8 ? 1 : 4; }
-template <int ACT, int CS>
-__global__ __launch_bounds__(ROUTE_THREADS, route_min_waves<CS>()) void route_kernel(Args a) {
+// RT: threads per workgroup.  512 (8 waves, two workgroups per CU); 1024
+// (16 waves, one per CU) above 8 rows when the launch fits one round of
+// those: the routing's top-k then takes up to 16 rows at once, one per wave,
+// and each shared-expert workgroup runs two items of eight waves with the
+// same arithmetic.
+template <int ACT, int CS, int RT = ROUTE_THREADS>
+__global__ __launch_bounds__(RT, route_min_waves<CS>()) void route_kernel(Args a) {
+  constexpr int WPB_R = RT / WAVE;
+  constexpr int UPW = WPB_R / RSPLIT;   // router units per workgroup
   struct RouterSmem {
-    double part[ROUTE_WPB][8];
+    double part[WPB_R][8];
     unsigned ticket;
-    RouteLDS<1024, ROUTE_WPB> L;
+    RouteLDS<1024, WPB_R> L;
   };
   __shared__ union {
     RouterSmem r;
-    MfmaLDS<ROUTE_WPB, 1> mf;
+    MfmaLDS<WPB_R, 1> mf;
   } sm;
   const int item = blockIdx.x, tid = threadIdx.x;
   const int wave = uniform_i(threadIdx.x >> 6);
   if (item < a.n_router_wg) {
-    double (&s_part)[ROUTE_WPB][8] = sm.r.part;
+    double (&s_part)[WPB_R][8] = sm.r.part;
     unsigned &s_ticket = sm.r.ticket;
-    RouteLDS<1024, ROUTE_WPB> &L = sm.r.L;
-    const int unit = item * ROUTE_UNITS_PER_WG + wave / RSPLIT, part = wave % RSPLIT;
+    RouteLDS<1024, WPB_R> &L = sm.r.L;
+    const int unit = item * UPW + wave / RSPLIT, part = wave % RSPLIT;
     const bool live = unit < a.n_router;
     double tot[8];
     if (live) router_part<ACT>(a, unit, part, tot);
@@ -3014,8 +3026,8 @@ __global__ __launch_bounds__(ROUTE_THREADS, route_min_waves<CS>()) void route_ke
       for (int r = 0; r < 8; ++r) s_part[wave][r] = live ? tot[r] : 0.0;
     }
     __syncthreads();
-    if (tid < ROUTE_UNITS_PER_WG * 8) {
-      const int ul = tid / 8, r = tid % 8, u = item * ROUTE_UNITS_PER_WG + ul;
+    if (tid < UPW * 8) {
+      const int ul = tid / 8, r = tid % 8, u = item * UPW + ul;
       const int nrows = router_rows(a);
       const int e = u % nrows, rr = (u / nrows) * 8 + r;
       if (u < a.n_router && rr < a.m) {
@@ -3030,18 +3042,26 @@ __global__ __launch_bounds__(ROUTE_THREADS, route_min_waves<CS>()) void route_ke
     // The logits go out through store_coherent and come back through
     // load_coherent (agent-scope atomics): the hand-off without fences.
     if (!last_arrival<false>(a.sync + SYNC_ROUTER_TICKET, (unsigned)a.n_router_wg, s_ticket)) return;
-    route_all<ROUTE_THREADS, true>(a, L, true, nullptr);
+    route_all<RT, true>(a, L, true, nullptr);
     if (tid == 0) a.sync[SYNC_ROUTER_TICKET] = 0u;  // every ticket is taken
     return;
   }
   const int sitem = item - a.n_router_wg;
   if (ACT == BF16 && a.shared_mfma) {
-    if (a.m > 16) shared_gu_mfma<2>(a, sitem, sm.mf);
-    else shared_gu_mfma<1>(a, sitem, sm.mf);
+    if constexpr (WPB_R == 8) {
+      if (a.m > 16) shared_gu_mfma<2>(a, sitem, sm.mf);
+      else shared_gu_mfma<1>(a, sitem, sm.mf);
+    } else {
+      // Eight waves per item: WPB_R / 8 items per workgroup.
+      const int wb = wave / 8 * 8, it = sitem * (WPB_R / 8) + wave / 8;
+      const bool live = it < a.n_shared_gu;
+      if (a.m > 16) shared_gu_mfma<2, WPB_R>(a, it, sm.mf, wb, live);
+      else shared_gu_mfma<1, WPB_R>(a, it, sm.mf, wb, live);
+    }
     return;
   }
   constexpr int NI = gate_up_ni<ACT>();
-  const int i0 = (sitem * ROUTE_WPB + wave) * NI;
+  const int i0 = (sitem * WPB_R + wave) * NI;
   if (i0 < a.Is)
     gate_up_rows<ACT, ACT, CS, NI>(a, a.sgw, a.suw, nullptr, nullptr, nullptr, nullptr, a.Is, i0, 0,
                                    a.m, nullptr, nullptr, a.sact, a.Is);

@@ -53,7 +53,7 @@ struct FormatKernels {
 
 // First launch: router items plus the shared expert's gate/up items.
 hipError_t launch_route(int act, int cs, const Args &a, int blocks, hipStream_t st, hipEvent_t start,
-                        hipEvent_t stop);
+                        hipEvent_t stop, bool wide);
 hipError_t launch_clear_sync(unsigned *sync, int n, hipStream_t st);
 // The grouped path's router: units of RT_E router rows x 8 input rows.
 hipError_t launch_route_tile(int act, const Args &a, int blocks, hipStream_t st, hipEvent_t start);

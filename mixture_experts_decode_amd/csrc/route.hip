@@ -8,14 +8,22 @@ __global__ void clear_sync_kernel(unsigned *sync, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) sync[i] = 0u;
 }
 
-template <int ACT, int CS>
+template <int ACT, int CS, int RT = ROUTE_THREADS>
 static hipError_t route_launch(const Args &a, int blocks, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
-  return launch_timed(route_kernel<ACT, CS>, blocks, ROUTE_THREADS, st, t0, t1, a);
+  return launch_timed(route_kernel<ACT, CS, RT>, blocks, RT, st, t0, t1, a);
 }
 
 // cs: shared-expert rows per pass, one of the values the host's pass
-// variants use (1, 2, 4, 8).
-hipError_t launch_route(int act, int cs, const Args &a, int blocks, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
+// variants use (1, 2, 4, 8).  wide: 1024-thread workgroups (bf16
+// activations; the shared expert on the matrix cores, or none).
+hipError_t launch_route(int act, int cs, const Args &a, int blocks, hipStream_t st, hipEvent_t t0, hipEvent_t t1,
+                        bool wide) {
+  if (wide) {
+    // Only shared experts on the matrix cores, or none, run there.
+    if (act == BF16 && (a.shared_mfma || a.n_shared_gu == 0))
+      return route_launch<BF16, 1, ROUTE_THREADS_WIDE>(a, blocks, st, t0, t1);
+    return hipErrorInvalidValue;
+  }
   if (act == F32) {
     if (cs == 1) return route_launch<F32, 1>(a, blocks, st, t0, t1);
     if (cs == 2) return route_launch<F32, 2>(a, blocks, st, t0, t1);
