@@ -590,6 +590,29 @@ def test_row_sweep_many_experts(shared_inter):
     torch.cuda.empty_cache()
 
 
+
+def test_row_sweep_many_experts_no_shared():
+    """256 experts, top-8, no shared expert, m from 32 down to 1: above 8 rows
+    the route launch runs on 16-wave workgroups (the top-k of up to 16 rows
+    at once), at most 8 rows on 8-wave ones; every row matches the oracle and
+    is bitwise the same at every m."""
+    spec = small(hidden=256, num_experts=256, top_k=8, inter=128, shared=False, rows=(32,))
+    layer = synth.make_layer(spec, seed=23)
+    x = layer.x(0)
+    ref = oracle.forward(layer, x)
+    dl = DeviceLayer(layer)
+    full = None
+    for m in range(32, 0, -1):
+        say(f"[gpu] E=256 k=8 no shared m={m}")
+        got, idx, w = run(dl, x, m)
+        check(spec, got, idx, w, ref, m, TOL["bf16"], f"no shared m={m}")
+        check_sort(dl, m, idx)
+        if full is None:
+            full = got
+        assert np.array_equal(got, full[:m]), f"rows differ between m={m} and m=32"
+    del dl
+    torch.cuda.empty_cache()
+
 # The 4-bit workloads with 256 experts, up to the decode path's 32 rows.
 @pytest.mark.parametrize("name", ["qwen35_35b_a3b_mxfp4", "qwen35_35b_a3b_nvfp4", "qwen35_35b_a3b_fp8"])
 def test_workload_rows_to_32(name):
