@@ -38,6 +38,12 @@ enum : int { F32 = 0, BF16 = 1, AFF4 = 2, MXFP4 = 3, NVFP4 = 4, FP8 = 5 };
 // (i / 32) * 8 + i % 8), so that in sub-step g adjacent lanes (adjacent
 // 32-element chunks) read adjacent 32-byte blocks.
 enum : int { F32P = 16 };
+// F32I: an f32 vector stored, 4 bytes per element, as the bf16 pair the
+// matrix-core products take -- the value's high half (its top 16 bits) in
+// the low 16 bits, the bf16 rounding of the rest in the high 16 -- written
+// once where the vector is produced; readers unpack pairs instead of
+// splitting every value in every item.
+enum : int { F32I = 17 };
 // The packed 4-bit formats (two codes per byte, per-row block scales).
 constexpr bool is_fp4(int f) { return f == AFF4 || f == MXFP4 || f == NVFP4; }
 // Formats whose chunks carry dequant constants beside the codes.
@@ -1067,6 +1073,27 @@ __device__ __forceinline__ void split_bf16(const u32x4 &a, const u32x4 &b, bf16x
   lo = __builtin_bit_cast(bf16x8, rv);
 }
 
+// F32I pairs (hi in the low half, lo in the high half) of 8 elements into
+// the hi and lo operands split_bf16 makes from the f32 values.
+__device__ __forceinline__ void unpack_bf16(const u32x4 &a, const u32x4 &b, bf16x8 &hi, bf16x8 &lo) {
+  const uint32_t p[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[4], r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = __builtin_amdgcn_perm(p[2 * i + 1], p[2 * i], 0x05040100u);
+    r[i] = __builtin_amdgcn_perm(p[2 * i + 1], p[2 * i], 0x07060302u);
+  }
+  const u32x4 hv = {h[0], h[1], h[2], h[3]}, rv = {r[0], r[1], r[2], r[3]};
+  hi = __builtin_bit_cast(bf16x8, hv);
+  lo = __builtin_bit_cast(bf16x8, rv);
+}
+
+// One f32 value as its F32I pair.
+__device__ __forceinline__ uint32_t f32i_pair(float v) {
+  const uint32_t f = __float_as_uint(v);
+  return (f >> 16) | ((uint32_t)f32_to_bf16(v - __uint_as_float(f & 0xFFFF0000u)) << 16);
+}
+
 __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const bf16x8 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
 }
@@ -1095,8 +1122,8 @@ __device__ __forceinline__ void mfma_slice_v(const __amdgpu_buffer_rsrc_t (&A)[N
                                              f32x4 (&acc)[NA][NCT]) {
   constexpr int ROW = MU * 64 + 16, STAGE = 16 * ROW;   // staging layout of MU k-steps
   static_assert(MU <= MF_U, "the wave's staging region holds MF_U k-steps");
-  constexpr int XB = XF == F32 ? 4 : 2;
-  constexpr int XL = XF == F32 ? 2 : 1;   // 16-byte x loads per step and column tile
+  constexpr int XB = XF == F32 || XF == F32I ? 4 : 2;
+  constexpr int XL = XF == BF16 ? 1 : 2;   // 16-byte x loads per step and column tile
   const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
   // Loader: a staged row is MU * 64 bytes, LR = 4 MU lanes of 16 bytes;
   // instruction i brings rows RI i + l / LR (RI = 16 / MU rows per
@@ -1171,7 +1198,8 @@ __device__ __forceinline__ void mfma_slice_v(const __amdgpu_buffer_rsrc_t (&A)[N
             for (int j = 0; j < NA; ++j) acc[j][ct] = mfma16(av[j], bb, acc[j][ct]);
           } else {
             bf16x8 hi, lo;
-            split_bf16(bv[u][ct][0], bv[u][ct][XL - 1], hi, lo);
+            if constexpr (XF == F32I) unpack_bf16(bv[u][ct][0], bv[u][ct][XL - 1], hi, lo);
+            else split_bf16(bv[u][ct][0], bv[u][ct][XL - 1], hi, lo);
 #pragma unroll
             for (int j = 0; j < NA; ++j) {
               acc[j][ct] = mfma16(av[j], hi, acc[j][ct]);
@@ -1192,7 +1220,7 @@ template <int XF, int NA, int NCT, int MU = MF_U>
 __device__ __forceinline__ void mfma_slice(const __amdgpu_buffer_rsrc_t (&A)[NA], int rb, int n0, int N,
                                            const char *x, size_t xstride, int nv, int kb, int ke,
                                            char *stage, f32x4 (&acc)[NA][NCT]) {
-  constexpr int XB = XF == F32 ? 4 : 2;
+  constexpr int XB = XF == F32 || XF == F32I ? 4 : 2;
   const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
   const char *xv[NCT];
 #pragma unroll
@@ -1352,7 +1380,7 @@ __device__ __forceinline__ void mfma_slice_q(const QMat<WF> (&A)[NA], int K, int
   constexpr int ROW = MU * 64 + 16, STAGE = 16 * ROW;
   static_assert(MU == 2, "two k steps per batch");
   static_assert(WF == MXFP4 || WF == NVFP4, "4-bit formats");
-  constexpr int XB = XF == F32 ? 4 : 2;
+  constexpr int XB = XF == F32 || XF == F32I ? 4 : 2;
   constexpr int XL = XF == F32 ? 2 : 1;
   const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
   const int lr = l >> 2, ks = (l >> 1) & 1, hh = l & 1;
@@ -1429,7 +1457,8 @@ __device__ __forceinline__ void mfma_slice_q(const QMat<WF> (&A)[NA], int K, int
             for (int j = 0; j < NA; ++j) acc[j][ct] = mfma16(av[j], bb, acc[j][ct]);
           } else {
             bf16x8 hi, lo;
-            split_bf16(bv[u][ct][0], bv[u][ct][XL - 1], hi, lo);
+            if constexpr (XF == F32I) unpack_bf16(bv[u][ct][0], bv[u][ct][XL - 1], hi, lo);
+            else split_bf16(bv[u][ct][0], bv[u][ct][XL - 1], hi, lo);
 #pragma unroll
             for (int j = 0; j < NA; ++j) {
               acc[j][ct] = mfma16(av[j], hi, acc[j][ct]);
@@ -1460,7 +1489,7 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
   static_assert(WF == MXFP4 || WF == NVFP4, "4-bit formats with one scale per code block");
   static_assert(MU == 1 || MU == 2 || MU == 4, "a lane's range lies in one scale block");
   constexpr int CB = 4 * MU;                       // code bytes per lane per batch
-  constexpr int XB = XF == F32 ? 4 : 2;
+  constexpr int XB = XF == F32 || XF == F32I ? 4 : 2;
   constexpr int XQ = 8 * MU * XB / 16;             // 16-byte x loads per lane, batch and tile
   const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
   const int row = min(n0 + rr, N - 1);
@@ -1549,7 +1578,8 @@ __device__ __forceinline__ void mfma_slice_qd(const QMat<WF> (&A)[NA], int K, in
           for (int j = 0; j < NA; ++j) acc[j][ct] = mfma16(av[j], bb, acc[j][ct]);
         } else {
           bf16x8 hi, lo;
-          split_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
+          if constexpr (XF == F32I) unpack_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
+          else split_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
 #pragma unroll
           for (int j = 0; j < NA; ++j) {
             acc[j][ct] = mfma16(av[j], hi, acc[j][ct]);
@@ -1604,7 +1634,7 @@ template <int XF, int NA, int NCT>
 __device__ __forceinline__ void mfma_slice_aff4(const QMat<AFF4> (&A)[NA], int K, int n0, int N,
                                                 const char *const (&xr)[NCT], int kb, int ke,
                                                 f32x4 (&acc)[NA][NCT]) {
-  constexpr int XB = XF == F32 ? 4 : 2;
+  constexpr int XB = XF == F32 || XF == F32I ? 4 : 2;
   constexpr int XQ = XB;                           // 16-byte x loads per lane, group and tile
   const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
   const int qoff = min(n0 + rr, N - 1) * (K / 2) + g * 8;
@@ -1673,7 +1703,8 @@ __device__ __forceinline__ void mfma_slice_aff4(const QMat<AFF4> (&A)[NA], int K
           for (int j = 0; j < NA; ++j) D[j][ct] = mfma16(av[j], bb, u ? D[j][ct] : zero);
         } else {
           bf16x8 hi, lo;
-          split_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
+          if constexpr (XF == F32I) unpack_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
+          else split_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
           X[ct] = mfma16(ones, hi, u ? X[ct] : zero);
           X[ct] = mfma16(ones, lo, X[ct]);
 #pragma unroll
@@ -1722,7 +1753,7 @@ template <int XF, int NA, int NCT>
 __device__ __forceinline__ void mfma_slice_f8(const QMat<FP8> (&A)[NA], int K, int n0, int N,
                                               const char *const (&xr)[NCT], int kb, int ke,
                                               f32x4 (&acc)[NA][NCT]) {
-  constexpr int XB = XF == F32 ? 4 : 2;
+  constexpr int XB = XF == F32 || XF == F32I ? 4 : 2;
   constexpr int XQ = XB;                           // 16-byte x loads per lane, batch and tile
   const int l = threadIdx.x & 63, g = l >> 4, rr = l & 15;
   const int qoff = min(n0 + rr, N - 1) * K + g * 16;
@@ -1784,7 +1815,8 @@ __device__ __forceinline__ void mfma_slice_f8(const QMat<FP8> (&A)[NA], int K, i
           for (int j = 0; j < NA; ++j) D[j][ct] = mfma16(av[j], bb, fresh ? zero : D[j][ct]);
         } else {
           bf16x8 hi, lo;
-          split_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
+          if constexpr (XF == F32I) unpack_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
+          else split_bf16(cx[ct][2 * u], cx[ct][2 * u + 1], hi, lo);
 #pragma unroll
           for (int j = 0; j < NA; ++j) {
             D[j][ct] = mfma16(av[j], hi, fresh ? zero : D[j][ct]);
@@ -3677,9 +3709,10 @@ __global__ __launch_bounds__(64 * gu_grouped_waves<EF>(), gu_grouped_min_waves<E
             gs *= wt;
             us *= wt;
           }
-          a.act[(size_t)(it.off + c0 + v) * a.I + row] = act_mul(a.flags, gs, us);
+          // Stored as F32I pairs, the form the grouped down reads.
+          reinterpret_cast<uint32_t *>(a.act)[(size_t)(it.off + c0 + v) * a.I + row] = f32i_pair(act_mul(a.flags, gs, us));
         } else {
-          a.sact[(size_t)(it.off + c0 + v) * a.Is + row] = act_mul(a.flags, gs, us);
+          reinterpret_cast<uint32_t *>(a.sact)[(size_t)(it.off + c0 + v) * a.Is + row] = f32i_pair(act_mul(a.flags, gs, us));
         }
       }
     }
@@ -3761,6 +3794,7 @@ __global__ __launch_bounds__((down_grouped_threads<EF, WIDE>())) void down_group
   if (EF == AFF4 && quant) k_slice64(K, w, NW, kb, ke);   // whole scale groups
   else if (EF == FP8 && quant) k_slice128(K, w, NW, kb, ke);
   else k_slice(K, w, NW, kb, ke);
+  // The input rows as F32I pairs (written so by the grouped gate/up).
   const char *xb = reinterpret_cast<const char *>((it.routed ? a.act : a.sact) + (size_t)it.off * K);
   float *dst = (it.routed ? a.y : a.sy) + (size_t)it.off * H;
   // One pass: NCT column tiles of 16 pairs from c0 on.
@@ -3770,13 +3804,13 @@ __global__ __launch_bounds__((down_grouped_threads<EF, WIDE>())) void down_group
     if (quant) {   // 4-bit codes straight into the operands; passes of one column tile
       if constexpr (NCT == 1) {
         const char *xr[1] = {xb + (size_t)(c0 + min(lane & 15, nv - 1)) * K * 4};
-        if constexpr (QF == AFF4) mfma_slice_aff4<F32, NA, 1>(Q, K, 0, 16, xr, kb, ke, acc);
-        else if constexpr (QF == FP8) mfma_slice_f8<F32, NA, 1>(Q, K, 0, 16, xr, kb, ke, acc);
-        else mfma_slice_qd<QF, F32, NA, 1, 2>(Q, K, 0, 16, xr, kb, ke, acc);
+        if constexpr (QF == AFF4) mfma_slice_aff4<F32I, NA, 1>(Q, K, 0, 16, xr, kb, ke, acc);
+        else if constexpr (QF == FP8) mfma_slice_f8<F32I, NA, 1>(Q, K, 0, 16, xr, kb, ke, acc);
+        else mfma_slice_qd<QF, F32I, NA, 1, 2>(Q, K, 0, 16, xr, kb, ke, acc);
       }
     } else {
-      mfma_slice<F32, NA, NCT, MU>(A, K * 2, 0, 16, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
-                                   S.stage[w], acc);
+      mfma_slice<F32I, NA, NCT, MU>(A, K * 2, 0, 16, xb + (size_t)c0 * K * 4, (size_t)K * 4, nv, kb, ke,
+                                    S.stage[w], acc);
     }
 #pragma unroll
     for (int j = 0; j < NA; ++j)
