@@ -1301,7 +1301,7 @@ __device__ __forceinline__ void mfma_slice_dma(__amdgpu_buffer_rsrc_t A, int rb,
             : "v"(pa), "v"(px)
             : "memory");
         bf16x8 hi, lo;
-        split_bf16(b0, b1, hi, lo);
+        unpack_bf16(b0, b1, hi, lo);   // the input is stored as F32I pairs
         acc = mfma16(av, hi, acc);
         acc = mfma16(av, lo, acc);
       }
@@ -2910,7 +2910,8 @@ __device__ __forceinline__ void shared_gu_mfma(const Args &a, int item, MfmaLDS<
       us += S.part[wb + 4 + p][0][ct][i][lane];
     }
     const int row = n0 + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
-    if (row < Is && v < m) a.sact[(size_t)v * Is + row] = act_mul(a.flags, gs, us);
+    // Stored as F32I pairs, the form the matrix-core shared down reads.
+    if (row < Is && v < m) reinterpret_cast<uint32_t *>(a.sact)[(size_t)v * Is + row] = f32i_pair(act_mul(a.flags, gs, us));
   }
 }
 
@@ -2928,8 +2929,8 @@ __device__ __forceinline__ void shared_dn_mfma(const Args &a, int item, MfmaLDS<
   k_slice(Is, q, P, pb, pe);
   k_slice(pe - pb, w, WPB, kb, ke);
   f32x4 acc[1][NCT];
-  mfma_slice<F32, 1, NCT, MU>(A, Is * 2, n0, H, reinterpret_cast<const char *>(a.sact), (size_t)Is * 4, m,
-                          pb + kb, pb + ke, S.stage[w], acc);
+  mfma_slice<F32I, 1, NCT, MU>(A, Is * 2, n0, H, reinterpret_cast<const char *>(a.sact), (size_t)Is * 4, m,
+                           pb + kb, pb + ke, S.stage[w], acc);
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
