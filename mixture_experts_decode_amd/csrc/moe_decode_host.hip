@@ -500,6 +500,10 @@ moe_status forward_impl(const moe_decode_plan_t *plan, const moe_decode_weights 
   // route launch, down in the gate/up launch) for bf16 activations when H and
   // Is are multiples of 32; on the vector units otherwise.
   a.shared_mfma = shared_on_matrix_cores(d);
+  // With bf16 experts the matrix-core shared activations travel as bf16
+  // pairs (their shared down skips the per-item split); the other formats'
+  // shared downs measured faster splitting f32.  A plan constant.
+  a.sact_pairs = a.shared_mfma && d.expert_fmt == MOE_BF16 ? 1 : 0;
   const int ni_r = d.expert_fmt >= MOE_AFF4_G64 && cr == 1 ? 4 : 2;   // gate_up_ni<EF, CR>()
   a.max_rows = d.max_rows;
   a.sd_parts = shared_down_parts(d);

@@ -154,6 +154,7 @@ struct Args {
   int n_router, n_router_wg, n_shared_gu, gu_items_per_slot, n_routed_gu, n_down, down_dq;
   int route_in_gu;         // 1: every gate/up workgroup routes; 0: the last router workgroup does
   int shared_mfma;         // shared expert on the matrix cores (bf16 activations, H and Is multiples of 32)
+  int sact_pairs;          // matrix-core shared activations stored as F32I pairs (bf16 experts), else f32
   int n_shared_dn;         // shared down items in the gate/up launch (matrix-core path)
   int sd_parts;            // parts of Is the shared down items split (partials in sy[part])
   int down_parts;          // parts of I each routed down row is split into (partials added in the blend)
@@ -2910,8 +2911,13 @@ __device__ __forceinline__ void shared_gu_mfma(const Args &a, int item, MfmaLDS<
       us += S.part[wb + 4 + p][0][ct][i][lane];
     }
     const int row = n0 + (lane >> 4) * 4 + i, v = 16 * ct + (lane & 15);
-    // Stored as F32I pairs, the form the matrix-core shared down reads.
-    if (row < Is && v < m) reinterpret_cast<uint32_t *>(a.sact)[(size_t)v * Is + row] = f32i_pair(act_mul(a.flags, gs, us));
+    // With bf16 experts stored as F32I pairs, the form their matrix-core
+    // shared down reads (it then skips the per-item split); else f32.
+    if (row < Is && v < m) {
+      const float y = act_mul(a.flags, gs, us);
+      if (a.sact_pairs) reinterpret_cast<uint32_t *>(a.sact)[(size_t)v * Is + row] = f32i_pair(y);
+      else a.sact[(size_t)v * Is + row] = y;
+    }
   }
 }
 
@@ -2919,7 +2925,8 @@ __device__ __forceinline__ void shared_gu_mfma(const Args &a, int item, MfmaLDS<
 // of the a.sd_parts parts of Is); the WPB waves of the workgroup split the
 // part, and the part's total goes to sy[q] (the blend adds the parts in
 // order).
-template <int NCT, int MU>
+// XF: how the shared activations are stored (F32I with bf16 experts, F32).
+template <int NCT, int MU, int XF>
 __device__ __forceinline__ void shared_dn_mfma(const Args &a, int item, MfmaLDS<WPB, 1, MU> &S) {
   const int w = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int H = a.H, Is = a.Is, m = a.m, P = a.sd_parts;
@@ -2929,8 +2936,8 @@ __device__ __forceinline__ void shared_dn_mfma(const Args &a, int item, MfmaLDS<
   k_slice(Is, q, P, pb, pe);
   k_slice(pe - pb, w, WPB, kb, ke);
   f32x4 acc[1][NCT];
-  mfma_slice<F32I, 1, NCT, MU>(A, Is * 2, n0, H, reinterpret_cast<const char *>(a.sact), (size_t)Is * 4, m,
-                           pb + kb, pb + ke, S.stage[w], acc);
+  mfma_slice<XF, 1, NCT, MU>(A, Is * 2, n0, H, reinterpret_cast<const char *>(a.sact), (size_t)Is * 4, m,
+                         pb + kb, pb + ke, S.stage[w], acc);
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -2972,9 +2979,10 @@ __device__ __forceinline__ void shared_dn_ring(const Args &a, int item, SharedDn
   __syncthreads();   // S is reused by the workgroup's next item
 }
 
-template <int ACT, int NCT, int MU>
+template <int ACT, int NCT, int MU, int EF>
 __device__ __forceinline__ void shared_dn_item(const Args &a, int item, MfmaLDS<WPB, 1, MU> &S) {
-  if constexpr (ACT == BF16 && NCT > 0) shared_dn_mfma<NCT, MU>(a, item, S);   // the matrix-core path
+  // The matrix-core path; the activations are F32I pairs with bf16 experts.
+  if constexpr (ACT == BF16 && NCT > 0) shared_dn_mfma<NCT, MU, EF == BF16 ? F32I : F32>(a, item, S);
 }
 
 // k-steps per batch of the shared down items in a gate/up variant: 2 where
@@ -3165,7 +3173,7 @@ void gate_up_kernel(Args a) {
   __shared__ std::conditional_t<RING, GateUpRingLDS, GateUpLDS<(SHD > 0), SDMU>> G;
   auto shared_item = [&](int it) {
     if constexpr (RING) shared_dn_ring(a, it, G.ring);
-    else if constexpr (SHD > 0) shared_dn_item<ACT, SHD, SDMU>(a, it, G.mf);
+    else if constexpr (SHD > 0) shared_dn_item<ACT, SHD, SDMU, EF>(a, it, G.mf);
   };
   // The route launch is over: its ticket word starts the next forward at 0,
   // whatever this forward found in it.
