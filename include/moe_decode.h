@@ -196,8 +196,13 @@ typedef struct {
                              down_w, down_s, down_b entries (uint64), then 40 zero bytes */
   size_t act;             /* float [te, I]: routed SwiGLU activations, sorted order; for 4-bit
                              experts each row is stored sub-step-major: element i at
-                             ((i % 32) / 8) * (I / 4) + (i / 32) * 8 + i % 8 */
-  size_t shared_act;      /* float [max_rows, Is] */
+                             ((i % 32) / 8) * (I / 4) + (i / 32) * 8 + i % 8.  Above 32
+                             rows each 4-byte element holds the value as a bf16 pair:
+                             its top 16 bits in the low half, the bf16 rounding of the
+                             remainder in the high half */
+  size_t shared_act;      /* float [max_rows, Is]; as bf16 pairs (like act above 32 rows)
+                             above 32 rows, and at every m with bf16 experts and the shared
+                             expert on the matrix cores */
   size_t shared_y;        /* float [P, max_rows, H]: shared-expert output in P parts of Is
                              (matrix-core path; P = max(1, min(Is / 2048, 16))) */
   size_t routed_y;        /* float [te, H]: routed expert outputs per pair, sorted order
